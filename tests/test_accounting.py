@@ -1,0 +1,62 @@
+"""Byte and FLOP accounting against the numbers the pages print."""
+import json
+import os
+
+import pytest
+
+from block_sparse_long_page_amd import accounting as acc
+from block_sparse_long_page_amd import configs
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+GiB = float(1 << 30)
+
+
+def _unit(v, unit):
+    return v * (GiB if unit == "GiB" else 1e9)
+
+
+@pytest.mark.parametrize("e", G["kv_bytes"], ids=lambda e: str(e["layers"]))
+def test_kv_bytes(e):
+    per = acc.kv_bytes_per_token(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"])
+    if "bytes_per_token" in e:
+        assert per == e["bytes_per_token"]
+    tol = e["tolerance"]
+    for tokens, val, unit in e.get("at_tokens", []):
+        got = acc.kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"], tokens)
+        assert abs(got - _unit(val, unit)) <= tol * _unit(val, unit)
+    for tokens, batch, val, unit in e.get("at_batch", []):
+        got = acc.kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"], tokens, batch)
+        assert abs(got - _unit(val, unit)) <= tol * _unit(val, unit)
+    for heads, val, unit in e.get("kv_heads_alt", []):
+        got = acc.kv_cache_bytes(e["layers"], heads, e["head_dim"], e["elem_bytes"], e["at_tokens"][0][0])
+        assert abs(got - _unit(val, unit)) <= tol * _unit(val, unit)
+
+
+def test_block_sparse_flop_ratio():
+    f = G["flop_ratio"]
+    r = acc.block_sparse_flops(f["n"], f["head_dim"], f["block"], f["topk"]) / acc.dense_flops(f["n"], f["head_dim"])
+    assert r == pytest.approx(f["ratio"], abs=1e-12)
+    assert r == pytest.approx(f["topk"] * f["block"] / f["n"])
+
+
+def test_read_time_floor():
+    r = G["read_time"]
+    ms = r["bytes_gib"] * GiB / (r["bandwidth_tb_s"] * 1e12) * 1e3
+    assert abs(ms - r["ms"]) <= r["tolerance"] * ms + 0.2
+
+
+@pytest.mark.parametrize("c", G["candidates"]["cases"], ids=lambda c: str(c["L"]))
+def test_candidate_counts(c):
+    assert acc.candidate_pages(c["L"], c["P"], c["S"], c["W"]) == c["candidates"]
+
+
+def test_headline_step_bytes():
+    w = configs.LLAMA3_70B
+    sb = acc.decode_step_bytes(B=w.batch, Hq=w.num_q_heads, Hkv=w.num_kv_heads, hd=w.head_dim, elem_bytes=2,
+                               L=w.context, P=w.page_size, S=w.sink, W=w.window, budget=w.budget, mode=0, splits=32)
+    # 256 sink + 4096 window + 128 pages x 64 = 12544 tokens per (b, kv head), 512 B each for K+V
+    assert sb.kv == 32 * 12544 * 512
+    assert sb.meta == 32 * 1980 * 512
+    # the attended share of the dense cache is (S + W + k P) / L
+    assert acc.attended_tokens(w.context, w.page_size, w.sink, w.window, w.k_pages) / w.context == pytest.approx(
+        12544 / 131072)
