@@ -1,0 +1,269 @@
+"""Benchmark: one decode step of block/page-sparse attention on one MI355X.
+
+A step is the whole per-token hot path on one batch: page selection (scores
++ per-KV-head top-k), split-K decode over sink + window + selected pages,
+and the log-sum-exp combine.  The workload is the Llama-3-70B-shaped layer
+at 128k context with GQA-8 (batch 4, 64 q / 8 KV heads, head dim 128, bf16,
+page 64, sink 256, window 4096, budget L/16 = 8192 tokens, Quest min/max
+scores, keys from 64 Gaussian clusters), on seeded synthetic inputs already
+resident in HBM.
+
+To keep the 256 MB last-level cache from serving repeated reads, the timed
+steps rotate over R copies of the cache (distinct physical pages, the same
+contents), so each step reads pages no recent step touched.
+
+Prints one JSON line: selected-KV GB/s (algorithmic bytes / step time),
+us/step, the roofline of the decode kernel (HIP-event time of its launches
+inside the timed region) and the fp64 CPU oracle timed on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--replicas R] [--splits S]
+                    [--no-cpu-baseline] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_long_page_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--dense-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
+    return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 10
+    print(json.dumps({"copy_bytes": n, "ms": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}))
+
+
+def traffic_record():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when the decode source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_src_sha256") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no collectives; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    from block_sparse_long_page_amd import accounting, binding as B, configs, synth
+    from block_sparse_long_page_amd.device import DeviceCache, SparseDecoder, to_device
+
+    wl = configs.LLAMA3_70B
+    t0 = time.time()
+    pr = synth.workload_problem(wl)
+    c = pr.cache
+    log(f"inputs {time.time() - t0:.1f}s")
+
+    # R copies of the cache in one physical-page pool; replica r's table points at its own pages
+    R = max(1, args.replicas)
+    pool = DeviceCache.from_host(c)
+    if R > 1:
+        k_all = torch.empty((R * c.num_phys,) + tuple(pool.k.shape[1:]), dtype=pool.k.dtype, device="cuda")
+        v_all = torch.empty_like(k_all)
+        for r in range(R):
+            k_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.k)
+            v_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.v)
+        pool.k, pool.v, pool.num_phys = k_all, v_all, R * c.num_phys
+    tables = []
+    for r in range(R):
+        bt = c.block_table.astype(np.int64)
+        bt = np.where(bt >= 0, bt + r * c.num_phys, -1).astype(np.int32)
+        tables.append(to_device(bt))
+    q = to_device(pr.q)
+
+    dec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
+                        splits=args.splits or None)
+    descs = [pool.desc(block_table=t) for t in tables]
+    for d in descs:
+        B.sparse_attn_build_page_meta(d, pr.mode, 0, pool.max_pages, dec.meta)
+    torch.cuda.synchronize()
+
+    def step(r, ev=None):
+        d = descs[r]
+        B.sparse_attn_select(d, q, 1, dec.meta, pr.mode, pr.sink, pr.window, pr.budget, dec.sel, dec.count,
+                             dec.ws, dec.ws_bytes)
+        if ev is not None:
+            ev[0].record()
+        B.sparse_attn_decode(d, q, 1, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, 0.0, dec.splits,
+                             dec.part_o, dec.part_ml)
+        if ev is not None:
+            ev[1].record()
+        B.sparse_attn_combine(dec.rows, c.hd, dec.splits, dec.part_o, dec.part_ml, dec.out, dec.out_dtype,
+                              dec.lse)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+
+    # algorithmic bytes of one step and of one decode launch
+    L = int(c.seq_lens[0])
+    attended = [accounting.attended_tokens_exact(L, c.P, pr.sink, pr.window, sel[b, h, 0, : cnt[b, h, 0]])
+                for b in range(c.B) for h in range(c.Hkv)]
+    sb = accounting.decode_step_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2, L=L, P=c.P, S=pr.sink,
+                                      W=pr.window, budget=pr.budget, mode=pr.mode, splits=dec.splits,
+                                      attended=attended)
+    dec_bytes = accounting.decode_kernel_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
+                                               ntok_total=sum(attended), splits=dec.splits,
+                                               sel_entries=int(cnt.sum()))
+
+    # timed region: K steps, each with HIP events around its decode launch
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(i % R, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / K
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+
+    # the same loop without the per-kernel events
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(i % R)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_noev = start.elapsed_time(stop) / K
+
+    # one replica (repeated reads may hit the last-level cache)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(0)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_hot = start.elapsed_time(stop) / K
+
+    # dense decode of the same cache: every page, same kernels, no selection
+    ddec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pool.max_pages * c.P)
+    for i in range(2):
+        ddec.desc = descs[i % R]
+        ddec.decode(q, dense=True)
+        ddec.combine()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.dense_steps):
+        ddec.desc = descs[i % R]
+        ddec.decode(q, dense=True)
+        ddec.combine()
+    stop.record()
+    torch.cuda.synchronize()
+    dense_ms = start.elapsed_time(stop) / args.dense_steps
+
+    gbps = sb.total / (ms * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        times = []
+        t_end = time.time() + args.cpu_seconds
+        while len(times) < 3 or time.time() < t_end:
+            t1 = time.perf_counter()
+            oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+            times.append(time.perf_counter() - t1)
+            if len(times) >= 200:
+                break
+        med = statistics.median(times)
+        cpu = {"value": round(sb.total / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": f"the full step (summaries of all pages, scores, top-k, attention) "
+                                           f"in fp64, repeated {len(times)} times; median {med * 1e3:.1f} ms/step",
+               "ms_per_step": round(med * 1e3, 2)}
+
+    rec = {
+        "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 128k ctx GQA-8",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded): K from 64 Gaussian clusters, V and q N(0,1)",
+        "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
+                   "context": L, "page": c.P, "sink": pr.sink, "window": pr.window, "budget": pr.budget,
+                   "score": "quest", "splits": dec.splits, "replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_record(), "bytes_per_launch": dec_bytes,
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "bytes_per_step": sb.as_dict(),
+        "us_per_step_no_events": round(ms_noev * 1e3, 2),
+        "us_per_step_one_replica": round(ms_hot * 1e3, 2),
+        "dense_us_per_step": round(dense_ms * 1e3, 2),
+        "speedup_vs_dense": round(dense_ms / ms, 2),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

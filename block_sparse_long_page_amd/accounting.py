@@ -105,3 +105,20 @@ def decode_kernel_bytes(*, B: int, Hq: int, Hkv: int, hd: int, elem_bytes: int, 
     selected page list it reads and the partials it writes."""
     rows = B * Hq * Q
     return ntok_total * 2 * hd * elem_bytes + rows * hd * elem_bytes + 4 * sel_entries + rows * splits * (hd + 2) * 4
+
+
+def attended_tokens_exact(L: int, P: int, S: int, W: int, pages, Q: int = 1, row: int = None) -> int:
+    """Tokens attended by query row `row` (default: the last) given the
+    selected logical pages: the sink, the window and the middle part of each
+    selected page, each position once, positions <= the row's own."""
+    import numpy as np
+
+    row = Q - 1 if row is None else row
+    pos = L - Q + row
+    se, ws = regions(L, S, W)
+    n = min(se, pos + 1) + max(0, min(L, pos + 1) - ws)
+    for p in np.unique(np.asarray(pages, dtype=np.int64)):
+        a = max(int(p) * P, se)
+        z = min((int(p) + 1) * P, ws, pos + 1)
+        n += max(0, z - a)
+    return n

@@ -1,0 +1,142 @@
+"""Thin ctypes binding of libsparse_attn.so (include/sparse_attn.h).
+
+The functions keep the C names and only marshal arguments: tensors become
+device pointers, the stream defaults to torch's current stream, and a
+non-zero status raises SparseAttnError.  Every step of the path runs in the
+library's HIP kernels; there is no fallback.  If the library has not been
+built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsparse_attn.so")
+HEADER = os.path.join(PKG, os.pardir, "include", "sparse_attn.h")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
+SA_F32, SA_BF16 = 0, 1
+SA_QUEST, SA_MEAN, SA_CENTROID = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(python -m block_sparse_long_page_amd._build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.sparse_attn_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+class sa_kv_desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_DESC = ctypes.POINTER(sa_kv_desc)
+_SIGS = {
+    "sparse_attn_build_page_meta": (ctypes.c_int, [_DESC, _I, _I, _I, _P, _P]),
+    "sparse_attn_select": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sparse_attn_workspace_bytes": (ctypes.c_size_t, [_DESC, _I]),
+    "sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P]),
+    "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
+    "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def header_symbols() -> list:
+    """Function names the public header declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+[\s\*]+(sparse_attn_\w+)\s*\(", text, re.M)))
+
+
+def library():
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != SA_OK:
+        raise SparseAttnError(rc, where)
+
+
+def make_kv_desc(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_phys_pages,
+                 max_seq_len, dtype, k_cache, v_cache, block_table, seq_lens) -> sa_kv_desc:
+    return sa_kv_desc(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_phys_pages,
+                      max_seq_len, dtype, _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens))
+
+
+def sparse_attn_build_page_meta(kv: sa_kv_desc, score_mode: int, page_begin: int, page_end: int, meta,
+                                stream=None) -> None:
+    _check(_lib.sparse_attn_build_page_meta(ctypes.byref(kv), score_mode, page_begin, page_end, _ptr(meta),
+                                            _stream(stream)), "sparse_attn_build_page_meta")
+
+
+def sparse_attn_workspace_bytes(kv: sa_kv_desc, num_q_rows: int) -> int:
+    return int(_lib.sparse_attn_workspace_bytes(ctypes.byref(kv), num_q_rows))
+
+
+def sparse_attn_select(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode: int, sink_len: int, window_len: int,
+                       token_budget: int, sel_pages, sel_count, workspace, workspace_bytes: int,
+                       stream=None) -> None:
+    _check(_lib.sparse_attn_select(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(meta), score_mode, sink_len,
+                                   window_len, token_budget, _ptr(sel_pages), _ptr(sel_count), _ptr(workspace),
+                                   workspace_bytes, _stream(stream)), "sparse_attn_select")
+
+
+def sparse_attn_default_splits(kv: sa_kv_desc, num_q_rows: int, sink_len: int, window_len: int, k_max: int) -> int:
+    return int(_lib.sparse_attn_default_splits(ctypes.byref(kv), num_q_rows, sink_len, window_len, k_max))
+
+
+def sparse_attn_decode(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count, k_max: int, sink_len: int,
+                       window_len: int, softmax_scale: float, num_splits: int, part_o, part_ml,
+                       stream=None) -> None:
+    _check(_lib.sparse_attn_decode(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(sel_pages), _ptr(sel_count), k_max,
+                                   sink_len, window_len, softmax_scale, num_splits, _ptr(part_o), _ptr(part_ml),
+                                   _stream(stream)), "sparse_attn_decode")
+
+
+def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, part_ml, out, out_dtype: int,
+                        lse=None, stream=None) -> None:
+    _check(_lib.sparse_attn_combine(num_rows, head_dim, num_splits, _ptr(part_o), _ptr(part_ml), _ptr(out),
+                                    out_dtype, _ptr(lse), _stream(stream)), "sparse_attn_combine")
+
+
+def sparse_attn_status_string(status: int) -> str:
+    return _lib.sparse_attn_status_string(status).decode()

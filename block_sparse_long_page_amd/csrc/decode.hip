@@ -1,0 +1,245 @@
+// Split-K flash decode over the attended token set (sink + window + the
+// middle tokens of the selected pages), exact softmax with a running maximum
+// and sum (FlashAttention's online softmax, attention-mechanisms article,
+// "FlashAttention does not change what the model looks at").
+//
+// Workgroup = one (sequence, KV head, query row, split); its four waves each
+// stream a contiguous quarter of the split's tokens.  Lane layout inside a
+// wave: LPT lanes hold one key/value row with 16-byte loads (8 bf16 or 4 fp32
+// channels per lane), so 64/LPT tokens are in flight per load instruction and
+// U loads of K and of V per lane per iteration.  Every K/V row is read once
+// and shared by the G query heads of the group.
+//
+// q.k: packed bf16 dot products into fp32 (or fp32 FMAs), summed over the
+// LPT lanes with DPP row operations.  Softmax in base 2 with a lazily
+// rescaled reference maximum: the accumulators are rescaled only when a
+// logit exceeds the reference by more than 2^8, which keeps every weight
+// <= 256 and skips most rescales.  p.v accumulates in fp32.  At the end the
+// token groups of a wave fold with shuffles and the four waves through LDS;
+// the workgroup writes its normalised partial and (m, l).  No atomics.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace sa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+template <int HD, int G, bool BF>
+__global__ __launch_bounds__(64 * kWaves) void k_decode(DecodeArgs a)
+{
+    constexpr int CH = BF ? 8 : 4;  // channels per lane
+    constexpr int LPT = HD / CH;    // lanes per token
+    constexpr int TPW = 64 / LPT;   // tokens per wave load
+    constexpr int U = 4;            // loads of K and V in flight per lane
+    typedef typename std::conditional<BF, uint16_t, float>::type E;
+    const Geometry& g = a.g;
+
+    __shared__ float lds_o[kWaves][G][HD];
+    __shared__ float lds_ml[kWaves][G][2];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPT, tg = lane / LPT;
+
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int kvh = bid % g.Hkv;
+    bid /= g.Hkv;
+    const int row = bid % a.Q;
+    const int b = bid / a.Q;
+
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int pos = L - a.Q + row;
+    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
+    TokenSet ts;
+    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max);
+    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
+
+    // this workgroup's slice of the token set, then this wave's
+    const int n = ts.total;
+    const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
+    const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
+    const int len = f1 - f0;
+    const int w0 = f0 + wave * (len / kWaves) + imin(wave, len % kWaves);
+    const int w1 = w0 + len / kWaves + (wave < len % kWaves ? 1 : 0);
+
+    // the group's queries, this lane's channels
+    uint32_t qw[G][CH / 2];  // bf16 pairs
+    float qf[G][CH];         // fp32
+    for (int h = 0; h < G; ++h) {
+        const E* qp = (const E*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD + sub * CH;
+        const uint4 w = *(const uint4*)qp;
+        if constexpr (BF) {
+            qw[h][0] = w.x;
+            qw[h][1] = w.y;
+            qw[h][2] = w.z;
+            qw[h][3] = w.w;
+        } else {
+            qf[h][0] = __uint_as_float(w.x);
+            qf[h][1] = __uint_as_float(w.y);
+            qf[h][2] = __uint_as_float(w.z);
+            qf[h][3] = __uint_as_float(w.w);
+        }
+    }
+
+    float m[G], l[G], o[G][CH];
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+        for (int c = 0; c < CH; ++c) o[h][c] = 0.f;
+    }
+
+    const E* kbase = (const E*)g.k + (long)kvh * g.P * HD + sub * CH;
+    const E* vbase = (const E*)g.v + (long)kvh * g.P * HD + sub * CH;
+    const long page_stride = (long)g.Hkv * g.P * HD;
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
+
+    for (int base = w0; base < w1; base += TPW * U) {
+        uint4 kw[U], vw[U];
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = base + u * TPW + tg;
+            int t = f < w1 ? ts.position(f, pdiv) : -1;
+            if (t > pos) t = -1;
+            long off = 0;
+            if (t >= 0) {
+                const int pg = pdiv.div(t);
+                const int phys = bt[pg];
+                if (phys >= 0 && phys < g.num_phys)
+                    off = (long)phys * page_stride + (long)(t - pg * g.P) * HD;
+                else
+                    t = -1;
+            }
+            valid[u] = t >= 0;
+            kw[u] = valid[u] ? *(const uint4*)(kbase + off) : make_uint4(0, 0, 0, 0);
+            vw[u] = valid[u] ? *(const uint4*)(vbase + off) : make_uint4(0, 0, 0, 0);
+        }
+
+        float z[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t* k32 = (const uint32_t*)&kw[u];
+            for (int h = 0; h < G; ++h) {
+                float d = 0.f;
+                if constexpr (BF) {
+                    for (int j = 0; j < 4; ++j) d = dot2_bf16(qw[h][j], k32[j], d);
+                } else {
+                    for (int j = 0; j < 4; ++j) d = fmaf(qf[h][j], __uint_as_float(k32[j]), d);
+                }
+                d = group_sum<LPT>(d);
+                z[u][h] = valid[u] ? d * a.scale_log2 : -INFINITY;
+            }
+        }
+
+        for (int h = 0; h < G; ++h) {
+            float mx = z[0][h];
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[u][h]);
+            if (mx > m[h] + kRescaleSlack) {
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);  // 0 while m = -inf
+                l[h] *= alpha;
+                for (int c = 0; c < CH; ++c) o[h][c] *= alpha;
+                m[h] = mx;
+            }
+            const float mref = m[h] == -INFINITY ? 0.f : m[h];
+            for (int u = 0; u < U; ++u) z[u][h] = __builtin_amdgcn_exp2f(z[u][h] - mref);  // -inf -> 0
+        }
+
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t* v32 = (const uint32_t*)&vw[u];
+            float v[CH];
+            if constexpr (BF) {
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = bf_lo(v32[j]);
+                    v[2 * j + 1] = bf_hi(v32[j]);
+                }
+            } else {
+                for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(v32[j]);
+            }
+            for (int h = 0; h < G; ++h) {
+                const float p = z[u][h];
+                l[h] += p;
+                for (int c = 0; c < CH; ++c) o[h][c] = fmaf(p, v[c], o[h][c]);
+            }
+        }
+    }
+
+    // fold the token groups of the wave (lanes sub, sub + LPT, ...)
+    for (int off = LPT; off < 64; off <<= 1) {
+        for (int h = 0; h < G; ++h) {
+            const float m2 = __shfl_xor(m[h], off);
+            const float l2 = __shfl_xor(l[h], off);
+            const float mn = fmaxf(m[h], m2);
+            const float a1 = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+            const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+            l[h] = l[h] * a1 + l2 * a2;
+            for (int c = 0; c < CH; ++c) o[h][c] = o[h][c] * a1 + __shfl_xor(o[h][c], off) * a2;
+            m[h] = mn;
+        }
+    }
+    if (tg == 0) {
+        for (int h = 0; h < G; ++h) {
+            for (int c = 0; c < CH; ++c) lds_o[wave][h][sub * CH + c] = o[h][c];
+            if (sub == 0) {
+                lds_ml[wave][h][0] = m[h];
+                lds_ml[wave][h][1] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+
+    // fold the waves and write the partial
+    for (int i = threadIdx.x; i < G * HD; i += 64 * kWaves) {
+        const int h = i / HD, c = i % HD;
+        float ms = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, lds_ml[w][h][0]);
+        float ls = 0.f, os = 0.f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = lds_ml[w][h][0];
+            const float aw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
+            ls = fmaf(lds_ml[w][h][1], aw, ls);
+            os = fmaf(lds_o[w][h][c], aw, os);
+        }
+        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.splits + split;
+        a.part_o[prow * HD + c] = ls > 0.f ? os / ls : 0.f;
+        if (c == 0) {
+            a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
+            a.part_ml[prow * 2 + 1] = ls;
+        }
+    }
+}
+
+template <int HD, bool BF>
+hipError_t launch_g(const DecodeArgs& a, dim3 grid, hipStream_t s)
+{
+    const dim3 block(64 * kWaves);
+    switch (a.g.G) {
+    case 1: hipLaunchKernelGGL((k_decode<HD, 1, BF>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_decode<HD, 2, BF>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_decode<HD, 4, BF>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_decode<HD, 8, BF>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_decode<HD, 16, BF>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s)
+{
+    const long wgs = (long)a.g.B * a.g.Hkv * a.Q * a.splits;
+    const dim3 grid((unsigned)wgs);
+    const bool bf = a.g.dtype == 1;
+    if (a.g.hd == 128) return bf ? launch_g<128, true>(a, grid, s) : launch_g<128, false>(a, grid, s);
+    if (a.g.hd == 64) return bf ? launch_g<64, true>(a, grid, s) : launch_g<64, false>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sa

@@ -1,0 +1,153 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 unpacking, packed
+// bf16 dot products, DPP row reductions and the token map of an attended set.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- bf16 ---------------------------------------------------------------
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + a.lo*b.lo + a.hi*b.hi with bf16 inputs and an fp32 accumulator
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc,
+                                           false);
+}
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ---- cross-lane -----------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N = 2..64); every lane of a group
+// receives the group total.  Groups of up to 16 stay inside a DPP row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^1
+    if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^2
+    if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+    if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror: the other 8 of the row
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x)
+{
+    if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+    if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+    if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+    if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+    if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+// n / d for 0 <= n < 2^31 with a host-computed magic pair (Granlund and
+// Montgomery's round-up method): q = (umulhi(n, magic) + n) >> shift.
+struct FastDiv {
+    uint32_t d, magic, shift;
+    __device__ __forceinline__ int div(int n) const
+    {
+        uint32_t hi = __umulhi((uint32_t)n, magic);
+        return (int)((hi + (uint32_t)n) >> shift);
+    }
+};
+
+// ---- the attended token set of one (sequence, KV head, row) ---------------
+//
+// Tokens in ascending position: the sink [0, se), the middle-region part of
+// each selected page (pages ascending), then the window [ws, L).  Flat index
+// f in [0, total) maps to a position.  Only the first and the last selected
+// page can be cut by the region edges; interior candidates are whole pages.
+struct TokenSet {
+    int L, se, ws, P;
+    int nsel;         // selected pages in use; -1 means every middle page (dense)
+    int first_start;  // position of the first middle token of sel[0]
+    int len0;         // middle tokens of sel[0]
+    int mid_total;    // middle tokens attended
+    int total;
+    const int32_t* sel;
+
+    __device__ __forceinline__ void init(int L_, int S, int W, int P_, const int32_t* sel_, int count, int k_max)
+    {
+        L = L_;
+        P = P_;
+        se = imin(S, L);
+        ws = imax(se, L - W);
+        sel = sel_;
+        nsel = 0;
+        first_start = se;
+        len0 = 0;
+        mid_total = 0;
+        if (ws > se) {
+            if (sel_ == nullptr) {
+                nsel = -1;
+                mid_total = ws - se;
+            } else {
+                const int plo = se / P, phi = (ws - 1) / P;
+                nsel = imax(0, imin(count, imin(k_max, phi - plo + 1)));
+                if (nsel > 0) {
+                    const int p0 = sel_[0];
+                    first_start = imax(p0 * P, se);
+                    len0 = imax(0, imin((p0 + 1) * P, ws) - first_start);
+                    mid_total = len0;
+                    if (nsel > 1) {
+                        const int pl = sel_[nsel - 1];
+                        const int lenl = imax(0, imin((pl + 1) * P, ws) - pl * P);
+                        mid_total += (nsel - 2) * P + lenl;
+                    }
+                }
+            }
+        }
+        total = se + mid_total + (L - ws);
+    }
+
+    // Position of flat index f; -1 when the entry does not name a middle
+    // token (a bad selected page), so the caller skips it.
+    __device__ __forceinline__ int position(int f, const FastDiv& pdiv) const
+    {
+        if (f < se) return f;
+        f -= se;
+        if (f >= mid_total) return ws + (f - mid_total);
+        if (nsel < 0) return se + f;
+        int t;
+        if (f < len0) {
+            t = first_start + f;
+        } else {
+            f -= len0;
+            const int j = pdiv.div(f);
+            t = sel[1 + j] * P + (f - j * P);
+        }
+        return (t >= se && t < ws) ? t : -1;
+    }
+};
+
+}  // namespace sa

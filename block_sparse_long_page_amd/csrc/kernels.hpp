@@ -1,0 +1,79 @@
+// Internal launcher interface between the C ABI (host validation and
+// dispatch) and the gfx950 kernels.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct FastDivHost {
+    uint32_t d, magic, shift;
+};
+
+// magic pair for n / d with 0 <= n < 2^31, d >= 1
+inline FastDivHost make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    uint64_t magic = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return FastDivHost{d, (uint32_t)magic, s};
+}
+
+struct Geometry {
+    int B, Hq, Hkv, G, hd, P, max_pages, num_phys, dtype;
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    FastDivHost pdiv;
+};
+
+struct MetaArgs {
+    Geometry g;
+    int mode;
+    int page_begin, page_end;  // logical range (clipped per sequence in the kernel)
+    void* meta;
+};
+
+struct SelectArgs {
+    Geometry g;
+    const void* q;
+    int Q;
+    const void* meta;
+    int mode;
+    int S, W, k_max;
+    int32_t* sel;
+    int32_t* count;
+    float* scores;  // workspace [B][Hkv][Q][max_pages]
+};
+
+struct DecodeArgs {
+    Geometry g;
+    const void* q;
+    int Q;
+    const int32_t* sel;
+    const int32_t* count;
+    int k_max, S, W;
+    float scale_log2;  // softmax scale * log2(e)
+    int splits;
+    float* part_o;
+    float* part_ml;
+};
+
+struct CombineArgs {
+    int rows, hd, splits, out_dtype;
+    const float* part_o;
+    const float* part_ml;
+    void* out;
+    float* lse;
+};
+
+// Each returns hipSuccess or the launch error; 1 for an unsupported
+// template combination (the host layer checks these first).
+hipError_t launch_page_meta(const MetaArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace sa

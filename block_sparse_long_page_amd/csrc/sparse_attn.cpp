@@ -1,0 +1,178 @@
+// C ABI: host-side validation and dispatch to the gfx950 kernels.
+// Every check runs before any HIP call, so a rejected call queues nothing
+// and touches no device state.  With SPARSE_ATTN_SYNC=1 in the environment
+// every entry point synchronises its stream and reports asynchronous
+// failures as SA_ERR_HIP (a debugging aid; off by default).
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/sparse_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr int kMaxSelectPages = 16384;  // LDS holds one key per candidate page
+constexpr long kMaxGridY = 65535;
+
+bool sync_mode()
+{
+    static const int on = [] {
+        const char* e = getenv("SPARSE_ATTN_SYNC");
+        return e && e[0] == '1' ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+int finish(hipError_t launch, hipStream_t s)
+{
+    if (launch != hipSuccess) return SA_ERR_HIP;
+    if (sync_mode()) {
+        if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    }
+    return SA_OK;
+}
+
+bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Validates the cache descriptor; fills `g` on success.
+int check_kv(const sa_kv_desc* kv, sa::Geometry* g)
+{
+    if (!kv) return SA_ERR_INVALID_ARG;
+    if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->num_q_heads < 1 || kv->page_size < 1 ||
+        kv->max_pages_per_seq < 1 || kv->num_phys_pages < 1 || kv->max_seq_len < 1)
+        return SA_ERR_INVALID_ARG;
+    if (kv->num_q_heads % kv->num_kv_heads != 0) return SA_ERR_INVALID_ARG;
+    if (kv->page_size > 16384) return SA_ERR_UNSUPPORTED;
+    if ((long)kv->max_seq_len > (long)kv->max_pages_per_seq * kv->page_size) return SA_ERR_INVALID_ARG;
+    if ((long)kv->max_pages_per_seq * kv->page_size >= (1l << 30)) return SA_ERR_UNSUPPORTED;
+    if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_F32 && kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (kv->head_dim != 64 && kv->head_dim != 128) return SA_ERR_UNSUPPORTED;
+    const int G = kv->num_q_heads / kv->num_kv_heads;
+    if (!pow2_group(G)) return SA_ERR_UNSUPPORTED;
+    const sa::FastDivHost pd = sa::make_fastdiv((uint32_t)kv->page_size);
+    *g = sa::Geometry{kv->batch, kv->num_q_heads, kv->num_kv_heads, G, kv->head_dim, kv->page_size,
+                      kv->max_pages_per_seq, kv->num_phys_pages, kv->dtype, kv->k_cache, kv->v_cache,
+                      kv->block_table, kv->seq_lens, pd};
+    return SA_OK;
+}
+
+size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
+{
+    return sizeof(float) * (size_t)kv->batch * kv->num_kv_heads * rows * kv->max_pages_per_seq;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_attn_status_string(int status)
+{
+    switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+size_t sparse_attn_workspace_bytes(const sa_kv_desc* kv, int32_t num_q_rows)
+{
+    if (!kv || num_q_rows < 1 || kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1) return 0;
+    return select_ws_bytes(kv, num_q_rows);
+}
+
+int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_t page_begin, int32_t page_end,
+                                void* meta, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!meta || page_begin < 0 || page_end < page_begin) return SA_ERR_INVALID_ARG;
+    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    const int end = page_end < g.max_pages ? page_end : g.max_pages;
+    if (end <= page_begin) return SA_OK;
+    sa::MetaArgs a{g, score_mode, page_begin, end, meta};
+    return finish(sa::launch_page_meta(a, stream), stream);
+}
+
+int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                       int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                       int32_t* sel_pages, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    if (!q || !meta || !sel_count || num_q_rows < 1 || sink_len < 0 || window_len < 1 || token_budget < 0)
+        return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    const int k_max = token_budget / kv->page_size;
+    if (k_max > 0 && !sel_pages) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if (k_max > 0) {
+        if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
+        if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
+    }
+    sa::SelectArgs a{g, q, num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages, sel_count,
+                     (float*)workspace};
+    return finish(sa::launch_select(a, stream), stream);
+}
+
+int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,
+                                   int32_t k_max)
+{
+    if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || num_q_rows < 1 || kv->page_size < 1) return 1;
+    // attended tokens per (sequence, KV head, row), at most
+    const long L = kv->max_seq_len;
+    long ntok = (long)(sink_len < 0 ? 0 : sink_len) + (window_len < 1 ? 1 : window_len) +
+                (long)(k_max < 0 ? 0 : k_max) * kv->page_size;
+    if (ntok > L) ntok = L;
+    const long problems = (long)kv->batch * kv->num_kv_heads * num_q_rows;
+    // about 1024 workgroups (4 per CU on 256 CUs), at least 256 tokens each
+    long s = (1024 + problems - 1) / problems;
+    const long by_tokens = ntok / 256 > 0 ? ntok / 256 : 1;
+    if (s > by_tokens) s = by_tokens;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int32_t)s;
+}
+
+int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                       float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!q || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 || k_max < 0)
+        return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (sel_pages && !sel_count) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    const long wgs = (long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits;
+    if (wgs > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    sa::DecodeArgs a{g,         q,           num_q_rows, sel_pages, sel_count, sel_pages ? k_max : 0,
+                     sink_len,  window_len,  scale * 1.4426950408889634f, num_splits, part_o, part_ml};
+    return finish(sa::launch_decode(a, stream), stream);
+}
+
+int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
+                        const float* part_ml, void* out, int32_t out_dtype, float* lse, hipStream_t stream)
+{
+    if (!part_o || !part_ml || !out || num_rows < 1) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    sa::CombineArgs a{num_rows, head_dim, num_splits, out_dtype, part_o, part_ml, out, lse};
+    return finish(sa::launch_combine(a, stream), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+"""Device buffers and a step runner on top of the C ABI.
+
+PyTorch only provides device memory and the stream; every computation is a
+call into libsparse_attn.so.  `SparseDecoder.step` runs one decode step:
+select (scores + per-KV-head top-k) -> decode (split-K attention) -> combine.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .synth import Cache
+
+_TORCH_ELEM = {B.SA_F32: torch.float32, B.SA_BF16: torch.int16}
+
+
+def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclass
+class DeviceCache:
+    B: int
+    Hq: int
+    Hkv: int
+    hd: int
+    P: int
+    max_pages: int
+    num_phys: int
+    dtype: int
+    k: torch.Tensor
+    v: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    max_seq_len: int
+
+    @classmethod
+    def from_host(cls, c: Cache, device="cuda", max_seq_len: Optional[int] = None) -> "DeviceCache":
+        msl = int(max_seq_len if max_seq_len is not None else max(1, int(np.max(c.seq_lens))))
+        return cls(c.B, c.Hq, c.Hkv, c.hd, c.P, c.max_pages, c.num_phys, c.dtype, to_device(c.k, device),
+                   to_device(c.v, device), to_device(c.block_table.astype(np.int32), device),
+                   to_device(c.seq_lens.astype(np.int32), device), msl)
+
+    def desc(self, block_table: Optional[torch.Tensor] = None) -> B.sa_kv_desc:
+        return B.make_kv_desc(batch=self.B, num_q_heads=self.Hq, num_kv_heads=self.Hkv, head_dim=self.hd,
+                               page_size=self.P, max_pages_per_seq=self.max_pages, num_phys_pages=self.num_phys,
+                               max_seq_len=self.max_seq_len, dtype=self.dtype, k_cache=self.k, v_cache=self.v,
+                               block_table=self.block_table if block_table is None else block_table,
+                               seq_lens=self.seq_lens)
+
+    def meta_shape(self, mode: int):
+        return (self.num_phys, self.Hkv, 2, self.hd) if mode == B.SA_QUEST else (self.num_phys, self.Hkv, self.hd)
+
+    def new_meta(self, mode: int) -> torch.Tensor:
+        dt = _TORCH_ELEM[self.dtype] if mode == B.SA_QUEST else torch.float32
+        return torch.zeros(self.meta_shape(mode), dtype=dt, device=self.k.device)
+
+
+class SparseDecoder:
+    """Buffers and calls of one decode step for a fixed shape."""
+
+    def __init__(self, cache: DeviceCache, *, mode: int, Q: int, sink: int, window: int, budget: int,
+                 splits: Optional[int] = None, out_dtype: Optional[int] = None, meta: Optional[torch.Tensor] = None):
+        self.c = cache
+        self.mode, self.Q, self.sink, self.window, self.budget = mode, Q, sink, window, budget
+        self.k_max = budget // cache.P
+        self.desc = cache.desc()
+        dev = cache.k.device
+        self.meta = meta if meta is not None else cache.new_meta(mode)
+        self.sel = torch.full((cache.B, cache.Hkv, Q, max(1, self.k_max)), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((cache.B, cache.Hkv, Q), dtype=torch.int32, device=dev)
+        self.ws_bytes = B.sparse_attn_workspace_bytes(self.desc, Q)
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.splits = splits or B.sparse_attn_default_splits(self.desc, Q, sink, window, self.k_max)
+        rows = cache.B * cache.Hq * Q
+        self.rows = rows
+        self.part_o = torch.empty((rows, self.splits, cache.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((rows, self.splits, 2), dtype=torch.float32, device=dev)
+        self.out_dtype = cache.dtype if out_dtype is None else out_dtype
+        self.out = torch.empty((rows, cache.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
+        self.lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+    def build_meta(self, page_begin: int = 0, page_end: Optional[int] = None, stream=None):
+        B.sparse_attn_build_page_meta(self.desc, self.mode, page_begin,
+                                      self.c.max_pages if page_end is None else page_end, self.meta, stream)
+
+    def select(self, q: torch.Tensor, window: Optional[int] = None, stream=None):
+        B.sparse_attn_select(self.desc, q, self.Q, self.meta, self.mode, self.sink,
+                             self.window if window is None else window, self.budget, self.sel, self.count, self.ws,
+                             self.ws_bytes, stream)
+
+    def decode(self, q: torch.Tensor, window: Optional[int] = None, dense: bool = False, scale: float = 0.0,
+               stream=None):
+        B.sparse_attn_decode(self.desc, q, self.Q, None if dense else self.sel, None if dense else self.count,
+                             self.k_max, self.sink, self.window if window is None else window, scale, self.splits,
+                             self.part_o, self.part_ml, stream)
+
+    def combine(self, stream=None):
+        B.sparse_attn_combine(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
+                              self.out_dtype, self.lse, stream)
+
+    def step(self, q: torch.Tensor, stream=None):
+        self.select(q, stream=stream)
+        self.decode(q, stream=stream)
+        self.combine(stream=stream)
+        return self.out
+
+    # ---- host copies ------------------------------------------------------
+    def out_f32(self) -> np.ndarray:
+        o = self.out.cpu().numpy()
+        if self.out_dtype == B.SA_BF16:
+            o = (o.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        return o.reshape(self.c.B, self.c.Hq, self.Q, self.c.hd)
+
+    def lse_f32(self) -> np.ndarray:
+        return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)
+
+    def selection(self):
+        cnt = self.count.cpu().numpy()
+        sel = self.sel.cpu().numpy()[..., : self.k_max]
+        return sel, cnt

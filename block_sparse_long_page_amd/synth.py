@@ -19,6 +19,8 @@ Conventions
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
@@ -37,14 +39,18 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     out = np.empty(u.shape, dtype=np.uint16)
     flat_u = u.reshape(-1)
     flat_o = out.reshape(-1)
-    step = 1 << 24
+    step = 1 << 22
     for s in range(0, flat_u.size, step):
         c = flat_u[s:s + step]
-        r = (c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        r = c >> np.uint32(16)
+        r &= np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += c
+        r >>= np.uint32(16)
         nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
         if nan.any():
             r[nan] = (c[nan] >> np.uint32(16)) | np.uint32(0x40)
-        flat_o[s:s + step] = r.astype(np.uint16)
+        flat_o[s:s + step] = r
     return out
 
 
@@ -138,6 +144,39 @@ def sample_vmf(rng: np.random.Generator, mu: np.ndarray, kappa: float, n: int) -
     return w[:, None] * mu[None, :] + np.sqrt(np.maximum(0.0, 1.0 - w * w))[:, None] * g
 
 
+_CHUNK_PAGES = 64
+
+
+def _fill_pages(k: np.ndarray, v: np.ndarray, rng: np.random.Generator, dt: int, *, mu=None,
+                cluster_noise: float = 0.5, out_ch=None, outlier_scale: float = 8.0) -> None:
+    """Fill k and v ([num_phys][Hkv][P][hd]) chunk by chunk of physical pages.
+    Each chunk draws from its own child generator (spawned from `rng`), so the
+    result depends only on the seed, and chunks fill in parallel threads."""
+    num_phys, Hkv, P, hd = k.shape
+    starts = list(range(0, num_phys, _CHUNK_PAGES))
+    children = rng.spawn(len(starts))
+
+    def fill(i):
+        s = starts[i]
+        e = min(num_phys, s + _CHUNK_PAGES)
+        r = children[i]
+        if mu is not None:
+            ids = r.integers(0, mu.shape[1], size=(e - s, Hkv, P))
+            kk = _normal(r, (e - s, Hkv, P, hd))
+            kk *= np.float32(cluster_noise)
+            kk += mu[np.arange(Hkv)[None, :, None], ids]
+        else:
+            kk = _normal(r, (e - s, Hkv, P, hd))
+        if out_ch is not None:
+            kk[..., out_ch] *= np.float32(outlier_scale)
+        k[s:e] = store(kk, dt)
+        v[s:e] = store(_normal(r, (e - s, Hkv, P, hd)), dt)
+
+    workers = min(16, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(len(starts))))
+
+
 # ---------------------------------------------------------------------------
 # generic random problem
 # ---------------------------------------------------------------------------
@@ -182,18 +221,7 @@ def random_problem(
     v = np.empty_like(k)
     mu = _normal(rng, (Hkv, clusters, hd)) if clusters else None
     out_ch = rng.choice(hd, size=outlier_channels, replace=False) if outlier_channels else None
-    chunk = 256
-    for s in range(0, num_phys, chunk):
-        e = min(num_phys, s + chunk)
-        if clusters:
-            ids = rng.integers(0, clusters, size=(e - s, Hkv, P))
-            kk = mu[np.arange(Hkv)[None, :, None], ids] + np.float32(cluster_noise) * _normal(rng, (e - s, Hkv, P, hd))
-        else:
-            kk = _normal(rng, (e - s, Hkv, P, hd))
-        if out_ch is not None:
-            kk[..., out_ch] *= np.float32(outlier_scale)
-        k[s:e] = store(kk, dt)
-        v[s:e] = store(_normal(rng, (e - s, Hkv, P, hd)), dt)
+    _fill_pages(k, v, rng, dt, mu=mu, cluster_noise=cluster_noise, out_ch=out_ch, outlier_scale=outlier_scale)
 
     needles: List[Tuple[int, int, int]] = []
     G = Hq // Hkv

@@ -1,0 +1,217 @@
+/*
+ * sparse_attn.h -- C ABI of block/page-sparse long-context decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (hybrid sparse attention page: full-attention layers read a
+ * 256-token prefix, a sliding window and the pages Quest rates most relevant;
+ * semantic-blocks page: queries are compared with block centres and attend
+ * the chosen blocks; course module 14, sections 14.2-14.3: attention sink +
+ * window, block gating) runs as four calls on a caller-owned HIP stream:
+ *
+ *   sparse_attn_build_page_meta  page summaries (min/max, mean or centroid)
+ *   sparse_attn_select           score pages, per-KV-head top-k
+ *   sparse_attn_decode           exact softmax attention over sink, window and
+ *                                the selected pages, split over the token set
+ *   sparse_attn_combine          log-sum-exp merge of the split partials
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  The caller allocates and owns every device buffer and the
+ *   stream.  The library allocates nothing, frees nothing, keeps no mutable
+ *   global state and never synchronises; calls on different streams are
+ *   independent.  Work is queued on `stream` and is complete when the stream
+ *   is.  All pointers are device pointers unless stated otherwise.
+ * Errors.  Every argument is checked on the host before any HIP call; a bad
+ *   argument returns SA_ERR_INVALID_ARG or SA_ERR_UNSUPPORTED and queues
+ *   nothing.  SA_ERR_HIP reports a failed kernel launch.  No C++ exception
+ *   crosses the boundary.  Device-side contents (seq_lens, block_table,
+ *   selected pages) cannot be checked on the host: the kernels clamp
+ *   seq_lens[b] to [0, max_pages_per_seq*page_size], ignore block-table
+ *   entries outside [0, num_phys_pages) and selected pages outside the
+ *   candidate range, so bad contents give wrong numbers, never stray memory
+ *   accesses.
+ * Positions.  seq_lens[b] = L counts every token in the cache, the current
+ *   one(s) included.  With Q query rows, row i sits at position L - Q + i and
+ *   attends causally (positions <= its own).
+ * Regions (StreamingLLM sink + window, course module 14, section 14.2; window
+ *   of the w most recent positions, self-indexing attention page, "Sliding
+ *   window").  sink = [0, min(S, L)); window = [max(sink end, L - W), L)
+ *   (the current token is in the window, so W >= 1); middle = between them.
+ *   A page is a candidate when it holds at least one middle token.  The
+ *   attended set is sink + window + the middle tokens of the selected pages,
+ *   each token once.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SA_OK 0
+#define SA_ERR_INVALID_ARG 1  /* null pointer, bad size or range, workspace too small */
+#define SA_ERR_UNSUPPORTED 2  /* valid but not built: head_dim, GQA ratio, dtype, mode */
+#define SA_ERR_HIP 3          /* a kernel launch failed (hipGetLastError) */
+
+/* element types of K, V, q, Quest summaries and outputs */
+#define SA_F32 0
+#define SA_BF16 1
+
+/* page-summary / scoring modes */
+#define SA_QUEST 0    /* per-channel min and max; score = sum_c max(q_c*min_c, q_c*max_c) */
+#define SA_MEAN 1     /* mean key of the page (MoBA-style block key); score = q.mean */
+#define SA_CENTROID 2 /* unit-norm mean of unit-norm keys (semantic block centre); score = q.c */
+
+/*
+ * The paged KV cache (PagedAttention-style page management, attention-
+ * mechanisms article, "Basic math and real cost").
+ *
+ *   k_cache, v_cache  [num_phys_pages][num_kv_heads][page_size][head_dim]
+ *                     in `dtype`; one (page, KV head) slab is contiguous.
+ *   block_table       int32 [batch][max_pages_per_seq]: logical page ->
+ *                     physical page.  Entries past a sequence's last page
+ *                     are never read.
+ *   seq_lens          int32 [batch]: tokens in each sequence (see above).
+ *
+ * Limits: batch >= 1; num_kv_heads >= 1; num_q_heads = G * num_kv_heads with
+ * G (the GQA ratio) in {1, 2, 4, 8, 16}; head_dim in {64, 128};
+ * 1 <= page_size <= 16384; max_pages_per_seq >= 1; num_phys_pages >= 1;
+ * 1 <= max_seq_len <= max_pages_per_seq * page_size and max_seq_len < 2^30
+ * (host-side bound on every seq_lens[b], used for grid sizing).
+ */
+typedef struct sa_kv_desc {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_pages_per_seq;
+    int32_t num_phys_pages;
+    int32_t max_seq_len;
+    int32_t dtype; /* SA_F32 or SA_BF16 */
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+} sa_kv_desc;
+
+/*
+ * Page summaries (hybrid sparse attention page: Quest pages; course module
+ * 14, section 14.3: one key per block; semantic-blocks page: block centres
+ * from normalised keys).
+ *
+ * For every sequence b, KV head and logical page p in
+ * [page_begin, min(page_end, ceil(L_b / page_size))), summarises the page's
+ * valid tokens [p*P, min((p+1)*P, L_b)) into meta at its physical page:
+ *   SA_QUEST     meta [num_phys_pages][num_kv_heads][2][head_dim] in `dtype`:
+ *                [0] = per-channel min, [1] = per-channel max (exact).
+ *   SA_MEAN      meta [num_phys_pages][num_kv_heads][head_dim] fp32: mean key.
+ *   SA_CENTROID  same layout: u = sum_t k_t/|k_t| (zero keys skipped),
+ *                meta = u/|u| (zeros when u = 0).
+ * Sums run in fp32.  Pages outside the range are left untouched, so after a
+ * one-token append only the last page needs rebuilding.
+ * Errors: kv or meta null, page_begin < 0, page_end < page_begin, bad mode.
+ */
+int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_t page_begin, int32_t page_end,
+                                void* meta, hipStream_t stream);
+
+/*
+ * Page selection: scores, then a per-KV-head top-k (hybrid sparse attention
+ * page: Quest pages per head; attention-mechanisms article, "Learned top-k
+ * sparse attention": top-16 blocks per GQA group; semantic-blocks page:
+ * budget L/16).
+ *
+ *   q           [batch][num_q_heads][num_q_rows][head_dim] in `dtype`.
+ *   meta        summaries from sparse_attn_build_page_meta, same score_mode.
+ *   sink_len S >= 0, window_len W >= 1 (the window of the selecting step),
+ *   token_budget >= 0: k_max = token_budget / page_size pages per KV head.
+ *   sel_pages   int32 [batch][num_kv_heads][num_q_rows][k_max] (written only
+ *               when k_max > 0): the chosen logical pages in ascending order,
+ *               -1 after the last.
+ *   sel_count   int32 [batch][num_kv_heads][num_q_rows]: min(k_max, #candidates).
+ *   workspace   device scratch of at least sparse_attn_workspace_bytes() bytes.
+ *
+ * For every (b, KV head, row) and candidate page p, each of the G query heads
+ * of the group scores the page (SA_QUEST: the exact maximum of q.x over the
+ * page's per-channel bounding box, an upper bound on max_t q.k_t; SA_MEAN /
+ * SA_CENTROID: q.summary); the group score is the maximum over the G heads.
+ * Pages are ranked by (group score desc, page index asc) in fp32 and the
+ * first k kept.  When k_max >= #candidates every candidate is kept (the
+ * dense fallback at short context).
+ * Errors: null pointers (sel_pages may be null only when k_max == 0),
+ * num_q_rows < 1, S < 0, W < 1, token_budget < 0, workspace too small.
+ */
+int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                       int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                       int32_t* sel_pages, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of device workspace sparse_attn_select needs for this cache and row count. */
+size_t sparse_attn_workspace_bytes(const sa_kv_desc* kv, int32_t num_q_rows);
+
+/*
+ * Exact softmax attention over the attended set, split over its tokens
+ * (FlashAttention's block-by-block softmax with a running maximum and sum,
+ * attention-mechanisms article, "FlashAttention does not change what the
+ * model looks at"; course module 14, exercise 14.1: logits q.k/sqrt(d)).
+ *
+ *   q            [batch][num_q_heads][num_q_rows][head_dim] in `dtype`.
+ *   sel_pages    [batch][num_kv_heads][num_q_rows][k_max] as written by
+ *                sparse_attn_select (ascending candidate pages), with
+ *                sel_count [batch][num_kv_heads][num_q_rows]; or NULL for
+ *                dense attention (every middle page).
+ *   window_len   the effective window: after a refresh the caller passes
+ *                W + (steps since the selection), so tokens appended since
+ *                stay visible (hybrid sparse attention page: selection
+ *                refreshed every 32 steps while the window grows).
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
+ *   num_splits   1..1024 parts of each row's token set (see
+ *                sparse_attn_default_splits); each part is one workgroup.
+ *   part_o       fp32 [batch][num_q_heads][num_q_rows][num_splits][head_dim]:
+ *                the part's normalised output sum_t e^{z_t-m} v_t / l.
+ *   part_ml      fp32 [batch][num_q_heads][num_q_rows][num_splits][2]:
+ *                (m, l) with m = max logit z (natural units) of the part and
+ *                l = sum_t e^{z_t-m}.  An empty part writes (-inf, 0), o = 0.
+ * No float atomics; results are bitwise reproducible.
+ * Errors: null pointers (sel_count may be null only with sel_pages null),
+ * num_q_rows < 1, S < 0, W < 1, k_max < 0, num_splits out of range.
+ */
+int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                       float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, hipStream_t stream);
+
+/* A split count that fills the GPU for this shape (host arithmetic only). */
+int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,
+                                   int32_t k_max);
+
+/*
+ * Log-sum-exp merge of split partials (attention-mechanisms article,
+ * DeepSeek-V4 section: combining partial results; the same running-max
+ * rescaling as FlashAttention's online softmax).
+ *
+ * For each of num_rows rows: m* = max_s m_s over non-empty parts,
+ * l = sum_s e^{m_s-m*} l_s, out = sum_s e^{m_s-m*} l_s o_s / l,
+ * lse = m* + ln l, in a fixed order over s (deterministic).
+ *   part_o [num_rows][num_splits][head_dim], part_ml [num_rows][num_splits][2]
+ *   out    [num_rows][head_dim] in out_dtype (SA_BF16: round to nearest even)
+ *   lse    fp32 [num_rows] or NULL.
+ * A row whose parts are all empty gets out = 0 and lse = -inf.
+ * Errors: null pointers, num_rows < 1, head_dim not 64/128, num_splits
+ * outside 1..1024, bad out_dtype.
+ */
+int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
+                        const float* part_ml, void* out, int32_t out_dtype, float* lse, hipStream_t stream);
+
+/* A static string naming a status code. */
+const char* sparse_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,187 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects every bad argument with its status code before
+any HIP call (so these run without a GPU and queue nothing)."""
+import ctypes
+
+import pytest
+
+B = pytest.importorskip("block_sparse_long_page_amd.binding")
+
+DEV = 0x1000  # a fake device address: never dereferenced, every call below fails validation
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, max_pages_per_seq=8,
+                num_phys_pages=16, max_seq_len=128, dtype=B.SA_BF16, k_cache=DEV, v_cache=DEV,
+                block_table=DEV, seq_lens=DEV)
+    base.update(kw)
+    return B.make_kv_desc(**base)
+
+
+def test_exports_every_header_function():
+    names = B.header_symbols()
+    assert set(names) == {
+        "sparse_attn_build_page_meta", "sparse_attn_select", "sparse_attn_workspace_bytes", "sparse_attn_decode",
+        "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string"}
+    lib = B.library()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    assert B.sparse_attn_status_string(0) == "ok"
+    assert "invalid" in B.sparse_attn_status_string(1)
+    assert "unsupported" in B.sparse_attn_status_string(2)
+    assert "HIP" in B.sparse_attn_status_string(3)
+    assert B.sparse_attn_status_string(99) == "unknown status"
+
+
+BAD_DESCS = [
+    (dict(batch=0), B.SA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), B.SA_ERR_INVALID_ARG),
+    (dict(num_q_heads=7), B.SA_ERR_INVALID_ARG),  # not a multiple of the KV heads
+    (dict(num_q_heads=6), B.SA_ERR_UNSUPPORTED),  # GQA ratio 3
+    (dict(num_q_heads=64), B.SA_ERR_UNSUPPORTED),  # GQA ratio 32
+    (dict(head_dim=96), B.SA_ERR_UNSUPPORTED),
+    (dict(dtype=5), B.SA_ERR_UNSUPPORTED),
+    (dict(page_size=0), B.SA_ERR_INVALID_ARG),
+    (dict(page_size=32768, max_pages_per_seq=1, max_seq_len=1), B.SA_ERR_UNSUPPORTED),
+    (dict(max_seq_len=129), B.SA_ERR_INVALID_ARG),  # more than max_pages * page_size
+    (dict(max_seq_len=0), B.SA_ERR_INVALID_ARG),
+    (dict(num_phys_pages=0), B.SA_ERR_INVALID_ARG),
+    (dict(k_cache=None), B.SA_ERR_INVALID_ARG),
+    (dict(v_cache=None), B.SA_ERR_INVALID_ARG),
+    (dict(block_table=None), B.SA_ERR_INVALID_ARG),
+    (dict(seq_lens=None), B.SA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_DESCS)
+def test_descriptor_checks(bad, code):
+    lib = B.library()
+    d = _desc(**bad)
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 0, 8, DEV, None) == code
+    assert lib.sparse_attn_select(ctypes.byref(d), DEV, 1, DEV, 0, 16, 16, 32, DEV, DEV, DEV, 1 << 20, None) == code
+    assert lib.sparse_attn_decode(ctypes.byref(d), DEV, 1, DEV, DEV, 2, 16, 16, 0.0, 4, DEV, DEV, None) == code
+
+
+def test_null_descriptor():
+    lib = B.library()
+    assert lib.sparse_attn_build_page_meta(None, 0, 0, 1, DEV, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_select(None, DEV, 1, DEV, 0, 0, 1, 0, DEV, DEV, DEV, 0, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_decode(None, DEV, 1, None, None, 0, 0, 1, 0.0, 1, DEV, DEV, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_workspace_bytes(None, 1) == 0
+
+
+def test_page_meta_checks():
+    lib = B.library()
+    d = _desc()
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 0, 8, None, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, -1, 8, DEV, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 5, 4, DEV, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 3, 0, 8, DEV, None) == B.SA_ERR_UNSUPPORTED
+    # an empty range is a valid no-op that queues nothing
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 4, 4, DEV, None) == B.SA_OK
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 8, 100, DEV, None) == B.SA_OK
+
+
+def test_select_checks():
+    lib = B.library()
+    d = _desc()
+    ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
+    assert ws == 4 * 2 * 2 * 1 * 8
+
+    def sel(**kw):
+        a = dict(q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, sel=DEV, cnt=DEV, ws=DEV, wsb=ws)
+        a.update(kw)
+        return lib.sparse_attn_select(ctypes.byref(d), a["q"], a["rows"], a["meta"], a["mode"], a["S"], a["W"],
+                                      a["budget"], a["sel"], a["cnt"], a["ws"], a["wsb"], None)
+
+    assert sel(q=None) == B.SA_ERR_INVALID_ARG
+    assert sel(meta=None) == B.SA_ERR_INVALID_ARG
+    assert sel(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert sel(sel=None) == B.SA_ERR_INVALID_ARG  # k_max = 2 needs an output
+    assert sel(rows=0) == B.SA_ERR_INVALID_ARG
+    assert sel(rows=129) == B.SA_ERR_INVALID_ARG  # more rows than tokens
+    assert sel(S=-1) == B.SA_ERR_INVALID_ARG
+    assert sel(W=0) == B.SA_ERR_INVALID_ARG  # the current token must be attended
+    assert sel(budget=-1) == B.SA_ERR_INVALID_ARG
+    assert sel(ws=None) == B.SA_ERR_INVALID_ARG
+    assert sel(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert sel(mode=7) == B.SA_ERR_UNSUPPORTED
+
+
+def test_decode_checks():
+    lib = B.library()
+    d = _desc()
+
+    def dec(**kw):
+        a = dict(q=DEV, rows=1, sel=DEV, cnt=DEV, kmax=2, S=16, W=16, scale=0.0, splits=4, po=DEV, pml=DEV)
+        a.update(kw)
+        return lib.sparse_attn_decode(ctypes.byref(d), a["q"], a["rows"], a["sel"], a["cnt"], a["kmax"], a["S"],
+                                      a["W"], a["scale"], a["splits"], a["po"], a["pml"], None)
+
+    assert dec(q=None) == B.SA_ERR_INVALID_ARG
+    assert dec(po=None) == B.SA_ERR_INVALID_ARG
+    assert dec(pml=None) == B.SA_ERR_INVALID_ARG
+    assert dec(cnt=None) == B.SA_ERR_INVALID_ARG  # a page list needs its counts
+    assert dec(rows=0) == B.SA_ERR_INVALID_ARG
+    assert dec(S=-1) == B.SA_ERR_INVALID_ARG
+    assert dec(W=0) == B.SA_ERR_INVALID_ARG
+    assert dec(kmax=-1) == B.SA_ERR_INVALID_ARG
+    assert dec(splits=0) == B.SA_ERR_INVALID_ARG
+    assert dec(splits=1025) == B.SA_ERR_INVALID_ARG
+    assert dec(scale=float("nan")) == B.SA_ERR_INVALID_ARG
+    assert dec(scale=float("inf")) == B.SA_ERR_INVALID_ARG
+
+
+def test_combine_checks():
+    lib = B.library()
+
+    def comb(**kw):
+        a = dict(rows=4, hd=128, splits=2, po=DEV, pml=DEV, out=DEV, odt=1, lse=None)
+        a.update(kw)
+        return lib.sparse_attn_combine(a["rows"], a["hd"], a["splits"], a["po"], a["pml"], a["out"], a["odt"],
+                                       a["lse"], None)
+
+    assert comb(rows=0) == B.SA_ERR_INVALID_ARG
+    assert comb(po=None) == B.SA_ERR_INVALID_ARG
+    assert comb(pml=None) == B.SA_ERR_INVALID_ARG
+    assert comb(out=None) == B.SA_ERR_INVALID_ARG
+    assert comb(splits=0) == B.SA_ERR_INVALID_ARG
+    assert comb(splits=2000) == B.SA_ERR_INVALID_ARG
+    assert comb(hd=96) == B.SA_ERR_UNSUPPORTED
+    assert comb(odt=3) == B.SA_ERR_UNSUPPORTED
+
+
+def test_default_splits_fill_the_gpu():
+    lib = B.library()
+    # the headline layer: 4 sequences x 8 KV heads, 12544 attended tokens each
+    d = _desc(batch=4, num_q_heads=64, num_kv_heads=8, page_size=64, max_pages_per_seq=2048,
+              num_phys_pages=8192, max_seq_len=131072)
+    s = lib.sparse_attn_default_splits(ctypes.byref(d), 1, 256, 4096, 128)
+    assert 16 <= s <= 64
+    tiny = _desc(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, max_pages_per_seq=128, max_seq_len=2048)
+    assert lib.sparse_attn_default_splits(ctypes.byref(tiny), 1, 16, 64, 8) >= 1
+
+
+def _fastdiv(d):
+    """The host's magic pair for n / d (mirrors make_fastdiv)."""
+    s = 0
+    while (1 << s) < d:
+        s += 1
+    magic = ((1 << 32) * ((1 << s) - d)) // d + 1
+    return magic & 0xFFFFFFFF, s
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 5, 7, 16, 24, 32, 48, 64, 100, 2047, 2048, 4095, 16384])
+def test_fast_division_is_exact_below_2_31(d):
+    import numpy as np
+
+    magic, s = _fastdiv(d)
+    rng = np.random.default_rng(d)
+    n = np.concatenate([np.arange(0, 5000), rng.integers(0, 2**31, 20000), [2**31 - 1, 2**31 - 2]]).astype(np.uint64)
+    hi = (n * np.uint64(magic)) >> np.uint64(32)
+    q = ((hi + n) & np.uint64(0xFFFFFFFF)) >> np.uint64(s)
+    assert ((hi + n) < np.uint64(1 << 32)).all()
+    np.testing.assert_array_equal(q, n // np.uint64(d))
