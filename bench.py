@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only the warmup and the timed region (for profiler runs)")
     return ap.parse_args()
 
 
@@ -129,13 +131,14 @@ def main():
     dec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
                         splits=args.splits or None)
     descs = [pool.desc(block_table=t) for t in tables]
-    for d in descs:
-        B.sparse_attn_build_page_meta(d, pr.mode, 0, pool.max_pages, dec.meta)
+    metas = [dec.meta] + [pool.new_meta(pr.mode) for _ in range(R - 1)]  # summaries per replica
+    for d, m in zip(descs, metas):
+        B.sparse_attn_build_page_meta(d, pr.mode, 0, pool.max_pages, m)
     torch.cuda.synchronize()
 
     def step(r, ev=None):
         d = descs[r]
-        B.sparse_attn_select(d, q, 1, dec.meta, pr.mode, pr.sink, pr.window, pr.budget, dec.sel, dec.count,
+        B.sparse_attn_select(d, q, 1, metas[r], pr.mode, pr.sink, pr.window, pr.budget, dec.sel, dec.count,
                              dec.ws, dec.ws_bytes)
         if ev is not None:
             ev[0].record()
@@ -162,54 +165,55 @@ def main():
                                                ntok_total=sum(attended), splits=dec.splits,
                                                sel_entries=int(cnt.sum()))
 
-    # timed region: K steps, each with HIP events around its decode launch
+    # timed region: K steps back to back
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        step(i % R, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / K
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
-
-    # the same loop without the per-kernel events
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
         step(i % R)
     stop.record()
     torch.cuda.synchronize()
-    ms_noev = start.elapsed_time(stop) / K
+    ms = start.elapsed_time(stop) / K
 
-    # one replica (repeated reads may hit the last-level cache)
+    # the same K steps again with HIP events around each decode launch (on the
+    # stream the kernels run on): the decode kernel's average launch duration.
+    # An event record adds a few microseconds between kernels, so these steps
+    # are not the ones the step time is taken from.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
-    start.record()
     for i in range(K):
-        step(0)
-    stop.record()
+        step(i % R, evs[i])
     torch.cuda.synchronize()
-    ms_hot = start.elapsed_time(stop) / K
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
 
-    # dense decode of the same cache: every page, same kernels, no selection
-    ddec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pool.max_pages * c.P)
-    for i in range(2):
-        ddec.desc = descs[i % R]
-        ddec.decode(q, dense=True)
-        ddec.combine()
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.dense_steps):
-        ddec.desc = descs[i % R]
-        ddec.decode(q, dense=True)
-        ddec.combine()
-    stop.record()
-    torch.cuda.synchronize()
-    dense_ms = start.elapsed_time(stop) / args.dense_steps
+    ms_hot = dense_ms = float('nan')
+    if not args.only_timed:
+        # one replica (repeated reads may hit the last-level cache)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K):
+            step(0)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_hot = start.elapsed_time(stop) / K
+
+        # dense decode of the same cache: every page, same kernels, no selection
+        ddec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pool.max_pages * c.P)
+        for i in range(2):
+            ddec.desc = descs[i % R]
+            ddec.decode(q, dense=True)
+            ddec.combine()
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.dense_steps):
+            ddec.desc = descs[i % R]
+            ddec.decode(q, dense=True)
+            ddec.combine()
+        stop.record()
+        torch.cuda.synchronize()
+        dense_ms = start.elapsed_time(stop) / args.dense_steps
 
     gbps = sb.total / (ms * 1e-3) / 1e9
     dec_gbps = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
@@ -257,10 +261,9 @@ def main():
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "bytes_per_step": sb.as_dict(),
-        "us_per_step_no_events": round(ms_noev * 1e3, 2),
-        "us_per_step_one_replica": round(ms_hot * 1e3, 2),
-        "dense_us_per_step": round(dense_ms * 1e3, 2),
-        "speedup_vs_dense": round(dense_ms / ms, 2),
+        "us_per_step_one_replica": None if args.only_timed else round(ms_hot * 1e3, 2),
+        "dense_us_per_step": None if args.only_timed else round(dense_ms * 1e3, 2),
+        "speedup_vs_dense": None if args.only_timed else round(dense_ms / ms, 2),
     }
     print(json.dumps(rec), flush=True)
 

@@ -14,7 +14,8 @@ import re
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsparse_attn.so")
+# SPARSE_ATTN_LIB selects another build of the same library (development sweeps)
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(PKG, "libsparse_attn.so")
 HEADER = os.path.join(PKG, os.pardir, "include", "sparse_attn.h")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3

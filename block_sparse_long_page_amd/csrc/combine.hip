@@ -15,31 +15,40 @@ template <int HD, bool OUT_BF>
 __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
 {
     constexpr int CPL = HD / 64;  // channels per lane
+    constexpr int UNROLL = 8;     // split loads in flight
     __shared__ float wts[kMaxSplits];
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
     const float* ml = a.part_ml + (long)row * a.splits * 2;
 
     float mx = -INFINITY;
-    for (int s = lane; s < a.splits; s += 64)
-        if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
-    mx = group_max<64>(mx);
-    float tot = 0.f;
     for (int s = lane; s < a.splits; s += 64) {
-        const float l = ml[2 * s + 1];
-        const float w = l > 0.f ? expf(ml[2 * s] - mx) * l : 0.f;
-        wts[s] = w;
+        const float2 v = *(const float2*)(ml + 2 * s);
+        if (v.y > 0.f) mx = fmaxf(mx, v.x);
+    }
+    mx = group_max<64>(mx);
+    for (int s = lane; s < a.splits; s += 64) {
+        const float2 v = *(const float2*)(ml + 2 * s);
+        wts[s] = v.y > 0.f ? expf(v.x - mx) * v.y : 0.f;
     }
     __syncthreads();
-    for (int s = 0; s < a.splits; ++s) tot += wts[s];  // same order in every lane
 
-    float acc[CPL];
+    float tot = 0.f, acc[CPL];
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
     const float* po = a.part_o + (long)row * a.splits * HD + lane * CPL;
-    for (int s = 0; s < a.splits; ++s) {
-        const float w = wts[s];
-        if (w == 0.f) continue;
-        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, po[(long)s * HD + c], acc[c]);
+    for (int s0 = 0; s0 < a.splits; s0 += UNROLL) {
+        float v[UNROLL][CPL];
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) v[j][c] = s0 + j < a.splits ? po[(long)(s0 + j) * HD + c] : 0.f;
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) {
+            const float w = s0 + j < a.splits ? wts[s0 + j] : 0.f;
+            tot += w;  // the same order in every lane
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, v[j][c], acc[c]);
+        }
     }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
     if constexpr (OUT_BF && CPL == 1) {

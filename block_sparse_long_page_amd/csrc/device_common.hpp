@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sa {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -34,10 +36,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 
 // ---- cross-lane -----------------------------------------------------------
 
+// DPP move for controls whose every lane reads a valid source lane (quad
+// permutes, row mirrors and rotations, row broadcasts): no "old" value needed.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
 // Sum over aligned groups of N lanes (N = 2..64); every lane of a group
@@ -65,6 +69,140 @@ __device__ __forceinline__ float group_max(float x)
     if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
     if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
     return x;
+}
+
+// Exchange with the lane whose index differs in bit BIT (and, for BIT 3 and
+// 2, in the lower bits too: row_mirror / row_half_mirror are involutions that
+// stay inside a 16- or 8-lane group).
+template <int BIT>
+__device__ __forceinline__ float flip(float x)
+{
+    if constexpr (BIT == 3) return dpp<0x140>(x);  // row_mirror
+    else if constexpr (BIT == 2) return dpp<0x141>(x);  // row_half_mirror
+    else if constexpr (BIT == 1) return dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+    else return dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+}
+
+// Reduce-scatter of C partial sums over the lanes of a group (bits BIT..0):
+// at each bit the lane keeps the lower or upper half of its values (by that
+// lane bit) and adds the partner's copy of that half; once one value is
+// left the remaining bits all-reduce it.
+template <int C, int BIT>
+__device__ __forceinline__ void reduce_scatter(float* d, int lane)
+{
+    if constexpr (BIT >= 0) {
+        if constexpr (C > 1) {
+            constexpr int H = C / 2;
+            const bool up = (lane >> BIT) & 1;
+#pragma unroll
+            for (int i = 0; i < H; ++i) {
+                const float send = up ? d[i] : d[i + H];
+                const float keep = up ? d[i + H] : d[i];
+                d[i] = keep + flip<BIT>(send);
+            }
+            reduce_scatter<H, BIT - 1>(d, lane);
+        } else {
+            d[0] += flip<BIT>(d[0]);
+            reduce_scatter<1, BIT - 1>(d, lane);
+        }
+    }
+}
+
+template <int N>
+constexpr int log2c() { return N <= 1 ? 0 : 1 + log2c<N / 2>(); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Broadcast lane SRC of each group of N lanes (N = 16: DPP row_newbcast;
+// N = 8: a bpermute inside the 8-lane half).
+template <int N, int SRC>
+__device__ __forceinline__ float group_bcast(float x, int lane)
+{
+    if constexpr (N == 16)
+        return dpp<0x150 + SRC>(x);  // row_newbcast
+    else
+        return __shfl(x, (lane & ~(N - 1)) + SRC);
+}
+
+// The value held by lane ^ OFF (OFF = 8, 16 or 32), without LDS: a DPP row
+// rotation by 8 inside a 16-lane row, or the gfx950 permlane swaps, which
+// exchange 16-lane rows (odd with even) or 32-lane halves of a register.
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float x)
+{
+    static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane offset");
+    if constexpr (OFF == 8) {
+        return dpp<0x128>(x);  // row_ror:8
+    } else {
+        const uint32_t u = __float_as_uint(x);
+        const int lane = __lane_id();
+        if constexpr (OFF == 16) {
+            const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            return __uint_as_float((lane & 16) ? r[0] : r[1]);
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            return __uint_as_float((lane & 32) ? r[0] : r[1]);
+        }
+    }
+}
+
+// ---- wave-wide integer primitives (DPP inside 16-lane rows, readlane across rows) ----
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x)
+{
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
+}
+
+// the row shifts leave lanes whose source is outside the row at 0
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr0(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
+{
+    x = min(x, (uint32_t)dpp_i<0xB1>((int)x));
+    x = min(x, (uint32_t)dpp_i<0x4E>((int)x));
+    x = min(x, (uint32_t)dpp_i<0x141>((int)x));
+    x = min(x, (uint32_t)dpp_i<0x140>((int)x));
+    const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    x = max(x, (uint32_t)dpp_i<0xB1>((int)x));
+    x = max(x, (uint32_t)dpp_i<0x4E>((int)x));
+    x = max(x, (uint32_t)dpp_i<0x141>((int)x));
+    x = max(x, (uint32_t)dpp_i<0x140>((int)x));
+    const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: row shifts by 1, 2,
+// 4, 8 inside each 16-lane row, then the totals of the lower rows.
+__device__ __forceinline__ int wave_inclusive_scan(int x)
+{
+    x += dpp_shr0<0x111>(x);  // row_shr:1
+    x += dpp_shr0<0x112>(x);  // row_shr:2
+    x += dpp_shr0<0x114>(x);  // row_shr:4
+    x += dpp_shr0<0x118>(x);  // row_shr:8
+    const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31);
+    const int t2 = __builtin_amdgcn_readlane(x, 47);
+    const int lane = __lane_id();
+    return x + (lane < 16 ? 0 : lane < 32 ? t0 : lane < 48 ? t0 + t1 : t0 + t1 + t2);
 }
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
     }
     if (rg != 0) return;
 
-    const long slab_id = (long)phys * g.Hkv + kvh;
+    const long slab_id = ((long)b * g.Hkv + kvh) * g.max_pages + page;  // by logical page
     if constexpr (MODE == 0) {
         E* out = (E*)a.meta + slab_id * 2 * HD + sub * CH;
         if constexpr (BF) {

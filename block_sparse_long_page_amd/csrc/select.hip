@@ -8,9 +8,10 @@
 //    query heads of the group and keep the group maximum, fp32, in the
 //    workspace.  Selection reads megabytes of summaries per step, so it is
 //    spread over the whole GPU rather than run by one workgroup per problem.
-//  * k_topk: one workgroup per (sequence, KV head, row) radix-selects the k-th
-//    largest order key in LDS and writes the chosen pages in ascending order.
-//    Ties go to the lower page index.
+//  * k_topk: one workgroup per (sequence, KV head, row) keeps the order keys
+//    of the candidates in registers, radix-selects the k-th largest starting
+//    at the highest bit where the keys differ, and writes the chosen pages in
+//    ascending order.  Ties go to the lower page index.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -20,18 +21,15 @@ namespace sa {
 
 namespace {
 
+#ifndef SA_SCORE_U
+#define SA_SCORE_U 8
+#endif
 constexpr int kScoreWaves = 4;
-constexpr int kScoreU = 4;  // page rows in flight per lane
+constexpr int kScoreU = SA_SCORE_U;  // page rows per lane, all loaded at once
 
-// Quest bound for one channel pair: max(q*mn, q*mx) = q * (q >= 0 ? mx : mn),
-// taken per bf16 half with a bit-select on q's sign bits.
-__device__ __forceinline__ uint32_t quest_pick(uint32_t qw, uint32_t mn, uint32_t mx)
-{
-    // 0xffff in each half whose q is negative
-    const uint32_t neg = ((qw >> 15) & 1u) * 0xffffu | ((qw >> 31) & 1u) * 0xffff0000u;
-    return (mn & neg) | (mx & ~neg);
-}
-
+// Each wave scores RPW * U consecutive candidate pages with every summary load
+// issued up front (selection is latency-bound: one round trip per wave); the
+// workgroup stages the group's queries in LDS once.
 template <int HD, int G, bool BF, bool QUEST>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
 {
@@ -42,7 +40,15 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     constexpr int LPT = HD / CH;
     constexpr int RPW = 64 / LPT;
     constexpr int U = kScoreU;
-    constexpr int PAGES_PER_WG = RPW * U * kScoreWaves;
+    constexpr int PER_WAVE = RPW * U;
+    constexpr int PAGES_PER_WG = PER_WAVE * kScoreWaves;
+    // packed-bf16 Quest scores reduce-scatter the G head sums (LPT <= 16)
+    constexpr bool RS = QUEST && BF && LPT <= 16;
+    constexpr int HPL = RS && G > LPT ? G / LPT : 1;
+    constexpr int QB = BF ? 2 : 4;             // bytes per query element
+    constexpr int QV = HD * QB / 16;           // 16-byte vectors per query row
+    typedef typename std::conditional<BF, uint16_t, float>::type E;
+    __shared__ uint4 q_lds[G * QV];
     const Geometry& g = a.g;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, rg = lane / LPT;
@@ -53,77 +59,105 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     const int kvh = pid % g.Hkv;
     const int b = pid / g.Hkv;
 
-    int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
     const int se = imin(a.S, L), ws = imax(se, L - a.W);
     if (ws <= se) return;
     const int plo = se / g.P, phi = (ws - 1) / g.P;
-    const int first = plo + blockIdx.x * PAGES_PER_WG + wave * RPW * U;
+    const int wg_first = plo + blockIdx.x * PAGES_PER_WG;
+    if (wg_first > phi) return;
+
+    const long qrow0 = (((long)b * g.Hq + kvh * G) * a.Q + row) * HD;
+    for (int i = threadIdx.x; i < G * QV; i += 64 * kScoreWaves) {
+        const int h = i / QV, v = i % QV;
+        q_lds[i] = ((const uint4*)((const E*)a.q + qrow0 + (long)h * a.Q * HD))[v];
+    }
+    __syncthreads();
+    const int first = wg_first + wave * PER_WAVE;
     if (first > phi) return;
 
-    // this lane's channels of the G queries of the group
-    typedef typename std::conditional<BF, uint16_t, float>::type E;
-    const long qrow0 = (((long)b * g.Hq + kvh * G) * a.Q + row) * HD;
-    const long qstride = (long)a.Q * HD;
-    uint32_t qw[G][4];   // QUEST && BF: packed bf16 pairs
+    // every summary row of this wave's pages, and their block-table entries
+    const long meta_row = ((long)b * g.Hkv + kvh) * g.max_pages;
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
+    uint4 w0[U], w1[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int p = first + u * RPW + rg;
+        const bool in = p <= phi;
+        const int phys = in ? bt[p] : -1;
+        ok[u] = phys >= 0 && phys < g.num_phys;
+        if constexpr (QUEST) {
+            const E* m = (const E*)a.meta + (meta_row + p) * 2 * HD + sub * CH;
+            w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
+            w1[u] = in ? *(const uint4*)(m + HD) : make_uint4(0, 0, 0, 0);
+        } else {
+            const float* m = (const float*)a.meta + (meta_row + p) * HD + sub * CH;
+            w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // this lane's channels of the G queries
+    uint32_t qw[G][4];   // Quest + bf16: packed pairs
+    uint32_t neg[G][4];  // Quest + bf16: 0xffff in each half whose q is negative
     float qf[G][CH];     // otherwise: fp32 channels
     for (int h = 0; h < G; ++h) {
-        const E* qp = (const E*)a.q + qrow0 + h * qstride;
         if constexpr (QUEST && BF) {
-            const uint4 w = *(const uint4*)(qp + sub * CH);
+            const uint4 w = q_lds[h * QV + sub];
             qw[h][0] = w.x;
             qw[h][1] = w.y;
             qw[h][2] = w.z;
             qw[h][3] = w.w;
+            for (int j = 0; j < 4; ++j)
+                neg[h][j] = ((qw[h][j] >> 15) & 1u) * 0xffffu | ((qw[h][j] >> 31) & 1u) * 0xffff0000u;
         } else {
+            const E* qh = (const E*)&q_lds[h * QV];
             for (int c = 0; c < CH; ++c) {
                 if constexpr (BF)
-                    qf[h][c] = __uint_as_float((uint32_t)((const uint16_t*)qp)[sub * CH + c] << 16);
+                    qf[h][c] = __uint_as_float((uint32_t)((const uint16_t*)qh)[sub * CH + c] << 16);
                 else
-                    qf[h][c] = ((const float*)qp)[sub * CH + c];
+                    qf[h][c] = ((const float*)qh)[sub * CH + c];
             }
         }
     }
 
     float* out = a.scores + (((long)b * g.Hkv + kvh) * a.Q + row) * g.max_pages;
-    uint4 w0[U], w1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int p = first + u * RPW + rg;
-        int phys = p <= phi ? g.block_table[(long)b * g.max_pages + p] : -1;
-        const bool ok = phys >= 0 && phys < g.num_phys;
-        if constexpr (QUEST) {
-            const E* m = (const E*)a.meta + ((long)phys * g.Hkv + kvh) * 2 * HD + sub * CH;
-            w0[u] = ok ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
-            w1[u] = ok ? *(const uint4*)(m + HD) : make_uint4(0, 0, 0, 0);
-        } else {
-            const float* m = (const float*)a.meta + ((long)phys * g.Hkv + kvh) * HD + sub * CH;
-            w0[u] = ok ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = first + u * RPW + rg;
-        const int phys = p <= phi ? g.block_table[(long)b * g.max_pages + p] : -1;
-        const bool ok = phys >= 0 && phys < g.num_phys;
         const uint32_t* a0 = (const uint32_t*)&w0[u];
         const uint32_t* a1 = (const uint32_t*)&w1[u];
-        float best = -INFINITY;
-        for (int h = 0; h < G; ++h) {
-            float s = 0.f;
-            if constexpr (QUEST && BF) {
-                for (int j = 0; j < 4; ++j) s = dot2_bf16(qw[h][j], quest_pick(qw[h][j], a0[j], a1[j]), s);
-            } else if constexpr (QUEST) {
-                for (int c = 0; c < CH; ++c) {
-                    const float q = qf[h][c];
-                    s = fmaf(q, q >= 0.f ? __uint_as_float(a1[c]) : __uint_as_float(a0[c]), s);
-                }
-            } else {
-                for (int c = 0; c < CH; ++c) s = fmaf(qf[h][c], __uint_as_float(a0[c]), s);
+        float best;
+        if constexpr (RS) {
+            // max(q*mn, q*mx) = q * (q >= 0 ? mx : mn), picked per bf16 half by q's sign
+            float d[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s = dot2_bf16(qw[h][j], (a0[j] & neg[h][j]) | (a1[j] & ~neg[h][j]), s);
+                d[h] = s;
             }
-            s = group_sum<LPT>(s);
-            best = fmaxf(best, s);
+            reduce_scatter<G, log2c<LPT>() - 1>(d, lane);
+            best = d[0];
+#pragma unroll
+            for (int j = 1; j < HPL; ++j) best = fmaxf(best, d[j]);
+            best = group_max<LPT>(best);
+        } else {
+            best = -INFINITY;
+            for (int h = 0; h < G; ++h) {
+                float s = 0.f;
+                if constexpr (QUEST) {
+                    for (int c = 0; c < CH; ++c) {
+                        const float q = qf[h][c];
+                        s = fmaf(q, q >= 0.f ? __uint_as_float(a1[c]) : __uint_as_float(a0[c]), s);
+                    }
+                } else {
+                    for (int c = 0; c < CH; ++c) s = fmaf(qf[h][c], __uint_as_float(a0[c]), s);
+                }
+                best = fmaxf(best, group_sum<LPT>(s));
+            }
         }
-        if (sub == 0 && p <= phi) out[p] = ok ? best : -INFINITY;
+        if (sub == 0 && p <= phi) out[p] = ok[u] ? best : -INFINITY;
     }
 }
 
@@ -134,35 +168,37 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 512;
+constexpr int kTopkMaxRounds = 24;  // keys per thread: up to 12288 candidate pages
 
-// Inclusive sum over the workgroup; returns the total in *total.
-__device__ int block_inclusive_scan(int x, int* lds, int* total)
+// Number of lanes of this wave below the calling lane whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) lds[wave] = x;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-        const int v = lds[w];
-        before += w < wave ? v : 0;
-        all += v;
-    }
-    __syncthreads();
-    *total = all;
-    return x + before;
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// One workgroup per (sequence, KV head, row); the order keys of the n
+// candidates live in LDS (key i at index i), loops stay rolled so the kernel
+// fits the instruction cache.
+//  1. min and max of the keys give the bits every key shares;
+//  2. radix select, 8 bits at a time from the highest differing bit: an LDS
+//     histogram of the digit among the keys that match the prefix decided so
+//     far (the keys spread over the bins, so the integer LDS atomics rarely
+//     collide); every wave then scans the histogram itself and finds the digit
+//     where the count from the top reaches k;
+//  3. compaction in ascending page order: every key above the k-th, then the
+//     lowest pages among those equal to it.
+// Wave-level reductions and scans use DPP and readlane.
 __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
 {
-    extern __shared__ uint32_t keys[];  // [phi - plo + 1]
-    __shared__ int hist[256];
-    __shared__ int scan_tmp[kTopkThreads / 64];
-    __shared__ int pick[2];
+    constexpr int NW = kTopkThreads / 64;
+    constexpr int kPasses = 4;  // 32 key bits, 8 per pass
+    extern __shared__ uint32_t keys[];  // [n]
+    __shared__ int hist[kPasses][256];
+    __shared__ uint32_t mm[NW][2];
+    __shared__ int cnt_eq[NW][kTopkMaxRounds];
+    __shared__ int cnt_in[NW][kTopkMaxRounds];
+    __shared__ int gts[NW];
     const Geometry& g = a.g;
     int pid = blockIdx.x;
     const int row = pid % a.Q;
@@ -177,7 +213,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
     const int plo = se / g.P;
     const int n = ws > se ? (ws - 1) / g.P - plo + 1 : 0;
     const int k = imin(a.k_max, n);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) a.count[prob] = k;
     if (sel)
         for (int i = k + tid; i < a.k_max; i += kTopkThreads) sel[i] = -1;
@@ -186,83 +222,114 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
         for (int i = tid; i < n; i += kTopkThreads) sel[i] = plo + i;
         return;
     }
+    for (int i = tid; i < kPasses * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
+    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;  // <= kTopkMaxRounds (host-checked)
     const float* sc = a.scores + prob * g.max_pages + plo;
-    for (int i = tid; i < n; i += kTopkThreads) keys[i] = order_key(sc[i]);
-
-    // radix select of the k-th largest key, 8 bits at a time from the top
-    uint32_t prefix = 0, mask = 0;
-    int need = k;  // keys still to take among those matching `prefix`
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;  // kTopkThreads == 256 bins
-        __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t key = keys[i];
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // lane j owns digits 255-4j .. 252-4j; suffix counts from the top
-            int c[4], s = 0;
-            for (int d = 0; d < 4; ++d) {
-                c[d] = hist[255 - 4 * tid - d];
-                s += c[d];
-            }
-            int incl = s;
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (tid >= off) incl += y;
-            }
-            int above = incl - s;  // keys with a larger digit than this lane's first
-            for (int d = 0; d < 4; ++d) {
-                if (above < need && above + c[d] >= need) {
-                    pick[0] = 255 - 4 * tid - d;
-                    pick[1] = above;
-                }
-                above += c[d];
-            }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)pick[0] << shift;
-        mask |= 255u << shift;
-        need -= pick[1];
-        __syncthreads();
+    uint32_t lo = 0xffffffffu, hi = 0;
+    for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t key = order_key(sc[i]);
+        keys[i] = key;
+        lo = min(lo, key);
+        hi = max(hi, key);
     }
-    const uint32_t kth = prefix;  // keys > kth are in; `need` of the keys == kth, lowest pages first
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        mm[wave][0] = lo;
+        mm[wave][1] = hi;
+    }
+    __syncthreads();
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, mm[w][0]);
+        hi = max(hi, mm[w][1]);
+    }
 
-    // ranks among equal keys and output slots, both in ascending page order
-    constexpr int PER = 32;  // pages per thread per pass
-    int eq_base = 0, out_base = 0;
-    for (int base = 0; base < n; base += kTopkThreads * PER) {
-        const int i0 = base + tid * PER;
-        int eq = 0, gt = 0;
-        for (int j = 0; j < PER; ++j) {
-            const int i = i0 + j;
-            if (i < n) {
-                eq += keys[i] == kth;
-                gt += keys[i] > kth;
-            }
-        }
-        int eq_total;
-        const int eq_before = block_inclusive_scan(eq, scan_tmp, &eq_total) - eq + eq_base;
-        // a thread takes min(eq, max(0, need - eq_before)) of its equal keys
-        const int take_eq = imin(eq, imax(0, need - eq_before));
-        int out_total;
-        const int out_before = block_inclusive_scan(gt + take_eq, scan_tmp, &out_total) - (gt + take_eq) + out_base;
-        int slot = out_before, taken = 0;
-        for (int j = 0; j < PER; ++j) {
-            const int i = i0 + j;
-            if (i < n) {
+    uint32_t kth = hi;  // the k-th largest key
+    if (lo != hi) {
+        int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+        uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+        int need = k;  // keys still to take among those matching the prefix
+        for (int pass = 0; top >= 0; ++pass) {
+            const int width = top + 1 < 8 ? top + 1 : 8;
+            const int shift = top + 1 - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            const int up = shift + width;  // bits >= up are decided
+            const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
+            for (int i = tid; i < n; i += kTopkThreads) {
                 const uint32_t key = keys[i];
-                bool in = key > kth;
-                if (key == kth && taken < take_eq) {
-                    in = true;
-                    ++taken;
-                }
-                if (in) sel[slot++] = plo + i;
+                if ((key & hmask) == prefix) atomicAdd(&hist[pass][(key >> shift) & dmask], 1);
             }
+            __syncthreads();
+            // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+            const int4 c = *(const int4*)&hist[pass][252 - 4 * lane];  // digits 252-4j .. 255-4j
+            const int s = c.x + c.y + c.z + c.w;
+            const int above = wave_inclusive_scan(s) - s;  // keys with a larger digit than this lane's
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(above < need && above + s >= need);
+            const int hl = (int)__builtin_ctzll(hit);
+            int acc = __builtin_amdgcn_readlane(above, hl);
+            const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+            const int cy = __builtin_amdgcn_readlane(c.y, hl);
+            int digit;
+            if (acc + cw >= need) {
+                digit = 255 - 4 * hl;
+            } else if (acc + cw + cz >= need) {
+                digit = 254 - 4 * hl;
+                acc += cw;
+            } else if (acc + cw + cz + cy >= need) {
+                digit = 253 - 4 * hl;
+                acc += cw + cz;
+            } else {
+                digit = 252 - 4 * hl;
+                acc += cw + cz + cy;
+            }
+            prefix |= (uint32_t)digit << shift;
+            need -= acc;
+            top = shift - 1;
         }
-        eq_base += eq_total;
-        out_base += out_total;
+        kth = prefix;
+    }
+
+    // per-wave counts of keys equal to kth and above it, round by round
+    int gt_local = 0;
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const int ne = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key == kth));
+        gt_local += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key > kth));
+        if (lane == 0) cnt_eq[wave][r] = ne;
+    }
+    if (lane == 0) gts[wave] = gt_local;
+    __syncthreads();
+    int gt = 0;
+    for (int w = 0; w < NW; ++w) gt += gts[w];
+    const int need = k - gt;  // equal keys to take, lowest pages first
+
+    // chosen: above kth, or equal to it and among the first `need` equal keys
+    // in page order (round, wave, lane)
+    int eq_base = 0;
+    uint32_t mine = 0;  // bit r: this thread's key of round r is chosen
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const bool eq = i < n && key == kth;
+        int rank = eq_base;
+        for (int w = 0; w < wave; ++w) rank += cnt_eq[w][r];
+        const bool in = i < n && (key > kth || (eq && rank + lanes_below(__builtin_amdgcn_ballot_w64(eq)) < need));
+        const int cc = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
+        if (lane == 0) cnt_in[wave][r] = cc;
+        for (int w = 0; w < NW; ++w) eq_base += cnt_eq[w][r];
+        mine |= (uint32_t)in << r;
+    }
+    __syncthreads();
+    int out_base = 0;
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const bool in = (mine >> r) & 1u;
+        const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
+        int here = out_base;
+        for (int w = 0; w < wave; ++w) here += cnt_in[w][r];
+        if (in) sel[here + lanes_below(inm)] = plo + i;
+        for (int w = 0; w < NW; ++w) out_base += cnt_in[w][r];
     }
 }
 
@@ -311,7 +378,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s)
             return hipErrorInvalidValue;
         if (e != hipSuccess) return e;
     }
-    const size_t lds = sizeof(uint32_t) * (size_t)(a.k_max > 0 ? g.max_pages : 1);
+    const size_t lds = sizeof(uint32_t) * (size_t)(a.k_max > 0 ? g.max_pages : 1);  // <= 48 KiB (host-checked)
     hipLaunchKernelGGL(k_topk, dim3((unsigned)problems), dim3(kTopkThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -13,7 +13,7 @@
 namespace {
 
 constexpr int kMaxSplits = 1024;
-constexpr int kMaxSelectPages = 16384;  // LDS holds one key per candidate page
+constexpr int kMaxSelectPages = 12288;  // the top-k workgroup holds one key per page in LDS
 constexpr long kMaxGridY = 65535;
 
 bool sync_mode()

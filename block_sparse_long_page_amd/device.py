@@ -56,7 +56,9 @@ class DeviceCache:
                                seq_lens=self.seq_lens)
 
     def meta_shape(self, mode: int):
-        return (self.num_phys, self.Hkv, 2, self.hd) if mode == B.SA_QUEST else (self.num_phys, self.Hkv, self.hd)
+        if mode == B.SA_QUEST:
+            return (self.B, self.Hkv, self.max_pages, 2, self.hd)
+        return (self.B, self.Hkv, self.max_pages, self.hd)
 
     def new_meta(self, mode: int) -> torch.Tensor:
         dt = _TORCH_ELEM[self.dtype] if mode == B.SA_QUEST else torch.float32

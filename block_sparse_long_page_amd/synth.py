@@ -33,24 +33,32 @@ from .configs import BF16, DTYPE_NAMES, F32, MODE_NAMES, Workload
 # bf16 bit patterns
 # ---------------------------------------------------------------------------
 
+def _round_chunk(c: np.ndarray, o: np.ndarray) -> None:
+    r = c >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += c
+    r >>= np.uint32(16)
+    nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        r[nan] = (c[nan] >> np.uint32(16)) | np.uint32(0x40)
+    o[:] = r
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     out = np.empty(u.shape, dtype=np.uint16)
     flat_u = u.reshape(-1)
     flat_o = out.reshape(-1)
-    step = 1 << 22
-    for s in range(0, flat_u.size, step):
-        c = flat_u[s:s + step]
-        r = c >> np.uint32(16)
-        r &= np.uint32(1)
-        r += np.uint32(0x7FFF)
-        r += c
-        r >>= np.uint32(16)
-        nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
-        if nan.any():
-            r[nan] = (c[nan] >> np.uint32(16)) | np.uint32(0x40)
-        flat_o[s:s + step] = r
+    step = 1 << 20
+    spans = [(s, min(flat_u.size, s + step)) for s in range(0, flat_u.size, step)]
+    if len(spans) <= 1:
+        for s, e in spans:
+            _round_chunk(flat_u[s:e], flat_o[s:e])
+    else:
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda se: _round_chunk(flat_u[se[0]:se[1]], flat_o[se[0]:se[1]]), spans))
     return out
 
 
@@ -118,11 +126,14 @@ def _unit(rng: np.random.Generator, n: int, d: int) -> np.ndarray:
 
 
 def sample_vmf(rng: np.random.Generator, mu: np.ndarray, kappa: float, n: int) -> np.ndarray:
-    """n unit vectors from the von Mises-Fisher law with mean direction mu and
-    concentration kappa, by Wood's (1994) rejection sampler for the cosine w
-    and a uniform direction in the tangent space of mu."""
+    """n unit vectors from the von Mises-Fisher law with concentration kappa
+    and mean direction mu ([d], or one row per sample [n][d]), by Wood's
+    (1994) rejection sampler for the cosine w and a uniform direction in the
+    tangent space of the mean."""
     mu = np.asarray(mu, dtype=np.float64)
-    d = mu.size
+    d = mu.shape[-1]
+    mus = np.broadcast_to(mu, (n, d)) if mu.ndim == 1 else mu
+    assert mus.shape == (n, d)
     m1 = d - 1.0
     b = (-2.0 * kappa + np.sqrt(4.0 * kappa * kappa + m1 * m1)) / m1
     x0 = (1.0 - b) / (1.0 + b)
@@ -139,9 +150,9 @@ def sample_vmf(rng: np.random.Generator, mu: np.ndarray, kappa: float, n: int) -
         w[filled:filled + got.size] = got
         filled += got.size
     g = rng.standard_normal((n, d))
-    g -= np.outer(g @ mu, mu)
+    g -= np.einsum("nd,nd->n", g, mus)[:, None] * mus
     g /= np.linalg.norm(g, axis=1, keepdims=True)
-    return w[:, None] * mu[None, :] + np.sqrt(np.maximum(0.0, 1.0 - w * w))[:, None] * g
+    return w[:, None] * mus + np.sqrt(np.maximum(0.0, 1.0 - w * w))[:, None] * g
 
 
 _CHUNK_PAGES = 64
@@ -152,7 +163,7 @@ def _fill_pages(k: np.ndarray, v: np.ndarray, rng: np.random.Generator, dt: int,
     """Fill k and v ([num_phys][Hkv][P][hd]) chunk by chunk of physical pages.
     Each chunk draws from its own child generator (spawned from `rng`), so the
     result depends only on the seed, and chunks fill in parallel threads."""
-    num_phys, Hkv, P, hd = k.shape
+    num_phys, Hkv, P, hd = v.shape
     starts = list(range(0, num_phys, _CHUNK_PAGES))
     children = rng.spawn(len(starts))
 
@@ -160,7 +171,9 @@ def _fill_pages(k: np.ndarray, v: np.ndarray, rng: np.random.Generator, dt: int,
         s = starts[i]
         e = min(num_phys, s + _CHUNK_PAGES)
         r = children[i]
-        if mu is not None:
+        if k is None:
+            pass
+        elif mu is not None:
             ids = r.integers(0, mu.shape[1], size=(e - s, Hkv, P))
             kk = _normal(r, (e - s, Hkv, P, hd))
             kk *= np.float32(cluster_noise)
@@ -169,7 +182,8 @@ def _fill_pages(k: np.ndarray, v: np.ndarray, rng: np.random.Generator, dt: int,
             kk = _normal(r, (e - s, Hkv, P, hd))
         if out_ch is not None:
             kk[..., out_ch] *= np.float32(outlier_scale)
-        k[s:e] = store(kk, dt)
+        if k is not None:
+            k[s:e] = store(kk, dt)
         v[s:e] = store(_normal(r, (e - s, Hkv, P, hd)), dt)
 
     workers = min(16, os.cpu_count() or 1)
@@ -294,25 +308,31 @@ def semantic_problem(wl: Workload, *, seed: Optional[int] = None, batch: Optiona
     v = np.empty_like(k)
     q = np.empty((B, Hq, Q, hd), dtype=np.uint16)
     G = Hq // Hkv
-    scale = np.sqrt(hd)
-    for b in range(B):
-        for kvh in range(Hkv):
-            mus = _unit(rng, blocks, hd)
-            for j in range(blocks):
-                kk = scale * sample_vmf(rng, mus[j], kappa, block_tokens)
-                k[bt[b, j], kvh] = store(kk.astype(np.float32), dt)
-            topic = rng.choice(blocks, size=topics, replace=False)
-            row_topic = topic[rng.integers(0, topics, size=Q)]
-            ck = np.zeros((P, hd), dtype=np.float32)
-            for i in range(Q):
-                ck[i] = scale * sample_vmf(rng, mus[row_topic[i]], kappa, 1)[0]
-            k[bt[b, blocks], kvh] = store(ck, dt)
-            for g in range(G):
-                for i in range(Q):
-                    q[b, kvh * G + g, i] = store((scale * sample_vmf(rng, mus[row_topic[i]], q_kappa, 1)[0]).astype(np.float32), dt)
-    for s in range(0, num_phys, 64):
-        e = min(num_phys, s + 64)
-        v[s:e] = store(_normal(rng, (e - s, Hkv, P, hd)), dt)
+    scale = np.float32(np.sqrt(hd))
+    per = 32  # clusters drawn per batch
+    children = rng.spawn(B * Hkv + 1)
+
+    def head(i):
+        b, kvh = divmod(i, Hkv)
+        r = children[i]
+        mus = _unit(r, blocks, hd)
+        for j0 in range(0, blocks, per):
+            j1 = min(blocks, j0 + per)
+            u = sample_vmf(r, np.repeat(mus[j0:j1], block_tokens, axis=0), kappa, (j1 - j0) * block_tokens)
+            kk = store(u.astype(np.float32).reshape(j1 - j0, block_tokens, hd) * scale, dt)
+            for j in range(j0, j1):
+                k[bt[b, j], kvh] = kk[j - j0]
+        topic = r.choice(blocks, size=topics, replace=False)
+        row_topic = topic[r.integers(0, topics, size=Q)]
+        ck = np.zeros((P, hd), dtype=np.float32)
+        ck[:Q] = sample_vmf(r, mus[row_topic], kappa, Q).astype(np.float32) * scale
+        k[bt[b, blocks], kvh] = store(ck, dt)
+        qq = sample_vmf(r, np.tile(mus[row_topic], (G, 1)), q_kappa, G * Q).astype(np.float32) * scale
+        q[b, kvh * G:(kvh + 1) * G] = store(qq.reshape(G, Q, hd), dt)
+
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(head, range(B * Hkv)))
+    _fill_pages(None, v, children[-1], dt)
     cache = Cache(B=B, Hq=Hq, Hkv=Hkv, hd=hd, P=P, max_pages=max_pages, num_phys=num_phys, dtype=dt,
                   k=k, v=v, block_table=bt, seq_lens=np.full(B, L, dtype=np.int32))
     return Problem(cache=cache, q=q, Q=Q, sink=wl.sink, window=wl.window, budget=wl.budget,

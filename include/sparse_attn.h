@@ -106,15 +106,20 @@ typedef struct sa_kv_desc {
  * from normalised keys).
  *
  * For every sequence b, KV head and logical page p in
- * [page_begin, min(page_end, ceil(L_b / page_size))), summarises the page's
- * valid tokens [p*P, min((p+1)*P, L_b)) into meta at its physical page:
- *   SA_QUEST     meta [num_phys_pages][num_kv_heads][2][head_dim] in `dtype`:
- *                [0] = per-channel min, [1] = per-channel max (exact).
- *   SA_MEAN      meta [num_phys_pages][num_kv_heads][head_dim] fp32: mean key.
+ * [page_begin, min(page_end, ceil(L_b / page_size))) whose block-table entry
+ * is a valid physical page, summarises the page's valid tokens
+ * [p*P, min((p+1)*P, L_b)) into meta at (b, KV head, p):
+ *   SA_QUEST     meta [batch][num_kv_heads][max_pages_per_seq][2][head_dim]
+ *                in `dtype`: [0] = per-channel min, [1] = per-channel max
+ *                (exact).
+ *   SA_MEAN      meta [batch][num_kv_heads][max_pages_per_seq][head_dim]
+ *                fp32: mean key.
  *   SA_CENTROID  same layout: u = sum_t k_t/|k_t| (zero keys skipped),
  *                meta = u/|u| (zeros when u = 0).
- * Sums run in fp32.  Pages outside the range are left untouched, so after a
- * one-token append only the last page needs rebuilding.
+ * Summaries are indexed by logical page, so selection streams one
+ * contiguous run per (sequence, KV head) without going through the block
+ * table.  Sums run in fp32.  Pages outside the range are left untouched, so
+ * after a one-token append only the last page needs rebuilding.
  * Errors: kv or meta null, page_begin < 0, page_end < page_begin, bad mode.
  */
 int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_t page_begin, int32_t page_end,
