@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--local-splits", type=int, default=0, help="splits of the sink+window decode")
+    ap.add_argument("--middle-splits", type=int, default=0, help="splits of the selected-pages decode")
+    ap.add_argument("--overlap", action="store_true",
+                    help="decode sink + window on a second stream beside the selection, then the selected pages")
     ap.add_argument("--dense-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -103,7 +107,7 @@ def main():
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth
-    from block_sparse_long_page_amd.device import DeviceCache, SparseDecoder, to_device
+    from block_sparse_long_page_amd.device import DeviceCache, OverlappedStep, SparseDecoder, to_device
 
     wl = configs.LLAMA3_70B
     t0 = time.time()
@@ -136,18 +140,25 @@ def main():
         B.sparse_attn_build_page_meta(d, pr.mode, 0, pool.max_pages, m)
     torch.cuda.synchronize()
 
-    def step(r, ev=None):
+    ov = OverlappedStep(dec, local_splits=args.local_splits or None, middle_splits=args.middle_splits or None)
+
+    def step_sequential(r, ev=None):
         d = descs[r]
         B.sparse_attn_select(d, q, 1, metas[r], pr.mode, pr.sink, pr.window, pr.budget, dec.sel, dec.count,
                              dec.ws, dec.ws_bytes)
         if ev is not None:
             ev[0].record()
-        B.sparse_attn_decode(d, q, 1, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, 0.0, dec.splits,
-                             dec.part_o, dec.part_ml)
+        B.sparse_attn_decode(d, q, 1, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, B.SA_PART_ALL, 0.0,
+                             dec.splits, 0, dec.part_o, dec.part_ml)
         if ev is not None:
             ev[1].record()
         B.sparse_attn_combine(dec.rows, c.hd, dec.splits, dec.part_o, dec.part_ml, dec.out, dec.out_dtype,
                               dec.lse)
+
+    def step_overlapped(r, ev=None):
+        ov.step(q, desc=descs[r], meta=metas[r], middle_events=ev)
+
+    step = step_sequential if not args.overlap else step_overlapped
 
     for i in range(args.warmup):
         step(i % R)
@@ -161,8 +172,15 @@ def main():
     sb = accounting.decode_step_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2, L=L, P=c.P, S=pr.sink,
                                       W=pr.window, budget=pr.budget, mode=pr.mode, splits=dec.splits,
                                       attended=attended)
+    if not args.overlap:
+        # one launch over sink + window + selected pages
+        dec_kernel, dec_tok, dec_splits = "k_decode (sink+window+selected)", sum(attended), dec.splits
+    else:
+        # the timed launch is the selected pages' decode; sink + window run beside the selection
+        local = accounting.attended_tokens_exact(L, c.P, pr.sink, pr.window, [])
+        dec_kernel, dec_tok, dec_splits = "k_decode (selected pages)", sum(attended) - local * c.B * c.Hkv, ov.sm
     dec_bytes = accounting.decode_kernel_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
-                                               ntok_total=sum(attended), splits=dec.splits,
+                                               ntok_total=dec_tok, splits=dec_splits,
                                                sel_entries=int(cnt.sum()))
 
     # timed region: K steps back to back
@@ -254,8 +272,10 @@ def main():
         "data": "synthetic (seeded): K from 64 Gaussian clusters, V and q N(0,1)",
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "context": L, "page": c.P, "sink": pr.sink, "window": pr.window, "budget": pr.budget,
-                   "score": "quest", "splits": dec.splits, "replicas": R},
-        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                   "score": "quest", "replicas": R,
+                   "splits": dec.splits if not args.overlap else {"sink_window": ov.sl, "selected": ov.sm},
+                   "streams": 1 if not args.overlap else 2},
+        "roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_record(), "bytes_per_launch": dec_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},

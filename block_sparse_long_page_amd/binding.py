@@ -21,6 +21,7 @@ HEADER = os.path.join(PKG, os.pardir, "include", "sparse_attn.h")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
 SA_F32, SA_BF16 = 0, 1
 SA_QUEST, SA_MEAN, SA_CENTROID = 0, 1, 2
+SA_PART_LOCAL, SA_PART_MIDDLE, SA_PART_ALL = 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
@@ -53,7 +54,7 @@ _SIGS = {
     "sparse_attn_build_page_meta": (ctypes.c_int, [_DESC, _I, _I, _I, _P, _P]),
     "sparse_attn_select": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_workspace_bytes": (ctypes.c_size_t, [_DESC, _I]),
-    "sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P]),
+    "sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P, _P]),
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -126,11 +127,11 @@ def sparse_attn_default_splits(kv: sa_kv_desc, num_q_rows: int, sink_len: int, w
 
 
 def sparse_attn_decode(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count, k_max: int, sink_len: int,
-                       window_len: int, softmax_scale: float, num_splits: int, part_o, part_ml,
-                       stream=None) -> None:
+                       window_len: int, parts: int, softmax_scale: float, num_splits: int, split_stride: int,
+                       part_o, part_ml, stream=None) -> None:
     _check(_lib.sparse_attn_decode(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(sel_pages), _ptr(sel_count), k_max,
-                                   sink_len, window_len, softmax_scale, num_splits, _ptr(part_o), _ptr(part_ml),
-                                   _stream(stream)), "sparse_attn_decode")
+                                   sink_len, window_len, parts, softmax_scale, num_splits, split_stride,
+                                   _ptr(part_o), _ptr(part_ml), _stream(stream)), "sparse_attn_decode")
 
 
 def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, part_ml, out, out_dtype: int,

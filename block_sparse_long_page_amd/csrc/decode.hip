@@ -60,7 +60,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_generic(DecodeArgs a)
     const int pos = L - a.Q + row;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
     TokenSet ts;
-    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max);
+    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max,
+            a.parts);
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
 
     // this workgroup's slice of the token set, then this wave's
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_generic(DecodeArgs a)
             ls = fmaf(lds_ml[w][h][1], aw, ls);
             os = fmaf(lds_o[w][h][c], aw, os);
         }
-        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.splits + split;
+        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
         a.part_o[prow * HD + c] = ls > 0.f ? os / ls : 0.f;
         if (c == 0) {
             a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
@@ -245,9 +246,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
     static_assert(U % 2 == 0, "tokens are paired for dot2");
     const Geometry& g = a.g;
 
+    constexpr int NGRP = kWaves * TPW;     // token groups of the workgroup, each with its own softmax state
+    // q.k partial sums are transposed through LDS when every head's sum fits
+    // in one lane group (G <= LPT); rows padded so the writes avoid bank conflicts
+    constexpr bool XPOSE = G <= LPT;
+    constexpr int XSTRIDE = G * LPT + LPT;
+    constexpr int XFLOATS = XPOSE ? kWaves * U * TPW * XSTRIDE : 1;
+    constexpr int OFLOATS = NGRP * G * HD;
     __shared__ int rows_lds[kWaves][CHUNK];
-    __shared__ float lds_o[kWaves][G][HD];
-    __shared__ float lds_ml[kWaves][G][2];
+    __shared__ float4 smem4[(XFLOATS > OFLOATS ? XFLOATS : OFLOATS) / 4];  // transpose area, then group outputs
+    __shared__ float grp_m[NGRP][G], grp_l[NGRP][G];
+    float* const xsum = (float*)smem4;
+    float4 (*const grp_o)[G][HD / 4] = (float4(*)[G][HD / 4])smem4;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, tg = lane / LPT;
@@ -265,7 +275,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
     const int pos = L - a.Q + row;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
     TokenSet ts;
-    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max);
+    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max,
+            a.parts);
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
 
     const int n = ts.total;
@@ -337,20 +348,57 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
 
         auto compute = [&](const uint4(&kw)[U], const uint4(&vw)[U], const int(&ri)[U]) {
             float z[U][HPL];
+            if constexpr (XPOSE) {
+                // each lane writes its partial sums [head][lane-in-group]; the DUP
+                // lanes holding a head then add that head's row and share the total
+                constexpr int PER = LPT / DUP;  // partials each of them adds
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t* k32 = (const uint32_t*)&kw[u];
-                float d[G];
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t* k32 = (const uint32_t*)&kw[u];
+                    float* xs = xsum + ((wave * U + u) * TPW + tg) * XSTRIDE;
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float acc = 0.f;
+                    for (int h = 0; h < G; ++h) {
+                        float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[h][j], k32[j], acc);
-                    d[h] = acc;
+                        for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[h][j], k32[j], acc);
+                        xs[h * LPT + sub] = acc;
+                    }
                 }
-                reduce_scatter<G, log2c<LPT>() - 1>(d, lane);
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int j = 0; j < HPL; ++j) z[u][j] = ri[u] >= 0 ? d[j] : -INFINITY;  // unscaled q.k
+                for (int u = 0; u < U; ++u) {
+                    const float* xs = xsum + ((wave * U + u) * TPW + tg) * XSTRIDE + head0 * LPT + (sub % DUP) * PER;
+                    float acc = 0.f;
+                    if constexpr (PER % 4 == 0) {
+#pragma unroll
+                        for (int v = 0; v < PER; v += 4) {
+                            const float4 t = *(const float4*)(xs + v);
+                            acc += (t.x + t.y) + (t.z + t.w);
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < PER; ++v) acc += xs[v];
+                    }
+                    acc = group_sum<DUP>(acc);
+                    z[u][0] = ri[u] >= 0 ? acc : -INFINITY;  // unscaled q.k
+                }
+                __builtin_amdgcn_wave_barrier();
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t* k32 = (const uint32_t*)&kw[u];
+                    float d[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[h][j], k32[j], acc);
+                        d[h] = acc;
+                    }
+                    reduce_scatter<G, log2c<LPT>() - 1>(d, lane);
+#pragma unroll
+                    for (int j = 0; j < HPL; ++j) z[u][j] = ri[u] >= 0 ? d[j] : -INFINITY;  // unscaled q.k
+                }
             }
             // reference maximum (unscaled q.k units): rescale only when a logit
             // passes it by more than the slack
@@ -428,59 +476,45 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
         __builtin_amdgcn_wave_barrier();
     }
 
-    // from raw q.k to base-2 logits for the merges below
-    for (int h = 0; h < G; ++h) m_all[h] *= sl2;
-    // every lane of a token group gets each head's sum from its holder
-    float l_all[G];
-    static_for<0, G>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        l_all[h] = group_bcast<LPT, (h / HPL) * DUP>(l_own[h % HPL], lane);
-    });
-
-    // fold the token groups of the wave (lanes sub, sub + LPT, ...) with
-    // cross-row register moves
-    static_for<0, 3>([&](auto sc) {
-        constexpr int OFF = LPT << decltype(sc)::value;
-        if constexpr (OFF < 64) {
+    // Every token group writes its state (base-2 reference maximum, sum and
+    // unnormalised output) to LDS; the workgroup then merges the groups with
+    // one exponential per (group, head) and writes the split's partial.  The
+    // output area reuses the transpose area, so all waves first leave the loop.
+    __syncthreads();
+    const int grp = wave * TPW + tg;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float m2 = xor_lanes<OFF>(m_all[h]);
-                const float l2 = xor_lanes<OFF>(l_all[h]);
-                const float mn = fmaxf(m_all[h], m2);
-                const float a1 = m_all[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_all[h] - mn);
-                const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-                l_all[h] = l_all[h] * a1 + l2 * a2;
-#pragma unroll
-                for (int c = 0; c < CH; ++c) o[h][c] = o[h][c] * a1 + xor_lanes<OFF>(o[h][c]) * a2;
-                m_all[h] = mn;
-            }
-        }
-    });
-    if (tg == 0) {
-        for (int h = 0; h < G; ++h) {
-            for (int c = 0; c < CH; ++c) lds_o[wave][h][sub * CH + c] = o[h][c];
-            if (sub == 0) {
-                lds_ml[wave][h][0] = m_all[h];
-                lds_ml[wave][h][1] = l_all[h];
-            }
-        }
+    for (int h = 0; h < G; ++h) {
+        grp_o[grp][h][sub * 2] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+        grp_o[grp][h][sub * 2 + 1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
     }
+#pragma unroll
+    for (int j = 0; j < HPL; ++j)
+        if (sub % DUP == 0) {
+            grp_m[grp][head0 + j] = m_own[j] * sl2;  // -inf stays -inf
+            grp_l[grp][head0 + j] = l_own[j];
+        }
     __syncthreads();
 
-    for (int i = threadIdx.x; i < G * HD; i += 64 * kWaves) {
-        const int h = i / HD, c = i % HD;
+    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * kWaves) {
+        const int h = i / (HD / 4), c4 = i % (HD / 4);
         float ms = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, lds_ml[w][h][0]);
-        float ls = 0.f, os = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = lds_ml[w][h][0];
-            const float aw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
-            ls = fmaf(lds_ml[w][h][1], aw, ls);
-            os = fmaf(lds_o[w][h][c], aw, os);
+        for (int gi = 0; gi < NGRP; ++gi) ms = fmaxf(ms, grp_m[gi][h]);
+        float ls = 0.f;
+        float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int gi = 0; gi < NGRP; ++gi) {
+            const float mg = grp_m[gi][h];
+            const float w = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - ms);
+            ls = fmaf(grp_l[gi][h], w, ls);
+            const float4 og = grp_o[gi][h][c4];
+            os.x = fmaf(og.x, w, os.x);
+            os.y = fmaf(og.y, w, os.y);
+            os.z = fmaf(og.z, w, os.z);
+            os.w = fmaf(og.w, w, os.w);
         }
-        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.splits + split;
-        a.part_o[prow * HD + c] = ls > 0.f ? os / ls : 0.f;
-        if (c == 0) {
+        const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
+        *(float4*)(a.part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
+        if (c4 == 0) {
             a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
             a.part_ml[prow * 2 + 1] = ls;
         }

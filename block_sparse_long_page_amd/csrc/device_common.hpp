@@ -225,16 +225,19 @@ struct FastDiv {
 // each selected page (pages ascending), then the window [ws, L).  Flat index
 // f in [0, total) maps to a position.  Only the first and the last selected
 // page can be cut by the region edges; interior candidates are whole pages.
+// `parts` keeps the sink and window (bit 0) and/or the middle (bit 1).
 struct TokenSet {
     int L, se, ws, P;
     int nsel;         // selected pages in use; -1 means every middle page (dense)
     int first_start;  // position of the first middle token of sel[0]
     int len0;         // middle tokens of sel[0]
     int mid_total;    // middle tokens attended
+    int n_sink, n_mid;
     int total;
     const int32_t* sel;
 
-    __device__ __forceinline__ void init(int L_, int S, int W, int P_, const int32_t* sel_, int count, int k_max)
+    __device__ __forceinline__ void init(int L_, int S, int W, int P_, const int32_t* sel_, int count, int k_max,
+                                         int parts)
     {
         L = L_;
         P = P_;
@@ -265,16 +268,18 @@ struct TokenSet {
                 }
             }
         }
-        total = se + mid_total + (L - ws);
+        n_sink = (parts & 1) ? se : 0;
+        n_mid = (parts & 2) ? mid_total : 0;
+        total = n_sink + n_mid + ((parts & 1) ? L - ws : 0);
     }
 
     // Position of flat index f; -1 when the entry does not name a middle
     // token (a bad selected page), so the caller skips it.
     __device__ __forceinline__ int position(int f, const FastDiv& pdiv) const
     {
-        if (f < se) return f;
-        f -= se;
-        if (f >= mid_total) return ws + (f - mid_total);
+        if (f < n_sink) return f;
+        f -= n_sink;
+        if (f >= n_mid) return ws + (f - n_mid);
         if (nsel < 0) return se + f;
         int t;
         if (f < len0) {

@@ -55,8 +55,10 @@ struct DecodeArgs {
     const int32_t* sel;
     const int32_t* count;
     int k_max, S, W;
+    int parts;         // bit 0: sink + window, bit 1: selected middle tokens
     float scale_log2;  // softmax scale * log2(e)
     int splits;
+    int split_stride;  // partial slots per row
     float* part_o;
     float* part_ml;
 };

@@ -66,16 +66,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     const int wg_first = plo + blockIdx.x * PAGES_PER_WG;
     if (wg_first > phi) return;
 
-    const long qrow0 = (((long)b * g.Hq + kvh * G) * a.Q + row) * HD;
-    for (int i = threadIdx.x; i < G * QV; i += 64 * kScoreWaves) {
-        const int h = i / QV, v = i % QV;
-        q_lds[i] = ((const uint4*)((const E*)a.q + qrow0 + (long)h * a.Q * HD))[v];
-    }
-    __syncthreads();
+    // every summary row of this wave's pages and their block-table entries
+    // are requested before the query staging, so the two round trips overlap
     const int first = wg_first + wave * PER_WAVE;
-    if (first > phi) return;
-
-    // every summary row of this wave's pages, and their block-table entries
     const long meta_row = ((long)b * g.Hkv + kvh) * g.max_pages;
     const int32_t* bt = g.block_table + (long)b * g.max_pages;
     uint4 w0[U], w1[U];
@@ -95,6 +88,14 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
             w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
         }
     }
+
+    const long qrow0 = (((long)b * g.Hq + kvh * G) * a.Q + row) * HD;
+    for (int i = threadIdx.x; i < G * QV; i += 64 * kScoreWaves) {
+        const int h = i / QV, v = i % QV;
+        q_lds[i] = ((const uint4*)((const E*)a.q + qrow0 + (long)h * a.Q * HD))[v];
+    }
+    __syncthreads();
+    if (first > phi) return;
 
     // this lane's channels of the G queries
     uint32_t qw[G][4];   // Quest + bf16: packed pairs

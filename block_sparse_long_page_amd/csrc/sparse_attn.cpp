@@ -144,8 +144,9 @@ int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int
 }
 
 int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
-                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
-                       float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, hipStream_t stream)
+                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len, int32_t parts,
+                       float softmax_scale, int32_t num_splits, int32_t split_stride, float* part_o, float* part_ml,
+                       hipStream_t stream)
 {
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
@@ -155,12 +156,16 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
     if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
     if (sel_pages && !sel_count) return SA_ERR_INVALID_ARG;
     if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (split_stride == 0) split_stride = num_splits;
+    if (split_stride < num_splits || split_stride > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (parts < SA_PART_LOCAL || parts > SA_PART_ALL) return SA_ERR_INVALID_ARG;
     if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
     const long wgs = (long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits;
     if (wgs > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
-    sa::DecodeArgs a{g,         q,           num_q_rows, sel_pages, sel_count, sel_pages ? k_max : 0,
-                     sink_len,  window_len,  scale * 1.4426950408889634f, num_splits, part_o, part_ml};
+    sa::DecodeArgs a{g,        q,          num_q_rows, sel_pages, sel_count, sel_pages ? k_max : 0,
+                     sink_len, window_len, parts,      scale * 1.4426950408889634f,   num_splits,
+                     split_stride, part_o, part_ml};
     return finish(sa::launch_decode(a, stream), stream);
 }
 

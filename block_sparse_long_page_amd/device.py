@@ -99,10 +99,10 @@ class SparseDecoder:
                              self.ws_bytes, stream)
 
     def decode(self, q: torch.Tensor, window: Optional[int] = None, dense: bool = False, scale: float = 0.0,
-               stream=None):
+               parts: int = B.SA_PART_ALL, stream=None):
         B.sparse_attn_decode(self.desc, q, self.Q, None if dense else self.sel, None if dense else self.count,
-                             self.k_max, self.sink, self.window if window is None else window, scale, self.splits,
-                             self.part_o, self.part_ml, stream)
+                             self.k_max, self.sink, self.window if window is None else window, parts, scale,
+                             self.splits, 0, self.part_o, self.part_ml, stream)
 
     def combine(self, stream=None):
         B.sparse_attn_combine(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
@@ -128,3 +128,55 @@ class SparseDecoder:
         cnt = self.count.cpu().numpy()
         sel = self.sel.cpu().numpy()[..., : self.k_max]
         return sel, cnt
+
+
+class OverlappedStep:
+    """One decode step with the selection hidden behind the sink+window work.
+
+    The sink and window do not depend on the selection, so their decode runs
+    on a side stream while `sparse_attn_select` runs on the caller's stream;
+    then the selected pages' middle tokens are decoded on the caller's stream.
+    Both decodes write split partials into disjoint slots of one buffer, and
+    one `sparse_attn_combine` merges them.  Streams keep the default priority.
+    """
+
+    def __init__(self, dec: SparseDecoder, local_splits: Optional[int] = None, middle_splits: Optional[int] = None):
+        self.dec = dec
+        c = dec.c
+        self.sl = local_splits or max(1, dec.splits * 3 // 8)
+        self.sm = middle_splits or max(1, dec.splits - self.sl)
+        self.stride = self.sl + self.sm
+        dev = c.k.device
+        self.part_o = torch.empty((dec.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((dec.rows, self.stride, 2), dtype=torch.float32, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+
+    def decode_middle(self, q, desc, window):
+        d = self.dec
+        B.sparse_attn_decode(desc, q, d.Q, d.sel, d.count, d.k_max, d.sink, window, B.SA_PART_MIDDLE, 0.0,
+                             self.sm, self.stride, self.part_o[:, self.sl:], self.part_ml[:, self.sl:])
+
+    def step(self, q: torch.Tensor, desc=None, meta=None, window: Optional[int] = None, middle_events=None):
+        d = self.dec
+        desc = d.desc if desc is None else desc
+        meta = d.meta if meta is None else meta
+        window = d.window if window is None else window
+        main = torch.cuda.current_stream()
+        self.fork.record(main)
+        self.side.wait_event(self.fork)
+        with torch.cuda.stream(self.side):
+            B.sparse_attn_decode(desc, q, d.Q, None, None, 0, d.sink, window, B.SA_PART_LOCAL, 0.0, self.sl,
+                                 self.stride, self.part_o, self.part_ml, self.side)
+        self.join.record(self.side)
+        B.sparse_attn_select(desc, q, d.Q, meta, d.mode, d.sink, window, d.budget, d.sel, d.count, d.ws,
+                             d.ws_bytes)
+        if middle_events is not None:
+            middle_events[0].record(main)
+        self.decode_middle(q, desc, window)
+        if middle_events is not None:
+            middle_events[1].record(main)
+        main.wait_event(self.join)
+        B.sparse_attn_combine(d.rows, d.c.hd, self.stride, self.part_o, self.part_ml, d.out, d.out_dtype, d.lse)
+        return d.out

@@ -62,6 +62,11 @@ extern "C" {
 #define SA_F32 0
 #define SA_BF16 1
 
+/* parts of the attended set a decode call covers */
+#define SA_PART_LOCAL 1  /* the sink and the window */
+#define SA_PART_MIDDLE 2 /* the middle-region tokens of the selected pages */
+#define SA_PART_ALL 3
+
 /* page-summary / scoring modes */
 #define SA_QUEST 0    /* per-channel min and max; score = sum_c max(q_c*min_c, q_c*max_c) */
 #define SA_MEAN 1     /* mean key of the page (MoBA-style block key); score = q.mean */
@@ -174,21 +179,33 @@ size_t sparse_attn_workspace_bytes(const sa_kv_desc* kv, int32_t num_q_rows);
  *                W + (steps since the selection), so tokens appended since
  *                stay visible (hybrid sparse attention page: selection
  *                refreshed every 32 steps while the window grows).
+ *   parts        SA_PART_ALL, or one of SA_PART_LOCAL (sink and window:
+ *                independent of the selection, so it can run on another
+ *                stream while sparse_attn_select runs) and SA_PART_MIDDLE
+ *                (the selected pages' middle tokens); the two partial
+ *                results merge in sparse_attn_combine like any other splits.
  *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
  *   num_splits   1..1024 parts of each row's token set (see
  *                sparse_attn_default_splits); each part is one workgroup.
- *   part_o       fp32 [batch][num_q_heads][num_q_rows][num_splits][head_dim]:
- *                the part's normalised output sum_t e^{z_t-m} v_t / l.
- *   part_ml      fp32 [batch][num_q_heads][num_q_rows][num_splits][2]:
- *                (m, l) with m = max logit z (natural units) of the part and
- *                l = sum_t e^{z_t-m}.  An empty part writes (-inf, 0), o = 0.
+ *   split_stride slots per row in part_o / part_ml (0 means num_splits,
+ *                else >= num_splits); this call writes slots [0, num_splits)
+ *                of every row, so a second call can fill the slots after
+ *                them through offset pointers.
+ *   part_o       fp32 [batch][num_q_heads][num_q_rows][split_stride][head_dim]:
+ *                the split's normalised output sum_t e^{z_t-m} v_t / l.
+ *   part_ml      fp32 [batch][num_q_heads][num_q_rows][split_stride][2]:
+ *                (m, l): m is a reference logit (natural units) within
+ *                8 ln 2 below the split's largest logit and l = sum_t e^{z_t-m}.
+ *                An empty split writes (-inf, 0) and o = 0.
  * No float atomics; results are bitwise reproducible.
  * Errors: null pointers (sel_count may be null only with sel_pages null),
- * num_q_rows < 1, S < 0, W < 1, k_max < 0, num_splits out of range.
+ * num_q_rows < 1, S < 0, W < 1, k_max < 0, parts not in 1..3, num_splits or
+ * split_stride out of range.
  */
 int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
-                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
-                       float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, hipStream_t stream);
+                       const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len, int32_t parts,
+                       float softmax_scale, int32_t num_splits, int32_t split_stride, float* part_o, float* part_ml,
+                       hipStream_t stream);
 
 /* A split count that fills the GPU for this shape (host arithmetic only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,

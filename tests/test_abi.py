@@ -62,14 +62,14 @@ def test_descriptor_checks(bad, code):
     d = _desc(**bad)
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 0, 8, DEV, None) == code
     assert lib.sparse_attn_select(ctypes.byref(d), DEV, 1, DEV, 0, 16, 16, 32, DEV, DEV, DEV, 1 << 20, None) == code
-    assert lib.sparse_attn_decode(ctypes.byref(d), DEV, 1, DEV, DEV, 2, 16, 16, 0.0, 4, DEV, DEV, None) == code
+    assert lib.sparse_attn_decode(ctypes.byref(d), DEV, 1, DEV, DEV, 2, 16, 16, 3, 0.0, 4, 0, DEV, DEV, None) == code
 
 
 def test_null_descriptor():
     lib = B.library()
     assert lib.sparse_attn_build_page_meta(None, 0, 0, 1, DEV, None) == B.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_select(None, DEV, 1, DEV, 0, 0, 1, 0, DEV, DEV, DEV, 0, None) == B.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_decode(None, DEV, 1, None, None, 0, 0, 1, 0.0, 1, DEV, DEV, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_decode(None, DEV, 1, None, None, 0, 0, 1, 3, 0.0, 1, 0, DEV, DEV, None) == B.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_workspace_bytes(None, 1) == 0
 
 
@@ -116,10 +116,12 @@ def test_decode_checks():
     d = _desc()
 
     def dec(**kw):
-        a = dict(q=DEV, rows=1, sel=DEV, cnt=DEV, kmax=2, S=16, W=16, scale=0.0, splits=4, po=DEV, pml=DEV)
+        a = dict(q=DEV, rows=1, sel=DEV, cnt=DEV, kmax=2, S=16, W=16, parts=3, scale=0.0, splits=4, stride=0,
+                 po=DEV, pml=DEV)
         a.update(kw)
         return lib.sparse_attn_decode(ctypes.byref(d), a["q"], a["rows"], a["sel"], a["cnt"], a["kmax"], a["S"],
-                                      a["W"], a["scale"], a["splits"], a["po"], a["pml"], None)
+                                      a["W"], a["parts"], a["scale"], a["splits"], a["stride"], a["po"], a["pml"],
+                                      None)
 
     assert dec(q=None) == B.SA_ERR_INVALID_ARG
     assert dec(po=None) == B.SA_ERR_INVALID_ARG
@@ -133,6 +135,10 @@ def test_decode_checks():
     assert dec(splits=1025) == B.SA_ERR_INVALID_ARG
     assert dec(scale=float("nan")) == B.SA_ERR_INVALID_ARG
     assert dec(scale=float("inf")) == B.SA_ERR_INVALID_ARG
+    assert dec(parts=0) == B.SA_ERR_INVALID_ARG
+    assert dec(parts=4) == B.SA_ERR_INVALID_ARG
+    assert dec(stride=3) == B.SA_ERR_INVALID_ARG  # fewer slots than splits
+    assert dec(stride=1025) == B.SA_ERR_INVALID_ARG
 
 
 def test_combine_checks():

@@ -210,3 +210,30 @@ def test_empty_sequence_gives_zero_output():
     ref = oracle.run(pr.cache, pr.q, mode=0, Q=1, sink=4, window=8, budget=32,
                      sel=dec.selection()[0], cnt=dec.selection()[1])
     check_output(out[0], ref.out[0], 0)
+
+
+@pytest.mark.parametrize("name", ["bf16-hd128-g8-p64", "bf16-hd128-g4-p16", "f32-hd64-g4-p16", "bf16-hd128-g8-q5"])
+@pytest.mark.parametrize("splits", [(1, 1), (3, 5), (7, 2)])
+def test_overlapped_sink_window_and_middle_decodes(name, splits):
+    from block_sparse_long_page_amd.device import OverlappedStep
+
+    pr = _problem(name, "quest", seed=4)
+    dc = DeviceCache.from_host(pr.cache)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget)
+    q = to_device(pr.q)
+    dec.build_meta()
+    ov = OverlappedStep(dec, local_splits=splits[0], middle_splits=splits[1])
+    ov.step(q)
+    torch.cuda.synchronize()
+    out_ov, lse_ov = dec.out_f32(), dec.lse_f32()
+    sel, cnt = dec.selection()
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                     sel=sel, cnt=cnt)
+    check_output(out_ov, ref.out, pr.cache.dtype, f"{name} overlapped")
+    check_lse(lse_ov, ref.lse, f"{name} overlapped")
+    dec.step(q)  # one call over the whole set
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out_ov, dec.out_f32(), atol=TOL_SPLIT[pr.cache.dtype], rtol=0)
+
+
+TOL_SPLIT = {0: 2e-6, 1: 1e-2}  # fp32 rounding only; bf16: outputs are rounded to bf16
