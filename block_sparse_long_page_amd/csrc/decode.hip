@@ -29,6 +29,12 @@ namespace {
 #ifndef SA_DECODE_U
 #define SA_DECODE_U 4
 #endif
+#ifndef SA_MFMA_TPS
+#define SA_MFMA_TPS 1
+#endif
+#ifndef SA_DECODE_VALU
+#define SA_DECODE_VALU 0
+#endif
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -220,48 +226,72 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_generic(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel.  Same work split as k_decode_generic; per wave:
-//  * prologue: the row index ((phys * Hkv + kvh) * P + offset) of each token
-//    of the wave's range is resolved once into LDS, so the K/V loads of the
-//    main loop never wait on the page list or the block table;
+// bf16 kernel.  One workgroup of NW waves per (sequence, KV head, query row,
+// split).  The split's tokens are taken in rounds of NW wave steps (wave w
+// takes the w-th step of each round) and the waves advance in lockstep.  NW is
+// 8 where the LDS of one workgroup allows it, so that one workgroup fills a
+// CU: the waves sharing a CU then belong to one workgroup and finish
+// together, instead of a second workgroup trailing the first.
+//  * prologue: the sequence length, the selected-page count and the whole
+//    page list (into LDS) are loaded in one round; the workgroup then resolves
+//    the row index ((phys * Hkv + kvh) * P + offset) of up to 2048 tokens into
+//    LDS with all block-table loads in flight together, so the K/V loads of
+//    the main loop never wait on the page list or the block table;
 //  * main loop: K/V rows double-buffered in registers (the next U token steps
 //    are in flight while the current ones are computed);
-//  * q.k: packed bf16 dot products, then a DPP reduce-scatter over the LPT
-//    lanes of a token, after which each lane holds the full sum of its own
-//    head(s): the exponentials are computed once per (token, head);
+//  * q.k: packed bf16 dot products, then the partial sums of the LPT lanes of
+//    a token are transposed through LDS (or reduce-scattered with DPP) so that
+//    each lane holds the full logit of its own head(s): the exponentials are
+//    computed once per (token, head);
 //  * p.v: the weights of two tokens are packed as a bf16 pair, broadcast from
-//    the lane holding each head, and accumulated with dot2 into fp32.
+//    the lane holding each head, and accumulated with dot2 into fp32;
+//  * epilogue: the token groups of a wave fold with lane swaps, the waves
+//    through LDS; the workgroup writes its normalised partial and (m, l).
 // ---------------------------------------------------------------------------
 
+constexpr int kSelCap = 1024;  // page-list entries staged in LDS; longer lists are read in place
+constexpr int kRowsWG = 2048;  // rows resolved per workgroup per prologue round
+
 template <int HD, int G>
-__global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
+struct Bf16Plan {
+    static constexpr int CH = 8;                     // bf16 channels per lane (one 16-byte load)
+    static constexpr int LPT = HD / CH;              // lanes per token: 16 (hd 128) or 8 (hd 64)
+    static constexpr int TPW = 64 / LPT;             // tokens per wave load
+    static constexpr int U = HD == 64 ? 2 : SA_DECODE_U;  // loads per buffer (even): 16 tokens per wave step
+    static constexpr bool XPOSE = G <= LPT;          // q.k sums transposed through LDS
+    static constexpr int XSTRIDE = G * LPT + LPT;    // padded so the writes avoid bank conflicts
+    static constexpr int xfloats(int nw) { return XPOSE ? nw * U * TPW * XSTRIDE : 4; }
+    static constexpr int ofloats(int nw) { return nw * G * HD; }
+    static constexpr int smem_floats(int nw) { return xfloats(nw) > ofloats(nw) ? xfloats(nw) : ofloats(nw); }
+    static constexpr int lds_bytes(int nw)
+    {
+        return 4 * (smem_floats(nw) + kSelCap + kRowsWG + 2 * nw * G);
+    }
+    static constexpr int NW = lds_bytes(8) <= 96 * 1024 ? 8 : 4;
+};
+
+template <int HD, int G>
+__global__ __launch_bounds__((64 * Bf16Plan<HD, G>::NW)) void k_decode_bf16(DecodeArgs a)
 {
-    constexpr int CH = 8;                  // bf16 channels per lane (one 16-byte load)
-    constexpr int LPT = HD / CH;           // lanes per token: 16 (hd 128) or 8 (hd 64)
-    constexpr int TPW = 64 / LPT;          // tokens per wave load
-    constexpr int U = SA_DECODE_U;         // token steps per buffer (even)
+    using Plan = Bf16Plan<HD, G>;
+    constexpr int NW = Plan::NW, CH = Plan::CH, LPT = Plan::LPT, TPW = Plan::TPW, U = Plan::U;
     constexpr int HPL = G > LPT ? G / LPT : 1;  // heads held per lane after the reduce-scatter
     constexpr int DUP = G < LPT ? LPT / G : 1;  // lanes holding the same head
-    constexpr int CHUNK = 256;             // tokens resolved per prologue
+    constexpr bool XPOSE = Plan::XPOSE;
+    constexpr int XSTRIDE = Plan::XSTRIDE;
     static_assert(U % 2 == 0, "tokens are paired for dot2");
     const Geometry& g = a.g;
 
-    constexpr int NGRP = kWaves * TPW;     // token groups of the workgroup, each with its own softmax state
-    // q.k partial sums are transposed through LDS when every head's sum fits
-    // in one lane group (G <= LPT); rows padded so the writes avoid bank conflicts
-    constexpr bool XPOSE = G <= LPT;
-    constexpr int XSTRIDE = G * LPT + LPT;
-    constexpr int XFLOATS = XPOSE ? kWaves * U * TPW * XSTRIDE : 1;
-    constexpr int OFLOATS = NGRP * G * HD;
-    __shared__ int rows_lds[kWaves][CHUNK];
-    __shared__ float4 smem4[(XFLOATS > OFLOATS ? XFLOATS : OFLOATS) / 4];  // transpose area, then group outputs
-    __shared__ float grp_m[NGRP][G], grp_l[NGRP][G];
+    __shared__ int sel_lds[kSelCap];
+    __shared__ __attribute__((aligned(16))) int rows_lds[kRowsWG];
+    __shared__ float4 smem4[Plan::smem_floats(NW) / 4];  // transpose area, then the waves' outputs
+    __shared__ float wv_m[NW][G], wv_l[NW][G];
     float* const xsum = (float*)smem4;
-    float4 (*const grp_o)[G][HD / 4] = (float4(*)[G][HD / 4])smem4;
+    float4 (*const wv_o)[G][HD / 4] = (float4(*)[G][HD / 4])smem4;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, tg = lane / LPT;
-    const int head0 = (sub / DUP) * HPL;   // first head this lane holds after the reduce-scatter
+    const int head0 = (sub / DUP) * HPL;  // first head this lane holds after the reduce-scatter
 
     int bid = blockIdx.x;
     const int split = bid % a.splits;
@@ -270,22 +300,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
     bid /= g.Hkv;
     const int row = bid % a.Q;
     const int b = bid / a.Q;
-
-    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
-    const int pos = L - a.Q + row;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
-    TokenSet ts;
-    ts.init(L, a.S, a.W, g.P, a.sel ? a.sel + prob * a.k_max : nullptr, a.sel ? a.count[prob] : 0, a.k_max,
-            a.parts);
-    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
 
-    const int n = ts.total;
-    const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
-    const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
-    const int len = f1 - f0;
-    const int w0 = f0 + wave * (len / kWaves) + imin(wave, len % kWaves);
-    const int w1 = w0 + len / kWaves + (wave < len % kWaves ? 1 : 0);
-
+    // one round of loads: length, count, page list, the group's queries
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int count = a.sel ? a.count[prob] : 0;
+    const int32_t* sel_g = a.sel ? a.sel + prob * a.k_max : nullptr;
+    const bool staged = sel_g != nullptr && a.k_max <= kSelCap;
+    if (staged)
+        for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_lds[i] = sel_g[i];
     uint32_t qw[G][4];
     for (int h = 0; h < G; ++h) {
         const uint4 w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD +
@@ -295,6 +318,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
         qw[h][2] = w.z;
         qw[h][3] = w.w;
     }
+    __syncthreads();
+
+    const int pos = L - a.Q + row;
+    TokenSet ts;
+    ts.init(L, a.S, a.W, g.P, staged ? (const int32_t*)sel_lds : sel_g, count, a.k_max, a.parts);
+    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
+
+    const int n = ts.total;
+    const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
+    const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
 
     float m_all[G], o[G][CH];
     float m_own[HPL], l_own[HPL];
@@ -316,29 +349,47 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
     const float sl2 = a.scale_log2;
     const float slack = kRescaleSlack / sl2;
 
-    for (int cb = w0; cb < w1; cb += CHUNK) {
-        const int ce = imin(w1, cb + CHUNK);
-        for (int f = cb + lane; f < ce; f += 64) {
-            int t = ts.position(f, pdiv);
-            int ri = -1;
-            if (t >= 0 && t <= pos) {
-                const int pg = pdiv.div(t);
-                const int phys = bt[pg];
-                if (phys >= 0 && phys < g.num_phys) ri = phys * hkvP + kvh * g.P + (t - pg * g.P);
-            }
-            rows_lds[wave][f - cb] = ri;
-        }
-        __builtin_amdgcn_wave_barrier();
+    constexpr int TS = TPW * U;  // tokens per wave step
+    constexpr int RT = NW * TS;  // tokens per round: wave w takes the w-th step of every round
+    constexpr int PER_T = kRowsWG / (64 * NW);
+    static_assert(kRowsWG % RT == 0 && kRowsWG % (64 * NW) == 0, "rounds tile the row chunk");
 
-        const int nst = (ce - cb + TPW * U - 1) / (TPW * U);
+    for (int cb = f0; cb < f1; cb += kRowsWG) {
+        const int ce = imin(f1, cb + kRowsWG);
+        // the workgroup resolves the chunk's rows, every block-table load in flight together
+        __syncthreads();  // the previous chunk's rows are no longer read
+        {
+            int tok[PER_T], phys[PER_T];
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int f = cb + i * 64 * NW + (int)threadIdx.x;
+                int t = f < ce ? ts.position(f, pdiv) : -1;
+                if (t > pos) t = -1;
+                tok[i] = t;
+                phys[i] = t >= 0 ? bt[pdiv.div(t)] : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int t = tok[i];
+                int ri = -1;
+                if (t >= 0 && phys[i] >= 0 && phys[i] < g.num_phys) {
+                    const int pg = pdiv.div(t);
+                    ri = phys[i] * hkvP + kvh * g.P + (t - pg * g.P);
+                }
+                rows_lds[i * 64 * NW + threadIdx.x] = ri;
+            }
+        }
+        __syncthreads();
+
+        const int nr = (ce - cb + RT - 1) / RT;  // rounds in this chunk, the same for every wave
 
         // Rows of tokens that are not attended are not loaded: their
         // registers keep earlier (finite) data, and their weight is 0.
-        auto load = [&](int s, uint4(&kw)[U], uint4(&vw)[U], int(&ri)[U]) {
+        auto load = [&](int r, uint4(&kw)[U], uint4(&vw)[U], int(&ri)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = s * (TPW * U) + u * TPW + tg;
-                ri[u] = cb + j < ce ? rows_lds[wave][j] : -1;
+                const int j = r * RT + wave * TS + u * TPW + tg;
+                ri[u] = cb + j < ce ? rows_lds[j] : -1;
                 if (ri[u] >= 0) {
                     kw[u] = *(const uint4*)(kbase + (long)ri[u] * HD);
                     vw[u] = *(const uint4*)(vbase + (long)ri[u] * HD);
@@ -465,51 +516,82 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
         int ra[U], rb[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) ka[u] = va[u] = kb[u] = vb[u] = make_uint4(0, 0, 0, 0);
+        // The waves of the workgroup advance in lockstep, one barrier per
+        // round: wave scheduling favours the oldest waves, and without the
+        // barrier the last waves of a CU would finish their share alone.
+        auto busy = [&](int r) { return cb + r * RT + wave * TS < ce; };
         load(0, ka, va, ra);
-        for (int s = 0; s < nst; s += 2) {
-            if (s + 1 < nst) load(s + 1, kb, vb, rb);
-            compute(ka, va, ra);
-            if (s + 1 >= nst) break;
-            if (s + 2 < nst) load(s + 2, ka, va, ra);
-            compute(kb, vb, rb);
+        for (int r = 0; r < nr; r += 2) {
+            if (r + 1 < nr) load(r + 1, kb, vb, rb);
+            if (busy(r)) compute(ka, va, ra);
+            __builtin_amdgcn_s_barrier();
+            if (r + 1 >= nr) break;
+            if (r + 2 < nr) load(r + 2, ka, va, ra);
+            if (busy(r + 1)) compute(kb, vb, rb);
+            __builtin_amdgcn_s_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
     }
 
-    // Every token group writes its state (base-2 reference maximum, sum and
-    // unnormalised output) to LDS; the workgroup then merges the groups with
-    // one exponential per (group, head) and writes the split's partial.  The
-    // output area reuses the transpose area, so all waves first leave the loop.
-    __syncthreads();
-    const int grp = wave * TPW + tg;
+    // Fold the TPW token groups of the wave (lanes sub, sub + LPT, ...): the
+    // partner lane holds the same channels and heads of another group.
+    static_for<0, log2c<TPW>()>([&](auto ic) {
+        constexpr int OFF = LPT << decltype(ic)::value;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        grp_o[grp][h][sub * 2] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-        grp_o[grp][h][sub * 2 + 1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-    }
+        for (int h = 0; h < G; ++h) {
+            const float m1 = m_all[h], m2 = xor_lanes<OFF>(m1);
+            const float mn = fmaxf(m1, m2);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * sl2);
+            const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
 #pragma unroll
-    for (int j = 0; j < HPL; ++j)
-        if (sub % DUP == 0) {
-            grp_m[grp][head0 + j] = m_own[j] * sl2;  // -inf stays -inf
-            grp_l[grp][head0 + j] = l_own[j];
+            for (int c = 0; c < CH; ++c) o[h][c] = fmaf(o[h][c], a1, xor_lanes<OFF>(o[h][c]) * a2);
+            m_all[h] = mn;
         }
+#pragma unroll
+        for (int j = 0; j < HPL; ++j) {
+            const float m1 = m_own[j], m2 = xor_lanes<OFF>(m1);
+            const float l2 = xor_lanes<OFF>(l_own[j]);
+            const float mn = fmaxf(m1, m2);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * sl2);
+            const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
+            l_own[j] = fmaf(l_own[j], a1, l2 * a2);
+            m_own[j] = mn;
+        }
+    });
+
+    // The waves' states go to LDS (the output area reuses the transpose area,
+    // so every wave first leaves its loop); the workgroup merges them with one
+    // exponential per (wave, head) and writes the split's partial.
+    __syncthreads();
+    if (tg == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            wv_o[wave][h][sub * 2] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+            wv_o[wave][h][sub * 2 + 1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+        }
+#pragma unroll
+        for (int j = 0; j < HPL; ++j)
+            if (sub % DUP == 0) {
+                wv_m[wave][head0 + j] = m_own[j] * sl2;  // -inf stays -inf
+                wv_l[wave][head0 + j] = l_own[j];
+            }
+    }
     __syncthreads();
 
-    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * kWaves) {
+    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
         const int h = i / (HD / 4), c4 = i % (HD / 4);
         float ms = -INFINITY;
-        for (int gi = 0; gi < NGRP; ++gi) ms = fmaxf(ms, grp_m[gi][h]);
+        for (int w = 0; w < NW; ++w) ms = fmaxf(ms, wv_m[w][h]);
         float ls = 0.f;
         float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int gi = 0; gi < NGRP; ++gi) {
-            const float mg = grp_m[gi][h];
-            const float w = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - ms);
-            ls = fmaf(grp_l[gi][h], w, ls);
-            const float4 og = grp_o[gi][h][c4];
-            os.x = fmaf(og.x, w, os.x);
-            os.y = fmaf(og.y, w, os.y);
-            os.z = fmaf(og.z, w, os.z);
-            os.w = fmaf(og.w, w, os.w);
+        for (int w = 0; w < NW; ++w) {
+            const float mw = wv_m[w][h];
+            const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
+            ls = fmaf(wv_l[w][h], wt, ls);
+            const float4 ow = wv_o[w][h][c4];
+            os.x = fmaf(ow.x, wt, os.x);
+            os.y = fmaf(ow.y, wt, os.y);
+            os.z = fmaf(ow.z, wt, os.z);
+            os.w = fmaf(ow.w, wt, os.w);
         }
         const float inv = ls > 0.f ? 1.0f / ls : 0.f;
         const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
@@ -521,20 +603,358 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_bf16(DecodeArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel on the matrix cores.  The G query heads of a KV group against a
+// tile of 16 tokens are a small dense product, so both products of a tile run
+// as MFMAs and the vector ALU only does the softmax:
+//  * q.k: v_mfma_f32_16x16x32_bf16 with the tile's keys as A (row = token,
+//    8 channels per lane straight from global memory) and the queries as B
+//    (column = head; heads past G are zero).  The result leaves, in lane
+//    (r, j) = (lane % 16, lane / 16), the logits of head r for tokens 4j..4j+3;
+//  * softmax per head with the lazily rescaled reference maximum (base 2, the
+//    scale folded into the exponent); the weights of lane (r, j) are exactly
+//    the A operand of the next product (row = head r, k = tokens 4j..4j+3);
+//  * p.v: v_mfma_f32_16x16x16_bf16 per 16 output channels with the values as
+//    B (k = token, column = channel).  The value rows are written to LDS as
+//    loaded (row-major, a 32-byte pad per 4 tokens so the column reads below
+//    hit distinct banks) and read back one bf16 per token and channel;
+//  * the accumulators hold rows = heads 4j..4j+3 and column = channel.
+// The split's tokens are taken in rounds of NW tiles, tile w of each round by
+// wave w.  Epilogue as in the vector kernel: the waves merge through LDS.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int HD, int G>
+struct MfmaPlan {
+    static constexpr int KK = HD / 32;                 // q.k products per tile (32 channels each)
+    static constexpr int NB = HD / 16;                 // p.v products per tile (16 channels each)
+    static constexpr int VLD = HD / 32;                // 16-byte value loads per lane per tile
+    static constexpr int LPT = HD / 8;                 // lanes per value row
+    static constexpr int VROW = HD * 2;                // bytes per value row
+    static constexpr int VTILE = 16 * VROW + 4 * 32;   // LDS bytes of one value tile (padded)
+    static constexpr int TPS = SA_MFMA_TPS;            // tiles per pipeline step
+    static constexpr int NW = 8;
+    static constexpr int vbytes(int nw) { return nw * TPS * VTILE; }
+    static constexpr int obytes(int nw) { return nw * G * HD * 4; }
+    static constexpr int smem_bytes(int nw) { return vbytes(nw) > obytes(nw) ? vbytes(nw) : obytes(nw); }
+};
+
+// LDS byte offset of (token t, byte b) in a value tile
+template <int VROW>
+__device__ __forceinline__ int vt_off(int t, int b)
+{
+    return t * VROW + (t >> 2) * 32 + b;
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(DecodeArgs a)
+{
+    using Plan = MfmaPlan<HD, G>;
+    constexpr int NW = Plan::NW, KK = Plan::KK, NB = Plan::NB, VLD = Plan::VLD, LPT = Plan::LPT;
+    constexpr int VROW = Plan::VROW, VTILE = Plan::VTILE, TPS = Plan::TPS;
+    constexpr int RT = NW * TPS * 16;  // tokens per round
+    constexpr int PER_T = kRowsWG / (64 * NW);
+    static_assert(kRowsWG % RT == 0 && kRowsWG % (64 * NW) == 0, "rounds tile the row chunk");
+    static_assert(G <= 16, "one MFMA column per head");
+    const Geometry& g = a.g;
+
+    __shared__ int sel_lds[kSelCap];
+    __shared__ __attribute__((aligned(16))) int rows_lds[kRowsWG];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Plan::smem_bytes(NW)];
+    __shared__ float wv_m[NW][G], wv_l[NW][G];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, j = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int kvh = bid % g.Hkv;
+    bid /= g.Hkv;
+    const int row = bid % a.Q;
+    const int b = bid / a.Q;
+    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
+
+    // one round of loads: length, count, page list, the group's queries
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int count = a.sel ? a.count[prob] : 0;
+    const int32_t* sel_g = a.sel ? a.sel + prob * a.k_max : nullptr;
+    const bool staged = sel_g != nullptr && a.k_max <= kSelCap;
+    if (staged)
+        for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_lds[i] = sel_g[i];
+    // B operand of q.k: head r, channels 32 kk + 8 j .. + 8
+    uint4 qb[KK];
+    for (int kk = 0; kk < KK; ++kk) {
+        qb[kk] = make_uint4(0, 0, 0, 0);
+        if (r < G)
+            qb[kk] = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + r) * a.Q + row) * HD +
+                                     32 * kk + 8 * j);
+    }
+    __syncthreads();
+
+    const int pos = L - a.Q + row;
+    TokenSet ts;
+    ts.init(L, a.S, a.W, g.P, staged ? (const int32_t*)sel_lds : sel_g, count, a.k_max, a.parts);
+    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
+    const int n = ts.total;
+    const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
+    const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
+
+    const float sl2 = a.scale_log2;
+    const float slack = kRescaleSlack / sl2;
+    f32x4_t o[NB];
+    for (int m = 0; m < NB; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // reference maximum of head r (raw q.k units)
+    float l_run = 0.f;        // this lane's share of head r's sum
+
+    const uint16_t* kbase = (const uint16_t*)g.k;
+    const uint16_t* vbase = (const uint16_t*)g.v;
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
+    const int hkvP = g.Hkv * g.P;
+    unsigned char* const vt = smem + wave * TPS * VTILE;  // this wave's value tiles
+
+    // value rows: lane (r, j) loads tokens 4j + v (hd 128) or 4j + 2v + r/8 (hd 64), 16 bytes each
+    const int vchunk = lane % LPT;
+    auto vtok = [&](int v) { return HD == 128 ? 4 * j + v : 4 * j + 2 * v + (r >> 3); };
+
+    for (int cb = f0; cb < f1; cb += kRowsWG) {
+        const int ce = imin(f1, cb + kRowsWG);
+        __syncthreads();  // the previous chunk's rows are no longer read
+        {
+            int tok[PER_T], phys[PER_T];
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int f = cb + i * 64 * NW + (int)threadIdx.x;
+                int t = f < ce ? ts.position(f, pdiv) : -1;
+                if (t > pos) t = -1;
+                tok[i] = t;
+                phys[i] = t >= 0 ? bt[pdiv.div(t)] : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int t = tok[i];
+                int ri = -1;
+                if (t >= 0 && phys[i] >= 0 && phys[i] < g.num_phys) {
+                    const int pg = pdiv.div(t);
+                    ri = phys[i] * hkvP + kvh * g.P + (t - pg * g.P);
+                }
+                if (cb + i * 64 * NW + (int)threadIdx.x < ce) rows_lds[i * 64 * NW + threadIdx.x] = ri;
+            }
+        }
+        __syncthreads();
+
+        const int nr = (ce - cb + RT - 1) / RT;  // rounds in this chunk
+
+        struct Buf {
+            uint4 k[TPS][KK];
+            uint4 v[TPS][VLD];
+            int4 rv[TPS];  // rows of tokens 4j .. 4j+3 of each tile (-1: not attended)
+        };
+        // Rows of tokens that are not attended are not loaded: their registers
+        // keep earlier (finite) data, and their logits are masked to -inf.
+        auto load = [&](int rd, Buf& B) {
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt) {
+                const int t0 = rd * RT + (wave * TPS + tt) * 16;  // tile start within the chunk
+                const int4 rv = cb + t0 + 4 * j + 3 < ce
+                                    ? *(const int4*)(rows_lds + t0 + 4 * j)
+                                    : make_int4(cb + t0 + 4 * j < ce ? rows_lds[t0 + 4 * j] : -1,
+                                                cb + t0 + 4 * j + 1 < ce ? rows_lds[t0 + 4 * j + 1] : -1,
+                                                cb + t0 + 4 * j + 2 < ce ? rows_lds[t0 + 4 * j + 2] : -1, -1);
+                B.rv[tt] = rv;
+                const int rk = cb + t0 + r < ce ? rows_lds[t0 + r] : -1;
+                if (rk >= 0) {
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
+                }
+                const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+                for (int v = 0; v < VLD; ++v) {
+                    const int rr = rows4[HD == 128 ? v : 2 * v + (r >> 3)];
+                    if (rr >= 0) B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
+                }
+            }
+        };
+
+        auto compute = [&](const Buf& B, int tt) {
+            // q.k
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[tt][kk]),
+                                                            __builtin_bit_cast(bf16x8_t, qb[kk]), s, 0, 0, 0);
+            const int4 rv = B.rv[tt];
+            float z[4] = {rv.x >= 0 ? s[0] : -INFINITY, rv.y >= 0 ? s[1] : -INFINITY, rv.z >= 0 ? s[2] : -INFINITY,
+                          rv.w >= 0 ? s[3] : -INFINITY};
+            // values to LDS as loaded
+#pragma unroll
+            for (int v = 0; v < VLD; ++v)
+                *(uint4*)(vt + tt * VTILE + vt_off<VROW>(vtok(v), 16 * vchunk)) = B.v[tt][v];
+            // softmax: tile maximum of head r over the 4 lanes holding it
+            float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+            mx = fmaxf(mx, xor_lanes<16>(mx));
+            mx = fmaxf(mx, xor_lanes<32>(mx));
+            const bool need = r < G && mx > m_run + slack;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float mn = need ? mx : m_run;
+                const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mn) * sl2) : 1.f;  // 0 while m = -inf
+                l_run *= alpha;
+                m_run = mn;
+                // accumulator rows are heads 4j + i: fetch their factors
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * j + i);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) o[m][i] *= ai;
+                }
+            }
+            const float mref = m_run == -INFINITY ? 0.f : -m_run * sl2;
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(fmaf(z[i], sl2, mref));  // -inf -> 0
+                l_run += p[i];
+            }
+            const uint2 pw = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+            const i16x4_t pa = __builtin_bit_cast(i16x4_t, pw);
+            __builtin_amdgcn_wave_barrier();
+            // p.v, 16 channels per product; B operand = values of tokens 4j .. 4j+3 at channel 16m + r
+            const unsigned char* vcol = vt + tt * VTILE + 2 * r;
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                i16x4_t vb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vb[i] = *(const short*)(vcol + vt_off<VROW>(4 * j + i, 32 * m));
+                o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[m], 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+
+        auto busy = [&](int rd, int tt) { return cb + rd * RT + (wave * TPS + tt) * 16 < ce; };
+
+        Buf A, Bb;
+#pragma unroll
+        for (int tt = 0; tt < TPS; ++tt) {
+            for (int kk = 0; kk < KK; ++kk) A.k[tt][kk] = Bb.k[tt][kk] = make_uint4(0, 0, 0, 0);
+            for (int v = 0; v < VLD; ++v) A.v[tt][v] = Bb.v[tt][v] = make_uint4(0, 0, 0, 0);
+        }
+        load(0, A);
+        for (int rd = 0; rd < nr; rd += 2) {
+            if (rd + 1 < nr) load(rd + 1, Bb);
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt)
+                if (busy(rd, tt)) compute(A, tt);
+            if (rd + 1 >= nr) break;
+            if (rd + 2 < nr) load(rd + 2, A);
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt)
+                if (busy(rd + 1, tt)) compute(Bb, tt);
+        }
+    }
+
+    // head r's sum over the 4 lanes holding it
+    l_run += xor_lanes<16>(l_run);
+    l_run += xor_lanes<32>(l_run);
+
+    // The waves' states go to LDS (the output area reuses the value tiles, so
+    // every wave first leaves its loop); the workgroup merges them with one
+    // exponential per (wave, head) and writes the split's partial.
+    __syncthreads();
+    float* const wv_o = (float*)smem;  // [NW][G][HD]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * j + i;
+        if (h < G) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m) wv_o[(wave * G + h) * HD + 16 * m + r] = o[m][i];
+        }
+    }
+    if (j == 0 && r < G) {
+        wv_m[wave][r] = m_run * sl2;  // -inf stays -inf
+        wv_l[wave][r] = l_run;
+    }
+    __syncthreads();
+
+    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
+        const int h = i / (HD / 4), c4 = i % (HD / 4);
+        float ms = -INFINITY;
+        for (int w = 0; w < NW; ++w) ms = fmaxf(ms, wv_m[w][h]);
+        float ls = 0.f;
+        float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int w = 0; w < NW; ++w) {
+            const float mw = wv_m[w][h];
+            const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
+            ls = fmaf(wv_l[w][h], wt, ls);
+            const float4 ow = *(const float4*)(wv_o + (w * G + h) * HD + 4 * c4);
+            os.x = fmaf(ow.x, wt, os.x);
+            os.y = fmaf(ow.y, wt, os.y);
+            os.z = fmaf(ow.z, wt, os.z);
+            os.w = fmaf(ow.w, wt, os.w);
+        }
+        const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
+        *(float4*)(a.part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
+        if (c4 == 0) {
+            a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
+            a.part_ml[prow * 2 + 1] = ls;
+        }
+    }
+}
+
+#if SA_DECODE_VALU
+template <int HD, int G>
+hipError_t launch_bf16(const DecodeArgs& a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_decode_bf16<HD, G>), grid, dim3(64 * Bf16Plan<HD, G>::NW), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int HD, int G>
+int bf16_wgs_per_cu()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_bf16<HD, G>, 64 * Bf16Plan<HD, G>::NW, 0) !=
+        hipSuccess)
+        return 1;
+    return n > 0 ? n : 1;
+}
+#else
+template <int HD, int G>
+hipError_t launch_bf16(const DecodeArgs& a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_decode_mfma<HD, G>), grid, dim3(64 * MfmaPlan<HD, G>::NW), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int HD, int G>
+int bf16_wgs_per_cu()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_mfma<HD, G>, 64 * MfmaPlan<HD, G>::NW, 0) !=
+        hipSuccess)
+        return 1;
+    return n > 0 ? n : 1;
+}
+#endif
+
 template <int HD, bool BF>
 hipError_t launch_g(const DecodeArgs& a, dim3 grid, hipStream_t s)
 {
-    const dim3 block(64 * kWaves);
     if constexpr (BF) {
         switch (a.g.G) {
-        case 1: hipLaunchKernelGGL((k_decode_bf16<HD, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_decode_bf16<HD, 2>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_decode_bf16<HD, 4>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((k_decode_bf16<HD, 8>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((k_decode_bf16<HD, 16>), grid, block, 0, s, a); break;
+        case 1: return launch_bf16<HD, 1>(a, grid, s);
+        case 2: return launch_bf16<HD, 2>(a, grid, s);
+        case 4: return launch_bf16<HD, 4>(a, grid, s);
+        case 8: return launch_bf16<HD, 8>(a, grid, s);
+        case 16: return launch_bf16<HD, 16>(a, grid, s);
         default: return hipErrorInvalidValue;
         }
     } else {
+        const dim3 block(64 * kWaves);
         switch (a.g.G) {
         case 1: hipLaunchKernelGGL((k_decode_generic<HD, 1, BF>), grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((k_decode_generic<HD, 2, BF>), grid, block, 0, s, a); break;
@@ -547,7 +967,26 @@ hipError_t launch_g(const DecodeArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int HD>
+int wgs_per_cu_g(int G)
+{
+    switch (G) {
+    case 1: return bf16_wgs_per_cu<HD, 1>();
+    case 2: return bf16_wgs_per_cu<HD, 2>();
+    case 4: return bf16_wgs_per_cu<HD, 4>();
+    case 8: return bf16_wgs_per_cu<HD, 8>();
+    case 16: return bf16_wgs_per_cu<HD, 16>();
+    default: return 1;
+    }
+}
+
 }  // namespace
+
+int decode_wgs_per_cu(int hd, int G, int dtype)
+{
+    if (dtype != 1) return 2;  // the fp32 kernel: 4 waves, two workgroups per CU
+    return hd == 128 ? wgs_per_cu_g<128>(G) : wgs_per_cu_g<64>(G);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s)
 {

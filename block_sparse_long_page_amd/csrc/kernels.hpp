@@ -76,6 +76,8 @@ struct CombineArgs {
 hipError_t launch_page_meta(const MetaArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// resident decode workgroups per CU for this shape (occupancy query)
+int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace sa

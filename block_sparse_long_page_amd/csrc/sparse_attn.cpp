@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/sparse_attn.h"
 #include "kernels.hpp"
 
@@ -48,6 +50,8 @@ int check_kv(const sa_kv_desc* kv, sa::Geometry* g)
     if (kv->page_size > 16384) return SA_ERR_UNSUPPORTED;
     if ((long)kv->max_seq_len > (long)kv->max_pages_per_seq * kv->page_size) return SA_ERR_INVALID_ARG;
     if ((long)kv->max_pages_per_seq * kv->page_size >= (1l << 30)) return SA_ERR_UNSUPPORTED;
+    // K/V rows are indexed with 32-bit integers
+    if ((long)kv->num_phys_pages * kv->num_kv_heads * kv->page_size >= (1l << 31)) return SA_ERR_UNSUPPORTED;
     if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens) return SA_ERR_INVALID_ARG;
     if (kv->dtype != SA_F32 && kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
     if (kv->head_dim != 64 && kv->head_dim != 128) return SA_ERR_UNSUPPORTED;
@@ -58,6 +62,22 @@ int check_kv(const sa_kv_desc* kv, sa::Geometry* g)
                       kv->max_pages_per_seq, kv->num_phys_pages, kv->dtype, kv->k_cache, kv->v_cache,
                       kv->block_table, kv->seq_lens, pd};
     return SA_OK;
+}
+
+// resident decode workgroups per CU, queried once per kernel shape
+int occupancy(int hd, int G, int dtype)
+{
+    static std::atomic<int> cache[2][2][5];
+    if ((hd != 64 && hd != 128) || (dtype != SA_F32 && dtype != SA_BF16) || !pow2_group(G)) return 1;
+    int gi = 0;
+    while ((1 << gi) < G) ++gi;
+    std::atomic<int>& c = cache[hd == 128][dtype == SA_BF16][gi];
+    int v = c.load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = sa::decode_wgs_per_cu(hd, G, dtype);
+        c.store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
@@ -134,8 +154,15 @@ int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int
                 (long)(k_max < 0 ? 0 : k_max) * kv->page_size;
     if (ntok > L) ntok = L;
     const long problems = (long)kv->batch * kv->num_kv_heads * num_q_rows;
-    // about 1024 workgroups (4 per CU on 256 CUs), at least 256 tokens each
-    long s = (1024 + problems - 1) / problems;
+    // one round of workgroups over the device: CUs x resident workgroups per CU,
+    // with at least 256 tokens per workgroup
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int G = kv->num_kv_heads > 0 ? kv->num_q_heads / kv->num_kv_heads : 1;
+    const long slots = (long)cus * occupancy(kv->head_dim, G, kv->dtype);
+    long s = (slots + problems - 1) / problems;
     const long by_tokens = ntok / 256 > 0 ? ntok / 256 : 1;
     if (s > by_tokens) s = by_tokens;
     if (s < 1) s = 1;

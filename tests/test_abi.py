@@ -166,7 +166,7 @@ def test_default_splits_fill_the_gpu():
     d = _desc(batch=4, num_q_heads=64, num_kv_heads=8, page_size=64, max_pages_per_seq=2048,
               num_phys_pages=8192, max_seq_len=131072)
     s = lib.sparse_attn_default_splits(ctypes.byref(d), 1, 256, 4096, 128)
-    assert 16 <= s <= 64
+    assert 8 <= s <= 64  # about one round of workgroups over the CUs
     tiny = _desc(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, max_pages_per_seq=128, max_seq_len=2048)
     assert lib.sparse_attn_default_splits(ctypes.byref(tiny), 1, 16, 64, 8) >= 1
 
