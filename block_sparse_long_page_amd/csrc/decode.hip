@@ -26,14 +26,14 @@ namespace sa {
 
 namespace {
 
-#ifndef SA_DECODE_U
-#define SA_DECODE_U 4
-#endif
 #ifndef SA_MFMA_TPS
 #define SA_MFMA_TPS 1
 #endif
-#ifndef SA_DECODE_VALU
-#define SA_DECODE_VALU 0
+#ifndef SA_MFMA_NW
+#define SA_MFMA_NW 8
+#endif
+#ifndef SA_MFMA_MINB
+#define SA_MFMA_MINB 1
 #endif
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
@@ -225,383 +225,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_generic(DecodeArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 kernel.  One workgroup of NW waves per (sequence, KV head, query row,
-// split).  The split's tokens are taken in rounds of NW wave steps (wave w
-// takes the w-th step of each round) and the waves advance in lockstep.  NW is
-// 8 where the LDS of one workgroup allows it, so that one workgroup fills a
-// CU: the waves sharing a CU then belong to one workgroup and finish
-// together, instead of a second workgroup trailing the first.
-//  * prologue: the sequence length, the selected-page count and the whole
-//    page list (into LDS) are loaded in one round; the workgroup then resolves
-//    the row index ((phys * Hkv + kvh) * P + offset) of up to 2048 tokens into
-//    LDS with all block-table loads in flight together, so the K/V loads of
-//    the main loop never wait on the page list or the block table;
-//  * main loop: K/V rows double-buffered in registers (the next U token steps
-//    are in flight while the current ones are computed);
-//  * q.k: packed bf16 dot products, then the partial sums of the LPT lanes of
-//    a token are transposed through LDS (or reduce-scattered with DPP) so that
-//    each lane holds the full logit of its own head(s): the exponentials are
-//    computed once per (token, head);
-//  * p.v: the weights of two tokens are packed as a bf16 pair, broadcast from
-//    the lane holding each head, and accumulated with dot2 into fp32;
-//  * epilogue: the token groups of a wave fold with lane swaps, the waves
-//    through LDS; the workgroup writes its normalised partial and (m, l).
-// ---------------------------------------------------------------------------
-
 constexpr int kSelCap = 1024;  // page-list entries staged in LDS; longer lists are read in place
 constexpr int kRowsWG = 2048;  // rows resolved per workgroup per prologue round
-
-template <int HD, int G>
-struct Bf16Plan {
-    static constexpr int CH = 8;                     // bf16 channels per lane (one 16-byte load)
-    static constexpr int LPT = HD / CH;              // lanes per token: 16 (hd 128) or 8 (hd 64)
-    static constexpr int TPW = 64 / LPT;             // tokens per wave load
-    static constexpr int U = HD == 64 ? 2 : SA_DECODE_U;  // loads per buffer (even): 16 tokens per wave step
-    static constexpr bool XPOSE = G <= LPT;          // q.k sums transposed through LDS
-    static constexpr int XSTRIDE = G * LPT + LPT;    // padded so the writes avoid bank conflicts
-    static constexpr int xfloats(int nw) { return XPOSE ? nw * U * TPW * XSTRIDE : 4; }
-    static constexpr int ofloats(int nw) { return nw * G * HD; }
-    static constexpr int smem_floats(int nw) { return xfloats(nw) > ofloats(nw) ? xfloats(nw) : ofloats(nw); }
-    static constexpr int lds_bytes(int nw)
-    {
-        return 4 * (smem_floats(nw) + kSelCap + kRowsWG + 2 * nw * G);
-    }
-    static constexpr int NW = lds_bytes(8) <= 96 * 1024 ? 8 : 4;
-};
-
-template <int HD, int G>
-__global__ __launch_bounds__((64 * Bf16Plan<HD, G>::NW)) void k_decode_bf16(DecodeArgs a)
-{
-    using Plan = Bf16Plan<HD, G>;
-    constexpr int NW = Plan::NW, CH = Plan::CH, LPT = Plan::LPT, TPW = Plan::TPW, U = Plan::U;
-    constexpr int HPL = G > LPT ? G / LPT : 1;  // heads held per lane after the reduce-scatter
-    constexpr int DUP = G < LPT ? LPT / G : 1;  // lanes holding the same head
-    constexpr bool XPOSE = Plan::XPOSE;
-    constexpr int XSTRIDE = Plan::XSTRIDE;
-    static_assert(U % 2 == 0, "tokens are paired for dot2");
-    const Geometry& g = a.g;
-
-    __shared__ int sel_lds[kSelCap];
-    __shared__ __attribute__((aligned(16))) int rows_lds[kRowsWG];
-    __shared__ float4 smem4[Plan::smem_floats(NW) / 4];  // transpose area, then the waves' outputs
-    __shared__ float wv_m[NW][G], wv_l[NW][G];
-    float* const xsum = (float*)smem4;
-    float4 (*const wv_o)[G][HD / 4] = (float4(*)[G][HD / 4])smem4;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane % LPT, tg = lane / LPT;
-    const int head0 = (sub / DUP) * HPL;  // first head this lane holds after the reduce-scatter
-
-    int bid = blockIdx.x;
-    const int split = bid % a.splits;
-    bid /= a.splits;
-    const int kvh = bid % g.Hkv;
-    bid /= g.Hkv;
-    const int row = bid % a.Q;
-    const int b = bid / a.Q;
-    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
-
-    // one round of loads: length, count, page list, the group's queries
-    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
-    const int count = a.sel ? a.count[prob] : 0;
-    const int32_t* sel_g = a.sel ? a.sel + prob * a.k_max : nullptr;
-    const bool staged = sel_g != nullptr && a.k_max <= kSelCap;
-    if (staged)
-        for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_lds[i] = sel_g[i];
-    uint32_t qw[G][4];
-    for (int h = 0; h < G; ++h) {
-        const uint4 w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD +
-                                        sub * CH);
-        qw[h][0] = w.x;
-        qw[h][1] = w.y;
-        qw[h][2] = w.z;
-        qw[h][3] = w.w;
-    }
-    __syncthreads();
-
-    const int pos = L - a.Q + row;
-    TokenSet ts;
-    ts.init(L, a.S, a.W, g.P, staged ? (const int32_t*)sel_lds : sel_g, count, a.k_max, a.parts);
-    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
-
-    const int n = ts.total;
-    const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
-    const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
-
-    float m_all[G], o[G][CH];
-    float m_own[HPL], l_own[HPL];
-    for (int h = 0; h < G; ++h) {
-        m_all[h] = -INFINITY;
-        for (int c = 0; c < CH; ++c) o[h][c] = 0.f;
-    }
-    for (int j = 0; j < HPL; ++j) {
-        m_own[j] = -INFINITY;
-        l_own[j] = 0.f;
-    }
-
-    const uint16_t* kbase = (const uint16_t*)g.k + sub * CH;
-    const uint16_t* vbase = (const uint16_t*)g.v + sub * CH;
-    const int32_t* bt = g.block_table + (long)b * g.max_pages;
-    const int hkvP = g.Hkv * g.P;
-    // logits are kept as raw q.k; the softmax scale (times log2 e) is applied
-    // inside the exponentials, and the rescale slack is 2^8 in weight
-    const float sl2 = a.scale_log2;
-    const float slack = kRescaleSlack / sl2;
-
-    constexpr int TS = TPW * U;  // tokens per wave step
-    constexpr int RT = NW * TS;  // tokens per round: wave w takes the w-th step of every round
-    constexpr int PER_T = kRowsWG / (64 * NW);
-    static_assert(kRowsWG % RT == 0 && kRowsWG % (64 * NW) == 0, "rounds tile the row chunk");
-
-    for (int cb = f0; cb < f1; cb += kRowsWG) {
-        const int ce = imin(f1, cb + kRowsWG);
-        // the workgroup resolves the chunk's rows, every block-table load in flight together
-        __syncthreads();  // the previous chunk's rows are no longer read
-        {
-            int tok[PER_T], phys[PER_T];
-#pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int f = cb + i * 64 * NW + (int)threadIdx.x;
-                int t = f < ce ? ts.position(f, pdiv) : -1;
-                if (t > pos) t = -1;
-                tok[i] = t;
-                phys[i] = t >= 0 ? bt[pdiv.div(t)] : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int t = tok[i];
-                int ri = -1;
-                if (t >= 0 && phys[i] >= 0 && phys[i] < g.num_phys) {
-                    const int pg = pdiv.div(t);
-                    ri = phys[i] * hkvP + kvh * g.P + (t - pg * g.P);
-                }
-                rows_lds[i * 64 * NW + threadIdx.x] = ri;
-            }
-        }
-        __syncthreads();
-
-        const int nr = (ce - cb + RT - 1) / RT;  // rounds in this chunk, the same for every wave
-
-        // Rows of tokens that are not attended are not loaded: their
-        // registers keep earlier (finite) data, and their weight is 0.
-        auto load = [&](int r, uint4(&kw)[U], uint4(&vw)[U], int(&ri)[U]) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = r * RT + wave * TS + u * TPW + tg;
-                ri[u] = cb + j < ce ? rows_lds[j] : -1;
-                if (ri[u] >= 0) {
-                    kw[u] = *(const uint4*)(kbase + (long)ri[u] * HD);
-                    vw[u] = *(const uint4*)(vbase + (long)ri[u] * HD);
-                }
-            }
-        };
-
-        auto compute = [&](const uint4(&kw)[U], const uint4(&vw)[U], const int(&ri)[U]) {
-            float z[U][HPL];
-            if constexpr (XPOSE) {
-                // each lane writes its partial sums [head][lane-in-group]; the DUP
-                // lanes holding a head then add that head's row and share the total
-                constexpr int PER = LPT / DUP;  // partials each of them adds
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t* k32 = (const uint32_t*)&kw[u];
-                    float* xs = xsum + ((wave * U + u) * TPW + tg) * XSTRIDE;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        float acc = 0.f;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[h][j], k32[j], acc);
-                        xs[h * LPT + sub] = acc;
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float* xs = xsum + ((wave * U + u) * TPW + tg) * XSTRIDE + head0 * LPT + (sub % DUP) * PER;
-                    float acc = 0.f;
-                    if constexpr (PER % 4 == 0) {
-#pragma unroll
-                        for (int v = 0; v < PER; v += 4) {
-                            const float4 t = *(const float4*)(xs + v);
-                            acc += (t.x + t.y) + (t.z + t.w);
-                        }
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < PER; ++v) acc += xs[v];
-                    }
-                    acc = group_sum<DUP>(acc);
-                    z[u][0] = ri[u] >= 0 ? acc : -INFINITY;  // unscaled q.k
-                }
-                __builtin_amdgcn_wave_barrier();
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t* k32 = (const uint32_t*)&kw[u];
-                    float d[G];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        float acc = 0.f;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc = dot2_bf16(qw[h][j], k32[j], acc);
-                        d[h] = acc;
-                    }
-                    reduce_scatter<G, log2c<LPT>() - 1>(d, lane);
-#pragma unroll
-                    for (int j = 0; j < HPL; ++j) z[u][j] = ri[u] >= 0 ? d[j] : -INFINITY;  // unscaled q.k
-                }
-            }
-            // reference maximum (unscaled q.k units): rescale only when a logit
-            // passes it by more than the slack
-            bool need = false;
-            float mx[HPL];
-#pragma unroll
-            for (int j = 0; j < HPL; ++j) {
-                mx[j] = z[0][j];
-#pragma unroll
-                for (int u = 1; u < U; ++u) mx[j] = fmaxf(mx[j], z[u][j]);
-                need |= mx[j] > m_own[j] + slack;
-            }
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                static_for<0, G>([&](auto hc) {
-                    constexpr int h = decltype(hc)::value;
-                    const float mh = group_bcast<LPT, (h / HPL) * DUP>(mx[h % HPL], lane);
-                    if (mh > m_all[h] + slack) {
-                        const float alpha = __builtin_amdgcn_exp2f((m_all[h] - mh) * sl2);  // 0 while m = -inf
-#pragma unroll
-                        for (int c = 0; c < CH; ++c) o[h][c] *= alpha;
-#pragma unroll
-                        for (int j = 0; j < HPL; ++j)
-                            if (head0 + j == h) {
-                                l_own[j] *= alpha;
-                                m_own[j] = mh;
-                            }
-                        m_all[h] = mh;
-                    }
-                });
-            }
-            float p[U][HPL];
-#pragma unroll
-            for (int j = 0; j < HPL; ++j) {
-                const float mref = m_own[j] == -INFINITY ? 0.f : -m_own[j] * sl2;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    p[u][j] = __builtin_amdgcn_exp2f(fmaf(z[u][j], sl2, mref));  // -inf -> 0
-                    l_own[j] += p[u][j];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; u += 2) {
-                const uint32_t* va = (const uint32_t*)&vw[u];
-                const uint32_t* vb = (const uint32_t*)&vw[u + 1];
-                uint32_t vv[CH];  // channel c of tokens u and u+1 as a bf16 pair
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    vv[2 * j] = __builtin_amdgcn_perm(vb[j], va[j], 0x05040100u);      // low halves
-                    vv[2 * j + 1] = __builtin_amdgcn_perm(vb[j], va[j], 0x07060302u);  // high halves
-                }
-                float pk[HPL];
-#pragma unroll
-                for (int j = 0; j < HPL; ++j) pk[j] = __uint_as_float(pack_bf16(p[u][j], p[u + 1][j]));
-                static_for<0, G>([&](auto hc) {
-                    constexpr int h = decltype(hc)::value;
-                    const uint32_t pp = __float_as_uint(group_bcast<LPT, (h / HPL) * DUP>(pk[h % HPL], lane));
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) o[h][c] = dot2_bf16(pp, vv[c], o[h][c]);
-                });
-            }
-        };
-
-        uint4 ka[U], va[U], kb[U], vb[U];
-        int ra[U], rb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) ka[u] = va[u] = kb[u] = vb[u] = make_uint4(0, 0, 0, 0);
-        // The waves of the workgroup advance in lockstep, one barrier per
-        // round: wave scheduling favours the oldest waves, and without the
-        // barrier the last waves of a CU would finish their share alone.
-        auto busy = [&](int r) { return cb + r * RT + wave * TS < ce; };
-        load(0, ka, va, ra);
-        for (int r = 0; r < nr; r += 2) {
-            if (r + 1 < nr) load(r + 1, kb, vb, rb);
-            if (busy(r)) compute(ka, va, ra);
-            __builtin_amdgcn_s_barrier();
-            if (r + 1 >= nr) break;
-            if (r + 2 < nr) load(r + 2, ka, va, ra);
-            if (busy(r + 1)) compute(kb, vb, rb);
-            __builtin_amdgcn_s_barrier();
-        }
-    }
-
-    // Fold the TPW token groups of the wave (lanes sub, sub + LPT, ...): the
-    // partner lane holds the same channels and heads of another group.
-    static_for<0, log2c<TPW>()>([&](auto ic) {
-        constexpr int OFF = LPT << decltype(ic)::value;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float m1 = m_all[h], m2 = xor_lanes<OFF>(m1);
-            const float mn = fmaxf(m1, m2);
-            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * sl2);
-            const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
-#pragma unroll
-            for (int c = 0; c < CH; ++c) o[h][c] = fmaf(o[h][c], a1, xor_lanes<OFF>(o[h][c]) * a2);
-            m_all[h] = mn;
-        }
-#pragma unroll
-        for (int j = 0; j < HPL; ++j) {
-            const float m1 = m_own[j], m2 = xor_lanes<OFF>(m1);
-            const float l2 = xor_lanes<OFF>(l_own[j]);
-            const float mn = fmaxf(m1, m2);
-            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * sl2);
-            const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
-            l_own[j] = fmaf(l_own[j], a1, l2 * a2);
-            m_own[j] = mn;
-        }
-    });
-
-    // The waves' states go to LDS (the output area reuses the transpose area,
-    // so every wave first leaves its loop); the workgroup merges them with one
-    // exponential per (wave, head) and writes the split's partial.
-    __syncthreads();
-    if (tg == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            wv_o[wave][h][sub * 2] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-            wv_o[wave][h][sub * 2 + 1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
-        }
-#pragma unroll
-        for (int j = 0; j < HPL; ++j)
-            if (sub % DUP == 0) {
-                wv_m[wave][head0 + j] = m_own[j] * sl2;  // -inf stays -inf
-                wv_l[wave][head0 + j] = l_own[j];
-            }
-    }
-    __syncthreads();
-
-    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
-        const int h = i / (HD / 4), c4 = i % (HD / 4);
-        float ms = -INFINITY;
-        for (int w = 0; w < NW; ++w) ms = fmaxf(ms, wv_m[w][h]);
-        float ls = 0.f;
-        float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int w = 0; w < NW; ++w) {
-            const float mw = wv_m[w][h];
-            const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
-            ls = fmaf(wv_l[w][h], wt, ls);
-            const float4 ow = wv_o[w][h][c4];
-            os.x = fmaf(ow.x, wt, os.x);
-            os.y = fmaf(ow.y, wt, os.y);
-            os.z = fmaf(ow.z, wt, os.z);
-            os.w = fmaf(ow.w, wt, os.w);
-        }
-        const float inv = ls > 0.f ? 1.0f / ls : 0.f;
-        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
-        *(float4*)(a.part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
-        if (c4 == 0) {
-            a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
-            a.part_ml[prow * 2 + 1] = ls;
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // bf16 kernel on the matrix cores.  The G query heads of a KV group against a
@@ -636,7 +261,7 @@ struct MfmaPlan {
     static constexpr int VROW = HD * 2;                // bytes per value row
     static constexpr int VTILE = 16 * VROW + 4 * 32;   // LDS bytes of one value tile (padded)
     static constexpr int TPS = SA_MFMA_TPS;            // tiles per pipeline step
-    static constexpr int NW = 8;
+    static constexpr int NW = SA_MFMA_NW;
     static constexpr int vbytes(int nw) { return nw * TPS * VTILE; }
     static constexpr int obytes(int nw) { return nw * G * HD * 4; }
     static constexpr int smem_bytes(int nw) { return vbytes(nw) > obytes(nw) ? vbytes(nw) : obytes(nw); }
@@ -650,7 +275,7 @@ __device__ __forceinline__ int vt_off(int t, int b)
 }
 
 template <int HD, int G>
-__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(DecodeArgs a)
+__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_decode_mfma(DecodeArgs a)
 {
     using Plan = MfmaPlan<HD, G>;
     constexpr int NW = Plan::NW, KK = Plan::KK, NB = Plan::NB, VLD = Plan::VLD, LPT = Plan::LPT;
@@ -678,13 +303,14 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
     const int b = bid / a.Q;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
 
-    // one round of loads: length, count, page list, the group's queries
+    // one round of loads: length, count, page list, block-table row, the group's queries
     const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
     const int count = a.sel ? a.count[prob] : 0;
     const int32_t* sel_g = a.sel ? a.sel + prob * a.k_max : nullptr;
     const bool staged = sel_g != nullptr && a.k_max <= kSelCap;
     if (staged)
         for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_lds[i] = sel_g[i];
+    const int32_t* const bt = g.block_table + (long)b * g.max_pages;
     // B operand of q.k: head r, channels 32 kk + 8 j .. + 8
     uint4 qb[KK];
     for (int kk = 0; kk < KK; ++kk) {
@@ -696,12 +322,16 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
     __syncthreads();
 
     const int pos = L - a.Q + row;
-    TokenSet ts;
-    ts.init(L, a.S, a.W, g.P, staged ? (const int32_t*)sel_lds : sel_g, count, a.k_max, a.parts);
+    // the token map reads the page list from LDS when it is staged there
+    TokenSetLds tsl;
+    TokenSet tsg;
+    tsl.init(L, a.S, a.W, g.P, (lds_i32_ptr)sel_lds, staged ? count : 0, a.k_max, a.parts);
+    tsg.init(L, a.S, a.W, g.P, staged ? nullptr : sel_g, count, a.k_max, a.parts);
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
-    const int n = ts.total;
+    const int n = staged ? tsl.total : tsg.total;
     const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
     const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
+    auto position = [&](int f) { return staged ? tsl.position(f, pdiv) : tsg.position(f, pdiv); };
 
     const float sl2 = a.scale_log2;
     const float slack = kRescaleSlack / sl2;
@@ -712,7 +342,6 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
 
     const uint16_t* kbase = (const uint16_t*)g.k;
     const uint16_t* vbase = (const uint16_t*)g.v;
-    const int32_t* bt = g.block_table + (long)b * g.max_pages;
     const int hkvP = g.Hkv * g.P;
     unsigned char* const vt = smem + wave * TPS * VTILE;  // this wave's value tiles
 
@@ -728,7 +357,7 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
                 const int f = cb + i * 64 * NW + (int)threadIdx.x;
-                int t = f < ce ? ts.position(f, pdiv) : -1;
+                int t = f < ce ? position(f) : -1;
                 if (t > pos) t = -1;
                 tok[i] = t;
                 phys[i] = t >= 0 ? bt[pdiv.div(t)] : -1;
@@ -905,24 +534,6 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
     }
 }
 
-#if SA_DECODE_VALU
-template <int HD, int G>
-hipError_t launch_bf16(const DecodeArgs& a, dim3 grid, hipStream_t s)
-{
-    hipLaunchKernelGGL((k_decode_bf16<HD, G>), grid, dim3(64 * Bf16Plan<HD, G>::NW), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int HD, int G>
-int bf16_wgs_per_cu()
-{
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_bf16<HD, G>, 64 * Bf16Plan<HD, G>::NW, 0) !=
-        hipSuccess)
-        return 1;
-    return n > 0 ? n : 1;
-}
-#else
 template <int HD, int G>
 hipError_t launch_bf16(const DecodeArgs& a, dim3 grid, hipStream_t s)
 {
@@ -939,7 +550,6 @@ int bf16_wgs_per_cu()
         return 1;
     return n > 0 ? n : 1;
 }
-#endif
 
 template <int HD, bool BF>
 hipError_t launch_g(const DecodeArgs& a, dim3 grid, hipStream_t s)

@@ -226,7 +226,8 @@ struct FastDiv {
 // f in [0, total) maps to a position.  Only the first and the last selected
 // page can be cut by the region edges; interior candidates are whole pages.
 // `parts` keeps the sink and window (bit 0) and/or the middle (bit 1).
-struct TokenSet {
+template <typename SelPtr>
+struct TokenSetT {
     int L, se, ws, P;
     int nsel;         // selected pages in use; -1 means every middle page (dense)
     int first_start;  // position of the first middle token of sel[0]
@@ -234,9 +235,9 @@ struct TokenSet {
     int mid_total;    // middle tokens attended
     int n_sink, n_mid;
     int total;
-    const int32_t* sel;
+    SelPtr sel;
 
-    __device__ __forceinline__ void init(int L_, int S, int W, int P_, const int32_t* sel_, int count, int k_max,
+    __device__ __forceinline__ void init(int L_, int S, int W, int P_, SelPtr sel_, int count, int k_max,
                                          int parts)
     {
         L = L_;
@@ -292,5 +293,9 @@ struct TokenSet {
         return (t >= se && t < ws) ? t : -1;
     }
 };
+
+typedef const __attribute__((address_space(3))) int32_t* lds_i32_ptr;
+using TokenSet = TokenSetT<const int32_t*>;       // page list in global memory
+using TokenSetLds = TokenSetT<lds_i32_ptr>;       // page list staged in LDS
 
 }  // namespace sa

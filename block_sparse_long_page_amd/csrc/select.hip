@@ -162,6 +162,106 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     }
 }
 
+// Quest scores of bf16 summaries on the matrix cores.  With q+ = max(q, 0) and
+// q- = min(q, 0), max(q_c mx_c, q_c mn_c) = q+_c mx_c + q-_c mn_c term by term,
+// so the bounds of 16 pages for the G heads are one product of the pages'
+// summary rows [mn | mx] (A: row = page, 8 elements per lane straight from
+// global memory) with the heads' [q- | q+] (B: column = head; heads past G are
+// zero), over K = 2 * head_dim.  Lane (r, j) = (lane % 16, lane / 16) then
+// holds head r's bounds of pages 4j .. 4j+3; the group maximum is a DPP max
+// over the 16 lanes of its row.  Each wave scores TW tiles of 16 pages with
+// every summary load issued up front.
+typedef __bf16 sbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float sf32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef SA_SCORE_TW
+#define SA_SCORE_TW 2
+#endif
+
+template <int HD, int G>
+__global__ __launch_bounds__(64 * kScoreWaves) void k_score_quest_mfma(SelectArgs a)
+{
+    constexpr int KQ = HD / 32;        // 32-channel groups per summary row half
+    constexpr int KS = 2 * KQ;         // products per tile (mn half, then mx half)
+    constexpr int TW = SA_SCORE_TW;    // tiles per wave
+    constexpr int PAGES_PER_WG = 16 * TW * kScoreWaves;
+    static_assert(G <= 16, "one MFMA column per head");
+    const Geometry& g = a.g;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, j = lane >> 4;
+
+    int pid = blockIdx.y;
+    const int row = pid % a.Q;
+    pid /= a.Q;
+    const int kvh = pid % g.Hkv;
+    const int b = pid / g.Hkv;
+
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int se = imin(a.S, L), ws = imax(se, L - a.W);
+    if (ws <= se) return;
+    const int plo = se / g.P, phi = (ws - 1) / g.P;
+    const int first = plo + blockIdx.x * PAGES_PER_WG + wave * 16 * TW;
+    if (first > phi) return;
+
+    // A: summary rows of this wave's pages, all in flight at once
+    const long meta_row = ((long)b * g.Hkv + kvh) * g.max_pages;
+    const uint16_t* meta = (const uint16_t*)a.meta;
+    uint4 am[TW][KS];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const int p = first + 16 * t + r;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            am[t][s] = make_uint4(0, 0, 0, 0);
+            if (p <= phi) am[t][s] = *(const uint4*)(meta + (meta_row + p) * 2 * HD + 32 * s + 8 * j);
+        }
+    }
+    // block-table entries of pages 4j .. 4j+3 of each tile (unmapped pages score -inf)
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
+    int ph[TW][4];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = first + 16 * t + 4 * j + i;
+            ph[t][i] = p <= phi ? bt[p] : -1;
+        }
+    // B: head r's q- (for the mn half) and q+ (for the mx half), 8 channels per lane
+    uint4 qn[KQ], qp[KQ];
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (r < G) w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + r) * a.Q + row) * HD +
+                                       32 * s + 8 * j);
+        uint32_t* wn = (uint32_t*)&qn[s];
+        uint32_t* wp = (uint32_t*)&qp[s];
+        const uint32_t* ww = (const uint32_t*)&w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t neg = ((ww[e] >> 15) & 1u) * 0xffffu | ((ww[e] >> 31) & 1u) * 0xffff0000u;
+            wn[e] = ww[e] & neg;
+            wp[e] = ww[e] & ~neg;
+        }
+    }
+
+    float* out = a.scores + (((long)b * g.Hkv + kvh) * a.Q + row) * g.max_pages;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        sf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sbf16x8_t, am[t][s]),
+                                                          __builtin_bit_cast(sbf16x8_t, s < KQ ? qn[s] : qp[s - KQ]),
+                                                          acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float best = group_max<16>(r < G ? acc[i] : -INFINITY);
+            const int p = first + 16 * t + 4 * j + i;
+            if (r == 0 && p <= phi) out[p] = ph[t][i] >= 0 && ph[t][i] < g.num_phys ? best : -INFINITY;
+        }
+    }
+}
+
 // order-preserving float -> uint32 (larger float, larger key); -0 maps to +0
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -176,6 +276,34 @@ constexpr int kTopkMaxRounds = 24;  // keys per thread: up to 12288 candidate pa
 __device__ __forceinline__ int lanes_below(uint64_t m)
 {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+constexpr int kCntChunks = (kTopkMaxRounds * (kTopkThreads / 64) + 63) / 64;
+
+// Exclusive prefix sums of cnt[0 .. n) held across the wave: entry e's prefix
+// is lane e % 64 of ex[e / 64].
+__device__ __forceinline__ void scan_counts(const int* cnt, int n, int lane, int (&ex)[kCntChunks])
+{
+    int carry = 0;
+#pragma unroll
+    for (int c = 0; c < kCntChunks; ++c) {
+        const int e = c * 64 + lane;
+        const int v = e < n ? cnt[e] : 0;
+        const int inc = wave_inclusive_scan(v);
+        ex[c] = inc - v + carry;
+        carry += __builtin_amdgcn_readlane(inc, 63);
+    }
+}
+
+// the prefix of entry e (wave-uniform)
+__device__ __forceinline__ int pick_count(const int (&ex)[kCntChunks], int e)
+{
+    const int c = e >> 6, l = e & 63;
+    int v = __builtin_amdgcn_readlane(ex[0], l);
+#pragma unroll
+    for (int i = 1; i < kCntChunks; ++i)
+        if (c == i) v = __builtin_amdgcn_readlane(ex[i], l);
+    return v;
 }
 
 // One workgroup per (sequence, KV head, row); the order keys of the n
@@ -197,8 +325,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
     extern __shared__ uint32_t keys[];  // [n]
     __shared__ int hist[kPasses][256];
     __shared__ uint32_t mm[NW][2];
-    __shared__ int cnt_eq[NW][kTopkMaxRounds];
-    __shared__ int cnt_in[NW][kTopkMaxRounds];
+    __shared__ int cnt_eq[kTopkMaxRounds * NW];  // round-major: flat (round, wave) order is page order
+    __shared__ int cnt_in[kTopkMaxRounds * NW];
     __shared__ int gts[NW];
     const Geometry& g = a.g;
     int pid = blockIdx.x;
@@ -227,11 +355,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
     const int rounds = (n + kTopkThreads - 1) / kTopkThreads;  // <= kTopkMaxRounds (host-checked)
     const float* sc = a.scores + prob * g.max_pages + plo;
     uint32_t lo = 0xffffffffu, hi = 0;
-    for (int i = tid; i < n; i += kTopkThreads) {
-        const uint32_t key = order_key(sc[i]);
-        keys[i] = key;
-        lo = min(lo, key);
-        hi = max(hi, key);
+    for (int base = 0; base < n; base += 4 * kTopkThreads) {
+        float v[4];  // four loads in flight per thread
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kTopkThreads + tid;
+            v[u] = i < n ? sc[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kTopkThreads + tid;
+            if (i < n) {
+                const uint32_t key = order_key(v[u]);
+                keys[i] = key;
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+        }
     }
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
@@ -256,6 +396,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
             const uint32_t dmask = (1u << width) - 1u;
             const int up = shift + width;  // bits >= up are decided
             const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
+#pragma unroll 4
             for (int i = tid; i < n; i += kTopkThreads) {
                 const uint32_t key = keys[i];
                 if ((key & hmask) == prefix) atomicAdd(&hist[pass][(key >> shift) & dmask], 1);
@@ -292,45 +433,48 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
 
     // per-wave counts of keys equal to kth and above it, round by round
     int gt_local = 0;
+#pragma unroll 4
     for (int r = 0; r < rounds; ++r) {
         const int i = r * kTopkThreads + tid;
         const uint32_t key = i < n ? keys[i] : 0u;
         const int ne = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key == kth));
         gt_local += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key > kth));
-        if (lane == 0) cnt_eq[wave][r] = ne;
+        if (lane == 0) cnt_eq[r * NW + wave] = ne;
     }
     if (lane == 0) gts[wave] = gt_local;
     __syncthreads();
     int gt = 0;
+#pragma unroll
     for (int w = 0; w < NW; ++w) gt += gts[w];
     const int need = k - gt;  // equal keys to take, lowest pages first
+    const int ncnt = rounds * NW;
 
     // chosen: above kth, or equal to it and among the first `need` equal keys
-    // in page order (round, wave, lane)
-    int eq_base = 0;
+    // in page order (round, wave, lane); the rank of a wave's first equal key
+    // is the exclusive prefix of the counts in (round, wave) order
+    int ex[kCntChunks];
+    scan_counts(cnt_eq, ncnt, lane, ex);
     uint32_t mine = 0;  // bit r: this thread's key of round r is chosen
+#pragma unroll 4
     for (int r = 0; r < rounds; ++r) {
         const int i = r * kTopkThreads + tid;
         const uint32_t key = i < n ? keys[i] : 0u;
         const bool eq = i < n && key == kth;
-        int rank = eq_base;
-        for (int w = 0; w < wave; ++w) rank += cnt_eq[w][r];
+        const int rank = pick_count(ex, r * NW + wave);
         const bool in = i < n && (key > kth || (eq && rank + lanes_below(__builtin_amdgcn_ballot_w64(eq)) < need));
         const int cc = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
-        if (lane == 0) cnt_in[wave][r] = cc;
-        for (int w = 0; w < NW; ++w) eq_base += cnt_eq[w][r];
+        if (lane == 0) cnt_in[r * NW + wave] = cc;
         mine |= (uint32_t)in << r;
     }
     __syncthreads();
-    int out_base = 0;
+    int ox[kCntChunks];
+    scan_counts(cnt_in, ncnt, lane, ox);
     for (int r = 0; r < rounds; ++r) {
         const int i = r * kTopkThreads + tid;
         const bool in = (mine >> r) & 1u;
         const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
-        int here = out_base;
-        for (int w = 0; w < wave; ++w) here += cnt_in[w][r];
+        const int here = pick_count(ox, r * NW + wave);
         if (in) sel[here + lanes_below(inm)] = plo + i;
-        for (int w = 0; w < NW; ++w) out_base += cnt_in[w][r];
     }
 }
 
@@ -342,6 +486,28 @@ hipError_t launch_score_mode(const SelectArgs& a, dim3 grid, hipStream_t s)
     else
         hipLaunchKernelGGL((k_score<HD, G, BF, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
     return hipGetLastError();
+}
+
+template <int HD, int G>
+hipError_t launch_score_quest_bf16(const SelectArgs& a, hipStream_t s)
+{
+    constexpr int per_wg = 16 * SA_SCORE_TW * kScoreWaves;
+    const dim3 grid((unsigned)((a.g.max_pages + per_wg - 1) / per_wg), (unsigned)(a.g.B * a.g.Hkv * a.Q));
+    hipLaunchKernelGGL((k_score_quest_mfma<HD, G>), grid, dim3(64 * kScoreWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_score_quest_bf16_g(const SelectArgs& a, hipStream_t s)
+{
+    switch (a.g.G) {
+    case 1: return launch_score_quest_bf16<HD, 1>(a, s);
+    case 2: return launch_score_quest_bf16<HD, 2>(a, s);
+    case 4: return launch_score_quest_bf16<HD, 4>(a, s);
+    case 8: return launch_score_quest_bf16<HD, 8>(a, s);
+    case 16: return launch_score_quest_bf16<HD, 16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int HD, bool BF>
@@ -363,7 +529,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s)
 {
     const Geometry& g = a.g;
     const int problems = g.B * g.Hkv * a.Q;
-    if (a.k_max > 0) {
+    if (a.k_max > 0 && a.mode == 0 && g.dtype == 1) {
+        const hipError_t e = g.hd == 128 ? launch_score_quest_bf16_g<128>(a, s) : launch_score_quest_bf16_g<64>(a, s);
+        if (e != hipSuccess) return e;
+    } else if (a.k_max > 0) {
         // rows per wave load of the score kernel, as in k_score
         const int eb = a.mode == 0 ? (g.dtype == 1 ? 2 : 4) : 4;
         const int lpt = g.hd / (16 / eb);
