@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--local-splits", type=int, default=0, help="splits of the sink+window decode")
     ap.add_argument("--middle-splits", type=int, default=0, help="splits of the selected-pages decode")
+    ap.add_argument("--separate", action="store_true",
+                    help="select, decode and combine as three launches instead of the fused select-and-decode step")
     ap.add_argument("--overlap", action="store_true",
                     help="decode sink + window on a second stream beside the selection, then the selected pages")
     ap.add_argument("--dense-steps", type=int, default=10)
@@ -158,7 +160,17 @@ def main():
     def step_overlapped(r, ev=None):
         ov.step(q, desc=descs[r], meta=metas[r], middle_events=ev)
 
-    step = step_sequential if not args.overlap else step_overlapped
+    def select_decode(r):
+        B.sparse_attn_decode_step(descs[r], q, 1, metas[r], pr.mode, pr.sink, pr.window, pr.budget, 0.0, dec.splits,
+                                  dec.sel, dec.count, dec.ws, dec.ws_bytes, dec.part_o, dec.part_ml)
+
+    def step_fused(r, ev=None):
+        select_decode(r)
+        B.sparse_attn_combine(dec.rows, c.hd, dec.splits, dec.part_o, dec.part_ml, dec.out, dec.out_dtype,
+                              dec.lse)
+
+    mode = "overlap" if args.overlap else "separate" if args.separate else "fused"
+    step = {"overlap": step_overlapped, "separate": step_sequential, "fused": step_fused}[mode]
 
     for i in range(args.warmup):
         step(i % R)
@@ -172,16 +184,26 @@ def main():
     sb = accounting.decode_step_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2, L=L, P=c.P, S=pr.sink,
                                       W=pr.window, budget=pr.budget, mode=pr.mode, splits=dec.splits,
                                       attended=attended)
-    if not args.overlap:
-        # one launch over sink + window + selected pages
-        dec_kernel, dec_tok, dec_splits = "k_decode (sink+window+selected)", sum(attended), dec.splits
+    n_cand = accounting.candidate_pages(L, c.P, pr.sink, pr.window)
+    if mode == "fused":
+        # the launch pair of sparse_attn_decode_step: page scores, then top-k + decode
+        dec_kernel = "k_score_quest_mfma + k_select_decode_mfma"
+        dec_bytes = accounting.select_decode_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
+                                                   ntok_total=sum(attended), splits=dec.splits, meta=sb.meta,
+                                                   n_cand=n_cand, k_max=dec.k_max)
+    elif mode == "separate":
+        # one decode launch over sink + window + selected pages
+        dec_kernel = "k_decode_mfma"
+        dec_bytes = accounting.decode_kernel_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
+                                                   ntok_total=sum(attended), splits=dec.splits,
+                                                   sel_entries=int(cnt.sum()))
     else:
         # the timed launch is the selected pages' decode; sink + window run beside the selection
         local = accounting.attended_tokens_exact(L, c.P, pr.sink, pr.window, [])
-        dec_kernel, dec_tok, dec_splits = "k_decode (selected pages)", sum(attended) - local * c.B * c.Hkv, ov.sm
-    dec_bytes = accounting.decode_kernel_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
-                                               ntok_total=dec_tok, splits=dec_splits,
-                                               sel_entries=int(cnt.sum()))
+        dec_kernel = "k_decode_mfma (selected pages)"
+        dec_bytes = accounting.decode_kernel_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
+                                                   ntok_total=sum(attended) - local * c.B * c.Hkv, splits=ov.sm,
+                                                   sel_entries=int(cnt.sum()))
 
     # timed region: K steps back to back
     K = args.steps
@@ -194,17 +216,28 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / K
 
-    # the same K steps again with HIP events around each decode launch (on the
-    # stream the kernels run on): the decode kernel's average launch duration.
-    # An event record adds a few microseconds between kernels, so these steps
-    # are not the ones the step time is taken from.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # the dominant launch(es) alone: K calls back to back on the stream they run
+    # on, between two HIP events (an event record between kernels would add a
+    # few microseconds to each), rotating over the replicas like the steps
+    if mode == "fused":
+        def launch(r):
+            select_decode(r)
+    elif mode == "separate":
+        def launch(r):
+            B.sparse_attn_decode(descs[r], q, 1, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, B.SA_PART_ALL,
+                                 0.0, dec.splits, 0, dec.part_o, dec.part_ml)
+    else:
+        def launch(r):
+            ov.decode_middle(q, descs[r], pr.window)
+    for i in range(3):
+        launch(i % R)
     torch.cuda.synchronize()
+    start.record()
     for i in range(K):
-        step(i % R, evs[i])
+        launch(i % R)
+    stop.record()
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_avg_ms = start.elapsed_time(stop) / K
 
     ms_hot = dense_ms = float('nan')
     if not args.only_timed:
@@ -273,8 +306,8 @@ def main():
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "context": L, "page": c.P, "sink": pr.sink, "window": pr.window, "budget": pr.budget,
                    "score": "quest", "replicas": R,
-                   "splits": dec.splits if not args.overlap else {"sink_window": ov.sl, "selected": ov.sm},
-                   "streams": 1 if not args.overlap else 2},
+                   "splits": dec.splits if mode != "overlap" else {"sink_window": ov.sl, "selected": ov.sm},
+                   "step": mode},
         "roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_record(), "bytes_per_launch": dec_bytes,

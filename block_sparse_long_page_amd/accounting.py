@@ -107,6 +107,19 @@ def decode_kernel_bytes(*, B: int, Hq: int, Hkv: int, hd: int, elem_bytes: int, 
     return ntok_total * 2 * hd * elem_bytes + rows * hd * elem_bytes + 4 * sel_entries + rows * splits * (hd + 2) * 4
 
 
+def select_decode_bytes(*, B: int, Hq: int, Hkv: int, hd: int, elem_bytes: int, ntok_total: int, splits: int,
+                        meta: int, n_cand: int, k_max: int, Q: int = 1) -> int:
+    """Bytes the score launch and the select-and-decode launch of one selecting
+    step must move: the page summaries, q, the fp32 page scores (written, then
+    read), the attended K+V, the page list written (k_max entries and a count
+    per problem) and the partials written."""
+    rows = B * Hq * Q
+    problems = B * Hkv * Q
+    scores = problems * n_cand * 4
+    return (meta + rows * hd * elem_bytes + 2 * scores + ntok_total * 2 * hd * elem_bytes +
+            problems * (k_max + 1) * 4 + rows * splits * (hd + 2) * 4)
+
+
 def attended_tokens_exact(L: int, P: int, S: int, W: int, pages, Q: int = 1, row: int = None) -> int:
     """Tokens attended by query row `row` (default: the last) given the
     selected logical pages: the sink, the window and the middle part of each

@@ -55,6 +55,8 @@ _SIGS = {
     "sparse_attn_select": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_workspace_bytes": (ctypes.c_size_t, [_DESC, _I]),
     "sparse_attn_decode": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P, _P]),
+    "sparse_attn_decode_step": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
+                                               ctypes.c_size_t, _P, _P, _P]),
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -132,6 +134,15 @@ def sparse_attn_decode(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count,
     _check(_lib.sparse_attn_decode(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(sel_pages), _ptr(sel_count), k_max,
                                    sink_len, window_len, parts, softmax_scale, num_splits, split_stride,
                                    _ptr(part_o), _ptr(part_ml), _stream(stream)), "sparse_attn_decode")
+
+
+def sparse_attn_decode_step(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode: int, sink_len: int,
+                            window_len: int, token_budget: int, softmax_scale: float, num_splits: int, sel_pages,
+                            sel_count, workspace, workspace_bytes: int, part_o, part_ml, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_step(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(meta), score_mode, sink_len,
+                                        window_len, token_budget, softmax_scale, num_splits, _ptr(sel_pages),
+                                        _ptr(sel_count), _ptr(workspace), workspace_bytes, _ptr(part_o),
+                                        _ptr(part_ml), _stream(stream)), "sparse_attn_decode_step")
 
 
 def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, part_ml, out, out_dtype: int,

@@ -21,6 +21,7 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "topk_block.hpp"
 
 namespace sa {
 
@@ -225,11 +226,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_decode_generic(DecodeArgs a)
     }
 }
 
-constexpr int kSelCap = 1024;  // page-list entries staged in LDS; longer lists are read in place
-constexpr int kRowsWG = 2048;  // rows resolved per workgroup per prologue round
+constexpr int kPartMiddle = 2;  // the selected pages' middle tokens (TokenSet parts bit)
 
 // ---------------------------------------------------------------------------
-// bf16 kernel on the matrix cores.  The G query heads of a KV group against a
+// bf16 decode on the matrix cores.  The G query heads of a KV group against a
 // tile of 16 tokens are a small dense product, so both products of a tile run
 // as MFMAs and the vector ALU only does the softmax:
 //  * q.k: v_mfma_f32_16x16x32_bf16 with the tile's keys as A (row = token,
@@ -244,8 +244,10 @@ constexpr int kRowsWG = 2048;  // rows resolved per workgroup per prologue round
 //    loaded (row-major, a 32-byte pad per 4 tokens so the column reads below
 //    hit distinct banks) and read back one bf16 per token and channel;
 //  * the accumulators hold rows = heads 4j..4j+3 and column = channel.
-// The split's tokens are taken in rounds of NW tiles, tile w of each round by
-// wave w.  Epilogue as in the vector kernel: the waves merge through LDS.
+// A workgroup's tokens are listed in a row table in LDS and taken in rounds of
+// NW tiles, tile w of each round by wave w, three rounds in flight per wave.
+// At the end the waves merge through LDS and the workgroup writes its
+// normalised partial and (m, l).
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -260,11 +262,15 @@ struct MfmaPlan {
     static constexpr int LPT = HD / 8;                 // lanes per value row
     static constexpr int VROW = HD * 2;                // bytes per value row
     static constexpr int VTILE = 16 * VROW + 4 * 32;   // LDS bytes of one value tile (padded)
-    static constexpr int TPS = SA_MFMA_TPS;            // tiles per pipeline step
-    static constexpr int NW = SA_MFMA_NW;
-    static constexpr int vbytes(int nw) { return nw * TPS * VTILE; }
-    static constexpr int obytes(int nw) { return nw * G * HD * 4; }
-    static constexpr int smem_bytes(int nw) { return vbytes(nw) > obytes(nw) ? vbytes(nw) : obytes(nw); }
+    static constexpr int TPS = SA_MFMA_TPS;            // tiles per wave per round
+    static constexpr int NW = SA_MFMA_NW;              // waves per workgroup
+    static constexpr int RT = NW * TPS * 16;           // tokens per round
+    static constexpr int vbytes() { return NW * TPS * VTILE; }
+    static constexpr int obytes() { return NW * G * HD * 4; }
+    static constexpr int smem_bytes() { return vbytes() > obytes() ? vbytes() : obytes(); }
+    static_assert(kRowsWG % RT == 0 && kRowsWG % (64 * NW) == 0, "rounds tile the row table");
+    static_assert(G <= 16, "one MFMA column per head");
+    static_assert(NW * 64 == kTopkThreads, "the select-and-decode workgroup runs the block top-k");
 };
 
 // LDS byte offset of (token t, byte b) in a value tile
@@ -274,25 +280,288 @@ __device__ __forceinline__ int vt_off(int t, int b)
     return t * VROW + (t >> 2) * 32 + b;
 }
 
+// LDS a workgroup of the matrix-core decode shares
+template <int HD, int G>
+struct MfmaLds {
+    using Plan = MfmaPlan<HD, G>;
+    __attribute__((aligned(16))) int rows[kRowsWG];
+    __attribute__((aligned(16))) unsigned char tiles[Plan::smem_bytes()];  // value tiles, then the waves' outputs
+    float wv_m[Plan::NW][G], wv_l[Plan::NW][G];
+};
+
+// Per-lane state and tile pipeline of the matrix-core decode.
+template <int HD, int G>
+struct MfmaCore {
+    using Plan = MfmaPlan<HD, G>;
+    static constexpr int NW = Plan::NW, KK = Plan::KK, NB = Plan::NB, VLD = Plan::VLD, LPT = Plan::LPT;
+    static constexpr int VROW = Plan::VROW, VTILE = Plan::VTILE, TPS = Plan::TPS, RT = Plan::RT;
+
+    struct Buf {
+        uint4 k[TPS][KK];
+        uint4 v[TPS][VLD];
+        int4 rv[TPS];  // rows of tokens 4j .. 4j+3 of each tile (-1: not attended)
+    };
+
+    MfmaLds<HD, G>& sm;
+    int lane, wave, r, j, vchunk;
+    float sl2, slack;
+    uint4 qb[KK];
+    f32x4_t o[NB];
+    float m_run;  // reference maximum of head r (raw q.k units)
+    float l_run;  // this lane's share of head r's sum
+    const uint16_t* kbase;
+    const uint16_t* vbase;
+    int nrows;    // entries of the row table in use
+
+    __device__ __forceinline__ MfmaCore(MfmaLds<HD, G>& s, const Geometry& g, float scale_log2)
+        : sm(s)
+    {
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        r = lane & 15;
+        j = lane >> 4;
+        vchunk = lane % LPT;
+        sl2 = scale_log2;
+        slack = kRescaleSlack / sl2;
+        for (int m = 0; m < NB; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        kbase = (const uint16_t*)g.k;
+        vbase = (const uint16_t*)g.v;
+        nrows = 0;
+    }
+
+    // B operand of q.k: head r, channels 32 kk + 8 j .. + 8 (heads past G are zero)
+    __device__ __forceinline__ void load_queries(const void* q, long qrow0, long head_stride)
+    {
+        for (int kk = 0; kk < KK; ++kk) {
+            qb[kk] = make_uint4(0, 0, 0, 0);
+            if (r < G) qb[kk] = *(const uint4*)((const uint16_t*)q + qrow0 + r * head_stride + 32 * kk + 8 * j);
+        }
+    }
+
+    // value rows: lane (r, j) loads tokens 4j + v (hd 128) or 4j + 2v + r/8 (hd 64), 16 bytes each
+    __device__ __forceinline__ int vtok(int v) const { return HD == 128 ? 4 * j + v : 4 * j + 2 * v + (r >> 3); }
+
+    __device__ __forceinline__ bool busy(int rd, int tt) const { return rd * RT + (wave * TPS + tt) * 16 < nrows; }
+
+    // Round rd of the row table.  Every lane issues every load, so the
+    // compiler can count the loads in flight and wait for one round only:
+    // tokens that are not attended read row 0 instead, their logits are
+    // masked to -inf and their value rows written as zeros.
+    __device__ __forceinline__ void load(int rd, Buf& B) const
+    {
+        const int* rows = sm.rows;
+#pragma unroll
+        for (int tt = 0; tt < TPS; ++tt) {
+            const int t0 = rd * RT + (wave * TPS + tt) * 16;  // tile start in the table
+            const int4 rv = t0 + 4 * j + 3 < nrows
+                                ? *(const int4*)(rows + t0 + 4 * j)
+                                : make_int4(t0 + 4 * j < nrows ? rows[t0 + 4 * j] : -1,
+                                            t0 + 4 * j + 1 < nrows ? rows[t0 + 4 * j + 1] : -1,
+                                            t0 + 4 * j + 2 < nrows ? rows[t0 + 4 * j + 2] : -1, -1);
+            B.rv[tt] = rv;
+            const int rk = t0 + r < nrows ? imax(rows[t0 + r], 0) : 0;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
+            const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+            for (int v = 0; v < VLD; ++v) {
+                const int rr = imax(rows4[HD == 128 ? v : 2 * v + (r >> 3)], 0);
+                B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void compute(const Buf& B, int tt)
+    {
+        unsigned char* const vt = sm.tiles + (wave * TPS + tt) * VTILE;  // this wave's value tile
+        // q.k
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[tt][kk]),
+                                                        __builtin_bit_cast(bf16x8_t, qb[kk]), s, 0, 0, 0);
+        const int4 rv = B.rv[tt];
+        const float z[4] = {rv.x >= 0 ? s[0] : -INFINITY, rv.y >= 0 ? s[1] : -INFINITY,
+                            rv.z >= 0 ? s[2] : -INFINITY, rv.w >= 0 ? s[3] : -INFINITY};
+        // values to LDS as loaded (zeros for tokens that are not attended;
+        // selected per component: a select of whole vectors would keep the
+        // buffers out of registers)
+        const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+        for (int v = 0; v < VLD; ++v) {
+            const bool ok = rows4[HD == 128 ? v : 2 * v + (r >> 3)] >= 0;
+            const uint4 w = B.v[tt][v];
+            *(uint4*)(vt + vt_off<VROW>(vtok(v), 16 * vchunk)) =
+                make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
+        }
+        // softmax: tile maximum of head r over the 4 lanes holding it
+        float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mx = fmaxf(mx, xor_lanes<16>(mx));
+        mx = fmaxf(mx, xor_lanes<32>(mx));
+        const bool need = r < G && mx > m_run + slack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float mn = need ? mx : m_run;
+            const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mn) * sl2) : 1.f;  // 0 while m = -inf
+            l_run *= alpha;
+            m_run = mn;
+            // accumulator rows are heads 4j + i: fetch their factors
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * j + i);
+#pragma unroll
+                for (int m = 0; m < NB; ++m) o[m][i] *= ai;
+            }
+        }
+        const float mref = m_run == -INFINITY ? 0.f : -m_run * sl2;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(fmaf(z[i], sl2, mref));  // -inf -> 0
+            l_run += p[i];
+        }
+        const uint2 pw = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+        const i16x4_t pa = __builtin_bit_cast(i16x4_t, pw);
+        __builtin_amdgcn_wave_barrier();
+        // p.v, 16 channels per product; B operand = values of tokens 4j .. 4j+3 at channel 16m + r
+        const unsigned char* vcol = vt + 2 * r;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            i16x4_t vb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vb[i] = *(const short*)(vcol + vt_off<VROW>(4 * j + i, 32 * m));
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[m], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // All rounds of the row table, three in flight per wave; the first
+    // `loaded` rounds (0 .. 3) may already be loaded into A, B, C.
+    __device__ __forceinline__ void run(Buf& A, Buf& B, Buf& C, int loaded)
+    {
+        const int nr = (nrows + RT - 1) / RT;
+        if (loaded < 1 && nr > 0) load(0, A);
+        if (loaded < 2 && nr > 1) load(1, B);
+        if (loaded < 3 && nr > 2) load(2, C);
+        for (int rd = 0; rd < nr; rd += 3) {
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt)
+                if (busy(rd, tt)) compute(A, tt);
+            if (rd + 3 < nr) load(rd + 3, A);
+            if (rd + 1 >= nr) break;
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt)
+                if (busy(rd + 1, tt)) compute(B, tt);
+            if (rd + 4 < nr) load(rd + 4, B);
+            if (rd + 2 >= nr) break;
+#pragma unroll
+            for (int tt = 0; tt < TPS; ++tt)
+                if (busy(rd + 2, tt)) compute(C, tt);
+            if (rd + 5 < nr) load(rd + 5, C);
+        }
+    }
+
+    __device__ __forceinline__ static void clear(Buf& A)
+    {
+#pragma unroll
+        for (int tt = 0; tt < TPS; ++tt) {
+            for (int kk = 0; kk < KK; ++kk) A.k[tt][kk] = make_uint4(0, 0, 0, 0);
+            for (int v = 0; v < VLD; ++v) A.v[tt][v] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // The waves' states go to LDS (the output area reuses the value tiles, so
+    // every wave first leaves its loop); the workgroup merges them with one
+    // exponential per (wave, head) and writes the partial of its G heads:
+    // part_o / part_ml rows prow0 + h * prow_step, slot `slot`.
+    __device__ __forceinline__ void finish(float* part_o, float* part_ml, long prow0, long prow_step, int stride,
+                                           int slot)
+    {
+        // head r's sum over the 4 lanes holding it
+        l_run += xor_lanes<16>(l_run);
+        l_run += xor_lanes<32>(l_run);
+        __syncthreads();
+        float* const wv_o = (float*)sm.tiles;  // [NW][G][HD]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * j + i;
+            if (h < G) {
+#pragma unroll
+                for (int m = 0; m < NB; ++m) wv_o[(wave * G + h) * HD + 16 * m + r] = o[m][i];
+            }
+        }
+        if (j == 0 && r < G) {
+            sm.wv_m[wave][r] = m_run * sl2;  // -inf stays -inf
+            sm.wv_l[wave][r] = l_run;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
+            const int h = i / (HD / 4), c4 = i % (HD / 4);
+            float ms = -INFINITY;
+            for (int w = 0; w < NW; ++w) ms = fmaxf(ms, sm.wv_m[w][h]);
+            float ls = 0.f;
+            float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int w = 0; w < NW; ++w) {
+                const float mw = sm.wv_m[w][h];
+                const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
+                ls = fmaf(sm.wv_l[w][h], wt, ls);
+                const float4 ow = *(const float4*)(wv_o + (w * G + h) * HD + 4 * c4);
+                os.x = fmaf(ow.x, wt, os.x);
+                os.y = fmaf(ow.y, wt, os.y);
+                os.z = fmaf(ow.z, wt, os.z);
+                os.w = fmaf(ow.w, wt, os.w);
+            }
+            const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+            const long prow = (prow0 + h * prow_step) * stride + slot;
+            *(float4*)(part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
+            if (c4 == 0) {
+                part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
+                part_ml[prow * 2 + 1] = ls;
+            }
+        }
+    }
+};
+
+// Row index ((phys * Hkv + kvh) * P + offset) of token t, or -1 when t is past
+// the row's position or its page is unmapped.
+__device__ __forceinline__ int token_row(int t, int pos, int phys, const Geometry& g, int kvh, const FastDiv& pdiv)
+{
+    if (t < 0 || t > pos || phys < 0 || phys >= g.num_phys) return -1;
+    const int pg = pdiv.div(t);
+    return phys * (g.Hkv * g.P) + kvh * g.P + (t - pg * g.P);
+}
+
+// Resolves table entries [first, first + cnt) from tokens tok(i), i = 0 ..
+// cnt-1, with all block-table loads of a thread in flight together.
+template <int NW, typename Tok>
+__device__ __forceinline__ void resolve_rows(int* rows, int first, int cnt, Tok tok, int pos, const int32_t* bt,
+                                             const Geometry& g, int kvh, const FastDiv& pdiv)
+{
+    constexpr int PER_T = kRowsWG / (64 * NW);
+    int tk[PER_T], ph[PER_T];
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+        const int i = u * 64 * NW + (int)threadIdx.x;
+        const int t = i < cnt ? tok(i) : -1;
+        tk[u] = t;
+        ph[u] = t >= 0 && t <= pos ? bt[pdiv.div(t)] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+        const int i = u * 64 * NW + (int)threadIdx.x;
+        if (i < cnt) rows[first + i] = token_row(tk[u], pos, ph[u], g, kvh, pdiv);
+    }
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_decode_mfma(DecodeArgs a)
 {
-    using Plan = MfmaPlan<HD, G>;
-    constexpr int NW = Plan::NW, KK = Plan::KK, NB = Plan::NB, VLD = Plan::VLD, LPT = Plan::LPT;
-    constexpr int VROW = Plan::VROW, VTILE = Plan::VTILE, TPS = Plan::TPS;
-    constexpr int RT = NW * TPS * 16;  // tokens per round
-    constexpr int PER_T = kRowsWG / (64 * NW);
-    static_assert(kRowsWG % RT == 0 && kRowsWG % (64 * NW) == 0, "rounds tile the row chunk");
-    static_assert(G <= 16, "one MFMA column per head");
+    using Core = MfmaCore<HD, G>;
+    constexpr int NW = Core::NW;
     const Geometry& g = a.g;
-
     __shared__ int sel_lds[kSelCap];
-    __shared__ __attribute__((aligned(16))) int rows_lds[kRowsWG];
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Plan::smem_bytes(NW)];
-    __shared__ float wv_m[NW][G], wv_l[NW][G];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, j = lane >> 4;
+    __shared__ MfmaLds<HD, G> lds;
 
     int bid = blockIdx.x;
     const int split = bid % a.splits;
@@ -303,22 +572,15 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_de
     const int b = bid / a.Q;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
 
-    // one round of loads: length, count, page list, block-table row, the group's queries
+    // one round of loads: length, count, page list, the group's queries
     const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
     const int count = a.sel ? a.count[prob] : 0;
     const int32_t* sel_g = a.sel ? a.sel + prob * a.k_max : nullptr;
     const bool staged = sel_g != nullptr && a.k_max <= kSelCap;
     if (staged)
         for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_lds[i] = sel_g[i];
-    const int32_t* const bt = g.block_table + (long)b * g.max_pages;
-    // B operand of q.k: head r, channels 32 kk + 8 j .. + 8
-    uint4 qb[KK];
-    for (int kk = 0; kk < KK; ++kk) {
-        qb[kk] = make_uint4(0, 0, 0, 0);
-        if (r < G)
-            qb[kk] = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + r) * a.Q + row) * HD +
-                                     32 * kk + 8 * j);
-    }
+    Core core(lds, g, a.scale_log2);
+    core.load_queries(a.q, (((long)b * g.Hq + kvh * G) * a.Q + row) * HD, (long)a.Q * HD);
     __syncthreads();
 
     const int pos = L - a.Q + row;
@@ -331,207 +593,133 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_de
     const int n = staged ? tsl.total : tsg.total;
     const int f0 = split * (n / a.splits) + imin(split, n % a.splits);
     const int f1 = f0 + n / a.splits + (split < n % a.splits ? 1 : 0);
-    auto position = [&](int f) { return staged ? tsl.position(f, pdiv) : tsg.position(f, pdiv); };
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
 
-    const float sl2 = a.scale_log2;
-    const float slack = kRescaleSlack / sl2;
-    f32x4_t o[NB];
-    for (int m = 0; m < NB; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // reference maximum of head r (raw q.k units)
-    float l_run = 0.f;        // this lane's share of head r's sum
-
-    const uint16_t* kbase = (const uint16_t*)g.k;
-    const uint16_t* vbase = (const uint16_t*)g.v;
-    const int hkvP = g.Hkv * g.P;
-    unsigned char* const vt = smem + wave * TPS * VTILE;  // this wave's value tiles
-
-    // value rows: lane (r, j) loads tokens 4j + v (hd 128) or 4j + 2v + r/8 (hd 64), 16 bytes each
-    const int vchunk = lane % LPT;
-    auto vtok = [&](int v) { return HD == 128 ? 4 * j + v : 4 * j + 2 * v + (r >> 3); };
-
+    typename Core::Buf A, B, C;
+    Core::clear(A);
+    Core::clear(B);
+    Core::clear(C);
     for (int cb = f0; cb < f1; cb += kRowsWG) {
-        const int ce = imin(f1, cb + kRowsWG);
+        const int cnt = imin(f1 - cb, kRowsWG);
         __syncthreads();  // the previous chunk's rows are no longer read
-        {
-            int tok[PER_T], phys[PER_T];
-#pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int f = cb + i * 64 * NW + (int)threadIdx.x;
-                int t = f < ce ? position(f) : -1;
-                if (t > pos) t = -1;
-                tok[i] = t;
-                phys[i] = t >= 0 ? bt[pdiv.div(t)] : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int t = tok[i];
-                int ri = -1;
-                if (t >= 0 && phys[i] >= 0 && phys[i] < g.num_phys) {
-                    const int pg = pdiv.div(t);
-                    ri = phys[i] * hkvP + kvh * g.P + (t - pg * g.P);
-                }
-                if (cb + i * 64 * NW + (int)threadIdx.x < ce) rows_lds[i * 64 * NW + threadIdx.x] = ri;
-            }
-        }
+        resolve_rows<NW>(lds.rows, 0, cnt,
+                         [&](int i) { return staged ? tsl.position(cb + i, pdiv) : tsg.position(cb + i, pdiv); },
+                         pos, bt, g, kvh, pdiv);
         __syncthreads();
+        core.nrows = cnt;
+        core.run(A, B, C, 0);
+    }
+    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
+}
 
-        const int nr = (ce - cb + RT - 1) / RT;  // rounds in this chunk
+// Selection and decode in one kernel, for the steps that select: every
+// workgroup of a (sequence, KV head, row) takes its share of the sink and
+// window tokens and issues their first rounds, runs the block top-k of the
+// problem's page scores while those loads are in flight, then takes its share
+// of the selected pages' middle tokens.  The workgroup of split 0 also writes
+// the page list and its count.
+template <int HD, int G>
+__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_select_decode_mfma(SelectDecodeArgs a)
+{
+    using Core = MfmaCore<HD, G>;
+    constexpr int NW = Core::NW, RT = Core::RT;
+    const Geometry& g = a.g;
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kFusedMaxCand];
+    __shared__ int bt_lds[kFusedMaxCand];
+    __shared__ TopkScratch tk;
+    __shared__ int sel_lds[kSelCap];
+    __shared__ MfmaLds<HD, G> lds;
 
-        struct Buf {
-            uint4 k[TPS][KK];
-            uint4 v[TPS][VLD];
-            int4 rv[TPS];  // rows of tokens 4j .. 4j+3 of each tile (-1: not attended)
-        };
-        // Rows of tokens that are not attended are not loaded: their registers
-        // keep earlier (finite) data, and their logits are masked to -inf.
-        auto load = [&](int rd, Buf& B) {
-#pragma unroll
-            for (int tt = 0; tt < TPS; ++tt) {
-                const int t0 = rd * RT + (wave * TPS + tt) * 16;  // tile start within the chunk
-                const int4 rv = cb + t0 + 4 * j + 3 < ce
-                                    ? *(const int4*)(rows_lds + t0 + 4 * j)
-                                    : make_int4(cb + t0 + 4 * j < ce ? rows_lds[t0 + 4 * j] : -1,
-                                                cb + t0 + 4 * j + 1 < ce ? rows_lds[t0 + 4 * j + 1] : -1,
-                                                cb + t0 + 4 * j + 2 < ce ? rows_lds[t0 + 4 * j + 2] : -1, -1);
-                B.rv[tt] = rv;
-                const int rk = cb + t0 + r < ce ? rows_lds[t0 + r] : -1;
-                if (rk >= 0) {
-#pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
-                }
-                const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-                for (int v = 0; v < VLD; ++v) {
-                    const int rr = rows4[HD == 128 ? v : 2 * v + (r >> 3)];
-                    if (rr >= 0) B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
-                }
-            }
-        };
+    int bid = blockIdx.x;
+    const int split = bid % a.splits;
+    bid /= a.splits;
+    const int kvh = bid % g.Hkv;
+    bid /= g.Hkv;
+    const int row = bid % a.Q;
+    const int b = bid / a.Q;
+    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
 
-        auto compute = [&](const Buf& B, int tt) {
-            // q.k
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[tt][kk]),
-                                                            __builtin_bit_cast(bf16x8_t, qb[kk]), s, 0, 0, 0);
-            const int4 rv = B.rv[tt];
-            float z[4] = {rv.x >= 0 ? s[0] : -INFINITY, rv.y >= 0 ? s[1] : -INFINITY, rv.z >= 0 ? s[2] : -INFINITY,
-                          rv.w >= 0 ? s[3] : -INFINITY};
-            // values to LDS as loaded
-#pragma unroll
-            for (int v = 0; v < VLD; ++v)
-                *(uint4*)(vt + tt * VTILE + vt_off<VROW>(vtok(v), 16 * vchunk)) = B.v[tt][v];
-            // softmax: tile maximum of head r over the 4 lanes holding it
-            float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-            mx = fmaxf(mx, xor_lanes<16>(mx));
-            mx = fmaxf(mx, xor_lanes<32>(mx));
-            const bool need = r < G && mx > m_run + slack;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float mn = need ? mx : m_run;
-                const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mn) * sl2) : 1.f;  // 0 while m = -inf
-                l_run *= alpha;
-                m_run = mn;
-                // accumulator rows are heads 4j + i: fetch their factors
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * j + i);
-#pragma unroll
-                    for (int m = 0; m < NB; ++m) o[m][i] *= ai;
-                }
-            }
-            const float mref = m_run == -INFINITY ? 0.f : -m_run * sl2;
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(fmaf(z[i], sl2, mref));  // -inf -> 0
-                l_run += p[i];
-            }
-            const uint2 pw = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
-            const i16x4_t pa = __builtin_bit_cast(i16x4_t, pw);
-            __builtin_amdgcn_wave_barrier();
-            // p.v, 16 channels per product; B operand = values of tokens 4j .. 4j+3 at channel 16m + r
-            const unsigned char* vcol = vt + tt * VTILE + 2 * r;
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                i16x4_t vb;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vb[i] = *(const short*)(vcol + vt_off<VROW>(4 * j + i, 32 * m));
-                o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[m], 0, 0, 0);
-            }
-            __builtin_amdgcn_wave_barrier();
-        };
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int pos = L - a.Q + row;
+    const int se = imin(a.S, L), ws = imax(se, L - a.W);
+    const int plo = se / g.P;
+    const int ncand = ws > se ? (ws - 1) / g.P - plo + 1 : 0;
+    const int k = imin(a.k_max, ncand);
+    Core core(lds, g, a.scale_log2);
+    core.load_queries(a.q, (((long)b * g.Hq + kvh * G) * a.Q + row) * HD, (long)a.Q * HD);
+    const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
 
-        auto busy = [&](int rd, int tt) { return cb + rd * RT + (wave * TPS + tt) * 16 < ce; };
-
-        Buf A, Bb;
+    // one round of loads: the block-table row of the sequence's pages into LDS
+    // and the candidates' scores as order keys, every load of a thread in flight
+    const int npg = imin(g.max_pages, (L + g.P - 1) / g.P);
+    const int32_t* bt_g = g.block_table + (long)b * g.max_pages;
+    const float* sc = a.scores + prob * g.max_pages + plo;
+    const bool rank = k > 0 && k < ncand;
+    uint32_t lo = 0xffffffffu, hi = 0;
+    for (int base = 0; base < imax(npg, ncand); base += 4 * 64 * NW) {
+        int bv[4];
+        float sv[4];
 #pragma unroll
-        for (int tt = 0; tt < TPS; ++tt) {
-            for (int kk = 0; kk < KK; ++kk) A.k[tt][kk] = Bb.k[tt][kk] = make_uint4(0, 0, 0, 0);
-            for (int v = 0; v < VLD; ++v) A.v[tt][v] = Bb.v[tt][v] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * 64 * NW + (int)threadIdx.x;
+            bv[u] = i < npg ? bt_g[i] : -1;
+            sv[u] = rank && i < ncand ? sc[i] : 0.f;
         }
-        load(0, A);
-        for (int rd = 0; rd < nr; rd += 2) {
-            if (rd + 1 < nr) load(rd + 1, Bb);
 #pragma unroll
-            for (int tt = 0; tt < TPS; ++tt)
-                if (busy(rd, tt)) compute(A, tt);
-            if (rd + 1 >= nr) break;
-            if (rd + 2 < nr) load(rd + 2, A);
-#pragma unroll
-            for (int tt = 0; tt < TPS; ++tt)
-                if (busy(rd + 1, tt)) compute(Bb, tt);
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * 64 * NW + (int)threadIdx.x;
+            if (i < npg) bt_lds[i] = bv[u];
+            if (rank && i < ncand) {
+                const uint32_t key = order_key(sv[u]);
+                keys[i] = key;
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
         }
     }
-
-    // head r's sum over the 4 lanes holding it
-    l_run += xor_lanes<16>(l_run);
-    l_run += xor_lanes<32>(l_run);
-
-    // The waves' states go to LDS (the output area reuses the value tiles, so
-    // every wave first leaves its loop); the workgroup merges them with one
-    // exponential per (wave, head) and writes the split's partial.
+    // this workgroup's share of the sink and window tokens, first in its table,
+    // resolved in the same round from the block table in global memory
+    const int nloc = se + (L - ws);
+    const int l0 = split * (nloc / a.splits) + imin(split, nloc % a.splits);
+    const int nl = nloc / a.splits + (split < nloc % a.splits ? 1 : 0);
+    resolve_rows<NW>(lds.rows, 0, nl, [&](int i) { const int f = l0 + i; return f < se ? f : ws + (f - se); }, pos,
+                     bt_g, g, kvh, pdiv);
     __syncthreads();
-    float* const wv_o = (float*)smem;  // [NW][G][HD]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = 4 * j + i;
-        if (h < G) {
-#pragma unroll
-            for (int m = 0; m < NB; ++m) wv_o[(wave * G + h) * HD + 16 * m + r] = o[m][i];
-        }
-    }
-    if (j == 0 && r < G) {
-        wv_m[wave][r] = m_run * sl2;  // -inf stays -inf
-        wv_l[wave][r] = l_run;
+    const int32_t* bt = bt_lds;
+    typename Core::Buf A, B, C;
+    Core::clear(A);
+    Core::clear(B);
+    Core::clear(C);
+    core.nrows = nl;
+    const int pre = imin(3, nl / RT);  // rounds made of sink and window tokens only, loaded now
+    if (pre > 0) core.load(0, A);
+    if (pre > 1) core.load(1, B);
+    if (pre > 2) core.load(2, C);
+
+    // the page list, while those loads are in flight
+    if (rank) {
+        block_topk_fast(ncand, k, keys, lo, hi, tk, [&](int p, int i) { sel_lds[p] = plo + i; });
+    } else {
+        for (int i = threadIdx.x; i < k; i += 64 * NW) sel_lds[i] = plo + i;
     }
     __syncthreads();
-
-    for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
-        const int h = i / (HD / 4), c4 = i % (HD / 4);
-        float ms = -INFINITY;
-        for (int w = 0; w < NW; ++w) ms = fmaxf(ms, wv_m[w][h]);
-        float ls = 0.f;
-        float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int w = 0; w < NW; ++w) {
-            const float mw = wv_m[w][h];
-            const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - ms);
-            ls = fmaf(wv_l[w][h], wt, ls);
-            const float4 ow = *(const float4*)(wv_o + (w * G + h) * HD + 4 * c4);
-            os.x = fmaf(ow.x, wt, os.x);
-            os.y = fmaf(ow.y, wt, os.y);
-            os.z = fmaf(ow.z, wt, os.z);
-            os.w = fmaf(ow.w, wt, os.w);
-        }
-        const float inv = ls > 0.f ? 1.0f / ls : 0.f;
-        const long prow = (((long)b * g.Hq + kvh * G + h) * a.Q + row) * a.split_stride + split;
-        *(float4*)(a.part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
-        if (c4 == 0) {
-            a.part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
-            a.part_ml[prow * 2 + 1] = ls;
-        }
+    if (split == 0) {
+        int32_t* sel_g = a.sel + prob * a.k_max;
+        for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_g[i] = i < k ? sel_lds[i] : -1;
+        if (threadIdx.x == 0) a.count[prob] = k;
     }
+
+    // this workgroup's share of the selected pages' middle tokens
+    TokenSetLds tsm;
+    tsm.init(L, a.S, a.W, g.P, (lds_i32_ptr)sel_lds, k, a.k_max, kPartMiddle);
+    const int nmid = tsm.total;
+    const int m0 = split * (nmid / a.splits) + imin(split, nmid % a.splits);
+    const int nm = nmid / a.splits + (split < nmid % a.splits ? 1 : 0);
+    resolve_rows<NW>(lds.rows, nl, nm, [&](int i) { return tsm.position(m0 + i, pdiv); }, pos, bt, g, kvh, pdiv);
+    __syncthreads();
+    core.nrows = nl + nm;
+    core.run(A, B, C, pre);
+    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
 }
 
 template <int HD, int G>
@@ -577,6 +765,26 @@ hipError_t launch_g(const DecodeArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int HD, int G>
+hipError_t launch_sd(const SelectDecodeArgs& a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_select_decode_mfma<HD, G>), grid, dim3(64 * MfmaPlan<HD, G>::NW), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_sd_g(const SelectDecodeArgs& a, dim3 grid, hipStream_t s)
+{
+    switch (a.g.G) {
+    case 1: return launch_sd<HD, 1>(a, grid, s);
+    case 2: return launch_sd<HD, 2>(a, grid, s);
+    case 4: return launch_sd<HD, 4>(a, grid, s);
+    case 8: return launch_sd<HD, 8>(a, grid, s);
+    case 16: return launch_sd<HD, 16>(a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int HD>
 int wgs_per_cu_g(int G)
 {
@@ -605,6 +813,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s)
     const bool bf = a.g.dtype == 1;
     if (a.g.hd == 128) return bf ? launch_g<128, true>(a, grid, s) : launch_g<128, false>(a, grid, s);
     if (a.g.hd == 64) return bf ? launch_g<64, true>(a, grid, s) : launch_g<64, false>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_decode(const SelectDecodeArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((long)a.g.B * a.g.Hkv * a.Q * a.splits));
+    if (a.g.dtype != 1) return hipErrorInvalidValue;
+    if (a.g.hd == 128) return launch_sd_g<128>(a, grid, s);
+    if (a.g.hd == 64) return launch_sd_g<64>(a, grid, s);
     return hipErrorInvalidValue;
 }
 

@@ -7,6 +7,10 @@
 
 namespace sa {
 
+constexpr int kSelCap = 1024;        // page-list entries the bf16 decode stages in LDS
+constexpr int kRowsWG = 2048;        // rows a decode workgroup resolves per prologue round
+constexpr int kFusedMaxCand = 8192;  // candidate pages the select-and-decode kernel ranks in LDS
+
 struct FastDivHost {
     uint32_t d, magic, shift;
 };
@@ -45,7 +49,8 @@ struct SelectArgs {
     int S, W, k_max;
     int32_t* sel;
     int32_t* count;
-    float* scores;  // workspace [B][Hkv][Q][max_pages]
+    float* scores;   // workspace [B][Hkv][Q][max_pages]
+    int score_only;  // 1: scores only (the select-and-decode kernel ranks them)
 };
 
 struct DecodeArgs {
@@ -63,6 +68,20 @@ struct DecodeArgs {
     float* part_ml;
 };
 
+struct SelectDecodeArgs {
+    Geometry g;
+    const void* q;
+    int Q;
+    const float* scores;  // [B][Hkv][Q][max_pages], written by the score kernel
+    int k_max, S, W;
+    float scale_log2;
+    int splits, split_stride;
+    float* part_o;
+    float* part_ml;
+    int32_t* sel;
+    int32_t* count;
+};
+
 struct CombineArgs {
     int rows, hd, splits, out_dtype;
     const float* part_o;
@@ -76,6 +95,7 @@ struct CombineArgs {
 hipError_t launch_page_meta(const MetaArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_select_decode(const SelectDecodeArgs& a, hipStream_t s);
 // resident decode workgroups per CU for this shape (occupancy query)
 int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

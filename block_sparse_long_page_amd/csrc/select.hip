@@ -16,6 +16,7 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "topk_block.hpp"
 
 namespace sa {
 
@@ -262,72 +263,12 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score_quest_mfma(SelectArg
     }
 }
 
-// order-preserving float -> uint32 (larger float, larger key); -0 maps to +0
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-constexpr int kTopkThreads = 512;
-constexpr int kTopkMaxRounds = 24;  // keys per thread: up to 12288 candidate pages
-
-// Number of lanes of this wave below the calling lane whose bit is set in m.
-__device__ __forceinline__ int lanes_below(uint64_t m)
-{
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-constexpr int kCntChunks = (kTopkMaxRounds * (kTopkThreads / 64) + 63) / 64;
-
-// Exclusive prefix sums of cnt[0 .. n) held across the wave: entry e's prefix
-// is lane e % 64 of ex[e / 64].
-__device__ __forceinline__ void scan_counts(const int* cnt, int n, int lane, int (&ex)[kCntChunks])
-{
-    int carry = 0;
-#pragma unroll
-    for (int c = 0; c < kCntChunks; ++c) {
-        const int e = c * 64 + lane;
-        const int v = e < n ? cnt[e] : 0;
-        const int inc = wave_inclusive_scan(v);
-        ex[c] = inc - v + carry;
-        carry += __builtin_amdgcn_readlane(inc, 63);
-    }
-}
-
-// the prefix of entry e (wave-uniform)
-__device__ __forceinline__ int pick_count(const int (&ex)[kCntChunks], int e)
-{
-    const int c = e >> 6, l = e & 63;
-    int v = __builtin_amdgcn_readlane(ex[0], l);
-#pragma unroll
-    for (int i = 1; i < kCntChunks; ++i)
-        if (c == i) v = __builtin_amdgcn_readlane(ex[i], l);
-    return v;
-}
-
-// One workgroup per (sequence, KV head, row); the order keys of the n
-// candidates live in LDS (key i at index i), loops stay rolled so the kernel
-// fits the instruction cache.
-//  1. min and max of the keys give the bits every key shares;
-//  2. radix select, 8 bits at a time from the highest differing bit: an LDS
-//     histogram of the digit among the keys that match the prefix decided so
-//     far (the keys spread over the bins, so the integer LDS atomics rarely
-//     collide); every wave then scans the histogram itself and finds the digit
-//     where the count from the top reaches k;
-//  3. compaction in ascending page order: every key above the k-th, then the
-//     lowest pages among those equal to it.
-// Wave-level reductions and scans use DPP and readlane.
+// One workgroup per (sequence, KV head, row): the block top-k of its
+// candidates' scores, written in ascending page order.
 __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
 {
-    constexpr int NW = kTopkThreads / 64;
-    constexpr int kPasses = 4;  // 32 key bits, 8 per pass
-    extern __shared__ uint32_t keys[];  // [n]
-    __shared__ int hist[kPasses][256];
-    __shared__ uint32_t mm[NW][2];
-    __shared__ int cnt_eq[kTopkMaxRounds * NW];  // round-major: flat (round, wave) order is page order
-    __shared__ int cnt_in[kTopkMaxRounds * NW];
-    __shared__ int gts[NW];
+    extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // [n]
+    __shared__ TopkScratch sh;
     const Geometry& g = a.g;
     int pid = blockIdx.x;
     const int row = pid % a.Q;
@@ -337,12 +278,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
     int32_t* sel = a.sel ? a.sel + prob * a.k_max : nullptr;
 
-    int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
     const int se = imin(a.S, L), ws = imax(se, L - a.W);
     const int plo = se / g.P;
     const int n = ws > se ? (ws - 1) / g.P - plo + 1 : 0;
     const int k = imin(a.k_max, n);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     if (tid == 0) a.count[prob] = k;
     if (sel)
         for (int i = k + tid; i < a.k_max; i += kTopkThreads) sel[i] = -1;
@@ -351,131 +292,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
         for (int i = tid; i < n; i += kTopkThreads) sel[i] = plo + i;
         return;
     }
-    for (int i = tid; i < kPasses * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
-    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;  // <= kTopkMaxRounds (host-checked)
-    const float* sc = a.scores + prob * g.max_pages + plo;
-    uint32_t lo = 0xffffffffu, hi = 0;
-    for (int base = 0; base < n; base += 4 * kTopkThreads) {
-        float v[4];  // four loads in flight per thread
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + u * kTopkThreads + tid;
-            v[u] = i < n ? sc[i] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + u * kTopkThreads + tid;
-            if (i < n) {
-                const uint32_t key = order_key(v[u]);
-                keys[i] = key;
-                lo = min(lo, key);
-                hi = max(hi, key);
-            }
-        }
-    }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    if (lane == 0) {
-        mm[wave][0] = lo;
-        mm[wave][1] = hi;
-    }
-    __syncthreads();
-    for (int w = 0; w < NW; ++w) {
-        lo = min(lo, mm[w][0]);
-        hi = max(hi, mm[w][1]);
-    }
-
-    uint32_t kth = hi;  // the k-th largest key
-    if (lo != hi) {
-        int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
-        uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
-        int need = k;  // keys still to take among those matching the prefix
-        for (int pass = 0; top >= 0; ++pass) {
-            const int width = top + 1 < 8 ? top + 1 : 8;
-            const int shift = top + 1 - width;
-            const uint32_t dmask = (1u << width) - 1u;
-            const int up = shift + width;  // bits >= up are decided
-            const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
-#pragma unroll 4
-            for (int i = tid; i < n; i += kTopkThreads) {
-                const uint32_t key = keys[i];
-                if ((key & hmask) == prefix) atomicAdd(&hist[pass][(key >> shift) & dmask], 1);
-            }
-            __syncthreads();
-            // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
-            const int4 c = *(const int4*)&hist[pass][252 - 4 * lane];  // digits 252-4j .. 255-4j
-            const int s = c.x + c.y + c.z + c.w;
-            const int above = wave_inclusive_scan(s) - s;  // keys with a larger digit than this lane's
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(above < need && above + s >= need);
-            const int hl = (int)__builtin_ctzll(hit);
-            int acc = __builtin_amdgcn_readlane(above, hl);
-            const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
-            const int cy = __builtin_amdgcn_readlane(c.y, hl);
-            int digit;
-            if (acc + cw >= need) {
-                digit = 255 - 4 * hl;
-            } else if (acc + cw + cz >= need) {
-                digit = 254 - 4 * hl;
-                acc += cw;
-            } else if (acc + cw + cz + cy >= need) {
-                digit = 253 - 4 * hl;
-                acc += cw + cz;
-            } else {
-                digit = 252 - 4 * hl;
-                acc += cw + cz + cy;
-            }
-            prefix |= (uint32_t)digit << shift;
-            need -= acc;
-            top = shift - 1;
-        }
-        kth = prefix;
-    }
-
-    // per-wave counts of keys equal to kth and above it, round by round
-    int gt_local = 0;
-#pragma unroll 4
-    for (int r = 0; r < rounds; ++r) {
-        const int i = r * kTopkThreads + tid;
-        const uint32_t key = i < n ? keys[i] : 0u;
-        const int ne = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key == kth));
-        gt_local += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key > kth));
-        if (lane == 0) cnt_eq[r * NW + wave] = ne;
-    }
-    if (lane == 0) gts[wave] = gt_local;
-    __syncthreads();
-    int gt = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) gt += gts[w];
-    const int need = k - gt;  // equal keys to take, lowest pages first
-    const int ncnt = rounds * NW;
-
-    // chosen: above kth, or equal to it and among the first `need` equal keys
-    // in page order (round, wave, lane); the rank of a wave's first equal key
-    // is the exclusive prefix of the counts in (round, wave) order
-    int ex[kCntChunks];
-    scan_counts(cnt_eq, ncnt, lane, ex);
-    uint32_t mine = 0;  // bit r: this thread's key of round r is chosen
-#pragma unroll 4
-    for (int r = 0; r < rounds; ++r) {
-        const int i = r * kTopkThreads + tid;
-        const uint32_t key = i < n ? keys[i] : 0u;
-        const bool eq = i < n && key == kth;
-        const int rank = pick_count(ex, r * NW + wave);
-        const bool in = i < n && (key > kth || (eq && rank + lanes_below(__builtin_amdgcn_ballot_w64(eq)) < need));
-        const int cc = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
-        if (lane == 0) cnt_in[r * NW + wave] = cc;
-        mine |= (uint32_t)in << r;
-    }
-    __syncthreads();
-    int ox[kCntChunks];
-    scan_counts(cnt_in, ncnt, lane, ox);
-    for (int r = 0; r < rounds; ++r) {
-        const int i = r * kTopkThreads + tid;
-        const bool in = (mine >> r) & 1u;
-        const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
-        const int here = pick_count(ox, r * NW + wave);
-        if (in) sel[here + lanes_below(inm)] = plo + i;
-    }
+    uint32_t lo, hi;
+    topk_load_keys(a.scores + prob * g.max_pages + plo, n, keys, lo, hi);
+    block_topk_fast(n, k, keys, lo, hi, sh, [&](int pos, int i) { sel[pos] = plo + i; });
 }
 
 template <int HD, int G, bool BF>
@@ -548,6 +367,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s)
             return hipErrorInvalidValue;
         if (e != hipSuccess) return e;
     }
+    if (a.score_only) return hipSuccess;
     const size_t lds = sizeof(uint32_t) * (size_t)(a.k_max > 0 ? g.max_pages : 1);  // <= 48 KiB (host-checked)
     hipLaunchKernelGGL(k_topk, dim3((unsigned)problems), dim3(kTopkThreads), lds, s, a);
     return hipGetLastError();

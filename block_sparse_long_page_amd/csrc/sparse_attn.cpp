@@ -80,6 +80,16 @@ int occupancy(int hd, int G, int dtype)
     return v;
 }
 
+// fewest splits that leave every workgroup of the select-and-decode kernel
+// at most kRowsWG tokens (a share of the sink + window plus a share of the
+// selected pages, each rounded up)
+long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32_t page_size)
+{
+    const long toks = (long)(sink_len > 0 ? sink_len : 0) + (window_len > 0 ? window_len : 0) +
+                      (long)(k_max > 0 ? k_max : 0) * page_size;
+    return (toks + sa::kRowsWG - 3) / (sa::kRowsWG - 2);
+}
+
 size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
 {
     return sizeof(float) * (size_t)kv->batch * kv->num_kv_heads * rows * kv->max_pages_per_seq;
@@ -140,7 +150,7 @@ int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
         if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
     }
     sa::SelectArgs a{g, q, num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages, sel_count,
-                     (float*)workspace};
+                     (float*)workspace, 0};
     return finish(sa::launch_select(a, stream), stream);
 }
 
@@ -166,6 +176,8 @@ int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int
     const long by_tokens = ntok / 256 > 0 ? ntok / 256 : 1;
     if (s > by_tokens) s = by_tokens;
     if (s < 1) s = 1;
+    const long fused = fused_min_splits(sink_len, window_len, k_max, kv->page_size);
+    if (s < fused) s = fused;
     if (s > kMaxSplits) s = kMaxSplits;
     return (int32_t)s;
 }
@@ -194,6 +206,52 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
                      sink_len, window_len, parts,      scale * 1.4426950408889634f,   num_splits,
                      split_stride, part_o, part_ml};
     return finish(sa::launch_decode(a, stream), stream);
+}
+
+int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                            int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                            float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                            void* workspace, size_t workspace_bytes, float* part_o, float* part_ml,
+                            hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    if (!q || !meta || !sel_count || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 ||
+        token_budget < 0)
+        return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    const int k_max = token_budget / kv->page_size;
+    if (k_max > 0 && !sel_pages) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    if (k_max > 0) {
+        if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
+        if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
+    }
+    const bool fused = kv->dtype == SA_BF16 && k_max >= 1 && k_max <= sa::kSelCap &&
+                       kv->max_pages_per_seq <= sa::kFusedMaxCand &&
+                       num_splits >= fused_min_splits(sink_len, window_len, k_max, kv->page_size);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    if (!fused) {
+        const int r1 = sparse_attn_select(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget,
+                                          sel_pages, sel_count, workspace, workspace_bytes, stream);
+        if (r1 != SA_OK) return r1;
+        return sparse_attn_decode(kv, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, SA_PART_ALL,
+                                  softmax_scale, num_splits, num_splits, part_o, part_ml, stream);
+    }
+    sa::SelectArgs sarg{g,        q,          num_q_rows, meta,      score_mode, sink_len, window_len,
+                        k_max,    sel_pages,  sel_count,  (float*)workspace, 1};
+    const int r1 = finish(sa::launch_select(sarg, stream), stream);
+    if (r1 != SA_OK) return r1;
+    sa::SelectDecodeArgs d{g,          q,          num_q_rows, (const float*)workspace,
+                           k_max,      sink_len,   window_len, scale * 1.4426950408889634f,
+                           num_splits, num_splits, part_o,     part_ml,
+                           sel_pages,  sel_count};
+    return finish(sa::launch_select_decode(d, stream), stream);
 }
 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,

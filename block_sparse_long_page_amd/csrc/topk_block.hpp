@@ -1,0 +1,482 @@
+// Block-wide top-k of the page scores of one (sequence, KV head, row), for
+// 512-thread workgroups: used by the selection kernel and by the decode kernel
+// that selects its own pages.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace sa {
+
+// order-preserving float -> uint32 (larger float, larger key); -0 maps to +0
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kTopkThreads = 512;
+constexpr int kTopkMaxRounds = 24;  // keys per thread: up to 12288 candidate pages
+
+// Number of lanes of this wave below the calling lane whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+constexpr int kCntChunks = (kTopkMaxRounds * (kTopkThreads / 64) + 63) / 64;
+
+// Exclusive prefix sums of cnt[0 .. n) held across the wave: entry e's prefix
+// is lane e % 64 of ex[e / 64].
+__device__ __forceinline__ void scan_counts(const int* cnt, int n, int lane, int (&ex)[kCntChunks])
+{
+    int carry = 0;
+#pragma unroll
+    for (int c = 0; c < kCntChunks; ++c) {
+        const int e = c * 64 + lane;
+        const int v = e < n ? cnt[e] : 0;
+        const int inc = wave_inclusive_scan(v);
+        ex[c] = inc - v + carry;
+        carry += __builtin_amdgcn_readlane(inc, 63);
+    }
+}
+
+// the prefix of entry e (wave-uniform)
+__device__ __forceinline__ int pick_count(const int (&ex)[kCntChunks], int e)
+{
+    const int c = e >> 6, l = e & 63;
+    int v = __builtin_amdgcn_readlane(ex[0], l);
+#pragma unroll
+    for (int i = 1; i < kCntChunks; ++i)
+        if (c == i) v = __builtin_amdgcn_readlane(ex[i], l);
+    return v;
+}
+
+constexpr int kTopkPasses = 4;  // 32 key bits, 8 per pass
+
+constexpr int kTopkBoundMax = 64;  // keys of the boundary digit ranked directly by one wave
+
+struct TopkScratch {
+    int hist[kTopkPasses][256];
+    uint32_t mm[kTopkThreads / 64][2];
+    int cnt_eq[kTopkMaxRounds * (kTopkThreads / 64)];  // round-major: flat (round, wave) order is page order
+    int cnt_in[kTopkMaxRounds * (kTopkThreads / 64)];
+    int gts[kTopkThreads / 64];
+    // one-pass path: the boundary digit's keys, then a bitmap of the chosen indices
+    int nb;
+    uint32_t b_key[kTopkBoundMax];
+    int b_idx[kTopkBoundMax];
+    uint64_t chosen[kTopkMaxRounds * kTopkThreads / 64];
+};
+
+// The k largest of the n scores sc[0 .. n) (1 <= k < n <= kTopkThreads *
+// kTopkMaxRounds), ties to the lower index, in ascending index order:
+// emit(position, index) once per chosen index.  Called by all 512 threads
+// with the n order keys in keys[] (LDS) and each thread's min and max key.
+//  1. min and max of the keys give the bits every key shares;
+//  2. radix select, 8 bits at a time from the highest differing bit: an LDS
+//     histogram of the digit among the keys that match the prefix decided so
+//     far; every wave then scans the histogram itself and finds the digit
+//     where the count from the top reaches k;
+//  3. compaction in ascending index order: every key above the k-th, then the
+//     lowest indices among those equal to it, placed by wave scans of the
+//     per-wave counts.
+// Loops over the keys stay rolled (unrolled by four) so the code fits the
+// instruction cache.
+// Loads the order keys of sc[0 .. n) into keys[] (all of a thread's loads in
+// flight together) and returns this thread's min and max key.
+__device__ __forceinline__ void topk_load_keys(const float* sc, int n, uint32_t* keys, uint32_t& lo, uint32_t& hi)
+{
+    const int tid = threadIdx.x;
+    lo = 0xffffffffu;
+    hi = 0;
+    for (int base = 0; base < n; base += 4 * kTopkThreads) {
+        float v[4];  // four loads in flight per thread
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kTopkThreads + tid;
+            v[u] = i < n ? sc[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kTopkThreads + tid;
+            if (i < n) {
+                const uint32_t key = order_key(v[u]);
+                keys[i] = key;
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+        }
+    }
+}
+
+template <typename Emit>
+__device__ __forceinline__ void block_topk_keys(int n, int k, const uint32_t* keys, uint32_t lo, uint32_t hi,
+                                                TopkScratch& sh, Emit emit)
+{
+    constexpr int NW = kTopkThreads / 64;
+    constexpr int kPasses = kTopkPasses;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kPasses * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;  // <= kTopkMaxRounds (host-checked)
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        sh.mm[wave][0] = lo;
+        sh.mm[wave][1] = hi;
+    }
+    __syncthreads();
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, sh.mm[w][0]);
+        hi = max(hi, sh.mm[w][1]);
+    }
+
+    uint32_t kth = hi;  // the k-th largest key
+    if (lo != hi) {
+        int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+        uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+        int need = k;  // keys still to take among those matching the prefix
+        for (int pass = 0; top >= 0; ++pass) {
+            const int width = top + 1 < 8 ? top + 1 : 8;
+            const int shift = top + 1 - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            const int up = shift + width;  // bits >= up are decided
+            const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
+#pragma unroll 4
+            for (int i = tid; i < n; i += kTopkThreads) {
+                const uint32_t key = keys[i];
+                if ((key & hmask) == prefix) atomicAdd(&sh.hist[pass][(key >> shift) & dmask], 1);
+            }
+            __syncthreads();
+            // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+            const int4 c = *(const int4*)&sh.hist[pass][252 - 4 * lane];  // digits 252-4j .. 255-4j
+            const int s = c.x + c.y + c.z + c.w;
+            const int above = wave_inclusive_scan(s) - s;  // keys with a larger digit than this lane's
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(above < need && above + s >= need);
+            const int hl = (int)__builtin_ctzll(hit);
+            int acc = __builtin_amdgcn_readlane(above, hl);
+            const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+            const int cy = __builtin_amdgcn_readlane(c.y, hl);
+            int digit;
+            if (acc + cw >= need) {
+                digit = 255 - 4 * hl;
+            } else if (acc + cw + cz >= need) {
+                digit = 254 - 4 * hl;
+                acc += cw;
+            } else if (acc + cw + cz + cy >= need) {
+                digit = 253 - 4 * hl;
+                acc += cw + cz;
+            } else {
+                digit = 252 - 4 * hl;
+                acc += cw + cz + cy;
+            }
+            prefix |= (uint32_t)digit << shift;
+            need -= acc;
+            top = shift - 1;
+        }
+        kth = prefix;
+    }
+
+    // per-wave counts of keys equal to kth and above it, round by round
+    int gt_local = 0;
+#pragma unroll 4
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const int ne = __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key == kth));
+        gt_local += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && key > kth));
+        if (lane == 0) sh.cnt_eq[r * NW + wave] = ne;
+    }
+    if (lane == 0) sh.gts[wave] = gt_local;
+    __syncthreads();
+    int gt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) gt += sh.gts[w];
+    const int need = k - gt;  // equal keys to take, lowest pages first
+    const int ncnt = rounds * NW;
+
+    // chosen: above kth, or equal to it and among the first `need` equal keys
+    // in page order (round, wave, lane); the rank of a wave's first equal key
+    // is the exclusive prefix of the counts in (round, wave) order
+    int ex[kCntChunks];
+    scan_counts(sh.cnt_eq, ncnt, lane, ex);
+    uint32_t mine = 0;  // bit r: this thread's key of round r is chosen
+#pragma unroll 4
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const bool eq = i < n && key == kth;
+        const int rank = pick_count(ex, r * NW + wave);
+        const bool in = i < n && (key > kth || (eq && rank + lanes_below(__builtin_amdgcn_ballot_w64(eq)) < need));
+        const int cc = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
+        if (lane == 0) sh.cnt_in[r * NW + wave] = cc;
+        mine |= (uint32_t)in << r;
+    }
+    __syncthreads();
+    int ox[kCntChunks];
+    scan_counts(sh.cnt_in, ncnt, lane, ox);
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const bool in = (mine >> r) & 1u;
+        const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
+        const int here = pick_count(ox, r * NW + wave);
+        if (in) emit(here + lanes_below(inm), i);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The same selection with one radix pass in the common case.  After the bits
+// every key shares, one 8-bit digit histogram gives the boundary digit d (the
+// count of keys with a larger digit is below k, with d included it reaches
+// k): keys with a larger digit are chosen outright (set in a bitmap by wave
+// ballots), and when at most 64 keys carry digit d they are gathered and one
+// wave ranks them by direct comparison of (key, lower index first), taking
+// the best k - (count above).  One wave then emits the bitmap in ascending
+// index order.  More than 64 keys at the boundary (many equal or nearly
+// equal scores) falls back to the multi-pass select above, same result.
+// ---------------------------------------------------------------------------
+template <typename Emit>
+__device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* keys, uint32_t lo, uint32_t hi,
+                                                TopkScratch& sh, Emit emit)
+{
+    constexpr int NW = kTopkThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;
+    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[0][i] = 0;
+    if (tid == 0) sh.nb = 0;
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        sh.mm[wave][0] = lo;
+        sh.mm[wave][1] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, sh.mm[w][0]);
+        hi = max(hi, sh.mm[w][1]);
+    }
+    if (lo == hi) {  // every key equal: the lowest k indices
+        for (int i = tid; i < k; i += kTopkThreads) emit(i, i);
+        return;
+    }
+    const int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll 4
+    for (int i = tid; i < n; i += kTopkThreads) atomicAdd(&sh.hist[0][(keys[i] >> shift) & dmask], 1);
+    __syncthreads();
+    // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+    const int4 c = *(const int4*)&sh.hist[0][252 - 4 * lane];
+    const int s4 = c.x + c.y + c.z + c.w;
+    const int above4 = wave_inclusive_scan(s4) - s4;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(above4 < k && above4 + s4 >= k);
+    const int hl = (int)__builtin_ctzll(hit);
+    int above = __builtin_amdgcn_readlane(above4, hl);
+    const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+    const int cy = __builtin_amdgcn_readlane(c.y, hl), cx = __builtin_amdgcn_readlane(c.x, hl);
+    int d, nd;
+    if (above + cw >= k) {
+        d = 255 - 4 * hl;
+        nd = cw;
+    } else if (above + cw + cz >= k) {
+        d = 254 - 4 * hl;
+        nd = cz;
+        above += cw;
+    } else if (above + cw + cz + cy >= k) {
+        d = 253 - 4 * hl;
+        nd = cy;
+        above += cw + cz;
+    } else {
+        d = 252 - 4 * hl;
+        nd = cx;
+        above += cw + cz + cy;
+    }
+    if (nd > kTopkBoundMax) {  // uniform: every wave read the same histogram
+        __syncthreads();       // the multi-pass select clears the histogram first
+        block_topk_keys(n, k, keys, lo, hi, sh, emit);
+        return;
+    }
+    const int need = k - above;  // boundary keys to take, 1 .. nd
+    // larger digits into the bitmap; boundary keys into the small list
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * kTopkThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const int dig = (int)((key >> shift) & dmask);
+        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && dig > d);
+        if (lane == 0) sh.chosen[r * NW + wave] = up;
+        if (i < n && dig == d) {
+            const int slot = atomicAdd(&sh.nb, 1);
+            sh.b_key[slot] = key;
+            sh.b_idx[slot] = i;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // rank of each boundary key among them: larger key first, then lower index
+        const bool mine = lane < nd;
+        const uint32_t bk = mine ? sh.b_key[lane] : 0u;
+        const int bi = mine ? sh.b_idx[lane] : 0;
+        int rank = 0;
+        for (int t = 0; t < nd; ++t) {
+            const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bk, t);
+            const int it = __builtin_amdgcn_readlane(bi, t);
+            rank += kt > bk || (kt == bk && it < bi);
+        }
+        if (mine && rank < need) atomicOr((unsigned long long*)&sh.chosen[bi >> 6], 1ull << (bi & 63));
+        __builtin_amdgcn_wave_barrier();
+        // emit in ascending index order: word w holds indices 64w .. 64w+63
+        const int nwords = (n + 63) / 64;
+        int base = 0;
+        for (int w0 = 0; w0 < nwords; w0 += 64) {
+            const int w = w0 + lane;
+            uint64_t bits = w < nwords ? sh.chosen[w] : 0ull;
+            const int cnt = __builtin_popcountll(bits);
+            const int inc = wave_inclusive_scan(cnt);
+            int pos = base + inc - cnt;
+            while (bits) {
+                const int b = __builtin_ctzll(bits);
+                emit(pos++, 64 * w + b);
+                bits &= bits - 1;
+            }
+            base += __builtin_amdgcn_readlane(inc, 63);
+        }
+    }
+}
+
+// The same from the scores in global memory.
+template <typename Emit>
+__device__ __forceinline__ void block_topk(const float* sc, int n, int k, uint32_t* keys, TopkScratch& sh, Emit emit)
+{
+    uint32_t lo, hi;
+    topk_load_keys(sc, n, keys, lo, hi);
+    block_topk_keys(n, k, keys, lo, hi, sh, emit);
+}
+
+// ---------------------------------------------------------------------------
+// One-wave top-k: the same selection (k largest of n order keys, ties to the
+// lower index, ascending index order) by a single wave, with no workgroup
+// barrier.  Lane l owns the contiguous keys [l * kpl, (l + 1) * kpl) with
+// kpl = wave_topk_kpl(n); keys[] (LDS) holds them, entries past n unused.
+//  1. min and max give the bits every key shares;
+//  2. radix select, 8 bits at a time from the highest differing bit: the
+//     lanes add the digit of every key matching the prefix decided so far into
+//     a 256-bin LDS histogram (LDS operations of one wave complete in order, so
+//     no barrier is needed), then scan it (4 bins per lane) and take the digit
+//     where the count from the top reaches k;
+//  3. each lane counts its keys above the k-th and equal to it; exclusive
+//     wave scans of those counts place every chosen key, equal keys taken in
+//     index order until k are chosen.
+// ---------------------------------------------------------------------------
+constexpr int kWaveTopkChunk = 32;  // keys a lane holds in registers at a time
+
+__host__ __device__ __forceinline__ int wave_topk_kpl(int n)
+{
+    const int kpl = (n + 63) / 64;
+    return (kpl + kWaveTopkChunk - 1) / kWaveTopkChunk * kWaveTopkChunk;
+}
+
+// f(key, index, valid) for each key of this lane, in index order
+template <typename F>
+__device__ __forceinline__ void wave_topk_scan_keys(const uint32_t* keys, int n, int kpl, int lane, F f)
+{
+    const int base = lane * kpl;
+    for (int c = 0; c < kpl; c += kWaveTopkChunk) {
+        uint32_t kv[kWaveTopkChunk];
+#pragma unroll
+        for (int v = 0; v < kWaveTopkChunk / 4; ++v) {
+            const uint4 w = *(const uint4*)(keys + base + c + 4 * v);
+            kv[4 * v] = w.x;
+            kv[4 * v + 1] = w.y;
+            kv[4 * v + 2] = w.z;
+            kv[4 * v + 3] = w.w;
+        }
+#pragma unroll
+        for (int m = 0; m < kWaveTopkChunk; ++m) {
+            const int i = base + c + m;
+            f(kv[m], i, i < n);
+        }
+    }
+}
+
+template <typename Emit>
+__device__ __forceinline__ void wave_topk(const uint32_t* keys, int n, int k, int* hist, Emit emit)
+{
+    const int lane = threadIdx.x & 63;
+    const int kpl = wave_topk_kpl(n);
+    uint32_t lo = 0xffffffffu, hi = 0;
+    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
+        if (ok) {
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+    });
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+
+    uint32_t kth = hi;  // the k-th largest key
+    if (lo != hi) {
+        int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+        uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+        int need = k;  // keys still to take among those matching the prefix
+        while (top >= 0) {
+            const int width = top + 1 < 8 ? top + 1 : 8;
+            const int shift = top + 1 - width;
+            const uint32_t dmask = (1u << width) - 1u;
+            const int up = shift + width;  // bits >= up are decided
+            const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
+            *(int4*)(hist + 4 * lane) = make_int4(0, 0, 0, 0);
+            wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
+                if (ok && (key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+            });
+            // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+            const int4 c = *(const int4*)(hist + 252 - 4 * lane);
+            const int s = c.x + c.y + c.z + c.w;
+            const int above = wave_inclusive_scan(s) - s;  // keys with a larger digit than this lane's
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(above < need && above + s >= need);
+            const int hl = (int)__builtin_ctzll(hit);
+            int acc = __builtin_amdgcn_readlane(above, hl);
+            const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+            const int cy = __builtin_amdgcn_readlane(c.y, hl);
+            int digit;
+            if (acc + cw >= need) {
+                digit = 255 - 4 * hl;
+            } else if (acc + cw + cz >= need) {
+                digit = 254 - 4 * hl;
+                acc += cw;
+            } else if (acc + cw + cz + cy >= need) {
+                digit = 253 - 4 * hl;
+                acc += cw + cz;
+            } else {
+                digit = 252 - 4 * hl;
+                acc += cw + cz + cy;
+            }
+            prefix |= (uint32_t)digit << shift;
+            need -= acc;
+            top = shift - 1;
+        }
+        kth = prefix;
+    }
+
+    // keys above kth and equal to it: per lane, then placed by wave scans
+    int gt = 0, eq = 0;
+    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
+        gt += ok && key > kth;
+        eq += ok && key == kth;
+    });
+    const int gt_all = wave_inclusive_scan(gt);
+    const int need = k - __builtin_amdgcn_readlane(gt_all, 63);  // equal keys to take, lowest indices first
+    int eq_rank = wave_inclusive_scan(eq) - eq;                   // equal keys in lower lanes
+    const int take_eq = imax(0, imin(eq, need - eq_rank));
+    int pos = wave_inclusive_scan(gt + take_eq) - (gt + take_eq);
+    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int i, bool ok) {
+        bool in = ok && key > kth;
+        if (ok && key == kth) {
+            in = eq_rank < need;
+            ++eq_rank;
+        }
+        if (in) emit(pos++, i);
+    });
+}
+
+}  // namespace sa

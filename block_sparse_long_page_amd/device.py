@@ -104,6 +104,17 @@ class SparseDecoder:
                              self.k_max, self.sink, self.window if window is None else window, parts, scale,
                              self.splits, 0, self.part_o, self.part_ml, stream)
 
+    def select_decode(self, q: torch.Tensor, scale: float = 0.0, stream=None):
+        """Selection and decode of a selecting step (sparse_attn_decode_step)."""
+        B.sparse_attn_decode_step(self.desc, q, self.Q, self.meta, self.mode, self.sink, self.window, self.budget,
+                                  scale, self.splits, self.sel, self.count, self.ws, self.ws_bytes, self.part_o,
+                                  self.part_ml, stream)
+
+    def fused_step(self, q: torch.Tensor, stream=None):
+        self.select_decode(q, stream=stream)
+        self.combine(stream=stream)
+        return self.out
+
     def combine(self, stream=None):
         B.sparse_attn_combine(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
                               self.out_dtype, self.lse, stream)

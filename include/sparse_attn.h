@@ -14,6 +14,9 @@
  *                                the selected pages, split over the token set
  *   sparse_attn_combine          log-sum-exp merge of the split partials
  *
+ * sparse_attn_decode_step runs select and decode of a selecting step with the
+ * top-k inside the decode kernel (two launches instead of three).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Ownership.  The caller allocates and owns every device buffer and the
@@ -207,7 +210,33 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
                        float softmax_scale, int32_t num_splits, int32_t split_stride, float* part_o, float* part_ml,
                        hipStream_t stream);
 
-/* A split count that fills the GPU for this shape (host arithmetic only). */
+/*
+ * One selecting step in two launches: the page scores of sparse_attn_select,
+ * then one kernel that ranks the pages and decodes.  Each of its workgroups
+ * takes its share of the sink and window tokens, issues their first loads,
+ * runs the top-k of its row's scores while they are in flight (the selection
+ * depends only on the scores, so every workgroup of a row computes the same
+ * page list), then takes its share of the selected pages' middle tokens.
+ * Same arithmetic as sparse_attn_select followed by sparse_attn_decode with
+ * parts = SA_PART_ALL; the tokens of a row are split over the workgroups
+ * differently, so the partials differ from sparse_attn_decode's by rounding
+ * only, and their merge by sparse_attn_combine is the same attention.
+ *   Arguments as in sparse_attn_select and sparse_attn_decode (split_stride
+ *   = num_splits).  Writes sel_pages / sel_count as sparse_attn_select does,
+ *   and part_o / part_ml for sparse_attn_combine.
+ * bf16 caches with 1 <= k_max <= 1024, at most 8192 pages per sequence, and
+ * num_splits >= (S + W + k_max * page_size) / 2046 (at most 2048 tokens per
+ * workgroup) take the fused kernel; any other valid call runs
+ * sparse_attn_select and then sparse_attn_decode, with the same results.
+ * Errors: those of sparse_attn_select and sparse_attn_decode.
+ */
+int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                            int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                            float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                            void* workspace, size_t workspace_bytes, float* part_o, float* part_ml,
+                            hipStream_t stream);
+
+/* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,
                                    int32_t k_max);
 

@@ -22,7 +22,7 @@ def test_exports_every_header_function():
     names = B.header_symbols()
     assert set(names) == {
         "sparse_attn_build_page_meta", "sparse_attn_select", "sparse_attn_workspace_bytes", "sparse_attn_decode",
-        "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string"}
+        "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -139,6 +139,41 @@ def test_decode_checks():
     assert dec(parts=4) == B.SA_ERR_INVALID_ARG
     assert dec(stride=3) == B.SA_ERR_INVALID_ARG  # fewer slots than splits
     assert dec(stride=1025) == B.SA_ERR_INVALID_ARG
+
+
+def test_decode_step_checks():
+    lib = B.library()
+    d = _desc()
+    ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
+
+    def step(**kw):
+        a = dict(q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, scale=0.0, splits=4, sel=DEV, cnt=DEV,
+                 ws=DEV, wsb=ws, po=DEV, pml=DEV)
+        a.update(kw)
+        return lib.sparse_attn_decode_step(ctypes.byref(d), a["q"], a["rows"], a["meta"], a["mode"], a["S"], a["W"],
+                                           a["budget"], a["scale"], a["splits"], a["sel"], a["cnt"], a["ws"],
+                                           a["wsb"], a["po"], a["pml"], None)
+
+    assert step(q=None) == B.SA_ERR_INVALID_ARG
+    assert step(meta=None) == B.SA_ERR_INVALID_ARG
+    assert step(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert step(sel=None) == B.SA_ERR_INVALID_ARG
+    assert step(po=None) == B.SA_ERR_INVALID_ARG
+    assert step(pml=None) == B.SA_ERR_INVALID_ARG
+    assert step(rows=0) == B.SA_ERR_INVALID_ARG
+    assert step(S=-1) == B.SA_ERR_INVALID_ARG
+    assert step(W=0) == B.SA_ERR_INVALID_ARG
+    assert step(budget=-1) == B.SA_ERR_INVALID_ARG
+    assert step(splits=0) == B.SA_ERR_INVALID_ARG
+    assert step(splits=1025) == B.SA_ERR_INVALID_ARG
+    assert step(scale=float("nan")) == B.SA_ERR_INVALID_ARG
+    assert step(ws=None) == B.SA_ERR_INVALID_ARG
+    assert step(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert step(mode=7) == B.SA_ERR_UNSUPPORTED
+    for bad, code in BAD_DESCS:
+        dd = _desc(**bad)
+        assert lib.sparse_attn_decode_step(ctypes.byref(dd), DEV, 1, DEV, 0, 16, 16, 32, 0.0, 4, DEV, DEV, DEV, ws,
+                                           DEV, DEV, None) == code
 
 
 def test_combine_checks():

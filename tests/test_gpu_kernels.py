@@ -101,6 +101,76 @@ def test_selection_and_output(name, mode):
 
 
 @pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("splits", [None, 1, 5])
+def test_select_decode_step(name, mode, splits):
+    """sparse_attn_decode_step: the same page lists as sparse_attn_select, the
+    oracle's attention over them, and bitwise-repeatable results."""
+    pr = _problem(name, mode, seed=7)
+    dc, dec = _run(pr, splits=splits)
+    sel_ref, cnt_ref = dec.selection()
+    q = to_device(pr.q)
+    dec.sel.fill_(-7)
+    dec.count.fill_(-7)
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    np.testing.assert_array_equal(cnt, cnt_ref)
+    np.testing.assert_array_equal(sel, sel_ref)
+    full = dec.sel.cpu().numpy()
+    for idx in np.ndindex(cnt.shape):
+        assert (full[idx][cnt[idx]:] == -1).all()
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                     sel=sel, cnt=cnt)
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, name)
+    check_lse(dec.lse_f32(), ref.lse, name)
+    out1, lse1 = dec.out.clone(), dec.lse.clone()
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.out, out1) and torch.equal(dec.lse, lse1)
+
+
+@pytest.mark.parametrize("pattern", ["all-equal", "two-values", "small-tie-band"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_tied_scores_take_the_lower_pages(pattern, fused):
+    """Exact ties in the page scores (pages whose tokens all hold one key
+    vector) go to the lower logical page, as in the oracle: every key equal,
+    a boundary of ~n/2 equal keys (the multi-pass select) and a boundary of a
+    few dozen equal keys (ranked directly)."""
+    pr = synth.random_problem(B=2, Hq=16, Hkv=2, hd=128, P=8, seq_lens=[2048, 1500], sink=32, window=64,
+                              budget=30 * 8, mode="quest", seed=11, shuffle=True)
+    c = pr.cache
+    rng = np.random.default_rng(3)
+    vecs = synth.store(rng.standard_normal((3, c.Hkv, c.hd)).astype(np.float32), c.dtype)
+    for b in range(c.B):
+        n_pages = -(-int(c.seq_lens[b]) // c.P)
+        for p in range(n_pages):
+            if pattern == "all-equal":
+                w = 0
+            elif pattern == "two-values":
+                w = p % 2
+            else:  # 10 pages of one value, 40 of a second, the rest a third
+                w = 0 if p % 50 < 10 else 1 if p % 50 < 50 and p < 50 else 2
+            c.k[c.block_table[b, p]] = vecs[w][:, None, :]
+    dc = DeviceCache.from_host(c)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+    q = to_device(pr.q)
+    dec.build_meta()
+    if fused:
+        dec.fused_step(q)
+    else:
+        dec.step(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    r = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, want_scores=True)
+    np.testing.assert_array_equal(cnt, r.cnt)
+    np.testing.assert_array_equal(sel, r.sel)  # exact ties: the same (lowest) pages
+    ref = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, sel=sel,
+                     cnt=cnt)
+    check_output(dec.out_f32(), ref.out, c.dtype, pattern)
+
+
+@pytest.mark.parametrize("name", list(CASES))
 def test_dense_path(name):
     pr = _problem(name, "quest")
     dc, dec = _run(pr, dense=True)

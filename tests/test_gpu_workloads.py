@@ -51,6 +51,17 @@ def test_single_step_workload(wl):
     same = int((sel == r.sel).all(axis=-1).sum())
     _say(f"[{wl.name}] max-abs {err:.2e}, pages in band {band}, identical sets {same}/{cnt.size}, "
          f"total {time.time() - t0:.1f}s")
+    # the selecting step with the top-k inside the decode kernel (what the benchmark times)
+    dec.sel.fill_(-7)
+    dec.count.fill_(-7)
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    sel2, cnt2 = dec.selection()
+    np.testing.assert_array_equal(cnt2, cnt)
+    np.testing.assert_array_equal(sel2, sel)  # same scores, same ranking
+    err2 = check_output(dec.out_f32(), ref.out, pr.cache.dtype, wl.name + " fused")
+    check_lse(dec.lse_f32(), ref.lse, wl.name + " fused")
+    _say(f"[{wl.name}] fused step max-abs {err2:.2e}")
 
 
 def test_hybrid_schedule():
@@ -74,11 +85,12 @@ def test_hybrid_schedule():
                 last = (L - 1) // dc.P
                 dec.build_meta(last, last + 1)
             q = to_device(hs.q[li][t])
-            if t % R == 0:
+            if t % R == 0:  # a selecting step: top-k inside the decode kernel
                 t_ref = t
-                dec.select(q, window=W)
+                dec.select_decode(q)
+            else:
+                dec.decode(q, window=W + (t - t_ref))
             w_eff = W + (t - t_ref)
-            dec.decode(q, window=w_eff)
             dec.combine()
             if t in check_at:
                 torch.cuda.synchronize()
