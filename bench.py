@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "block_sparse_long_page_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "block_sparse_long_page_amd", "csrc")
 
 
 def log(*a):
@@ -83,14 +83,24 @@ def copy_probe():
     print(json.dumps({"copy_bytes": n, "ms": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}))
 
 
-def traffic_record():
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when the decode source changed since they were taken."""
+def kernel_sources_sha256() -> str:
+    """Digest of every kernel source (the .hip and .hpp files of the library)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or
+    None when a kernel source changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("decode_src_sha256") != src_hash:
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256() or rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
 
@@ -310,7 +320,7 @@ def main():
                    "step": mode},
         "roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_record(), "bytes_per_launch": dec_bytes,
+                     "traffic": traffic_record(dec_kernel), "bytes_per_launch": dec_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "bytes_per_step": sb.as_dict(),

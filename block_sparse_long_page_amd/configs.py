@@ -68,32 +68,32 @@ class Workload:
         return replace(self, **kw)
 
 
-# configuration 0: tiny fp32 case with one planted needle page
+# tiny fp32 case with one planted needle page
 TINY = Workload(
     name="tiny-fp32-2k", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype="f32",
     context=2048, page_size=16, sink=16, window=64, budget=128, seed=0,
 )
 
-# configuration 1: one Qwen3-8B-shaped layer, 32k context, budget L/16
+# one Qwen3-8B-shaped layer, 32k context, budget L/16
 QWEN3_8B = Workload(
     name="qwen3-8b-layer-32k", batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
     context=32768, page_size=16, sink=256, window=1024, budget=32768 // 16, seed=1,
 )
 
-# configuration 2 (headline): one Llama-3-70B-shaped layer, 128k context, GQA-8
+# one Llama-3-70B-shaped layer, 128k context, GQA-8
 LLAMA3_70B = Workload(
     name="llama3-70b-layer-128k", batch=4, num_q_heads=64, num_kv_heads=8, head_dim=128, dtype="bf16",
     context=131072, page_size=64, sink=256, window=4096, budget=131072 // 16, seed=2,
 )
 
-# configuration 3: hybrid model, 3 full-attention layers at 256k, 128 decode steps
+# hybrid model, 3 full-attention layers at 256k, 128 decode steps
 HYBRID_256K = Workload(
     name="hybrid-3layer-256k", batch=4, num_q_heads=32, num_kv_heads=4, head_dim=128, dtype="bf16",
     context=262144, page_size=32, sink=256, window=2048, budget=8192, seed=3,
     layers=(Layer(2048, 8192), Layer(4096, 4096), Layer(1024, 16384)), steps=128, refresh=32,
 )
 
-# configuration 4: semantic blocks at 512K, 64-query chunk per step
+# semantic blocks at 512K, 64-query chunk per step
 SEMANTIC_512K = Workload(
     name="semantic-512k", batch=2, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16",
     context=524288 + 64, page_size=2048, sink=0, window=64, budget=524288 // 16, mode="centroid",

@@ -30,12 +30,6 @@ namespace {
 #ifndef SA_MFMA_TPS
 #define SA_MFMA_TPS 1
 #endif
-#ifndef SA_MFMA_NW
-#define SA_MFMA_NW 8
-#endif
-#ifndef SA_MFMA_MINB
-#define SA_MFMA_MINB 1
-#endif
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -263,7 +257,7 @@ struct MfmaPlan {
     static constexpr int VROW = HD * 2;                // bytes per value row
     static constexpr int VTILE = 16 * VROW + 4 * 32;   // LDS bytes of one value tile (padded)
     static constexpr int TPS = SA_MFMA_TPS;            // tiles per wave per round
-    static constexpr int NW = SA_MFMA_NW;              // waves per workgroup
+    static constexpr int NW = 8;                       // waves per workgroup: one workgroup fills a CU
     static constexpr int RT = NW * TPS * 16;           // tokens per round
     static constexpr int vbytes() { return NW * TPS * VTILE; }
     static constexpr int obytes() { return NW * G * HD * 4; }
@@ -555,7 +549,7 @@ __device__ __forceinline__ void resolve_rows(int* rows, int first, int cnt, Tok 
 }
 
 template <int HD, int G>
-__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_decode_mfma(DecodeArgs a)
+__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(DecodeArgs a)
 {
     using Core = MfmaCore<HD, G>;
     constexpr int NW = Core::NW;
@@ -619,7 +613,7 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_de
 // of the selected pages' middle tokens.  The workgroup of split 0 also writes
 // the page list and its count.
 template <int HD, int G>
-__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW), SA_MFMA_MINB) void k_select_decode_mfma(SelectDecodeArgs a)
+__global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mfma(SelectDecodeArgs a)
 {
     using Core = MfmaCore<HD, G>;
     constexpr int NW = Core::NW, RT = Core::RT;

@@ -344,139 +344,4 @@ __device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* ke
     }
 }
 
-// The same from the scores in global memory.
-template <typename Emit>
-__device__ __forceinline__ void block_topk(const float* sc, int n, int k, uint32_t* keys, TopkScratch& sh, Emit emit)
-{
-    uint32_t lo, hi;
-    topk_load_keys(sc, n, keys, lo, hi);
-    block_topk_keys(n, k, keys, lo, hi, sh, emit);
-}
-
-// ---------------------------------------------------------------------------
-// One-wave top-k: the same selection (k largest of n order keys, ties to the
-// lower index, ascending index order) by a single wave, with no workgroup
-// barrier.  Lane l owns the contiguous keys [l * kpl, (l + 1) * kpl) with
-// kpl = wave_topk_kpl(n); keys[] (LDS) holds them, entries past n unused.
-//  1. min and max give the bits every key shares;
-//  2. radix select, 8 bits at a time from the highest differing bit: the
-//     lanes add the digit of every key matching the prefix decided so far into
-//     a 256-bin LDS histogram (LDS operations of one wave complete in order, so
-//     no barrier is needed), then scan it (4 bins per lane) and take the digit
-//     where the count from the top reaches k;
-//  3. each lane counts its keys above the k-th and equal to it; exclusive
-//     wave scans of those counts place every chosen key, equal keys taken in
-//     index order until k are chosen.
-// ---------------------------------------------------------------------------
-constexpr int kWaveTopkChunk = 32;  // keys a lane holds in registers at a time
-
-__host__ __device__ __forceinline__ int wave_topk_kpl(int n)
-{
-    const int kpl = (n + 63) / 64;
-    return (kpl + kWaveTopkChunk - 1) / kWaveTopkChunk * kWaveTopkChunk;
-}
-
-// f(key, index, valid) for each key of this lane, in index order
-template <typename F>
-__device__ __forceinline__ void wave_topk_scan_keys(const uint32_t* keys, int n, int kpl, int lane, F f)
-{
-    const int base = lane * kpl;
-    for (int c = 0; c < kpl; c += kWaveTopkChunk) {
-        uint32_t kv[kWaveTopkChunk];
-#pragma unroll
-        for (int v = 0; v < kWaveTopkChunk / 4; ++v) {
-            const uint4 w = *(const uint4*)(keys + base + c + 4 * v);
-            kv[4 * v] = w.x;
-            kv[4 * v + 1] = w.y;
-            kv[4 * v + 2] = w.z;
-            kv[4 * v + 3] = w.w;
-        }
-#pragma unroll
-        for (int m = 0; m < kWaveTopkChunk; ++m) {
-            const int i = base + c + m;
-            f(kv[m], i, i < n);
-        }
-    }
-}
-
-template <typename Emit>
-__device__ __forceinline__ void wave_topk(const uint32_t* keys, int n, int k, int* hist, Emit emit)
-{
-    const int lane = threadIdx.x & 63;
-    const int kpl = wave_topk_kpl(n);
-    uint32_t lo = 0xffffffffu, hi = 0;
-    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
-        if (ok) {
-            lo = min(lo, key);
-            hi = max(hi, key);
-        }
-    });
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-
-    uint32_t kth = hi;  // the k-th largest key
-    if (lo != hi) {
-        int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
-        uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
-        int need = k;  // keys still to take among those matching the prefix
-        while (top >= 0) {
-            const int width = top + 1 < 8 ? top + 1 : 8;
-            const int shift = top + 1 - width;
-            const uint32_t dmask = (1u << width) - 1u;
-            const int up = shift + width;  // bits >= up are decided
-            const uint32_t hmask = up >= 32 ? 0u : ~((1u << up) - 1u);
-            *(int4*)(hist + 4 * lane) = make_int4(0, 0, 0, 0);
-            wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
-                if (ok && (key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
-            });
-            // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
-            const int4 c = *(const int4*)(hist + 252 - 4 * lane);
-            const int s = c.x + c.y + c.z + c.w;
-            const int above = wave_inclusive_scan(s) - s;  // keys with a larger digit than this lane's
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(above < need && above + s >= need);
-            const int hl = (int)__builtin_ctzll(hit);
-            int acc = __builtin_amdgcn_readlane(above, hl);
-            const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
-            const int cy = __builtin_amdgcn_readlane(c.y, hl);
-            int digit;
-            if (acc + cw >= need) {
-                digit = 255 - 4 * hl;
-            } else if (acc + cw + cz >= need) {
-                digit = 254 - 4 * hl;
-                acc += cw;
-            } else if (acc + cw + cz + cy >= need) {
-                digit = 253 - 4 * hl;
-                acc += cw + cz;
-            } else {
-                digit = 252 - 4 * hl;
-                acc += cw + cz + cy;
-            }
-            prefix |= (uint32_t)digit << shift;
-            need -= acc;
-            top = shift - 1;
-        }
-        kth = prefix;
-    }
-
-    // keys above kth and equal to it: per lane, then placed by wave scans
-    int gt = 0, eq = 0;
-    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int, bool ok) {
-        gt += ok && key > kth;
-        eq += ok && key == kth;
-    });
-    const int gt_all = wave_inclusive_scan(gt);
-    const int need = k - __builtin_amdgcn_readlane(gt_all, 63);  // equal keys to take, lowest indices first
-    int eq_rank = wave_inclusive_scan(eq) - eq;                   // equal keys in lower lanes
-    const int take_eq = imax(0, imin(eq, need - eq_rank));
-    int pos = wave_inclusive_scan(gt + take_eq) - (gt + take_eq);
-    wave_topk_scan_keys(keys, n, kpl, lane, [&](uint32_t key, int i, bool ok) {
-        bool in = ok && key > kth;
-        if (ok && key == kth) {
-            in = eq_rank < need;
-            ++eq_rank;
-        }
-        if (in) emit(pos++, i);
-    });
-}
-
 }  // namespace sa

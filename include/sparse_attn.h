@@ -2,8 +2,8 @@
  * sparse_attn.h -- C ABI of block/page-sparse long-context decode attention
  * for AMD Instinct MI355X (gfx950).
  *
- * The method (hybrid sparse attention page: full-attention layers read a
- * 256-token prefix, a sliding window and the pages Quest rates most relevant;
+ * The method (hybrid sparse attention page: full-attention layers attend a
+ * 256-token prefix, a recent window and the pages that Quest scores highest;
  * semantic-blocks page: queries are compared with block centres and attend
  * the chosen blocks; course module 14, sections 14.2-14.3: attention sink +
  * window, block gating) runs as four calls on a caller-owned HIP stream:

@@ -9,14 +9,14 @@
  * What it computes, step by step, in the order the pages describe it:
  *
  *   1. page summaries  -- Quest-style per-channel min and max of the keys of a
- *      page (hybrid sparse attention page: "each full-attention layer reads the
- *      256-token prefix, a sliding window and the pages Quest rates most
- *      relevant"); MoBA-style block key taken as the mean of the block's keys
+ *      page (hybrid sparse attention page: full-attention layers attend a
+ *      256-token prefix, a recent window and the pages that Quest scores
+ *      highest); MoBA-style block key taken as the mean of the block's keys
  *      (course module 14, section 14.3; the page's gate key is a trained
  *      parameter, which we replace by the mean because no weights exist);
  *      semantic-block centroid = unit-norm mean of unit-norm keys (semantic
- *      blocks page, "a block joins similar keys": normalized keys clustered
- *      by spherical k-means, the query compared with block centres).
+ *      blocks page: keys are normalised and grouped by spherical k-means into
+ *      blocks, and a query is compared with the block centres).
  *   2. regions -- attention sink [0, S), sliding window of the last W
  *      positions [L-W, L), middle [S, L-W) (course module 14, section 14.2,
  *      StreamingLLM; self-indexing attention page, "Sliding window").
