@@ -1,7 +1,7 @@
 // Log-sum-exp merge of split partials (attention-mechanisms article,
 // DeepSeek-V4 section: partial results are combined; FlashAttention's
-// running-max rescaling).  One wave per output row; the split weights
-// e^{m_s - m*} l_s go through LDS, the sums run over s in a fixed order.
+// running-max rescaling).  One wave per output row; the sums run over the
+// splits in a fixed order, so the result does not depend on timing.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -16,39 +16,50 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
 {
     constexpr int CPL = HD / 64;  // channels per lane
     constexpr int UNROLL = 8;     // split loads in flight
-    __shared__ float wts[kMaxSplits];
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
-    const float* ml = a.part_ml + (long)row * a.splits * 2;
+    const int n = a.splits;
+    const float* ml = a.part_ml + (long)row * n * 2;
+    const float* po = a.part_o + (long)row * n * HD + lane * CPL;
 
-    float mx = -INFINITY;
-    for (int s = lane; s < a.splits; s += 64) {
-        const float2 v = *(const float2*)(ml + 2 * s);
-        if (v.y > 0.f) mx = fmaxf(mx, v.x);
-    }
-    mx = group_max<64>(mx);
-    for (int s = lane; s < a.splits; s += 64) {
-        const float2 v = *(const float2*)(ml + 2 * s);
-        wts[s] = v.y > 0.f ? expf(v.x - mx) * v.y : 0.f;
-    }
-    __syncthreads();
-
-    float tot = 0.f, acc[CPL];
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-    const float* po = a.part_o + (long)row * a.splits * HD + lane * CPL;
-    for (int s0 = 0; s0 < a.splits; s0 += UNROLL) {
-        float v[UNROLL][CPL];
+    // the partials of the first splits go out together with the (m, l) pairs
+    float v[UNROLL][CPL];
+    auto fetch = [&](int s0) {
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) v[j][c] = s0 + j < a.splits ? po[(long)(s0 + j) * HD + c] : 0.f;
+            for (int c = 0; c < CPL; ++c) v[j][c] = s0 + j < n ? po[(long)(s0 + j) * HD + c] : 0.f;
+    };
+    fetch(0);
+    float mx = -INFINITY;
+    for (int s = lane; s < n; s += 64) {
+        const float2 p = *(const float2*)(ml + 2 * s);
+        if (p.y > 0.f) mx = fmaxf(mx, p.x);
+    }
+    mx = group_max<64>(mx);
+
+    // split s's weight e^{m_s - m*} l_s sits in lane s % 64 of its block of 64
+    // splits and is read out uniformly, so the sums run over s in one order
+    float tot = 0.f, acc[CPL], w = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < n; s0 += UNROLL) {
+        if ((s0 & 63) == 0) {
+            const int s = s0 + lane;
+            w = 0.f;
+            if (s < n) {
+                const float2 p = *(const float2*)(ml + 2 * s);
+                w = p.y > 0.f ? expf(p.x - mx) * p.y : 0.f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const float w = s0 + j < a.splits ? wts[s0 + j] : 0.f;
-            tot += w;  // the same order in every lane
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (s0 & 63) + j));
+            tot += wj;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, v[j][c], acc[c]);
+            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wj, v[j][c], acc[c]);
         }
+        if (s0 + UNROLL < n) fetch(s0 + UNROLL);
     }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
     if constexpr (OUT_BF && CPL == 1) {

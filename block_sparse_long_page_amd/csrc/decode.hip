@@ -311,7 +311,7 @@ struct MfmaCore {
         : sm(s)
     {
         lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
+        wave = wave_index();
         r = lane & 15;
         j = lane >> 4;
         vchunk = lane % LPT;
@@ -343,27 +343,32 @@ struct MfmaCore {
     // compiler can count the loads in flight and wait for one round only:
     // tokens that are not attended read row 0 instead, their logits are
     // masked to -inf and their value rows written as zeros.
-    __device__ __forceinline__ void load(int rd, Buf& B) const
+    __device__ __forceinline__ void load(int rd, Buf& B) const { load(rd, B, nrows); }
+
+    // the same with entries at or past `limit` taken as not attended
+    __device__ __forceinline__ void load(int rd, Buf& B, int limit) const
+    {
+#pragma unroll
+        for (int tt = 0; tt < TPS; ++tt) load_at(rd * RT + (wave * TPS + tt) * 16, B, tt, limit);
+    }
+
+    // the tile of table entries t0 .. t0+15 (t0 a multiple of 16) into slot tt
+    __device__ __forceinline__ void load_at(int t0, Buf& B, int tt, int limit) const
     {
         const int* rows = sm.rows;
+        const int4 rv = t0 + 4 * j + 3 < limit ? *(const int4*)(rows + t0 + 4 * j)
+                                               : make_int4(t0 + 4 * j < limit ? rows[t0 + 4 * j] : -1,
+                                                           t0 + 4 * j + 1 < limit ? rows[t0 + 4 * j + 1] : -1,
+                                                           t0 + 4 * j + 2 < limit ? rows[t0 + 4 * j + 2] : -1, -1);
+        B.rv[tt] = rv;
+        const int rk = t0 + r < limit ? imax(rows[t0 + r], 0) : 0;
 #pragma unroll
-        for (int tt = 0; tt < TPS; ++tt) {
-            const int t0 = rd * RT + (wave * TPS + tt) * 16;  // tile start in the table
-            const int4 rv = t0 + 4 * j + 3 < nrows
-                                ? *(const int4*)(rows + t0 + 4 * j)
-                                : make_int4(t0 + 4 * j < nrows ? rows[t0 + 4 * j] : -1,
-                                            t0 + 4 * j + 1 < nrows ? rows[t0 + 4 * j + 1] : -1,
-                                            t0 + 4 * j + 2 < nrows ? rows[t0 + 4 * j + 2] : -1, -1);
-            B.rv[tt] = rv;
-            const int rk = t0 + r < nrows ? imax(rows[t0 + r], 0) : 0;
+        for (int kk = 0; kk < KK; ++kk) B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
+        const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
-            const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-            for (int v = 0; v < VLD; ++v) {
-                const int rr = imax(rows4[HD == 128 ? v : 2 * v + (r >> 3)], 0);
-                B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
-            }
+        for (int v = 0; v < VLD; ++v) {
+            const int rr = imax(rows4[HD == 128 ? v : 2 * v + (r >> 3)], 0);
+            B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
         }
     }
 
@@ -453,15 +458,6 @@ struct MfmaCore {
             for (int tt = 0; tt < TPS; ++tt)
                 if (busy(rd + 2, tt)) compute(C, tt);
             if (rd + 5 < nr) load(rd + 5, C);
-        }
-    }
-
-    __device__ __forceinline__ static void clear(Buf& A)
-    {
-#pragma unroll
-        for (int tt = 0; tt < TPS; ++tt) {
-            for (int kk = 0; kk < KK; ++kk) A.k[tt][kk] = make_uint4(0, 0, 0, 0);
-            for (int v = 0; v < VLD; ++v) A.v[tt][v] = make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -590,9 +586,6 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
     const int32_t* bt = g.block_table + (long)b * g.max_pages;
 
     typename Core::Buf A, B, C;
-    Core::clear(A);
-    Core::clear(B);
-    Core::clear(C);
     for (int cb = f0; cb < f1; cb += kRowsWG) {
         const int cnt = imin(f1 - cb, kRowsWG);
         __syncthreads();  // the previous chunk's rows are no longer read
@@ -606,22 +599,34 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
     core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
 }
 
-// Selection and decode in one kernel, for the steps that select: every
-// workgroup of a (sequence, KV head, row) takes its share of the sink and
-// window tokens and issues their first rounds, runs the block top-k of the
-// problem's page scores while those loads are in flight, then takes its share
-// of the selected pages' middle tokens.  The workgroup of split 0 also writes
+// Selection and decode in one kernel, for the steps that select.  Every
+// workgroup of a (sequence, KV head, row) stages the problem's block-table
+// row and page scores in LDS, and all its threads take the ranking up to
+// the bitmap of pages above the boundary score digit and the few keys at it;
+// then its waves part.  The last wave ranks those keys, emits the ascending
+// page list and publishes it through an LDS flag while the other waves
+// already stream the workgroup's share of the sink and window tokens (the
+// last wave joins them after).  Each wave then resolves the rows of
+// its own tiles of the selected pages' middle tokens and streams them, so no
+// workgroup barrier stands between the two shares and the K/V loads keep
+// going while the pages are ranked.  The workgroup of split 0 also writes
 // the page list and its count.
+
+constexpr int kSelSpinMax = 1 << 24;  // bound on the wait for the page list
+
 template <int HD, int G>
 __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mfma(SelectDecodeArgs a)
 {
     using Core = MfmaCore<HD, G>;
-    constexpr int NW = Core::NW, RT = Core::RT;
+    constexpr int NW = Core::NW;
+    constexpr int SW = NW - 1;  // the wave that ranks the pages
+    static_assert(Core::TPS == 1, "one tile per wave step");
     const Geometry& g = a.g;
     __shared__ __attribute__((aligned(16))) uint32_t keys[kFusedMaxCand];
     __shared__ int bt_lds[kFusedMaxCand];
     __shared__ TopkScratch tk;
     __shared__ int sel_lds[kSelCap];
+    __shared__ int sel_ready;
     __shared__ MfmaLds<HD, G> lds;
 
     int bid = blockIdx.x;
@@ -633,6 +638,18 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     const int b = bid / a.Q;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
 
+    // The first loads do not depend on the sequence length, so they go out
+    // with it at entry: the first 2048 entries of the block-table row and of
+    // the score row, one 16-byte load each per thread (the host passes
+    // 16-byte aligned rows).  Quads past a row's end re-read its last quad
+    // and are masked when staged.
+    const int32_t* bt_g = g.block_table + (long)b * g.max_pages;
+    const float* srow = a.scores + prob * g.max_pages;  // scores of logical pages, candidates from plo
+    const int e0 = 4 * (int)threadIdx.x;
+    const int ec = imin(e0, g.max_pages - 4);
+    const int4 bv = *(const int4*)(bt_g + ec);
+    const uint4 sv = *(const uint4*)(srow + ec);
+
     const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
     const int pos = L - a.Q + row;
     const int se = imin(a.S, L), ws = imax(se, L - a.W);
@@ -642,77 +659,138 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     Core core(lds, g, a.scale_log2);
     core.load_queries(a.q, (((long)b * g.Hq + kvh * G) * a.Q + row) * HD, (long)a.Q * HD);
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
+    const int lane = threadIdx.x & 63, wave = wave_index();
 
-    // one round of loads: the block-table row of the sequence's pages into LDS
-    // and the candidates' scores as order keys, every load of a thread in flight
-    const int npg = imin(g.max_pages, (L + g.P - 1) / g.P);
-    const int32_t* bt_g = g.block_table + (long)b * g.max_pages;
-    const float* sc = a.scores + prob * g.max_pages + plo;
-    const bool rank = k > 0 && k < ncand;
-    uint32_t lo = 0xffffffffu, hi = 0;
-    for (int base = 0; base < imax(npg, ncand); base += 4 * 64 * NW) {
-        int bv[4];
-        float sv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + u * 64 * NW + (int)threadIdx.x;
-            bv[u] = i < npg ? bt_g[i] : -1;
-            sv[u] = rank && i < ncand ? sc[i] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + u * 64 * NW + (int)threadIdx.x;
-            if (i < npg) bt_lds[i] = bv[u];
-            if (rank && i < ncand) {
-                const uint32_t key = order_key(sv[u]);
-                keys[i] = key;
-                lo = min(lo, key);
-                hi = max(hi, key);
-            }
-        }
-    }
-    // this workgroup's share of the sink and window tokens, first in its table,
-    // resolved in the same round from the block table in global memory
+    // this workgroup's share of the sink and window tokens, first in its
+    // table; the middle share starts at the next multiple of 16
     const int nloc = se + (L - ws);
     const int l0 = split * (nloc / a.splits) + imin(split, nloc % a.splits);
     const int nl = nloc / a.splits + (split < nloc % a.splits ? 1 : 0);
-    resolve_rows<NW>(lds.rows, 0, nl, [&](int i) { const int f = l0 + i; return f < se ? f : ws + (f - se); }, pos,
-                     bt_g, g, kvh, pdiv);
+    const int nlp = (nl + 15) & ~15;
+    auto local_tok = [&](int i) { const int f = l0 + i; return f < se ? f : ws + (f - se); };
+
+    // the block-table row into LDS and the candidates' scores as order keys
+    const int npg = imin(g.max_pages, (L + g.P - 1) / g.P);
+    const bool rank = k > 0 && k < ncand;
+    const int nsc = rank ? plo + ncand : 0;  // score row entries needed
+    uint32_t lo = 0xffffffffu, hi = 0;
+    auto stage = [&](int e, int btv, float scv) {  // entry e of both rows
+        if (e < npg) bt_lds[e] = btv;
+        const int i = e - plo;  // candidate index
+        if (rank && i >= 0 && i < ncand) {
+            const uint32_t key = order_key(scv);
+            keys[i] = key;
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+    };
+    stage(e0, bv.x, __uint_as_float(sv.x));
+    stage(e0 + 1, bv.y, __uint_as_float(sv.y));
+    stage(e0 + 2, bv.z, __uint_as_float(sv.z));
+    stage(e0 + 3, bv.w, __uint_as_float(sv.w));
+    const int span = imax(npg, nsc);
+    for (int e = 4 * 64 * NW + (int)threadIdx.x; e < span; e += 64 * NW)  // longer sequences
+        stage(e, e < npg ? bt_g[e] : -1, e < nsc ? srow[e] : 0.f);
+    topk_begin(tk, lo, hi);
+    if (threadIdx.x == 0) sel_ready = 0;
     __syncthreads();
     const int32_t* bt = bt_lds;
+
+    // the local rows (padding entries are not attended) and the histogram
+    resolve_rows<NW>(lds.rows, 0, nlp, [&](int i) { return i < nl ? local_tok(i) : -1; }, pos, bt, g, kvh, pdiv);
+    TopkPlan tp = {0u, 0u, 0, 0u, -1, 0, 0};
+    if (rank) tp = topk_digits(tk, ncand, keys);
+    __syncthreads();
+
+    auto emit = [&](int p, int i) { sel_lds[p] = plo + i; };
+    const bool sorted = !rank || tp.lo == tp.hi;  // the list is the lowest k candidates
+    if (!sorted) topk_boundary(tk, k, tp);
+    const bool multipass = !sorted && tp.nd > kTopkBoundMax;  // uniform: one histogram
+    if (multipass) {
+        __syncthreads();  // the multi-pass select clears the histogram first
+        block_topk_keys(ncand, k, keys, tp.lo, tp.hi, tk, emit);
+        __syncthreads();
+    } else if (!sorted) {
+        topk_collect_block(ncand, keys, tp, tk);
+        __syncthreads();
+    }
+    if (wave == SW) {
+        if (sorted) {
+            for (int i = lane; i < k; i += 64) emit(i, i);
+        } else if (!multipass) {
+            topk_emit_wave(ncand, k, tp, tk, emit);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (split == 0) {
+            int32_t* sel_g = a.sel + prob * a.k_max;
+            for (int i = lane; i < a.k_max; i += 64) sel_g[i] = i < k ? sel_lds[i] : -1;
+            if (lane == 0) a.count[prob] = k;
+        }
+        __hip_atomic_store(&sel_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+
+    // Tiles of this wave: local tiles wave, wave + NW, ..., then middle tiles
+    // wave, wave + NW, ...  The middle ones become known when the page list
+    // is published.
+    constexpr int kMidTilesW = kRowsWG / 16 / NW;  // most middle tiles of a wave
+    const int nloc_w = imax(0, (nlp / 16 - wave + NW - 1) / NW);
+    int nt = nloc_w, nm = 0, next = 0;  // tiles known, middle entries, next tile to load
+    bool have_mid = false;
+    // Takes the page list once the ranking wave has published it (never
+    // waits): this wave's middle tiles and their rows, four tiles per step.
+    auto poll = [&]() {
+        if (have_mid || __hip_atomic_load(&sel_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) return;
+        TokenSetLds tsm;
+        tsm.init(L, a.S, a.W, g.P, (lds_i32_ptr)sel_lds, k, a.k_max, kPartMiddle);
+        const int nmid = tsm.total;
+        const int m0 = split * (nmid / a.splits) + imin(split, nmid % a.splits);
+        nm = nmid / a.splits + (split < nmid % a.splits ? 1 : 0);
+        const int nmid_w = imax(0, ((nm + 15) / 16 - wave + NW - 1) / NW);
+#pragma unroll
+        for (int q = 0; q < kMidTilesW; q += 4) {
+            const int tq = q + (lane >> 4);
+            const int e = 16 * (wave + NW * tq) + (lane & 15);  // entry of the middle share
+            if (tq < nmid_w && e < nm) {
+                const int t = tsm.position(m0 + e, pdiv);
+                lds.rows[nlp + e] = token_row(t, pos, t >= 0 && t <= pos ? bt[pdiv.div(t)] : -1, g, kvh, pdiv);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        nt = nloc_w + nmid_w;
+        have_mid = true;
+    };
+    // Loads the next tile into X and returns true, or, when none is known
+    // yet or left, loads row 0 masked and returns false: every step issues
+    // the same loads, so the waits count one tile each.
+    auto issue = [&](typename Core::Buf& X) {
+        const bool real = next < nt;
+        const bool loc = next < nloc_w;
+        const int t0 = 16 * (wave + NW * (loc ? next : next - nloc_w)) + (loc ? 0 : nlp);
+        core.load_at(real ? t0 : 0, X, 0, real ? (loc ? nlp : nlp + nm) : 0);
+        next += real ? 1 : 0;
+        return real;
+    };
+    // Three tiles in flight per wave.  Real tiles are computed in tile order
+    // whatever the timing of the page list, so results do not depend on it.
     typename Core::Buf A, B, C;
-    Core::clear(A);
-    Core::clear(B);
-    Core::clear(C);
-    core.nrows = nl;
-    const int pre = imin(3, nl / RT);  // rounds made of sink and window tokens only, loaded now
-    if (pre > 0) core.load(0, A);
-    if (pre > 1) core.load(1, B);
-    if (pre > 2) core.load(2, C);
-
-    // the page list, while those loads are in flight
-    if (rank) {
-        block_topk_fast(ncand, k, keys, lo, hi, tk, [&](int p, int i) { sel_lds[p] = plo + i; });
-    } else {
-        for (int i = threadIdx.x; i < k; i += 64 * NW) sel_lds[i] = plo + i;
+    poll();
+    bool ra = issue(A), rb = issue(B), rc = issue(C);
+    // The only exit is at the end of a round of three, where the loads in
+    // flight are in the same order as on the way round, so the waits inside
+    // the loop stay at one tile each.
+    for (int step = 0; step < kSelSpinMax; ++step) {
+        if (!have_mid && next >= nloc_w) poll();
+        if (ra) core.compute(A, 0);
+        ra = issue(A);
+        if (rb) core.compute(B, 0);
+        rb = issue(B);
+        if (rc) core.compute(C, 0);
+        rc = issue(C);
+        if (!ra && !rb && !rc) {
+            if (have_mid && next >= nt) break;
+            __builtin_amdgcn_s_sleep(2);  // waiting for the page list
+        }
     }
-    __syncthreads();
-    if (split == 0) {
-        int32_t* sel_g = a.sel + prob * a.k_max;
-        for (int i = threadIdx.x; i < a.k_max; i += 64 * NW) sel_g[i] = i < k ? sel_lds[i] : -1;
-        if (threadIdx.x == 0) a.count[prob] = k;
-    }
-
-    // this workgroup's share of the selected pages' middle tokens
-    TokenSetLds tsm;
-    tsm.init(L, a.S, a.W, g.P, (lds_i32_ptr)sel_lds, k, a.k_max, kPartMiddle);
-    const int nmid = tsm.total;
-    const int m0 = split * (nmid / a.splits) + imin(split, nmid % a.splits);
-    const int nm = nmid / a.splits + (split < nmid % a.splits ? 1 : 0);
-    resolve_rows<NW>(lds.rows, nl, nm, [&](int i) { return tsm.position(m0 + i, pdiv); }, pos, bt, g, kvh, pdiv);
-    __syncthreads();
-    core.nrows = nl + nm;
-    core.run(A, B, C, pre);
     core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
 }
 

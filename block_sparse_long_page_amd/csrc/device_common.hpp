@@ -169,6 +169,10 @@ __device__ __forceinline__ int dpp_shr0(int x)
     return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
 }
 
+// the wave's index in its workgroup, in a scalar register (the compiler does
+// not infer that threadIdx.x / 64 is the same across a wave)
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
 {
     x = min(x, (uint32_t)dpp_i<0xB1>((int)x));

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cstdint>
 
 #include "../../include/sparse_attn.h"
 #include "kernels.hpp"
@@ -81,13 +82,14 @@ int occupancy(int hd, int G, int dtype)
 }
 
 // fewest splits that leave every workgroup of the select-and-decode kernel
-// at most kRowsWG tokens (a share of the sink + window plus a share of the
-// selected pages, each rounded up)
+// at most kRowsWG row-table entries: a share of the sink + window rounded up
+// to a multiple of 16 (up to 16 more than toks / s) plus a share of the
+// selected pages (up to 1 more)
 long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32_t page_size)
 {
     const long toks = (long)(sink_len > 0 ? sink_len : 0) + (window_len > 0 ? window_len : 0) +
                       (long)(k_max > 0 ? k_max : 0) * page_size;
-    return (toks + sa::kRowsWG - 3) / (sa::kRowsWG - 2);
+    return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
 }
 
 size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
@@ -232,8 +234,11 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
         if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
     }
+    // the fused kernel reads the block-table and score rows as 16-byte vectors
+    const bool aligned = kv->max_pages_per_seq % 4 == 0 && ((uintptr_t)kv->block_table & 15) == 0 &&
+                         ((uintptr_t)workspace & 15) == 0;
     const bool fused = kv->dtype == SA_BF16 && k_max >= 1 && k_max <= sa::kSelCap &&
-                       kv->max_pages_per_seq <= sa::kFusedMaxCand &&
+                       kv->max_pages_per_seq <= sa::kFusedMaxCand && aligned &&
                        num_splits >= fused_min_splits(sink_len, window_len, k_max, kv->page_size);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
     if (!fused) {

@@ -10,7 +10,8 @@ namespace sa {
 // order-preserving float -> uint32 (larger float, larger key); -0 maps to +0
 __device__ __forceinline__ uint32_t order_key(float f)
 {
-    const uint32_t u = __float_as_uint(f + 0.0f);
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -53,7 +54,7 @@ __device__ __forceinline__ int pick_count(const int (&ex)[kCntChunks], int e)
 
 constexpr int kTopkPasses = 4;  // 32 key bits, 8 per pass
 
-constexpr int kTopkBoundMax = 64;  // keys of the boundary digit ranked directly by one wave
+constexpr int kTopkBoundMax = 64;  // keys of the boundary digit ranked directly by one wave, one per lane
 
 struct TopkScratch {
     int hist[kTopkPasses][256];
@@ -233,14 +234,29 @@ __device__ __forceinline__ void block_topk_keys(int n, int k, const uint32_t* ke
 // the best k - (count above).  One wave then emits the bitmap in ascending
 // index order.  More than 64 keys at the boundary (many equal or nearly
 // equal scores) falls back to the multi-pass select above, same result.
+//
+// The steps are separate functions so that a caller can run the last ones on
+// a single wave while its other waves go on with other work:
+//   topk_begin       every thread, before the barrier that publishes the keys
+//   topk_digits      every thread after it (histogram), then a barrier
+//   topk_boundary    any wave: the boundary digit, its count, the count above
+//   topk_collect_block  every thread: the bitmap of larger digits and the
+//                       boundary keys, then a barrier
+//   topk_emit_wave   one wave: ranks the boundary keys, emits ascending
 // ---------------------------------------------------------------------------
-template <typename Emit>
-__device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* keys, uint32_t lo, uint32_t hi,
-                                                TopkScratch& sh, Emit emit)
+
+struct TopkPlan {
+    uint32_t lo, hi;  // smallest and largest key
+    int shift;        // the digit is (key >> shift) & dmask
+    uint32_t dmask;
+    int d, nd, above;  // boundary digit, its key count, keys with a larger digit
+};
+
+// Every thread, with its min and max key: clears the histogram and publishes
+// the wave's key range.
+__device__ __forceinline__ void topk_begin(TopkScratch& sh, uint32_t lo, uint32_t hi)
 {
-    constexpr int NW = kTopkThreads / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;
     for (int i = tid; i < 256; i += kTopkThreads) sh.hist[0][i] = 0;
     if (tid == 0) sh.nb = 0;
     lo = wave_min_u32(lo);
@@ -249,23 +265,42 @@ __device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* ke
         sh.mm[wave][0] = lo;
         sh.mm[wave][1] = hi;
     }
-    __syncthreads();
+}
+
+// Every thread, after the barrier that follows topk_begin: the key range and
+// the digit below the bits every key shares; unless every key is equal, the
+// thread's keys go into the digit histogram (a barrier must follow).
+__device__ __forceinline__ TopkPlan topk_digits(TopkScratch& sh, int n, const uint32_t* keys)
+{
+    constexpr int NW = kTopkThreads / 64;
+    TopkPlan t;
+    t.lo = 0xffffffffu;
+    t.hi = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        lo = min(lo, sh.mm[w][0]);
-        hi = max(hi, sh.mm[w][1]);
+        t.lo = min(t.lo, sh.mm[w][0]);
+        t.hi = max(t.hi, sh.mm[w][1]);
     }
-    if (lo == hi) {  // every key equal: the lowest k indices
-        for (int i = tid; i < k; i += kTopkThreads) emit(i, i);
-        return;
-    }
-    const int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+    t.shift = 0;
+    t.dmask = 0;
+    t.d = -1;
+    t.nd = 0;
+    t.above = 0;
+    if (t.lo == t.hi) return t;
+    const int top = 31 - __builtin_clz(t.lo ^ t.hi);  // highest bit that differs
     const int width = top + 1 < 8 ? top + 1 : 8;
-    const int shift = top + 1 - width;
-    const uint32_t dmask = (1u << width) - 1u;
+    t.shift = top + 1 - width;
+    t.dmask = (1u << width) - 1u;
 #pragma unroll 4
-    for (int i = tid; i < n; i += kTopkThreads) atomicAdd(&sh.hist[0][(keys[i] >> shift) & dmask], 1);
-    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kTopkThreads) atomicAdd(&sh.hist[0][(keys[i] >> t.shift) & t.dmask], 1);
+    return t;
+}
+
+// Any wave, after the histogram's barrier (and only when lo != hi): the
+// digit where the count of keys from the top reaches k.
+__device__ __forceinline__ void topk_boundary(const TopkScratch& sh, int k, TopkPlan& t)
+{
+    const int lane = threadIdx.x & 63;
     // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
     const int4 c = *(const int4*)&sh.hist[0][252 - 4 * lane];
     const int s4 = c.x + c.y + c.z + c.w;
@@ -275,73 +310,108 @@ __device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* ke
     int above = __builtin_amdgcn_readlane(above4, hl);
     const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
     const int cy = __builtin_amdgcn_readlane(c.y, hl), cx = __builtin_amdgcn_readlane(c.x, hl);
-    int d, nd;
     if (above + cw >= k) {
-        d = 255 - 4 * hl;
-        nd = cw;
+        t.d = 255 - 4 * hl;
+        t.nd = cw;
     } else if (above + cw + cz >= k) {
-        d = 254 - 4 * hl;
-        nd = cz;
+        t.d = 254 - 4 * hl;
+        t.nd = cz;
         above += cw;
     } else if (above + cw + cz + cy >= k) {
-        d = 253 - 4 * hl;
-        nd = cy;
+        t.d = 253 - 4 * hl;
+        t.nd = cy;
         above += cw + cz;
     } else {
-        d = 252 - 4 * hl;
-        nd = cx;
+        t.d = 252 - 4 * hl;
+        t.nd = cx;
         above += cw + cz + cy;
     }
-    if (nd > kTopkBoundMax) {  // uniform: every wave read the same histogram
-        __syncthreads();       // the multi-pass select clears the histogram first
-        block_topk_keys(n, k, keys, lo, hi, sh, emit);
-        return;
-    }
-    const int need = k - above;  // boundary keys to take, 1 .. nd
-    // larger digits into the bitmap; boundary keys into the small list
+    t.above = above;
+}
+
+// Every thread (a barrier must follow): keys with a larger digit into the
+// bitmap (word w holds indices 64w .. 64w+63), keys with digit d into the
+// boundary list (t.nd <= kTopkBoundMax).
+__device__ __forceinline__ void topk_collect_block(int n, const uint32_t* keys, const TopkPlan& t, TopkScratch& sh)
+{
+    constexpr int NW = kTopkThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rounds = (n + kTopkThreads - 1) / kTopkThreads;
     for (int r = 0; r < rounds; ++r) {
         const int i = r * kTopkThreads + tid;
         const uint32_t key = i < n ? keys[i] : 0u;
-        const int dig = (int)((key >> shift) & dmask);
-        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && dig > d);
+        const int dig = (int)((key >> t.shift) & t.dmask);
+        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && dig > t.d);
         if (lane == 0) sh.chosen[r * NW + wave] = up;
-        if (i < n && dig == d) {
+        if (i < n && dig == t.d) {
             const int slot = atomicAdd(&sh.nb, 1);
             sh.b_key[slot] = key;
             sh.b_idx[slot] = i;
         }
     }
-    __syncthreads();
-    if (wave == 0) {
-        // rank of each boundary key among them: larger key first, then lower index
-        const bool mine = lane < nd;
-        const uint32_t bk = mine ? sh.b_key[lane] : 0u;
-        const int bi = mine ? sh.b_idx[lane] : 0;
-        int rank = 0;
-        for (int t = 0; t < nd; ++t) {
-            const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bk, t);
-            const int it = __builtin_amdgcn_readlane(bi, t);
-            rank += kt > bk || (kt == bk && it < bi);
-        }
-        if (mine && rank < need) atomicOr((unsigned long long*)&sh.chosen[bi >> 6], 1ull << (bi & 63));
-        __builtin_amdgcn_wave_barrier();
-        // emit in ascending index order: word w holds indices 64w .. 64w+63
-        const int nwords = (n + 63) / 64;
-        int base = 0;
-        for (int w0 = 0; w0 < nwords; w0 += 64) {
-            const int w = w0 + lane;
-            uint64_t bits = w < nwords ? sh.chosen[w] : 0ull;
-            const int cnt = __builtin_popcountll(bits);
-            const int inc = wave_inclusive_scan(cnt);
-            int pos = base + inc - cnt;
-            while (bits) {
-                const int b = __builtin_ctzll(bits);
-                emit(pos++, 64 * w + b);
-                bits &= bits - 1;
-            }
-            base += __builtin_amdgcn_readlane(inc, 63);
-        }
+}
+
+// One wave, once the bitmap and the boundary list are complete: ranks the
+// boundary keys (larger key first, then lower index) by lane reads from
+// registers, sets the best k - above of them and emits every chosen index
+// in ascending order.
+template <typename Emit>
+__device__ __forceinline__ void topk_emit_wave(int n, int k, const TopkPlan& t, TopkScratch& sh, Emit emit)
+{
+    const int lane = threadIdx.x & 63;
+    const int nd = t.nd, need = k - t.above;  // boundary keys to take, 1 .. nd
+    const bool mine = lane < nd;
+    const uint32_t bk = mine ? sh.b_key[lane] : 0u;
+    const int bi = mine ? sh.b_idx[lane] : 0;
+    int rank = 0;
+    for (int u = 0; u < nd; ++u) {
+        const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)bk, u);
+        const int iu = __builtin_amdgcn_readlane(bi, u);
+        rank += ku > bk || (ku == bk && iu < bi);
     }
+    if (mine && rank < need) atomicOr((unsigned long long*)&sh.chosen[bi >> 6], 1ull << (bi & 63));
+    __builtin_amdgcn_wave_barrier();
+    const int nwords = (n + 63) / 64;
+    int base = 0;
+    for (int w0 = 0; w0 < nwords; w0 += 64) {
+        const int w = w0 + lane;
+        uint64_t bits = w < nwords ? sh.chosen[w] : 0ull;
+        const int cnt = __builtin_popcountll(bits);
+        const int inc = wave_inclusive_scan(cnt);
+        int pos = base + inc - cnt;
+        while (bits) {
+            const int b = __builtin_ctzll(bits);
+            emit(pos++, 64 * w + b);
+            bits &= bits - 1;
+        }
+        base += __builtin_amdgcn_readlane(inc, 63);
+    }
+}
+
+// The whole selection by the block (all 512 threads), keys already in LDS
+// and each thread's min and max key given.
+template <typename Emit>
+__device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* keys, uint32_t lo, uint32_t hi,
+                                                TopkScratch& sh, Emit emit)
+{
+    const int tid = threadIdx.x;
+    topk_begin(sh, lo, hi);
+    __syncthreads();
+    TopkPlan t = topk_digits(sh, n, keys);
+    if (t.lo == t.hi) {  // every key equal: the lowest k indices
+        for (int i = tid; i < k; i += kTopkThreads) emit(i, i);
+        return;
+    }
+    __syncthreads();
+    topk_boundary(sh, k, t);
+    if (t.nd > kTopkBoundMax) {  // uniform: every wave read the same histogram
+        __syncthreads();         // the multi-pass select clears the histogram first
+        block_topk_keys(n, k, keys, t.lo, t.hi, sh, emit);
+        return;
+    }
+    topk_collect_block(n, keys, t, sh);
+    __syncthreads();
+    if ((tid >> 6) == 0) topk_emit_wave(n, k, t, sh, emit);
 }
 
 }  // namespace sa

@@ -213,10 +213,11 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
 /*
  * One selecting step in two launches: the page scores of sparse_attn_select,
  * then one kernel that ranks the pages and decodes.  Each of its workgroups
- * takes its share of the sink and window tokens, issues their first loads,
- * runs the top-k of its row's scores while they are in flight (the selection
- * depends only on the scores, so every workgroup of a row computes the same
- * page list), then takes its share of the selected pages' middle tokens.
+ * stages its row's block-table row and scores, then one of its waves ranks
+ * the pages (the selection depends only on the scores, so every workgroup of
+ * a row computes the same page list) while the others stream the
+ * workgroup's share of the sink and window tokens; then all its waves take
+ * their share of the selected pages' middle tokens.
  * Same arithmetic as sparse_attn_select followed by sparse_attn_decode with
  * parts = SA_PART_ALL; the tokens of a row are split over the workgroups
  * differently, so the partials differ from sparse_attn_decode's by rounding
@@ -224,10 +225,12 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
  *   Arguments as in sparse_attn_select and sparse_attn_decode (split_stride
  *   = num_splits).  Writes sel_pages / sel_count as sparse_attn_select does,
  *   and part_o / part_ml for sparse_attn_combine.
- * bf16 caches with 1 <= k_max <= 1024, at most 8192 pages per sequence, and
- * num_splits >= (S + W + k_max * page_size) / 2046 (at most 2048 tokens per
- * workgroup) take the fused kernel; any other valid call runs
- * sparse_attn_select and then sparse_attn_decode, with the same results.
+ * The fused kernel runs for bf16 caches with 1 <= k_max <= 1024, at most 8192
+ * pages per sequence, max_pages_per_seq a multiple of 4, block_table and
+ * workspace 16-byte aligned, and num_splits >= (S + W + k_max * page_size) /
+ * 2031 (at most 2048 row-table entries per workgroup, 15 of them padding);
+ * any other valid call runs sparse_attn_select and then sparse_attn_decode,
+ * with the same results.
  * Errors: those of sparse_attn_select and sparse_attn_decode.
  */
 int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,

@@ -130,14 +130,16 @@ def test_select_decode_step(name, mode, splits):
     assert torch.equal(dec.out, out1) and torch.equal(dec.lse, lse1)
 
 
-@pytest.mark.parametrize("pattern", ["all-equal", "two-values", "small-tie-band"])
+@pytest.mark.parametrize("pattern", ["all-equal", "two-values", "two-values-wide", "small-tie-band"])
 @pytest.mark.parametrize("fused", [False, True])
 def test_tied_scores_take_the_lower_pages(pattern, fused):
     """Exact ties in the page scores (pages whose tokens all hold one key
-    vector) go to the lower logical page, as in the oracle: every key equal,
-    a boundary of ~n/2 equal keys (the multi-pass select) and a boundary of a
-    few dozen equal keys (ranked directly)."""
-    pr = synth.random_problem(B=2, Hq=16, Hkv=2, hd=128, P=8, seq_lens=[2048, 1500], sink=32, window=64,
+    vector) go to the lower logical page, as in the oracle: every key equal;
+    a boundary of ~n/2 equal keys (the multi-pass select), about 120 and,
+    over 2000 pages, about 1000; and a boundary of a few dozen equal keys
+    (ranked directly)."""
+    lens = [16384, 3000] if pattern == "two-values-wide" else [2048, 1500]
+    pr = synth.random_problem(B=2, Hq=16, Hkv=2, hd=128, P=8, seq_lens=lens, sink=32, window=64,
                               budget=30 * 8, mode="quest", seed=11, shuffle=True)
     c = pr.cache
     rng = np.random.default_rng(3)
@@ -147,7 +149,7 @@ def test_tied_scores_take_the_lower_pages(pattern, fused):
         for p in range(n_pages):
             if pattern == "all-equal":
                 w = 0
-            elif pattern == "two-values":
+            elif pattern in ("two-values", "two-values-wide"):
                 w = p % 2
             else:  # 10 pages of one value, 40 of a second, the rest a third
                 w = 0 if p % 50 < 10 else 1 if p % 50 < 50 and p < 50 else 2
