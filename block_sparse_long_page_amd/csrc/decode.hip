@@ -696,39 +696,6 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     __syncthreads();
     const int32_t* bt = bt_lds;
 
-    // the local rows (padding entries are not attended) and the histogram
-    resolve_rows<NW>(lds.rows, 0, nlp, [&](int i) { return i < nl ? local_tok(i) : -1; }, pos, bt, g, kvh, pdiv);
-    TopkPlan tp = {0u, 0u, 0, 0u, -1, 0, 0};
-    if (rank) tp = topk_digits(tk, ncand, keys);
-    __syncthreads();
-
-    auto emit = [&](int p, int i) { sel_lds[p] = plo + i; };
-    const bool sorted = !rank || tp.lo == tp.hi;  // the list is the lowest k candidates
-    if (!sorted) topk_boundary(tk, k, tp);
-    const bool multipass = !sorted && tp.nd > kTopkBoundMax;  // uniform: one histogram
-    if (multipass) {
-        __syncthreads();  // the multi-pass select clears the histogram first
-        block_topk_keys(ncand, k, keys, tp.lo, tp.hi, tk, emit);
-        __syncthreads();
-    } else if (!sorted) {
-        topk_collect_block(ncand, keys, tp, tk);
-        __syncthreads();
-    }
-    if (wave == SW) {
-        if (sorted) {
-            for (int i = lane; i < k; i += 64) emit(i, i);
-        } else if (!multipass) {
-            topk_emit_wave(ncand, k, tp, tk, emit);
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (split == 0) {
-            int32_t* sel_g = a.sel + prob * a.k_max;
-            for (int i = lane; i < a.k_max; i += 64) sel_g[i] = i < k ? sel_lds[i] : -1;
-            if (lane == 0) a.count[prob] = k;
-        }
-        __hip_atomic_store(&sel_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-
     // Tiles of this wave: local tiles wave, wave + NW, ..., then middle tiles
     // wave, wave + NW, ...  The middle ones become known when the page list
     // is published.
@@ -770,11 +737,61 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
         next += real ? 1 : 0;
         return real;
     };
+    typename Core::Buf A, B, C;
+    // The local rows (padding entries are not attended): each wave first
+    // resolves its own first tile and issues its loads, which then overlap
+    // the ranking; all threads resolve the rest.
+    if (lane < 16 && 16 * wave + lane < nlp) {
+        const int e = 16 * wave + lane;
+        const int t = e < nl ? local_tok(e) : -1;
+        lds.rows[e] = token_row(t, pos, t >= 0 && t <= pos ? bt[pdiv.div(t)] : -1, g, kvh, pdiv);
+    }
+    __builtin_amdgcn_wave_barrier();
+    bool ra = issue(A);
+    resolve_rows<NW>(
+        lds.rows, 16 * NW, imax(0, nlp - 16 * NW),
+        [&](int i) {
+            const int e = 16 * NW + i;
+            return e < nl ? local_tok(e) : -1;
+        },
+        pos, bt, g, kvh, pdiv);
+
+    // the histogram
+    TopkPlan tp = {0u, 0u, 0, 0u, -1, 0, 0};
+    if (rank) tp = topk_digits(tk, ncand, keys);
+    __syncthreads();
+
+    auto emit = [&](int p, int i) { sel_lds[p] = plo + i; };
+    const bool sorted = !rank || tp.lo == tp.hi;  // the list is the lowest k candidates
+    if (!sorted) topk_boundary(tk, k, tp);
+    const bool multipass = !sorted && tp.nd > kTopkBoundMax;  // uniform: one histogram
+    if (multipass) {
+        __syncthreads();  // the multi-pass select clears the histogram first
+        block_topk_keys(ncand, k, keys, tp.lo, tp.hi, tk, emit);
+        __syncthreads();
+    } else if (!sorted) {
+        topk_collect_block(ncand, keys, tp, tk);
+        __syncthreads();
+    }
+    if (wave == SW) {
+        if (sorted) {
+            for (int i = lane; i < k; i += 64) emit(i, i);
+        } else if (!multipass) {
+            topk_emit_wave(ncand, k, tp, tk, emit);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (split == 0) {
+            int32_t* sel_g = a.sel + prob * a.k_max;
+            for (int i = lane; i < a.k_max; i += 64) sel_g[i] = i < k ? sel_lds[i] : -1;
+            if (lane == 0) a.count[prob] = k;
+        }
+        __hip_atomic_store(&sel_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+
     // Three tiles in flight per wave.  Real tiles are computed in tile order
     // whatever the timing of the page list, so results do not depend on it.
-    typename Core::Buf A, B, C;
     poll();
-    bool ra = issue(A), rb = issue(B), rc = issue(C);
+    bool rb = issue(B), rc = issue(C);
     // The only exit is at the end of a round of three, where the loads in
     // flight are in the same order as on the way round, so the waits inside
     // the loop stay at one tile each.
