@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the warmup and the timed region (for profiler runs)")
+    ap.add_argument("--token-splits", type=int, default=0, help="semantic-512k: token chunks per page (0: default)")
+    ap.add_argument("--workload", default="llama3-70b-layer-128k",
+                    choices=["llama3-70b-layer-128k", "semantic-512k"],
+                    help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine)")
     return ap.parse_args()
 
 
@@ -105,6 +109,133 @@ def traffic_record(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def replicate(pool, c, R):
+    """R copies of the cache in one physical-page pool and the block table of
+    each copy (so repeated steps do not find their pages in the last-level
+    cache)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_long_page_amd.device import to_device
+
+    if R > 1:
+        k_all = torch.empty((R * c.num_phys,) + tuple(pool.k.shape[1:]), dtype=pool.k.dtype, device="cuda")
+        v_all = torch.empty_like(k_all)
+        for r in range(R):
+            k_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.k)
+            v_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.v)
+        pool.k, pool.v, pool.num_phys = k_all, v_all, R * c.num_phys
+    tables = []
+    for r in range(R):
+        bt = c.block_table.astype(np.int64)
+        tables.append(to_device(np.where(bt >= 0, bt + r * c.num_phys, -1).astype(np.int32)))
+    return tables
+
+
+def bench_semantic(args):
+    """The semantic-block chunk (64 query rows, 2048-token blocks, 16 blocks
+    per row at 512K context): selection, the decode grouped by page and the
+    combine, against the per-row decode of the same lists."""
+    import numpy as np
+    import torch
+
+    from block_sparse_long_page_amd import accounting, binding as B, configs, synth
+    from block_sparse_long_page_amd.device import DeviceCache, GroupedStep, SparseDecoder, to_device
+
+    wl = configs.SEMANTIC_512K
+    t0 = time.time()
+    pr = synth.workload_problem(wl)
+    c = pr.cache
+    log(f"inputs {time.time() - t0:.1f}s")
+    R = max(1, min(args.replicas, 3))  # 2 GiB of K+V per copy
+    pool = DeviceCache.from_host(c)
+    tables = replicate(pool, c, R)
+    q = to_device(pr.q)
+    Q = pr.Q
+    dec = SparseDecoder(pool, mode=pr.mode, Q=Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                        splits=args.splits or None)
+    gs = GroupedStep(dec, token_splits=args.token_splits or None)
+    descs = [pool.desc(block_table=t) for t in tables]
+    metas = [dec.meta] + [pool.new_meta(pr.mode) for _ in range(R - 1)]
+    for d, m in zip(descs, metas):
+        B.sparse_attn_build_page_meta(d, pr.mode, 0, pool.max_pages, m)
+    torch.cuda.synchronize()
+
+    def select(r):
+        B.sparse_attn_select(descs[r], q, Q, metas[r], pr.mode, pr.sink, pr.window, pr.budget, dec.sel, dec.count,
+                             dec.ws, dec.ws_bytes)
+
+    def step_grouped(r):
+        select(r)
+        B.sparse_attn_decode_grouped(descs[r], q, Q, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, 0.0, gs.ts,
+                                     gs.ls, gs.part_o, gs.part_ml, gs.ws, gs.ws_bytes)
+        gs.combine()
+
+    def step_rows(r):
+        select(r)
+        B.sparse_attn_decode(descs[r], q, Q, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, B.SA_PART_ALL, 0.0,
+                             dec.splits, 0, dec.part_o, dec.part_ml)
+        dec.combine()
+
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(step, n):
+        for i in range(args.warmup):
+            step(i % R)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            step(i % R)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n
+
+    ms = timed(step_grouped, K)
+    ms_rows = float("nan") if args.only_timed else timed(step_rows, max(1, K // 5))
+
+    # bytes: the union of the rows' pages per (sequence, KV head), read once
+    sel, cnt = dec.selection()
+    L = int(c.seq_lens[0])
+    se, ws = accounting.regions(L, pr.sink, pr.window)
+    union_tok = union_pages = list_pages = 0
+    flops = 0
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            rows_of = {}
+            for i in range(Q):
+                for p in sel[b, h, i, : cnt[b, h, i]]:
+                    rows_of.setdefault(int(p), []).append(i)
+            list_pages += int(cnt[b, h].sum())
+            union_pages += len(rows_of)
+            for p, rows in rows_of.items():
+                n = max(0, min((p + 1) * c.P, ws) - max(p * c.P, se))
+                union_tok += n
+                flops += 4 * n * c.hd * len(rows) * (c.Hq // c.Hkv)
+    local_tok = c.B * c.Hkv * (se + (L - ws))
+    flops += 4 * local_tok * c.hd * Q * (c.Hq // c.Hkv)  # an upper bound: rows attend causal parts of the window
+    n_cand = accounting.candidate_pages(L, c.P, pr.sink, pr.window)
+    sb = accounting.grouped_step_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2, Q=Q, n_cand=n_cand,
+                                       k_max=dec.k_max, mode=pr.mode, union_tokens=union_tok,
+                                       local_tokens=local_tok, stride=gs.stride)
+    gbs = sb.total / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 512K ctx semantic blocks, 64-row chunk",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2), "pct_hbm_peak": round(100 * gbs / 8000, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded): 256 vMF clusters of 2048 keys per (b, kvh), V N(0,1), rows around 4 topics",
+        "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
+                   "context": L, "page": c.P, "rows": Q, "budget": pr.budget, "window": pr.window,
+                   "score": "centroid", "replicas": R, "token_splits": gs.ts, "local_splits": gs.ls,
+                   "step": "select + grouped decode + combine"},
+        "union_pages": union_pages, "listed_pages": list_pages,
+        "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1), "flops_per_step": flops,
+        "per_row_us_per_step": round(ms_rows * 1e3, 2), "speedup_vs_per_row": round(ms_rows / ms, 2),
+        "bytes_per_step": sb.as_dict(),
+    }))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +247,10 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+
+    if args.workload == "semantic-512k":
+        bench_semantic(args)
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth
@@ -130,18 +265,7 @@ def main():
     # R copies of the cache in one physical-page pool; replica r's table points at its own pages
     R = max(1, args.replicas)
     pool = DeviceCache.from_host(c)
-    if R > 1:
-        k_all = torch.empty((R * c.num_phys,) + tuple(pool.k.shape[1:]), dtype=pool.k.dtype, device="cuda")
-        v_all = torch.empty_like(k_all)
-        for r in range(R):
-            k_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.k)
-            v_all[r * c.num_phys:(r + 1) * c.num_phys].copy_(pool.v)
-        pool.k, pool.v, pool.num_phys = k_all, v_all, R * c.num_phys
-    tables = []
-    for r in range(R):
-        bt = c.block_table.astype(np.int64)
-        bt = np.where(bt >= 0, bt + r * c.num_phys, -1).astype(np.int32)
-        tables.append(to_device(bt))
+    tables = replicate(pool, c, R)
     q = to_device(pr.q)
 
     dec = SparseDecoder(pool, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,

@@ -135,3 +135,22 @@ def attended_tokens_exact(L: int, P: int, S: int, W: int, pages, Q: int = 1, row
         z = min((int(p) + 1) * P, ws, pos + 1)
         n += max(0, z - a)
     return n
+
+
+def grouped_step_bytes(*, B: int, Hq: int, Hkv: int, hd: int, elem_bytes: int, Q: int, n_cand: int, k_max: int,
+                       mode: int, union_tokens: int, local_tokens: int, stride: int) -> StepBytes:
+    """Algorithmic bytes of one multi-query step decoded by page: the page
+    summaries once per (sequence, KV head), q, the per-row page scores
+    (written and read back) and page lists, the K+V of the union of the rows'
+    selected pages (`union_tokens` middle tokens over all (b, kvh)) and of
+    the sink and window (`local_tokens`, each read once per (b, kvh)), the
+    partials (`stride` slots per row, written and read) and the output."""
+    rows = B * Hq * Q
+    problems = B * Hkv * Q
+    meta = B * Hkv * n_cand * summary_bytes_per_page(mode, hd, elem_bytes)
+    scores = 2 * problems * n_cand * 4 + problems * (k_max + 1) * 4
+    kv = (union_tokens + local_tokens) * 2 * hd * elem_bytes
+    partials = 2 * rows * stride * (hd + 2) * 4
+    out = rows * hd * elem_bytes + rows * 4
+    return StepBytes(kv=kv, meta=meta + scores, q=rows * hd * elem_bytes, partials=partials, out=out)
+

@@ -27,6 +27,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                       "(python -m block_sparse_long_page_amd._build)")
 
+# The library and PyTorch both need libamdhip64.so.7, and the first copy
+# loaded serves the whole process: load PyTorch's (which allocates the
+# tensors this binding passes) before the library, so one HIP runtime backs
+# both, whatever module imported this one first.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -59,6 +65,9 @@ _SIGS = {
                                                ctypes.c_size_t, _P, _P, _P]),
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "sparse_attn_decode_grouped": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P,
+                                                  _P, ctypes.c_size_t, _P]),
+    "sparse_attn_grouped_workspace_bytes": (ctypes.c_size_t, [_DESC]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -149,6 +158,19 @@ def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, p
                         lse=None, stream=None) -> None:
     _check(_lib.sparse_attn_combine(num_rows, head_dim, num_splits, _ptr(part_o), _ptr(part_ml), _ptr(out),
                                     out_dtype, _ptr(lse), _stream(stream)), "sparse_attn_combine")
+
+
+def sparse_attn_decode_grouped(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count, k_max: int, sink_len: int,
+                               window_len: int, softmax_scale: float, token_splits: int, local_splits: int, part_o,
+                               part_ml, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_grouped(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(sel_pages), _ptr(sel_count),
+                                           k_max, sink_len, window_len, softmax_scale, token_splits, local_splits,
+                                           _ptr(part_o), _ptr(part_ml), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)), "sparse_attn_decode_grouped")
+
+
+def sparse_attn_grouped_workspace_bytes(kv: sa_kv_desc) -> int:
+    return int(_lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(kv)))
 
 
 def sparse_attn_status_string(status: int) -> str:

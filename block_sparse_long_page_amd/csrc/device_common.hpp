@@ -173,6 +173,12 @@ __device__ __forceinline__ int dpp_shr0(int x)
 // not infer that threadIdx.x / 64 is the same across a wave)
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
+// Number of lanes of this wave below the calling lane whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
 {
     x = min(x, (uint32_t)dpp_i<0xB1>((int)x));

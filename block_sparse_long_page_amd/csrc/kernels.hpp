@@ -10,6 +10,8 @@ namespace sa {
 constexpr int kSelCap = 1024;        // page-list entries the bf16 decode stages in LDS
 constexpr int kRowsWG = 2048;        // rows a decode workgroup resolves per prologue round
 constexpr int kFusedMaxCand = 8192;  // candidate pages the select-and-decode kernel ranks in LDS
+constexpr int kGroupMaxPages = 4096; // pages per sequence the grouped decode's plan holds in LDS (12 B each)
+constexpr int kGroupMaxRows = 64;    // query rows of the grouped decode (one mask bit each)
 
 struct FastDivHost {
     uint32_t d, magic, shift;
@@ -82,6 +84,27 @@ struct SelectDecodeArgs {
     int32_t* count;
 };
 
+// Multi-query decode grouped by page: the union of the rows' page lists is
+// streamed once per (sequence, KV head).
+struct GroupArgs {
+    Geometry g;
+    const void* q;
+    int Q;
+    const int32_t* sel;    // [B][Hkv][Q][k_max], each row ascending
+    const int32_t* count;  // [B][Hkv][Q]
+    int k_max, S, W;
+    float scale_log2;
+    int tsplit;        // token chunks per page; slot of (list index j, chunk s) = j * tsplit + s
+    int split_stride;  // partial slots per row
+    float* part_o;
+    float* part_ml;
+    // workspace: the plan
+    int32_t* nunion;               // [B][Hkv] pages in the union
+    int32_t* upages;               // [B][Hkv][max_pages] the union, ascending
+    unsigned long long* umasks;    // [B][Hkv][max_pages] rows that chose each page
+    int16_t* slots;                // [B][Hkv][max_pages][64] each row's list index of each union page
+};
+
 struct CombineArgs {
     int rows, hd, splits, out_dtype;
     const float* part_o;
@@ -99,5 +122,7 @@ hipError_t launch_select_decode(const SelectDecodeArgs& a, hipStream_t s);
 // resident decode workgroups per CU for this shape (occupancy query)
 int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// plan kernel, then the grouped decode over max_union pages per (sequence, KV head)
+hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
 
 }  // namespace sa

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 
@@ -18,6 +19,7 @@ namespace {
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxSelectPages = 12288;  // the top-k workgroup holds one key per page in LDS
 constexpr long kMaxGridY = 65535;
+constexpr int kMaxTokenSplits = 64;  // token chunks per page of the grouped decode
 
 bool sync_mode()
 {
@@ -90,6 +92,24 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
     const long toks = (long)(sink_len > 0 ? sink_len : 0) + (window_len > 0 ? window_len : 0) +
                       (long)(k_max > 0 ? k_max : 0) * page_size;
     return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
+}
+
+// workspace of the grouped decode: byte offsets of its four arrays, each
+// 256-byte aligned
+struct GroupedWs {
+    size_t nunion, upages, umasks, slots, total;
+};
+GroupedWs grouped_ws(const sa_kv_desc* kv)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads, mp = (size_t)kv->max_pages_per_seq;
+    GroupedWs w;
+    w.nunion = 0;
+    w.upages = up(w.nunion + bh * sizeof(int32_t));
+    w.umasks = up(w.upages + bh * mp * sizeof(int32_t));
+    w.slots = up(w.umasks + bh * mp * sizeof(unsigned long long));
+    w.total = up(w.slots + bh * mp * sa::kGroupMaxRows * sizeof(int16_t));
+    return w;
 }
 
 size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
@@ -257,6 +277,54 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
                            num_splits, num_splits, part_o,     part_ml,
                            sel_pages,  sel_count};
     return finish(sa::launch_select_decode(d, stream), stream);
+}
+
+size_t sparse_attn_grouped_workspace_bytes(const sa_kv_desc* kv)
+{
+    if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1) return 0;
+    return grouped_ws(kv).total;
+}
+
+int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                               const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                               float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
+                               float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!q || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 || k_max < 0)
+        return SA_ERR_INVALID_ARG;
+    if (k_max > 0 && (!sel_pages || !sel_count)) return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (token_splits < 1 || token_splits > kMaxTokenSplits || local_splits < 1) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    const long stride = (long)k_max * token_splits + local_splits;
+    if (stride > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_BF16 || num_q_rows > sa::kGroupMaxRows || kv->max_pages_per_seq > sa::kGroupMaxPages)
+        return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    const GroupedWs w = grouped_ws(kv);
+    if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
+        return SA_ERR_INVALID_ARG;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    const float sl2 = scale * 1.4426950408889634f;
+    if (k_max > 0) {
+        char* base = (char*)workspace;
+        const long max_union = std::min<long>(kv->max_pages_per_seq, (long)num_q_rows * k_max);
+        sa::GroupArgs a{g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, sl2, token_splits,
+                        (int)stride, part_o, part_ml, (int32_t*)(base + w.nunion), (int32_t*)(base + w.upages),
+                        (unsigned long long*)(base + w.umasks), (int16_t*)(base + w.slots)};
+        const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
+        if (r1 != SA_OK) return r1;
+    }
+    // the sink and window tokens: the per-row decode into the slots after the pages'
+    const long off = (long)k_max * token_splits;
+    sa::DecodeArgs d{g,        q,          num_q_rows, nullptr,       nullptr, 0,
+                     sink_len, window_len, SA_PART_LOCAL, sl2,        local_splits,
+                     (int)stride, part_o + off * kv->head_dim, part_ml + off * 2};
+    return finish(sa::launch_decode(d, stream), stream);
 }
 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,

@@ -18,12 +18,6 @@ __device__ __forceinline__ uint32_t order_key(float f)
 constexpr int kTopkThreads = 512;
 constexpr int kTopkMaxRounds = 24;  // keys per thread: up to 12288 candidate pages
 
-// Number of lanes of this wave below the calling lane whose bit is set in m.
-__device__ __forceinline__ int lanes_below(uint64_t m)
-{
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 constexpr int kCntChunks = (kTopkMaxRounds * (kTopkThreads / 64) + 63) / 64;
 
 // Exclusive prefix sums of cnt[0 .. n) held across the wave: entry e's prefix

@@ -191,3 +191,43 @@ class OverlappedStep:
         main.wait_event(self.join)
         B.sparse_attn_combine(d.rows, d.c.hd, self.stride, self.part_o, self.part_ml, d.out, d.out_dtype, d.lse)
         return d.out
+
+
+class GroupedStep:
+    """Multi-query decode grouped by page (sparse_attn_decode_grouped) on a
+    SparseDecoder's page lists, merged into that decoder's output: every
+    selected page is read once per (sequence, KV head) for all the rows that
+    chose it."""
+
+    def __init__(self, dec: SparseDecoder, token_splits: Optional[int] = None,
+                 local_splits: Optional[int] = None):
+        c = dec.c
+        self.dec = dec
+        # one workgroup per page up to 4096-token pages (measured best at 2048); sink + window
+        # splits of about 512 tokens
+        self.ts = token_splits or max(1, min(4, c.P // 4096))
+        self.ls = local_splits or max(1, min(16, (dec.sink + dec.window + 511) // 512))
+        self.stride = dec.k_max * self.ts + self.ls
+        self.ws_bytes = B.sparse_attn_grouped_workspace_bytes(dec.desc)
+        dev = c.k.device
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.part_o = torch.empty((dec.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((dec.rows, self.stride, 2), dtype=torch.float32, device=dev)
+
+    def decode(self, q: torch.Tensor, window: Optional[int] = None, scale: float = 0.0, stream=None):
+        d = self.dec
+        B.sparse_attn_decode_grouped(d.desc, q, d.Q, d.sel, d.count, d.k_max, d.sink,
+                                     d.window if window is None else window, scale, self.ts, self.ls, self.part_o,
+                                     self.part_ml, self.ws, self.ws_bytes, stream)
+
+    def combine(self, stream=None):
+        d = self.dec
+        B.sparse_attn_combine(d.rows, d.c.hd, self.stride, self.part_o, self.part_ml, d.out, d.out_dtype, d.lse,
+                              stream)
+
+    def step(self, q: torch.Tensor, stream=None):
+        self.dec.select(q, stream=stream)
+        self.decode(q, stream=stream)
+        self.combine(stream=stream)
+        return self.dec.out
+

@@ -13,6 +13,8 @@
  *   sparse_attn_decode           exact softmax attention over sink, window and
  *                                the selected pages, split over the token set
  *   sparse_attn_combine          log-sum-exp merge of the split partials
+ *   sparse_attn_decode_grouped   multi-query decode that reads each selected
+ *                                page once for all the rows that chose it
  *
  * sparse_attn_decode_step runs select and decode of a selecting step with the
  * top-k inside the decode kernel (two launches instead of three).
@@ -238,6 +240,45 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
                             float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
                             void* workspace, size_t workspace_bytes, float* part_o, float* part_ml,
                             hipStream_t stream);
+
+/*
+ * Multi-query decode grouped by page (semantic-blocks page: the query rows
+ * that chose the same block are collected and the block's keys and values
+ * are loaded once for all of them).  The same attention as sparse_attn_decode
+ * with parts = SA_PART_ALL for num_q_rows rows with per-row page lists: per
+ * (sequence, KV head) the union of the rows' selected pages is streamed once,
+ * and every page's middle-region tokens are attended by each row (and each
+ * of the G heads of the group) that listed it, on the matrix cores.  The sink
+ * and window tokens run through the per-row decode.
+ *   sel_pages, sel_count, k_max  per-row page lists as sparse_attn_select
+ *                writes them: ascending, distinct candidate pages; entries
+ *                that are not give unspecified results (never an access out
+ *                of bounds).  k_max = 0 attends the sink and window only.
+ *   token_splits 1..64 chunks of each page's middle tokens, one workgroup
+ *                each (more workgroups for few, long pages).
+ *   local_splits >= 1 splits of each row's sink and window tokens.
+ *   part_o, part_ml  as in sparse_attn_decode with split_stride =
+ *                k_max * token_splits + local_splits (<= 1024): slot
+ *                j * token_splits + c holds chunk c of the row's j-th page,
+ *                slots k_max * token_splits + s the sink/window split s; an
+ *                unused slot holds (-inf, 0) and o = 0.  Merge them with
+ *                sparse_attn_combine(num_splits = split_stride).
+ *   workspace    >= sparse_attn_grouped_workspace_bytes(kv) bytes, 256-byte
+ *                aligned (the per-(sequence, KV head) plan: page union, row
+ *                masks, slots); needed when k_max > 0.
+ * bf16 caches, num_q_rows <= 64, max_pages_per_seq <= 4096.  Results are
+ * bitwise reproducible (fixed slots, fixed merge order).
+ * Errors: those of sparse_attn_decode; SA_ERR_UNSUPPORTED outside the limits
+ * above; SA_ERR_INVALID_ARG for a bad split count, a small or misaligned
+ * workspace or missing page lists.
+ */
+int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                               const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                               float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
+                               float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of sparse_attn_decode_grouped for this cache (host only; 0 for a bad descriptor). */
+size_t sparse_attn_grouped_workspace_bytes(const sa_kv_desc* kv);
 
 /* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,

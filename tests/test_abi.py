@@ -22,7 +22,8 @@ def test_exports_every_header_function():
     names = B.header_symbols()
     assert set(names) == {
         "sparse_attn_build_page_meta", "sparse_attn_select", "sparse_attn_workspace_bytes", "sparse_attn_decode",
-        "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string"}
+        "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string",
+        "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -174,6 +175,46 @@ def test_decode_step_checks():
         dd = _desc(**bad)
         assert lib.sparse_attn_decode_step(ctypes.byref(dd), DEV, 1, DEV, 0, 16, 16, 32, 0.0, 4, DEV, DEV, DEV, ws,
                                            DEV, DEV, None) == code
+
+
+def test_decode_grouped_checks():
+    lib = B.library()
+    d = _desc()
+    ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
+    # four 256-byte aligned arrays: counts, pages, row masks, per-row slots
+    assert ws == 256 + 256 + 256 + ((2 * 2 * 8 * 64 * 2 + 255) // 256) * 256
+    assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
+
+    def grouped(**kw):
+        a = dict(q=DEV, rows=4, sel=DEV, cnt=DEV, kmax=4, S=16, W=16, scale=0.0, ts=2, ls=1, po=DEV, pml=DEV,
+                 ws=DEV, wsb=ws)
+        a.update(kw)
+        return lib.sparse_attn_decode_grouped(ctypes.byref(a.get("desc", d)), a["q"], a["rows"], a["sel"], a["cnt"],
+                                              a["kmax"], a["S"], a["W"], a["scale"], a["ts"], a["ls"], a["po"],
+                                              a["pml"], a["ws"], a["wsb"], None)
+
+    assert grouped(q=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(po=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(pml=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(sel=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(rows=0) == B.SA_ERR_INVALID_ARG
+    assert grouped(rows=129) == B.SA_ERR_INVALID_ARG  # more rows than the cache holds tokens
+    assert grouped(S=-1) == B.SA_ERR_INVALID_ARG
+    assert grouped(W=0) == B.SA_ERR_INVALID_ARG
+    assert grouped(kmax=-1) == B.SA_ERR_INVALID_ARG
+    assert grouped(ts=0) == B.SA_ERR_INVALID_ARG
+    assert grouped(ts=65) == B.SA_ERR_INVALID_ARG
+    assert grouped(ls=0) == B.SA_ERR_INVALID_ARG
+    assert grouped(kmax=600, ts=2) == B.SA_ERR_INVALID_ARG  # more than 1024 slots per row
+    assert grouped(scale=float("nan")) == B.SA_ERR_INVALID_ARG
+    assert grouped(ws=None) == B.SA_ERR_INVALID_ARG
+    assert grouped(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert grouped(ws=DEV + 16) == B.SA_ERR_INVALID_ARG  # not 256-byte aligned
+    assert grouped(rows=65) == B.SA_ERR_UNSUPPORTED  # one mask bit per row
+    assert grouped(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    for bad, code in BAD_DESCS:
+        assert grouped(desc=_desc(**bad)) == code
 
 
 def test_combine_checks():

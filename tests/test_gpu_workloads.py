@@ -18,7 +18,8 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from block_sparse_long_page_amd.device import DeviceCache, SparseDecoder, to_device  # noqa: E402
+from block_sparse_long_page_amd import binding as B  # noqa: E402
+from block_sparse_long_page_amd.device import DeviceCache, GroupedStep, SparseDecoder, to_device  # noqa: E402
 
 
 def _say(*a):
@@ -62,6 +63,17 @@ def test_single_step_workload(wl):
     err2 = check_output(dec.out_f32(), ref.out, pr.cache.dtype, wl.name + " fused")
     check_lse(dec.lse_f32(), ref.lse, wl.name + " fused")
     _say(f"[{wl.name}] fused step max-abs {err2:.2e}")
+    if pr.Q > 1 and pr.cache.dtype == B.SA_BF16:
+        # several query rows: the decode grouped by page reads each selected page once
+        gs = GroupedStep(dec)
+        gs.decode(q)
+        gs.combine()
+        torch.cuda.synchronize()
+        err3 = check_output(dec.out_f32(), ref.out, pr.cache.dtype, wl.name + " grouped")
+        check_lse(dec.lse_f32(), ref.lse, wl.name + " grouped")
+        union = int(gs.ws[: 4 * pr.cache.B * pr.cache.Hkv].view(torch.int32).sum())
+        _say(f"[{wl.name}] grouped max-abs {err3:.2e}, pages in the unions {union} "
+             f"(per-row lists {int(cnt.sum())})")
 
 
 def test_hybrid_schedule():
