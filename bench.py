@@ -231,7 +231,8 @@ def bench_semantic(args):
                    "step": "select + grouped decode + combine"},
         "union_pages": union_pages, "listed_pages": list_pages,
         "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1), "flops_per_step": flops,
-        "per_row_us_per_step": round(ms_rows * 1e3, 2), "speedup_vs_per_row": round(ms_rows / ms, 2),
+        "per_row_us_per_step": None if ms_rows != ms_rows else round(ms_rows * 1e3, 2),
+        "speedup_vs_per_row": None if ms_rows != ms_rows else round(ms_rows / ms, 2),
         "bytes_per_step": sb.as_dict(),
     }))
 
