@@ -62,8 +62,10 @@ def parse():
                     help="run only the warmup and the timed region (for profiler runs)")
     ap.add_argument("--token-splits", type=int, default=0, help="semantic-512k: token chunks per page (0: default)")
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
-                    choices=["llama3-70b-layer-128k", "semantic-512k"],
-                    help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine)")
+                    choices=["llama3-70b-layer-128k", "semantic-512k", "hybrid-3layer-256k"],
+                    help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
+                         "hybrid-3layer-256k: the 128-step schedule of three layers (summary refresh of the last "
+                         "page every step, selection every 32 steps, growing window between)")
     return ap.parse_args()
 
 
@@ -237,6 +239,111 @@ def bench_semantic(args):
     }))
 
 
+def bench_hybrid(args):
+    """The hybrid model's three full-attention layers at 256k over 128 decode
+    steps: every step appends a token to every sequence; steps 0, 32, 64, 96
+    summarise the pages appended since the previous selection and select and
+    decode with the top-k inside the decode kernel, the others decode the
+    kept pages with the window grown by the steps since the selection; then
+    the combine.  Reports the average per layer-step over the schedule."""
+    import torch
+
+    from block_sparse_long_page_amd import accounting, configs, synth
+    from block_sparse_long_page_amd.device import DeviceCache, SparseDecoder, to_device
+
+    wl = configs.HYBRID_256K
+    t0 = time.time()
+    hs = synth.hybrid_schedule(wl)
+    L0, T, RF = hs.context, hs.steps, hs.refresh
+    log(f"inputs {time.time() - t0:.1f}s")
+    layers = []
+    seq_lens = None  # the layers of one model share the sequences' lengths
+    for li in range(len(hs.caches)):
+        cache = hs.caches[li]
+        cache.seq_lens[:] = L0
+        dc = DeviceCache.from_host(cache, max_seq_len=L0 + T)
+        if seq_lens is None:
+            seq_lens = dc.seq_lens
+        dc.seq_lens = seq_lens
+        dec = SparseDecoder(dc, mode=hs.mode, Q=1, sink=hs.sink, window=hs.windows[li], budget=hs.budgets[li],
+                            splits=args.splits or None)
+        dec.build_meta()
+        layers.append((dc, dec, hs.windows[li], [to_device(hs.q[li][t]) for t in range(T)]))
+        hs.caches[li] = None  # the host copy is no longer needed
+    torch.cuda.synchronize()
+    P = layers[0][0].P
+
+    def reset():
+        seq_lens.fill_(L0)
+        for dc, dec, W, qs in layers:
+            dec.build_meta((L0 - 1) // P, dc.max_pages)
+
+    def schedule(steps):
+        # The summaries are read only when selecting, so the pages appended
+        # since the last selection are summarised right before the next one
+        # (the same summaries as folding each token in as it arrives).
+        t_ref = 0
+        for t in range(steps):
+            L = L0 + t
+            if t > 0:
+                seq_lens.fill_(L)  # one token appended to every sequence
+            if t % RF == 0:
+                first = (L0 + t_ref - 1) // P  # the page that held the last token at the previous selection
+                t_ref = t
+            for dc, dec, W, qs in layers:
+                if t == t_ref:
+                    if t > 0:
+                        dec.build_meta(first, (L - 1) // P + 1)
+                    dec.select_decode(qs[t])
+                else:
+                    dec.decode(qs[t], window=W + (t - t_ref))
+                dec.combine()
+
+    schedule(min(args.warmup, T))
+    torch.cuda.synchronize()
+    reset()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    schedule(T)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+
+    # algorithmic bytes of the schedule
+    total = 0
+    c0 = layers[0][0]
+    for dc, dec, W, qs in layers:
+        t_ref = 0
+        for t in range(T):
+            L = L0 + t
+            if t % RF == 0:
+                t_ref = t
+            w_eff = W + (t - t_ref)
+            sb = accounting.decode_step_bytes(B=dc.B, Hq=dc.Hq, Hkv=dc.Hkv, hd=dc.hd, elem_bytes=2, L=L, P=P,
+                                              S=hs.sink, W=w_eff, budget=dec.budget, mode=0, splits=dec.splits)
+            step = sb.total if t == t_ref else sb.total - sb.meta  # summaries are read when selecting
+            if t == t_ref and t > 0:  # the pages appended since the last selection summarised
+                pages = (L - 1) // P - (L0 + t - RF - 1) // P + 1
+                step += dc.B * dc.Hkv * pages * (P * dc.hd * 2 + 2 * dc.hd * 2)
+            total += step
+    n = T * len(layers)
+    gbs = total / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, hybrid 3-layer 256k, average over 128 steps",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": T, "warmup": min(args.warmup, T),
+        "ms_per_step": round(ms / T, 5), "us_per_step": round(1e3 * ms / T, 2),
+        "us_per_layer_step": round(1e3 * ms / n, 2), "pct_hbm_peak": round(100 * gbs / 8000, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded): K, V, q N(0,1); one token appended per step and layer",
+        "config": {"workload": wl.name, "batch": c0.B, "q_heads": c0.Hq, "kv_heads": c0.Hkv, "head_dim": c0.hd,
+                   "context": L0, "page": P, "sink": hs.sink, "layers": [
+                       {"window": W, "budget": dec.budget, "splits": dec.splits} for dc, dec, W, qs in layers],
+                   "refresh": RF, "step": "summary refresh + (select-and-decode | decode) + combine per layer"},
+        "bytes_per_schedule": total,
+    }))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -252,6 +359,9 @@ def main():
 
     if args.workload == "semantic-512k":
         bench_semantic(args)
+        return
+    if args.workload == "hybrid-3layer-256k":
+        bench_hybrid(args)
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth

@@ -9,7 +9,7 @@ namespace sa {
 
 constexpr int kSelCap = 1024;        // page-list entries the bf16 decode stages in LDS
 constexpr int kRowsWG = 2048;        // rows a decode workgroup resolves per prologue round
-constexpr int kFusedMaxCand = 8192;  // candidate pages the select-and-decode kernel ranks in LDS
+constexpr int kFusedMaxCand = 8448;  // pages per sequence the select-and-decode kernel stages in LDS (256k + 8k tokens at P 32)
 constexpr int kGroupMaxPages = 4096; // pages per sequence the grouped decode's plan holds in LDS (12 B each)
 constexpr int kGroupMaxRows = 64;    // query rows of the grouped decode (one mask bit each)
 

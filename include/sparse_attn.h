@@ -227,7 +227,7 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
  *   Arguments as in sparse_attn_select and sparse_attn_decode (split_stride
  *   = num_splits).  Writes sel_pages / sel_count as sparse_attn_select does,
  *   and part_o / part_ml for sparse_attn_combine.
- * The fused kernel runs for bf16 caches with 1 <= k_max <= 1024, at most 8192
+ * The fused kernel runs for bf16 caches with 1 <= k_max <= 1024, at most 8448
  * pages per sequence, max_pages_per_seq a multiple of 4, block_table and
  * workspace 16-byte aligned, and num_splits >= (S + W + k_max * page_size) /
  * 2031 (at most 2048 row-table entries per workgroup, 15 of them padding);

@@ -172,6 +172,30 @@ def test_tied_scores_take_the_lower_pages(pattern, fused):
     check_output(dec.out_f32(), ref.out, c.dtype, pattern)
 
 
+def test_select_decode_at_the_candidate_limit():
+    """8448 pages per sequence (the most the select-and-decode kernel stages
+    in its local memory; 33792 tokens of 4-token pages): the fused step keeps
+    the oracle's page lists and attention, and so does the sequence next to
+    it that is a few pages short of the limit."""
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=128, P=4, seq_lens=[33792, 33781], sink=16, window=64,
+                              budget=4 * 700, mode="quest", dtype="bf16", seed=31, shuffle=True, clusters=8)
+    assert pr.cache.max_pages == 8448
+    dc = DeviceCache.from_host(pr.cache)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+    q = to_device(pr.q)
+    dec.build_meta()
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    r = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
+                   want_scores=True)
+    check_selection(sel, cnt, r.scores, pr.k_pages)
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, sel=sel,
+                     cnt=cnt)
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, "candidate limit")
+    check_lse(dec.lse_f32(), ref.lse, "candidate limit")
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_dense_path(name):
     pr = _problem(name, "quest")
