@@ -601,16 +601,14 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
 
 // Selection and decode in one kernel, for the steps that select.  Every
 // workgroup of a (sequence, KV head, row) stages the problem's block-table
-// row and page scores in LDS, and all its threads take the ranking up to
-// the bitmap of pages above the boundary score digit and the few keys at it;
-// then its waves part.  The last wave ranks those keys, emits the ascending
-// page list and publishes it through an LDS flag while the other waves
-// already stream the workgroup's share of the sink and window tokens (the
-// last wave joins them after).  Each wave then resolves the rows of
-// its own tiles of the selected pages' middle tokens and streams them, so no
-// workgroup barrier stands between the two shares and the K/V loads keep
-// going while the pages are ranked.  The workgroup of split 0 also writes
-// the page list and its count.
+// row and page scores in LDS; after that one barrier its waves part.  The
+// last wave ranks the pages alone (radix select in one wave), emits the
+// ascending page list and publishes it through an LDS flag, while the other
+// waves stream the workgroup's share of the sink and window tokens.  Each
+// wave then resolves the rows of its own tiles of the selected pages'
+// middle tokens and streams them, so no workgroup barrier stands between
+// the two shares and the K/V loads keep going while the pages are ranked.
+// The workgroup of split 0 also writes the page list and its count.
 
 constexpr int kSelSpinMax = 1 << 24;  // bound on the wait for the page list
 
@@ -621,10 +619,13 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     constexpr int NW = Core::NW;
     constexpr int SW = NW - 1;  // the wave that ranks the pages
     static_assert(Core::TPS == 1, "one tile per wave step");
+    static_assert(kFusedMaxCand % 4 == 0 && kFusedMaxCand <= kTopkThreads * kTopkMaxRounds,
+                  "the wave top-k reads the keys four at a time and marks them in its bitmap");
     const Geometry& g = a.g;
     __shared__ __attribute__((aligned(16))) uint32_t keys[kFusedMaxCand];
     __shared__ int bt_lds[kFusedMaxCand];
-    __shared__ TopkScratch tk;
+    __shared__ WaveTopkScratch tk;
+    __shared__ uint32_t key_range[NW][2];
     __shared__ int sel_lds[kSelCap];
     __shared__ int sel_ready;
     __shared__ MfmaLds<HD, G> lds;
@@ -691,16 +692,22 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     const int span = imax(npg, nsc);
     for (int e = 4 * 64 * NW + (int)threadIdx.x; e < span; e += 64 * NW)  // longer sequences
         stage(e, e < npg ? bt_g[e] : -1, e < nsc ? srow[e] : 0.f);
-    topk_begin(tk, lo, hi);
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        key_range[wave][0] = lo;
+        key_range[wave][1] = hi;
+    }
     if (threadIdx.x == 0) sel_ready = 0;
     __syncthreads();
     const int32_t* bt = bt_lds;
 
-    // Tiles of this wave: local tiles wave, wave + NW, ..., then middle tiles
-    // wave, wave + NW, ...  The middle ones become known when the page list
-    // is published.
+    // Tiles of this wave: local tiles wave, wave + NL, ... (the ranking wave
+    // has none), then middle tiles wave, wave + NW, ...  The middle ones
+    // become known when the page list is published.
+    constexpr int NL = NW - 1;                      // waves that stream the local share
     constexpr int kMidTilesW = kRowsWG / 16 / NW;  // most middle tiles of a wave
-    const int nloc_w = imax(0, (nlp / 16 - wave + NW - 1) / NW);
+    const int nloc_w = wave == SW ? 0 : imax(0, (nlp / 16 - wave + NL - 1) / NL);
     int nt = nloc_w, nm = 0, next = 0;  // tiles known, middle entries, next tile to load
     bool have_mid = false;
     // Takes the page list once the ranking wave has published it (never
@@ -732,52 +739,37 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     auto issue = [&](typename Core::Buf& X) {
         const bool real = next < nt;
         const bool loc = next < nloc_w;
-        const int t0 = 16 * (wave + NW * (loc ? next : next - nloc_w)) + (loc ? 0 : nlp);
+        const int t0 = loc ? 16 * (wave + NL * next) : 16 * (wave + NW * (next - nloc_w)) + nlp;
         core.load_at(real ? t0 : 0, X, 0, real ? (loc ? nlp : nlp + nm) : 0);
         next += real ? 1 : 0;
         return real;
     };
-    typename Core::Buf A, B, C;
-    // The local rows (padding entries are not attended): each wave first
-    // resolves its own first tile and issues its loads, which then overlap
-    // the ranking; all threads resolve the rest.
-    if (lane < 16 && 16 * wave + lane < nlp) {
-        const int e = 16 * wave + lane;
-        const int t = e < nl ? local_tok(e) : -1;
-        lds.rows[e] = token_row(t, pos, t >= 0 && t <= pos ? bt[pdiv.div(t)] : -1, g, kvh, pdiv);
-    }
-    __builtin_amdgcn_wave_barrier();
-    bool ra = issue(A);
-    resolve_rows<NW>(
-        lds.rows, 16 * NW, imax(0, nlp - 16 * NW),
-        [&](int i) {
-            const int e = 16 * NW + i;
-            return e < nl ? local_tok(e) : -1;
-        },
-        pos, bt, g, kvh, pdiv);
+    // The rows of this wave's local tiles (padding entries are not
+    // attended), four tiles per step; the first three tiles' loads go out
+    // after the first step.
+    auto resolve_local = [&](int q0) {
+        const int tq = q0 + (lane >> 4);
+        if (tq < nloc_w) {
+            const int e = 16 * (wave + NL * tq) + (lane & 15);
+            const int t = e < nl ? local_tok(e) : -1;
+            lds.rows[e] = token_row(t, pos, t >= 0 && t <= pos ? bt[pdiv.div(t)] : -1, g, kvh, pdiv);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+    resolve_local(0);
 
-    // the histogram
-    TopkPlan tp = {0u, 0u, 0, 0u, -1, 0, 0};
-    if (rank) tp = topk_digits(tk, ncand, keys);
-    __syncthreads();
-
-    auto emit = [&](int p, int i) { sel_lds[p] = plo + i; };
-    const bool sorted = !rank || tp.lo == tp.hi;  // the list is the lowest k candidates
-    if (!sorted) topk_boundary(tk, k, tp);
-    const bool multipass = !sorted && tp.nd > kTopkBoundMax;  // uniform: one histogram
-    if (multipass) {
-        __syncthreads();  // the multi-pass select clears the histogram first
-        block_topk_keys(ncand, k, keys, tp.lo, tp.hi, tk, emit);
-        __syncthreads();
-    } else if (!sorted) {
-        topk_collect_block(ncand, keys, tp, tk);
-        __syncthreads();
-    }
-    if (wave == SW) {
-        if (sorted) {
+    if (wave == SW) {  // the ranking, while the other waves stream
+        auto emit = [&](int p, int i) { sel_lds[p] = plo + i; };
+        uint32_t klo = 0xffffffffu, khi = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            klo = min(klo, key_range[w][0]);
+            khi = max(khi, key_range[w][1]);
+        }
+        if (!rank || klo == khi) {  // the list is the lowest k candidates
             for (int i = lane; i < k; i += 64) emit(i, i);
-        } else if (!multipass) {
-            topk_emit_wave(ncand, k, tp, tk, emit);
+        } else {
+            wave_topk(ncand, k, keys, klo, khi, tk, emit);
         }
         __builtin_amdgcn_wave_barrier();
         if (split == 0) {
@@ -790,8 +782,10 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
 
     // Three tiles in flight per wave.  Real tiles are computed in tile order
     // whatever the timing of the page list, so results do not depend on it.
+    typename Core::Buf A, B, C;
     poll();
-    bool rb = issue(B), rc = issue(C);
+    bool ra = issue(A), rb = issue(B), rc = issue(C);
+    for (int q0 = 4; q0 < nloc_w; q0 += 4) resolve_local(q0);
     // The only exit is at the end of a round of three, where the loads in
     // flight are in the same order as on the way round, so the waits inside
     // the loop stay at one tile each.

@@ -345,31 +345,35 @@ __device__ __forceinline__ void topk_collect_block(int n, const uint32_t* keys, 
     }
 }
 
-// One wave, once the bitmap and the boundary list are complete: ranks the
-// boundary keys (larger key first, then lower index) by lane reads from
-// registers, sets the best k - above of them and emits every chosen index
-// in ascending order.
-template <typename Emit>
-__device__ __forceinline__ void topk_emit_wave(int n, int k, const TopkPlan& t, TopkScratch& sh, Emit emit)
+// One wave: ranks the nd <= 64 boundary keys b_key/b_idx (larger key first,
+// then lower index) by lane reads from registers and sets the best `need`
+// of them in the bitmap.
+__device__ __forceinline__ void take_boundary(int nd, int need, const uint32_t* b_key, const int* b_idx,
+                                              uint64_t* chosen)
 {
     const int lane = threadIdx.x & 63;
-    const int nd = t.nd, need = k - t.above;  // boundary keys to take, 1 .. nd
     const bool mine = lane < nd;
-    const uint32_t bk = mine ? sh.b_key[lane] : 0u;
-    const int bi = mine ? sh.b_idx[lane] : 0;
+    const uint32_t bk = mine ? b_key[lane] : 0u;
+    const int bi = mine ? b_idx[lane] : 0;
     int rank = 0;
     for (int u = 0; u < nd; ++u) {
         const uint32_t ku = (uint32_t)__builtin_amdgcn_readlane((int)bk, u);
         const int iu = __builtin_amdgcn_readlane(bi, u);
         rank += ku > bk || (ku == bk && iu < bi);
     }
-    if (mine && rank < need) atomicOr((unsigned long long*)&sh.chosen[bi >> 6], 1ull << (bi & 63));
-    __builtin_amdgcn_wave_barrier();
+    if (mine && rank < need) atomicOr((unsigned long long*)&chosen[bi >> 6], 1ull << (bi & 63));
+}
+
+// One wave: emits the set bits of the bitmap of n indices in ascending order.
+template <typename Emit>
+__device__ __forceinline__ void emit_bitmap(int n, const uint64_t* chosen, Emit emit)
+{
+    const int lane = threadIdx.x & 63;
     const int nwords = (n + 63) / 64;
     int base = 0;
     for (int w0 = 0; w0 < nwords; w0 += 64) {
         const int w = w0 + lane;
-        uint64_t bits = w < nwords ? sh.chosen[w] : 0ull;
+        uint64_t bits = w < nwords ? chosen[w] : 0ull;
         const int cnt = __builtin_popcountll(bits);
         const int inc = wave_inclusive_scan(cnt);
         int pos = base + inc - cnt;
@@ -380,6 +384,17 @@ __device__ __forceinline__ void topk_emit_wave(int n, int k, const TopkPlan& t, 
         }
         base += __builtin_amdgcn_readlane(inc, 63);
     }
+}
+
+// One wave, once the bitmap and the boundary list are complete: takes the
+// best k - above boundary keys and emits every chosen index in ascending
+// order.
+template <typename Emit>
+__device__ __forceinline__ void topk_emit_wave(int n, int k, const TopkPlan& t, TopkScratch& sh, Emit emit)
+{
+    take_boundary(t.nd, k - t.above, sh.b_key, sh.b_idx, sh.chosen);
+    __builtin_amdgcn_wave_barrier();
+    emit_bitmap(n, sh.chosen, emit);
 }
 
 // The whole selection by the block (all 512 threads), keys already in LDS
@@ -406,6 +421,113 @@ __device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* ke
     topk_collect_block(n, keys, t, sh);
     __syncthreads();
     if ((tid >> 6) == 0) topk_emit_wave(n, k, t, sh, emit);
+}
+
+// ---------------------------------------------------------------------------
+// The same selection by one wave alone, so that a workgroup's other waves can
+// go on with other work once the keys are in LDS.  Radix select 8 bits at a
+// time from the highest bit where the smallest and largest key differ: each
+// pass histograms the digit of the keys that match the bits decided so far
+// and finds the digit where the count from the top reaches the keys still
+// needed.  The passes stop once the boundary bucket (the keys that match
+// every decided bit) holds at most 64 keys, or when every bit is decided
+// (the bucket's keys are then all equal).  One pass over the keys in index
+// order then sets the bitmap of the keys above the bucket and either
+// gathers the bucket (ranked by key, then lower index) or, for equal keys,
+// takes the lowest indices; the bitmap is emitted in ascending order.
+// ---------------------------------------------------------------------------
+
+struct WaveTopkScratch {
+    alignas(16) int hist[256];
+    uint32_t b_key[kTopkBoundMax];
+    int b_idx[kTopkBoundMax];
+    uint64_t chosen[kTopkMaxRounds * kTopkThreads / 64];
+};
+
+// The k largest of the n keys keys[0 .. n) (1 <= k < n <= kTopkThreads *
+// kTopkMaxRounds; lo < hi the smallest and largest key; the array 16-byte
+// aligned and readable up to the next multiple of 4), ties to the lower
+// index: emit(position, index) once per chosen index, ascending.  One wave.
+template <typename Emit>
+__device__ __forceinline__ void wave_topk(int n, int k, const uint32_t* keys, uint32_t lo, uint32_t hi,
+                                          WaveTopkScratch& sh, Emit emit)
+{
+    const int lane = threadIdx.x & 63;
+    int top = 31 - __builtin_clz(lo ^ hi);  // highest bit that differs
+    uint32_t hmask = top == 31 ? 0u : ~((2u << top) - 1u);  // the bits decided
+    uint32_t prefix = hi & hmask;
+    int need = k;  // keys still to take among those matching the prefix
+    int nb;        // keys matching the prefix
+    for (;;) {
+        const int width = top + 1 < 8 ? top + 1 : 8;
+        const int shift = top + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        *(int4*)&sh.hist[4 * lane] = make_int4(0, 0, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+        for (int i = 4 * lane; i < n; i += 256) {  // four keys per lane and step
+            const uint4 kv = *(const uint4*)(keys + i);
+            const uint32_t kq[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i + u < n && (kq[u] & hmask) == prefix) atomicAdd(&sh.hist[(kq[u] >> shift) & dmask], 1);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+        const int4 c = *(const int4*)&sh.hist[252 - 4 * lane];
+        const int s4 = c.x + c.y + c.z + c.w;
+        const int above4 = wave_inclusive_scan(s4) - s4;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(above4 < need && above4 + s4 >= need);
+        const int hl = (int)__builtin_ctzll(hit);
+        int above = __builtin_amdgcn_readlane(above4, hl);
+        const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+        const int cy = __builtin_amdgcn_readlane(c.y, hl), cx = __builtin_amdgcn_readlane(c.x, hl);
+        int d;
+        if (above + cw >= need) {
+            d = 255 - 4 * hl;
+            nb = cw;
+        } else if (above + cw + cz >= need) {
+            d = 254 - 4 * hl;
+            nb = cz;
+            above += cw;
+        } else if (above + cw + cz + cy >= need) {
+            d = 253 - 4 * hl;
+            nb = cy;
+            above += cw + cz;
+        } else {
+            d = 252 - 4 * hl;
+            nb = cx;
+            above += cw + cz + cy;
+        }
+        need -= above;
+        prefix |= (uint32_t)d << shift;
+        hmask |= dmask << shift;
+        if (nb <= kTopkBoundMax || shift == 0) break;
+        top = shift - 1;
+    }
+
+    // keys above the bucket: (key & hmask) > prefix; in it: == prefix
+    const bool gather = nb <= kTopkBoundMax;  // otherwise every bucket key is equal
+    int seen = 0;                             // bucket keys at lower indices
+    for (int w = 0; 64 * w < n; ++w) {
+        const int i = 64 * w + lane;
+        const uint32_t hk = (i < n ? keys[i] : 0u) & hmask;
+        const bool in = i < n && hk == prefix;
+        const uint64_t inm = __builtin_amdgcn_ballot_w64(in);
+        const int below = seen + lanes_below(inm);
+        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && (hk > prefix || (!gather && in && below < need)));
+        if (gather && in) {
+            sh.b_key[below] = keys[i];
+            sh.b_idx[below] = i;
+        }
+        seen += __builtin_popcountll(inm);
+        if (lane == 0) sh.chosen[w] = up;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (gather) {
+        take_boundary(nb, need, sh.b_key, sh.b_idx, sh.chosen);
+        __builtin_amdgcn_wave_barrier();
+    }
+    emit_bitmap(n, sh.chosen, emit);
 }
 
 }  // namespace sa
