@@ -64,8 +64,9 @@ def parse():
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
                     choices=["llama3-70b-layer-128k", "semantic-512k", "hybrid-3layer-256k"],
                     help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
-                         "hybrid-3layer-256k: the 128-step schedule of three layers (summary refresh of the last "
-                         "page every step, selection every 32 steps, growing window between)")
+                         "hybrid-3layer-256k: the 128-step schedule of three layers (one token appended every step, "
+                         "selection every 32 steps after summarising the pages appended since the last one, "
+                         "growing window between)")
     return ap.parse_args()
 
 
