@@ -6,14 +6,16 @@
 // rows that chose each page, and then streams every page of the union once.
 //
 // k_group_plan: one workgroup per (sequence, KV head).  Builds the row masks
-// in LDS with 64-bit atomic ORs, compacts the pages that carry a mask in
-// ascending order, records for every row its index in its own list of each
+// in LDS with 64-bit atomic ORs, writes the pages that carry a mask as
+// records (page, physical page, mask) in launch order (most rows first),
+// records for every row its index in its own list of each
 // page of the union (the row's slot for that page), and writes the empty
 // partial (m = -inf, l = 0, o = 0) of every slot a row does not use
 // (entries past its count).
 //
 // k_group_decode_mfma: one workgroup per (sequence, KV head, page of the
-// union, token chunk of the page).  The chunk's middle-region tokens are
+// union, token chunk of the page), launched with the pages chosen by the
+// most rows first.  The chunk's middle-region tokens are
 // contiguous rows of one physical page; 64-token stages of K and V go
 // through LDS (three stages in flight in registers, two in LDS) and are read
 // by every wave.  Query columns are (row, head) pairs of the rows in the
@@ -68,12 +70,12 @@ struct Regions {
 
 __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
 {
-    extern __shared__ unsigned long long mask[];  // [max_pages], then the union index of each page
-    __shared__ int wsum[kPlanThreads / 64];
+    extern __shared__ unsigned long long mask[];  // [max_pages], then each page's launch rank
+    __shared__ int by_rows[65];
     const Geometry& g = a.g;
-    int* uidx = (int*)(mask + g.max_pages);
+    int* rank = (int*)(mask + g.max_pages);
     const int bk = blockIdx.x, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const Regions rg(g, b, a.S, a.W);
     for (int p = tid; p < g.max_pages; p += kPlanThreads) mask[p] = 0ull;
     __syncthreads();
@@ -101,32 +103,43 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     }
     __syncthreads();
 
-    // pages with a mask, ascending, 256 at a time: wave ballots, then the
-    // waves' counts in order
-    int32_t* up = a.upages + (long)bk * g.max_pages;
-    unsigned long long* um = a.umasks + (long)bk * g.max_pages;
-    int base = 0;
-    for (int p0 = 0; p0 < g.max_pages; p0 += kPlanThreads) {
-        const int p = p0 + tid;
-        const unsigned long long m = p < g.max_pages ? mask[p] : 0ull;
-        const uint64_t on = __builtin_amdgcn_ballot_w64(m != 0ull);
-        if (lane == 0) wsum[wave] = __builtin_popcountll(on);
-        __syncthreads();
-        int before = base, total = base;
-        for (int w = 0; w < kPlanThreads / 64; ++w) {
-            before += w < wave ? wsum[w] : 0;
-            total += wsum[w];
+    // The union in launch order: pages chosen by more rows first (a counting
+    // sort by the mask's row count), so the longest workgroups start first
+    // and the last to start are short.  The order within a row count follows
+    // the atomics; it affects timing only.  Each page's record carries what
+    // its workgroup needs first (page, physical page, row mask).
+    for (int c = tid; c <= 64; c += kPlanThreads) by_rows[c] = 0;
+    __syncthreads();
+    for (int p = tid; p < g.max_pages; p += kPlanThreads)
+        if (mask[p] != 0ull) atomicAdd(&by_rows[__builtin_popcountll(mask[p])], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int c = 64; c >= 1; --c) {
+            const int nc = by_rows[c];
+            by_rows[c] = acc;
+            acc += nc;
         }
-        if (m != 0ull) {
-            const int at = before + lanes_below(on);
-            up[at] = p;
-            um[at] = m;
-            uidx[p] = at;
-        }
-        base = total;
-        __syncthreads();  // wsum is rewritten by the next chunk
+        a.nunion[bk] = acc;
     }
-    if (tid == 0) a.nunion[bk] = base;
+    __syncthreads();
+    GroupPage* up = a.upages + (long)bk * g.max_pages;
+    const int32_t* btr = g.block_table + (long)b * g.max_pages;
+    for (int p = tid; p < g.max_pages; p += kPlanThreads) {
+        const unsigned long long m = mask[p];
+        if (m != 0ull) {
+            const int at = atomicAdd(&by_rows[__builtin_popcountll(m)], 1);
+            const int ph = btr[p];
+            GroupPage e;
+            e.page = p;
+            e.phys = ph >= 0 && ph < g.num_phys ? ph : -1;
+            e.mask_lo = (uint32_t)m;
+            e.mask_hi = (uint32_t)(m >> 32);
+            up[at] = e;
+            rank[p] = at;
+        }
+    }
+    __syncthreads();
 
     // each row's index j of every page it lists: its slot for that page
     int16_t* sl = a.slots + (long)bk * g.max_pages * 64;
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         const int r = idx / a.k_max, j = idx - r * a.k_max;
         if (j < imax(0, imin(cnt[r], a.k_max))) {
             const int p = sel[idx];
-            if (p >= rg.plo && p <= rg.phi) sl[uidx[p] * 64 + r] = (int16_t)j;
+            if (p >= rg.plo && p <= rg.phi) sl[rank[p] * 64 + r] = (int16_t)j;
         }
     }
 }
@@ -163,11 +176,16 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     static_assert(kStage % 16 == 0, "stages hold whole subtiles");
 
     const Geometry& g = a.g;
-    const int bk = blockIdx.y, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-    const int ui = blockIdx.x / a.tsplit, chunk = blockIdx.x - ui * a.tsplit;
-    if (ui >= a.nunion[bk]) return;
-    const int p = a.upages[(long)bk * g.max_pages + ui];
-    const unsigned long long M = a.umasks[(long)bk * g.max_pages + ui];
+    // workgroup id = (rank * B * Hkv + bk) * tsplit + chunk: the pages of
+    // every (sequence, KV head) in their launch order, interleaved
+    const int nbk = g.B * g.Hkv;
+    const int chunk = blockIdx.x % a.tsplit, rest = blockIdx.x / a.tsplit;
+    const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+    const long ui = (long)bk * g.max_pages + rank;  // rank < max_pages: the record exists
+    const GroupPage e = a.upages[ui];
+    if (rank >= a.nunion[bk]) return;
+    const int p = e.page;
+    const unsigned long long M = ((unsigned long long)e.mask_hi << 32) | e.mask_lo;
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
     const Regions rg(g, b, a.S, a.W);
@@ -176,7 +194,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int nr = __builtin_popcountll(M);
     if (wave == 0 && ((M >> lane) & 1ull)) {
         rows_l[lanes_below(M)] = lane;
-        slot_l[lanes_below(M)] = a.slots[((long)bk * g.max_pages + ui) * 64 + lane];
+        slot_l[lanes_below(M)] = a.slots[ui * 64 + lane];
     }
     __syncthreads();
 
@@ -186,8 +204,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int n = imax(0, a1 - a0);
     const int csz = (n + a.tsplit - 1) / a.tsplit;
     const int t0 = a0 + imin(n, chunk * csz);
-    const int phys = g.block_table[(long)b * g.max_pages + p];
-    const bool mapped = phys >= 0 && phys < g.num_phys;
+    const int phys = e.phys;
+    const bool mapped = phys >= 0;
     const int t1 = mapped ? imin(a1, t0 + csz) : t0;
     const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
     // K/V row of token t0 (inside the page even when the chunk is empty)
@@ -426,7 +444,7 @@ hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_union < 1) return e;
-    const dim3 grid((unsigned)(max_union * a.tsplit), (unsigned)(g.B * g.Hkv));
+    const dim3 grid((unsigned)((long)max_union * a.tsplit * g.B * g.Hkv));
     if (g.hd == 128) return launch_group_g<128>(a, grid, s);
     if (g.hd == 64) return launch_group_g<64>(a, grid, s);
     return hipErrorInvalidValue;

@@ -84,6 +84,13 @@ struct SelectDecodeArgs {
     int32_t* count;
 };
 
+// A page of the union of the rows' page lists of one (sequence, KV head).
+struct __attribute__((aligned(16))) GroupPage {
+    int32_t page;               // logical page
+    int32_t phys;               // its physical page, -1 when unmapped
+    uint32_t mask_lo, mask_hi;  // the rows that chose it
+};
+
 // Multi-query decode grouped by page: the union of the rows' page lists is
 // streamed once per (sequence, KV head).
 struct GroupArgs {
@@ -99,10 +106,9 @@ struct GroupArgs {
     float* part_o;
     float* part_ml;
     // workspace: the plan
-    int32_t* nunion;               // [B][Hkv] pages in the union
-    int32_t* upages;               // [B][Hkv][max_pages] the union, ascending
-    unsigned long long* umasks;    // [B][Hkv][max_pages] rows that chose each page
-    int16_t* slots;                // [B][Hkv][max_pages][64] each row's list index of each union page
+    int32_t* nunion;    // [B][Hkv] pages in the union
+    GroupPage* upages;  // [B][Hkv][max_pages] the union in launch order (most rows first)
+    int16_t* slots;     // [B][Hkv][max_pages][64] each row's list index of each union page (same order)
 };
 
 struct CombineArgs {

@@ -97,7 +97,7 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
 // workspace of the grouped decode: byte offsets of its four arrays, each
 // 256-byte aligned
 struct GroupedWs {
-    size_t nunion, upages, umasks, slots, total;
+    size_t nunion, upages, slots, total;
 };
 GroupedWs grouped_ws(const sa_kv_desc* kv)
 {
@@ -106,8 +106,7 @@ GroupedWs grouped_ws(const sa_kv_desc* kv)
     GroupedWs w;
     w.nunion = 0;
     w.upages = up(w.nunion + bh * sizeof(int32_t));
-    w.umasks = up(w.upages + bh * mp * sizeof(int32_t));
-    w.slots = up(w.umasks + bh * mp * sizeof(unsigned long long));
+    w.slots = up(w.upages + bh * mp * sizeof(sa::GroupPage));
     w.total = up(w.slots + bh * mp * sa::kGroupMaxRows * sizeof(int16_t));
     return w;
 }
@@ -314,8 +313,8 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
         char* base = (char*)workspace;
         const long max_union = std::min<long>(kv->max_pages_per_seq, (long)num_q_rows * k_max);
         sa::GroupArgs a{g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, sl2, token_splits,
-                        (int)stride, part_o, part_ml, (int32_t*)(base + w.nunion), (int32_t*)(base + w.upages),
-                        (unsigned long long*)(base + w.umasks), (int16_t*)(base + w.slots)};
+                        (int)stride, part_o, part_ml, (int32_t*)(base + w.nunion),
+                        (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots)};
         const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
         if (r1 != SA_OK) return r1;
     }

@@ -264,8 +264,9 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
  *                unused slot holds (-inf, 0) and o = 0.  Merge them with
  *                sparse_attn_combine(num_splits = split_stride).
  *   workspace    >= sparse_attn_grouped_workspace_bytes(kv) bytes, 256-byte
- *                aligned (the per-(sequence, KV head) plan: page union, row
- *                masks, slots); needed when k_max > 0.
+ *                aligned (the per-(sequence, KV head) plan: the page union
+ *                with its row masks in launch order, the rows' slots);
+ *                needed when k_max > 0.
  * bf16 caches, num_q_rows <= 64, max_pages_per_seq <= 4096.  Results are
  * bitwise reproducible (fixed slots, fixed merge order).
  * Errors: those of sparse_attn_decode; SA_ERR_UNSUPPORTED outside the limits

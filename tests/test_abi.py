@@ -182,7 +182,8 @@ def test_decode_grouped_checks():
     d = _desc()
     ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
     # four 256-byte aligned arrays: counts, pages, row masks, per-row slots
-    assert ws == 256 + 256 + 256 + ((2 * 2 * 8 * 64 * 2 + 255) // 256) * 256
+    # counts, page records (16 bytes), slots; each region 256-byte aligned
+    assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 64 * 2 + 255) // 256) * 256
     assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
 
     def grouped(**kw):
