@@ -183,6 +183,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
     const long ui = (long)bk * g.max_pages + rank;  // rank < max_pages: the record exists
     const GroupPage e = a.upages[ui];
+    const int16_t lane_slot = a.slots[ui * 64 + (threadIdx.x & 63)];  // with the record, not after it
     if (rank >= a.nunion[bk]) return;
     const int p = e.page;
     const unsigned long long M = ((unsigned long long)e.mask_hi << 32) | e.mask_lo;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int nr = __builtin_popcountll(M);
     if (wave == 0 && ((M >> lane) & 1ull)) {
         rows_l[lanes_below(M)] = lane;
-        slot_l[lanes_below(M)] = a.slots[ui * 64 + lane];
+        slot_l[lanes_below(M)] = lane_slot;
     }
     __syncthreads();
 

@@ -269,6 +269,50 @@ def test_incremental_summary_of_an_appended_page():
     assert torch.equal(meta, full)
 
 
+def test_summaries_refreshed_at_selection_match_per_token_folding():
+    """The refresh schedule of the hybrid decode loop, two ways over 70 steps
+    of one appended token each (selection every 32 steps, the window grown
+    by the steps since): folding each token into the last page's summary as
+    it arrives, and summarising the pages appended since the last selection
+    right before the next one.  Summaries are read only when selecting, so
+    the summaries at every selection and every step's output are identical."""
+    L0, T, R, W = 4000, 70, 32, 64
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=128, P=32, seq_lens=[L0 + T, L0 + T], sink=16, window=W,
+                              budget=32 * 16, dtype="bf16", seed=21, shuffle=True, clusters=8)
+    c = pr.cache
+    c.seq_lens[:] = L0
+    dc = DeviceCache.from_host(c, max_seq_len=L0 + T)
+    eager = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=W, budget=pr.budget)
+    lazy = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=W, budget=pr.budget)
+    eager.build_meta()
+    lazy.build_meta()
+    rng = np.random.default_rng(5)
+    t_ref = 0
+    for t in range(T):
+        L = L0 + t
+        if t > 0:
+            dc.seq_lens.fill_(L)
+            eager.build_meta((L - 1) // dc.P, (L - 1) // dc.P + 1)
+        q = to_device(synth.store(rng.standard_normal((c.B, c.Hq, 1, c.hd)).astype(np.float32), c.dtype))
+        outs = []
+        for dec in (eager, lazy):
+            if t % R == 0:
+                if dec is lazy and t > 0:
+                    dec.build_meta((L0 + t_ref - 1) // dc.P, (L - 1) // dc.P + 1)
+                dec.select_decode(q)
+            else:
+                dec.decode(q, window=W + (t - t_ref))
+            dec.combine()
+            outs.append(dec.out.clone())
+        if t % R == 0:
+            t_ref = t
+            torch.cuda.synchronize()
+            assert torch.equal(eager.meta, lazy.meta), t
+            assert torch.equal(eager.sel, lazy.sel) and torch.equal(eager.count, lazy.count), t
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), t
+
+
 @pytest.mark.parametrize("L,S,W,budget,Q", [
     (1, 0, 1, 0, 1),  # a single token
     (5, 2, 1, 64, 5),  # every position is a query row
