@@ -94,7 +94,7 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
     return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
 }
 
-// workspace of the grouped decode: byte offsets of its four arrays, each
+// workspace of the grouped decode: byte offsets of its three arrays, each
 // 256-byte aligned
 struct GroupedWs {
     size_t nunion, upages, slots, total;

@@ -288,13 +288,16 @@ def workload_problem(wl: Workload, *, seed: Optional[int] = None, batch: Optiona
 
 def semantic_problem(wl: Workload, *, seed: Optional[int] = None, batch: Optional[int] = None,
                      blocks: int = 256, block_tokens: int = 2048, kappa: float = 100.0,
-                     q_kappa: float = 50.0, topics: int = 4) -> Problem:
+                     q_kappa: float = 50.0, topics: int = 4, scatter: bool = False) -> Problem:
     """Keys from `blocks` von Mises-Fisher clusters per (b, KV head) on the unit
     sphere scaled by sqrt(hd), exactly `block_tokens` per cluster, stored
     cluster by cluster (the permuted, block-contiguous layout), one cluster per
-    page of P = block_tokens.  The current chunk of Q queries is appended as a
-    final partial page; each query row and chunk key follows one of `topics`
-    clusters drawn per (b, KV head)."""
+    page of P = block_tokens.  With `scatter` the prefix tokens of each
+    (b, KV head) are instead placed in a seeded random order (a document in
+    which the semantic blocks are interleaved; the index builder's input).
+    The current chunk of Q queries is appended as a final partial page; each
+    query row and chunk key follows one of `topics` clusters drawn per
+    (b, KV head)."""
     seed = wl.seed if seed is None else seed
     rng = np.random.default_rng(seed)
     B = wl.batch if batch is None else batch
@@ -316,12 +319,17 @@ def semantic_problem(wl: Workload, *, seed: Optional[int] = None, batch: Optiona
         b, kvh = divmod(i, Hkv)
         r = children[i]
         mus = _unit(r, blocks, hd)
+        order = r.permutation(blocks * block_tokens) if scatter else None  # position of each clustered token
         for j0 in range(0, blocks, per):
             j1 = min(blocks, j0 + per)
             u = sample_vmf(r, np.repeat(mus[j0:j1], block_tokens, axis=0), kappa, (j1 - j0) * block_tokens)
             kk = store(u.astype(np.float32).reshape(j1 - j0, block_tokens, hd) * scale, dt)
-            for j in range(j0, j1):
-                k[bt[b, j], kvh] = kk[j - j0]
+            if order is None:
+                for j in range(j0, j1):
+                    k[bt[b, j], kvh] = kk[j - j0]
+            else:
+                pos = order[j0 * block_tokens:j1 * block_tokens]
+                k[bt[b, pos // P], kvh, pos % P] = kk.reshape(-1, hd)
         topic = r.choice(blocks, size=topics, replace=False)
         row_topic = topic[r.integers(0, topics, size=Q)]
         ck = np.zeros((P, hd), dtype=np.float32)
