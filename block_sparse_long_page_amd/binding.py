@@ -53,9 +53,18 @@ class sa_kv_desc(ctypes.Structure):
     ]
 
 
+class sa_block_index(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("offsets", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p), ("centres", ctypes.c_void_p), ("k_blocks", ctypes.c_void_p),
+        ("v_blocks", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _DESC = ctypes.POINTER(sa_kv_desc)
+_IDX = ctypes.POINTER(sa_block_index)
 _SIGS = {
     "sparse_attn_build_page_meta": (ctypes.c_int, [_DESC, _I, _I, _I, _P, _P]),
     "sparse_attn_select": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -68,6 +77,12 @@ _SIGS = {
     "sparse_attn_decode_grouped": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                   _P, ctypes.c_size_t, _P]),
     "sparse_attn_grouped_workspace_bytes": (ctypes.c_size_t, [_DESC]),
+    "sparse_attn_index_workspace_bytes": (ctypes.c_size_t, [_DESC, _I, _I]),
+    "sparse_attn_build_block_index": (ctypes.c_int, [_DESC, _I, _IDX, _P, _P, ctypes.c_size_t, _P]),
+    "sparse_attn_select_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _P, _P, _P]),
+    "sparse_attn_blocks_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX]),
+    "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
+                                                 _P, ctypes.c_size_t, _P]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -171,6 +186,42 @@ def sparse_attn_decode_grouped(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, se
 
 def sparse_attn_grouped_workspace_bytes(kv: sa_kv_desc) -> int:
     return int(_lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(kv)))
+
+
+def make_block_index(*, num_tokens, num_blocks, offsets, positions, centres, k_blocks, v_blocks) -> sa_block_index:
+    return sa_block_index(num_tokens, num_blocks, _ptr(offsets), _ptr(positions), _ptr(centres), _ptr(k_blocks),
+                          _ptr(v_blocks))
+
+
+def sparse_attn_index_workspace_bytes(kv: sa_kv_desc, num_tokens: int, num_blocks: int) -> int:
+    return int(_lib.sparse_attn_index_workspace_bytes(ctypes.byref(kv), num_tokens, num_blocks))
+
+
+def sparse_attn_build_block_index(kv: sa_kv_desc, iterations: int, index: sa_block_index, assignment, workspace,
+                                  workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sparse_attn_build_block_index(ctypes.byref(kv), iterations, ctypes.byref(index), _ptr(assignment),
+                                              _ptr(workspace), workspace_bytes, _stream(stream)),
+           "sparse_attn_build_block_index")
+
+
+def sparse_attn_select_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_rows: int, token_budget: int,
+                              k_max: int, sel_blocks, sel_count, stream=None) -> None:
+    _check(_lib.sparse_attn_select_blocks(ctypes.byref(kv), ctypes.byref(index), _ptr(q), num_q_rows, token_budget,
+                                          k_max, _ptr(sel_blocks), _ptr(sel_count), _stream(stream)),
+           "sparse_attn_select_blocks")
+
+
+def sparse_attn_blocks_workspace_bytes(kv: sa_kv_desc, index: sa_block_index) -> int:
+    return int(_lib.sparse_attn_blocks_workspace_bytes(ctypes.byref(kv), ctypes.byref(index)))
+
+
+def sparse_attn_decode_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_rows: int, sel_blocks, sel_count,
+                              k_max: int, window_len: int, softmax_scale: float, token_splits: int, local_splits: int,
+                              part_o, part_ml, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_blocks(ctypes.byref(kv), ctypes.byref(index), _ptr(q), num_q_rows,
+                                          _ptr(sel_blocks), _ptr(sel_count), k_max, window_len, softmax_scale,
+                                          token_splits, local_splits, _ptr(part_o), _ptr(part_ml), _ptr(workspace),
+                                          workspace_bytes, _stream(stream)), "sparse_attn_decode_blocks")
 
 
 def sparse_attn_status_string(status: int) -> str:

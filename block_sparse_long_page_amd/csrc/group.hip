@@ -70,14 +70,17 @@ struct Regions {
 
 __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
 {
-    extern __shared__ unsigned long long mask[];  // [max_pages], then each page's launch rank
+    extern __shared__ unsigned long long mask[];  // [npg], then each unit's launch rank
     __shared__ int by_rows[65];
     const Geometry& g = a.g;
-    int* rank = (int*)(mask + g.max_pages);
+    const int npg = a.npg;
+    int* rank = (int*)(mask + npg);
     const int bk = blockIdx.x, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
     const int tid = threadIdx.x;
     const Regions rg(g, b, a.S, a.W);
-    for (int p = tid; p < g.max_pages; p += kPlanThreads) mask[p] = 0ull;
+    // candidates: the pages with middle-region tokens, or every block
+    const int lo = a.blk_off ? 0 : rg.plo, hi = a.blk_off ? npg - 1 : rg.phi;
+    for (int p = tid; p < npg; p += kPlanThreads) mask[p] = 0ull;
     __syncthreads();
 
     const int32_t* sel = a.sel + (long)bk * a.Q * a.k_max;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         const int c = imax(0, imin(cnt[r], a.k_max));
         if (j < c) {
             const int p = sel[idx];
-            if (p >= rg.plo && p <= rg.phi) atomicOr(&mask[p], 1ull << r);
+            if (p >= lo && p <= hi) atomicOr(&mask[p], 1ull << r);
         } else {
             // a slot this row does not use: the empty partial, for every head and chunk
             for (int h = 0; h < g.G; ++h) {
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     // its workgroup needs first (page, physical page, row mask).
     for (int c = tid; c <= 64; c += kPlanThreads) by_rows[c] = 0;
     __syncthreads();
-    for (int p = tid; p < g.max_pages; p += kPlanThreads)
+    for (int p = tid; p < npg; p += kPlanThreads)
         if (mask[p] != 0ull) atomicAdd(&by_rows[__builtin_popcountll(mask[p])], 1);
     __syncthreads();
     if (tid == 0) {
@@ -123,13 +126,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         a.nunion[bk] = acc;
     }
     __syncthreads();
-    GroupPage* up = a.upages + (long)bk * g.max_pages;
+    GroupPage* up = a.upages + (long)bk * npg;
     const int32_t* btr = g.block_table + (long)b * g.max_pages;
-    for (int p = tid; p < g.max_pages; p += kPlanThreads) {
+    for (int p = tid; p < npg; p += kPlanThreads) {
         const unsigned long long m = mask[p];
         if (m != 0ull) {
             const int at = atomicAdd(&by_rows[__builtin_popcountll(m)], 1);
-            const int ph = btr[p];
+            const int ph = a.blk_off ? 0 : btr[p];  // blocks: rows of the block layout
             GroupPage e;
             e.page = p;
             e.phys = ph >= 0 && ph < g.num_phys ? ph : -1;
@@ -142,12 +145,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     __syncthreads();
 
     // each row's index j of every page it lists: its slot for that page
-    int16_t* sl = a.slots + (long)bk * g.max_pages * 64;
+    int16_t* sl = a.slots + (long)bk * npg * 64;
     for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
         const int r = idx / a.k_max, j = idx - r * a.k_max;
         if (j < imax(0, imin(cnt[r], a.k_max))) {
             const int p = sel[idx];
-            if (p >= rg.plo && p <= rg.phi) sl[rank[p] * 64 + r] = (int16_t)j;
+            if (p >= lo && p <= hi) sl[rank[p] * 64 + r] = (int16_t)j;
         }
     }
 }
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int nbk = g.B * g.Hkv;
     const int chunk = blockIdx.x % a.tsplit, rest = blockIdx.x / a.tsplit;
     const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-    const long ui = (long)bk * g.max_pages + rank;  // rank < max_pages: the record exists
+    const long ui = (long)bk * a.npg + rank;  // rank < npg: the record exists
     const GroupPage e = a.upages[ui];
     const int16_t lane_slot = a.slots[ui * 64 + (threadIdx.x & 63)];  // with the record, not after it
     if (rank >= a.nunion[bk]) return;
@@ -200,8 +203,18 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     __syncthreads();
 
     // this chunk of the page's middle-region tokens: contiguous rows of one
-    // physical page (an unmapped page attends nothing)
-    const int a0 = imax(p * g.P, rg.se), a1 = imin((p + 1) * g.P, rg.ws);
+    // physical page (an unmapped page attends nothing); or of the block's
+    // rows in the block layout
+    const bool blocks = a.blk_off != nullptr;
+    int a0, a1;
+    if (blocks) {
+        const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
+        a0 = bo[p];
+        a1 = bo[p + 1];
+    } else {
+        a0 = imax(p * g.P, rg.se);
+        a1 = imin((p + 1) * g.P, rg.ws);
+    }
     const int n = imax(0, a1 - a0);
     const int csz = (n + a.tsplit - 1) / a.tsplit;
     const int t0 = a0 + imin(n, chunk * csz);
@@ -209,10 +222,12 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const bool mapped = phys >= 0;
     const int t1 = mapped ? imin(a1, t0 + csz) : t0;
     const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
-    // K/V row of token t0 (inside the page even when the chunk is empty)
-    const long row0 = mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1) : 0;
-    const uint16_t* kp = (const uint16_t*)g.k + row0 * HD;
-    const uint16_t* vp = (const uint16_t*)g.v + row0 * HD;
+    // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
+    const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
+                      : mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1)
+                               : 0;
+    const uint16_t* kp = (const uint16_t*)(blocks ? a.blk_k : g.k) + row0 * HD;
+    const uint16_t* vp = (const uint16_t*)(blocks ? a.blk_v : g.v) + row0 * HD;
     const int ntok = t1 - t0;
 
     const float sl2 = a.scale_log2, slack = kGSlack / sl2;
@@ -238,7 +253,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             const int col = 16 * cb + r, ri = col / G, h = col - ri * G;
             const bool live = ri < nr;
             const int row = live ? rows_l[ri] : 0;
-            cpos = live ? rg.L - a.Q + row : -1;
+            // a block's tokens precede every row's window: no causal test
+            cpos = !live ? -1 : blocks ? 0x7fffffff : rg.L - a.Q + row;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 uint4 w = make_uint4(0, 0, 0, 0);
@@ -440,8 +456,8 @@ hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > 64 || g.max_pages > kGroupMaxPages) return hipErrorInvalidValue;
-    const size_t lds = (sizeof(unsigned long long) + sizeof(int)) * (size_t)g.max_pages;
+    if (g.dtype != 1 || a.Q > 64 || a.npg > kGroupMaxPages) return hipErrorInvalidValue;
+    const size_t lds = (sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_union < 1) return e;

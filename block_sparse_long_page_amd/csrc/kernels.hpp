@@ -107,8 +107,56 @@ struct GroupArgs {
     float* part_ml;
     // workspace: the plan
     int32_t* nunion;    // [B][Hkv] pages in the union
-    GroupPage* upages;  // [B][Hkv][max_pages] the union in launch order (most rows first)
-    int16_t* slots;     // [B][Hkv][max_pages][64] each row's list index of each union page (same order)
+    GroupPage* upages;  // [B][Hkv][npg] the union in launch order (most rows first)
+    int16_t* slots;     // [B][Hkv][npg][64] each row's list index of each union page (same order)
+    int npg;            // candidate units per (sequence, KV head): max_pages, or the index's blocks
+    // block mode (semantic index; blk_off == nullptr: pages of the paged
+    // cache): the units are the blocks of a contiguous per-(b, KV head)
+    // layout, whose tokens all precede every row's window
+    const int32_t* blk_off;  // [B][Hkv][npg + 1] first row of each block
+    const void* blk_k;       // [B][Hkv][blk_n][hd]
+    const void* blk_v;
+    int blk_n;               // rows per (sequence, KV head)
+};
+
+// Semantic block index: spherical k-means of the unit keys of positions
+// [0, N) of every (sequence, KV head) into C blocks, and the block layout.
+struct IndexArgs {
+    Geometry g;
+    int N, C, iters;
+    // the index (caller's buffers)
+    int32_t* offsets;    // [B][Hkv][C + 1]
+    int32_t* positions;  // [B][Hkv][N] position of each row of the block layout
+    float* centres;      // [B][Hkv][C][hd]
+    void* k_blocks;      // [B][Hkv][N][hd]
+    void* v_blocks;
+    int32_t* assign_out;  // optional copy of the final assignment [B][Hkv][N]
+    // workspace
+    float* inv_norm;     // [B][Hkv][N] 1 / |k_t| (0 for a zero key)
+    uint16_t* cent_bf;   // [B][Hkv][C][hd] the centres rounded to bf16 (the assignment's operand)
+    int32_t* assign;     // [B][Hkv][N]
+    int32_t* cnt;        // [B][Hkv][nchunks][C] per-chunk block counts, then bases
+    int32_t* seg_base;   // [B][Hkv][C + 1] first update segment of each block
+    int32_t* seg_block;  // [B][Hkv][nseg] block of each segment
+    float* seg_sum;      // [B][Hkv][nseg][hd] sum of a segment's unit keys
+    int nchunks, nseg;
+};
+
+constexpr int kIndexChunk = 1024;    // tokens per counting-sort chunk
+constexpr int kIndexSegment = 128;   // rows per centre-update segment
+constexpr int kIndexMaxBlocks = 4096;
+
+// Block choice of one (sequence, KV head, row) against an index.
+struct SelectBlocksArgs {
+    Geometry g;
+    const void* q;
+    int Q;
+    int C;
+    const int32_t* offsets;  // [B][Hkv][C + 1]
+    const float* centres;    // [B][Hkv][C][hd]
+    int budget, k_max;
+    int32_t* sel;            // [B][Hkv][Q][k_max] ascending, -1 after the count
+    int32_t* count;          // [B][Hkv][Q]
 };
 
 struct CombineArgs {
@@ -130,5 +178,8 @@ int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // plan kernel, then the grouped decode over max_union pages per (sequence, KV head)
 hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
+// the whole index build (every kernel of every iteration)
+hipError_t launch_index_build(const IndexArgs& a, hipStream_t s);
+hipError_t launch_select_blocks(const SelectBlocksArgs& a, hipStream_t s);
 
 }  // namespace sa

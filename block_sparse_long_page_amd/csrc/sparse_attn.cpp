@@ -99,10 +99,11 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
 struct GroupedWs {
     size_t nunion, upages, slots, total;
 };
-GroupedWs grouped_ws(const sa_kv_desc* kv)
+// npg: candidate units per (sequence, KV head) (pages, or an index's blocks)
+GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t bh = (size_t)kv->batch * kv->num_kv_heads, mp = (size_t)kv->max_pages_per_seq;
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads, mp = (size_t)npg;
     GroupedWs w;
     w.nunion = 0;
     w.upages = up(w.nunion + bh * sizeof(int32_t));
@@ -281,7 +282,181 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
 size_t sparse_attn_grouped_workspace_bytes(const sa_kv_desc* kv)
 {
     if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1) return 0;
-    return grouped_ws(kv).total;
+    return grouped_ws(kv, kv->max_pages_per_seq).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The union plan and grouped decode of the rows' lists of units (pages of
+// the paged cache, or blocks of an index with blk_off != nullptr), then the
+// per-row decode of the sink and window into the slots after the units'.
+int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int32_t num_q_rows,
+                 const int32_t* sel, const int32_t* cnt, int32_t k_max, int32_t sink_len, int32_t window_len,
+                 float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o, float* part_ml,
+                 void* workspace, size_t workspace_bytes, int npg, const int32_t* blk_off, const void* blk_k,
+                 const void* blk_v, int blk_n, hipStream_t stream)
+{
+    if (!q || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 || k_max < 0)
+        return SA_ERR_INVALID_ARG;
+    if (k_max > 0 && (!sel || !cnt)) return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (token_splits < 1 || token_splits > kMaxTokenSplits || local_splits < 1) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    const long stride = (long)k_max * token_splits + local_splits;
+    if (stride > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_BF16 || num_q_rows > sa::kGroupMaxRows || npg > sa::kGroupMaxPages)
+        return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    const GroupedWs w = grouped_ws(kv, npg);
+    if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
+        return SA_ERR_INVALID_ARG;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    const float sl2 = scale * 1.4426950408889634f;
+    if (k_max > 0) {
+        char* base = (char*)workspace;
+        const long max_union = std::min<long>(npg, (long)num_q_rows * k_max);
+        sa::GroupArgs a{g,          q,          num_q_rows, sel,     cnt,
+                        k_max,      sink_len,   window_len, sl2,     token_splits,
+                        (int)stride, part_o,    part_ml,    (int32_t*)(base + w.nunion),
+                        (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots),
+                        npg,        blk_off,    blk_k,      blk_v,   blk_n};
+        const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
+        if (r1 != SA_OK) return r1;
+    }
+    const long off = (long)k_max * token_splits;
+    sa::DecodeArgs d{g,        q,          num_q_rows, nullptr,       nullptr, 0,
+                     sink_len, window_len, SA_PART_LOCAL, sl2,        local_splits,
+                     (int)stride, part_o + off * kv->head_dim, part_ml + off * 2};
+    return finish(sa::launch_decode(d, stream), stream);
+}
+
+// the index's arrays, and its sizes against the cache
+int check_index(const sa_kv_desc* kv, const sa_block_index* idx)
+{
+    if (!idx || !idx->offsets || !idx->positions || !idx->centres || !idx->k_blocks || !idx->v_blocks)
+        return SA_ERR_INVALID_ARG;
+    if (idx->num_tokens < 1 || idx->num_tokens > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (idx->num_blocks < 1 || idx->num_blocks > idx->num_tokens) return SA_ERR_INVALID_ARG;
+    if (idx->num_blocks > sa::kIndexMaxBlocks) return SA_ERR_UNSUPPORTED;
+    if ((long)kv->batch * kv->num_kv_heads * idx->num_tokens >= (1l << 31)) return SA_ERR_UNSUPPORTED;
+    // 16-byte rows are read and written whole
+    if (((uintptr_t)idx->k_blocks & 15) || ((uintptr_t)idx->v_blocks & 15) || ((uintptr_t)idx->centres & 15))
+        return SA_ERR_INVALID_ARG;
+    return SA_OK;
+}
+
+struct IndexWs {
+    size_t inv_norm, cent_bf, assign, cnt, seg_base, seg_block, seg_sum, total;
+    int nchunks, nseg;
+};
+IndexWs index_ws(const sa_kv_desc* kv, long N, long C)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
+    IndexWs w;
+    w.nchunks = (int)((N + sa::kIndexChunk - 1) / sa::kIndexChunk);
+    w.nseg = (int)((N + sa::kIndexSegment - 1) / sa::kIndexSegment + C);
+    w.inv_norm = 0;
+    w.cent_bf = up(w.inv_norm + bh * N * sizeof(float));
+    w.assign = up(w.cent_bf + bh * C * kv->head_dim * sizeof(uint16_t));
+    w.cnt = up(w.assign + bh * N * sizeof(int32_t));
+    w.seg_base = up(w.cnt + bh * w.nchunks * C * sizeof(int32_t));
+    w.seg_block = up(w.seg_base + bh * (C + 1) * sizeof(int32_t));
+    w.seg_sum = up(w.seg_block + bh * w.nseg * sizeof(int32_t));
+    w.total = up(w.seg_sum + bh * w.nseg * kv->head_dim * sizeof(float));
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_index_workspace_bytes(const sa_kv_desc* kv, int32_t num_tokens, int32_t num_blocks)
+{
+    if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || (kv->head_dim != 64 && kv->head_dim != 128) ||
+        num_tokens < 1 || num_blocks < 1)
+        return 0;
+    return index_ws(kv, num_tokens, num_blocks).total;
+}
+
+int sparse_attn_build_block_index(const sa_kv_desc* kv, int32_t iterations, const sa_block_index* index,
+                                  int32_t* assignment, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    const int ri = check_index(kv, index);
+    if (ri != SA_OK) return ri;
+    if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (iterations < 0 || iterations > 64) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    const IndexWs w = index_ws(kv, index->num_tokens, index->num_blocks);
+    if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0) return SA_ERR_INVALID_ARG;
+    char* base = (char*)workspace;
+    sa::IndexArgs a{g,
+                    index->num_tokens,
+                    index->num_blocks,
+                    iterations,
+                    index->offsets,
+                    index->positions,
+                    index->centres,
+                    index->k_blocks,
+                    index->v_blocks,
+                    assignment,
+                    (float*)(base + w.inv_norm),
+                    (uint16_t*)(base + w.cent_bf),
+                    (int32_t*)(base + w.assign),
+                    (int32_t*)(base + w.cnt),
+                    (int32_t*)(base + w.seg_base),
+                    (int32_t*)(base + w.seg_block),
+                    (float*)(base + w.seg_sum),
+                    w.nchunks,
+                    w.nseg};
+    return finish(sa::launch_index_build(a, stream), stream);
+}
+
+int sparse_attn_select_blocks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              int32_t token_budget, int32_t k_max, int32_t* sel_blocks, int32_t* sel_count,
+                              hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    const int ri = check_index(kv, index);
+    if (ri != SA_OK) return ri;
+    if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (!q || !sel_blocks || !sel_count || num_q_rows < 1 || token_budget < 0) return SA_ERR_INVALID_ARG;
+    if (k_max < 1 || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    sa::SelectBlocksArgs a{g,          q,     num_q_rows, index->num_blocks, index->offsets, index->centres,
+                           token_budget, k_max, sel_blocks, sel_count};
+    return finish(sa::launch_select_blocks(a, stream), stream);
+}
+
+size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index)
+{
+    if (!kv || !index || kv->batch < 1 || kv->num_kv_heads < 1 || index->num_blocks < 1) return 0;
+    return grouped_ws(kv, index->num_blocks).total;
+}
+
+int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              const int32_t* sel_blocks, const int32_t* sel_count, int32_t k_max, int32_t window_len,
+                              float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
+                              float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    const int ri = check_index(kv, index);
+    if (ri != SA_OK) return ri;
+    // the rows' window holds the current fragment, and the blocks' tokens precede it
+    if (window_len < num_q_rows || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
+    return grouped_impl(kv, g, q, num_q_rows, sel_blocks, sel_count, k_max, 0, window_len, softmax_scale,
+                        token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes, index->num_blocks,
+                        index->offsets, index->k_blocks, index->v_blocks, index->num_tokens, stream);
 }
 
 int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
@@ -292,38 +467,9 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
     if (rc != SA_OK) return rc;
-    if (!q || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 || k_max < 0)
-        return SA_ERR_INVALID_ARG;
-    if (k_max > 0 && (!sel_pages || !sel_count)) return SA_ERR_INVALID_ARG;
-    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
-    if (token_splits < 1 || token_splits > kMaxTokenSplits || local_splits < 1) return SA_ERR_INVALID_ARG;
-    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
-    const long stride = (long)k_max * token_splits + local_splits;
-    if (stride > kMaxSplits) return SA_ERR_INVALID_ARG;
-    if (kv->dtype != SA_BF16 || num_q_rows > sa::kGroupMaxRows || kv->max_pages_per_seq > sa::kGroupMaxPages)
-        return SA_ERR_UNSUPPORTED;
-    if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
-    const GroupedWs w = grouped_ws(kv);
-    if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
-        return SA_ERR_INVALID_ARG;
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
-    const float sl2 = scale * 1.4426950408889634f;
-    if (k_max > 0) {
-        char* base = (char*)workspace;
-        const long max_union = std::min<long>(kv->max_pages_per_seq, (long)num_q_rows * k_max);
-        sa::GroupArgs a{g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, sl2, token_splits,
-                        (int)stride, part_o, part_ml, (int32_t*)(base + w.nunion),
-                        (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots)};
-        const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
-        if (r1 != SA_OK) return r1;
-    }
-    // the sink and window tokens: the per-row decode into the slots after the pages'
-    const long off = (long)k_max * token_splits;
-    sa::DecodeArgs d{g,        q,          num_q_rows, nullptr,       nullptr, 0,
-                     sink_len, window_len, SA_PART_LOCAL, sl2,        local_splits,
-                     (int)stride, part_o + off * kv->head_dim, part_ml + off * 2};
-    return finish(sa::launch_decode(d, stream), stream);
+    return grouped_impl(kv, g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, softmax_scale,
+                        token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes,
+                        kv->max_pages_per_seq, nullptr, nullptr, nullptr, 0, stream);
 }
 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,

@@ -231,3 +231,78 @@ class GroupedStep:
         self.combine(stream=stream)
         return self.dec.out
 
+
+
+class BlockIndex:
+    """A semantic block index of a DeviceCache (sparse_attn_build_block_index)
+    and the decode against it: block choice under a token budget
+    (sparse_attn_select_blocks), the grouped decode of the chosen blocks plus
+    the window of recent tokens (sparse_attn_decode_blocks) and the combine.
+
+    The index covers positions [0, num_tokens); num_blocks defaults to one
+    block per 2048 tokens (the semantic-blocks page's average block)."""
+
+    def __init__(self, cache: DeviceCache, num_tokens: int, num_blocks: Optional[int] = None, Q: int = 1,
+                 window: int = 64, budget: int = 0, k_max: Optional[int] = None,
+                 token_splits: int = 1, local_splits: int = 1, out_dtype: Optional[int] = None):
+        c = cache
+        self.c, self.N, self.Q, self.window, self.budget = c, num_tokens, Q, window, budget
+        self.C = num_blocks or max(1, -(-num_tokens // 2048))
+        self.k_max = k_max or self.C
+        self.ts, self.ls = token_splits, local_splits
+        dev = c.k.device
+        self.offsets = torch.zeros((c.B, c.Hkv, self.C + 1), dtype=torch.int32, device=dev)
+        self.positions = torch.zeros((c.B, c.Hkv, self.N), dtype=torch.int32, device=dev)
+        self.centres = torch.zeros((c.B, c.Hkv, self.C, c.hd), dtype=torch.float32, device=dev)
+        self.k_blocks = torch.zeros((c.B, c.Hkv, self.N, c.hd), dtype=c.k.dtype, device=dev)
+        self.v_blocks = torch.zeros_like(self.k_blocks)
+        self.assignment = torch.zeros((c.B, c.Hkv, self.N), dtype=torch.int32, device=dev)
+        self.desc = c.desc()
+        self.index = B.make_block_index(num_tokens=self.N, num_blocks=self.C, offsets=self.offsets,
+                                        positions=self.positions, centres=self.centres, k_blocks=self.k_blocks,
+                                        v_blocks=self.v_blocks)
+        self.build_ws_bytes = B.sparse_attn_index_workspace_bytes(self.desc, self.N, self.C)
+        self.build_ws = torch.empty(max(1, self.build_ws_bytes), dtype=torch.uint8, device=dev)
+        self.rows = c.B * c.Hq * Q
+        self.sel = torch.full((c.B, c.Hkv, Q, self.k_max), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((c.B, c.Hkv, Q), dtype=torch.int32, device=dev)
+        self.stride = self.k_max * self.ts + self.ls
+        self.ws_bytes = B.sparse_attn_blocks_workspace_bytes(self.desc, self.index)
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.part_o = torch.empty((self.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((self.rows, self.stride, 2), dtype=torch.float32, device=dev)
+        self.out_dtype = c.dtype if out_dtype is None else out_dtype
+        self.out = torch.empty((self.rows, c.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
+        self.lse = torch.empty((self.rows,), dtype=torch.float32, device=dev)
+
+    def build(self, iterations: int = 8, stream=None):
+        B.sparse_attn_build_block_index(self.desc, iterations, self.index, self.assignment, self.build_ws,
+                                        self.build_ws_bytes, stream)
+
+    def select(self, q: torch.Tensor, stream=None):
+        B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, self.budget, self.k_max, self.sel, self.count,
+                                    stream)
+
+    def decode(self, q: torch.Tensor, scale: float = 0.0, stream=None):
+        B.sparse_attn_decode_blocks(self.desc, self.index, q, self.Q, self.sel, self.count, self.k_max, self.window,
+                                    scale, self.ts, self.ls, self.part_o, self.part_ml, self.ws, self.ws_bytes,
+                                    stream)
+
+    def combine(self, stream=None):
+        B.sparse_attn_combine(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out, self.out_dtype,
+                              self.lse, stream)
+
+    def step(self, q: torch.Tensor, stream=None):
+        self.select(q, stream=stream)
+        self.decode(q, stream=stream)
+        self.combine(stream=stream)
+        return self.out
+
+    def out_f32(self) -> np.ndarray:
+        o = self.out.cpu().numpy()
+        if self.out_dtype == B.SA_BF16:
+            o = (o.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        return o.reshape(self.c.B, self.c.Hq, self.Q, self.c.hd)
+
+    def lse_f32(self) -> np.ndarray:
+        return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)

@@ -16,6 +16,15 @@
  *   sparse_attn_decode_grouped   multi-query decode that reads each selected
  *                                page once for all the rows that chose it
  *
+ * and, for the semantic block index (semantic-blocks page: spherical k-means
+ * of the normalised keys into blocks, keys and values laid out block by
+ * block, blocks chosen by centre score up to a token budget):
+ *
+ *   sparse_attn_build_block_index  k-means and the block layout
+ *   sparse_attn_select_blocks      per-row block choice under a token budget
+ *   sparse_attn_decode_blocks      grouped decode over the chosen blocks plus
+ *                                  the window of recent tokens
+ *
  * sparse_attn_decode_step runs select and decode of a selecting step with the
  * top-k inside the decode kernel (two launches instead of three).
  *
@@ -280,6 +289,98 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
 
 /* Workspace bytes of sparse_attn_decode_grouped for this cache (host only; 0 for a bad descriptor). */
 size_t sparse_attn_grouped_workspace_bytes(const sa_kv_desc* kv);
+
+/*
+ * Semantic block index of a cache (semantic-blocks page: per request, layer
+ * and KV head the normalised keys are grouped into semantic blocks by
+ * spherical k-means, and the keys and values are laid out again block by
+ * block).  It covers positions [0, num_tokens) of every sequence; every
+ * sequence must hold at least num_tokens tokens.  All buffers are the
+ * caller's device memory; k_blocks, v_blocks and centres 16-byte aligned.
+ */
+typedef struct sa_block_index {
+    int32_t num_tokens;  /* N: indexed positions per sequence, 1 <= N <= max_seq_len */
+    int32_t num_blocks;  /* C: 1 <= C <= min(N, 4096) */
+    int32_t* offsets;    /* [batch][num_kv_heads][C + 1] first row of each block (CSR) */
+    int32_t* positions;  /* [batch][num_kv_heads][N] position of each row of the block layout */
+    float* centres;      /* [batch][num_kv_heads][C][head_dim] unit-length block centres */
+    void* k_blocks;      /* [batch][num_kv_heads][N][head_dim] keys in block order, KV dtype */
+    void* v_blocks;      /* [batch][num_kv_heads][N][head_dim] values in block order */
+} sa_block_index;
+
+/* Workspace bytes of sparse_attn_build_block_index (host only; 0 for bad sizes). */
+size_t sparse_attn_index_workspace_bytes(const sa_kv_desc* kv, int32_t num_tokens, int32_t num_blocks);
+
+/*
+ * Builds `index` from the keys and values of kv, per (sequence, KV head):
+ * unit keys u_t = k_t / |k_t| (a zero key stays zero); centre c starts as
+ * the unit key at position floor(c N / C); `iterations` times each key goes
+ * to the centre with the largest dot product (ties: the lower centre; the
+ * products use the centres rounded to bf16 and the bf16 keys, summed in
+ * fp32 on the matrix cores) and each centre becomes the normalised sum of
+ * its unit keys in fp32 (a centre without keys keeps its value).  A last
+ * assignment to the final centres defines the blocks: block c holds the
+ * keys assigned to c, rows in position order, blocks in order.  offsets,
+ * positions, centres and the K/V copies are written; `assignment` (nullable,
+ * [batch][num_kv_heads][N] int32) receives that last assignment.  Every sum
+ * runs in a fixed order, so the result is bitwise reproducible.
+ *   iterations  0..64 (0: the starting centres)
+ *   workspace   >= sparse_attn_index_workspace_bytes(kv, N, C) bytes,
+ *               256-byte aligned
+ * bf16 caches only.  Errors: SA_ERR_INVALID_ARG for missing or misaligned
+ * buffers, sizes out of range or a small workspace; SA_ERR_UNSUPPORTED for
+ * other dtypes or C > 4096.
+ */
+int sparse_attn_build_block_index(const sa_kv_desc* kv, int32_t iterations, const sa_block_index* index,
+                                  int32_t* assignment, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block choice of every (sequence, KV head, row) (semantic-blocks page: the
+ * query is compared with the block centres and the best blocks are taken up
+ * to a budget of tokens): block c scores max over the group's heads of
+ * q_h . centre_c (fp32); blocks are taken in order of (score desc, block
+ * asc) while the running token count stays <= token_budget, at least one
+ * and at most k_max; blocks without tokens are never taken.
+ *   q           [batch][num_q_heads][num_q_rows][head_dim], bf16
+ *   sel_blocks  [batch][num_kv_heads][num_q_rows][k_max]: the chosen blocks
+ *               ascending, -1 after the last; sel_count [..][num_q_rows]
+ *   k_max       1..C
+ * Errors: as sparse_attn_build_block_index; SA_ERR_INVALID_ARG for k_max out
+ * of range or a negative budget.
+ */
+int sparse_attn_select_blocks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              int32_t token_budget, int32_t k_max, int32_t* sel_blocks, int32_t* sel_count,
+                              hipStream_t stream);
+
+/* Workspace bytes of sparse_attn_decode_blocks for this index (host only; 0 for bad sizes). */
+size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index);
+
+/*
+ * The attention of num_q_rows rows over their chosen blocks and the window:
+ * each block of the union of the rows' lists (per sequence and KV head) is
+ * read once from the block layout and attended by every row that listed it
+ * (the grouped decode of sparse_attn_decode_grouped, with blocks for pages),
+ * and the window [L - window_len, L) of the paged cache by the per-row
+ * decode (no sink).  The blocks' tokens are attended without a causal test:
+ * the caller keeps the index to positions before every row's window, i.e.
+ * num_tokens <= L - window_len for every sequence, and window_len >=
+ * num_q_rows so that the window holds the rows themselves.
+ *   sel_blocks, sel_count, k_max  as sparse_attn_select_blocks writes them
+ *   token_splits, local_splits, part_o, part_ml  as in
+ *               sparse_attn_decode_grouped (slot j * token_splits + c holds
+ *               chunk c of the row's j-th block); merge with
+ *               sparse_attn_combine(num_splits = k_max * token_splits +
+ *               local_splits)
+ *   workspace   >= sparse_attn_blocks_workspace_bytes(kv, index) bytes,
+ *               256-byte aligned; needed when k_max > 0
+ * bf16 caches, num_q_rows <= 64.  Results are bitwise reproducible.
+ * Errors: those of sparse_attn_decode_grouped and of the index checks;
+ * SA_ERR_INVALID_ARG when window_len < num_q_rows or k_max > C.
+ */
+int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              const int32_t* sel_blocks, const int32_t* sel_count, int32_t k_max, int32_t window_len,
+                              float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
+                              float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,

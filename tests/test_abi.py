@@ -23,7 +23,9 @@ def test_exports_every_header_function():
     assert set(names) == {
         "sparse_attn_build_page_meta", "sparse_attn_select", "sparse_attn_workspace_bytes", "sparse_attn_decode",
         "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string",
-        "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes"}
+        "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes", "sparse_attn_index_workspace_bytes",
+        "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
+        "sparse_attn_decode_blocks"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -181,7 +183,6 @@ def test_decode_grouped_checks():
     lib = B.library()
     d = _desc()
     ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
-    # four 256-byte aligned arrays: counts, pages, row masks, per-row slots
     # counts, page records (16 bytes), slots; each region 256-byte aligned
     assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 64 * 2 + 255) // 256) * 256
     assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
@@ -268,3 +269,83 @@ def test_fast_division_is_exact_below_2_31(d):
     q = ((hi + n) & np.uint64(0xFFFFFFFF)) >> np.uint64(s)
     assert ((hi + n) < np.uint64(1 << 32)).all()
     np.testing.assert_array_equal(q, n // np.uint64(d))
+
+
+def _index(**kw):
+    base = dict(num_tokens=100, num_blocks=4, offsets=DEV, positions=DEV, centres=DEV, k_blocks=DEV, v_blocks=DEV)
+    base.update(kw)
+    return B.make_block_index(**base)
+
+
+def test_block_index_checks():
+    lib = B.library()
+    d = _desc()
+    ix = _index()
+    ws = lib.sparse_attn_index_workspace_bytes(ctypes.byref(d), 100, 4)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nbk, N, C, hd = 4, 100, 4, 128
+    nseg = (N + 127) // 128 + C
+    # 1/|k|, bf16 centres, assignment, chunk counts, segment bases, segment blocks, segment sums
+    assert ws == (up(nbk * N * 4) + up(nbk * C * hd * 2) + up(nbk * N * 4) + up(nbk * 1 * C * 4)
+                  + up(nbk * (C + 1) * 4) + up(nbk * nseg * 4) + up(nbk * nseg * hd * 4))
+    assert lib.sparse_attn_index_workspace_bytes(None, 100, 4) == 0
+    assert lib.sparse_attn_index_workspace_bytes(ctypes.byref(d), 0, 4) == 0
+
+    def build(**kw):
+        a = dict(desc=d, it=4, ix=ix, assign=None, ws=DEV, wsb=ws)
+        a.update(kw)
+        ixp = ctypes.byref(a["ix"]) if a["ix"] is not None else None
+        return lib.sparse_attn_build_block_index(ctypes.byref(a["desc"]), a["it"], ixp, a["assign"], a["ws"],
+                                                 a["wsb"], None)
+
+    assert build(ix=None) == B.SA_ERR_INVALID_ARG
+    for f in ("offsets", "positions", "centres", "k_blocks", "v_blocks"):
+        assert build(ix=_index(**{f: None})) == B.SA_ERR_INVALID_ARG
+    assert build(ix=_index(k_blocks=DEV + 8)) == B.SA_ERR_INVALID_ARG  # rows are written 16 bytes at a time
+    assert build(ix=_index(num_tokens=0)) == B.SA_ERR_INVALID_ARG
+    assert build(ix=_index(num_tokens=129)) == B.SA_ERR_INVALID_ARG  # beyond max_seq_len
+    assert build(ix=_index(num_blocks=0)) == B.SA_ERR_INVALID_ARG
+    assert build(ix=_index(num_blocks=101)) == B.SA_ERR_INVALID_ARG  # more blocks than tokens
+    assert build(it=-1) == B.SA_ERR_INVALID_ARG
+    assert build(it=65) == B.SA_ERR_INVALID_ARG
+    assert build(ws=None) == B.SA_ERR_INVALID_ARG
+    assert build(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert build(ws=DEV + 16) == B.SA_ERR_INVALID_ARG
+    assert build(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    big = _desc(max_seq_len=8192, max_pages_per_seq=512, num_phys_pages=1024)
+    assert build(desc=big, ix=_index(num_tokens=8192, num_blocks=4097)) == B.SA_ERR_UNSUPPORTED
+    for bad, code in BAD_DESCS:
+        assert build(desc=_desc(**bad)) == code
+
+    def select(**kw):
+        a = dict(q=DEV, rows=2, budget=64, kmax=2, sel=DEV, cnt=DEV)
+        a.update(kw)
+        return lib.sparse_attn_select_blocks(ctypes.byref(d), ctypes.byref(ix), a["q"], a["rows"], a["budget"],
+                                             a["kmax"], a["sel"], a["cnt"], None)
+
+    assert select(q=None) == B.SA_ERR_INVALID_ARG
+    assert select(sel=None) == B.SA_ERR_INVALID_ARG
+    assert select(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert select(rows=0) == B.SA_ERR_INVALID_ARG
+    assert select(budget=-1) == B.SA_ERR_INVALID_ARG
+    assert select(kmax=0) == B.SA_ERR_INVALID_ARG
+    assert select(kmax=5) == B.SA_ERR_INVALID_ARG  # more than the index's blocks
+
+    wsd = lib.sparse_attn_blocks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
+    assert wsd == 256 + up(nbk * C * 16) + up(nbk * C * 64 * 2)
+
+    def decode(**kw):
+        a = dict(q=DEV, rows=2, sel=DEV, cnt=DEV, kmax=2, W=4, scale=0.0, ts=1, ls=1, po=DEV, pml=DEV, ws=DEV, wsb=wsd)
+        a.update(kw)
+        return lib.sparse_attn_decode_blocks(ctypes.byref(d), ctypes.byref(ix), a["q"], a["rows"], a["sel"],
+                                             a["cnt"], a["kmax"], a["W"], a["scale"], a["ts"], a["ls"], a["po"],
+                                             a["pml"], a["ws"], a["wsb"], None)
+
+    assert decode(W=1) == B.SA_ERR_INVALID_ARG  # the window must hold the rows
+    assert decode(kmax=5) == B.SA_ERR_INVALID_ARG
+    assert decode(sel=None) == B.SA_ERR_INVALID_ARG
+    assert decode(ws=None) == B.SA_ERR_INVALID_ARG
+    assert decode(wsb=wsd - 1) == B.SA_ERR_INVALID_ARG
+    assert decode(ts=0) == B.SA_ERR_INVALID_ARG
+    assert decode(po=None) == B.SA_ERR_INVALID_ARG
+    assert decode(rows=65, W=65) == B.SA_ERR_UNSUPPORTED
