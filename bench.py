@@ -61,9 +61,13 @@ def parse():
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the warmup and the timed region (for profiler runs)")
     ap.add_argument("--token-splits", type=int, default=0, help="semantic-512k: token chunks per page (0: default)")
+    ap.add_argument("--iterations", type=int, default=8, help="semantic-512k-index: k-means iterations")
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
-                    choices=["llama3-70b-layer-128k", "semantic-512k", "hybrid-3layer-256k"],
+                    choices=["llama3-70b-layer-128k", "semantic-512k", "semantic-512k-index", "hybrid-3layer-256k"],
                     help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
+                         "semantic-512k-index: the same chunk over a semantic block index built from keys "
+                         "interleaved in position order (index build, then block choice, grouped decode of the "
+                         "blocks, combine); "
                          "hybrid-3layer-256k: the 128-step schedule of three layers (one token appended every step, "
                          "selection every 32 steps after summarising the pages appended since the last one, "
                          "growing window between)")
@@ -240,6 +244,96 @@ def bench_semantic(args):
     }))
 
 
+def bench_semantic_index(args):
+    """The semantic-block chunk at 512K with keys interleaved in position
+    order: the block index is built (spherical k-means, block layout of K and
+    V), then each step chooses the rows' blocks under the L/16 token budget,
+    decodes the union of the chosen blocks once per (sequence, KV head) plus
+    the 64-token window, and combines."""
+    import numpy as np
+    import torch
+
+    from block_sparse_long_page_amd import configs, synth
+    from block_sparse_long_page_amd.device import BlockIndex, DeviceCache, to_device
+
+    wl = configs.SEMANTIC_512K
+    t0 = time.time()
+    pr = synth.semantic_problem(wl, scatter=True)
+    c = pr.cache
+    log(f"inputs {time.time() - t0:.1f}s")
+    L = int(c.seq_lens[0])
+    N = L - pr.window
+    C = N // 2048
+    dc = DeviceCache.from_host(c)
+    q = to_device(pr.q)
+    ix = BlockIndex(dc, N, C, Q=pr.Q, window=pr.window, budget=pr.budget, k_max=64)
+    nbk, hd, it = c.B * c.Hkv, c.hd, args.iterations
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    ix.build(it)
+    torch.cuda.synchronize()
+    nb = 3
+    start.record()
+    for _ in range(nb):
+        ix.build(it)
+    stop.record()
+    torch.cuda.synchronize()
+    build_ms = start.elapsed_time(stop) / nb
+    # bytes the build must move: keys once for the lengths, twice per
+    # iteration (assignment, centre update), once for the final assignment,
+    # keys and values read and written by the layout copy
+    row = hd * 2
+    build_bytes = nbk * N * row * (1 + 2 * it + 1 + 4)
+    build_flops = 2 * nbk * N * C * hd * (it + 1)
+
+    for _ in range(args.warmup):
+        ix.step(q)
+    torch.cuda.synchronize()
+    K = args.steps
+    start.record()
+    for _ in range(K):
+        ix.step(q)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+
+    sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
+    off = ix.offsets.cpu().numpy()
+    sizes = np.diff(off, axis=-1)
+    union_tok = union_blocks = listed = 0
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            u = set()
+            for i in range(pr.Q):
+                u.update(int(x) for x in sel[b, h, i, :cnt[b, h, i]])
+            listed += int(cnt[b, h].sum())
+            union_blocks += len(u)
+            union_tok += int(sum(sizes[b, h, x] for x in u))
+    Q = pr.Q
+    local_tok = nbk * pr.window
+    partial_bytes = c.B * c.Hq * Q * ix.stride * (hd + 2) * 4
+    step_bytes = (union_tok * row * 2 + local_tok * row * 2 + nbk * C * (hd * 4 + 4) + c.B * c.Hq * Q * hd * 2 * 2
+                  + 2 * partial_bytes)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 512K ctx semantic block index, 64-row chunk",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2), "pct_hbm_peak": round(100 * gbs / 8000, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded): 256 vMF clusters of 2048 keys per (b, kvh) interleaved in position order, "
+                "V N(0,1), rows around 4 topics",
+        "config": {"workload": "semantic-512k-index", "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv,
+                   "head_dim": hd, "context": L, "indexed_tokens": N, "blocks": C, "iterations": it, "rows": Q,
+                   "budget": pr.budget, "window": pr.window, "k_max": ix.k_max,
+                   "step": "block choice + grouped decode of the blocks + combine"},
+        "build_ms": round(build_ms, 3), "build_GBps": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
+        "build_tflops": round(build_flops / (build_ms * 1e-3) / 1e12, 1),
+        "block_tokens": {"min": int(sizes.min()), "mean": float(sizes.mean()), "max": int(sizes.max()),
+                         "empty": int((sizes == 0).sum())},
+        "union_blocks": union_blocks, "listed_blocks": listed, "bytes_per_step": step_bytes,
+    }))
+
+
 def bench_hybrid(args):
     """The hybrid model's three full-attention layers at 256k over 128 decode
     steps: every step appends a token to every sequence; steps 0, 32, 64, 96
@@ -363,6 +457,9 @@ def main():
         return
     if args.workload == "hybrid-3layer-256k":
         bench_hybrid(args)
+        return
+    if args.workload == "semantic-512k-index":
+        bench_semantic_index(args)
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth

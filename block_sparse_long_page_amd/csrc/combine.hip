@@ -1,7 +1,8 @@
 // Log-sum-exp merge of split partials (attention-mechanisms article,
 // DeepSeek-V4 section: partial results are combined; FlashAttention's
 // running-max rescaling).  One wave per output row; the sums run over the
-// splits in a fixed order, so the result does not depend on timing.
+// splits in a fixed order, so the result does not depend on timing.  A
+// partial with l = 0 is empty and its o is not read into the sum.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -56,8 +57,9 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
         for (int j = 0; j < UNROLL; ++j) {
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (s0 & 63) + j));
             tot += wj;
+            if (wj > 0.f)  // an empty partial (l = 0) contributes nothing, whatever its o holds
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wj, v[j][c], acc[c]);
+                for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wj, v[j][c], acc[c]);
         }
         if (s0 + UNROLL < n) fetch(s0 + UNROLL);
     }

@@ -7,15 +7,15 @@
 //
 // k_group_plan: one workgroup per (sequence, KV head).  Builds the row masks
 // in LDS with 64-bit atomic ORs, writes the pages that carry a mask as
-// records (page, physical page, mask) in launch order (most rows first),
+// records (page, physical page, mask) in launch order (costliest first),
 // records for every row its index in its own list of each
-// page of the union (the row's slot for that page), and writes the empty
-// partial (m = -inf, l = 0, o = 0) of every slot a row does not use
-// (entries past its count).
+// page of the union (the row's slot for that page), and marks every slot a
+// row does not use (entries past its count) as an empty partial (m = -inf,
+// l = 0; the combine leaves its o out).
 //
 // k_group_decode_mfma: one workgroup per (sequence, KV head, page of the
-// union, token chunk of the page), launched with the pages chosen by the
-// most rows first.  The chunk's middle-region tokens are
+// union, token chunk of the page), launched with the costliest pages (tokens
+// times rows) first.  The chunk's middle-region tokens are
 // contiguous rows of one physical page; 64-token stages of K and V go
 // through LDS (three stages in flight in registers, two in LDS) and are read
 // by every wave.  Query columns are (row, head) pairs of the rows in the
@@ -71,7 +71,7 @@ struct Regions {
 __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
 {
     extern __shared__ unsigned long long mask[];  // [npg], then each unit's launch rank
-    __shared__ int by_rows[65];
+    __shared__ int by_cost[256];
     const Geometry& g = a.g;
     const int npg = a.npg;
     int* rank = (int*)(mask + npg);
@@ -92,35 +92,50 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
             const int p = sel[idx];
             if (p >= lo && p <= hi) atomicOr(&mask[p], 1ull << r);
         } else {
-            // a slot this row does not use: the empty partial, for every head and chunk
+            // a slot this row does not use: an empty partial (m = -inf, l = 0)
+            // for every head and chunk; the combine does not read its o
             for (int h = 0; h < g.G; ++h) {
                 const long prow = ((long)b * g.Hq + kvh * g.G + h) * a.Q + r;
                 for (int s = 0; s < a.tsplit; ++s) {
                     const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
                     a.part_ml[slot * 2 + 0] = -INFINITY;
                     a.part_ml[slot * 2 + 1] = 0.f;
-                    for (int d = 0; d < g.hd; ++d) a.part_o[slot * g.hd + d] = 0.f;
                 }
             }
         }
     }
     __syncthreads();
 
-    // The union in launch order: pages chosen by more rows first (a counting
-    // sort by the mask's row count), so the longest workgroups start first
-    // and the last to start are short.  The order within a row count follows
-    // the atomics; it affects timing only.  Each page's record carries what
-    // its workgroup needs first (page, physical page, row mask).
-    for (int c = tid; c <= 64; c += kPlanThreads) by_rows[c] = 0;
+    // The union in launch order: the costliest units first, so the longest
+    // workgroups start first and the last to start are short.  A unit's cost
+    // is its tokens times (8 + the rows that chose it) (more rows, more
+    // matrix-core work per token); a counting sort over quarter-octave
+    // buckets of the cost.  The order within a bucket follows the atomics;
+    // it affects timing only.  Each unit's record carries what its
+    // workgroup needs first (page or block, physical page, row mask).
+    auto cost_bucket = [&](int p) {
+        int ntok;
+        if (a.blk_off) {
+            const int32_t* bo = a.blk_off + (long)bk * (npg + 1);
+            ntok = bo[p + 1] - bo[p];
+        } else {
+            ntok = imin((p + 1) * g.P, rg.ws) - imax(p * g.P, rg.se);
+        }
+        const uint64_t cost = (uint64_t)imax(1, ntok) * (uint64_t)(8 + __builtin_popcountll(mask[p]));
+        const int lb = 63 - __builtin_clzll(cost);
+        const int frac = lb >= 2 ? (int)((cost >> (lb - 2)) & 3u) : 0;
+        return 255 - (4 * lb + frac);  // 0: the costliest
+    };
+    for (int c = tid; c < 256; c += kPlanThreads) by_cost[c] = 0;
     __syncthreads();
     for (int p = tid; p < npg; p += kPlanThreads)
-        if (mask[p] != 0ull) atomicAdd(&by_rows[__builtin_popcountll(mask[p])], 1);
+        if (mask[p] != 0ull) atomicAdd(&by_cost[cost_bucket(p)], 1);
     __syncthreads();
     if (tid == 0) {
         int acc = 0;
-        for (int c = 64; c >= 1; --c) {
-            const int nc = by_rows[c];
-            by_rows[c] = acc;
+        for (int c = 0; c < 256; ++c) {
+            const int nc = by_cost[c];
+            by_cost[c] = acc;
             acc += nc;
         }
         a.nunion[bk] = acc;
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     for (int p = tid; p < npg; p += kPlanThreads) {
         const unsigned long long m = mask[p];
         if (m != 0ull) {
-            const int at = atomicAdd(&by_rows[__builtin_popcountll(m)], 1);
+            const int at = atomicAdd(&by_cost[cost_bucket(p)], 1);
             const int ph = a.blk_off ? 0 : btr[p];  // blocks: rows of the block layout
             GroupPage e;
             e.page = p;

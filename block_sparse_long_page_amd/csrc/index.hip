@@ -26,7 +26,8 @@
 // Every sum runs in a fixed order, so the build is bitwise reproducible.
 //
 // k_select_blocks: one workgroup per (sequence, KV head, row): the largest
-// q_h . centre_c over the group's heads for every block, a bitonic sort by
+// q_h . centre_c over the group's heads for every block (a thread per block,
+// channels in order), a bitonic sort by
 // (score desc, block asc), the running token count in that order, and the
 // blocks taken while it stays within the budget (at least one), emitted
 // ascending.
@@ -126,14 +127,14 @@ __global__ __launch_bounds__(256) void k_idx_init(IndexArgs a)
 }
 
 // 256 keys per workgroup (4 waves x 4 tiles of 16); the centres go through
-// LDS 256 at a time.  Lane (r, j) of a product holds key r of the tile and
+// LDS 128 at a time.  Lane (r, j) of a product holds key r of the tile and
 // centres 4j .. 4j+3 of the 16-centre block.
 template <int HD>
 __global__ __launch_bounds__(256) void k_idx_assign(IndexArgs a)
 {
     constexpr int KK = HD / 32;  // products per 16 x 16 block (32 channels each)
     constexpr int TT = 4;        // key tiles per wave
-    constexpr int CH = 256;      // centres per LDS round
+    constexpr int CH = 128;      // centres per LDS round (32 KiB at hd 128: four workgroups per CU)
     __shared__ __attribute__((aligned(16))) uint16_t cl[CH * HD];
     const Geometry& g = a.g;
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
@@ -222,28 +223,36 @@ __global__ __launch_bounds__(256) void k_idx_hist(IndexArgs a)
         if (t < a.N) atomicAdd(&h[as[t]], 1);
     }
     __syncthreads();
-    int32_t* cnt = a.cnt + ((long)bk * a.nchunks + chunk) * a.C;
-    for (int c = threadIdx.x; c < a.C; c += 256) cnt[c] = h[c];
+    int32_t* cnt = a.cnt + (long)bk * a.C * a.nchunks + chunk;  // [C][nchunks]
+    for (int c = threadIdx.x; c < a.C; c += 256) cnt[(long)c * a.nchunks] = h[c];
 }
 
-// One workgroup per (sequence, KV head); thread i owns blocks 4i .. 4i+3.
+// One workgroup per (sequence, KV head).  The counts are block-major
+// ([C][nchunks]): a wave reduces a block's chunk counts, the workgroup scans
+// the block totals (thread i owns blocks 4i .. 4i+3), then a wave turns a
+// block's chunk counts into each chunk's first row in the block.
 __global__ __launch_bounds__(1024) void k_idx_scan(IndexArgs a)
 {
     constexpr int PER = kIndexMaxBlocks / 1024;
     __shared__ int wsum[16];
-    const int bk = blockIdx.x;
-    int32_t* cnt = a.cnt + (long)bk * a.nchunks * a.C;
+    __shared__ int tot_l[kIndexMaxBlocks], off_l[kIndexMaxBlocks];
+    const int bk = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t* cnt = a.cnt + (long)bk * a.C * a.nchunks;
+    for (int c = wave; c < a.C; c += 16) {
+        int s = 0;
+        for (int k = lane; k < a.nchunks; k += 64) s += cnt[(long)c * a.nchunks + k];
+        s = __builtin_amdgcn_readlane(wave_inclusive_scan(s), 63);
+        if (lane == 0) tot_l[c] = s;
+    }
+    __syncthreads();
     int tot[PER], nseg[PER];
     int mine = 0, segs = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int c = PER * (int)threadIdx.x + u;
-        int s = 0;
-        if (c < a.C)
-            for (int k = 0; k < a.nchunks; ++k) s += cnt[(long)k * a.C + c];
-        tot[u] = s;
-        nseg[u] = (s + kIndexSegment - 1) / kIndexSegment;
-        mine += s;
+        tot[u] = c < a.C ? tot_l[c] : 0;
+        nseg[u] = (tot[u] + kIndexSegment - 1) / kIndexSegment;
+        mine += tot[u];
         segs += nseg[u];
     }
     int total, seg_total;
@@ -257,15 +266,9 @@ __global__ __launch_bounds__(1024) void k_idx_scan(IndexArgs a)
         const int c = PER * (int)threadIdx.x + u;
         if (c < a.C) {
             offsets[c] = off;
+            off_l[c] = off;
             sb[c] = soff;
             for (int m = 0; m < nseg[u]; ++m) sblk[soff + m] = c;
-            // each chunk's first row in block c
-            int run = off;
-            for (int k = 0; k < a.nchunks; ++k) {
-                const int n = cnt[(long)k * a.C + c];
-                cnt[(long)k * a.C + c] = run;
-                run += n;
-            }
         }
         off += tot[u];
         soff += nseg[u];
@@ -273,6 +276,18 @@ __global__ __launch_bounds__(1024) void k_idx_scan(IndexArgs a)
     if (threadIdx.x == 0) {
         offsets[a.C] = total;
         sb[a.C] = seg_total;
+    }
+    __syncthreads();
+    // each chunk's first row in block c: off[c] + the counts of the earlier chunks
+    for (int c = wave; c < a.C; c += 16) {
+        int carry = off_l[c];
+        for (int k0 = 0; k0 < a.nchunks; k0 += 64) {
+            const int k = k0 + lane;
+            const int n = k < a.nchunks ? cnt[(long)c * a.nchunks + k] : 0;
+            const int inc = wave_inclusive_scan(n);
+            if (k < a.nchunks) cnt[(long)c * a.nchunks + k] = carry + inc - n;
+            carry += __builtin_amdgcn_readlane(inc, 63);
+        }
     }
 }
 
@@ -283,8 +298,8 @@ __global__ __launch_bounds__(64) void k_idx_scatter(IndexArgs a)
 {
     extern __shared__ int cur[];  // [C] next free row of each block for this chunk
     const int bk = blockIdx.y, chunk = blockIdx.x, lane = threadIdx.x;
-    const int32_t* base = a.cnt + ((long)bk * a.nchunks + chunk) * a.C;
-    for (int c = lane; c < a.C; c += 64) cur[c] = base[c];
+    const int32_t* base = a.cnt + (long)bk * a.C * a.nchunks + chunk;
+    for (int c = lane; c < a.C; c += 64) cur[c] = base[(long)c * a.nchunks];
     __builtin_amdgcn_wave_barrier();
     const int32_t* as = a.assign + (long)bk * a.N;
     int32_t* pos = a.positions + (long)bk * a.N;
@@ -308,12 +323,15 @@ __global__ __launch_bounds__(64) void k_idx_scatter(IndexArgs a)
 }
 
 // One wave per segment: the sum of the unit keys of its rows, rows in order.
+// The segment's positions, key rows and 1/|k| are loaded first (two rows per
+// lane) and broadcast row by row, so U key rows are in flight at a time.
 // Lane l holds channels 2l, 2l+1 (hd 128) or channel l (hd 64).
 template <int HD>
 __global__ __launch_bounds__(256) void k_idx_seg(IndexArgs a)
 {
     constexpr int CPL = HD / 64;  // channels per lane
-    constexpr int U = 8;          // rows in flight
+    constexpr int U = 16;         // rows in flight
+    static_assert(kIndexSegment == 128 && kIndexSegment % U == 0, "two rows per lane");
     const Geometry& g = a.g;
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
     const int bk = blockIdx.y, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
@@ -324,27 +342,41 @@ __global__ __launch_bounds__(256) void k_idx_seg(IndexArgs a)
     const int c = a.seg_block[(long)bk * a.nseg + s];
     const int32_t* offsets = a.offsets + (long)bk * (a.C + 1);
     const int r0 = offsets[c] + (s - sb[c]) * kIndexSegment;
-    const int r1 = imin(offsets[c + 1], r0 + kIndexSegment);
+    const int nrows = imin(offsets[c + 1] - r0, kIndexSegment);
     const int32_t* pos = a.positions + (long)bk * a.N;
     const float* inv = a.inv_norm + (long)bk * a.N;
+    // row r of the segment: lane r (r < 64) or lane r - 64 of the second pair
+    int rowA = 0, rowB = 0;
+    float wA = 0.f, wB = 0.f;
+    if (lane < nrows) {
+        const int t = pos[r0 + lane];
+        const long row = key_row(g, pdiv, b, kvh, t);
+        rowA = row >= 0 ? (int)row : 0;  // rows fit 31 bits (checked on the host)
+        wA = row >= 0 ? inv[t] : 0.f;
+    }
+    if (64 + lane < nrows) {
+        const int t = pos[r0 + 64 + lane];
+        const long row = key_row(g, pdiv, b, kvh, t);
+        rowB = row >= 0 ? (int)row : 0;
+        wB = row >= 0 ? inv[t] : 0.f;
+    }
     float acc[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
-    for (int i0 = r0; i0 < r1; i0 += U) {
+    for (int q0 = 0; q0 < nrows; q0 += U) {  // rows past nrows weigh 0
         float x[U][CPL], w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + u;
-            const int t = i < r1 ? pos[i] : pos[r0];
-            const long row = key_row(g, pdiv, b, kvh, t);
-            w[u] = i < r1 && row >= 0 ? inv[t] : 0.f;
-            const long rr = row >= 0 ? row : 0;
+            const int r = q0 + u;
+            const int rr = r < 64 ? __builtin_amdgcn_readlane(rowA, r) : __builtin_amdgcn_readlane(rowB, r - 64);
+            w[u] = __int_as_float(r < 64 ? __builtin_amdgcn_readlane(__float_as_int(wA), r)
+                                         : __builtin_amdgcn_readlane(__float_as_int(wB), r - 64));
             if constexpr (CPL == 2) {
-                const uint32_t v = *((const uint32_t*)((const uint16_t*)g.k + rr * HD) + lane);
+                const uint32_t v = *((const uint32_t*)((const uint16_t*)g.k + (long)rr * HD) + lane);
                 x[u][0] = bf_lo(v);
                 x[u][1] = bf_hi(v);
             } else {
-                x[u][0] = __uint_as_float((uint32_t)((const uint16_t*)g.k)[rr * HD + lane] << 16);
+                x[u][0] = __uint_as_float((uint32_t)((const uint16_t*)g.k)[(long)rr * HD + lane] << 16);
             }
         }
 #pragma unroll
@@ -448,23 +480,21 @@ hipError_t build_hd(const IndexArgs& a, hipStream_t s)
 
 // ---- block choice ----------------------------------------------------------
 
-template <int HD>
+template <int HD, int G>
 __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
 {
-    constexpr int CPL = HD / 64;
-    __shared__ float qs[16][HD];
+    __shared__ float qs[G][HD];
     __shared__ unsigned long long key[kIndexMaxBlocks];
     __shared__ int wsum[4];
     __shared__ __attribute__((aligned(16))) uint64_t chosen[kIndexMaxBlocks / 64];
     const Geometry& g = a.g;
-    const int G = g.G;
     int bid = blockIdx.x;
     const int row = bid % a.Q;
     bid /= a.Q;
     const int kvh = bid % g.Hkv, b = bid / g.Hkv;
     const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
     const int bk = b * g.Hkv + kvh;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
 
     for (int e = threadIdx.x; e < G * HD; e += 256) {
         const int h = e / HD, d = e - h * HD;
@@ -477,21 +507,28 @@ __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
     for (int w = threadIdx.x; w < kIndexMaxBlocks / 64; w += 256) chosen[w] = 0ull;
     __syncthreads();
 
-    // scores: a wave per block, lanes over channels, a fixed reduction tree
+    // scores: a thread per block, channels in order for every head
     const int32_t* off = a.offsets + (long)bk * (a.C + 1);
-    for (int c = wave; c < a.C; c += 4) {
-        const float* mu = a.centres + ((long)bk * a.C + c) * HD + CPL * lane;
-        float m[CPL];
+    for (int c = threadIdx.x; c < a.C; c += 256) {
+        const float4* mu = (const float4*)(a.centres + ((long)bk * a.C + c) * HD);
+        float dot[G];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) m[e] = mu[e];
-        float best = -INFINITY;
-        for (int h = 0; h < G; ++h) {
-            float p = 0.f;
+        for (int h = 0; h < G; ++h) dot[h] = 0.f;
+#pragma unroll 4
+        for (int d4 = 0; d4 < HD / 4; ++d4) {
+            const float4 m = mu[d4];
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) p = fmaf(qs[h][CPL * lane + e], m[e], p);
-            best = fmaxf(best, group_sum<64>(p));
+            for (int h = 0; h < G; ++h) {
+                dot[h] = fmaf(qs[h][4 * d4 + 0], m.x, dot[h]);
+                dot[h] = fmaf(qs[h][4 * d4 + 1], m.y, dot[h]);
+                dot[h] = fmaf(qs[h][4 * d4 + 2], m.z, dot[h]);
+                dot[h] = fmaf(qs[h][4 * d4 + 3], m.w, dot[h]);
+            }
         }
-        if (lane == 0 && off[c + 1] > off[c])  // blocks without tokens are never taken
+        float best = dot[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) best = fmaxf(best, dot[h]);
+        if (off[c + 1] > off[c])  // blocks without tokens are never taken
             key[c] = ((unsigned long long)order_key(best) << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
     }
     __syncthreads();
@@ -562,14 +599,27 @@ hipError_t launch_index_build(const IndexArgs& a, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+template <int HD>
+hipError_t select_blocks_g(const SelectBlocksArgs& a, dim3 grid, hipStream_t s)
+{
+    switch (a.g.G) {
+    case 1: hipLaunchKernelGGL((k_select_blocks<HD, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_select_blocks<HD, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_select_blocks<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_select_blocks<HD, 8>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_select_blocks<HD, 16>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_select_blocks(const SelectBlocksArgs& a, hipStream_t s)
 {
-    if (a.g.dtype != 1 || a.C < 1 || a.C > kIndexMaxBlocks || a.g.G > 16) return hipErrorInvalidValue;
+    if (a.g.dtype != 1 || a.C < 1 || a.C > kIndexMaxBlocks) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((long)a.g.B * a.g.Hkv * a.Q));
-    if (a.g.hd == 128) hipLaunchKernelGGL(k_select_blocks<128>, grid, dim3(256), 0, s, a);
-    else if (a.g.hd == 64) hipLaunchKernelGGL(k_select_blocks<64>, grid, dim3(256), 0, s, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.g.hd == 128) return select_blocks_g<128>(a, grid, s);
+    if (a.g.hd == 64) return select_blocks_g<64>(a, grid, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sa

@@ -107,7 +107,7 @@ struct GroupArgs {
     float* part_ml;
     // workspace: the plan
     int32_t* nunion;    // [B][Hkv] pages in the union
-    GroupPage* upages;  // [B][Hkv][npg] the union in launch order (most rows first)
+    GroupPage* upages;  // [B][Hkv][npg] the union in launch order (costliest first)
     int16_t* slots;     // [B][Hkv][npg][64] each row's list index of each union page (same order)
     int npg;            // candidate units per (sequence, KV head): max_pages, or the index's blocks
     // block mode (semantic index; blk_off == nullptr: pages of the paged
@@ -135,7 +135,7 @@ struct IndexArgs {
     float* inv_norm;     // [B][Hkv][N] 1 / |k_t| (0 for a zero key)
     uint16_t* cent_bf;   // [B][Hkv][C][hd] the centres rounded to bf16 (the assignment's operand)
     int32_t* assign;     // [B][Hkv][N]
-    int32_t* cnt;        // [B][Hkv][nchunks][C] per-chunk block counts, then bases
+    int32_t* cnt;        // [B][Hkv][C][nchunks] per-chunk block counts, then each chunk's first row
     int32_t* seg_base;   // [B][Hkv][C + 1] first update segment of each block
     int32_t* seg_block;  // [B][Hkv][nseg] block of each segment
     float* seg_sum;      // [B][Hkv][nseg][hd] sum of a segment's unit keys

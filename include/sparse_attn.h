@@ -270,7 +270,8 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
  *                k_max * token_splits + local_splits (<= 1024): slot
  *                j * token_splits + c holds chunk c of the row's j-th page,
  *                slots k_max * token_splits + s the sink/window split s; an
- *                unused slot holds (-inf, 0) and o = 0.  Merge them with
+ *                unused slot holds (m, l) = (-inf, 0) and its o is left
+ *                as it was (the combine skips it).  Merge them with
  *                sparse_attn_combine(num_splits = split_stride).
  *   workspace    >= sparse_attn_grouped_workspace_bytes(kv) bytes, 256-byte
  *                aligned (the per-(sequence, KV head) plan: the page union
@@ -397,7 +398,8 @@ int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int
  *   part_o [num_rows][num_splits][head_dim], part_ml [num_rows][num_splits][2]
  *   out    [num_rows][head_dim] in out_dtype (SA_BF16: round to nearest even)
  *   lse    fp32 [num_rows] or NULL.
- * A row whose parts are all empty gets out = 0 and lse = -inf.
+ * A part with l = 0 is empty: its o is not read into the sum (it may hold
+ * anything).  A row whose parts are all empty gets out = 0 and lse = -inf.
  * Errors: null pointers, num_rows < 1, head_dim not 64/128, num_splits
  * outside 1..1024, bad out_dtype.
  */

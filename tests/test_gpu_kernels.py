@@ -232,6 +232,11 @@ def test_combine_matches_oracle_merge():
     ml[3, :, 1] = 0
     ml[5, 2:7, 0] = -np.inf  # some empty parts
     ml[5, 2:7, 1] = 0
+    clean = po.copy()
+    po[3, :, :] = np.nan  # whatever an empty part's o holds is left out
+    po[5, 2:7, ::2] = np.inf
+    po[5, 2:7, 1::2] = np.nan
+    clean[3], clean[5, 2:7] = 0, 0
     out = torch.empty((rows, hd), dtype=torch.float32, device="cuda")
     lse = torch.empty(rows, dtype=torch.float32, device="cuda")
     B.sparse_attn_combine(rows, hd, splits, to_device(po), to_device(ml), out, B.SA_F32, lse)
@@ -241,7 +246,7 @@ def test_combine_matches_oracle_merge():
         if r == 3:
             assert (got[r] == 0).all() and gl[r] == -np.inf
             continue
-        ref, rl = oracle.merge(po[r], ml[r, :, 0], ml[r, :, 1])
+        ref, rl = oracle.merge(clean[r], ml[r, :, 0], ml[r, :, 1])
         np.testing.assert_allclose(got[r], ref, atol=2e-6, rtol=1e-5)
         assert abs(gl[r] - rl) < 1e-5 * max(1, abs(rl))
 
