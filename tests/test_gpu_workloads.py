@@ -2,7 +2,10 @@
 the benchmark times (the library's default split count): the tiny fp32
 case, the Qwen3-8B-shaped and Llama-3-70B-shaped layers, the 3-layer hybrid
 256k schedule (every refresh step and the last step) and the semantic-block
-512K chunk.  The oracle computes every output at these sizes."""
+512K chunk, paged and over a block index built from interleaved keys.  The
+oracle computes every output at these sizes (the index: its layout and the
+block choice of every row exactly, the assignment and the last centre
+update on samples, and the outputs of sampled rows)."""
 import time
 
 import numpy as np
@@ -19,7 +22,9 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 from block_sparse_long_page_amd import binding as B  # noqa: E402
-from block_sparse_long_page_amd.device import DeviceCache, GroupedStep, SparseDecoder, to_device  # noqa: E402
+from block_sparse_long_page_amd.device import (BlockIndex, DeviceCache, GroupedStep, SparseDecoder,  # noqa: E402
+                                               to_device)
+from oracle import semantic as sem  # noqa: E402
 
 
 def _say(*a):
@@ -121,3 +126,80 @@ def test_hybrid_schedule():
         del dc, dec
         torch.cuda.empty_cache()
     _say(f"[{wl.name}] total {time.time() - t0:.1f}s")
+
+
+def test_semantic_index_workload():
+    """The 512K semantic chunk with keys interleaved in position order, over
+    the index the benchmark builds (one block per 2048 tokens, 8 k-means
+    iterations, L/16 token budget, at most 64 blocks per row)."""
+    wl = configs.SEMANTIC_512K
+    t0 = time.time()
+    pr = synth.semantic_problem(wl, scatter=True)
+    c = pr.cache
+    L = int(c.seq_lens[0])
+    N, C = L - pr.window, (L - pr.window) // 2048
+    dc = DeviceCache.from_host(c)
+    q = to_device(pr.q)
+    ix = BlockIndex(dc, N, C, Q=pr.Q, window=pr.window, budget=pr.budget, k_max=64)
+    ix.build(7)
+    torch.cuda.synchronize()
+    prev_c, prev_a = ix.centres.cpu().numpy().astype(np.float64), ix.assignment.cpu().numpy()
+    ix.build(8)
+    ix.step(q)
+    torch.cuda.synchronize()
+    cen, asg = ix.centres.cpu().numpy().astype(np.float64), ix.assignment.cpu().numpy()
+    off, perm = ix.offsets.cpu().numpy(), ix.positions.cpu().numpy()
+    sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
+    out, lse = ix.out_f32(), ix.lse_f32()
+    _say(f"[{wl.name} index] built and stepped {time.time() - t0:.1f}s")
+    rng = np.random.default_rng(0)
+    G = c.Hq // c.Hkv
+    scale = 1.0 / np.sqrt(c.hd)
+    for b in range(c.B):
+        for kvh in range(c.Hkv):
+            n_pages = -(-L // c.P)
+            phys = c.block_table[b, :n_pages]
+            K = synth.to_f32(c.k[phys, kvh], c.dtype).astype(np.float64).reshape(-1, c.hd)[:L]
+            V = synth.to_f32(c.v[phys, kvh], c.dtype).astype(np.float64).reshape(-1, c.hd)[:L]
+            # the layout of the final assignment, exactly
+            p_ref, o_ref = sem.block_layout(asg[b, kvh], C)
+            np.testing.assert_array_equal(off[b, kvh], o_ref)
+            np.testing.assert_array_equal(perm[b, kvh], p_ref)
+            # sampled keys: the best centre within the rounding of bf16 products summed in fp32
+            ts = rng.choice(N, 4096, replace=False)
+            cb = (cen[b, kvh].astype(np.float32).view(np.uint32).astype(np.uint64))
+            cb = ((((cb + 0x7FFF + ((cb >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+                  .astype(np.float64))
+            d = K[ts] @ cb.T
+            bound = 1e-5 * (np.abs(K[ts]) @ np.abs(cb).T).max(axis=1)
+            assert np.all(d[np.arange(len(ts)), asg[b, kvh, ts]] >= d.max(axis=1) - bound)
+            # the last update of a few blocks from the previous assignment
+            u = sem.unit_keys(K[:N])
+            for x in rng.choice(C, 6, replace=False):
+                members = np.flatnonzero(prev_a[b, kvh] == x)
+                if members.size:
+                    want = u[members].sum(axis=0)
+                    want /= np.linalg.norm(want)
+                    np.testing.assert_allclose(cen[b, kvh, x], want, rtol=0, atol=2e-5)
+            # every row's block choice
+            sizes = np.diff(off[b, kvh])
+            for i in range(pr.Q):
+                qg = np.stack([synth.to_f32(pr.q[b, kvh * G + h, i], c.dtype).astype(np.float64) for h in range(G)])
+                s_ = sem.block_scores(qg, cen[b, kvh])
+                want = sem.select_blocks(s_, sizes, ix.budget, ix.k_max)
+                order = sorted((x for x in range(C) if sizes[x] > 0), key=lambda x: (-s_[x], x))
+                n = len(want)
+                edge = s_[order[max(0, n - 1):n + 2]]
+                got = sel[b, kvh, i, :cnt[b, kvh, i]]
+                if len(edge) < 2 or np.min(-np.diff(edge)) > 1e-4 * np.abs(s_).max():
+                    np.testing.assert_array_equal(got, want)
+                # sampled rows: the oracle's attention over the GPU's blocks and the window
+                if i % 16 == 5:
+                    pos = L - pr.Q + i
+                    toks = np.concatenate([perm[b, kvh, off[b, kvh, x]:off[b, kvh, x + 1]] for x in got] +
+                                          [np.arange(L - pr.window, pos + 1)])
+                    for h in range(G):
+                        o, l_ = sem.attend(qg[h], K[toks], V[toks], scale)
+                        check_output(out[b, kvh * G + h, i], o, c.dtype, f"b{b} kvh{kvh} row{i} head{h}")
+                        check_lse(np.array([lse[b, kvh * G + h, i]]), np.array([l_]), "index lse")
+    _say(f"[{wl.name} index] checked {time.time() - t0:.1f}s; blocks {sizes.min()}..{sizes.max()} tokens")
