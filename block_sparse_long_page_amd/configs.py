@@ -17,8 +17,8 @@ from __future__ import annotations
 from dataclasses import dataclass, field, replace
 from typing import Tuple
 
-QUEST, MEAN, CENTROID = 0, 1, 2
-MODE_NAMES = {"quest": QUEST, "mean": MEAN, "centroid": CENTROID}
+QUEST, MEAN, CENTROID, COMPRESSED = 0, 1, 2, 3
+MODE_NAMES = {"quest": QUEST, "mean": MEAN, "centroid": CENTROID, "compressed": COMPRESSED}
 F32, BF16 = 0, 1
 DTYPE_NAMES = {"f32": F32, "bf16": BF16}
 

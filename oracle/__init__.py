@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-QUEST, MEAN, CENTROID = 0, 1, 2
+QUEST, MEAN, CENTROID, COMPRESSED = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:

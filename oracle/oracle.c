@@ -16,13 +16,20 @@
  *      parameter, which we replace by the mean because no weights exist);
  *      semantic-block centroid = unit-norm mean of unit-norm keys (semantic
  *      blocks page: keys are normalised and grouped by spherical k-means into
- *      blocks, and a query is compared with the block centres).
+ *      blocks, and a query is compared with the block centres); compressed
+ *      key of the block of two pages starting at the page, the mean of its
+ *      keys (self-indexing attention page, "Compressed keys": blocks of l
+ *      keys with stride d, stride/block about 0.5; the trained MLP that
+ *      compresses a block is replaced by the mean because no weights exist).
  *   2. regions -- attention sink [0, S), sliding window of the last W
  *      positions [L-W, L), middle [S, L-W) (course module 14, section 14.2,
  *      StreamingLLM; self-indexing attention page, "Sliding window").
  *   3. scores -- per q-head, the exact maximum of q.x over the page's
  *      per-channel bounding box, sum_c max(q_c*mx_c, q_c*mn_c); or q.mean; or
- *      q.centroid.  One selection per KV head: the group score is the maximum
+ *      q.centroid; or, for compressed keys, the larger of q.c over the two
+ *      blocks that cover the page (starting at the page before and at the
+ *      page itself; the page's softmax over blocks is monotone, so it is
+ *      skipped).  One selection per KV head: the group score is the maximum
  *      over the G query heads that share the KV head (GQA, attention-mechanisms
  *      article, "MQA/GQA"; MSA picks blocks per GQA group, same article,
  *      "Learned top-k sparse attention").
@@ -45,7 +52,7 @@
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
-enum { ORC_QUEST = 0, ORC_MEAN = 1, ORC_CENTROID = 2 };
+enum { ORC_QUEST = 0, ORC_MEAN = 1, ORC_CENTROID = 2, ORC_COMPRESSED = 3 };
 
 /* A paged KV cache: K and V are each [num_phys][Hkv][P][hd] in `dtype`. */
 typedef struct {
@@ -84,12 +91,15 @@ int orc_summary_size(int mode, int hd) { return mode == ORC_QUEST ? 2 * hd : hd;
 /* Writes the summary of logical page `page` of (b, kvh) over its valid tokens
  * [page*P, min((page+1)*P, L)).  Quest: out[0..hd) = min, out[hd..2hd) = max.
  * Mean: out[c] = mean of k_c.  Centroid: u = sum of k/|k| (zero keys skipped),
- * out = u/|u| (all zeros when u = 0).  Returns the number of valid tokens. */
+ * out = u/|u| (all zeros when u = 0).  Compressed: the mean of the valid keys
+ * of the two pages starting at `page`, [page*P, min((page+2)*P, L)).
+ * Returns the number of tokens summarised. */
 int orc_page_summary(const orc_cache* c, int mode, int b, int kvh, int page, double* out)
 {
     int L = c->seq_lens[b];
     int t0 = page * c->P;
-    int t1 = t0 + c->P < L ? t0 + c->P : L;
+    int span = mode == ORC_COMPRESSED ? 2 * c->P : c->P;
+    int t1 = t0 + span < L ? t0 + span : L;
     int n = t1 - t0;
     int hd = c->hd;
     if (n <= 0) return 0;
@@ -104,7 +114,7 @@ int orc_page_summary(const orc_cache* c, int mode, int b, int kvh, int page, dou
             out[ch] = mn;
             out[hd + ch] = mx;
         }
-    } else if (mode == ORC_MEAN) {
+    } else if (mode == ORC_MEAN || mode == ORC_COMPRESSED) {
         for (int ch = 0; ch < hd; ++ch) {
             double s = 0.0;
             for (int t = t0; t < t1; ++t) s += elem(c->k, c->dtype, kv_index(c, b, kvh, t, ch));
@@ -356,6 +366,11 @@ int orc_run(const orc_cache* c, int mode, const void* q, int Q, int S, int W, in
                     for (int ch = 0; ch < hd; ++ch) qh[ch] = elem(q, c->dtype, qrow + ch);
                     for (int p = 0; p < c->max_pages; ++p) {
                         double u = cand[p] ? orc_page_score(mode, summ + (size_t)p * msz, qh, hd) : NAN;
+                        if (cand[p] && mode == ORC_COMPRESSED && p > 0) {
+                            /* the block starting at the page before also covers this page */
+                            double v = orc_page_score(mode, summ + (size_t)(p - 1) * msz, qh, hd);
+                            if (v > u) u = v;
+                        }
                         if (hscores_out) hscores_out[(((size_t)b * c->Hq + h) * Q + i) * c->max_pages + p] = u;
                         if (cand[p] && (g == 0 || u > gscore[p])) gscore[p] = u;
                     }

@@ -62,7 +62,7 @@ def _check_against_mask(pr, r, pages_of=None, tol=1e-12):
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
-@pytest.mark.parametrize("mode", ["quest", "mean", "centroid"])
+@pytest.mark.parametrize("mode", ["quest", "mean", "centroid", "compressed"])
 @pytest.mark.parametrize("shuffle", [False, True])
 def test_budget_covering_context_is_dense_attention(case, mode, shuffle):
     kw = dict(SMALL[case])
@@ -221,6 +221,12 @@ def _brute_scores(pr, b, kvh, i, mode):
                 s = seq_dot(np.ones_like(qh), np.maximum(qh * kp.min(0), qh * kp.max(0)))
             elif mode == "mean":
                 s = seq_dot(qh, kp.sum(0) / len(kp))
+            elif mode == "compressed":  # blocks of two pages with a one-page stride: the two that cover p
+                s = -np.inf
+                for j in (p - 1, p):
+                    if j >= 0:
+                        kb = K[j * c.P:min(L, (j + 2) * c.P)]
+                        s = max(s, seq_dot(qh, kb.sum(0) / len(kb)))
             else:
                 u = (kp / np.linalg.norm(kp, axis=1, keepdims=True)).sum(0)
                 s = seq_dot(qh, u / np.linalg.norm(u))
@@ -243,7 +249,7 @@ def _brute_topk(scores, k):
 
 
 @pytest.mark.parametrize("seed", range(6))
-@pytest.mark.parametrize("mode", ["quest", "mean", "centroid"])
+@pytest.mark.parametrize("mode", ["quest", "mean", "centroid", "compressed"])
 def test_selection_and_output_match_brute_force(seed, mode):
     rng = np.random.default_rng(100 + seed)
     P = [4, 8][seed % 2]
@@ -339,3 +345,39 @@ def test_planted_needle_pages_are_selected(wl):
     for (b, kvh, p) in pr.needles:
         assert p in set(r.sel[b, kvh, 0, : r.cnt[b, kvh, 0]])
     assert (r.cnt == wl.k_pages).all()
+
+
+def test_compressed_key_is_the_mean_over_two_pages():
+    """The compressed key of the block starting at page p is the mean of the
+    two pages' keys: the token-weighted average of the two pages' mean
+    summaries (pinned above), ragged last page included."""
+    pr = synth.random_problem(B=2, Hq=4, Hkv=2, hd=16, P=8, seq_lens=[83, 60], sink=4, window=8, budget=16,
+                              dtype="bf16", seed=41, shuffle=True)
+    c = pr.cache
+    for b in range(2):
+        n_pages = -(-int(c.seq_lens[b]) // c.P)
+        for kvh in range(2):
+            for p in range(n_pages):
+                got, n = oracle.page_summary(c, oracle.COMPRESSED, b, kvh, p)
+                m0, n0 = oracle.page_summary(c, oracle.MEAN, b, kvh, p)
+                m1, n1 = oracle.page_summary(c, oracle.MEAN, b, kvh, p + 1) if p + 1 < n_pages else (0.0, 0)
+                assert n == n0 + n1
+                np.testing.assert_allclose(got, (n0 * m0 + n1 * np.asarray(m1)) / (n0 + n1), rtol=0, atol=1e-13)
+
+
+def test_compressed_blocks_pull_in_the_needle_neighbours():
+    """A needle page p (every token 3 q + noise) lifts both blocks that hold
+    it, so pages p-1, p and p+1 (each covered by one of them) outscore the
+    rest; with the mean summaries only page p stands out."""
+    rng = np.random.default_rng(9)
+    pr = synth.random_problem(B=1, Hq=1, Hkv=1, hd=32, P=16, seq_lens=[40 * 16], sink=0, window=16, budget=3 * 16,
+                              dtype="bf16", seed=42, shuffle=True)
+    c = pr.cache
+    q = synth.to_f32(pr.q[0, 0, 0], c.dtype)
+    p = 17
+    keys = 3 * q[None, :] + rng.standard_normal((c.P, c.hd)).astype(np.float32)
+    c.k[c.block_table[0, p], 0] = synth.store(keys, c.dtype)
+    rc = oracle.run(c, pr.q, mode=oracle.COMPRESSED, Q=1, sink=0, window=16, budget=3 * 16)
+    np.testing.assert_array_equal(rc.sel[0, 0, 0], [p - 1, p, p + 1])
+    rm = oracle.run(c, pr.q, mode=oracle.MEAN, Q=1, sink=0, window=16, budget=16)
+    np.testing.assert_array_equal(rm.sel[0, 0, 0], [p])
