@@ -62,6 +62,9 @@ def parse():
                     help="run only the warmup and the timed region (for profiler runs)")
     ap.add_argument("--token-splits", type=int, default=0, help="semantic-512k: token chunks per page (0: default)")
     ap.add_argument("--iterations", type=int, default=8, help="semantic-512k-index: k-means iterations")
+    ap.add_argument("--score", default="quest", choices=["quest", "mean", "centroid", "compressed"],
+                    help="llama3-70b-layer-128k: page summary and score (compressed: mean keys of two-page "
+                         "blocks with a one-page stride)")
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
                     choices=["llama3-70b-layer-128k", "semantic-512k", "semantic-512k-index", "hybrid-3layer-256k"],
                     help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
@@ -465,7 +468,7 @@ def main():
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth
     from block_sparse_long_page_amd.device import DeviceCache, OverlappedStep, SparseDecoder, to_device
 
-    wl = configs.LLAMA3_70B
+    wl = configs.LLAMA3_70B.scaled(mode=args.score)
     t0 = time.time()
     pr = synth.workload_problem(wl)
     c = pr.cache
@@ -530,7 +533,7 @@ def main():
     n_cand = accounting.candidate_pages(L, c.P, pr.sink, pr.window)
     if mode == "fused":
         # the launch pair of sparse_attn_decode_step: page scores, then top-k + decode
-        dec_kernel = "k_score_quest_mfma + k_select_decode_mfma"
+        dec_kernel = ("k_score_quest_mfma" if pr.mode == B.SA_QUEST else "k_score") + " + k_select_decode_mfma"
         dec_bytes = accounting.select_decode_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
                                                    ntok_total=sum(attended), splits=dec.splits, meta=sb.meta,
                                                    n_cand=n_cand, k_max=dec.k_max)
@@ -648,7 +651,7 @@ def main():
         "data": "synthetic (seeded): K from 64 Gaussian clusters, V and q N(0,1)",
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "context": L, "page": c.P, "sink": pr.sink, "window": pr.window, "budget": pr.budget,
-                   "score": "quest", "replicas": R,
+                   "score": wl.mode, "replicas": R,
                    "splits": dec.splits if mode != "overlap" else {"sink_window": ov.sl, "selected": ov.sm},
                    "step": mode},
         "roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,

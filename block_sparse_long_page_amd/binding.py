@@ -20,7 +20,7 @@ HEADER = os.path.join(PKG, os.pardir, "include", "sparse_attn.h")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
 SA_F32, SA_BF16 = 0, 1
-SA_QUEST, SA_MEAN, SA_CENTROID = 0, 1, 2
+SA_QUEST, SA_MEAN, SA_CENTROID, SA_COMPRESSED = 0, 1, 2, 3
 SA_PART_LOCAL, SA_PART_MIDDLE, SA_PART_ALL = 1, 2, 3
 
 if not os.path.exists(LIB_PATH):

@@ -1,8 +1,10 @@
 // Page summaries: per (physical page, KV head) slab of P x hd keys, the
 // per-channel min and max (Quest pages, hybrid sparse attention page), the
 // mean key (a block key for MoBA-style gating, course module 14, section
-// 14.3) or the unit-norm mean of unit-norm keys (semantic block centres,
-// semantic-blocks page).
+// 14.3), the unit-norm mean of unit-norm keys (semantic block centres,
+// semantic-blocks page), or the mean key of the two pages starting at the
+// page (compressed key of a block of 2P keys with stride P, self-indexing
+// attention page, "Compressed keys", mean-pooled).
 //
 // One wave per (sequence, logical page, KV head).  The wave reads the slab
 // with 16-byte loads: LPT lanes cover one key row (8 bf16 or 4 fp32 channels
@@ -47,6 +49,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
 
     typedef typename std::conditional<BF, uint16_t, float>::type E;
     const E* slab = (const E*)g.k + ((long)phys * g.Hkv + kvh) * (long)g.P * HD + sub * CH;
+    // compressed keys: rows P .. 2P-1 are the next page's (when this page is
+    // full and the next one is mapped)
+    const E* slab1 = slab;
+    int nt = n;  // rows summarised
+    if constexpr (MODE == 3) {
+        const int ph1 = page + 1 < g.max_pages ? g.block_table[(long)b * g.max_pages + page + 1] : -1;
+        const int n1 = n == g.P && ph1 >= 0 && ph1 < g.num_phys ? imin(g.P, L - t0 - g.P) : 0;
+        if (n1 > 0) {
+            slab1 = (const E*)g.k + ((long)ph1 * g.Hkv + kvh) * (long)g.P * HD + sub * CH;
+            nt = n + n1;
+        }
+    }
 
     float acc0[CH], acc1[CH];  // Quest: min / max; mean, centroid: running sum in acc0
     for (int c = 0; c < CH; ++c) {
@@ -54,17 +68,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
         acc1[c] = -INFINITY;
     }
 
-    for (int base = 0; base < n; base += RPW * U) {
+    for (int base = 0; base < nt; base += RPW * U) {
         uint4 w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = base + u * RPW + rg;
-            w[u] = r < n ? *(const uint4*)(slab + (long)r * HD) : make_uint4(0, 0, 0, 0);
+            const E* row = r < g.P ? slab + (long)r * HD : slab1 + (long)(r - g.P) * HD;
+            w[u] = r < nt ? *(const uint4*)row : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = base + u * RPW + rg;
-            const bool valid = r < n;
+            const bool valid = r < nt;
             float x[CH];
             const uint32_t* ww = (const uint32_t*)&w[u];
             if constexpr (BF) {
@@ -81,7 +96,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
                         acc0[c] = fminf(acc0[c], x[c]);
                         acc1[c] = fmaxf(acc1[c], x[c]);
                     }
-            } else if constexpr (MODE == 1) {
+            } else if constexpr (MODE == 1 || MODE == 3) {
                 for (int c = 0; c < CH; ++c) acc0[c] += x[c];  // invalid rows loaded as 0
             } else {
                 float ss = 0.f;
@@ -106,8 +121,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
             }
         }
     }
-    if constexpr (MODE == 1) {
-        const float invn = 1.0f / (float)n;
+    if constexpr (MODE == 1 || MODE == 3) {
+        const float invn = 1.0f / (float)nt;
         for (int c = 0; c < CH; ++c) acc0[c] *= invn;
     } else if constexpr (MODE == 2) {
         float ss = 0.f;
@@ -149,6 +164,7 @@ hipError_t launch_mode(const MetaArgs& a, dim3 grid, hipStream_t s)
     case 0: hipLaunchKernelGGL((k_page_meta<HD, BF, 0>), grid, dim3(64 * kWaves), 0, s, a); break;
     case 1: hipLaunchKernelGGL((k_page_meta<HD, BF, 1>), grid, dim3(64 * kWaves), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_page_meta<HD, BF, 2>), grid, dim3(64 * kWaves), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_page_meta<HD, BF, 3>), grid, dim3(64 * kWaves), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -31,7 +31,10 @@ constexpr int kScoreU = SA_SCORE_U;  // page rows per lane, all loaded at once
 // Each wave scores RPW * U consecutive candidate pages with every summary load
 // issued up front (selection is latency-bound: one round trip per wave); the
 // workgroup stages the group's queries in LDS once.
-template <int HD, int G, bool BF, bool QUEST>
+// PREV (compressed keys): a page also scores against the summary of the
+// page before when that page is mapped (the block starting there covers this
+// page too); its score is the larger of the two.
+template <int HD, int G, bool BF, bool QUEST, bool PREV>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
 {
     // lanes per page row: Quest reads min and max rows in the cache dtype,
@@ -73,13 +76,17 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     const long meta_row = ((long)b * g.Hkv + kvh) * g.max_pages;
     const int32_t* bt = g.block_table + (long)b * g.max_pages;
     uint4 w0[U], w1[U];
-    bool ok[U];
+    bool ok[U], okp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int p = first + u * RPW + rg;
         const bool in = p <= phi;
         const int phys = in ? bt[p] : -1;
         ok[u] = phys >= 0 && phys < g.num_phys;
+        if constexpr (PREV) {
+            const int pp = in && p > 0 ? bt[p - 1] : -1;
+            okp[u] = pp >= 0 && pp < g.num_phys;
+        }
         if constexpr (QUEST) {
             const E* m = (const E*)a.meta + (meta_row + p) * 2 * HD + sub * CH;
             w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
         } else {
             const float* m = (const float*)a.meta + (meta_row + p) * HD + sub * CH;
             w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
+            if constexpr (PREV) w1[u] = okp[u] ? *(const uint4*)(m - HD) : make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -157,6 +165,12 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
                     for (int c = 0; c < CH; ++c) s = fmaf(qf[h][c], __uint_as_float(a0[c]), s);
                 }
                 best = fmaxf(best, group_sum<LPT>(s));
+                if constexpr (PREV) {
+                    float s1 = 0.f;
+                    for (int c = 0; c < CH; ++c) s1 = fmaf(qf[h][c], __uint_as_float(a1[c]), s1);
+                    s1 = group_sum<LPT>(s1);
+                    if (okp[u]) best = fmaxf(best, s1);
+                }
             }
         }
         if (sub == 0 && p <= phi) out[p] = ok[u] ? best : -INFINITY;
@@ -301,9 +315,11 @@ template <int HD, int G, bool BF>
 hipError_t launch_score_mode(const SelectArgs& a, dim3 grid, hipStream_t s)
 {
     if (a.mode == 0)
-        hipLaunchKernelGGL((k_score<HD, G, BF, true>), grid, dim3(64 * kScoreWaves), 0, s, a);
+        hipLaunchKernelGGL((k_score<HD, G, BF, true, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
+    else if (a.mode == 3)
+        hipLaunchKernelGGL((k_score<HD, G, BF, false, true>), grid, dim3(64 * kScoreWaves), 0, s, a);
     else
-        hipLaunchKernelGGL((k_score<HD, G, BF, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
+        hipLaunchKernelGGL((k_score<HD, G, BF, false, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
     return hipGetLastError();
 }
 

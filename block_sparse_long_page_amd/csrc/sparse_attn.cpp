@@ -145,7 +145,7 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
     const int rc = check_kv(kv, &g);
     if (rc != SA_OK) return rc;
     if (!meta || page_begin < 0 || page_end < page_begin) return SA_ERR_INVALID_ARG;
-    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
     const int end = page_end < g.max_pages ? page_end : g.max_pages;
     if (end <= page_begin) return SA_OK;
     sa::MetaArgs a{g, score_mode, page_begin, end, meta};
@@ -160,7 +160,7 @@ int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
     if (rc != SA_OK) return rc;
-    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
     if (!q || !meta || !sel_count || num_q_rows < 1 || sink_len < 0 || window_len < 1 || token_budget < 0)
         return SA_ERR_INVALID_ARG;
     if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
@@ -239,7 +239,7 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
     if (rc != SA_OK) return rc;
-    if (score_mode != SA_QUEST && score_mode != SA_MEAN && score_mode != SA_CENTROID) return SA_ERR_UNSUPPORTED;
+    if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
     if (!q || !meta || !sel_count || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 ||
         token_budget < 0)
         return SA_ERR_INVALID_ARG;

@@ -85,6 +85,8 @@ extern "C" {
 #define SA_QUEST 0    /* per-channel min and max; score = sum_c max(q_c*min_c, q_c*max_c) */
 #define SA_MEAN 1     /* mean key of the page (MoBA-style block key); score = q.mean */
 #define SA_CENTROID 2 /* unit-norm mean of unit-norm keys (semantic block centre); score = q.c */
+#define SA_COMPRESSED 3 /* mean key of the block of two pages starting at the page (compressed keys
+                           with block length 2P and stride P); score = max(q.c_p, q.c_{p-1}) */
 
 /*
  * The paged KV cache (PagedAttention-style page management, attention-
@@ -135,6 +137,12 @@ typedef struct sa_kv_desc {
  *                fp32: mean key.
  *   SA_CENTROID  same layout: u = sum_t k_t/|k_t| (zero keys skipped),
  *                meta = u/|u| (zeros when u = 0).
+ *   SA_COMPRESSED same layout: mean of the valid keys of pages p and p+1
+ *                (self-indexing attention page, "Compressed keys": blocks of
+ *                2P keys with stride P, mean-pooled); page p+1 counts only
+ *                when page p is full and p+1 is mapped.  A change to page p
+ *                also changes summary p-1, so after an append rebuild
+ *                [last-1, last+1).
  * Summaries are indexed by logical page, so selection streams one
  * contiguous run per (sequence, KV head) without going through the block
  * table.  Sums run in fp32.  Pages outside the range are left untouched, so
@@ -163,7 +171,9 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
  * For every (b, KV head, row) and candidate page p, each of the G query heads
  * of the group scores the page (SA_QUEST: the exact maximum of q.x over the
  * page's per-channel bounding box, an upper bound on max_t q.k_t; SA_MEAN /
- * SA_CENTROID: q.summary); the group score is the maximum over the G heads.
+ * SA_CENTROID: q.summary; SA_COMPRESSED: the larger of q.summary_p and, when
+ * page p-1 is mapped, q.summary_{p-1}, since both blocks cover page p); the
+ * group score is the maximum over the G heads.
  * Pages are ranked by (group score desc, page index asc) in fp32 and the
  * first k kept.  When k_max >= #candidates every candidate is kept (the
  * dense fallback at short context).

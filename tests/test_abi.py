@@ -82,7 +82,7 @@ def test_page_meta_checks():
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 0, 8, None, None) == B.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, -1, 8, DEV, None) == B.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 5, 4, DEV, None) == B.SA_ERR_INVALID_ARG
-    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 3, 0, 8, DEV, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 4, 0, 8, DEV, None) == B.SA_ERR_UNSUPPORTED
     # an empty range is a valid no-op that queues nothing
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 4, 4, DEV, None) == B.SA_OK
     assert lib.sparse_attn_build_page_meta(ctypes.byref(d), 0, 8, 100, DEV, None) == B.SA_OK

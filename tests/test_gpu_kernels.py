@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 from block_sparse_long_page_amd import synth
+from helpers import dense_keys_values
 from parity import check_lse, check_output, check_selection
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +35,7 @@ CASES = {
     "bf16-hd128-g8-q5": dict(B=2, Hq=16, Hkv=2, hd=128, P=32, seq_lens=[1500, 700], sink=16, window=3, budget=256,
                              dtype="bf16", Q=5),
 }
-MODES = ["quest", "mean", "centroid"]
+MODES = ["quest", "mean", "centroid", "compressed"]
 
 
 def _problem(name, mode, seed=0, **over):
@@ -73,15 +74,14 @@ def test_page_summaries(name, mode):
         n_pages = -(-L // c.P)
         assert (got[b, :, n_pages:] == 0).all()  # pages past the sequence are never written
         for p in range(n_pages):
-            phys = c.block_table[b, p]
             for kvh in range(c.Hkv):
                 ref, n = oracle.page_summary(c, pr.mode, b, kvh, p)
                 g = got[b, kvh, p].reshape(-1).astype(np.float64)
                 if pr.mode == oracle.QUEST:
                     np.testing.assert_array_equal(g, ref)  # min/max are exact
                 else:
-                    K = synth.to_f32(c.k[phys, kvh, :n], c.dtype).astype(np.float64)
-                    scale = np.abs(K).mean(0) if pr.mode == oracle.MEAN else 1.0
+                    K = dense_keys_values(c, b, kvh)[0][p * c.P:p * c.P + n]
+                    scale = np.abs(K).mean(0) if pr.mode in (oracle.MEAN, oracle.COMPRESSED) else 1.0
                     assert np.all(np.abs(g - ref) <= 2e-6 * (scale + 1e-30) + 1e-7 * (pr.mode == oracle.CENTROID))
 
 
@@ -251,14 +251,20 @@ def test_combine_matches_oracle_merge():
         assert abs(gl[r] - rl) < 1e-5 * max(1, abs(rl))
 
 
-def test_incremental_summary_of_an_appended_page():
+@pytest.mark.parametrize("mode", ["quest", "compressed"])
+def test_incremental_summary_of_an_appended_page(mode):
+    """An append changes the last page's summary and, for compressed keys,
+    the one before it (its block reaches into the last page): rebuilding
+    just those gives the full rebuild bit for bit."""
     pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=128, P=32, seq_lens=[1000, 1000], sink=16, window=64,
-                              budget=256, dtype="bf16", seed=9, max_pages=40)
+                              budget=256, dtype="bf16", seed=9, max_pages=40, mode=mode)
     c = pr.cache
+    m = pr.mode
+    reach = 1 if m == oracle.COMPRESSED else 0
     dc = DeviceCache.from_host(c, max_seq_len=40 * 32)
-    meta = dc.new_meta(0)
+    meta = dc.new_meta(m)
     d = dc.desc()
-    B.sparse_attn_build_page_meta(d, 0, 0, dc.max_pages, meta)
+    B.sparse_attn_build_page_meta(d, m, 0, dc.max_pages, meta)
     for L in (1001, 1023, 1024, 1025):  # append tokens one page-piece at a time
         dc.seq_lens.fill_(L)
         c.seq_lens[:] = L
@@ -267,9 +273,9 @@ def test_incremental_summary_of_an_appended_page():
             for b in range(c.B):
                 c.block_table[b, last] = b * c.max_pages + last
             dc.block_table.copy_(to_device(c.block_table))
-        B.sparse_attn_build_page_meta(d, 0, last, last + 1, meta)
-    full = dc.new_meta(0)
-    B.sparse_attn_build_page_meta(d, 0, 0, dc.max_pages, full)
+        B.sparse_attn_build_page_meta(d, m, max(0, last - reach), last + 1, meta)
+    full = dc.new_meta(m)
+    B.sparse_attn_build_page_meta(d, m, 0, dc.max_pages, full)
     torch.cuda.synchronize()
     assert torch.equal(meta, full)
 
