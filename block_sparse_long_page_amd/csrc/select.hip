@@ -3,17 +3,17 @@
 // "Learned top-k sparse attention": top-k blocks per GQA group).
 //
 // Two kernels:
-//  * k_score: many workgroups per (sequence, KV head, row) stream the page
+//  * k_score_quest_mfma (Quest, bf16 cache) / k_score_f32_mfma (fp32
+//    summaries): many workgroups per (sequence, KV head, row) stream the page
 //    summaries of the candidate pages once, score each page against the G
-//    query heads of the group and keep the group maximum, fp32, in the
-//    workspace.  Selection reads megabytes of summaries per step, so it is
-//    spread over the whole GPU rather than run by one workgroup per problem.
+//    query heads of the group on the matrix cores and keep the group
+//    maximum, fp32, in the workspace.  Selection reads megabytes of summaries
+//    per step, so it is spread over the whole GPU rather than run by one
+//    workgroup per problem.
 //  * k_topk: one workgroup per (sequence, KV head, row) keeps the order keys
 //    of the candidates in registers, radix-selects the k-th largest starting
 //    at the highest bit where the keys differ, and writes the chosen pages in
 //    ascending order.  Ties go to the lower page index.
-#include <type_traits>
-
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "topk_block.hpp"
@@ -22,40 +22,55 @@ namespace sa {
 
 namespace {
 
-#ifndef SA_SCORE_U
-#define SA_SCORE_U 8
-#endif
 constexpr int kScoreWaves = 4;
-constexpr int kScoreU = SA_SCORE_U;  // page rows per lane, all loaded at once
 
-// Each wave scores RPW * U consecutive candidate pages with every summary load
-// issued up front (selection is latency-bound: one round trip per wave); the
-// workgroup stages the group's queries in LDS once.
-// PREV (compressed keys): a page also scores against the summary of the
-// page before when that page is mapped (the block starting there covers this
-// page too); its score is the larger of the two.
-template <int HD, int G, bool BF, bool QUEST, bool PREV>
-__global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
+typedef __bf16 sbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float sf32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef SA_SCORE_TW
+#define SA_SCORE_TW 2
+#endif
+
+// Scores of fp32 summary rows on the matrix cores (fp32 product, fp32 sums):
+// the scores of 16 pages for the G heads are one product of the pages'
+// summary rows (A: row = page) with the heads' query rows (B: column = head;
+// heads past G are zero) over K = the row length, four channels per step.
+// Lane (r, j) = (lane % 16, lane / 16) loads channels 4j .. 4j+3 of every
+// 16-channel group of its row as one 16-byte vector, and step (s, i) takes
+// channel 16 s + 4j + i of both operands; lane (r, j) of the result holds
+// head r's scores of pages 4j .. 4j+3, and the group maximum is a DPP max
+// over the 16 lanes of its row.
+//   KIND 0 (Quest, fp32 cache): rows [mn | mx] against [q- | q+] (K = 2 hd),
+//     since max(q_c mn_c, q_c mx_c) = q-_c mn_c + q+_c mx_c term by term.
+//   KIND 1 (mean, centroid): rows = the summary, score = q . summary.
+//   KIND 2 (compressed keys): as KIND 1, and page p also takes the score of
+//     the block starting at p-1 (it covers p too) when p-1 is mapped.  A wave
+//     then scores the page before its first output page as well, and each
+//     output page takes the larger of its own score and its predecessor's
+//     (same lane, the lane group before, or the tile before).
+// With a bf16 cache (KIND 1 and 2) the queries are exact in bf16 and each
+// fp32 summary element splits exactly into three bf16 parts, hi + mid + lo
+// (each the rounded remainder of the one before; 24 bits in all), so the
+// product runs as three bf16 products with fp32 sums (16x16x32 steps, lane
+// (r, j) holding channels 8j .. 8j+7 of every 32-channel group): an fp32
+// product at a third of the matrix-core time, since the fp32 steps would
+// spend half their columns on absent heads when G = 8.
+template <int HD, int G, bool BF, int KIND>
+__global__ __launch_bounds__(64 * kScoreWaves) void k_score_f32_mfma(SelectArgs a)
 {
-    // lanes per page row: Quest reads min and max rows in the cache dtype,
-    // mean/centroid read one fp32 row
-    constexpr int EB = QUEST ? (BF ? 2 : 4) : 4;
-    constexpr int CH = 16 / EB;
-    constexpr int LPT = HD / CH;
-    constexpr int RPW = 64 / LPT;
-    constexpr int U = kScoreU;
-    constexpr int PER_WAVE = RPW * U;
-    constexpr int PAGES_PER_WG = PER_WAVE * kScoreWaves;
-    // packed-bf16 Quest scores reduce-scatter the G head sums (LPT <= 16)
-    constexpr bool RS = QUEST && BF && LPT <= 16;
-    constexpr int HPL = RS && G > LPT ? G / LPT : 1;
-    constexpr int QB = BF ? 2 : 4;             // bytes per query element
-    constexpr int QV = HD * QB / 16;           // 16-byte vectors per query row
-    typedef typename std::conditional<BF, uint16_t, float>::type E;
-    __shared__ uint4 q_lds[G * QV];
+    constexpr bool QUEST = KIND == 0, PREV = KIND == 2;
+    constexpr bool SPLIT = BF && !QUEST;               // three bf16 parts per summary element
+    constexpr int RL = QUEST ? 2 * HD : HD;           // fp32 elements per summary row
+    constexpr int KV = RL / 16;                        // 16-byte pieces per lane per row
+    constexpr int QP = HD / 16;                        // query pieces per lane (fp32 steps)
+    constexpr int KC = HD / 32;                        // 32-channel groups (bf16 steps)
+    constexpr int TW = QUEST ? 1 : SA_SCORE_TW;        // tiles of 16 pages per wave
+    constexpr int OUT_PER_WAVE = 16 * TW - (PREV ? 1 : 0);
+    constexpr int OUT_PER_WG = OUT_PER_WAVE * kScoreWaves;
+    static_assert(G <= 16, "one MFMA column per head");
     const Geometry& g = a.g;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane % LPT, rg = lane / LPT;
+    const int r = lane & 15, j = lane >> 4;
 
     int pid = blockIdx.y;
     const int row = pid % a.Q;
@@ -67,113 +82,130 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
     const int se = imin(a.S, L), ws = imax(se, L - a.W);
     if (ws <= se) return;
     const int plo = se / g.P, phi = (ws - 1) / g.P;
-    const int wg_first = plo + blockIdx.x * PAGES_PER_WG;
-    if (wg_first > phi) return;
+    const int first_out = plo + blockIdx.x * OUT_PER_WG + wave * OUT_PER_WAVE;
+    if (first_out > phi) return;
+    const int first = first_out - (PREV ? 1 : 0);  // page of tile row 0 (-1 when there is none)
 
-    // every summary row of this wave's pages and their block-table entries
-    // are requested before the query staging, so the two round trips overlap
-    const int first = wg_first + wave * PER_WAVE;
+    // A: summary rows of this wave's pages, all in flight at once
     const long meta_row = ((long)b * g.Hkv + kvh) * g.max_pages;
-    const int32_t* bt = g.block_table + (long)b * g.max_pages;
-    uint4 w0[U], w1[U];
-    bool ok[U], okp[U];
+    const float* meta = (const float*)a.meta;
+    float4 am[TW][KV];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = first + u * RPW + rg;
-        const bool in = p <= phi;
-        const int phys = in ? bt[p] : -1;
-        ok[u] = phys >= 0 && phys < g.num_phys;
-        if constexpr (PREV) {
-            const int pp = in && p > 0 ? bt[p - 1] : -1;
-            okp[u] = pp >= 0 && pp < g.num_phys;
-        }
-        if constexpr (QUEST) {
-            const E* m = (const E*)a.meta + (meta_row + p) * 2 * HD + sub * CH;
-            w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
-            w1[u] = in ? *(const uint4*)(m + HD) : make_uint4(0, 0, 0, 0);
-        } else {
-            const float* m = (const float*)a.meta + (meta_row + p) * HD + sub * CH;
-            w0[u] = in ? *(const uint4*)m : make_uint4(0, 0, 0, 0);
-            if constexpr (PREV) w1[u] = okp[u] ? *(const uint4*)(m - HD) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < TW; ++t) {
+        const int p = first + 16 * t + r;
+#pragma unroll
+        for (int s = 0; s < KV; ++s) {
+            // fp32 steps: channels 16 s + 4j .. +3; bf16 steps: piece s covers
+            // channels 32 (s/2) + 8j + 4 (s%2) .. +3
+            const int ch = SPLIT ? 32 * (s >> 1) + 8 * j + 4 * (s & 1) : 16 * s + 4 * j;
+            am[t][s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p >= 0 && p <= phi) am[t][s] = *(const float4*)(meta + (meta_row + p) * RL + ch);
         }
     }
-
-    const long qrow0 = (((long)b * g.Hq + kvh * G) * a.Q + row) * HD;
-    for (int i = threadIdx.x; i < G * QV; i += 64 * kScoreWaves) {
-        const int h = i / QV, v = i % QV;
-        q_lds[i] = ((const uint4*)((const E*)a.q + qrow0 + (long)h * a.Q * HD))[v];
-    }
-    __syncthreads();
-    if (first > phi) return;
-
-    // this lane's channels of the G queries
-    uint32_t qw[G][4];   // Quest + bf16: packed pairs
-    uint32_t neg[G][4];  // Quest + bf16: 0xffff in each half whose q is negative
-    float qf[G][CH];     // otherwise: fp32 channels
-    for (int h = 0; h < G; ++h) {
-        if constexpr (QUEST && BF) {
-            const uint4 w = q_lds[h * QV + sub];
-            qw[h][0] = w.x;
-            qw[h][1] = w.y;
-            qw[h][2] = w.z;
-            qw[h][3] = w.w;
-            for (int j = 0; j < 4; ++j)
-                neg[h][j] = ((qw[h][j] >> 15) & 1u) * 0xffffu | ((qw[h][j] >> 31) & 1u) * 0xffff0000u;
-        } else {
-            const E* qh = (const E*)&q_lds[h * QV];
-            for (int c = 0; c < CH; ++c) {
-                if constexpr (BF)
-                    qf[h][c] = __uint_as_float((uint32_t)((const uint16_t*)qh)[sub * CH + c] << 16);
-                else
-                    qf[h][c] = ((const float*)qh)[sub * CH + c];
+    // block-table entries of pages 4j .. 4j+3 of each tile (unmapped pages score -inf)
+    const int32_t* bt = g.block_table + (long)b * g.max_pages;
+    bool ok[TW][4];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = first + 16 * t + 4 * j + i;
+            const int ph = p >= 0 && p <= phi ? bt[p] : -1;
+            ok[t][i] = ph >= 0 && ph < g.num_phys;
+        }
+    // B: head r's channels, in fp32 (16 s + 4j .. +3) or bf16 (32 s + 8j .. +7)
+    const long qoff = (((long)b * g.Hq + kvh * G + r) * a.Q + row) * HD;
+    float4 qv[SPLIT ? 1 : QP];
+    uint4 qb[SPLIT ? KC : 1];
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+            qb[s] = r < G ? *(const uint4*)((const uint16_t*)a.q + qoff + 32 * s + 8 * j) : make_uint4(0, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int s = 0; s < QP; ++s) {
+            qv[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < G) {
+                if constexpr (BF) {
+                    const uint2 w = *(const uint2*)((const uint16_t*)a.q + qoff + 16 * s + 4 * j);
+                    qv[s] = make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+                } else {
+                    qv[s] = *(const float4*)((const float*)a.q + qoff + 16 * s + 4 * j);
+                }
             }
         }
     }
 
     float* out = a.scores + (((long)b * g.Hkv + kvh) * a.Q + row) * g.max_pages;
+    float prev3 = -INFINITY;  // the tile before's score of its last page (PREV)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = first + u * RPW + rg;
-        const uint32_t* a0 = (const uint32_t*)&w0[u];
-        const uint32_t* a1 = (const uint32_t*)&w1[u];
-        float best;
-        if constexpr (RS) {
-            // max(q*mn, q*mx) = q * (q >= 0 ? mx : mn), picked per bf16 half by q's sign
-            float d[G];
+    for (int t = 0; t < TW; ++t) {
+        sf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (SPLIT) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float s = 0.f;
+            for (int s = 0; s < KC; ++s) {
+                const float* x = (const float*)&am[t][2 * s];  // 8 channels (two adjacent pieces)
+                const float* y = (const float*)&am[t][2 * s + 1];
+                float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s = dot2_bf16(qw[h][j], (a0[j] & neg[h][j]) | (a1[j] & ~neg[h][j]), s);
-                d[h] = s;
-            }
-            reduce_scatter<G, log2c<LPT>() - 1>(d, lane);
-            best = d[0];
+                for (int part = 0; part < 3; ++part) {
+                    uint4 w;
+                    uint32_t* ww = (uint32_t*)&w;
 #pragma unroll
-            for (int j = 1; j < HPL; ++j) best = fmaxf(best, d[j]);
-            best = group_max<LPT>(best);
-        } else {
-            best = -INFINITY;
-            for (int h = 0; h < G; ++h) {
-                float s = 0.f;
-                if constexpr (QUEST) {
-                    for (int c = 0; c < CH; ++c) {
-                        const float q = qf[h][c];
-                        s = fmaf(q, q >= 0.f ? __uint_as_float(a1[c]) : __uint_as_float(a0[c]), s);
+                    for (int e = 0; e < 4; ++e) {
+                        ww[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
+                        v[2 * e] -= bf_lo(ww[e]);  // exact: the remainder of a rounding
+                        v[2 * e + 1] -= bf_hi(ww[e]);
                     }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sbf16x8_t, w),
+                                                                  __builtin_bit_cast(sbf16x8_t, qb[s]), acc, 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KV; ++s) {
+                const float* av = (const float*)&am[t][s];
+                float bq[4];
+                if constexpr (QUEST) {
+                    // pieces 0 .. QP-1 are the min row (q-), QP .. 2QP-1 the max row (q+)
+                    const float* qq = (const float*)&qv[s % QP];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bq[i] = s < QP ? fminf(qq[i], 0.f) : fmaxf(qq[i], 0.f);
                 } else {
-                    for (int c = 0; c < CH; ++c) s = fmaf(qf[h][c], __uint_as_float(a0[c]), s);
+                    const float* qq = (const float*)&qv[s];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bq[i] = qq[i];
                 }
-                best = fmaxf(best, group_sum<LPT>(s));
-                if constexpr (PREV) {
-                    float s1 = 0.f;
-                    for (int c = 0; c < CH; ++c) s1 = fmaf(qf[h][c], __uint_as_float(a1[c]), s1);
-                    s1 = group_sum<LPT>(s1);
-                    if (okp[u]) best = fmaxf(best, s1);
-                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bq[i], acc, 0, 0, 0);
             }
         }
-        if (sub == 0 && p <= phi) out[p] = ok[u] ? best : -INFINITY;
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float best = group_max<16>(r < G ? acc[i] : -INFINITY);
+            sc[i] = ok[t][i] ? best : -INFINITY;
+        }
+        if constexpr (PREV) {
+            // predecessor of page 4j: the lane group before (j > 0) or the tile before (j == 0)
+            const int src = (lane + 48) & 63;
+            const float from_group = __shfl(sc[3], src);
+            const float pred0 = j > 0 ? from_group : prev3;
+            prev3 = __shfl(sc[3], (lane & 15) + 48);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ri = 16 * t + 4 * j + i;
+                const int p = first + ri;
+                const float pred = i > 0 ? sc[i - 1] : pred0;
+                if (r == 0 && ri > 0 && p <= phi) out[p] = ok[t][i] ? fmaxf(sc[i], pred) : -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = first + 16 * t + 4 * j + i;
+                if (r == 0 && p <= phi) out[p] = sc[i];
+            }
+        }
     }
 }
 
@@ -186,13 +218,6 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(SelectArgs a)
 // holds head r's bounds of pages 4j .. 4j+3; the group maximum is a DPP max
 // over the 16 lanes of its row.  Each wave scores TW tiles of 16 pages with
 // every summary load issued up front.
-typedef __bf16 sbf16x8_t __attribute__((ext_vector_type(8)));
-typedef float sf32x4_t __attribute__((ext_vector_type(4)));
-
-#ifndef SA_SCORE_TW
-#define SA_SCORE_TW 2
-#endif
-
 template <int HD, int G>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score_quest_mfma(SelectArgs a)
 {
@@ -312,14 +337,20 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
 }
 
 template <int HD, int G, bool BF>
-hipError_t launch_score_mode(const SelectArgs& a, dim3 grid, hipStream_t s)
+hipError_t launch_score_f32(const SelectArgs& a, hipStream_t s)
 {
-    if (a.mode == 0)
-        hipLaunchKernelGGL((k_score<HD, G, BF, true, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
-    else if (a.mode == 3)
-        hipLaunchKernelGGL((k_score<HD, G, BF, false, true>), grid, dim3(64 * kScoreWaves), 0, s, a);
+    const int kind = a.mode == 0 ? 0 : a.mode == 3 ? 2 : 1;
+    const int tw = kind == 0 ? 1 : SA_SCORE_TW;
+    const int per_wg = (16 * tw - (kind == 2 ? 1 : 0)) * kScoreWaves;
+    const dim3 grid((unsigned)((a.g.max_pages + per_wg - 1) / per_wg), (unsigned)(a.g.B * a.g.Hkv * a.Q));
+    const dim3 block(64 * kScoreWaves);
+    if (kind == 0) {
+        if constexpr (BF) return hipErrorInvalidValue;  // bf16 Quest bounds: k_score_quest_mfma
+        else hipLaunchKernelGGL((k_score_f32_mfma<HD, G, BF, 0>), grid, block, 0, s, a);
+    } else if (kind == 1)
+        hipLaunchKernelGGL((k_score_f32_mfma<HD, G, BF, 1>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_score<HD, G, BF, false, false>), grid, dim3(64 * kScoreWaves), 0, s, a);
+        hipLaunchKernelGGL((k_score_f32_mfma<HD, G, BF, 2>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -346,14 +377,14 @@ hipError_t launch_score_quest_bf16_g(const SelectArgs& a, hipStream_t s)
 }
 
 template <int HD, bool BF>
-hipError_t launch_score_g(const SelectArgs& a, dim3 grid, hipStream_t s)
+hipError_t launch_score_f32_g(const SelectArgs& a, hipStream_t s)
 {
     switch (a.g.G) {
-    case 1: return launch_score_mode<HD, 1, BF>(a, grid, s);
-    case 2: return launch_score_mode<HD, 2, BF>(a, grid, s);
-    case 4: return launch_score_mode<HD, 4, BF>(a, grid, s);
-    case 8: return launch_score_mode<HD, 8, BF>(a, grid, s);
-    case 16: return launch_score_mode<HD, 16, BF>(a, grid, s);
+    case 1: return launch_score_f32<HD, 1, BF>(a, s);
+    case 2: return launch_score_f32<HD, 2, BF>(a, s);
+    case 4: return launch_score_f32<HD, 4, BF>(a, s);
+    case 8: return launch_score_f32<HD, 8, BF>(a, s);
+    case 16: return launch_score_f32<HD, 16, BF>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -368,17 +399,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s)
         const hipError_t e = g.hd == 128 ? launch_score_quest_bf16_g<128>(a, s) : launch_score_quest_bf16_g<64>(a, s);
         if (e != hipSuccess) return e;
     } else if (a.k_max > 0) {
-        // rows per wave load of the score kernel, as in k_score
-        const int eb = a.mode == 0 ? (g.dtype == 1 ? 2 : 4) : 4;
-        const int lpt = g.hd / (16 / eb);
-        const int pages_per_wg = (64 / lpt) * kScoreU * kScoreWaves;
-        const dim3 grid((unsigned)((g.max_pages + pages_per_wg - 1) / pages_per_wg), (unsigned)problems);
+        // fp32 summaries (and Quest bounds of an fp32 cache)
         const bool bf = g.dtype == 1;
         hipError_t e;
         if (g.hd == 128)
-            e = bf ? launch_score_g<128, true>(a, grid, s) : launch_score_g<128, false>(a, grid, s);
+            e = bf ? launch_score_f32_g<128, true>(a, s) : launch_score_f32_g<128, false>(a, s);
         else if (g.hd == 64)
-            e = bf ? launch_score_g<64, true>(a, grid, s) : launch_score_g<64, false>(a, grid, s);
+            e = bf ? launch_score_f32_g<64, true>(a, s) : launch_score_f32_g<64, false>(a, s);
         else
             return hipErrorInvalidValue;
         if (e != hipSuccess) return e;

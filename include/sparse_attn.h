@@ -166,7 +166,10 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
  *               when k_max > 0): the chosen logical pages in ascending order,
  *               -1 after the last.
  *   sel_count   int32 [batch][num_kv_heads][num_q_rows]: min(k_max, #candidates).
- *   workspace   device scratch of at least sparse_attn_workspace_bytes() bytes.
+ *   workspace   device scratch of at least sparse_attn_workspace_bytes() bytes;
+ *               on return its first B*Hkv*Q*max_pages_per_seq floats hold the
+ *               group scores, [batch][num_kv_heads][num_q_rows][max_pages],
+ *               of the candidate pages (other entries undefined).
  *
  * For every (b, KV head, row) and candidate page p, each of the G query heads
  * of the group scores the page (SA_QUEST: the exact maximum of q.x over the
@@ -174,8 +177,10 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
  * SA_CENTROID: q.summary; SA_COMPRESSED: the larger of q.summary_p and, when
  * page p-1 is mapped, q.summary_{p-1}, since both blocks cover page p); the
  * group score is the maximum over the G heads.
- * Pages are ranked by (group score desc, page index asc) in fp32 and the
- * first k kept.  When k_max >= #candidates every candidate is kept (the
+ * Scores are fp32 products with fp32 sums (with a bf16 cache the fp32
+ * summaries of the dot-product modes enter the matrix cores as three exact
+ * bf16 parts).  Pages are ranked by (group score desc, page index asc) in
+ * fp32 and the first k kept.  When k_max >= #candidates every candidate is kept (the
  * dense fallback at short context).
  * Errors: null pointers (sel_pages may be null only when k_max == 0),
  * num_q_rows < 1, S < 0, W < 1, token_budget < 0, workspace too small.

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from block_sparse_long_page_amd import synth
-from helpers import dense_keys_values
+from helpers import dense_keys_values, query
 from parity import check_lse, check_output, check_selection
 
 pytestmark = pytest.mark.gpu
@@ -194,6 +194,42 @@ def test_select_decode_at_the_candidate_limit():
                      cnt=cnt)
     check_output(dec.out_f32(), ref.out, pr.cache.dtype, "candidate limit")
     check_lse(dec.lse_f32(), ref.lse, "candidate limit")
+
+
+@pytest.mark.parametrize("name", ["bf16-hd128-g8-p64", "f32-hd64-g4-p16", "bf16-hd128-g16-p32", "bf16-hd128-g8-q5",
+                                  "bf16-hd64-g1-p7"])
+@pytest.mark.parametrize("mode", MODES)
+def test_group_scores_are_fp32_accurate(name, mode):
+    """The group scores sparse_attn_select leaves in its workspace agree with
+    the oracle's fp64 scores to fp32 rounding: within SCORE_REL of
+    max_h |q_h|_1 * max(max |k|, 1) (every summary element is at most
+    max |k| in size, a centroid's at most 1), for every candidate page."""
+    SCORE_REL = 3e-6
+    pr = _problem(name, mode, seed=5)
+    c = pr.cache
+    dc = DeviceCache.from_host(c)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget)
+    q = to_device(pr.q)
+    dec.build_meta()
+    dec.select(q)
+    torch.cuda.synchronize()
+    n = c.B * c.Hkv * pr.Q * c.max_pages
+    got = dec.ws[: 4 * n].view(torch.float32).reshape(c.B, c.Hkv, pr.Q, c.max_pages).cpu().numpy()
+    r = oracle.run(c, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                   want_scores=True)
+    G = c.Hq // c.Hkv
+    worst = 0.0
+    for b in range(c.B):
+        for kvh in range(c.Hkv):
+            kmax = max(float(np.abs(dense_keys_values(c, b, kvh)[0]).max()), 1.0)
+            for i in range(pr.Q):
+                ref = r.scores[b, kvh, i]
+                cand = ~np.isnan(ref)
+                qn = max(np.abs(query(pr, b, kvh * G + h, i)).sum() for h in range(G))
+                err = np.abs(got[b, kvh, i][cand].astype(np.float64) - ref[cand]) / (qn * kmax)
+                worst = max(worst, float(err.max()) if err.size else 0.0)
+    print(f"{name} {mode}: worst score error {worst:.2e} of |q|_1 max|k|")
+    assert worst <= SCORE_REL
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -1,6 +1,7 @@
 """End-to-end parity at the workloads' full sizes, in the launch configuration
 the benchmark times (the library's default split count): the tiny fp32
-case, the Qwen3-8B-shaped and Llama-3-70B-shaped layers, the 3-layer hybrid
+case, the Qwen3-8B-shaped and Llama-3-70B-shaped layers (the latter also with
+compressed-key scores), the 3-layer hybrid
 256k schedule (every refresh step and the last step) and the semantic-block
 512K chunk, paged and over a block index built from interleaved keys.  The
 oracle computes every output at these sizes (the index: its layout and the
@@ -31,7 +32,9 @@ def _say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("wl", [configs.TINY, configs.QWEN3_8B, configs.LLAMA3_70B, configs.SEMANTIC_512K],
+@pytest.mark.parametrize("wl", [configs.TINY, configs.QWEN3_8B, configs.LLAMA3_70B,
+                                configs.LLAMA3_70B.scaled(name="llama3-70b-layer-128k-compressed", mode="compressed"),
+                                configs.SEMANTIC_512K],
                          ids=lambda w: w.name)
 def test_single_step_workload(wl):
     t0 = time.time()
