@@ -66,14 +66,17 @@ def parse():
                     help="llama3-70b-layer-128k: page summary and score (compressed: mean keys of two-page "
                          "blocks with a one-page stride)")
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
-                    choices=["llama3-70b-layer-128k", "semantic-512k", "semantic-512k-index", "hybrid-3layer-256k"],
+                    choices=["llama3-70b-layer-128k", "semantic-512k", "semantic-512k-index", "hybrid-3layer-256k",
+                             "keydiff-llama3.1-8b-8k"],
                     help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
                          "semantic-512k-index: the same chunk over a semantic block index built from keys "
                          "interleaved in position order (index build, then block choice, grouped decode of the "
                          "blocks, combine); "
                          "hybrid-3layer-256k: the 128-step schedule of three layers (one token appended every step, "
                          "selection every 32 steps after summarising the pages appended since the last one, "
-                         "growing window between)")
+                         "growing window between); "
+                         "keydiff-llama3.1-8b-8k: KeyDiff eviction of a cache of 10240 tokens back to 8192 "
+                         "(distances to the mean key, top-k, compaction of the kept K/V rows)")
     return ap.parse_args()
 
 
@@ -337,6 +340,89 @@ def bench_semantic_index(args):
     }))
 
 
+def bench_keydiff(args):
+    """KeyDiff eviction of a Llama-3.1-8B-shaped layer (batch 8, 32 q / 8 KV
+    heads, bf16) whose cache holds an 8192-token budget plus one 2048-token
+    block: each step ranks every token of every (sequence, KV head) by the
+    distance of its key to the mean key, keeps the sink and the farthest
+    tokens up to the budget, and copies the kept K and V rows into the
+    evicted cache."""
+    import torch
+
+    from block_sparse_long_page_amd import binding as B, configs, synth
+    from block_sparse_long_page_amd.device import DeviceCache, KeyDiffEviction
+
+    wl = configs.KEYDIFF_8K
+    t0 = time.time()
+    pr = synth.workload_problem(wl)
+    c = pr.cache
+    log(f"inputs {time.time() - t0:.1f}s")
+    R = max(1, args.replicas)
+    pool = DeviceCache.from_host(c)
+    tables = replicate(pool, c, R)
+    dst = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, wl.budget, c.dtype)
+    evs = []
+    for r in range(R):
+        ev = KeyDiffEviction(pool, dst, wl.budget, wl.sink)
+        ev.src_desc = pool.desc(tables[r])
+        evs.append(ev)
+
+    def select(r):
+        evs[r].select()
+
+    def compact(r):
+        B.sparse_attn_keydiff_compact(evs[r].src_desc, evs[r].kept, evs[r].count, wl.budget, evs[r].dst_desc)
+
+    def step(r):
+        select(r)
+        compact(r)
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, K):
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K):
+            fn(i % R)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / K
+
+    for i in range(args.warmup):
+        step(i % R)
+    K = args.steps
+    ms = timed(step, K)
+    sel_ms = timed(select, K)
+    comp_ms = timed(compact, K)
+
+    nbk, L, row = c.B * c.Hkv, int(c.seq_lens[0]), c.hd * 2
+    kept_n = min(L, wl.budget)
+    nch = -(-pool.max_seq_len // 1024)
+    # keys once, the chunk sums written and read back by every distance
+    # workgroup, distances written and read, kept positions written; the copy
+    # reads the kept positions and the kept K and V rows and writes the rows
+    sel_bytes = nbk * (L * row + nch * c.hd * 4 * (1 + nch) + L * 4 * 2 + wl.budget * 4)
+    comp_bytes = nbk * (kept_n * 4 + kept_n * row * 2 * 2)
+    step_bytes = sel_bytes + comp_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    comp_gbs = comp_bytes / (comp_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "evicted-cache GB/s + us per eviction, 10240 -> 8192 tokens, Llama-3.1-8B-shaped layer",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2), "pct_hbm_peak": round(100 * gbs / 8000, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded): K from 64 Gaussian clusters with 4 needle pages per (b, kvh), V N(0,1)",
+        "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
+                   "cache_tokens": L, "budget": wl.budget, "block": wl.block, "sink": wl.sink, "page": c.P,
+                   "replicas": R, "step": "keydiff select (sums, distances, top-k) + compaction"},
+        "roofline": {"bound": "hbm", "kernel": "k_kd_compact", "achieved": round(comp_gbs, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(comp_gbs / 8000.0, 4), "traffic": None,
+                     "bytes_per_launch": comp_bytes, "avg_launch_us": round(comp_ms * 1e3, 2)},
+        "select_us": round(sel_ms * 1e3, 2), "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+        "bytes_per_step": step_bytes,
+    }))
+
+
 def bench_hybrid(args):
     """The hybrid model's three full-attention layers at 256k over 128 decode
     steps: every step appends a token to every sequence; steps 0, 32, 64, 96
@@ -463,6 +549,9 @@ def main():
         return
     if args.workload == "semantic-512k-index":
         bench_semantic_index(args)
+        return
+    if args.workload == "keydiff-llama3.1-8b-8k":
+        bench_keydiff(args)
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "combine.hip", "sparse_attn.cpp"]
+SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "keydiff.hip", "combine.hip", "sparse_attn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

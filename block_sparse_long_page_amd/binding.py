@@ -83,6 +83,9 @@ _SIGS = {
     "sparse_attn_blocks_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX]),
     "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                  _P, ctypes.c_size_t, _P]),
+    "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC]),
+    "sparse_attn_keydiff_select": (ctypes.c_int, [_DESC, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sparse_attn_keydiff_compact": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -209,6 +212,23 @@ def sparse_attn_select_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_ro
     _check(_lib.sparse_attn_select_blocks(ctypes.byref(kv), ctypes.byref(index), _ptr(q), num_q_rows, token_budget,
                                           k_max, _ptr(sel_blocks), _ptr(sel_count), _stream(stream)),
            "sparse_attn_select_blocks")
+
+
+def sparse_attn_keydiff_workspace_bytes(kv: sa_kv_desc) -> int:
+    return int(_lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(kv)))
+
+
+def sparse_attn_keydiff_select(kv: sa_kv_desc, sink_len: int, budget: int, kept, kept_count, workspace,
+                               workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sparse_attn_keydiff_select(ctypes.byref(kv), sink_len, budget, _ptr(kept), _ptr(kept_count),
+                                           _ptr(workspace), workspace_bytes, _stream(stream)),
+           "sparse_attn_keydiff_select")
+
+
+def sparse_attn_keydiff_compact(src: sa_kv_desc, kept, kept_count, budget: int, dst: sa_kv_desc,
+                                stream=None) -> None:
+    _check(_lib.sparse_attn_keydiff_compact(ctypes.byref(src), _ptr(kept), _ptr(kept_count), budget,
+                                            ctypes.byref(dst), _stream(stream)), "sparse_attn_keydiff_compact")
 
 
 def sparse_attn_blocks_workspace_bytes(kv: sa_kv_desc, index: sa_block_index) -> int:

@@ -50,6 +50,7 @@ class Workload:
     layers: Tuple[Layer, ...] = field(default_factory=tuple)  # multi-layer schedule
     steps: int = 0  # decode steps (multi-layer schedule)
     refresh: int = 0  # re-select every `refresh` steps (multi-layer schedule)
+    block: int = 0  # tokens appended between two evictions (eviction workload)
 
     @property
     def group(self) -> int:
@@ -100,5 +101,12 @@ SEMANTIC_512K = Workload(
     q_rows=64, seed=4,
 )
 
-ALL = (TINY, QWEN3_8B, LLAMA3_70B, HYBRID_256K, SEMANTIC_512K)
+# KeyDiff eviction: a Llama-3.1-8B-shaped layer whose cache holds an 8K-token
+# budget plus one 2048-token block, evicted back to the budget (sink of 4)
+KEYDIFF_8K = Workload(
+    name="keydiff-llama3.1-8b-8k", batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+    context=8192 + 2048, page_size=16, sink=4, window=1, budget=8192, seed=5, block=2048,
+)
+
+ALL = (TINY, QWEN3_8B, LLAMA3_70B, HYBRID_256K, SEMANTIC_512K, KEYDIFF_8K)
 BY_NAME = {w.name: w for w in ALL}

@@ -159,6 +159,29 @@ struct SelectBlocksArgs {
     int32_t* count;          // [B][Hkv][Q]
 };
 
+// KeyDiff eviction of a cache back to a token budget (distance of each key to
+// the mean key; the sink is kept)
+constexpr int kKdChunk = 1024;     // tokens per workgroup of the sum and distance passes
+constexpr int kKdMaxCand = 12288;  // candidates the top-k workgroup holds in LDS
+
+struct KeydiffArgs {
+    Geometry g;
+    int T;             // token stride of the distance rows (the descriptor's max_seq_len)
+    int sink, budget;
+    int nchunks;       // ceil(T / kKdChunk)
+    float* partial;    // [B][Hkv][nchunks][hd] fp32 key sums of each chunk
+    float* dist;       // [B][Hkv][T] squared distances to the mean key
+    int32_t* kept;     // [B][Hkv][budget] kept positions ascending, -1 after the count
+    int32_t* count;    // [B][Hkv]
+};
+
+struct CompactArgs {
+    Geometry src, dst;
+    int budget;
+    const int32_t* kept;
+    const int32_t* count;
+};
+
 struct CombineArgs {
     int rows, hd, splits, out_dtype;
     const float* part_o;
@@ -181,5 +204,8 @@ hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
 // the whole index build (every kernel of every iteration)
 hipError_t launch_index_build(const IndexArgs& a, hipStream_t s);
 hipError_t launch_select_blocks(const SelectBlocksArgs& a, hipStream_t s);
+// key sums, distances and the kept positions
+hipError_t launch_keydiff_select(const KeydiffArgs& a, hipStream_t s);
+hipError_t launch_keydiff_compact(const CompactArgs& a, hipStream_t s);
 
 }  // namespace sa

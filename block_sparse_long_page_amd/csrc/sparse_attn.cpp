@@ -94,6 +94,24 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
     return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
 }
 
+// workspace of the KeyDiff selection: the chunk key sums, then the
+// distances, each 256-byte aligned
+struct KeydiffWs {
+    int nchunks;
+    size_t partial, dist, total;
+};
+KeydiffWs keydiff_ws(const sa_kv_desc* kv)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
+    KeydiffWs w;
+    w.nchunks = (kv->max_seq_len + sa::kKdChunk - 1) / sa::kKdChunk;
+    w.partial = 0;
+    w.dist = up(bh * (size_t)w.nchunks * kv->head_dim * sizeof(float));
+    w.total = up(w.dist + bh * (size_t)kv->max_seq_len * sizeof(float));
+    return w;
+}
+
 // workspace of the grouped decode: byte offsets of its three arrays, each
 // 256-byte aligned
 struct GroupedWs {
@@ -470,6 +488,49 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
     return grouped_impl(kv, g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, softmax_scale,
                         token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes,
                         kv->max_pages_per_seq, nullptr, nullptr, nullptr, 0, stream);
+}
+
+size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv)
+{
+    sa::Geometry g;
+    if (check_kv(kv, &g) != SA_OK) return 0;
+    return keydiff_ws(kv).total;
+}
+
+int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
+                               int32_t* kept_count, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!kept || !kept_count || sink_len < 0 || budget < 1 || budget < sink_len) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    // the top-k workgroup holds every candidate's key in LDS
+    if (kv->max_seq_len > budget && (long)kv->max_seq_len - sink_len > sa::kKdMaxCand) return SA_ERR_UNSUPPORTED;
+    const KeydiffWs w = keydiff_ws(kv);
+    if (!workspace || workspace_bytes < w.total) return SA_ERR_INVALID_ARG;
+    char* base = (char*)workspace;
+    sa::KeydiffArgs a{g,         kv->max_seq_len, sink_len, budget, w.nchunks, (float*)(base + w.partial),
+                      (float*)(base + w.dist), kept, kept_count};
+    return finish(sa::launch_keydiff_select(a, stream), stream);
+}
+
+int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
+                                int32_t budget, const sa_kv_desc* dst, hipStream_t stream)
+{
+    sa::Geometry gs, gd;
+    const int rs = check_kv(src, &gs);
+    if (rs != SA_OK) return rs;
+    const int rd = check_kv(dst, &gd);
+    if (rd != SA_OK) return rd;
+    if (!kept || !kept_count || budget < 1) return SA_ERR_INVALID_ARG;
+    if (dst->batch != src->batch || dst->num_kv_heads != src->num_kv_heads || dst->head_dim != src->head_dim ||
+        dst->dtype != src->dtype)
+        return SA_ERR_INVALID_ARG;
+    if ((long)dst->max_pages_per_seq * dst->page_size < budget) return SA_ERR_INVALID_ARG;
+    if ((long)src->batch * src->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    sa::CompactArgs a{gs, gd, budget, kept, kept_count};
+    return finish(sa::launch_keydiff_compact(a, stream), stream);
 }
 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,

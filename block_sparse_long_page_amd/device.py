@@ -48,6 +48,17 @@ class DeviceCache:
                    to_device(c.v, device), to_device(c.block_table.astype(np.int32), device),
                    to_device(c.seq_lens.astype(np.int32), device), msl)
 
+    @classmethod
+    def empty(cls, B_: int, Hq: int, Hkv: int, hd: int, P: int, tokens: int, dtype: int,
+              device="cuda") -> "DeviceCache":
+        """A cache of `tokens` token slots per sequence, pages laid out in
+        order (sequence b owns physical pages b*n .. b*n+n-1), lengths 0."""
+        n = -(-tokens // P)
+        k = torch.zeros((B_ * n, Hkv, P, hd), dtype=_TORCH_ELEM[dtype], device=device)
+        bt = torch.arange(B_ * n, dtype=torch.int32, device=device).reshape(B_, n)
+        return cls(B_, Hq, Hkv, hd, P, n, B_ * n, dtype, k, torch.zeros_like(k), bt,
+                   torch.zeros(B_, dtype=torch.int32, device=device), n * P)
+
     def desc(self, block_table: Optional[torch.Tensor] = None) -> B.sa_kv_desc:
         return B.make_kv_desc(batch=self.B, num_q_heads=self.Hq, num_kv_heads=self.Hkv, head_dim=self.hd,
                                page_size=self.P, max_pages_per_seq=self.max_pages, num_phys_pages=self.num_phys,
@@ -306,3 +317,38 @@ class BlockIndex:
 
     def lse_f32(self) -> np.ndarray:
         return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)
+
+
+class KeyDiffEviction:
+    """KeyDiff eviction of a DeviceCache to a token budget: the kept tokens of
+    every (sequence, KV head) (sparse_attn_keydiff_select) and their K and V
+    rows copied, in order, into `dst` (sparse_attn_keydiff_compact), whose
+    lengths are then set to the kept counts."""
+
+    def __init__(self, src: DeviceCache, dst: DeviceCache, budget: int, sink: int):
+        self.src, self.dst, self.budget, self.sink = src, dst, budget, sink
+        dev = src.k.device
+        self.kept = torch.full((src.B, src.Hkv, budget), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((src.B, src.Hkv), dtype=torch.int32, device=dev)
+        self.src_desc, self.dst_desc = src.desc(), dst.desc()
+        self.ws_bytes = B.sparse_attn_keydiff_workspace_bytes(self.src_desc)
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+
+    def select(self, stream=None):
+        B.sparse_attn_keydiff_select(self.src_desc, self.sink, self.budget, self.kept, self.count, self.ws,
+                                     self.ws_bytes, stream)
+
+    def compact(self, stream=None):
+        B.sparse_attn_keydiff_compact(self.src_desc, self.kept, self.count, self.budget, self.dst_desc, stream)
+        # every KV head keeps min(L, budget) tokens: the first head's count is the sequence's
+        self.dst.seq_lens.copy_(self.count[:, 0])
+
+    def evict(self, stream=None):
+        self.select(stream)
+        self.compact(stream)
+
+    def kept_positions(self):
+        """[b][kvh] -> numpy array of the kept positions."""
+        kept, cnt = self.kept.cpu().numpy(), self.count.cpu().numpy()
+        return [[kept[b, h, : cnt[b, h]] for h in range(kept.shape[1])] for b in range(kept.shape[0])]
+

@@ -281,6 +281,8 @@ def workload_problem(wl: Workload, *, seed: Optional[int] = None, batch: Optiona
         return random_problem(**common, needles_per_head=4, outlier_channels=4, outlier_scale=8.0)
     if wl.name.startswith("llama3"):
         return random_problem(**common, clusters=64, cluster_noise=0.5)
+    if wl.name.startswith("keydiff"):
+        return random_problem(**common, clusters=64, cluster_noise=0.5, needles_per_head=4)
     if wl.name.startswith("semantic"):
         return semantic_problem(wl, seed=seed, batch=B)
     raise ValueError(f"no single-layer generator for {wl.name}")

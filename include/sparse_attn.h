@@ -25,6 +25,14 @@
  *   sparse_attn_decode_blocks      grouped decode over the chosen blocks plus
  *                                  the window of recent tokens
  *
+ * and, for KeyDiff eviction (course module 14, section 14.4: tokens whose
+ * keys lie closest to the mean key are evicted, the sink never, blockwise so
+ * the cache never exceeds its budget by more than a block):
+ *
+ *   sparse_attn_keydiff_select     the tokens each (sequence, KV head) keeps
+ *   sparse_attn_keydiff_compact    their K and V rows, in order, into a cache
+ *                                  of the budget's size
+ *
  * sparse_attn_decode_step runs select and decode of a selecting step with the
  * top-k inside the decode kernel (two launches instead of three).
  *
@@ -397,6 +405,51 @@ int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index,
                               const int32_t* sel_blocks, const int32_t* sel_count, int32_t k_max, int32_t window_len,
                               float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
                               float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of sparse_attn_keydiff_select (host only; 0 for a bad descriptor). */
+size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv);
+
+/*
+ * KeyDiff eviction, the choice (course module 14, section 14.4 and exercise
+ * 14.2: importance of a token = how far its key lies from the mean key of the
+ * tokens the cache holds; the least distinctive are evicted; the first
+ * positions are never evicted).
+ *
+ * For every sequence b and KV head, over the tokens [0, L_b) the cache holds:
+ * m = the mean key (fp32 sums), d_t = |k_t - m|^2 (fp32).  When L_b <= budget
+ * every token is kept.  Otherwise the positions [0, min(sink_len, L_b)) and
+ * the budget - sink_len others with the largest d_t are kept; among equal
+ * distances the later position is kept (the earlier is evicted first).  One
+ * call evicts down to the budget at once (the mean is the whole cache's).
+ *   kept        int32 [batch][num_kv_heads][budget]: kept positions ascending,
+ *               -1 after the count.
+ *   kept_count  int32 [batch][num_kv_heads]: min(L_b, budget).
+ *   workspace   device scratch of sparse_attn_keydiff_workspace_bytes(kv).
+ * Called after each block of new tokens, this keeps a cache within budget +
+ * block tokens.  A token whose page is unmapped counts as a zero key.
+ * Errors: null pointers, sink_len < 0, budget < 1 or < sink_len, workspace
+ * too small; SA_ERR_UNSUPPORTED when max_seq_len > budget and
+ * max_seq_len - sink_len > 12288 (the candidates of one (sequence, KV head)
+ * are ranked in one workgroup's LDS) or batch * num_kv_heads > 65535.
+ */
+int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
+                               int32_t* kept_count, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * KeyDiff eviction, the copy: the K and V rows of the kept positions of
+ * every (sequence, KV head), in order, into slots 0 .. kept_count-1 of the
+ * same sequence and KV head in `dst` (the evicted cache is physically
+ * shorter).  src and dst share batch, num_kv_heads, head_dim and dtype; dst
+ * holds at least `budget` tokens per sequence (max_pages_per_seq *
+ * page_size); its page size may differ.  dst's pages must not overlap the
+ * pages src reads (rows are copied by many workgroups at once).  The caller
+ * sets dst's seq_lens to kept_count.  Kept positions outside src's pages or
+ * on unmapped pages, and unmapped dst pages, are skipped.
+ * Errors: null pointers, mismatched descriptors, budget < 1 or above dst's
+ * capacity.
+ */
+int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
+                                int32_t budget, const sa_kv_desc* dst, hipStream_t stream);
 
 /* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,

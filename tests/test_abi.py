@@ -25,7 +25,8 @@ def test_exports_every_header_function():
         "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string",
         "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes", "sparse_attn_index_workspace_bytes",
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
-        "sparse_attn_decode_blocks"}
+        "sparse_attn_decode_blocks", "sparse_attn_keydiff_workspace_bytes", "sparse_attn_keydiff_select",
+        "sparse_attn_keydiff_compact"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -349,3 +350,54 @@ def test_block_index_checks():
     assert decode(ts=0) == B.SA_ERR_INVALID_ARG
     assert decode(po=None) == B.SA_ERR_INVALID_ARG
     assert decode(rows=65, W=65) == B.SA_ERR_UNSUPPORTED
+
+
+def test_keydiff_checks():
+    lib = B.library()
+    d = _desc()
+    ws = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d))
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # chunk key sums (1 chunk of 1024 tokens), then the distances
+    assert ws == up(2 * 2 * 1 * 128 * 4) + up(2 * 2 * 128 * 4)
+    assert lib.sparse_attn_keydiff_workspace_bytes(None) == 0
+
+    def sel(**kw):
+        a = dict(desc=d, sink=4, budget=64, kept=DEV, cnt=DEV, ws=DEV, wsb=ws)
+        a.update(kw)
+        return lib.sparse_attn_keydiff_select(ctypes.byref(a["desc"]), a["sink"], a["budget"], a["kept"], a["cnt"],
+                                              a["ws"], a["wsb"], None)
+
+    assert sel(kept=None) == B.SA_ERR_INVALID_ARG
+    assert sel(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert sel(ws=None) == B.SA_ERR_INVALID_ARG
+    assert sel(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert sel(sink=-1) == B.SA_ERR_INVALID_ARG
+    assert sel(budget=0) == B.SA_ERR_INVALID_ARG
+    assert sel(budget=3) == B.SA_ERR_INVALID_ARG  # below the sink
+    big = _desc(max_seq_len=16384, max_pages_per_seq=1024, num_phys_pages=2048)
+    wsb = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(big))
+    assert sel(desc=big, wsb=wsb, budget=2048, sink=4) == B.SA_ERR_UNSUPPORTED  # 16380 candidates
+    for bad, code in BAD_DESCS:
+        assert sel(desc=_desc(**bad)) == code
+
+    def comp(**kw):
+        a = dict(src=d, dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64), kept=DEV, cnt=DEV,
+                 budget=64)
+        a.update(kw)
+        return lib.sparse_attn_keydiff_compact(ctypes.byref(a["src"]), a["kept"], a["cnt"], a["budget"],
+                                               ctypes.byref(a["dst"]), None)
+
+    assert comp(kept=None) == B.SA_ERR_INVALID_ARG
+    assert comp(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert comp(budget=0) == B.SA_ERR_INVALID_ARG
+    assert comp(budget=65) == B.SA_ERR_INVALID_ARG  # beyond the destination's 64 slots
+    assert comp(dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64, head_dim=64)) == B.SA_ERR_INVALID_ARG
+    assert comp(dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64, dtype=B.SA_F32)) == \
+        B.SA_ERR_INVALID_ARG
+    assert comp(dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64, batch=3)) == B.SA_ERR_INVALID_ARG
+    assert comp(dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64, num_kv_heads=4)) == \
+        B.SA_ERR_INVALID_ARG
+    for bad, code in BAD_DESCS:
+        assert comp(src=_desc(**bad)) == code
+        assert comp(dst=_desc(**bad)) == code
+
