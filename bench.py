@@ -397,7 +397,7 @@ def bench_keydiff(args):
 
     nbk, L, row = c.B * c.Hkv, int(c.seq_lens[0]), c.hd * 2
     kept_n = min(L, wl.budget)
-    nch = -(-pool.max_seq_len // 1024)
+    nch = -(-pool.max_seq_len // 512)  # chunks of 512 tokens
     # keys once, the chunk sums written and read back by every distance
     # workgroup, distances written and read, kept positions written; the copy
     # reads the kept positions and the kept K and V rows and writes the rows

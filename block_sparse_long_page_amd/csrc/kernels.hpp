@@ -161,7 +161,7 @@ struct SelectBlocksArgs {
 
 // KeyDiff eviction of a cache back to a token budget (distance of each key to
 // the mean key; the sink is kept)
-constexpr int kKdChunk = 1024;     // tokens per workgroup of the sum and distance passes
+constexpr int kKdChunk = 512;      // tokens per workgroup of the sum and distance passes
 constexpr int kKdMaxCand = 12288;  // candidates the top-k workgroup holds in LDS
 
 struct KeydiffArgs {

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kKdWaves = 4;
 constexpr int kKdRowsPerWave = kKdChunk / kKdWaves;
-constexpr int kKdU = 8;             // row loads per lane in flight
+constexpr int kKdU = 16;            // row loads per lane in flight
 constexpr int kKdSlots = 64;        // destination slots per compaction workgroup
 constexpr int kKdCopyThreads = 256;
 

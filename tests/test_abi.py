@@ -357,7 +357,7 @@ def test_keydiff_checks():
     d = _desc()
     ws = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d))
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # chunk key sums (1 chunk of 1024 tokens), then the distances
+    # chunk key sums (one chunk), then the distances
     assert ws == up(2 * 2 * 1 * 128 * 4) + up(2 * 2 * 128 * 4)
     assert lib.sparse_attn_keydiff_workspace_bytes(None) == 0
 
