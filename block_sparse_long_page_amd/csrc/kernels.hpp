@@ -166,11 +166,13 @@ constexpr int kKdMaxCand = 12288;  // candidates the top-k workgroup holds in LD
 
 struct KeydiffArgs {
     Geometry g;
-    int T;             // token stride of the distance rows (the descriptor's max_seq_len)
+    int T;             // longest sequence (the descriptor's max_seq_len)
+    int Tk;            // row stride of okeys: T rounded up to a multiple of 4
     int sink, budget;
     int nchunks;       // ceil(T / kKdChunk)
     float* partial;    // [B][Hkv][nchunks][hd] fp32 key sums of each chunk
-    float* dist;       // [B][Hkv][T] squared distances to the mean key
+    uint32_t* okeys;   // [B][Hkv][Tk] order keys of the squared distances to the mean
+                       // key, position t at index L-1-t (the candidates come first)
     int32_t* kept;     // [B][Hkv][budget] kept positions ascending, -1 after the count
     int32_t* count;    // [B][Hkv]
 };

@@ -8,7 +8,8 @@
 //    of the keys (rows in order in each lane, then lanes and waves in a fixed
 //    order: bitwise reproducible).
 //  * k_kd_dist: every workgroup rebuilds the mean key from the chunk sums, in
-//    chunk order, and writes each of its tokens' squared distance to it.
+//    chunk order, and writes the order key of each candidate's squared
+//    distance to it, candidates in reverse position order.
 //  * k_kd_topk: one workgroup per (sequence, KV head) keeps the sink and the
 //    budget - sink farthest other tokens.  Among equal distances the later
 //    position is kept: the candidates are ranked in reverse position order
@@ -83,8 +84,8 @@ struct KdLayout {
 };
 
 // Streams rows [r0, r1) of (b, kvh), kKdU loads per lane in flight, calling
-// f(row, x) for every valid row with this lane's CH channels; unmapped rows
-// are skipped.
+// f(row, x) with this lane's CH channels of each row; rows past r1 and rows
+// on unmapped pages read as zeros (a zero key).
 template <int HD, bool BF, typename F>
 __device__ __forceinline__ void kd_stream(const Geometry& g, const FastDiv& pdiv, int b, int kvh, int r0, int r1, F f)
 {
@@ -98,15 +99,13 @@ __device__ __forceinline__ void kd_stream(const Geometry& g, const FastDiv& pdiv
     wp.init(g.block_table + (long)b * g.max_pages, pg0, pdiv.div(r1 - 1) - pg0 + 1, g.num_phys);
     for (int base = r0; base < r1; base += Lay::RPW * kKdU) {
         uint4 w[kKdU];
-        bool ok[kKdU];
 #pragma unroll
         for (int u = 0; u < kKdU; ++u) {
             const int t = base + u * Lay::RPW + rg;
             const int page = pdiv.div(imin(t, r1 - 1));
             const int ph = wp.phys(page);  // every lane takes part in the exchange
-            ok[u] = t < r1 && ph >= 0;
             w[u] = make_uint4(0, 0, 0, 0);
-            if (ok[u])
+            if (t < r1 && ph >= 0)
                 w[u] = *(const uint4*)((const E*)g.k + (((long)ph * g.Hkv + kvh) * g.P + (t - page * g.P)) * HD +
                                        sub * Lay::CH);
         }
@@ -114,7 +113,7 @@ __device__ __forceinline__ void kd_stream(const Geometry& g, const FastDiv& pdiv
         for (int u = 0; u < kKdU; ++u) {
             float x[Lay::CH];
             Lay::unpack(w[u], x);
-            f(base + u * Lay::RPW + rg, ok[u], x);
+            f(base + u * Lay::RPW + rg, x);
         }
     }
 }
@@ -137,10 +136,9 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_sum(KeydiffArgs a)
     float acc[Lay::CH];
 #pragma unroll
     for (int c = 0; c < Lay::CH; ++c) acc[c] = 0.f;
-    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int, bool ok, const float (&x)[Lay::CH]) {
-        if (ok)
+    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int, const float (&x)[Lay::CH]) {
 #pragma unroll
-            for (int c = 0; c < Lay::CH; ++c) acc[c] += x[c];
+        for (int c = 0; c < Lay::CH; ++c) acc[c] += x[c];
     });
     // the wave's row groups, then the waves, in a fixed order
 #pragma unroll
@@ -183,16 +181,17 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_dist(KeydiffArgs a)
 #pragma unroll
     for (int c = 0; c < Lay::CH; ++c) m[c] = mean[sub * Lay::CH + c];
     const int r0 = imin(L, t0 + wave * kKdRowsPerWave), r1 = imin(L, r0 + kKdRowsPerWave);
-    float* dist = a.dist + (long)bh * a.T;
-    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int t, bool ok, const float (&x)[Lay::CH]) {
+    // token t goes to index L-1-t (the sink's indices, past the candidates, are never read)
+    uint32_t* okeys = a.okeys + (long)bh * a.Tk + (L - 1);
+    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int t, const float (&x)[Lay::CH]) {
         float d = 0.f;
 #pragma unroll
         for (int c = 0; c < Lay::CH; ++c) {
-            const float e = (ok ? x[c] : 0.f) - m[c];  // an unmapped row counts as a zero key
+            const float e = x[c] - m[c];
             d = fmaf(e, e, d);
         }
         d = group_sum<Lay::LPT>(d);
-        if (sub == 0 && t < r1) dist[t] = d;
+        if (sub == 0 && t < r1) okeys[-t] = order_key(d);
     });
 }
 
@@ -217,14 +216,32 @@ __global__ __launch_bounds__(kTopkThreads) void k_kd_topk(KeydiffArgs a)
     const int k = a.budget - s0;
     const int m = imin(L - s0, kKdMaxCand);  // the host keeps max_seq_len - sink within the limit
     if (k <= 0 || k >= m) return;
-    // candidate j is position L-1-j: later positions get lower indices
-    const float* d = a.dist + (long)bh * a.T;
+    // candidate j is position L-1-j: later positions get lower indices.  Every
+    // thread's 16-byte loads are in flight together (rows are 16-byte aligned
+    // and padded to a multiple of 4; keys past m are not used).
+    constexpr int NV = kKdMaxCand / (4 * kTopkThreads);
+    static_assert(NV * 4 * kTopkThreads == kKdMaxCand, "16-byte loads tile the candidates");
+    const uint32_t* src = a.okeys + (long)bh * a.Tk;
+    uint4 w[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int j = 4 * (i * kTopkThreads + tid);
+        w[i] = j < m ? *(const uint4*)(src + j) : make_uint4(0, 0, 0, 0);
+    }
     uint32_t lo = 0xffffffffu, hi = 0;
-    for (int j = tid; j < m; j += kTopkThreads) {
-        const uint32_t key = order_key(d[L - 1 - j]);
-        keys[j] = key;
-        lo = min(lo, key);
-        hi = max(hi, key);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int j = 4 * (i * kTopkThreads + tid);
+        if (j < m) {
+            *(uint4*)(keys + j) = w[i];
+            const uint32_t* v = (const uint32_t*)&w[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < m) {
+                    lo = min(lo, v[e]);
+                    hi = max(hi, v[e]);
+                }
+        }
     }
     block_topk_fast(m, k, keys, lo, hi, sh, [&](int pos, int j) { kept[s0 + (k - 1 - pos)] = L - 1 - j; });
 }

@@ -94,11 +94,12 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
     return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
 }
 
-// workspace of the KeyDiff selection: the chunk key sums, then the
-// distances, each 256-byte aligned
+// workspace of the KeyDiff selection: the chunk key sums, then the order
+// keys of the distances (rows padded to a multiple of 4), each 256-byte
+// aligned
 struct KeydiffWs {
-    int nchunks;
-    size_t partial, dist, total;
+    int nchunks, Tk;
+    size_t partial, okeys, total;
 };
 KeydiffWs keydiff_ws(const sa_kv_desc* kv)
 {
@@ -106,9 +107,10 @@ KeydiffWs keydiff_ws(const sa_kv_desc* kv)
     const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
     KeydiffWs w;
     w.nchunks = (kv->max_seq_len + sa::kKdChunk - 1) / sa::kKdChunk;
+    w.Tk = (kv->max_seq_len + 3) & ~3;
     w.partial = 0;
-    w.dist = up(bh * (size_t)w.nchunks * kv->head_dim * sizeof(float));
-    w.total = up(w.dist + bh * (size_t)kv->max_seq_len * sizeof(float));
+    w.okeys = up(bh * (size_t)w.nchunks * kv->head_dim * sizeof(float));
+    w.total = up(w.okeys + bh * (size_t)w.Tk * sizeof(uint32_t));
     return w;
 }
 
@@ -508,10 +510,11 @@ int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t b
     // the top-k workgroup holds every candidate's key in LDS
     if (kv->max_seq_len > budget && (long)kv->max_seq_len - sink_len > sa::kKdMaxCand) return SA_ERR_UNSUPPORTED;
     const KeydiffWs w = keydiff_ws(kv);
-    if (!workspace || workspace_bytes < w.total) return SA_ERR_INVALID_ARG;
+    // the top-k reads the order keys as 16-byte vectors
+    if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 15) != 0) return SA_ERR_INVALID_ARG;
     char* base = (char*)workspace;
-    sa::KeydiffArgs a{g,         kv->max_seq_len, sink_len, budget, w.nchunks, (float*)(base + w.partial),
-                      (float*)(base + w.dist), kept, kept_count};
+    sa::KeydiffArgs a{g,         kv->max_seq_len, w.Tk, sink_len, budget, w.nchunks, (float*)(base + w.partial),
+                      (uint32_t*)(base + w.okeys), kept, kept_count};
     return finish(sa::launch_keydiff_select(a, stream), stream);
 }
 

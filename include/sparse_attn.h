@@ -424,11 +424,12 @@ size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv);
  *   kept        int32 [batch][num_kv_heads][budget]: kept positions ascending,
  *               -1 after the count.
  *   kept_count  int32 [batch][num_kv_heads]: min(L_b, budget).
- *   workspace   device scratch of sparse_attn_keydiff_workspace_bytes(kv).
+ *   workspace   device scratch of sparse_attn_keydiff_workspace_bytes(kv),
+ *               16-byte aligned.
  * Called after each block of new tokens, this keeps a cache within budget +
  * block tokens.  A token whose page is unmapped counts as a zero key.
  * Errors: null pointers, sink_len < 0, budget < 1 or < sink_len, workspace
- * too small; SA_ERR_UNSUPPORTED when max_seq_len > budget and
+ * too small or misaligned; SA_ERR_UNSUPPORTED when max_seq_len > budget and
  * max_seq_len - sink_len > 12288 (the candidates of one (sequence, KV head)
  * are ranked in one workgroup's LDS) or batch * num_kv_heads > 65535.
  */

@@ -371,6 +371,7 @@ def test_keydiff_checks():
     assert sel(cnt=None) == B.SA_ERR_INVALID_ARG
     assert sel(ws=None) == B.SA_ERR_INVALID_ARG
     assert sel(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert sel(ws=DEV + 8) == B.SA_ERR_INVALID_ARG  # read as 16-byte vectors
     assert sel(sink=-1) == B.SA_ERR_INVALID_ARG
     assert sel(budget=0) == B.SA_ERR_INVALID_ARG
     assert sel(budget=3) == B.SA_ERR_INVALID_ARG  # below the sink
