@@ -398,10 +398,10 @@ def bench_keydiff(args):
     nbk, L, row = c.B * c.Hkv, int(c.seq_lens[0]), c.hd * 2
     kept_n = min(L, wl.budget)
     nch = -(-pool.max_seq_len // 512)  # chunks of 512 tokens
-    # keys once, the chunk sums written and read back by every distance
-    # workgroup, distances written and read, kept positions written; the copy
-    # reads the kept positions and the kept K and V rows and writes the rows
-    sel_bytes = nbk * (L * row + nch * c.hd * 4 * (1 + nch) + L * 4 * 2 + wl.budget * 4)
+    # keys once, the chunk sums written and read once, the distances' order
+    # keys written and read, kept positions written; the copy reads the kept
+    # positions and the kept K and V rows and writes the rows
+    sel_bytes = nbk * (L * row + nch * c.hd * 4 * 2 + L * 4 * 2 + wl.budget * 4)
     comp_bytes = nbk * (kept_n * 4 + kept_n * row * 2 * 2)
     step_bytes = sel_bytes + comp_bytes
     gbs = step_bytes / (ms * 1e-3) / 1e9
