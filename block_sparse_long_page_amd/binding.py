@@ -57,7 +57,7 @@ class sa_block_index(ctypes.Structure):
     _fields_ = [
         ("num_tokens", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("offsets", ctypes.c_void_p),
         ("positions", ctypes.c_void_p), ("centres", ctypes.c_void_p), ("k_blocks", ctypes.c_void_p),
-        ("v_blocks", ctypes.c_void_p),
+        ("v_blocks", ctypes.c_void_p), ("visible_end", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +81,7 @@ _SIGS = {
     "sparse_attn_build_block_index": (ctypes.c_int, [_DESC, _I, _IDX, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_select_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _P, _P, _P]),
     "sparse_attn_blocks_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX]),
+    "sparse_attn_blocks_visible": (ctypes.c_int, [_DESC, _IDX, _I, _P, _P]),
     "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                  _P, ctypes.c_size_t, _P]),
     "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC]),
@@ -191,9 +192,10 @@ def sparse_attn_grouped_workspace_bytes(kv: sa_kv_desc) -> int:
     return int(_lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(kv)))
 
 
-def make_block_index(*, num_tokens, num_blocks, offsets, positions, centres, k_blocks, v_blocks) -> sa_block_index:
+def make_block_index(*, num_tokens, num_blocks, offsets, positions, centres, k_blocks, v_blocks,
+                     visible_end=None) -> sa_block_index:
     return sa_block_index(num_tokens, num_blocks, _ptr(offsets), _ptr(positions), _ptr(centres), _ptr(k_blocks),
-                          _ptr(v_blocks))
+                          _ptr(v_blocks), _ptr(visible_end))
 
 
 def sparse_attn_index_workspace_bytes(kv: sa_kv_desc, num_tokens: int, num_blocks: int) -> int:
@@ -229,6 +231,12 @@ def sparse_attn_keydiff_compact(src: sa_kv_desc, kept, kept_count, budget: int, 
                                 stream=None) -> None:
     _check(_lib.sparse_attn_keydiff_compact(ctypes.byref(src), _ptr(kept), _ptr(kept_count), budget,
                                             ctypes.byref(dst), _stream(stream)), "sparse_attn_keydiff_compact")
+
+
+def sparse_attn_blocks_visible(kv: sa_kv_desc, index: sa_block_index, window_len: int, visible_end,
+                               stream=None) -> None:
+    _check(_lib.sparse_attn_blocks_visible(ctypes.byref(kv), ctypes.byref(index), window_len, _ptr(visible_end),
+                                           _stream(stream)), "sparse_attn_blocks_visible")
 
 
 def sparse_attn_blocks_workspace_bytes(kv: sa_kv_desc, index: sa_block_index) -> int:

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         int ntok;
         if (a.blk_off) {
             const int32_t* bo = a.blk_off + (long)bk * (npg + 1);
-            ntok = bo[p + 1] - bo[p];
+            const int end = a.blk_end ? imax(bo[p], imin(a.blk_end[(long)bk * npg + p], bo[p + 1])) : bo[p + 1];
+            ntok = end - bo[p];
         } else {
             ntok = imin((p + 1) * g.P, rg.ws) - imax(p * g.P, rg.se);
         }
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     if (blocks) {
         const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
         a0 = bo[p];
-        a1 = bo[p + 1];
+        a1 = a.blk_end ? imax(a0, imin(a.blk_end[(long)bk * a.npg + p], bo[p + 1])) : bo[p + 1];
     } else {
         a0 = imax(p * g.P, rg.se);
         a1 = imin((p + 1) * g.P, rg.ws);

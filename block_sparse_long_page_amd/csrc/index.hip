@@ -509,6 +509,8 @@ __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
 
     // scores: a thread per block, channels in order for every head
     const int32_t* off = a.offsets + (long)bk * (a.C + 1);
+    const int32_t* ends = a.ends ? a.ends + (long)bk * a.C : nullptr;
+    auto end_of = [&](int c) { return ends ? imax(off[c], imin(ends[c], off[c + 1])) : off[c + 1]; };
     for (int c = threadIdx.x; c < a.C; c += 256) {
         const float4* mu = (const float4*)(a.centres + ((long)bk * a.C + c) * HD);
         float dot[G];
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
         float best = dot[0];
 #pragma unroll
         for (int h = 1; h < G; ++h) best = fmaxf(best, dot[h]);
-        if (off[c + 1] > off[c])  // blocks without tokens are never taken
+        if (end_of(c) > off[c])  // blocks without (visible) tokens are never taken
             key[c] = ((unsigned long long)order_key(best) << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
     }
     __syncthreads();
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
     auto size_at = [&](int i) {
         const unsigned long long k = i < n ? key[i] : 0ull;
         const int c = (int)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
-        return k != 0ull ? off[c + 1] - off[c] : 0;
+        return k != 0ull ? end_of(c) - off[c] : 0;
     };
     int mine = 0;
     for (int u = 0; u < per; ++u) mine += size_at(per * (int)threadIdx.x + u);
@@ -589,7 +591,38 @@ __global__ __launch_bounds__(256) void k_select_blocks(SelectBlocksArgs a)
     if (threadIdx.x == 0) a.count[prob] = count;
 }
 
+// A thread per (sequence, KV head, block): the first row of the block whose
+// position is at or after L - W (binary search; positions ascend in a block).
+__global__ __launch_bounds__(256) void k_blocks_visible(VisibleArgs a)
+{
+    const Geometry& g = a.g;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)g.B * g.Hkv * a.C) return;
+    const int bk = (int)(idx / a.C), c = (int)(idx - (long)bk * a.C);
+    const int b = bk / g.Hkv;
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int bound = L - a.W;
+    const int32_t* off = a.offsets + (long)bk * (a.C + 1);
+    const int32_t* pos = a.positions + (long)bk * a.N;
+    int lo = imax(0, imin(off[c], a.N)), hi = imax(lo, imin(off[c + 1], a.N));
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pos[mid] < bound)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    a.ends[idx] = lo;
+}
+
 }  // namespace
+
+hipError_t launch_blocks_visible(const VisibleArgs& a, hipStream_t s)
+{
+    const long n = (long)a.g.B * a.g.Hkv * a.C;
+    hipLaunchKernelGGL(k_blocks_visible, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_index_build(const IndexArgs& a, hipStream_t s)
 {

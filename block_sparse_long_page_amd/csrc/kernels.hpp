@@ -117,6 +117,7 @@ struct GroupArgs {
     const void* blk_k;       // [B][Hkv][blk_n][hd]
     const void* blk_v;
     int blk_n;               // rows per (sequence, KV head)
+    const int32_t* blk_end;  // [B][Hkv][npg] end row of each block's visible part, or null (whole blocks)
 };
 
 // Semantic block index: spherical k-means of the unit keys of positions
@@ -157,6 +158,17 @@ struct SelectBlocksArgs {
     int budget, k_max;
     int32_t* sel;            // [B][Hkv][Q][k_max] ascending, -1 after the count
     int32_t* count;          // [B][Hkv][Q]
+    const int32_t* ends;     // [B][Hkv][C] end row of each block's visible part, or null (whole blocks)
+};
+
+// end row of the visible part of every block: the rows of positions before
+// L - W (positions ascend inside a block, so the part is a prefix)
+struct VisibleArgs {
+    Geometry g;
+    int N, C, W;
+    const int32_t* offsets;    // [B][Hkv][C + 1]
+    const int32_t* positions;  // [B][Hkv][N]
+    int32_t* ends;             // [B][Hkv][C]
 };
 
 // KeyDiff eviction of a cache back to a token budget (distance of each key to
@@ -206,6 +218,7 @@ hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
 // the whole index build (every kernel of every iteration)
 hipError_t launch_index_build(const IndexArgs& a, hipStream_t s);
 hipError_t launch_select_blocks(const SelectBlocksArgs& a, hipStream_t s);
+hipError_t launch_blocks_visible(const VisibleArgs& a, hipStream_t s);
 // key sums, distances and the kept positions
 hipError_t launch_keydiff_select(const KeydiffArgs& a, hipStream_t s);
 hipError_t launch_keydiff_compact(const CompactArgs& a, hipStream_t s);

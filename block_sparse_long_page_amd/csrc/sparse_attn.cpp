@@ -316,7 +316,7 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
                  const int32_t* sel, const int32_t* cnt, int32_t k_max, int32_t sink_len, int32_t window_len,
                  float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o, float* part_ml,
                  void* workspace, size_t workspace_bytes, int npg, const int32_t* blk_off, const void* blk_k,
-                 const void* blk_v, int blk_n, hipStream_t stream)
+                 const void* blk_v, int blk_n, const int32_t* blk_end, hipStream_t stream)
 {
     if (!q || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 || k_max < 0)
         return SA_ERR_INVALID_ARG;
@@ -342,7 +342,8 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
                         k_max,      sink_len,   window_len, sl2,     token_splits,
                         (int)stride, part_o,    part_ml,    (int32_t*)(base + w.nunion),
                         (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots),
-                        npg,        blk_off,    blk_k,      blk_v,   blk_n};
+                        npg,        blk_off,    blk_k,      blk_v,   blk_n,
+                        blk_end};
         const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
         if (r1 != SA_OK) return r1;
     }
@@ -452,8 +453,22 @@ int sparse_attn_select_blocks(const sa_kv_desc* kv, const sa_block_index* index,
     if (k_max < 1 || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
     if ((long)kv->batch * kv->num_kv_heads * num_q_rows > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
     sa::SelectBlocksArgs a{g,          q,     num_q_rows, index->num_blocks, index->offsets, index->centres,
-                           token_budget, k_max, sel_blocks, sel_count};
+                           token_budget, k_max, sel_blocks, sel_count, index->visible_end};
     return finish(sa::launch_select_blocks(a, stream), stream);
+}
+
+int sparse_attn_blocks_visible(const sa_kv_desc* kv, const sa_block_index* index, int32_t window_len,
+                               int32_t* visible_end, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    const int ri = check_index(kv, index);
+    if (ri != SA_OK) return ri;
+    if (!visible_end || window_len < 0) return SA_ERR_INVALID_ARG;
+    sa::VisibleArgs a{g, index->num_tokens, index->num_blocks, window_len, index->offsets, index->positions,
+                      visible_end};
+    return finish(sa::launch_blocks_visible(a, stream), stream);
 }
 
 size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index)
@@ -476,7 +491,8 @@ int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index,
     if (window_len < num_q_rows || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
     return grouped_impl(kv, g, q, num_q_rows, sel_blocks, sel_count, k_max, 0, window_len, softmax_scale,
                         token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes, index->num_blocks,
-                        index->offsets, index->k_blocks, index->v_blocks, index->num_tokens, stream);
+                        index->offsets, index->k_blocks, index->v_blocks, index->num_tokens, index->visible_end,
+                        stream);
 }
 
 int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
@@ -489,7 +505,7 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
     if (rc != SA_OK) return rc;
     return grouped_impl(kv, g, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, softmax_scale,
                         token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes,
-                        kv->max_pages_per_seq, nullptr, nullptr, nullptr, 0, stream);
+                        kv->max_pages_per_seq, nullptr, nullptr, nullptr, 0, nullptr, stream);
 }
 
 size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv)

@@ -24,6 +24,9 @@
  *   sparse_attn_select_blocks      per-row block choice under a token budget
  *   sparse_attn_decode_blocks      grouped decode over the chosen blocks plus
  *                                  the window of recent tokens
+ *   sparse_attn_blocks_visible     the part of each block before a prompt
+ *                                  chunk's window (chunked prefill over an
+ *                                  index of the whole prompt)
  *
  * and, for KeyDiff eviction (course module 14, section 14.4: tokens whose
  * keys lie closest to the mean key are evicted, the sink never, blockwise so
@@ -330,6 +333,11 @@ typedef struct sa_block_index {
     float* centres;      /* [batch][num_kv_heads][C][head_dim] unit-length block centres */
     void* k_blocks;      /* [batch][num_kv_heads][N][head_dim] keys in block order, KV dtype */
     void* v_blocks;      /* [batch][num_kv_heads][N][head_dim] values in block order */
+    /* optional [batch][num_kv_heads][C]: the end row of each block's visible
+       part (sparse_attn_blocks_visible); NULL: whole blocks.  Read by
+       sparse_attn_select_blocks (block sizes) and sparse_attn_decode_blocks
+       (rows attended); the build ignores it. */
+    const int32_t* visible_end;
 } sa_block_index;
 
 /* Workspace bytes of sparse_attn_build_block_index (host only; 0 for bad sizes). */
@@ -364,7 +372,9 @@ int sparse_attn_build_block_index(const sa_kv_desc* kv, int32_t iterations, cons
  * to a budget of tokens): block c scores max over the group's heads of
  * q_h . centre_c (fp32); blocks are taken in order of (score desc, block
  * asc) while the running token count stays <= token_budget, at least one
- * and at most k_max; blocks without tokens are never taken.
+ * and at most k_max; blocks without tokens are never taken.  With
+ * index->visible_end set, a block's size is its visible part (blocks with
+ * none are never taken).
  *   q           [batch][num_q_heads][num_q_rows][head_dim], bf16
  *   sel_blocks  [batch][num_kv_heads][num_q_rows][k_max]: the chosen blocks
  *               ascending, -1 after the last; sel_count [..][num_q_rows]
@@ -375,6 +385,24 @@ int sparse_attn_build_block_index(const sa_kv_desc* kv, int32_t iterations, cons
 int sparse_attn_select_blocks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
                               int32_t token_budget, int32_t k_max, int32_t* sel_blocks, int32_t* sel_count,
                               hipStream_t stream);
+
+/*
+ * The visible part of every block for a chunk of rows (semantic-blocks page:
+ * one index serves the prompt's processing as well as generation, and a
+ * prompt chunk attends its own tokens and the recent history without
+ * selection): visible_end[b][kvh][c] = the first row of block c whose
+ * position is >= L_b - window_len (positions ascend inside a block, so the
+ * rows before it, of positions < L_b - window_len, are its visible part).
+ * With visible_end stored in index->visible_end, sparse_attn_select_blocks
+ * sizes the blocks by their visible parts and sparse_attn_decode_blocks
+ * attends only those rows, so an index of the whole prompt serves every
+ * chunk: the chunk's rows see the index only before their window.
+ *   visible_end  int32 [batch][num_kv_heads][C]
+ * Errors: those of the index checks; SA_ERR_INVALID_ARG for a null
+ * visible_end or window_len < 0.
+ */
+int sparse_attn_blocks_visible(const sa_kv_desc* kv, const sa_block_index* index, int32_t window_len,
+                               int32_t* visible_end, hipStream_t stream);
 
 /* Workspace bytes of sparse_attn_decode_blocks for this index (host only; 0 for bad sizes). */
 size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index);
@@ -387,8 +415,10 @@ size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_i
  * and the window [L - window_len, L) of the paged cache by the per-row
  * decode (no sink).  The blocks' tokens are attended without a causal test:
  * the caller keeps the index to positions before every row's window, i.e.
- * num_tokens <= L - window_len for every sequence, and window_len >=
- * num_q_rows so that the window holds the rows themselves.
+ * num_tokens <= L - window_len for every sequence, or sets
+ * index->visible_end from sparse_attn_blocks_visible with the same
+ * window_len (then only the rows before the window are attended), and
+ * window_len >= num_q_rows so that the window holds the rows themselves.
  *   sel_blocks, sel_count, k_max  as sparse_attn_select_blocks writes them
  *   token_splits, local_splits, part_o, part_ml  as in
  *               sparse_attn_decode_grouped (slot j * token_splits + c holds

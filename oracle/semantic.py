@@ -25,7 +25,12 @@ Where the page leaves a step open this module takes the plainest reading
   * a query row scores block c by the largest q_h . centre_c over the heads
     of its group; blocks are taken in order of score (ties: lower block)
     while the running token count stays within the budget, at least one;
-    blocks without tokens are never taken.
+    blocks without tokens are never taken;
+  * the prompt is processed in chunks of rows over one index of the whole
+    prompt (one index serves the prompt and the generation): a chunk's
+    window (its own rows and the recent history) is attended causally
+    without selection, and of the index it sees only the tokens before the
+    window, so a block's size for the budget is its visible part.
 """
 from __future__ import annotations
 
@@ -107,6 +112,36 @@ def select_blocks(scores: np.ndarray, sizes: np.ndarray, budget: int, k_max: int
         taken.append(c)
         total += int(sizes[c])
     return np.array(sorted(taken), dtype=np.int32)
+
+
+def visible_sizes(perm: np.ndarray, offsets: np.ndarray, bound: int) -> np.ndarray:
+    """Tokens of each block at positions before `bound` (the part of the
+    index a prompt chunk may see: everything before its window)."""
+    C = len(offsets) - 1
+    return np.array([int(np.sum(perm[offsets[c]:offsets[c + 1]] < bound)) for c in range(C)], dtype=np.int64)
+
+
+def prefill_chunk(K, V, qrows, centres, perm, offsets, c0: int, window: int, budget: int, k_max: int,
+                  scale: float):
+    """One chunk of a sparse prefill over an index of the whole prompt.  Rows
+    i = 0 .. len(qrows)-1 sit at positions c0 + i; the chunk's window is
+    [c0 + T - window, c0 + T) (T rows), attended causally and without
+    selection; before it each row chooses blocks by centre score among their
+    visible parts (positions before the window) under the token budget.
+    qrows[i] is the [G][hd] query group of row i.  Returns, per row, the
+    chosen blocks and the per-head (output, lse)."""
+    T = len(qrows)
+    bound = c0 + T - window
+    vis = visible_sizes(perm, offsets, bound)
+    res = []
+    for i in range(T):
+        pos = c0 + i
+        qg = np.asarray(qrows[i], dtype=np.float64)
+        blocks = select_blocks(block_scores(qg, centres), vis, budget, k_max)
+        toks = np.concatenate([perm[offsets[x]:offsets[x + 1]][perm[offsets[x]:offsets[x + 1]] < bound]
+                               for x in blocks] + [np.arange(max(0, bound), pos + 1)]).astype(np.int64)
+        res.append((blocks, [attend(qg[h], K[toks], V[toks], scale) for h in range(len(qg))]))
+    return res
 
 
 def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):

@@ -15,7 +15,11 @@ function it pins:
     budget the best one, and a larger budget never drops a block;
   * attention over every block plus the recent tokens is dense causal
     attention (tests/helpers.py), and on a cache whose clusters are already
-    its pages the index reproduces the paged centroid path of the C oracle.
+    its pages the index reproduces the paged centroid path of the C oracle;
+  * a prefill chunk over an index of the whole prompt: with every block
+    chosen each row is dense causal attention over its prefix, whatever the
+    chunk and window; with an index of the prefix before the window only it
+    is the decode path above; visible sizes count positions directly.
 """
 import numpy as np
 import pytest
@@ -201,3 +205,56 @@ def test_pages_that_are_clusters_give_the_paged_centroid_path():
             for h in range(G):
                 np.testing.assert_allclose(res[h, i][0], r.out[0, kvh * G + h, i], atol=1e-12)
                 assert abs(res[h, i][1] - r.lse[0, kvh * G + h, i]) < 1e-12
+
+
+def _prefill_setup(seed=0):
+    pr = _tiny_semantic(scatter=True, seed=seed)
+    c = pr.cache
+    K, V = dense_keys_values(c, 0, 1)
+    L = K.shape[0]
+    mu, a, _ = sem.spherical_kmeans(K, 8, 4)  # an index of the whole prompt
+    perm, off = sem.block_layout(a, 8)
+    G = c.Hq // c.Hkv
+    q = np.random.default_rng(seed).standard_normal((L, G, c.hd))
+    return c, K, V, L, mu, perm, off, q
+
+
+def test_visible_sizes_count_positions():
+    c, K, V, L, mu, perm, off, q = _prefill_setup()
+    for bound in (0, 1, 100, 333, L, L + 5):
+        vis = sem.visible_sizes(perm, off, bound)
+        for x in range(8):
+            assert vis[x] == len([t for t in perm[off[x]:off[x + 1]] if t < bound])
+    np.testing.assert_array_equal(sem.visible_sizes(perm, off, L), np.diff(off))
+
+
+@pytest.mark.parametrize("c0,T,W", [(0, 4, 4), (100, 8, 8), (200, 16, 40), (510, 6, 6)])  # 510 + 6 = L
+def test_prefill_with_every_block_is_dense_causal(c0, T, W):
+    c, K, V, L, mu, perm, off, q = _prefill_setup()
+    res = sem.prefill_chunk(K, V, q[c0:c0 + T], mu, perm, off, c0, W, budget=10**9, k_max=8,
+                            scale=1.0 / np.sqrt(c.hd))
+    for i, (blocks, heads) in enumerate(res):
+        pos = c0 + i
+        for h, (o, lse) in enumerate(heads):
+            ref_o, ref_l = masked_attention(q[pos, h], K, V, np.arange(L) <= pos, 1.0 / np.sqrt(c.hd))
+            np.testing.assert_allclose(o, ref_o, atol=1e-12)
+            assert abs(lse - ref_l) < 1e-12
+
+
+def test_prefill_chunk_over_the_prefix_index_is_the_decode():
+    """An index of [0, N) with N at the chunk's window start: every block is
+    wholly visible, and the chunk is the decode path over blocks + window."""
+    pr = _tiny_semantic(scatter=True, seed=3)
+    c = pr.cache
+    res, chosen, (mu, a, perm, off) = _blocked_reference(pr, 0, 1, 8, 4, pr.budget, k_max=8)
+    K, V = dense_keys_values(c, 0, 1)
+    L = K.shape[0]
+    G = c.Hq // c.Hkv
+    qrows = [np.stack([query(pr, 0, G + h, i) for h in range(G)]) for i in range(pr.Q)]
+    got = sem.prefill_chunk(K, V, qrows, mu, perm, off, L - pr.Q, pr.window, pr.budget, 8, 1.0 / np.sqrt(c.hd))
+    for i, (blocks, heads) in enumerate(got):
+        np.testing.assert_array_equal(blocks, chosen[i])
+        for h, (o, lse) in enumerate(heads):
+            np.testing.assert_allclose(o, res[h, i][0], atol=1e-12)
+            assert abs(lse - res[h, i][1]) < 1e-12
+
