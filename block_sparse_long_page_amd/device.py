@@ -319,6 +319,34 @@ class BlockIndex:
         return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)
 
 
+class ChunkedPrefill:
+    """Sparse prefill of a prompt over one block index of the whole prompt
+    (BlockIndex with num_tokens = the prompt length, Q = the chunk's rows):
+    the rows at [c0, c0 + Q) see the index only before their window
+    [c0 + Q - window, c0 + Q) (sparse_attn_blocks_visible), choose blocks
+    under the token budget, read each chosen block once for all the chunk's
+    rows plus the window causally (sparse_attn_decode_blocks), and combine.
+    The cache's lengths are set to c0 + Q for the chunk."""
+
+    def __init__(self, ix: "BlockIndex", window: int):
+        self.ix, self.window = ix, window
+        c = ix.c
+        self.ends = torch.zeros((c.B, c.Hkv, ix.C), dtype=torch.int32, device=c.k.device)
+        self.index = B.make_block_index(num_tokens=ix.N, num_blocks=ix.C, offsets=ix.offsets,
+                                        positions=ix.positions, centres=ix.centres, k_blocks=ix.k_blocks,
+                                        v_blocks=ix.v_blocks, visible_end=self.ends)
+
+    def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
+        ix = self.ix
+        ix.c.seq_lens.fill_(c0 + ix.Q)
+        B.sparse_attn_blocks_visible(ix.desc, self.index, self.window, self.ends, stream)
+        B.sparse_attn_select_blocks(ix.desc, self.index, q, ix.Q, budget, ix.k_max, ix.sel, ix.count, stream)
+        B.sparse_attn_decode_blocks(ix.desc, self.index, q, ix.Q, ix.sel, ix.count, ix.k_max, self.window, 0.0,
+                                    ix.ts, ix.ls, ix.part_o, ix.part_ml, ix.ws, ix.ws_bytes, stream)
+        ix.combine(stream=stream)
+        return ix.out
+
+
 class KeyDiffEviction:
     """KeyDiff eviction of a DeviceCache to a token budget: the kept tokens of
     every (sequence, KV head) (sparse_attn_keydiff_select) and their K and V

@@ -25,8 +25,8 @@ def test_exports_every_header_function():
         "sparse_attn_decode_step", "sparse_attn_default_splits", "sparse_attn_combine", "sparse_attn_status_string",
         "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes", "sparse_attn_index_workspace_bytes",
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
-        "sparse_attn_decode_blocks", "sparse_attn_keydiff_workspace_bytes", "sparse_attn_keydiff_select",
-        "sparse_attn_keydiff_compact"}
+        "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
+        "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -401,4 +401,22 @@ def test_keydiff_checks():
     for bad, code in BAD_DESCS:
         assert comp(src=_desc(**bad)) == code
         assert comp(dst=_desc(**bad)) == code
+
+
+def test_blocks_visible_checks():
+    lib = B.library()
+
+    def vis(**kw):
+        a = dict(desc=_desc(), ix=_index(), W=8, out=DEV)
+        a.update(kw)
+        ixp = ctypes.byref(a["ix"]) if a["ix"] is not None else None
+        return lib.sparse_attn_blocks_visible(ctypes.byref(a["desc"]), ixp, a["W"], a["out"], None)
+
+    assert vis(out=None) == B.SA_ERR_INVALID_ARG
+    assert vis(W=-1) == B.SA_ERR_INVALID_ARG
+    assert vis(ix=None) == B.SA_ERR_INVALID_ARG
+    assert vis(ix=_index(positions=None)) == B.SA_ERR_INVALID_ARG
+    assert vis(ix=_index(num_blocks=0)) == B.SA_ERR_INVALID_ARG
+    for bad, code in BAD_DESCS:
+        assert vis(desc=_desc(**bad)) == code
 
