@@ -67,7 +67,7 @@ def parse():
                          "blocks with a one-page stride)")
     ap.add_argument("--workload", default="llama3-70b-layer-128k",
                     choices=["llama3-70b-layer-128k", "semantic-512k", "semantic-512k-index", "hybrid-3layer-256k",
-                             "keydiff-llama3.1-8b-8k"],
+                             "keydiff-llama3.1-8b-8k", "semantic-prefill-64k"],
                     help="semantic-512k: the 64-row chunk decoded by page (selection, grouped decode, combine); "
                          "semantic-512k-index: the same chunk over a semantic block index built from keys "
                          "interleaved in position order (index build, then block choice, grouped decode of the "
@@ -76,7 +76,8 @@ def parse():
                          "selection every 32 steps after summarising the pages appended since the last one, "
                          "growing window between); "
                          "keydiff-llama3.1-8b-8k: KeyDiff eviction of a cache of 10240 tokens back to 8192 "
-                         "(distances to the mean key, top-k, compaction of the kept K/V rows)")
+                         "(distances to the mean key, top-k, compaction of the kept K/V rows); "
+                         "semantic-prefill-64k: chunked sparse prefill of a 64K prompt over one block index")
     return ap.parse_args()
 
 
@@ -423,6 +424,78 @@ def bench_keydiff(args):
     }))
 
 
+def bench_prefill(args):
+    """Chunked sparse prefill of a 64K-token prompt (batch 2, 16 q / 4 KV
+    heads, keys of 32 semantic clusters interleaved in position order): one
+    block index of the whole prompt is built, then the prompt's rows are
+    processed 64 at a time; each chunk sees the index only before its own
+    tokens, chooses blocks per row under a budget of 1/16 of its length,
+    reads each chosen block once for all its rows and attends its own tokens
+    causally.  The same chunks with every visible block chosen (dense over
+    the prefix, same kernels, no index build) are timed beside it."""
+    import numpy as np
+    import torch
+
+    from block_sparse_long_page_amd import configs, synth
+    from block_sparse_long_page_amd.device import BlockIndex, ChunkedPrefill, DeviceCache, to_device
+
+    wl = configs.SEMANTIC_PREFILL_64K
+    t0 = time.time()
+    pr = synth.semantic_problem(wl, scatter=True, blocks=(wl.context - wl.q_rows) // 2048)
+    q_all = synth.prefill_queries(pr, seed=wl.seed)
+    c = pr.cache
+    L = int(c.seq_lens[0])
+    T, W = wl.q_rows, wl.window
+    nch = L // T
+    C = L // 2048
+    log(f"inputs {time.time() - t0:.1f}s")
+    dc = DeviceCache.from_host(c)
+    # chunk-major queries: chunk j is the contiguous [B][Hq][T][hd] block j
+    q_dev = to_device(q_all).view(c.B, c.Hq, nch, T, c.hd).permute(2, 0, 1, 3, 4).contiguous()
+    del q_all
+    ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
+    pf = ChunkedPrefill(ix, W)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        start.record()
+        fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
+    def build():
+        ix.build(args.iterations)
+
+    def chunks(dense):
+        for j in range(nch):
+            pf.chunk(q_dev[j], j * T, 10**9 if dense else max(1, (j + 1) * T // 16))
+
+    build()
+    chunks(False)
+    chunks(True)
+    build_ms = timed(build)
+    sparse_ms = timed(lambda: chunks(False))
+    dense_ms = timed(lambda: chunks(True))
+    total_ms = build_ms + sparse_ms
+    toks = c.B * L
+    print(json.dumps({
+        "metric": "prefill tokens/s, 64K prompt, semantic block index, 64-row chunks",
+        "value": round(toks / (total_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": 1,
+        "warmup": 1, "ms_per_step": round(total_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded): 32 vMF clusters of 2048 keys per (b, kvh) interleaved in position order, "
+                "V N(0,1), query rows around 4 topics per (b, kvh)",
+        "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
+                   "prompt": L, "chunk": T, "window": W, "blocks": C, "iterations": args.iterations,
+                   "budget": "1/16 of the chunk's length"},
+        "index_build_ms": round(build_ms, 3), "sparse_chunks_ms": round(sparse_ms, 3),
+        "dense_chunks_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / total_ms, 2),
+        "us_per_chunk": round(sparse_ms * 1e3 / nch, 2),
+    }))
+
+
 def bench_hybrid(args):
     """The hybrid model's three full-attention layers at 256k over 128 decode
     steps: every step appends a token to every sequence; steps 0, 32, 64, 96
@@ -552,6 +625,9 @@ def main():
         return
     if args.workload == "keydiff-llama3.1-8b-8k":
         bench_keydiff(args)
+        return
+    if args.workload == "semantic-prefill-64k":
+        bench_prefill(args)
         return
 
     from block_sparse_long_page_amd import accounting, binding as B, configs, synth

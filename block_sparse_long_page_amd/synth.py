@@ -384,3 +384,33 @@ def hybrid_schedule(wl: Workload, *, seed: Optional[int] = None, batch: Optional
     return HybridSchedule(caches=caches, q=qs, context=L0, steps=T, refresh=wl.refresh, sink=wl.sink,
                           windows=[l.window for l in wl.layers], budgets=[l.budget for l in wl.layers],
                           mode=MODE_NAMES[wl.mode], name=wl.name)
+
+
+def prefill_queries(pr: Problem, *, seed: int = 0, topics: int = 4, q_kappa: float = 50.0) -> np.ndarray:
+    """Query rows for every position of a problem's cache (a prompt to
+    prefill): per (b, KV head) `topics` directions, the unit keys at random
+    positions (a key lies close to its cluster's direction); each row follows
+    one of them for every head of the group (von Mises-Fisher, concentration
+    q_kappa), scaled by sqrt(hd).  [B][Hq][L][hd] in the cache dtype."""
+    c = pr.cache
+    L = int(c.seq_lens[0])
+    G = c.Hq // c.Hkv
+    n_pages = -(-L // c.P)
+    q = np.empty((c.B, c.Hq, L, c.hd), dtype=np.uint16 if c.dtype == BF16 else np.float32)
+    children = np.random.default_rng(seed).spawn(c.B * c.Hkv)
+
+    def head(i):
+        b, kvh = divmod(i, c.Hkv)
+        r = children[i]
+        keys = to_f32(c.k[c.block_table[b, :n_pages], kvh], c.dtype).reshape(-1, c.hd)[:L]
+        dirs = keys[r.integers(0, L, size=topics)].astype(np.float64)
+        dirs /= np.maximum(np.linalg.norm(dirs, axis=1, keepdims=True), 1e-30)
+        row_topic = r.integers(0, topics, size=L)
+        for g in range(G):
+            u = sample_vmf(r, dirs[row_topic], q_kappa, L).astype(np.float32) * np.float32(np.sqrt(c.hd))
+            q[b, kvh * G + g] = store(u, c.dtype)
+
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(head, range(c.B * c.Hkv)))
+    return q
+
