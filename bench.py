@@ -81,6 +81,30 @@ def parse():
     return ap.parse_args()
 
 
+def oracle_seconds(fn, seconds: float, max_calls: int = 200):
+    """Median seconds per call of an oracle call `fn`, repeated until
+    `seconds` have passed (at least once); returns (median, calls)."""
+    times = []
+    t_end = time.time() + seconds
+    while not times or time.time() < t_end:
+        t1 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t1)
+        if len(times) >= max_calls:
+            break
+    return statistics.median(times), len(times)
+
+
+def roofline_record(kernel: str, bytes_per_launch: int, launch_ms: float) -> dict:
+    """HBM roofline of one launch (or one call of several kernels) from its
+    algorithmic bytes and its average duration (HIP events around
+    back-to-back launches on their stream)."""
+    gbs = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_us": round(launch_ms * 1e3, 2)}
+
+
 def copy_probe():
     import torch
 
@@ -208,6 +232,12 @@ def bench_semantic(args):
     ms = timed(step_grouped, K)
     ms_rows = float("nan") if args.only_timed else timed(step_rows, max(1, K // 5))
 
+    def decode_grouped(r):  # the dominant call alone, on the last step's lists
+        B.sparse_attn_decode_grouped(descs[r], q, Q, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, 0.0, gs.ts,
+                                     gs.ls, gs.part_o, gs.part_ml, gs.ws, gs.ws_bytes)
+
+    dec_ms = timed(decode_grouped, K)
+
     # bytes: the union of the rows' pages per (sequence, KV head), read once
     sel, cnt = dec.selection()
     L = int(c.seq_lens[0])
@@ -233,6 +263,20 @@ def bench_semantic(args):
                                        k_max=dec.k_max, mode=pr.mode, union_tokens=union_tok,
                                        local_tokens=local_tok, stride=gs.stride)
     gbs = sb.total / (ms * 1e-3) / 1e9
+    # the grouped call reads the page lists, q and the K/V of the unions and
+    # of the windows once, and writes the partials
+    dec_bytes = sb.kv + sb.q + sb.partials // 2 + c.B * c.Hkv * Q * (dec.k_max + 1) * 4
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        med, calls = oracle_seconds(lambda: oracle.run(c, pr.q, mode=pr.mode, Q=Q, sink=pr.sink, window=pr.window,
+                                                       budget=pr.budget), args.cpu_seconds)
+        cpu = {"value": round(sb.total / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": f"the full 64-row step (centroids of every page, scores, top-k, "
+                                           f"attention) in fp64, {calls} run(s); median {med * 1e3:.0f} ms/step",
+               "ms_per_step": round(med * 1e3, 1)}
     print(json.dumps({
         "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 512K ctx semantic blocks, 64-row chunk",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -248,6 +292,9 @@ def bench_semantic(args):
         "per_row_us_per_step": None if ms_rows != ms_rows else round(ms_rows * 1e3, 2),
         "speedup_vs_per_row": None if ms_rows != ms_rows else round(ms_rows / ms, 2),
         "bytes_per_step": sb.as_dict(),
+        "roofline": roofline_record("sparse_attn_decode_grouped (k_group_plan + k_group_decode_mfma + k_decode_mfma)",
+                                    dec_bytes, dec_ms),
+        "cpu_baseline": cpu,
     }))
 
 
@@ -303,6 +350,13 @@ def bench_semantic_index(args):
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / K
+    # the block decode alone (plan + grouped decode of the blocks + window), on the last step's lists
+    start.record()
+    for _ in range(K):
+        ix.decode(q)
+    stop.record()
+    torch.cuda.synchronize()
+    dec_ms = start.elapsed_time(stop) / K
 
     sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
     off = ix.offsets.cpu().numpy()
@@ -318,10 +372,44 @@ def bench_semantic_index(args):
             union_tok += int(sum(sizes[b, h, x] for x in u))
     Q = pr.Q
     local_tok = nbk * pr.window
-    partial_bytes = c.B * c.Hq * Q * ix.stride * (hd + 2) * 4
+    # partials: a used slot (a listed block's chunk or the window's split)
+    # holds o and (m, l) for every head, an unused one only (m, l)
+    used = (c.Hq // c.Hkv) * (listed * ix.ts + nbk * Q * ix.ls)
+    partial_bytes = (used * (hd + 2) + (c.B * c.Hq * Q * ix.stride - used) * 2) * 4
     step_bytes = (union_tok * row * 2 + local_tok * row * 2 + nbk * C * (hd * 4 + 4) + c.B * c.Hq * Q * hd * 2 * 2
                   + 2 * partial_bytes)
     gbs = step_bytes / (ms * 1e-3) / 1e9
+    dec_bytes = union_tok * row * 2 + local_tok * row * 2 + c.B * c.Hq * Q * hd * 2 + partial_bytes \
+        + nbk * Q * (ix.k_max + 1) * 4
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's block choice and attention for the 64 rows of one
+        # (sequence, KV head), over the index the GPU built (fp64 numpy, one thread)
+        from threadpoolctl import threadpool_limits
+
+        from oracle import semantic as sem
+
+        cent = ix.centres.cpu().numpy().astype(np.float64)[0, 0]
+        perm0, off0 = ix.positions.cpu().numpy()[0, 0], ix.offsets.cpu().numpy()[0, 0]
+        n_pages = -(-L // c.P)
+        Kf = synth.to_f32(c.k[c.block_table[0, :n_pages], 0], c.dtype).reshape(-1, hd)[:L].astype(np.float64)
+        Vf = synth.to_f32(c.v[c.block_table[0, :n_pages], 0], c.dtype).reshape(-1, hd)[:L].astype(np.float64)
+        G = c.Hq // c.Hkv
+        qf = synth.to_f32(pr.q[0, :G], c.dtype).astype(np.float64)  # [G][Q][hd]
+
+        def rows():
+            for i in range(Q):
+                blocks = sem.select_blocks(sem.block_scores(qf[:, i], cent), sizes[0, 0], pr.budget, ix.k_max)
+                toks = np.concatenate([perm0[off0[x]:off0[x + 1]] for x in blocks] + [np.arange(N, L - Q + i + 1)])
+                for h in range(G):
+                    sem.attend(qf[h, i], Kf[toks], Vf[toks], 1.0 / np.sqrt(hd))
+
+        with threadpool_limits(1):
+            med, calls = oracle_seconds(rows, args.cpu_seconds)
+        cpu = {"value": round(step_bytes / nbk / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"(sequence 0, KV head 0): block choice and attention of its {Q} rows over the GPU-built "
+                         f"index in fp64 numpy, {calls} run(s), median {med * 1e3:.0f} ms, scaled by the "
+                         f"{nbk} (sequence, KV head) pairs of the step's bytes"}
     print(json.dumps({
         "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 512K ctx semantic block index, 64-row chunk",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -338,6 +426,9 @@ def bench_semantic_index(args):
         "block_tokens": {"min": int(sizes.min()), "mean": float(sizes.mean()), "max": int(sizes.max()),
                          "empty": int((sizes == 0).sum())},
         "union_blocks": union_blocks, "listed_blocks": listed, "bytes_per_step": step_bytes,
+        "roofline": roofline_record("sparse_attn_decode_blocks (k_group_plan + k_group_decode_mfma + k_decode_mfma)",
+                                    dec_bytes, dec_ms),
+        "cpu_baseline": cpu,
     }))
 
 
@@ -407,6 +498,32 @@ def bench_keydiff(args):
     step_bytes = sel_bytes + comp_bytes
     gbs = step_bytes / (ms * 1e-3) / 1e9
     comp_gbs = comp_bytes / (comp_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's eviction (distances, kept set) and the copy of the kept
+        # rows for (sequence, KV head) pairs in turn (fp64 numpy, one thread)
+        import numpy as np
+        from threadpoolctl import threadpool_limits
+
+        from oracle import keydiff as kd
+
+        n_pages = -(-L // c.P)
+        pairs = [(b, h) for b in range(c.B) for h in range(c.Hkv)][:8]
+        kv = [(synth.to_f32(c.k[c.block_table[b, :n_pages], h], c.dtype).reshape(-1, c.hd)[:L].astype(np.float64),
+               synth.to_f32(c.v[c.block_table[b, :n_pages], h], c.dtype).reshape(-1, c.hd)[:L].astype(np.float64))
+              for b, h in pairs]
+
+        def evict_pairs():
+            for Kf, Vf in kv:
+                kept = kd.keep(Kf, wl.budget, wl.sink)
+                _ = (Kf[kept], Vf[kept])  # the copy into the evicted cache
+
+        with threadpool_limits(1):
+            med, calls = oracle_seconds(evict_pairs, args.cpu_seconds)
+        cpu = {"value": round(step_bytes * len(pairs) / nbk / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"{len(pairs)} of the {nbk} (sequence, KV head) pairs evicted in fp64 "
+                                           f"numpy, {calls} run(s), median {med * 1e3:.0f} ms, against their share "
+                                           f"of the step's bytes"}
     print(json.dumps({
         "metric": "evicted-cache GB/s + us per eviction, 10240 -> 8192 tokens, Llama-3.1-8B-shaped layer",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -421,6 +538,7 @@ def bench_keydiff(args):
                      "bytes_per_launch": comp_bytes, "avg_launch_us": round(comp_ms * 1e3, 2)},
         "select_us": round(sel_ms * 1e3, 2), "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
         "bytes_per_step": step_bytes,
+        "cpu_baseline": cpu,
     }))
 
 
@@ -452,6 +570,7 @@ def bench_prefill(args):
     dc = DeviceCache.from_host(c)
     # chunk-major queries: chunk j is the contiguous [B][Hq][T][hd] block j
     q_dev = to_device(q_all).view(c.B, c.Hq, nch, T, c.hd).permute(2, 0, 1, 3, 4).contiguous()
+    q0 = np.ascontiguousarray(q_all[0, :c.Hq // c.Hkv])  # sequence 0's first group, for the CPU baseline
     del q_all
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
     pf = ChunkedPrefill(ix, W)
@@ -480,6 +599,64 @@ def bench_prefill(args):
     dense_ms = timed(lambda: chunks(True))
     total_ms = build_ms + sparse_ms
     toks = c.B * L
+
+    # algorithmic bytes of the sparse chunks (an untimed pass that reads each
+    # chunk's lists back): the visible K/V of the union of the rows' blocks
+    # and of the window, once per (sequence, KV head), q, the page lists, the
+    # partials written and read, the output
+    nbk, row, G = c.B * c.Hkv, c.hd * 2, c.Hq // c.Hkv
+    chunk_bytes = 0
+    for j in range(nch):
+        pf.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
+        sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
+        ends, off = pf.ends.cpu().numpy(), ix.offsets.cpu().numpy()
+        vis_tok = 0
+        for b in range(c.B):
+            for h in range(c.Hkv):
+                u = set()
+                for i in range(T):
+                    u.update(int(x) for x in sel[b, h, i, :cnt[b, h, i]])
+                vis_tok += sum(int(ends[b, h, x] - off[b, h, x]) for x in u)
+        win = min(W, (j + 1) * T)
+        # a used slot (a listed block or the window) holds o and (m, l) for
+        # every head, an unused one only (m, l); written, then read by the combine
+        used = G * (int(cnt.sum()) * ix.ts + nbk * T * ix.ls)
+        partials = 2 * (used * (c.hd + 2) + (c.B * c.Hq * T * ix.stride - used) * 2) * 4
+        chunk_bytes += ((vis_tok + nbk * win) * row * 2 + c.B * c.Hq * T * c.hd * 2 * 2
+                        + nbk * T * (C + 1) * 4 + partials + nbk * C * 4)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's prefill of one (sequence, KV head): its index (spherical
+        # k-means of the whole prompt, layout) once, and chunks spread over the
+        # prompt; the whole prompt's time is projected from their average
+        from threadpoolctl import threadpool_limits
+
+        from oracle import semantic as sem
+
+        n_pages = -(-L // c.P)
+        Kf = synth.to_f32(c.k[c.block_table[0, :n_pages], 0], c.dtype).reshape(-1, c.hd)[:L].astype(np.float64)
+        Vf = synth.to_f32(c.v[c.block_table[0, :n_pages], 0], c.dtype).reshape(-1, c.hd)[:L].astype(np.float64)
+        qf = synth.to_f32(q0, c.dtype).astype(np.float64).transpose(1, 0, 2)  # [L][G][hd]
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            mu, a, _ = sem.spherical_kmeans(Kf, C, args.iterations)
+            perm, offs = sem.block_layout(a, C)
+            t_index = time.perf_counter() - t1
+            picks = np.linspace(0, nch - 1, 9).astype(int)
+            times = []
+            t_end = time.time() + args.cpu_seconds
+            for j in picks:
+                t1 = time.perf_counter()
+                sem.prefill_chunk(Kf, Vf, qf[j * T:(j + 1) * T], mu, perm, offs, j * T, W, max(1, (j + 1) * T // 16),
+                                  C, 1.0 / np.sqrt(c.hd))
+                times.append(time.perf_counter() - t1)
+                if time.time() > t_end:
+                    break
+        per_pair = t_index + nch * float(np.mean(times))
+        cpu = {"value": round(toks / (nbk * per_pair), 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"(sequence 0, KV head 0): the index ({t_index:.2f} s) and {len(times)} chunks spread over "
+                         f"the prompt (mean {1e3 * float(np.mean(times)):.0f} ms) in fp64 numpy; the prompt's "
+                         f"{nch} chunks and {nbk} (sequence, KV head) pairs projected from them"}
     print(json.dumps({
         "metric": "prefill tokens/s, 64K prompt, semantic block index, 64-row chunks",
         "value": round(toks / (total_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": 1,
@@ -493,6 +670,10 @@ def bench_prefill(args):
         "index_build_ms": round(build_ms, 3), "sparse_chunks_ms": round(sparse_ms, 3),
         "dense_chunks_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / total_ms, 2),
         "us_per_chunk": round(sparse_ms * 1e3 / nch, 2),
+        "bytes_sparse_chunks": chunk_bytes,
+        "roofline": roofline_record("every launch of the sparse chunks (visible ends, block choice, plan, grouped "
+                                    "decode, window decode, combine)", chunk_bytes, sparse_ms),
+        "cpu_baseline": cpu,
     }))
 
 
@@ -526,7 +707,8 @@ def bench_hybrid(args):
                             splits=args.splits or None)
         dec.build_meta()
         layers.append((dc, dec, hs.windows[li], [to_device(hs.q[li][t]) for t in range(T)]))
-        hs.caches[li] = None  # the host copy is no longer needed
+        if li > 0:
+            hs.caches[li] = None  # the host copy is no longer needed (layer 0's serves the CPU baseline)
     torch.cuda.synchronize()
     P = layers[0][0].P
 
@@ -567,6 +749,42 @@ def bench_hybrid(args):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop)
 
+    # the dominant call alone: layer 0's decode of its kept pages one step
+    # after a selection (window grown by one), back to back
+    dc0, dec0, W0, qs0 = layers[0]
+    reset()
+    dec0.select_decode(qs0[0])
+    seq_lens.fill_(L0 + 1)
+    torch.cuda.synchronize()
+    K = 50
+    start.record()
+    for _ in range(K):
+        dec0.decode(qs0[1], window=W0 + 1)
+    stop.record()
+    torch.cuda.synchronize()
+    dec_ms = start.elapsed_time(stop) / K
+    sel0, cnt0 = dec0.selection()
+    ntok = sum(accounting.attended_tokens_exact(L0 + 1, P, hs.sink, W0 + 1, sel0[b, h, 0, :cnt0[b, h, 0]])
+               for b in range(dc0.B) for h in range(dc0.Hkv))
+    dec_bytes = accounting.decode_kernel_bytes(B=dc0.B, Hq=dc0.Hq, Hkv=dc0.Hkv, hd=dc0.hd, elem_bytes=2,
+                                               ntok_total=ntok, splits=dec0.splits, sel_entries=int(cnt0.sum()))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        host = hs.caches[0]
+        host.seq_lens[:] = L0
+        sb0 = accounting.decode_step_bytes(B=dc0.B, Hq=dc0.Hq, Hkv=dc0.Hkv, hd=dc0.hd, elem_bytes=2, L=L0, P=P,
+                                           S=hs.sink, W=W0, budget=dec0.budget, mode=0, splits=dec0.splits)
+        med, calls = oracle_seconds(lambda: oracle.run(host, hs.q[0][0], mode=hs.mode, Q=1, sink=hs.sink, window=W0,
+                                                       budget=dec0.budget), args.cpu_seconds)
+        cpu = {"value": round(sb0.total / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": f"the first layer's selecting step at {L0} tokens (summaries of all "
+                                           f"pages, scores, top-k, attention) in fp64, {calls} run(s); median "
+                                           f"{med * 1e3:.0f} ms, against that step's algorithmic bytes",
+               "ms_per_step": round(med * 1e3, 1)}
+
     # algorithmic bytes of the schedule
     total = 0
     c0 = layers[0][0]
@@ -598,6 +816,9 @@ def bench_hybrid(args):
                        {"window": W, "budget": dec.budget, "splits": dec.splits} for dc, dec, W, qs in layers],
                    "refresh": RF, "step": "summary refresh + (select-and-decode | decode) + combine per layer"},
         "bytes_per_schedule": total,
+        "roofline": roofline_record("k_decode_mfma (kept pages, first layer, one step after a selection)",
+                                    dec_bytes, dec_ms),
+        "cpu_baseline": cpu,
     }))
 
 
