@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the warmup and the timed region (for profiler runs)")
-    ap.add_argument("--token-splits", type=int, default=0, help="semantic-512k: token chunks per page (0: default)")
+    ap.add_argument("--token-splits", type=int, default=0,
+                    help="semantic-512k: token chunks per page; semantic-prefill-64k: per block (0: default)")
     ap.add_argument("--iterations", type=int, default=8, help="semantic-512k-index: k-means iterations")
     ap.add_argument("--score", default="quest", choices=["quest", "mean", "centroid", "compressed"],
                     help="llama3-70b-layer-128k: page summary and score (compressed: mean keys of two-page "
@@ -573,7 +574,12 @@ def bench_prefill(args):
     q0 = np.ascontiguousarray(q_all[0, :c.Hq // c.Hkv])  # sequence 0's first group, for the CPU baseline
     del q_all
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
-    pf = ChunkedPrefill(ix, W)
+    # at most 16 blocks per row (the budget, 1/16 of at most 65600 tokens,
+    # holds about 2 blocks of the average 2048 tokens; rows that reach the cap
+    # are counted below), each block in 4 token chunks so that the few blocks
+    # a chunk reads spread over the GPU; the dense run takes every block
+    pf = ChunkedPrefill(ix, T, W, k_max=min(C, 16), token_splits=args.token_splits or 4)
+    pf_dense = ChunkedPrefill(ix, T, W, k_max=C, token_splits=1)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
@@ -589,7 +595,10 @@ def bench_prefill(args):
 
     def chunks(dense):
         for j in range(nch):
-            pf.chunk(q_dev[j], j * T, 10**9 if dense else max(1, (j + 1) * T // 16))
+            if dense:
+                pf_dense.chunk(q_dev[j], j * T, 10**9)
+            else:
+                pf.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
 
     build()
     chunks(False)
@@ -606,9 +615,11 @@ def bench_prefill(args):
     # partials written and read, the output
     nbk, row, G = c.B * c.Hkv, c.hd * 2, c.Hq // c.Hkv
     chunk_bytes = 0
+    at_cap = 0
     for j in range(nch):
         pf.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
-        sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
+        sel, cnt = pf.sel.cpu().numpy(), pf.count.cpu().numpy()
+        at_cap += int((cnt == pf.k_max).sum())
         ends, off = pf.ends.cpu().numpy(), ix.offsets.cpu().numpy()
         vis_tok = 0
         for b in range(c.B):
@@ -620,10 +631,10 @@ def bench_prefill(args):
         win = min(W, (j + 1) * T)
         # a used slot (a listed block or the window) holds o and (m, l) for
         # every head, an unused one only (m, l); written, then read by the combine
-        used = G * (int(cnt.sum()) * ix.ts + nbk * T * ix.ls)
-        partials = 2 * (used * (c.hd + 2) + (c.B * c.Hq * T * ix.stride - used) * 2) * 4
+        used = G * (int(cnt.sum()) * pf.ts + nbk * T * pf.ls)
+        partials = 2 * (used * (c.hd + 2) + (c.B * c.Hq * T * pf.stride - used) * 2) * 4
         chunk_bytes += ((vis_tok + nbk * win) * row * 2 + c.B * c.Hq * T * c.hd * 2 * 2
-                        + nbk * T * (C + 1) * 4 + partials + nbk * C * 4)
+                        + nbk * T * (pf.k_max + 1) * 4 + partials + nbk * C * 4)
     cpu = None
     if not args.no_cpu_baseline:
         # the oracle's prefill of one (sequence, KV head): its index (spherical
@@ -648,7 +659,7 @@ def bench_prefill(args):
             for j in picks:
                 t1 = time.perf_counter()
                 sem.prefill_chunk(Kf, Vf, qf[j * T:(j + 1) * T], mu, perm, offs, j * T, W, max(1, (j + 1) * T // 16),
-                                  C, 1.0 / np.sqrt(c.hd))
+                                  pf.k_max, 1.0 / np.sqrt(c.hd))
                 times.append(time.perf_counter() - t1)
                 if time.time() > t_end:
                     break
@@ -666,11 +677,12 @@ def bench_prefill(args):
                 "V N(0,1), query rows around 4 topics per (b, kvh)",
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "prompt": L, "chunk": T, "window": W, "blocks": C, "iterations": args.iterations,
+                   "k_max": pf.k_max, "token_splits": pf.ts,
                    "budget": "1/16 of the chunk's length"},
         "index_build_ms": round(build_ms, 3), "sparse_chunks_ms": round(sparse_ms, 3),
         "dense_chunks_ms": round(dense_ms, 3), "speedup_vs_dense": round(dense_ms / total_ms, 2),
         "us_per_chunk": round(sparse_ms * 1e3 / nch, 2),
-        "bytes_sparse_chunks": chunk_bytes,
+        "bytes_sparse_chunks": chunk_bytes, "rows_at_k_max": at_cap,
         "roofline": roofline_record("every launch of the sparse chunks (visible ends, block choice, plan, grouped "
                                     "decode, window decode, combine)", chunk_bytes, sparse_ms),
         "cpu_baseline": cpu,

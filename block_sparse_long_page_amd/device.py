@@ -321,30 +321,57 @@ class BlockIndex:
 
 class ChunkedPrefill:
     """Sparse prefill of a prompt over one block index of the whole prompt
-    (BlockIndex with num_tokens = the prompt length, Q = the chunk's rows):
-    the rows at [c0, c0 + Q) see the index only before their window
-    [c0 + Q - window, c0 + Q) (sparse_attn_blocks_visible), choose blocks
-    under the token budget, read each chosen block once for all the chunk's
-    rows plus the window causally (sparse_attn_decode_blocks), and combine.
-    The cache's lengths are set to c0 + Q for the chunk."""
+    (a built BlockIndex with num_tokens = the prompt length): the Q rows at
+    [c0, c0 + Q) see the index only before their window [c0 + Q - window,
+    c0 + Q) (sparse_attn_blocks_visible), choose at most k_max blocks under
+    the token budget, read each chosen block once for all the chunk's rows
+    (split into token_splits chunks) plus the window causally
+    (sparse_attn_decode_blocks), and combine.  The cache's lengths are set to
+    c0 + Q for the chunk."""
 
-    def __init__(self, ix: "BlockIndex", window: int):
-        self.ix, self.window = ix, window
+    def __init__(self, ix: "BlockIndex", Q: int, window: int, k_max: Optional[int] = None, token_splits: int = 1,
+                 local_splits: int = 1, out_dtype: Optional[int] = None):
         c = ix.c
-        self.ends = torch.zeros((c.B, c.Hkv, ix.C), dtype=torch.int32, device=c.k.device)
+        self.ix, self.c, self.Q, self.window = ix, c, Q, window
+        self.k_max = k_max or ix.C
+        self.ts, self.ls = token_splits, local_splits
+        dev = c.k.device
+        self.ends = torch.zeros((c.B, c.Hkv, ix.C), dtype=torch.int32, device=dev)
         self.index = B.make_block_index(num_tokens=ix.N, num_blocks=ix.C, offsets=ix.offsets,
                                         positions=ix.positions, centres=ix.centres, k_blocks=ix.k_blocks,
                                         v_blocks=ix.v_blocks, visible_end=self.ends)
+        self.desc = c.desc()
+        self.rows = c.B * c.Hq * Q
+        self.sel = torch.full((c.B, c.Hkv, Q, self.k_max), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((c.B, c.Hkv, Q), dtype=torch.int32, device=dev)
+        self.stride = self.k_max * self.ts + self.ls
+        self.ws_bytes = B.sparse_attn_blocks_workspace_bytes(self.desc, self.index)
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.part_o = torch.empty((self.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((self.rows, self.stride, 2), dtype=torch.float32, device=dev)
+        self.out_dtype = c.dtype if out_dtype is None else out_dtype
+        self.out = torch.empty((self.rows, c.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
+        self.lse = torch.empty((self.rows,), dtype=torch.float32, device=dev)
 
     def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
-        ix = self.ix
-        ix.c.seq_lens.fill_(c0 + ix.Q)
-        B.sparse_attn_blocks_visible(ix.desc, self.index, self.window, self.ends, stream)
-        B.sparse_attn_select_blocks(ix.desc, self.index, q, ix.Q, budget, ix.k_max, ix.sel, ix.count, stream)
-        B.sparse_attn_decode_blocks(ix.desc, self.index, q, ix.Q, ix.sel, ix.count, ix.k_max, self.window, 0.0,
-                                    ix.ts, ix.ls, ix.part_o, ix.part_ml, ix.ws, ix.ws_bytes, stream)
-        ix.combine(stream=stream)
-        return ix.out
+        self.c.seq_lens.fill_(c0 + self.Q)
+        B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
+        B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
+                                    stream)
+        B.sparse_attn_decode_blocks(self.desc, self.index, q, self.Q, self.sel, self.count, self.k_max, self.window,
+                                    0.0, self.ts, self.ls, self.part_o, self.part_ml, self.ws, self.ws_bytes, stream)
+        B.sparse_attn_combine(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out, self.out_dtype,
+                              self.lse, stream)
+        return self.out
+
+    def out_f32(self) -> np.ndarray:
+        o = self.out.cpu().numpy()
+        if self.out_dtype == B.SA_BF16:
+            o = (o.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        return o.reshape(self.c.B, self.c.Hq, self.Q, self.c.hd)
+
+    def lse_f32(self) -> np.ndarray:
+        return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)
 
 
 class KeyDiffEviction:

@@ -32,7 +32,7 @@ CASES = {
 }
 
 
-def _setup(name, seed=0):
+def _setup(name, seed=0, ts=1, k_max=None):
     G, hd, nblk, T, W, C = CASES[name]
     wl = configs.SEMANTIC_512K.scaled(batch=2, num_q_heads=2 * G, num_kv_heads=2, head_dim=hd,
                                       context=nblk * 64 + 5, page_size=64, window=T, budget=4 * 64, q_rows=T)
@@ -45,7 +45,7 @@ def _setup(name, seed=0):
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
     ix.build(iterations=3)
     torch.cuda.synchronize()
-    return pr, c, dc, ix, ChunkedPrefill(ix, W), q_all, L, T, W, C
+    return pr, c, dc, ix, ChunkedPrefill(ix, T, W, k_max=k_max, token_splits=ts), q_all, L, T, W, C
 
 
 def _qchunk(q_all, c0, T):
@@ -57,9 +57,10 @@ def _qgroup(q_all, c, b, kvh, pos):
     return np.stack([to_f32(q_all[b, kvh * G + h, pos], c.dtype).astype(np.float64) for h in range(G)])
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_prefill_chunks_match_the_oracle(name):
-    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=1)
+@pytest.mark.parametrize("name,ts,k_max", [(n, 1, None) for n in CASES] + [("g4-hd128", 3, None),
+                                                                          ("g8-hd128-chunk64", 2, 3)])
+def test_prefill_chunks_match_the_oracle(name, ts, k_max):
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=1, ts=ts, k_max=k_max)
     G = c.Hq // c.Hkv
     perm_all, off_all = ix.positions.cpu().numpy(), ix.offsets.cpu().numpy()
     mu_all = ix.centres.cpu().numpy().astype(np.float64)
@@ -71,8 +72,8 @@ def test_prefill_chunks_match_the_oracle(name):
         pf.chunk(_qchunk(q_all, c0, T), c0, budget)
         torch.cuda.synchronize()
         ends = pf.ends.cpu().numpy()
-        sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
-        out, lse = ix.out_f32(), ix.lse_f32()
+        sel, cnt = pf.sel.cpu().numpy(), pf.count.cpu().numpy()
+        out, lse = pf.out_f32(), pf.lse_f32()
         bound = c0 + T - W
         for b in range(c.B):
             for kvh in range(c.Hkv):
@@ -84,7 +85,7 @@ def test_prefill_chunks_match_the_oracle(name):
                     pos = c0 + i
                     qg = _qgroup(q_all, c, b, kvh, pos)
                     s = sem.block_scores(qg, mu)
-                    want = sem.select_blocks(s, vis, budget, C)
+                    want = sem.select_blocks(s, vis, budget, pf.k_max)
                     got = sel[b, kvh, i, :cnt[b, kvh, i]]
                     assert np.all(np.diff(got) > 0) and np.all(vis[got] > 0)
                     order = sorted((x for x in range(C) if vis[x] > 0), key=lambda x: (-s[x], x))
@@ -103,17 +104,18 @@ def test_prefill_chunks_match_the_oracle(name):
     assert exact > 0
 
 
-@pytest.mark.parametrize("name", ["g4-hd128", "g2-hd64-ragged"])
-def test_prefill_with_every_block_is_dense_causal(name):
+@pytest.mark.parametrize("name,ts", [("g4-hd128", 1), ("g2-hd64-ragged", 4)])
+def test_prefill_with_every_block_is_dense_causal(name, ts):
     """Every chunk of the prompt with an unlimited budget: each row attends
-    its whole prefix exactly once (visible block parts + window)."""
-    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=2)
+    its whole prefix exactly once (visible block parts + window), whatever
+    the token chunks per block."""
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=2, ts=ts)
     G = c.Hq // c.Hkv
     keys = [[dense_keys_values(c, b, kvh) for kvh in range(c.Hkv)] for b in range(c.B)]
     for c0 in range(0, L - T + 1, T):
         pf.chunk(_qchunk(q_all, c0, T), c0, 10**9)
         torch.cuda.synchronize()
-        out, lse = ix.out_f32(), ix.lse_f32()
+        out, lse = pf.out_f32(), pf.lse_f32()
         ref_o = np.zeros(out.shape)
         ref_l = np.zeros(lse.shape)
         for b in range(c.B):
