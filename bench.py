@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--token-splits", type=int, default=0,
                     help="semantic-512k: token chunks per page; semantic-prefill-64k: per block (0: default)")
     ap.add_argument("--iterations", type=int, default=8, help="semantic-512k-index: k-means iterations")
+    ap.add_argument("--k-max", type=int, default=8, help="semantic-prefill-64k: most blocks a row takes")
     ap.add_argument("--score", default="quest", choices=["quest", "mean", "centroid", "compressed"],
                     help="llama3-70b-layer-128k: page summary and score (compressed: mean keys of two-page "
                          "blocks with a one-page stride)")
@@ -574,11 +575,11 @@ def bench_prefill(args):
     q0 = np.ascontiguousarray(q_all[0, :c.Hq // c.Hkv])  # sequence 0's first group, for the CPU baseline
     del q_all
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
-    # at most 16 blocks per row (the budget, 1/16 of at most 65600 tokens,
+    # at most 8 blocks per row (the budget, 1/16 of at most 65600 tokens,
     # holds about 2 blocks of the average 2048 tokens; rows that reach the cap
-    # are counted below), each block in 4 token chunks so that the few blocks
+    # are counted below), each block in 3 token chunks so that the few blocks
     # a chunk reads spread over the GPU; the dense run takes every block
-    pf = ChunkedPrefill(ix, T, W, k_max=min(C, 16), token_splits=args.token_splits or 4)
+    pf = ChunkedPrefill(ix, T, W, k_max=min(C, args.k_max), token_splits=args.token_splits or 3)
     pf_dense = ChunkedPrefill(ix, T, W, k_max=C, token_splits=1)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
