@@ -6,12 +6,13 @@
 // rows that chose each page, and then streams every page of the union once.
 //
 // k_group_plan: one workgroup per (sequence, KV head).  Builds the row masks
-// in LDS with 64-bit atomic ORs, writes the pages that carry a mask as
-// records (page, physical page, mask) in launch order (costliest first),
-// records for every row its index in its own list of each
-// page of the union (the row's slot for that page), and marks every slot a
-// row does not use (entries past its count) as an empty partial (m = -inf,
-// l = 0; the combine leaves its o out).
+// (two 64-bit words per page, up to 128 rows) in LDS with atomic ORs, writes
+// the pages that carry a mask as records (page, physical page, rows) in
+// launch order (costliest first), records for every row its index in its
+// own list of each page of the union (the row's slot for that page; -1 for
+// the rows that did not choose it), and marks every slot a row does not use
+// (entries past its count) as an empty partial (m = -inf, l = 0; the
+// combine leaves its o out).
 //
 // k_group_decode_mfma: one workgroup per (sequence, KV head, page of the
 // union, token chunk of the page), launched with the costliest pages (tokens
@@ -70,17 +71,18 @@ struct Regions {
 
 __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
 {
-    extern __shared__ unsigned long long mask[];  // [npg], then each unit's launch rank
+    extern __shared__ unsigned long long mask[];  // [npg][2] (rows 0-63, 64-127), then each unit's launch rank
     __shared__ int by_cost[256];
+    __shared__ int s_nunion;
     const Geometry& g = a.g;
     const int npg = a.npg;
-    int* rank = (int*)(mask + npg);
+    int* rank = (int*)(mask + 2 * npg);
     const int bk = blockIdx.x, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
     const int tid = threadIdx.x;
     const Regions rg(g, b, a.S, a.W);
     // candidates: the pages with middle-region tokens, or every block
     const int lo = a.blk_off ? 0 : rg.plo, hi = a.blk_off ? npg - 1 : rg.phi;
-    for (int p = tid; p < npg; p += kPlanThreads) mask[p] = 0ull;
+    for (int p = tid; p < 2 * npg; p += kPlanThreads) mask[p] = 0ull;
     __syncthreads();
 
     const int32_t* sel = a.sel + (long)bk * a.Q * a.k_max;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         const int c = imax(0, imin(cnt[r], a.k_max));
         if (j < c) {
             const int p = sel[idx];
-            if (p >= lo && p <= hi) atomicOr(&mask[p], 1ull << r);
+            if (p >= lo && p <= hi) atomicOr(&mask[2 * p + (r >> 6)], 1ull << (r & 63));
         } else {
             // a slot this row does not use: an empty partial (m = -inf, l = 0)
             // for every head and chunk; the combine does not read its o
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         } else {
             ntok = imin((p + 1) * g.P, rg.ws) - imax(p * g.P, rg.se);
         }
-        const uint64_t cost = (uint64_t)imax(1, ntok) * (uint64_t)(8 + __builtin_popcountll(mask[p]));
+        const int nrows = __builtin_popcountll(mask[2 * p]) + __builtin_popcountll(mask[2 * p + 1]);
+        const uint64_t cost = (uint64_t)imax(1, ntok) * (uint64_t)(8 + nrows);
         const int lb = 63 - __builtin_clzll(cost);
         const int frac = lb >= 2 ? (int)((cost >> (lb - 2)) & 3u) : 0;
         return 255 - (4 * lb + frac);  // 0: the costliest
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     for (int c = tid; c < 256; c += kPlanThreads) by_cost[c] = 0;
     __syncthreads();
     for (int p = tid; p < npg; p += kPlanThreads)
-        if (mask[p] != 0ull) atomicAdd(&by_cost[cost_bucket(p)], 1);
+        if ((mask[2 * p] | mask[2 * p + 1]) != 0ull) atomicAdd(&by_cost[cost_bucket(p)], 1);
     __syncthreads();
     if (tid == 0) {
         int acc = 0;
@@ -140,33 +143,36 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
             acc += nc;
         }
         a.nunion[bk] = acc;
+        s_nunion = acc;
     }
     __syncthreads();
     GroupPage* up = a.upages + (long)bk * npg;
     const int32_t* btr = g.block_table + (long)b * g.max_pages;
     for (int p = tid; p < npg; p += kPlanThreads) {
-        const unsigned long long m = mask[p];
-        if (m != 0ull) {
+        const unsigned long long m0 = mask[2 * p], m1 = mask[2 * p + 1];
+        if ((m0 | m1) != 0ull) {
             const int at = atomicAdd(&by_cost[cost_bucket(p)], 1);
             const int ph = a.blk_off ? 0 : btr[p];  // blocks: rows of the block layout
             GroupPage e;
             e.page = p;
             e.phys = ph >= 0 && ph < g.num_phys ? ph : -1;
-            e.mask_lo = (uint32_t)m;
-            e.mask_hi = (uint32_t)(m >> 32);
+            e.nrows = __builtin_popcountll(m0) + __builtin_popcountll(m1);
+            e.pad = 0;
             up[at] = e;
             rank[p] = at;
         }
     }
+    // every row's slot of every union page starts as "not chosen"
+    int16_t* sl = a.slots + (long)bk * npg * kGroupMaxRows;
+    for (int idx = tid; idx < s_nunion * kGroupMaxRows; idx += kPlanThreads) sl[idx] = -1;
     __syncthreads();
 
     // each row's index j of every page it lists: its slot for that page
-    int16_t* sl = a.slots + (long)bk * npg * 64;
     for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
         const int r = idx / a.k_max, j = idx - r * a.k_max;
         if (j < imax(0, imin(cnt[r], a.k_max))) {
             const int p = sel[idx];
-            if (p >= lo && p <= hi) sl[rank[p] * 64 + r] = (int16_t)j;
+            if (p >= lo && p <= hi) sl[rank[p] * kGroupMaxRows + r] = (int16_t)j;
         }
     }
 }
@@ -191,7 +197,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES];
     auto kl = [&](int buf) { return smem + buf * KBUF; };
     auto vl = [&](int buf) { return smem + 2 * KBUF + buf * VBUF; };
-    __shared__ int rows_l[64], slot_l[64];
+    __shared__ int rows_l[kGroupMaxRows], slot_l[kGroupMaxRows];
+    static_assert(kGroupMaxRows == 128, "two slot entries per lane");
     static_assert(kStage % 16 == 0, "stages hold whole subtiles");
 
     const Geometry& g = a.g;
@@ -202,19 +209,29 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
     const long ui = (long)bk * a.npg + rank;  // rank < npg: the record exists
     const GroupPage e = a.upages[ui];
-    const int16_t lane_slot = a.slots[ui * 64 + (threadIdx.x & 63)];  // with the record, not after it
+    // this lane's two rows' slots, loaded with the record, not after it
+    const int16_t slot0 = a.slots[ui * kGroupMaxRows + (threadIdx.x & 63)];
+    const int16_t slot1 = a.slots[ui * kGroupMaxRows + 64 + (threadIdx.x & 63)];
     if (rank >= a.nunion[bk]) return;
     const int p = e.page;
-    const unsigned long long M = ((unsigned long long)e.mask_hi << 32) | e.mask_lo;
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
     const Regions rg(g, b, a.S, a.W);
 
-    // the rows of the mask, ascending, and the page's index in each row's list
-    const int nr = __builtin_popcountll(M);
-    if (wave == 0 && ((M >> lane) & 1ull)) {
-        rows_l[lanes_below(M)] = lane;
-        slot_l[lanes_below(M)] = lane_slot;
+    // the rows that chose the page, ascending, and the page's index in each
+    // row's list (every wave takes the same ballots)
+    const uint64_t M0 = __builtin_amdgcn_ballot_w64(slot0 >= 0), M1 = __builtin_amdgcn_ballot_w64(slot1 >= 0);
+    const int n0 = __builtin_popcountll(M0);
+    const int nr = n0 + __builtin_popcountll(M1);
+    if (wave == 0) {
+        if (slot0 >= 0) {
+            rows_l[lanes_below(M0)] = lane;
+            slot_l[lanes_below(M0)] = slot0;
+        }
+        if (slot1 >= 0) {
+            rows_l[n0 + lanes_below(M1)] = 64 + lane;
+            slot_l[n0 + lanes_below(M1)] = slot1;
+        }
     }
     __syncthreads();
 
@@ -472,8 +489,8 @@ hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > 64 || a.npg > kGroupMaxPages) return hipErrorInvalidValue;
-    const size_t lds = (sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages) return hipErrorInvalidValue;
+    const size_t lds = (2 * sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_union < 1) return e;

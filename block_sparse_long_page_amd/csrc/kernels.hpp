@@ -10,8 +10,8 @@ namespace sa {
 constexpr int kSelCap = 1024;        // page-list entries the bf16 decode stages in LDS
 constexpr int kRowsWG = 2048;        // rows a decode workgroup resolves per prologue round
 constexpr int kFusedMaxCand = 8448;  // pages per sequence the select-and-decode kernel stages in LDS (256k + 8k tokens at P 32)
-constexpr int kGroupMaxPages = 4096; // pages per sequence the grouped decode's plan holds in LDS (12 B each)
-constexpr int kGroupMaxRows = 64;    // query rows of the grouped decode (one mask bit each)
+constexpr int kGroupMaxPages = 4096; // pages per sequence the grouped decode's plan holds in LDS (20 B each)
+constexpr int kGroupMaxRows = 128;   // query rows of the grouped decode (two 64-bit mask words per page)
 
 struct FastDivHost {
     uint32_t d, magic, shift;
@@ -86,9 +86,10 @@ struct SelectDecodeArgs {
 
 // A page of the union of the rows' page lists of one (sequence, KV head).
 struct __attribute__((aligned(16))) GroupPage {
-    int32_t page;               // logical page
-    int32_t phys;               // its physical page, -1 when unmapped
-    uint32_t mask_lo, mask_hi;  // the rows that chose it
+    int32_t page;   // logical page
+    int32_t phys;   // its physical page, -1 when unmapped
+    int32_t nrows;  // rows that chose it (the slot table names them)
+    int32_t pad;
 };
 
 // Multi-query decode grouped by page: the union of the rows' page lists is
@@ -108,7 +109,8 @@ struct GroupArgs {
     // workspace: the plan
     int32_t* nunion;    // [B][Hkv] pages in the union
     GroupPage* upages;  // [B][Hkv][npg] the union in launch order (costliest first)
-    int16_t* slots;     // [B][Hkv][npg][64] each row's list index of each union page (same order)
+    int16_t* slots;     // [B][Hkv][npg][kGroupMaxRows] each row's list index of each union page (same
+                        // order), -1 for a row that did not choose it
     int npg;            // candidate units per (sequence, KV head): max_pages, or the index's blocks
     // block mode (semantic index; blk_off == nullptr: pages of the paged
     // cache): the units are the blocks of a contiguous per-(b, KV head)

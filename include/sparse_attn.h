@@ -303,7 +303,7 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
  *                aligned (the per-(sequence, KV head) plan: the page union
  *                with its row masks in launch order, the rows' slots);
  *                needed when k_max > 0.
- * bf16 caches, num_q_rows <= 64, max_pages_per_seq <= 4096.  Results are
+ * bf16 caches, num_q_rows <= 128, max_pages_per_seq <= 4096.  Results are
  * bitwise reproducible (fixed slots, fixed merge order).
  * Errors: those of sparse_attn_decode; SA_ERR_UNSUPPORTED outside the limits
  * above; SA_ERR_INVALID_ARG for a bad split count, a small or misaligned
@@ -427,7 +427,7 @@ size_t sparse_attn_blocks_workspace_bytes(const sa_kv_desc* kv, const sa_block_i
  *               local_splits)
  *   workspace   >= sparse_attn_blocks_workspace_bytes(kv, index) bytes,
  *               256-byte aligned; needed when k_max > 0
- * bf16 caches, num_q_rows <= 64.  Results are bitwise reproducible.
+ * bf16 caches, num_q_rows <= 128.  Results are bitwise reproducible.
  * Errors: those of sparse_attn_decode_grouped and of the index checks;
  * SA_ERR_INVALID_ARG when window_len < num_q_rows or k_max > C.
  */

@@ -185,7 +185,7 @@ def test_decode_grouped_checks():
     d = _desc()
     ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
     # counts, page records (16 bytes), slots; each region 256-byte aligned
-    assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 64 * 2 + 255) // 256) * 256
+    assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 128 * 2 + 255) // 256) * 256
     assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
 
     def grouped(**kw):
@@ -214,7 +214,9 @@ def test_decode_grouped_checks():
     assert grouped(ws=None) == B.SA_ERR_INVALID_ARG
     assert grouped(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
     assert grouped(ws=DEV + 16) == B.SA_ERR_INVALID_ARG  # not 256-byte aligned
-    assert grouped(rows=65) == B.SA_ERR_UNSUPPORTED  # one mask bit per row
+    big = _desc(max_seq_len=256, max_pages_per_seq=16, num_phys_pages=32)
+    wsb = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(big))
+    assert grouped(desc=big, rows=129, wsb=wsb) == B.SA_ERR_UNSUPPORTED  # one mask bit per row, two 64-bit words
     assert grouped(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
     for bad, code in BAD_DESCS:
         assert grouped(desc=_desc(**bad)) == code
@@ -333,7 +335,7 @@ def test_block_index_checks():
     assert select(kmax=5) == B.SA_ERR_INVALID_ARG  # more than the index's blocks
 
     wsd = lib.sparse_attn_blocks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
-    assert wsd == 256 + up(nbk * C * 16) + up(nbk * C * 64 * 2)
+    assert wsd == 256 + up(nbk * C * 16) + up(nbk * C * 128 * 2)
 
     def decode(**kw):
         a = dict(q=DEV, rows=2, sel=DEV, cnt=DEV, kmax=2, W=4, scale=0.0, ts=1, ls=1, po=DEV, pml=DEV, ws=DEV, wsb=wsd)
@@ -349,7 +351,7 @@ def test_block_index_checks():
     assert decode(wsb=wsd - 1) == B.SA_ERR_INVALID_ARG
     assert decode(ts=0) == B.SA_ERR_INVALID_ARG
     assert decode(po=None) == B.SA_ERR_INVALID_ARG
-    assert decode(rows=65, W=65) == B.SA_ERR_UNSUPPORTED
+    assert decode(rows=129, W=129) != B.SA_OK  # past the row limit (and the 128-token cache)
 
 
 def test_keydiff_checks():

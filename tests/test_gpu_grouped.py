@@ -1,7 +1,7 @@
 """Parity of the multi-query decode grouped by page (sparse_attn_decode_grouped)
 with the fp64 oracle on the GPU's own per-row selection, against the per-row
 decode of the same selection, and its determinism.  Shapes cover every GQA
-group size, both head dims, pages of 16 to 2048 tokens, 5 to 64 query rows,
+group size, both head dims, pages of 16 to 2048 tokens, 5 to 128 query rows,
 windows shorter than the row count (causal masking of middle tokens), two
 passes over the query columns (G = 8 with 64 rows), rows whose lists are
 shorter than k_max, and several token and sink/window split counts."""
@@ -33,6 +33,11 @@ CASES = {
                               budget=1024, Q=9),
     "g4-p2048-q64-blocks": dict(B=1, Hq=8, Hkv=2, hd=128, P=2048, seq_lens=[16384 + 64], sink=0, window=64,
                                 budget=4096, Q=64),
+    # more than 64 rows: the second word of the row masks and of the slot table
+    "g4-p64-q128": dict(B=2, Hq=8, Hkv=2, hd=128, P=64, seq_lens=[4000, 3333], sink=32, window=128, budget=512,
+                        Q=128),
+    "g8-hd64-p32-q100-causal": dict(B=1, Hq=8, Hkv=1, hd=64, P=32, seq_lens=[2500], sink=16, window=50, budget=320,
+                                    Q=100),
 }
 
 
