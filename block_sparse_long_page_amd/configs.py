@@ -109,12 +109,12 @@ KEYDIFF_8K = Workload(
 )
 
 # chunked sparse prefill of a 64K-token prompt over one semantic block index
-# of the whole prompt: 64-row chunks whose window is the chunk itself,
+# of the whole prompt: 128-row chunks whose window is the chunk itself,
 # budget L/16 of each chunk's length
 SEMANTIC_PREFILL_64K = Workload(
     name="semantic-prefill-64k", batch=2, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16",
-    context=65536 + 64, page_size=2048, sink=0, window=64, budget=65536 // 16, mode="centroid",
-    q_rows=64, seed=6,
+    context=65536 + 128, page_size=2048, sink=0, window=128, budget=65536 // 16, mode="centroid",
+    q_rows=128, seed=6,
 )
 
 ALL = (TINY, QWEN3_8B, LLAMA3_70B, HYBRID_256K, SEMANTIC_512K, KEYDIFF_8K, SEMANTIC_PREFILL_64K)

@@ -25,18 +25,20 @@ if not torch.cuda.is_available():
 from block_sparse_long_page_amd.device import BlockIndex, ChunkedPrefill, DeviceCache, to_device  # noqa: E402
 
 CASES = {
-    # (G, head_dim, blocks of 64 tokens, chunk rows, window, index blocks)
+    # (G, head_dim, blocks of 64 tokens (128 for chunks of more than 64 rows), chunk rows, window, index blocks)
     "g4-hd128": (4, 128, 16, 16, 48, 12),
     "g2-hd64-ragged": (2, 64, 12, 24, 30, 9),
     "g8-hd128-chunk64": (8, 128, 20, 64, 64, 16),
+    "g4-hd128-chunk128": (4, 128, 20, 128, 128, 16),
 }
 
 
 def _setup(name, seed=0, ts=1, k_max=None):
     G, hd, nblk, T, W, C = CASES[name]
+    bt = 64 if T <= 64 else 128  # the generator appends the last chunk as one page
     wl = configs.SEMANTIC_512K.scaled(batch=2, num_q_heads=2 * G, num_kv_heads=2, head_dim=hd,
-                                      context=nblk * 64 + 5, page_size=64, window=T, budget=4 * 64, q_rows=T)
-    pr = synth.semantic_problem(wl, seed=seed, blocks=nblk, block_tokens=64, scatter=True)
+                                      context=nblk * bt + 5, page_size=bt, window=T, budget=4 * bt, q_rows=T)
+    pr = synth.semantic_problem(wl, seed=seed, blocks=nblk, block_tokens=bt, scatter=True)
     c = pr.cache
     L = int(c.seq_lens[0])
     rng = np.random.default_rng(seed)
