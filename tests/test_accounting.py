@@ -2,6 +2,7 @@
 import json
 import os
 
+import numpy as np
 import pytest
 
 from block_sparse_long_page_amd import accounting as acc
@@ -45,9 +46,25 @@ def test_read_time_floor():
     assert abs(ms - r["ms"]) <= r["tolerance"] * ms + 0.2
 
 
-@pytest.mark.parametrize("c", G["candidates"]["cases"], ids=lambda c: str(c["L"]))
-def test_candidate_counts(c):
-    assert acc.candidate_pages(c["L"], c["P"], c["S"], c["W"]) == c["candidates"]
+@pytest.mark.parametrize("L,P,S,W", [
+    (2048, 16, 16, 64),        # the tiny workload
+    (32768, 16, 256, 1024),    # the Qwen3-8B-shaped layer
+    (131072, 64, 256, 4096),   # the Llama-3-70B-shaped layer
+    (262144 + 5, 32, 256, 2048 + 5),  # a hybrid layer between refreshes (ragged last page)
+    (1000, 16, 40, 30),        # sink and window edges inside pages
+    (300, 16, 200, 100),       # sink and window meet: no middle region
+    (100, 16, 256, 64),        # sink longer than the sequence
+])
+def test_candidate_counts_match_the_oracle(L, P, S, W):
+    """The byte accounting's candidate count equals the number of pages the
+    oracle scores (the non-NaN entries of its score row)."""
+    import oracle
+    from block_sparse_long_page_amd import synth
+
+    pr = synth.random_problem(B=1, Hq=1, Hkv=1, hd=64, P=P, seq_lens=[L], sink=S, window=W, budget=P,
+                              dtype="f32", seed=L % 97)
+    r = oracle.run(pr.cache, pr.q, mode=oracle.QUEST, Q=1, sink=S, window=W, budget=P, want_scores=True)
+    assert int(np.count_nonzero(~np.isnan(r.scores[0, 0, 0]))) == acc.candidate_pages(L, P, S, W)
 
 
 def test_headline_step_bytes():

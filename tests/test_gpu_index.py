@@ -8,9 +8,11 @@ state: every key's block must be within the fp32 rounding bound of the best
 centre (computed in fp64 from the same bf16 operands), each centre update
 must match the oracle's update of the GPU's previous assignment, and the
 block layout, the copied keys and values and the block choice are compared
-exactly (the choice where no two block scores are within 1e-4 relative of
-each other at the budget's edge).  The decode is compared with the
-oracle's attention over the GPU's blocks and the window.  Shapes cover both
+exactly; the block choice must equal the oracle's where no two block scores
+at the budget's edge are within 1e-4 relative of each other, and elsewhere be
+what the greedy rule gives for an order consistent within that band
+(tests/parity.py::check_block_choice), with the number of such rows bounded.
+The decode is compared with the oracle's attention over the GPU's blocks and the window.  Shapes cover both
 head dims, several GQA groups, ragged chunk, segment and tile tails, more
 than 256 blocks (two rounds of centres in LDS), empty blocks, and keys
 interleaved in position order."""
@@ -20,7 +22,7 @@ import pytest
 from oracle import semantic as sem
 from block_sparse_long_page_amd import configs, synth
 from block_sparse_long_page_amd.synth import to_f32
-from parity import check_lse, check_output
+from parity import check_block_choice, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
 
@@ -163,32 +165,21 @@ def test_block_choice_matches_the_oracle(name, budget):
     ix.select(to_device(pr.q))
     st = _state(ix)
     sel, cnt = ix.sel.cpu().numpy(), ix.count.cpu().numpy()
-    exact = 0
+    ties = 0
     for b in range(c.B):
         for kvh in range(c.Hkv):
             mu = st["centres"][b, kvh]
             sizes = np.diff(st["offsets"][b, kvh])
             for i in range(pr.Q):
                 s = sem.block_scores(_query_group(pr, b, kvh, i), mu)
-                want = sem.select_blocks(s, sizes, ix.budget, ix.k_max)
                 got = sel[b, kvh, i, :cnt[b, kvh, i]]
                 assert (sel[b, kvh, i, cnt[b, kvh, i]:] == -1).all()
-                assert np.all(np.diff(got) > 0) and np.all(sizes[got] > 0)
-                # The taken blocks are a prefix of the score order; reordering
-                # inside it keeps every running count within the budget, so
-                # the choice depends on the order only through the last taken
-                # block, the first left out and the one after it.
-                order = sorted((x for x in range(C) if sizes[x] > 0), key=lambda x: (-s[x], x))
-                n = len(want)
-                edge = s[order[max(0, n - 1):n + 2]]
-                tau = 1e-4 * max(1e-30, np.abs(s).max())
-                if len(edge) < 2 or np.min(-np.diff(edge)) > tau:
-                    np.testing.assert_array_equal(got, want)
-                    exact += 1
-                else:  # near-equal scores at the edge: a valid choice of the same size rule
-                    assert 1 <= len(got) <= ix.k_max
-                    assert len(got) == 1 or sizes[got].sum() <= ix.budget
-    assert exact > 0
+                # the oracle's choice where the edge is clear; elsewhere the
+                # greedy rule's result for an order consistent within the band
+                ties += check_block_choice(got, s, sizes, ix.budget, ix.k_max)
+    rows = c.B * c.Hkv * pr.Q
+    print(f"{name} budget={budget}: {ties} of {rows} rows with a near tie at the edge")
+    assert ties <= max(2, rows // 10)
 
 
 @pytest.mark.parametrize("name", list(CASES))

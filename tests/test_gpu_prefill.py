@@ -3,7 +3,9 @@ sparse_attn_select_blocks and sparse_attn_decode_blocks over one index of the
 whole prompt) against the fp64 oracle of oracle/semantic.py, on the GPU's own
 index: the visible part of every block exactly, the block choice exactly
 where no two block scores are within 1e-4 relative of each other at the
-budget's edge, and the outputs against the oracle's attention over the GPU's
+budget's edge and elsewhere a valid greedy choice for an order consistent
+within that band (tests/parity.py::check_block_choice, such rows counted and
+bounded), and the outputs against the oracle's attention over the GPU's
 blocks (their visible rows) and the chunk's window.  With every block chosen
 each row must be dense causal attention over its prefix, chunk after chunk
 over the whole prompt."""
@@ -14,7 +16,7 @@ from oracle import semantic as sem
 from block_sparse_long_page_amd import configs, synth
 from block_sparse_long_page_amd.synth import to_f32
 from helpers import dense_keys_values, masked_attention
-from parity import check_lse, check_output
+from parity import check_block_choice, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +70,7 @@ def test_prefill_chunks_match_the_oracle(name, ts, k_max):
     mu_all = ix.centres.cpu().numpy().astype(np.float64)
     # the first chunk sees no index, the next ones a growing part, the last all but its window
     starts = sorted({0, T, (L - T) // 3, (L - T) // 2, L - T})
-    exact = 0
+    ties = rows = 0
     for c0 in starts:
         budget = max(1, (c0 + T) // 16)
         pf.chunk(_qchunk(q_all, c0, T), c0, budget)
@@ -87,23 +89,18 @@ def test_prefill_chunks_match_the_oracle(name, ts, k_max):
                     pos = c0 + i
                     qg = _qgroup(q_all, c, b, kvh, pos)
                     s = sem.block_scores(qg, mu)
-                    want = sem.select_blocks(s, vis, budget, pf.k_max)
                     got = sel[b, kvh, i, :cnt[b, kvh, i]]
-                    assert np.all(np.diff(got) > 0) and np.all(vis[got] > 0)
-                    order = sorted((x for x in range(C) if vis[x] > 0), key=lambda x: (-s[x], x))
-                    n = len(want)
-                    edge = s[order[max(0, n - 1):n + 2]] if order else np.zeros(0)
-                    tau = 1e-4 * max(1e-30, np.abs(s).max())
-                    if len(edge) < 2 or np.min(-np.diff(edge)) > tau:
-                        np.testing.assert_array_equal(got, want)
-                        exact += 1
+                    assert (sel[b, kvh, i, cnt[b, kvh, i]:] == -1).all()
+                    ties += check_block_choice(got, s, vis, budget, pf.k_max)
+                    rows += 1
                     toks = np.concatenate([perm[off[x]:off[x] + vis[x]] for x in got] +
                                           [np.arange(max(0, bound), pos + 1)]).astype(np.int64)
                     for h in range(G):
                         o, l_ = sem.attend(qg[h], K[toks], V[toks], 1.0 / np.sqrt(c.hd))
                         check_output(out[b, kvh * G + h, i][None], o[None], c.dtype, f"{name} c0={c0}")
                         check_lse(lse[b, kvh * G + h, i][None], np.array([l_]), f"{name} c0={c0}")
-    assert exact > 0
+    print(f"{name}: {ties} of {rows} rows with a near tie at the edge")
+    assert ties <= max(2, rows // 10)
 
 
 @pytest.mark.parametrize("name,ts", [("g4-hd128", 1), ("g2-hd64-ragged", 4)])

@@ -4,9 +4,9 @@ case, the Qwen3-8B-shaped and Llama-3-70B-shaped layers (the latter also with
 compressed-key scores), the 3-layer hybrid
 256k schedule (every refresh step and the last step) and the semantic-block
 512K chunk, paged and over a block index built from interleaved keys.  The
-oracle computes every output at these sizes (the index: its layout and the
-block choice of every row exactly, the assignment and the last centre
-update on samples, and the outputs of sampled rows)."""
+oracle computes every output at these sizes (the index: its layout exactly,
+every key's assignment within the rounding bound, the last centre update on
+samples, and every row's block choice and outputs)."""
 import time
 
 import numpy as np
@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from block_sparse_long_page_amd import configs, synth
-from parity import check_lse, check_output, check_selection
+from parity import check_block_choice, check_lse, check_output, check_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,7 @@ def test_semantic_index_workload():
     rng = np.random.default_rng(0)
     G = c.Hq // c.Hkv
     scale = 1.0 / np.sqrt(c.hd)
+    ties = 0
     for b in range(c.B):
         for kvh in range(c.Hkv):
             n_pages = -(-L // c.P)
@@ -168,14 +169,16 @@ def test_semantic_index_workload():
             p_ref, o_ref = sem.block_layout(asg[b, kvh], C)
             np.testing.assert_array_equal(off[b, kvh], o_ref)
             np.testing.assert_array_equal(perm[b, kvh], p_ref)
-            # sampled keys: the best centre within the rounding of bf16 products summed in fp32
-            ts = rng.choice(N, 4096, replace=False)
+            # every key: the best centre within the rounding of bf16 products summed in fp32
             cb = (cen[b, kvh].astype(np.float32).view(np.uint32).astype(np.uint64))
             cb = ((((cb + 0x7FFF + ((cb >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
                   .astype(np.float64))
-            d = K[ts] @ cb.T
-            bound = 1e-5 * (np.abs(K[ts]) @ np.abs(cb).T).max(axis=1)
-            assert np.all(d[np.arange(len(ts)), asg[b, kvh, ts]] >= d.max(axis=1) - bound)
+            for k0 in range(0, N, 1 << 16):
+                Kc = K[k0:min(N, k0 + (1 << 16))]
+                d = Kc @ cb.T
+                bound = 1e-5 * (np.abs(Kc) @ np.abs(cb).T).max(axis=1)
+                a = asg[b, kvh, k0:k0 + len(Kc)]
+                assert np.all(d[np.arange(len(Kc)), a] >= d.max(axis=1) - bound), (b, kvh, k0)
             # the last update of a few blocks from the previous assignment
             u = sem.unit_keys(K[:N])
             for x in rng.choice(C, 6, replace=False):
@@ -184,25 +187,23 @@ def test_semantic_index_workload():
                     want = u[members].sum(axis=0)
                     want /= np.linalg.norm(want)
                     np.testing.assert_allclose(cen[b, kvh, x], want, rtol=0, atol=2e-5)
-            # every row's block choice
+            # every row: its block choice, then the oracle's attention over the GPU's blocks and the window
             sizes = np.diff(off[b, kvh])
             for i in range(pr.Q):
                 qg = np.stack([synth.to_f32(pr.q[b, kvh * G + h, i], c.dtype).astype(np.float64) for h in range(G)])
                 s_ = sem.block_scores(qg, cen[b, kvh])
-                want = sem.select_blocks(s_, sizes, ix.budget, ix.k_max)
-                order = sorted((x for x in range(C) if sizes[x] > 0), key=lambda x: (-s_[x], x))
-                n = len(want)
-                edge = s_[order[max(0, n - 1):n + 2]]
                 got = sel[b, kvh, i, :cnt[b, kvh, i]]
-                if len(edge) < 2 or np.min(-np.diff(edge)) > 1e-4 * np.abs(s_).max():
-                    np.testing.assert_array_equal(got, want)
-                # sampled rows: the oracle's attention over the GPU's blocks and the window
-                if i % 16 == 5:
-                    pos = L - pr.Q + i
-                    toks = np.concatenate([perm[b, kvh, off[b, kvh, x]:off[b, kvh, x + 1]] for x in got] +
-                                          [np.arange(L - pr.window, pos + 1)])
-                    for h in range(G):
-                        o, l_ = sem.attend(qg[h], K[toks], V[toks], scale)
-                        check_output(out[b, kvh * G + h, i], o, c.dtype, f"b{b} kvh{kvh} row{i} head{h}")
-                        check_lse(np.array([lse[b, kvh * G + h, i]]), np.array([l_]), "index lse")
+                assert (sel[b, kvh, i, cnt[b, kvh, i]:] == -1).all()
+                ties += check_block_choice(got, s_, sizes, ix.budget, ix.k_max)
+                pos = L - pr.Q + i
+                toks = np.concatenate([perm[b, kvh, off[b, kvh, x]:off[b, kvh, x + 1]] for x in got] +
+                                      [np.arange(L - pr.window, pos + 1)])
+                Kt, Vt = K[toks], V[toks]
+                for h in range(G):
+                    o, l_ = sem.attend(qg[h], Kt, Vt, scale)
+                    check_output(out[b, kvh * G + h, i], o, c.dtype, f"b{b} kvh{kvh} row{i} head{h}")
+                    check_lse(np.array([lse[b, kvh * G + h, i]]), np.array([l_]), "index lse")
+    rows = c.B * c.Hkv * pr.Q
+    _say(f"[{wl.name} index] {ties} of {rows} rows with a near tie at the edge")
+    assert ties <= max(2, rows // 10)
     _say(f"[{wl.name} index] checked {time.time() - t0:.1f}s; blocks {sizes.min()}..{sizes.max()} tokens")
