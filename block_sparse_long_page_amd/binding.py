@@ -22,6 +22,7 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
 SA_F32, SA_BF16 = 0, 1
 SA_QUEST, SA_MEAN, SA_CENTROID, SA_COMPRESSED = 0, 1, 2, 3
 SA_PART_LOCAL, SA_PART_MIDDLE, SA_PART_ALL = 1, 2, 3
+SA_STEP_SEPARATE, SA_STEP_FUSED = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
@@ -73,6 +74,7 @@ _SIGS = {
     "sparse_attn_decode_step": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                                                ctypes.c_size_t, _P, _P, _P]),
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
+    "sparse_attn_step_path": (ctypes.c_int32, [_DESC, _I, _I, _I, _I, _P]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "sparse_attn_decode_grouped": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                   _P, ctypes.c_size_t, _P]),
@@ -150,6 +152,12 @@ def sparse_attn_select(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode: int
     _check(_lib.sparse_attn_select(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(meta), score_mode, sink_len,
                                    window_len, token_budget, _ptr(sel_pages), _ptr(sel_count), _ptr(workspace),
                                    workspace_bytes, _stream(stream)), "sparse_attn_select")
+
+
+def sparse_attn_step_path(kv: sa_kv_desc, sink_len: int, window_len: int, token_budget: int, num_splits: int,
+                          workspace) -> int:
+    return int(_lib.sparse_attn_step_path(ctypes.byref(kv), sink_len, window_len, token_budget, num_splits,
+                                          _ptr(workspace)))
 
 
 def sparse_attn_default_splits(kv: sa_kv_desc, num_q_rows: int, sink_len: int, window_len: int, k_max: int) -> int:

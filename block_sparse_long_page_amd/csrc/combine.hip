@@ -2,7 +2,9 @@
 // DeepSeek-V4 section: partial results are combined; FlashAttention's
 // running-max rescaling).  One wave per output row; the sums run over the
 // splits in a fixed order, so the result does not depend on timing.  A
-// partial with l = 0 is empty and its o is not read into the sum.
+// partial with l = 0 is empty and its o is not read into the sum; one with
+// l = NaN marks a share that was not computed and makes the row's output and
+// lse NaN.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -50,7 +52,8 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
             w = 0.f;
             if (s < n) {
                 const float2 p = *(const float2*)(ml + 2 * s);
-                w = p.y > 0.f ? expf(p.x - mx) * p.y : 0.f;
+                // l = NaN marks a share that was not computed: it poisons the row
+                w = p.y > 0.f ? expf(p.x - mx) * p.y : (p.y == p.y ? 0.f : p.y);
             }
         }
 #pragma unroll
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
         }
         if (s0 + UNROLL < n) fetch(s0 + UNROLL);
     }
-    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    const float inv = tot > 0.f ? 1.0f / tot : (tot == tot ? 0.f : tot);  // NaN stays NaN
     if constexpr (OUT_BF && CPL == 1) {
         uint16_t* out = (uint16_t*)a.out + (long)row * HD + lane;
         *out = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
         float* out = (float*)a.out + (long)row * HD + lane * CPL;
         for (int c = 0; c < CPL; ++c) out[c] = acc[c] * inv;
     }
-    if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+    if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? mx + logf(tot) : (tot == tot ? -INFINITY : tot);
 }
 
 }  // namespace

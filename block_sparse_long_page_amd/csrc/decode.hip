@@ -466,7 +466,7 @@ struct MfmaCore {
     // exponential per (wave, head) and writes the partial of its G heads:
     // part_o / part_ml rows prow0 + h * prow_step, slot `slot`.
     __device__ __forceinline__ void finish(float* part_o, float* part_ml, long prow0, long prow_step, int stride,
-                                           int slot)
+                                           int slot, bool failed = false)
     {
         // head r's sum over the 4 lanes holding it
         l_run += xor_lanes<16>(l_run);
@@ -502,11 +502,17 @@ struct MfmaCore {
                 os.z = fmaf(ow.z, wt, os.z);
                 os.w = fmaf(ow.w, wt, os.w);
             }
-            const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+            float inv = ls > 0.f ? 1.0f / ls : 0.f;
+            float mo = ls > 0.f ? ms * kLn2 : -INFINITY;
+            if (failed) {  // a share was left out: NaN partial, which poisons the row in the combine
+                inv = __builtin_nanf("");
+                mo = inv;
+                ls = inv;
+            }
             const long prow = (prow0 + h * prow_step) * stride + slot;
             *(float4*)(part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
             if (c4 == 0) {
-                part_ml[prow * 2 + 0] = ls > 0.f ? ms * kLn2 : -INFINITY;
+                part_ml[prow * 2 + 0] = mo;
                 part_ml[prow * 2 + 1] = ls;
             }
         }
@@ -609,8 +615,6 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
 // middle tokens and streams them, so no workgroup barrier stands between
 // the two shares and the K/V loads keep going while the pages are ranked.
 // The workgroup of split 0 also writes the page list and its count.
-
-constexpr int kSelSpinMax = 1 << 24;  // bound on the wait for the page list
 
 template <int HD, int G>
 __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mfma(SelectDecodeArgs a)
@@ -789,7 +793,12 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     // The only exit is at the end of a round of three, where the loads in
     // flight are in the same order as on the way round, so the waits inside
     // the loop stay at one tile each.
-    for (int step = 0; step < kSelSpinMax; ++step) {
+    // The wait for the page list is bounded (its publisher is a wave of this
+    // workgroup, so it ends long before the bound); a wave that reaches the
+    // bound leaves its share undone, and the workgroup then writes NaN
+    // partials and sets the status word instead of a wrong result.
+    bool done = false;
+    for (int step = 0; step < a.spin_max; ++step) {
         if (!have_mid && next >= nloc_w) poll();
         if (ra) core.compute(A, 0);
         ra = issue(A);
@@ -798,11 +807,17 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
         if (rc) core.compute(C, 0);
         rc = issue(C);
         if (!ra && !rb && !rc) {
-            if (have_mid && next >= nt) break;
+            if (have_mid && next >= nt) {
+                done = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(2);  // waiting for the page list
         }
     }
-    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
+    const bool failed = __syncthreads_or(!done) != 0;
+    if (failed && threadIdx.x == 0 && a.status) __hip_atomic_store(a.status, kStatusGaveUp, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT);
+    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split, failed);
 }
 
 template <int HD, int G>

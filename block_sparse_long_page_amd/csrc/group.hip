@@ -11,8 +11,9 @@
 // launch order (costliest first), records for every row its index in its
 // own list of each page of the union (the row's slot for that page; -1 for
 // the rows that did not choose it), and marks every slot a row does not use
-// (entries past its count) as an empty partial (m = -inf, l = 0; the
-// combine leaves its o out).
+// (entries past its count, outside the candidates, or not above the entry
+// before it) as an empty partial (m = -inf, l = 0; the combine leaves its o
+// out).
 //
 // k_group_decode_mfma: one workgroup per (sequence, KV head, page of the
 // union, token chunk of the page), launched with the costliest pages (tokens
@@ -87,12 +88,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
 
     const int32_t* sel = a.sel + (long)bk * a.Q * a.k_max;
     const int32_t* cnt = a.count + (long)bk * a.Q;
+    // The unit of entry idx = (row r, list index j) when the row uses it, it
+    // names a candidate unit and it lies above the entry before it (lists
+    // are ascending), else -1.  Entries past the count, outside the
+    // candidates, or not above their predecessor (a repeated unit among
+    // them) are not attended: their slots hold empty partials, so a page is
+    // attended at most once per row and the results stay deterministic.
+    auto listed = [&](int idx, int r, int j) -> int {
+        if (j >= imax(0, imin(cnt[r], a.k_max))) return -1;
+        const int p = sel[idx];
+        if (p < lo || p > hi) return -1;
+        return j == 0 || p > sel[idx - 1] ? p : -1;
+    };
     for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
         const int r = idx / a.k_max, j = idx - r * a.k_max;
-        const int c = imax(0, imin(cnt[r], a.k_max));
-        if (j < c) {
-            const int p = sel[idx];
-            if (p >= lo && p <= hi) atomicOr(&mask[2 * p + (r >> 6)], 1ull << (r & 63));
+        const int p = listed(idx, r, j);
+        if (p >= 0) {
+            atomicOr(&mask[2 * p + (r >> 6)], 1ull << (r & 63));
         } else {
             // a slot this row does not use: an empty partial (m = -inf, l = 0)
             // for every head and chunk; the combine does not read its o
@@ -170,10 +182,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     // each row's index j of every page it lists: its slot for that page
     for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
         const int r = idx / a.k_max, j = idx - r * a.k_max;
-        if (j < imax(0, imin(cnt[r], a.k_max))) {
-            const int p = sel[idx];
-            if (p >= lo && p <= hi) sl[rank[p] * kGroupMaxRows + r] = (int16_t)j;
-        }
+        const int p = listed(idx, r, j);
+        if (p >= 0) sl[rank[p] * kGroupMaxRows + r] = (int16_t)j;
     }
 }
 

@@ -53,6 +53,7 @@ struct SelectArgs {
     int32_t* count;
     float* scores;   // workspace [B][Hkv][Q][max_pages]
     int score_only;  // 1: scores only (the select-and-decode kernel ranks them)
+    uint32_t* status;  // the step's status word, cleared by the score kernel (or null)
 };
 
 struct DecodeArgs {
@@ -82,7 +83,11 @@ struct SelectDecodeArgs {
     float* part_ml;
     int32_t* sel;
     int32_t* count;
+    uint32_t* status;  // set to kStatusGaveUp by a workgroup whose bounded wait ran out
+    int spin_max;      // bound on the wait for the page list (rounds)
 };
+
+constexpr uint32_t kStatusGaveUp = 1;  // a share of the attended set was not computed
 
 // A page of the union of the rows' page lists of one (sequence, KV head).
 struct __attribute__((aligned(16))) GroupPage {

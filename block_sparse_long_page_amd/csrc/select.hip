@@ -72,6 +72,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score_f32_mfma(SelectArgs 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, j = lane >> 4;
 
+    if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.status = 0u;
     int pid = blockIdx.y;
     const int row = pid % a.Q;
     pid /= a.Q;
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score_quest_mfma(SelectArg
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, j = lane >> 4;
 
+    if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.status = 0u;
     int pid = blockIdx.y;
     const int row = pid % a.Q;
     pid /= a.Q;

@@ -21,13 +21,22 @@ constexpr int kMaxSelectPages = 12288;  // the top-k workgroup holds one key per
 constexpr long kMaxGridY = 65535;
 constexpr int kMaxTokenSplits = 64;  // token chunks per page of the grouped decode
 
+// debugging aids, read at every call
 bool sync_mode()
 {
-    static const int on = [] {
-        const char* e = getenv("SPARSE_ATTN_SYNC");
-        return e && e[0] == '1' ? 1 : 0;
-    }();
-    return on != 0;
+    const char* e = getenv("SPARSE_ATTN_SYNC");
+    return e && e[0] == '1';
+}
+
+// bound on the selecting kernel's wait for its page list (rounds of three
+// tiles); SPARSE_ATTN_SPIN_LIMIT lowers it to exercise the give-up path
+int spin_limit()
+{
+    constexpr int kDefault = 1 << 24;
+    const char* e = getenv("SPARSE_ATTN_SPIN_LIMIT");
+    if (!e || !e[0]) return kDefault;
+    const long v = strtol(e, nullptr, 10);
+    return v >= 1 && v < kDefault ? (int)v : kDefault;
 }
 
 int finish(hipError_t launch, hipStream_t s)
@@ -41,6 +50,11 @@ int finish(hipError_t launch, hipStream_t s)
 }
 
 bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// A launch of `wgs` workgroups of `threads` work-items each fits the
+// dispatch packet, whose grid size is a 32-bit count of work-items.
+bool grid_fits(long wgs, long threads) { return wgs >= 0 && wgs * threads <= 0xffffffffl; }
+constexpr long kDecodeThreads = 512;  // the largest decode workgroup (8 waves)
 
 // Validates the cache descriptor; fills `g` on success.
 int check_kv(const sa_kv_desc* kv, sa::Geometry* g)
@@ -94,6 +108,18 @@ long fused_min_splits(int32_t sink_len, int32_t window_len, int32_t k_max, int32
     return (toks + sa::kRowsWG - 18) / (sa::kRowsWG - 17);
 }
 
+// Whether sparse_attn_decode_step runs the select-and-decode kernel (else
+// the separate top-k and decode).  The kernel reads the block-table and score
+// rows as 16-byte vectors.
+bool fused_step_ok(const sa_kv_desc* kv, int32_t sink_len, int32_t window_len, int32_t k_max, int32_t num_splits,
+                   const void* workspace)
+{
+    const bool aligned = kv->max_pages_per_seq % 4 == 0 && ((uintptr_t)kv->block_table & 15) == 0 &&
+                         ((uintptr_t)workspace & 15) == 0;
+    return kv->dtype == SA_BF16 && k_max >= 1 && k_max <= sa::kSelCap && kv->max_pages_per_seq <= sa::kFusedMaxCand &&
+           aligned && num_splits >= fused_min_splits(sink_len, window_len, k_max, kv->page_size);
+}
+
 // workspace of the KeyDiff selection: the chunk key sums, then the order
 // keys of the distances (rows padded to a multiple of 4), each 256-byte
 // aligned
@@ -137,6 +163,11 @@ size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
     return sizeof(float) * (size_t)kv->batch * kv->num_kv_heads * rows * kv->max_pages_per_seq;
 }
 
+// the selecting step's workspace: the scores, then (256-byte aligned) its
+// status word
+size_t status_offset(const sa_kv_desc* kv, int32_t rows) { return (select_ws_bytes(kv, rows) + 255) & ~(size_t)255; }
+size_t step_ws_bytes(const sa_kv_desc* kv, int32_t rows) { return status_offset(kv, rows) + 256; }
+
 }  // namespace
 
 extern "C" {
@@ -155,7 +186,7 @@ const char* sparse_attn_status_string(int status)
 size_t sparse_attn_workspace_bytes(const sa_kv_desc* kv, int32_t num_q_rows)
 {
     if (!kv || num_q_rows < 1 || kv->batch < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1) return 0;
-    return select_ws_bytes(kv, num_q_rows);
+    return step_ws_bytes(kv, num_q_rows);
 }
 
 int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_t page_begin, int32_t page_end,
@@ -168,6 +199,8 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
     if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
     const int end = page_end < g.max_pages ? page_end : g.max_pages;
     if (end <= page_begin) return SA_OK;
+    // one wave per (sequence, page, KV head)
+    if (!grid_fits((long)kv->batch * (end - page_begin) * kv->num_kv_heads, 64)) return SA_ERR_UNSUPPORTED;
     sa::MetaArgs a{g, score_mode, page_begin, end, meta};
     return finish(sa::launch_page_meta(a, stream), stream);
 }
@@ -192,7 +225,7 @@ int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
         if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
     }
     sa::SelectArgs a{g, q, num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages, sel_count,
-                     (float*)workspace, 0};
+                     (float*)workspace, 0, nullptr};
     return finish(sa::launch_select(a, stream), stream);
 }
 
@@ -241,8 +274,8 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
     if (split_stride < num_splits || split_stride > kMaxSplits) return SA_ERR_INVALID_ARG;
     if (parts < SA_PART_LOCAL || parts > SA_PART_ALL) return SA_ERR_INVALID_ARG;
     if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
-    const long wgs = (long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits;
-    if (wgs > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
     sa::DecodeArgs a{g,        q,          num_q_rows, sel_pages, sel_count, sel_pages ? k_max : 0,
                      sink_len, window_len, parts,      scale * 1.4426950408889634f,   num_splits,
@@ -269,17 +302,13 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
     if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
     if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
     if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
     if (k_max > 0) {
         if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
-        if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
+        if (!workspace || workspace_bytes < step_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
     }
-    // the fused kernel reads the block-table and score rows as 16-byte vectors
-    const bool aligned = kv->max_pages_per_seq % 4 == 0 && ((uintptr_t)kv->block_table & 15) == 0 &&
-                         ((uintptr_t)workspace & 15) == 0;
-    const bool fused = kv->dtype == SA_BF16 && k_max >= 1 && k_max <= sa::kSelCap &&
-                       kv->max_pages_per_seq <= sa::kFusedMaxCand && aligned &&
-                       num_splits >= fused_min_splits(sink_len, window_len, k_max, kv->page_size);
+    const bool fused = fused_step_ok(kv, sink_len, window_len, k_max, num_splits, workspace);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
     if (!fused) {
         const int r1 = sparse_attn_select(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget,
@@ -288,15 +317,32 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
         return sparse_attn_decode(kv, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len, SA_PART_ALL,
                                   softmax_scale, num_splits, num_splits, part_o, part_ml, stream);
     }
+    uint32_t* status = (uint32_t*)((char*)workspace + status_offset(kv, num_q_rows));
     sa::SelectArgs sarg{g,        q,          num_q_rows, meta,      score_mode, sink_len, window_len,
-                        k_max,    sel_pages,  sel_count,  (float*)workspace, 1};
+                        k_max,    sel_pages,  sel_count,  (float*)workspace, 1, status};
     const int r1 = finish(sa::launch_select(sarg, stream), stream);
     if (r1 != SA_OK) return r1;
     sa::SelectDecodeArgs d{g,          q,          num_q_rows, (const float*)workspace,
                            k_max,      sink_len,   window_len, scale * 1.4426950408889634f,
                            num_splits, num_splits, part_o,     part_ml,
-                           sel_pages,  sel_count};
-    return finish(sa::launch_select_decode(d, stream), stream);
+                           sel_pages,  sel_count,  status,     spin_limit()};
+    const int r2 = finish(sa::launch_select_decode(d, stream), stream);
+    if (r2 != SA_OK || !sync_mode()) return r2;
+    // synchronised: a workgroup whose bounded wait ran out left NaN partials
+    uint32_t st = 0;
+    if (hipMemcpy(&st, status, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return SA_ERR_HIP;
+    return st == 0 ? SA_OK : SA_ERR_HIP;
+}
+
+int32_t sparse_attn_step_path(const sa_kv_desc* kv, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                              int32_t num_splits, const void* workspace)
+{
+    sa::Geometry g;
+    if (check_kv(kv, &g) != SA_OK || sink_len < 0 || window_len < 1 || token_budget < 0 || num_splits < 1)
+        return -SA_ERR_INVALID_ARG;
+    return fused_step_ok(kv, sink_len, window_len, token_budget / kv->page_size, num_splits, workspace)
+               ? SA_STEP_FUSED
+               : SA_STEP_SEPARATE;
 }
 
 size_t sparse_attn_grouped_workspace_bytes(const sa_kv_desc* kv)
@@ -329,7 +375,11 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
     if (kv->dtype != SA_BF16 || num_q_rows > sa::kGroupMaxRows || npg > sa::kGroupMaxPages)
         return SA_ERR_UNSUPPORTED;
     if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    if ((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
+    const long max_union = std::min<long>(npg, (long)num_q_rows * k_max);
+    if (!grid_fits(max_union * token_splits * kv->batch * kv->num_kv_heads, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
     const GroupedWs w = grouped_ws(kv, npg);
     if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
         return SA_ERR_INVALID_ARG;
@@ -337,7 +387,6 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
     const float sl2 = scale * 1.4426950408889634f;
     if (k_max > 0) {
         char* base = (char*)workspace;
-        const long max_union = std::min<long>(npg, (long)num_q_rows * k_max);
         sa::GroupArgs a{g,          q,          num_q_rows, sel,     cnt,
                         k_max,      sink_len,   window_len, sl2,     token_splits,
                         (int)stride, part_o,    part_ml,    (int32_t*)(base + w.nunion),
@@ -414,6 +463,8 @@ int sparse_attn_build_block_index(const sa_kv_desc* kv, int32_t iterations, cons
     if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
     if (iterations < 0 || iterations > 64) return SA_ERR_INVALID_ARG;
     if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    // the widest launch: one work-item per 16-byte piece of a key row (plus a workgroup of rounding)
+    if (!grid_fits((long)index->num_tokens * kv->head_dim / 8 + 256, 1)) return SA_ERR_UNSUPPORTED;
     const IndexWs w = index_ws(kv, index->num_tokens, index->num_blocks);
     if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0) return SA_ERR_INVALID_ARG;
     char* base = (char*)workspace;
@@ -451,7 +502,7 @@ int sparse_attn_select_blocks(const sa_kv_desc* kv, const sa_block_index* index,
     if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
     if (!q || !sel_blocks || !sel_count || num_q_rows < 1 || token_budget < 0) return SA_ERR_INVALID_ARG;
     if (k_max < 1 || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
-    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > 0x7fffffffl) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows, 256)) return SA_ERR_UNSUPPORTED;
     sa::SelectBlocksArgs a{g,          q,     num_q_rows, index->num_blocks, index->offsets, index->centres,
                            token_budget, k_max, sel_blocks, sel_count, index->visible_end};
     return finish(sa::launch_select_blocks(a, stream), stream);
@@ -548,6 +599,7 @@ int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, cons
         return SA_ERR_INVALID_ARG;
     if ((long)dst->max_pages_per_seq * dst->page_size < budget) return SA_ERR_INVALID_ARG;
     if ((long)src->batch * src->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits(((long)budget + 63) / 64, 256)) return SA_ERR_UNSUPPORTED;
     sa::CompactArgs a{gs, gd, budget, kept, kept_count};
     return finish(sa::launch_keydiff_compact(a, stream), stream);
 }
@@ -559,6 +611,7 @@ int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, 
     if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
     if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits(num_rows, 64)) return SA_ERR_UNSUPPORTED;
     sa::CombineArgs a{num_rows, head_dim, num_splits, out_dtype, part_o, part_ml, out, lse};
     return finish(sa::launch_combine(a, stream), stream);
 }

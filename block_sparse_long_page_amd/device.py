@@ -6,6 +6,7 @@ select (scores + per-KV-head top-k) -> decode (split-K attention) -> combine.
 """
 from __future__ import annotations
 
+import contextlib
 from dataclasses import dataclass
 from typing import Optional
 
@@ -16,6 +17,17 @@ from . import binding as B
 from .synth import Cache
 
 _TORCH_ELEM = {B.SA_F32: torch.float32, B.SA_BF16: torch.int16}
+
+
+def on_stream(stream):
+    """Context manager that queues torch's own work (fills, copies) on the
+    stream the library calls use: `stream` is None (torch's current stream),
+    a raw stream handle or a torch stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
 
 
 def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
@@ -354,7 +366,8 @@ class ChunkedPrefill:
         self.lse = torch.empty((self.rows,), dtype=torch.float32, device=dev)
 
     def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
-        self.c.seq_lens.fill_(c0 + self.Q)
+        with on_stream(stream):
+            self.c.seq_lens.fill_(c0 + self.Q)
         B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
         B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
                                     stream)
@@ -396,7 +409,8 @@ class KeyDiffEviction:
     def compact(self, stream=None):
         B.sparse_attn_keydiff_compact(self.src_desc, self.kept, self.count, self.budget, self.dst_desc, stream)
         # every KV head keeps min(L, budget) tokens: the first head's count is the sequence's
-        self.dst.seq_lens.copy_(self.count[:, 0])
+        with on_stream(stream):
+            self.dst.seq_lens.copy_(self.count[:, 0])
 
     def evict(self, stream=None):
         self.select(stream)

@@ -42,13 +42,17 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Ownership.  The caller allocates and owns every device buffer and the
- *   stream.  The library allocates nothing, frees nothing, keeps no mutable
- *   global state and never synchronises; calls on different streams are
- *   independent.  Work is queued on `stream` and is complete when the stream
- *   is.  All pointers are device pointers unless stated otherwise.
+ *   stream.  The library allocates nothing, frees nothing and never
+ *   synchronises; its only process-wide state is a table of occupancy
+ *   figures, each queried from the runtime once per kernel shape and
+ *   read-only afterwards.  Calls on different streams are independent.  Work
+ *   is queued on `stream` and is complete when the stream is.  All pointers
+ *   are device pointers unless stated otherwise.
  * Errors.  Every argument is checked on the host before any HIP call; a bad
  *   argument returns SA_ERR_INVALID_ARG or SA_ERR_UNSUPPORTED and queues
- *   nothing.  SA_ERR_HIP reports a failed kernel launch.  No C++ exception
+ *   nothing.  A call whose launches would exceed the dispatch limit of 2^32
+ *   work-items returns SA_ERR_UNSUPPORTED.  SA_ERR_HIP reports a failed
+ *   kernel launch.  No C++ exception
  *   crosses the boundary.  Device-side contents (seq_lens, block_table,
  *   selected pages) cannot be checked on the host: the kernels clamp
  *   seq_lens[b] to [0, max_pages_per_seq*page_size], ignore block-table
@@ -201,7 +205,8 @@ int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
                        int32_t* sel_pages, int32_t* sel_count, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
-/* Bytes of device workspace sparse_attn_select needs for this cache and row count. */
+/* Bytes of device workspace sparse_attn_select and sparse_attn_decode_step
+ * need for this cache and row count (the scores and the step's status word). */
 size_t sparse_attn_workspace_bytes(const sa_kv_desc* kv, int32_t num_q_rows);
 
 /*
@@ -262,13 +267,21 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
  *   Arguments as in sparse_attn_select and sparse_attn_decode (split_stride
  *   = num_splits).  Writes sel_pages / sel_count as sparse_attn_select does,
  *   and part_o / part_ml for sparse_attn_combine.
+ *   workspace   at least sparse_attn_workspace_bytes(kv, num_q_rows) bytes:
+ *               the scores, then a status word (cleared by the step's first
+ *               kernel).
  * The fused kernel runs for bf16 caches with 1 <= k_max <= 1024, at most 8448
  * pages per sequence, max_pages_per_seq a multiple of 4, block_table and
  * workspace 16-byte aligned, and num_splits >= (S + W + k_max * page_size) /
  * 2031 (at most 2048 row-table entries per workgroup, 15 of them padding);
  * any other valid call runs sparse_attn_select and then sparse_attn_decode,
- * with the same results.
- * Errors: those of sparse_attn_select and sparse_attn_decode.
+ * with the same results.  sparse_attn_step_path tells the caller which.
+ * A workgroup of the fused kernel waits for its page list (published by one
+ * of its own waves) for a bounded number of rounds; should the bound ever
+ * run out, the workgroup writes NaN partials (l = NaN, so the combined row
+ * is NaN, never a silently wrong value) and sets the status word.
+ * Errors: those of sparse_attn_select and sparse_attn_decode; with
+ * SPARSE_ATTN_SYNC=1, SA_ERR_HIP also when the status word is set.
  */
 int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
                             int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
@@ -286,9 +299,11 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
  * of the G heads of the group) that listed it, on the matrix cores.  The sink
  * and window tokens run through the per-row decode.
  *   sel_pages, sel_count, k_max  per-row page lists as sparse_attn_select
- *                writes them: ascending, distinct candidate pages; entries
- *                that are not give unspecified results (never an access out
- *                of bounds).  k_max = 0 attends the sink and window only.
+ *                writes them: ascending, distinct candidate pages.  An entry
+ *                outside the candidate pages, or not above the entry before
+ *                it (a repeated page among them), is not attended: its slot
+ *                holds an empty partial.  k_max = 0 attends the sink and
+ *                window only.
  *   token_splits 1..64 chunks of each page's middle tokens, one workgroup
  *                each (more workgroups for few, long pages).
  *   local_splits >= 1 splits of each row's sink and window tokens.
@@ -482,6 +497,15 @@ int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t b
 int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
                                 int32_t budget, const sa_kv_desc* dst, hipStream_t stream);
 
+/* Which kernels sparse_attn_decode_step queues for these arguments (host
+ * only): SA_STEP_FUSED (score kernel, then the select-and-decode kernel) or
+ * SA_STEP_SEPARATE (sparse_attn_select, then sparse_attn_decode);
+ * -SA_ERR_INVALID_ARG for a bad descriptor or range. */
+#define SA_STEP_SEPARATE 0
+#define SA_STEP_FUSED 1
+int32_t sparse_attn_step_path(const sa_kv_desc* kv, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                              int32_t num_splits, const void* workspace);
+
 /* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,
                                    int32_t k_max);
@@ -499,6 +523,8 @@ int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int
  *   lse    fp32 [num_rows] or NULL.
  * A part with l = 0 is empty: its o is not read into the sum (it may hold
  * anything).  A row whose parts are all empty gets out = 0 and lse = -inf.
+ * A part with l = NaN marks a share that was not computed (see
+ * sparse_attn_decode_step): the row's out and lse are NaN.
  * Errors: null pointers, num_rows < 1, head_dim not 64/128, num_splits
  * outside 1..1024, bad out_dtype.
  */

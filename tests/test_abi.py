@@ -26,7 +26,7 @@ def test_exports_every_header_function():
         "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes", "sparse_attn_index_workspace_bytes",
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
         "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
-        "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact"}
+        "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -93,7 +93,8 @@ def test_select_checks():
     lib = B.library()
     d = _desc()
     ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
-    assert ws == 4 * 2 * 2 * 1 * 8
+    # fp32 scores [B][Hkv][Q][max_pages], then a 256-byte status area of the selecting step
+    assert ws == ((4 * 2 * 2 * 1 * 8 + 255) // 256) * 256 + 256
 
     def sel(**kw):
         a = dict(q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, sel=DEV, cnt=DEV, ws=DEV, wsb=ws)
@@ -111,7 +112,7 @@ def test_select_checks():
     assert sel(W=0) == B.SA_ERR_INVALID_ARG  # the current token must be attended
     assert sel(budget=-1) == B.SA_ERR_INVALID_ARG
     assert sel(ws=None) == B.SA_ERR_INVALID_ARG
-    assert sel(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert sel(wsb=4 * 2 * 2 * 1 * 8 - 1) == B.SA_ERR_INVALID_ARG  # the scores alone do not fit
     assert sel(mode=7) == B.SA_ERR_UNSUPPORTED
 
 
@@ -422,3 +423,40 @@ def test_blocks_visible_checks():
     for bad, code in BAD_DESCS:
         assert vis(desc=_desc(**bad)) == code
 
+
+
+def test_launches_past_the_dispatch_limit_are_refused():
+    """A launch whose grid would exceed 2^32 work-items is refused on the
+    host (SA_ERR_UNSUPPORTED), before anything is queued."""
+    lib = B.library()
+    # decode: 1024 * 8 * 1 * 1024 workgroups of 512 work-items = 2^32
+    d = _desc(batch=1024, num_q_heads=8, num_kv_heads=8)
+    assert lib.sparse_attn_decode(ctypes.byref(d), DEV, 1, DEV, DEV, 2, 16, 16, 3, 0.0, 1024, 0, DEV, DEV,
+                                  None) == B.SA_ERR_UNSUPPORTED
+    ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
+    assert lib.sparse_attn_decode_step(ctypes.byref(d), DEV, 1, DEV, 0, 16, 16, 32, 0.0, 1024, DEV, DEV, DEV, ws,
+                                       DEV, DEV, None) == B.SA_ERR_UNSUPPORTED
+    # grouped: union of min(4096 pages, 128 rows * 8) = 1024 pages x 64 token chunks x 128 (b, kvh) x 512
+    g = _desc(batch=64, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=4096, num_phys_pages=4096,
+              max_seq_len=4096 * 16)
+    gws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(g))
+    assert lib.sparse_attn_decode_grouped(ctypes.byref(g), DEV, 128, DEV, DEV, 8, 16, 128, 0.0, 64, 1, DEV, DEV,
+                                          DEV, gws, None) == B.SA_ERR_UNSUPPORTED
+    # combine: one 64-lane wave per row
+    assert lib.sparse_attn_combine(1 << 26, 128, 2, DEV, DEV, DEV, 1, None, None) == B.SA_ERR_UNSUPPORTED
+
+
+def test_step_path_reports_the_kernels_decode_step_queues():
+    lib = B.library()
+    d = _desc(max_pages_per_seq=8)
+    ws = 0x10000  # 16-byte aligned
+    assert B.sparse_attn_step_path(d, 16, 16, 32, 4, ws) == B.SA_STEP_FUSED
+    assert B.sparse_attn_step_path(d, 16, 16, 32, 4, ws + 4) == B.SA_STEP_SEPARATE  # misaligned workspace
+    assert B.sparse_attn_step_path(_desc(dtype=B.SA_F32), 16, 16, 32, 4, ws) == B.SA_STEP_SEPARATE
+    assert B.sparse_attn_step_path(d, 16, 16, 0, 4, ws) == B.SA_STEP_SEPARATE  # no pages to select
+    assert B.sparse_attn_step_path(_desc(max_pages_per_seq=10, max_seq_len=160), 16, 16, 32, 4,
+                                   ws) == B.SA_STEP_SEPARATE  # rows not a multiple of 4 entries
+    # a sink + window + budget that one workgroup of the fused kernel cannot hold at one split
+    assert B.sparse_attn_step_path(d, 4000, 16, 32, 1, ws) == B.SA_STEP_SEPARATE
+    assert B.sparse_attn_step_path(_desc(batch=0), 16, 16, 32, 4, ws) == -B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_step_path(None, 16, 16, 32, 4, ws) == -B.SA_ERR_INVALID_ARG

@@ -114,3 +114,52 @@ def test_grouped_without_pages_is_the_sink_and_window():
     ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=0,
                      sel=sel, cnt=cnt)
     check_output(dec.out_f32(), ref.out, pr.cache.dtype, "no pages")
+
+
+def test_grouped_ignores_bad_list_entries():
+    """Entries outside the candidate pages, or not above the entry before
+    them (a repeated page among them), are not attended by the grouped
+    decode: its output equals the oracle over the lists with those entries
+    removed, and no slot is left unwritten (finite outputs)."""
+    pr = _problem("g4-p64-q16", seed=5)
+    dc, dec, gs, q = _setup(pr)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    sel, cnt = sel.copy(), cnt.copy()
+    c = pr.cache
+    k_max = sel.shape[-1]
+    for b in range(c.B):
+        L = int(c.seq_lens[b])
+        se = min(pr.sink, L)
+        ws = max(se, L - pr.window)
+        phi = (ws - 1) // c.P
+        for kvh in range(c.Hkv):
+            assert (cnt[b, kvh, :4] >= 4).all()
+            sel[b, kvh, 0, 1] = phi + 1 + kvh          # past the candidates (a window page or beyond)
+            sel[b, kvh, 1, 2] = sel[b, kvh, 1, 1]      # a repeated page
+            sel[b, kvh, 2, 3] = -7                     # negative
+            sel[b, kvh, 3, cnt[b, kvh, 3] - 1] = sel[b, kvh, 3, 0]  # below its predecessor
+    full = dec.sel.cpu().numpy()
+    full[..., :k_max] = sel
+    dec.sel.copy_(torch.from_numpy(full))
+    gs.decode(q)
+    gs.combine()
+    torch.cuda.synchronize()
+    clean_sel = np.full_like(sel, -1)
+    clean_cnt = np.zeros_like(cnt)
+    for b in range(c.B):
+        L = int(c.seq_lens[b])
+        se = min(pr.sink, L)
+        ws = max(se, L - pr.window)
+        plo, phi = se // c.P, (ws - 1) // c.P
+        for kvh in range(c.Hkv):
+            for i in range(pr.Q):
+                row = sel[b, kvh, i, :cnt[b, kvh, i]]
+                keep = [int(p) for j, p in enumerate(row) if plo <= p <= phi and (j == 0 or p > row[j - 1])]
+                clean_sel[b, kvh, i, :len(keep)] = keep
+                clean_cnt[b, kvh, i] = len(keep)
+    assert (clean_cnt < cnt).sum() == 4 * c.B * c.Hkv
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                     sel=clean_sel[..., :k_max], cnt=clean_cnt)
+    check_output(dec.out_f32(), ref.out, c.dtype, "bad entries")
+    check_lse(dec.lse_f32(), ref.lse, "bad entries")

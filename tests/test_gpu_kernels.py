@@ -424,3 +424,35 @@ def test_overlapped_sink_window_and_middle_decodes(name, splits):
 
 
 TOL_SPLIT = {0: 2e-6, 1: 1e-2}  # fp32 rounding only; bf16: outputs are rounded to bf16
+
+
+def test_select_decode_wait_bound_is_reported(monkeypatch):
+    """The select-and-decode kernel's wait for its page list is bounded.  With
+    the bound lowered to one round from the host (every wave still leaves its
+    loop and the kernel ends normally), the workgroups that could not finish
+    their share write NaN partials: the combined rows are NaN, never a silently
+    wrong value, and a synchronised call reports SA_ERR_HIP.  The next call at
+    the normal bound finds the status word cleared and matches the oracle."""
+    pr = synth.random_problem(B=1, Hq=8, Hkv=1, hd=128, P=64, seq_lens=[16384], sink=64, window=1024,
+                              budget=2048, mode="quest", dtype="bf16", seed=5, shuffle=True)
+    dc = DeviceCache.from_host(pr.cache)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, splits=2)
+    q = to_device(pr.q)
+    dec.build_meta()
+    assert B.sparse_attn_step_path(dec.desc, pr.sink, pr.window, pr.budget, dec.splits, dec.ws) == B.SA_STEP_FUSED
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SPARSE_ATTN_SPIN_LIMIT", "1")
+    monkeypatch.setenv("SPARSE_ATTN_SYNC", "1")
+    with pytest.raises(B.SparseAttnError) as err:
+        dec.select_decode(q)
+    assert err.value.status == B.SA_ERR_HIP
+    dec.combine()
+    torch.cuda.synchronize()
+    assert np.isnan(dec.out_f32()).all() and np.isnan(dec.lse_f32()).all()
+    monkeypatch.delenv("SPARSE_ATTN_SPIN_LIMIT")
+    dec.fused_step(q)  # still synchronised: the status word must read clear
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
+                     sel=sel, cnt=cnt)
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, "after the bound")
