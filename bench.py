@@ -107,6 +107,84 @@ def roofline_record(kernel: str, bytes_per_launch: int, launch_ms: float) -> dic
             "avg_launch_us": round(launch_ms * 1e3, 2)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (for the oracle's record)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+class Probes:
+    """The load-only reference kernels of libsa_probe.so (block_sparse_long_page_amd/csrc/probe.hip):
+    the attended K/V pages of a step read in the decode's tile pattern, and a contiguous read."""
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        path = os.path.join(ROOT, "block_sparse_long_page_amd", "libsa_probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        self.lib.sa_probe_pages.restype = I
+        self.lib.sa_probe_pages.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
+        self.lib.sa_probe_stream.restype = I
+        self.lib.sa_probe_stream.argtypes = [P, ctypes.c_size_t, I, P, P]
+        self.out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+
+    def pages(self, pool, slabs, offsets, problems, splits):
+        import torch
+
+        rc = self.lib.sa_probe_pages(pool.k.data_ptr(), pool.v.data_ptr(), slabs.data_ptr(), offsets.data_ptr(),
+                                     problems, splits, pool.P, pool.hd, 2, self.out.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, f"sa_probe_pages: {rc}"
+
+    def stream(self, buf, workgroups):
+        import torch
+
+        rc = self.lib.sa_probe_stream(buf.data_ptr(), buf.numel() * buf.element_size(), workgroups,
+                                      self.out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, f"sa_probe_stream: {rc}"
+
+
+def attended_slabs(table, P, Hkv, L, S, W, sel, cnt):
+    """Per (sequence, KV head) the physical page slabs a decode step attends
+    (sink pages, window pages, selected pages; each once), as a flat int32
+    list with offsets: the input of the load-only page probe."""
+    import numpy as np
+
+    B_ = table.shape[0]
+    slabs, offsets = [], [0]
+    n_pages = -(-L // P)
+    for b in range(B_):
+        for h in range(Hkv):
+            pages = set(range(0, -(-min(S, L) // P)))
+            pages |= set(range(max(0, L - W) // P, n_pages))
+            pages |= set(int(x) for x in sel[b, h, 0, :cnt[b, h, 0]])
+            slabs.extend(int(table[b, p]) * Hkv + h for p in sorted(pages))
+            offsets.append(len(slabs))
+    return np.asarray(slabs, dtype=np.int32), np.asarray(offsets, dtype=np.int32)
+
+
+def percentiles(ms_list):
+    """Median, p10 and p90 in microseconds of durations given in milliseconds."""
+    import numpy as np
+
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
 def copy_probe():
     import torch
 
@@ -984,6 +1062,53 @@ def main():
     torch.cuda.synchronize()
     dec_avg_ms = start.elapsed_time(stop) / K
 
+    # per-step distribution: one event between consecutive steps (each
+    # difference is a step plus one event record)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(K):
+        step(i % R)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    step_dist = percentiles([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
+    step_dist["method"] = f"{K} steps, an event between consecutive steps, replicas rotated"
+
+    # load-only references on the same box: the step's attended K/V pages in
+    # the decode's tile pattern and launch shape, and a contiguous read
+    probes = Probes()
+    slab_lists = []
+    for r in range(R):
+        s_np, o_np = attended_slabs(tables[r].cpu().numpy(), c.P, c.Hkv, L, pr.sink, pr.window, sel, cnt)
+        slab_lists.append((torch.from_numpy(s_np).cuda(), torch.from_numpy(o_np).cuda()))
+    probe_bytes = int(len(s_np)) * 2 * c.P * c.hd * 2
+    for i in range(3):
+        probes.pages(pool, *slab_lists[i % R], c.B * c.Hkv, dec.splits)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        probes.pages(pool, *slab_lists[i % R], c.B * c.Hkv, dec.splits)
+    stop.record()
+    torch.cuda.synchronize()
+    probe_ms = start.elapsed_time(stop) / K
+    sbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sbuf.fill_(1)
+    for i in range(2):
+        probes.stream(sbuf, 256 * 16)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(5):
+        probes.stream(sbuf, 256 * 16)
+    stop.record()
+    torch.cuda.synchronize()
+    stream_ms = start.elapsed_time(stop) / 5
+    del sbuf
+    probe_gbps = probe_bytes / (probe_ms * 1e-3) / 1e9
+    stream_ref = {"kernel": "k_probe_pages", "what": "load-only read of the step's attended K/V pages in 16-token "
+                                                     "tiles, the decode's launch shape, replicas rotated",
+                  "bytes": probe_bytes, "us": round(probe_ms * 1e3, 2), "GBps": round(probe_gbps, 1),
+                  "contiguous_read_GBps": round((1 << 30) / (stream_ms * 1e-3) / 1e9, 1)}
+
     ms_hot = dense_ms = float('nan')
     if not args.only_timed:
         # one replica (repeated reads may hit the last-level cache)
@@ -1031,7 +1156,7 @@ def main():
         cpu = {"value": round(sb.total / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
                "kind": "oracle", "sample": f"the full step (summaries of all pages, scores, top-k, attention) "
                                            f"in fp64, repeated {len(times)} times; median {med * 1e3:.1f} ms/step",
-               "ms_per_step": round(med * 1e3, 2)}
+               "ms_per_step": round(med * 1e3, 2), "cpu_model": cpu_model()}
 
     rec = {
         "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 128k ctx GQA-8",
@@ -1058,6 +1183,11 @@ def main():
                      "traffic": traffic_record(dec_kernel), "bytes_per_launch": dec_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
+        "step_us": step_dist,
+        "stream_ref": stream_ref,
+        "stream_ref_us": stream_ref["us"],
+        "frac_of_stream": round(gbps / probe_gbps, 4),
+        "pair_frac_of_stream": round(dec_gbps / probe_gbps, 4),
         "bytes_per_step": sb.as_dict(),
         "us_per_step_one_replica": None if args.only_timed else round(ms_hot * 1e3, 2),
         "dense_us_per_step": None if args.only_timed else round(dense_ms * 1e3, 2),

@@ -11,7 +11,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "keydiff.hip", "combine.hip", "sparse_attn.cpp"]
+# load-only reference kernels the benchmark times beside the path (not part of it)
+PROBE_LIB = os.path.join(PKG, "libsa_probe.so")
+PROBE_SOURCE = "probe.hip"
+SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "keydiff.hip", "combine.hip",
+           "sparse_attn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -36,14 +40,19 @@ def build(extra=(), jobs: int = 0) -> str:
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = LIB + ".tmp"
+    _link(objs, LIB)
+    _link([_compile(PROBE_SOURCE, list(extra))], PROBE_LIB)
+    return LIB
+
+
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":
