@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libsparse_attn.so")
 PROBE_LIB = os.path.join(PKG, "libsa_probe.so")
 PROBE_SOURCE = "probe.hip"
 SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "keydiff.hip", "combine.hip",
-           "sparse_attn.cpp"]
+           "noalloc.hip", "sparse_attn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(PKG, "libsparse_attn.so")
 HEADER = os.path.join(PKG, os.pardir, "include", "sparse_attn.h")
 
-SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_SCRATCH = 0, 1, 2, 3, 4
 SA_F32, SA_BF16 = 0, 1
 SA_QUEST, SA_MEAN, SA_CENTROID, SA_COMPRESSED = 0, 1, 2, 3
 SA_PART_LOCAL, SA_PART_MIDDLE, SA_PART_ALL = 1, 2, 3
@@ -76,6 +76,8 @@ _SIGS = {
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
     "sparse_attn_step_path": (ctypes.c_int32, [_DESC, _I, _I, _I, _I, _P]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "sparse_attn_decode_step_static": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P,
+                                                      _P, _I, _P, _P]),
     "sparse_attn_decode_grouped": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                   _P, ctypes.c_size_t, _P]),
     "sparse_attn_grouped_workspace_bytes": (ctypes.c_size_t, [_DESC]),
@@ -179,6 +181,15 @@ def sparse_attn_decode_step(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode
                                         window_len, token_budget, softmax_scale, num_splits, _ptr(sel_pages),
                                         _ptr(sel_count), _ptr(workspace), workspace_bytes, _ptr(part_o),
                                         _ptr(part_ml), _stream(stream)), "sparse_attn_decode_step")
+
+
+def sparse_attn_decode_step_static(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode: int, sink_len: int,
+                                   window_len: int, token_budget: int, softmax_scale: float, num_splits: int,
+                                   sel_pages, sel_count, out, out_dtype: int, lse=None, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_step_static(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(meta), score_mode,
+                                               sink_len, window_len, token_budget, softmax_scale, num_splits,
+                                               _ptr(sel_pages), _ptr(sel_count), _ptr(out), out_dtype, _ptr(lse),
+                                               _stream(stream)), "sparse_attn_decode_step_static")
 
 
 def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, part_ml, out, out_dtype: int,

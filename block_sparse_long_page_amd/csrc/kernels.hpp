@@ -211,6 +211,12 @@ struct CombineArgs {
     float* lse;
 };
 
+// The static device scratch of the entry point that allocates nothing:
+// its size, and its device address on the current device (taken once per
+// device with hipGetSymbolAddress, then kept).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
+
 // Each returns hipSuccess or the launch error; 1 for an unsupported
 // template combination (the host layer checks these first).
 hipError_t launch_page_meta(const MetaArgs& a, hipStream_t s);

@@ -168,6 +168,31 @@ size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
 size_t status_offset(const sa_kv_desc* kv, int32_t rows) { return (select_ws_bytes(kv, rows) + 255) & ~(size_t)255; }
 size_t step_ws_bytes(const sa_kv_desc* kv, int32_t rows) { return status_offset(kv, rows) + 256; }
 
+// The checks of sparse_attn_decode_step's arguments other than its
+// workspace and partials (shared with the variant that keeps them in the
+// static scratch).
+int check_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta, int32_t score_mode,
+               int32_t sink_len, int32_t window_len, int32_t token_budget, float softmax_scale, int32_t num_splits,
+               const int32_t* sel_pages, const int32_t* sel_count)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
+    if (!q || !meta || !sel_count || num_q_rows < 1 || sink_len < 0 || window_len < 1 || token_budget < 0)
+        return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    const int k_max = token_budget / kv->page_size;
+    if (k_max > 0 && !sel_pages) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
+    if (k_max > 0 && kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +204,7 @@ const char* sparse_attn_status_string(int status)
     case SA_ERR_INVALID_ARG: return "invalid argument";
     case SA_ERR_UNSUPPORTED: return "unsupported configuration";
     case SA_ERR_HIP: return "HIP launch error";
+    case SA_ERR_SCRATCH: return "needs more than the library's static scratch (16 MiB)";
     default: return "unknown status";
     }
 }
@@ -289,25 +315,14 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
                             void* workspace, size_t workspace_bytes, float* part_o, float* part_ml,
                             hipStream_t stream)
 {
-    sa::Geometry g;
-    const int rc = check_kv(kv, &g);
+    const int rc = check_step(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget, softmax_scale,
+                              num_splits, sel_pages, sel_count);
     if (rc != SA_OK) return rc;
-    if (score_mode < SA_QUEST || score_mode > SA_COMPRESSED) return SA_ERR_UNSUPPORTED;
-    if (!q || !meta || !sel_count || !part_o || !part_ml || num_q_rows < 1 || sink_len < 0 || window_len < 1 ||
-        token_budget < 0)
-        return SA_ERR_INVALID_ARG;
-    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (!part_o || !part_ml) return SA_ERR_INVALID_ARG;
     const int k_max = token_budget / kv->page_size;
-    if (k_max > 0 && !sel_pages) return SA_ERR_INVALID_ARG;
-    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
-    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
-    if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
-        return SA_ERR_UNSUPPORTED;
-    if (k_max > 0) {
-        if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
-        if (!workspace || workspace_bytes < step_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
-    }
+    if (k_max > 0 && (!workspace || workspace_bytes < step_ws_bytes(kv, num_q_rows))) return SA_ERR_INVALID_ARG;
+    sa::Geometry g;
+    (void)check_kv(kv, &g);  // validated above: fills g
     const bool fused = fused_step_ok(kv, sink_len, window_len, k_max, num_splits, workspace);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
     if (!fused) {
@@ -602,6 +617,39 @@ int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, cons
     if (!grid_fits(((long)budget + 63) / 64, 256)) return SA_ERR_UNSUPPORTED;
     sa::CompactArgs a{gs, gd, budget, kept, kept_count};
     return finish(sa::launch_keydiff_compact(a, stream), stream);
+}
+
+int sparse_attn_decode_step_static(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                                   int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                                   float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                                   void* out, int32_t out_dtype, float* lse, hipStream_t stream)
+{
+    // every check of both calls before any HIP call
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!out || num_q_rows < 1) return SA_ERR_INVALID_ARG;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    const long rows = (long)kv->batch * kv->num_q_heads * num_q_rows;
+    if (!grid_fits(rows, 64)) return SA_ERR_UNSUPPORTED;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t ws = up(step_ws_bytes(kv, num_q_rows));
+    const size_t po_bytes = up((size_t)rows * num_splits * kv->head_dim * sizeof(float));
+    const size_t pml_bytes = up((size_t)rows * num_splits * 2 * sizeof(float));
+    if (ws + po_bytes + pml_bytes > sa::kStaticScratchBytes) return SA_ERR_SCRATCH;
+    const int r0 = check_step(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget,
+                              softmax_scale, num_splits, sel_pages, sel_count);
+    if (r0 != SA_OK) return r0;
+    void* base = nullptr;
+    if (sa::static_scratch(&base) != hipSuccess) return SA_ERR_HIP;
+    float* part_o = (float*)((char*)base + ws);
+    float* part_ml = (float*)((char*)base + ws + po_bytes);
+    const int r1 = sparse_attn_decode_step(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget,
+                                           softmax_scale, num_splits, sel_pages, sel_count, base, ws, part_o, part_ml,
+                                           stream);
+    if (r1 != SA_OK) return r1;
+    return sparse_attn_combine((int32_t)rows, kv->head_dim, num_splits, part_o, part_ml, out, out_dtype, lse, stream);
 }
 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,

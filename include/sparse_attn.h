@@ -43,9 +43,10 @@
  * ---------------------------------------
  * Ownership.  The caller allocates and owns every device buffer and the
  *   stream.  The library allocates nothing, frees nothing and never
- *   synchronises; its only process-wide state is a table of occupancy
- *   figures, each queried from the runtime once per kernel shape and
- *   read-only afterwards.  Calls on different streams are independent.  Work
+ *   synchronises; its process-wide state is a table of occupancy figures,
+ *   each queried from the runtime once per kernel shape and read-only
+ *   afterwards, and the static scratch of sparse_attn_decode_step_static
+ *   (a device array of the code object, with its address per device).  Calls on different streams are independent.  Work
  *   is queued on `stream` and is complete when the stream is.  All pointers
  *   are device pointers unless stated otherwise.
  * Errors.  Every argument is checked on the host before any HIP call; a bad
@@ -86,6 +87,7 @@ extern "C" {
 #define SA_ERR_INVALID_ARG 1  /* null pointer, bad size or range, workspace too small */
 #define SA_ERR_UNSUPPORTED 2  /* valid but not built: head_dim, GQA ratio, dtype, mode */
 #define SA_ERR_HIP 3          /* a kernel launch failed (hipGetLastError) */
+#define SA_ERR_SCRATCH 4      /* sparse_attn_decode_step_static: more than the static scratch holds */
 
 /* element types of K, V, q, Quest summaries and outputs */
 #define SA_F32 0
@@ -509,6 +511,37 @@ int32_t sparse_attn_step_path(const sa_kv_desc* kv, int32_t sink_len, int32_t wi
 /* A split count that fills the GPU for this shape and suits sparse_attn_decode_step (host only). */
 int32_t sparse_attn_default_splits(const sa_kv_desc* kv, int32_t num_q_rows, int32_t sink_len, int32_t window_len,
                                    int32_t k_max);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one whole
+ * selecting step, sparse_attn_decode_step followed by sparse_attn_combine,
+ * whose workspace and split partials live in a static device array of the
+ * library (16 MiB per GPU, held from the library's load until the process
+ * ends) instead of caller buffers.  The caller passes the inputs and the
+ * outputs only.
+ *   Arguments as in sparse_attn_decode_step (sel_pages, sel_count written
+ *   the same way) and sparse_attn_combine (out [batch][num_q_heads]
+ *   [num_q_rows][head_dim] in out_dtype, lse fp32 or NULL).
+ * The scratch needs the step's workspace (sparse_attn_workspace_bytes) plus
+ * batch * num_q_heads * num_q_rows * num_splits * (head_dim + 2) * 4 bytes of
+ * partials, each rounded up to 256 bytes; a call needing more than 16 MiB
+ * returns SA_ERR_SCRATCH and queues nothing.  Nothing is allocated: the
+ * array's device address is looked up once per device, on the first call
+ * with that device current.  Every call on a GPU uses that GPU's one array,
+ * so calls that overlap on one GPU (on different streams, or from several
+ * threads) race and must be serialised by the caller; calls in a row on one
+ * stream are fine.  The kernels write every scratch byte they read in the
+ * same call (the status word is cleared by the step's first kernel), so the
+ * contents a previous call left do not matter.  Results are identical to
+ * sparse_attn_decode_step + sparse_attn_combine with the same arguments.
+ * Errors: those of the two calls, checked before any HIP call;
+ * SA_ERR_SCRATCH as above.
+ */
+int sparse_attn_decode_step_static(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                                   int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                                   float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                                   void* out, int32_t out_dtype, float* lse, hipStream_t stream);
 
 /*
  * Log-sum-exp merge of split partials (attention-mechanisms article,

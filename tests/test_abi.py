@@ -26,7 +26,8 @@ def test_exports_every_header_function():
         "sparse_attn_decode_grouped", "sparse_attn_grouped_workspace_bytes", "sparse_attn_index_workspace_bytes",
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
         "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
-        "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path"}
+        "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path",
+        "sparse_attn_decode_step_static"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -460,3 +461,35 @@ def test_step_path_reports_the_kernels_decode_step_queues():
     assert B.sparse_attn_step_path(d, 4000, 16, 32, 1, ws) == B.SA_STEP_SEPARATE
     assert B.sparse_attn_step_path(_desc(batch=0), 16, 16, 32, 4, ws) == -B.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_step_path(None, 16, 16, 32, 4, ws) == -B.SA_ERR_INVALID_ARG
+
+
+def test_static_step_checks():
+    """The entry point without caller buffers checks everything, and the
+    size of its static scratch, before any HIP call."""
+    lib = B.library()
+    d = _desc()
+
+    def st(desc=None, **kw):
+        a = dict(q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, scale=0.0, splits=4, sel=DEV, cnt=DEV,
+                 out=DEV, odt=1, lse=None)
+        a.update(kw)
+        return lib.sparse_attn_decode_step_static(ctypes.byref(desc or d), a["q"], a["rows"], a["meta"], a["mode"],
+                                                  a["S"], a["W"], a["budget"], a["scale"], a["splits"], a["sel"],
+                                                  a["cnt"], a["out"], a["odt"], a["lse"], None)
+
+    assert st(q=None) == B.SA_ERR_INVALID_ARG
+    assert st(meta=None) == B.SA_ERR_INVALID_ARG
+    assert st(out=None) == B.SA_ERR_INVALID_ARG
+    assert st(sel=None) == B.SA_ERR_INVALID_ARG
+    assert st(cnt=None) == B.SA_ERR_INVALID_ARG
+    assert st(rows=0) == B.SA_ERR_INVALID_ARG
+    assert st(W=0) == B.SA_ERR_INVALID_ARG
+    assert st(splits=0) == B.SA_ERR_INVALID_ARG
+    assert st(odt=5) == B.SA_ERR_UNSUPPORTED
+    assert st(mode=9) == B.SA_ERR_UNSUPPORTED
+    # 64 sequences x 64 q heads x 64 splits of (128 + 2) floats: 136 MB of partials
+    big = _desc(batch=64, num_q_heads=64, num_kv_heads=8)
+    assert st(desc=big, splits=64) == B.SA_ERR_SCRATCH
+    assert "static scratch" in B.sparse_attn_status_string(B.SA_ERR_SCRATCH)
+    for bad, code in BAD_DESCS:
+        assert st(desc=_desc(**bad)) == code
