@@ -54,7 +54,17 @@ struct SelectArgs {
     float* scores;   // workspace [B][Hkv][Q][max_pages]
     int score_only;  // 1: scores only (the select-and-decode kernel ranks them)
     uint32_t* status;  // the step's status word, cleared by the score kernel (or null)
+    // Selection over more candidates than one workgroup holds: a local top-k
+    // per chunk of kTopkChunk candidates, then a merge of the chunks' winners
+    // (nchunks == 0: one workgroup per problem ranks all its candidates).
+    int nchunks;           // chunks per problem
+    int kc;                // winners per chunk: min(k_max, kTopkChunk)
+    uint32_t* part_keys;   // [B][Hkv][Q][nchunks][kc] order keys of each chunk's winners
+    int32_t* part_idx;     // [B][Hkv][Q][nchunks][kc] their candidate indices, ascending
 };
+
+constexpr int kTopkChunk = 8192;   // candidates a chunk of the two-stage selection ranks
+constexpr int kTopkMerge = 12288;  // winners the merge workgroup ranks (nchunks * kc)
 
 struct DecodeArgs {
     Geometry g;

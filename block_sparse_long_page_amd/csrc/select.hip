@@ -338,6 +338,111 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(SelectArgs a)
     block_topk_fast(n, k, keys, lo, hi, sh, [&](int pos, int i) { sel[pos] = plo + i; });
 }
 
+// Two-stage selection, stage 1: workgroup (chunk c, problem) ranks the
+// candidates [c * kTopkChunk, (c + 1) * kTopkChunk) of its problem and
+// writes its min(k, chunk size) best (ties to the lower index) as order keys
+// and candidate indices, ascending.  Every candidate among the problem's k
+// best is among its chunk's best, so the merge of the winners is exact.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_chunk(SelectArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // [kTopkChunk]
+    __shared__ TopkScratch sh;
+    const Geometry& g = a.g;
+    const int c = blockIdx.x;
+    int pid = blockIdx.y;
+    const int row = pid % a.Q;
+    pid /= a.Q;
+    const int kvh = pid % g.Hkv;
+    const int b = pid / g.Hkv;
+    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
+
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int se = imin(a.S, L), ws = imax(se, L - a.W);
+    const int plo = se / g.P;
+    const int n = ws > se ? (ws - 1) / g.P - plo + 1 : 0;
+    const int k = imin(a.k_max, n);
+    const int c0 = c * kTopkChunk;
+    const int nc = imin(n - c0, kTopkChunk);
+    if (k == 0 || k == n || nc <= 0) return;  // the merge needs no winners from this chunk
+    const int kc = imin(k, nc);
+    uint32_t* pk = a.part_keys + (prob * a.nchunks + c) * a.kc;
+    int32_t* pi = a.part_idx + (prob * a.nchunks + c) * a.kc;
+    uint32_t lo, hi;
+    topk_load_keys(a.scores + prob * g.max_pages + plo + c0, nc, keys, lo, hi);
+    if (kc == nc) {  // the whole chunk
+        __syncthreads();
+        for (int i = threadIdx.x; i < nc; i += kTopkThreads) {
+            pk[i] = keys[i];
+            pi[i] = c0 + i;
+        }
+        return;
+    }
+    block_topk_fast(nc, kc, keys, lo, hi, sh, [&](int pos, int i) {
+        pk[pos] = keys[i];
+        pi[pos] = c0 + i;
+    });
+}
+
+// Stage 2: one workgroup per problem ranks the chunks' winners, laid out
+// chunk after chunk (so ascending candidate order and ties to the lower
+// page carry over), and writes the k best pages ascending.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_merge(SelectArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t keys[];  // [kTopkMerge]
+    __shared__ TopkScratch sh;
+    __shared__ int off[kTopkMerge / 64 + 2];  // first merged position of each chunk's winners
+    const Geometry& g = a.g;
+    int pid = blockIdx.x;
+    const int row = pid % a.Q;
+    pid /= a.Q;
+    const int kvh = pid % g.Hkv;
+    const int b = pid / g.Hkv;
+    const long prob = ((long)b * g.Hkv + kvh) * a.Q + row;
+    int32_t* sel = a.sel + prob * a.k_max;
+
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int se = imin(a.S, L), ws = imax(se, L - a.W);
+    const int plo = se / g.P;
+    const int n = ws > se ? (ws - 1) / g.P - plo + 1 : 0;
+    const int k = imin(a.k_max, n);
+    const int tid = threadIdx.x;
+    if (tid == 0) a.count[prob] = k;
+    for (int i = k + tid; i < a.k_max; i += kTopkThreads) sel[i] = -1;
+    if (k == 0) return;
+    if (k == n) {
+        for (int i = tid; i < n; i += kTopkThreads) sel[i] = plo + i;
+        return;
+    }
+    const int nch = (n + kTopkChunk - 1) / kTopkChunk;  // <= a.nchunks
+    if (tid == 0) {
+        int m = 0;
+        for (int c = 0; c < nch; ++c) {
+            off[c] = m;
+            m += imin(k, imin(n - c * kTopkChunk, kTopkChunk));
+        }
+        off[nch] = m;
+    }
+    __syncthreads();
+    const int m = off[nch];  // <= kTopkMerge (host-checked)
+    const uint32_t* pk = a.part_keys + prob * a.nchunks * a.kc;
+    const int32_t* pi = a.part_idx + prob * a.nchunks * a.kc;
+    uint32_t lo = 0xffffffffu, hi = 0;
+    for (int c = 0; c < nch; ++c) {
+        const int cnt = off[c + 1] - off[c];
+        for (int i = tid; i < cnt; i += kTopkThreads) {
+            const uint32_t key = pk[c * a.kc + i];
+            keys[off[c] + i] = key;
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+    }
+    block_topk_fast(m, k, keys, lo, hi, sh, [&](int pos, int i) {
+        int c = 0;
+        while (c + 1 < nch && off[c + 1] <= i) ++c;
+        sel[pos] = plo + pi[c * a.kc + (i - off[c])];
+    });
+}
+
 template <int HD, int G, bool BF>
 hipError_t launch_score_f32(const SelectArgs& a, hipStream_t s)
 {
@@ -413,6 +518,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     if (a.score_only) return hipSuccess;
+    if (a.nchunks > 0 && a.k_max > 0) {  // more candidates than one workgroup ranks
+        hipLaunchKernelGGL(k_topk_chunk, dim3((unsigned)a.nchunks, (unsigned)problems), dim3(kTopkThreads),
+                           sizeof(uint32_t) * kTopkChunk, s, a);
+        hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)problems), dim3(kTopkThreads), sizeof(uint32_t) * kTopkMerge,
+                           s, a);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(uint32_t) * (size_t)(a.k_max > 0 ? g.max_pages : 1);  // <= 48 KiB (host-checked)
     hipLaunchKernelGGL(k_topk, dim3((unsigned)problems), dim3(kTopkThreads), lds, s, a);
     return hipGetLastError();

@@ -17,7 +17,8 @@
 namespace {
 
 constexpr int kMaxSplits = 1024;
-constexpr int kMaxSelectPages = 12288;  // the top-k workgroup holds one key per page in LDS
+constexpr int kMaxSelectPages = 12288;  // one top-k workgroup holds one key per page in LDS
+constexpr int kMaxChunks = 64;          // chunks of the two-stage selection (524288 pages)
 constexpr long kMaxGridY = 65535;
 constexpr int kMaxTokenSplits = 64;  // token chunks per page of the grouped decode
 
@@ -158,9 +159,41 @@ GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
     return w;
 }
 
-size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows)
+// The selection's workspace: the fp32 scores [B][Hkv][Q][max_pages]; past
+// kMaxSelectPages pages per sequence also every chunk's winners (order keys,
+// then candidate indices, [B][Hkv][Q][nchunks][kTopkChunk] each), 256-byte
+// aligned.
+struct SelectWs {
+    int nchunks;  // 0: one workgroup ranks all of a problem's candidates
+    size_t part_keys, part_idx, total;
+};
+SelectWs select_ws(const sa_kv_desc* kv, int32_t rows)
 {
-    return sizeof(float) * (size_t)kv->batch * kv->num_kv_heads * rows * kv->max_pages_per_seq;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t problems = (size_t)kv->batch * kv->num_kv_heads * rows;
+    SelectWs w;
+    w.total = sizeof(float) * problems * kv->max_pages_per_seq;
+    w.nchunks = 0;
+    w.part_keys = w.part_idx = 0;
+    if (kv->max_pages_per_seq > kMaxSelectPages) {
+        w.nchunks = (kv->max_pages_per_seq + sa::kTopkChunk - 1) / sa::kTopkChunk;
+        const size_t part = sizeof(uint32_t) * problems * w.nchunks * sa::kTopkChunk;
+        w.part_keys = up(w.total);
+        w.part_idx = w.part_keys + up(part);
+        w.total = w.part_idx + up(part);
+    }
+    return w;
+}
+size_t select_ws_bytes(const sa_kv_desc* kv, int32_t rows) { return select_ws(kv, rows).total; }
+
+// Whether the selection can rank k_max of max_pages candidates: one
+// workgroup holds up to kMaxSelectPages; past that, at most kMaxChunks chunks
+// whose winners (min(k_max, kTopkChunk) each) fit the merge workgroup.
+bool select_fits(const sa_kv_desc* kv, int32_t k_max)
+{
+    if (k_max <= 0 || kv->max_pages_per_seq <= kMaxSelectPages) return true;
+    const long nchunks = (kv->max_pages_per_seq + sa::kTopkChunk - 1) / sa::kTopkChunk;
+    return nchunks <= kMaxChunks && nchunks * std::min<long>(k_max, sa::kTopkChunk) <= sa::kTopkMerge;
 }
 
 // the selecting step's workspace: the scores, then (256-byte aligned) its
@@ -189,7 +222,7 @@ int check_step(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const vo
     if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
     if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
         return SA_ERR_UNSUPPORTED;
-    if (k_max > 0 && kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
+    if (!select_fits(kv, k_max)) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
 
@@ -247,11 +280,15 @@ int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
     if (k_max > 0 && !sel_pages) return SA_ERR_INVALID_ARG;
     if ((long)kv->batch * kv->num_kv_heads * num_q_rows > kMaxGridY) return SA_ERR_UNSUPPORTED;
     if (k_max > 0) {
-        if (kv->max_pages_per_seq > kMaxSelectPages) return SA_ERR_UNSUPPORTED;
+        if (!select_fits(kv, k_max)) return SA_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < select_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
     }
-    sa::SelectArgs a{g, q, num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages, sel_count,
-                     (float*)workspace, 0, nullptr};
+    const SelectWs w = select_ws(kv, num_q_rows);
+    char* base = (char*)workspace;
+    sa::SelectArgs a{g,         q,          num_q_rows, meta,      score_mode,        sink_len, window_len,
+                     k_max,     sel_pages,  sel_count,  (float*)workspace, 0,          nullptr,  w.nchunks,
+                     sa::kTopkChunk, w.nchunks ? (uint32_t*)(base + w.part_keys) : nullptr,
+                     w.nchunks ? (int32_t*)(base + w.part_idx) : nullptr};
     return finish(sa::launch_select(a, stream), stream);
 }
 
@@ -333,8 +370,8 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
                                   softmax_scale, num_splits, num_splits, part_o, part_ml, stream);
     }
     uint32_t* status = (uint32_t*)((char*)workspace + status_offset(kv, num_q_rows));
-    sa::SelectArgs sarg{g,        q,          num_q_rows, meta,      score_mode, sink_len, window_len,
-                        k_max,    sel_pages,  sel_count,  (float*)workspace, 1, status};
+    sa::SelectArgs sarg{g,     q,         num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages,
+                        sel_count, (float*)workspace, 1, status, 0, 0, nullptr, nullptr};
     const int r1 = finish(sa::launch_select(sarg, stream), stream);
     if (r1 != SA_OK) return r1;
     sa::SelectDecodeArgs d{g,          q,          num_q_rows, (const float*)workspace,

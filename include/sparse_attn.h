@@ -198,9 +198,16 @@ int sparse_attn_build_page_meta(const sa_kv_desc* kv, int32_t score_mode, int32_
  * summaries of the dot-product modes enter the matrix cores as three exact
  * bf16 parts).  Pages are ranked by (group score desc, page index asc) in
  * fp32 and the first k kept.  When k_max >= #candidates every candidate is kept (the
- * dense fallback at short context).
+ * dense fallback at short context).  Up to 12288 pages per sequence one
+ * workgroup ranks a problem's candidates; past that, each chunk of 8192
+ * candidates is ranked by its own workgroup and one workgroup per problem
+ * ranks the chunks' winners (the same pages: every page among the k best is
+ * among its chunk's best).  This needs at most 64 chunks (524288 pages per
+ * sequence) and chunks * min(k_max, 8192) <= 12288, e.g. 16384 pages (1M
+ * tokens of 64-token pages) with k_max <= 6144.
  * Errors: null pointers (sel_pages may be null only when k_max == 0),
- * num_q_rows < 1, S < 0, W < 1, token_budget < 0, workspace too small.
+ * num_q_rows < 1, S < 0, W < 1, token_budget < 0, workspace too small;
+ * SA_ERR_UNSUPPORTED past the two-stage limits above.
  */
 int sparse_attn_select(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
                        int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,

@@ -493,3 +493,28 @@ def test_static_step_checks():
     assert "static scratch" in B.sparse_attn_status_string(B.SA_ERR_SCRATCH)
     for bad, code in BAD_DESCS:
         assert st(desc=_desc(**bad)) == code
+
+
+def test_selection_past_one_workgroup_sizes_and_limits():
+    """Past 12288 candidate pages per sequence the selection runs per chunk of
+    8192 and merges the winners: the workspace holds every chunk's winners,
+    and shapes whose winners would not fit the merge are refused."""
+    lib = B.library()
+    d = _desc(batch=1, num_q_heads=8, num_kv_heads=1, page_size=64, max_pages_per_seq=16384,
+              num_phys_pages=16384, max_seq_len=16384 * 64)
+    ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
+    scores = 4 * 16384
+    part = 4 * 2 * 8192  # two chunks of 8192 winners, keys and indices
+    assert ws >= scores + 2 * part
+    sel = lambda budget, wsb=ws: lib.sparse_attn_select(ctypes.byref(d), DEV, 1, DEV, 0, 256, 4096, budget, DEV,
+                                                       DEV, DEV, wsb, None)
+    assert sel(64 * 6145) == B.SA_ERR_UNSUPPORTED  # 2 chunks x 6145 winners > 12288
+    assert sel(64 * 1024, wsb=scores + part) == B.SA_ERR_INVALID_ARG  # no room for the winners
+    big = _desc(batch=1, num_q_heads=8, num_kv_heads=1, page_size=1, max_pages_per_seq=65 * 8192,
+                num_phys_pages=65 * 8192, max_seq_len=65 * 8192)
+    wsb = lib.sparse_attn_workspace_bytes(ctypes.byref(big), 1)
+    assert lib.sparse_attn_select(ctypes.byref(big), DEV, 1, DEV, 0, 0, 16, 8, DEV, DEV, DEV, wsb,
+                                  None) == B.SA_ERR_UNSUPPORTED  # more than 64 chunks
+    # the step refuses the same shapes before any launch
+    assert lib.sparse_attn_decode_step(ctypes.byref(d), DEV, 1, DEV, 0, 256, 4096, 64 * 6145, 0.0, 8, DEV, DEV, DEV,
+                                       ws, DEV, DEV, None) == B.SA_ERR_UNSUPPORTED

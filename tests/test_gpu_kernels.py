@@ -456,3 +456,37 @@ def test_select_decode_wait_bound_is_reported(monkeypatch):
     ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
                      sel=sel, cnt=cnt)
     check_output(dec.out_f32(), ref.out, pr.cache.dtype, "after the bound")
+
+
+@pytest.mark.parametrize("pattern", ["random", "all-equal"])
+def test_selection_over_chunks_of_candidates(pattern):
+    """More candidate pages than one workgroup ranks (20000 and 12500 pages of
+    4 tokens): each chunk of 8192 candidates keeps its best and a merge ranks
+    them.  The pages match the oracle within the band, and with every key
+    equal (exact ties across the chunk boundaries) they are exactly the
+    lowest candidates, as in the oracle."""
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=64, P=4, seq_lens=[80000, 50000], sink=16, window=64,
+                              budget=4 * 900, mode="quest", dtype="bf16", seed=17, shuffle=True, clusters=8)
+    c = pr.cache
+    if pattern == "all-equal":
+        vec = synth.store(np.random.default_rng(5).standard_normal((c.Hkv, c.hd)).astype(np.float32), c.dtype)
+        c.k[:] = vec[None, :, None, :]
+    assert c.max_pages == 20000
+    dc = DeviceCache.from_host(c)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+    assert B.sparse_attn_step_path(dec.desc, pr.sink, pr.window, pr.budget, dec.splits, dec.ws) == B.SA_STEP_SEPARATE
+    q = to_device(pr.q)
+    dec.build_meta()
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    r = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, want_scores=True)
+    if pattern == "all-equal":
+        np.testing.assert_array_equal(cnt, r.cnt)
+        np.testing.assert_array_equal(sel, r.sel)
+    else:
+        check_selection(sel, cnt, r.scores, pr.k_pages)
+    ref = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget, sel=sel,
+                     cnt=cnt)
+    check_output(dec.out_f32(), ref.out, c.dtype, pattern)
+    check_lse(dec.lse_f32(), ref.lse, pattern)

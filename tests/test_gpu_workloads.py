@@ -1,7 +1,8 @@
 """End-to-end parity at the workloads' full sizes, in the launch configuration
 the benchmark times (the library's default split count): the tiny fp32
 case, the Qwen3-8B-shaped and Llama-3-70B-shaped layers (the latter also with
-compressed-key scores), the 3-layer hybrid
+compressed-key scores, and one KV head's share of a 1M-token context: 16384
+pages, ranked in chunks and merged), the 3-layer hybrid
 256k schedule (every refresh step and the last step) and the semantic-block
 512K chunk, paged and over a block index built from interleaved keys.  The
 oracle computes every output at these sizes (the index: its layout exactly,
@@ -34,6 +35,11 @@ def _say(*a):
 
 @pytest.mark.parametrize("wl", [configs.TINY, configs.QWEN3_8B, configs.LLAMA3_70B,
                                 configs.LLAMA3_70B.scaled(name="llama3-70b-layer-128k-compressed", mode="compressed"),
+                                # one GPU's share (one KV head, its 8 query heads) of a 1M-token context:
+                                # 16384 pages, more than one workgroup ranks, so the selection merges chunks
+                                configs.LLAMA3_70B.scaled(name="llama3-70b-layer-1m-one-kv-head", batch=1,
+                                                          num_q_heads=8, num_kv_heads=1, context=1 << 20,
+                                                          budget=(1 << 20) // 16),
                                 configs.SEMANTIC_512K],
                          ids=lambda w: w.name)
 def test_single_step_workload(wl):
