@@ -88,7 +88,7 @@ _SIGS = {
     "sparse_attn_blocks_visible": (ctypes.c_int, [_DESC, _IDX, _I, _P, _P]),
     "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                  _P, ctypes.c_size_t, _P]),
-    "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC]),
+    "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC, _I, _I]),
     "sparse_attn_keydiff_select": (ctypes.c_int, [_DESC, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_keydiff_compact": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -235,8 +235,8 @@ def sparse_attn_select_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_ro
            "sparse_attn_select_blocks")
 
 
-def sparse_attn_keydiff_workspace_bytes(kv: sa_kv_desc) -> int:
-    return int(_lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(kv)))
+def sparse_attn_keydiff_workspace_bytes(kv: sa_kv_desc, sink_len: int, budget: int) -> int:
+    return int(_lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(kv), sink_len, budget))
 
 
 def sparse_attn_keydiff_select(kv: sa_kv_desc, sink_len: int, budget: int, kept, kept_count, workspace,

@@ -204,7 +204,14 @@ struct KeydiffArgs {
                        // key, position t at index L-1-t (the candidates come first)
     int32_t* kept;     // [B][Hkv][budget] kept positions ascending, -1 after the count
     int32_t* count;    // [B][Hkv]
+    // More candidates than one workgroup holds: each chunk of kTopkChunk
+    // candidates (position order) picks its tokens to evict, and a merge
+    // picks the evicted set among them (ecnk == 0: one workgroup ranks all)
+    int ecnk;             // chunks per (sequence, KV head)
+    uint32_t* part_keys;  // [B][Hkv][ecnk][kTopkChunk] inverted order keys of each chunk's picks
+    int32_t* part_idx;    // [B][Hkv][ecnk][kTopkChunk] their candidate indices, ascending
 };
+constexpr int kKdMaxChunks = 16;  // chunks of the two-stage eviction (131072 candidates)
 
 struct CompactArgs {
     Geometry src, dst;

@@ -246,6 +246,150 @@ __global__ __launch_bounds__(kTopkThreads) void k_kd_topk(KeydiffArgs a)
     block_topk_fast(m, k, keys, lo, hi, sh, [&](int pos, int j) { kept[s0 + (k - 1 - pos)] = L - 1 - j; });
 }
 
+// Past kKdMaxCand candidates the evicted tokens are chosen instead of the
+// kept ones (there are fewer of them): candidate i is position sink + i, its
+// key the inverted distance key (the nearest to the mean first), and ties go
+// to the lower index, i.e. the earlier position is evicted first, as in the
+// one-workgroup path.  Stage 1: workgroup (chunk c, sequence and KV head)
+// writes the min(e, chunk size) candidates of its chunk to evict first, e =
+// the number evicted, ascending.  Every token among the e evicted is among
+// its chunk's picks.
+__global__ __launch_bounds__(kTopkThreads) void k_kd_evict_chunk(KeydiffArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkChunk];
+    __shared__ TopkScratch sh;
+    const Geometry& g = a.g;
+    const int c = blockIdx.x, bh = blockIdx.y, b = bh / g.Hkv;
+    const int L = kd_len(g, a.T, b);
+    if (L <= a.budget) return;
+    const int s0 = imin(a.sink, L);
+    const int m = L - s0, k = a.budget - s0;  // candidates, kept among them
+    const int e = m - k;                      // evicted (>= 1)
+    const int c0 = c * kTopkChunk;
+    const int nc = imin(m - c0, kTopkChunk);
+    if (k <= 0 || nc <= 0) return;
+    const int ke = imin(e, nc);
+    const uint32_t* src = a.okeys + (long)bh * a.Tk;  // candidate i at index m - 1 - i
+    uint32_t lo = 0xffffffffu, hi = 0;
+    for (int i = threadIdx.x; i < nc; i += kTopkThreads) {
+        const uint32_t key = ~src[m - 1 - (c0 + i)];
+        keys[i] = key;
+        lo = min(lo, key);
+        hi = max(hi, key);
+    }
+    uint32_t* pk = a.part_keys + ((long)bh * a.ecnk + c) * kTopkChunk;
+    int32_t* pi = a.part_idx + ((long)bh * a.ecnk + c) * kTopkChunk;
+    if (ke == nc) {  // the whole chunk
+        for (int i = threadIdx.x; i < nc; i += kTopkThreads) {
+            pk[i] = keys[i];
+            pi[i] = c0 + i;
+        }
+        return;
+    }
+    __syncthreads();
+    block_topk_fast(nc, ke, keys, lo, hi, sh, [&](int pos, int i) {
+        pk[pos] = keys[i];
+        pi[pos] = c0 + i;
+    });
+}
+
+// Stage 2: one workgroup per (sequence, KV head) picks the e evicted tokens
+// among the chunks' picks (laid out chunk after chunk, so ascending
+// candidates and ties to the earlier position carry over), marks them in a
+// bitmap and writes the sink and every unmarked candidate, ascending.
+__global__ __launch_bounds__(kTopkThreads) void k_kd_evict_merge(KeydiffArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkMerge];
+    __shared__ TopkScratch sh;
+    __shared__ uint32_t evicted[kKdMaxChunks * kTopkChunk / 32];
+    __shared__ int off[kKdMaxChunks + 1];
+    __shared__ int wsum[kTopkThreads / 64];
+    const Geometry& g = a.g;
+    const int bh = blockIdx.x, b = bh / g.Hkv;
+    const int L = kd_len(g, a.T, b);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t* kept = a.kept + (long)bh * a.budget;
+    const int cnt = imin(L, a.budget);
+    if (tid == 0) a.count[bh] = cnt;
+    for (int i = cnt + tid; i < a.budget; i += kTopkThreads) kept[i] = -1;
+    if (L <= a.budget) {
+        for (int i = tid; i < L; i += kTopkThreads) kept[i] = i;
+        return;
+    }
+    const int s0 = imin(a.sink, L);
+    for (int i = tid; i < s0; i += kTopkThreads) kept[i] = i;
+    const int m = L - s0, k = a.budget - s0, e = m - k;
+    if (k <= 0) return;  // the sink alone
+    const int nch = (m + kTopkChunk - 1) / kTopkChunk;  // <= ecnk
+    const int nw = (m + 31) / 32;
+    for (int w = tid; w < nw; w += kTopkThreads) evicted[w] = 0u;
+    if (tid == 0) {
+        int acc = 0;
+        for (int c = 0; c < nch; ++c) {
+            off[c] = acc;
+            acc += imin(e, imin(m - c * kTopkChunk, kTopkChunk));
+        }
+        off[nch] = acc;
+    }
+    __syncthreads();
+    const int mw = off[nch];  // <= kTopkMerge (host-checked)
+    const uint32_t* pk = a.part_keys + (long)bh * a.ecnk * kTopkChunk;
+    const int32_t* pi = a.part_idx + (long)bh * a.ecnk * kTopkChunk;
+    auto cand_of = [&](int i) {  // candidate index of merged pick i
+        int c = 0;
+        while (c + 1 < nch && off[c + 1] <= i) ++c;
+        return pi[c * kTopkChunk + (i - off[c])];
+    };
+    if (e >= mw) {  // every pick is evicted
+        for (int i = tid; i < mw; i += kTopkThreads) {
+            const int ci = cand_of(i);
+            atomicOr(&evicted[ci >> 5], 1u << (ci & 31));
+        }
+    } else {
+        uint32_t lo = 0xffffffffu, hi = 0;
+        for (int c = 0; c < nch; ++c) {
+            const int n = off[c + 1] - off[c];
+            for (int i = tid; i < n; i += kTopkThreads) {
+                const uint32_t key = pk[c * kTopkChunk + i];
+                keys[off[c] + i] = key;
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+        }
+        block_topk_fast(mw, e, keys, lo, hi, sh, [&](int, int i) {
+            const int ci = cand_of(i);
+            atomicOr(&evicted[ci >> 5], 1u << (ci & 31));
+        });
+    }
+    __syncthreads();
+    // the kept candidates in order: a block scan of the per-word counts, 512 words a round
+    int base = 0;
+    for (int w0 = 0; w0 < nw; w0 += kTopkThreads) {
+        const int w = w0 + tid;
+        uint32_t keep = 0u;
+        if (w < nw) {
+            keep = ~evicted[w];
+            if (32 * w + 32 > m) keep &= (m - 32 * w >= 32) ? 0xffffffffu : ((1u << (m - 32 * w)) - 1u);
+        }
+        const int n = __builtin_popcount(keep);
+        const int inc = wave_inclusive_scan(n);
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        int before = base;
+        for (int v = 0; v < wave; ++v) before += wsum[v];
+        int total = base;
+        for (int v = 0; v < kTopkThreads / 64; ++v) total += wsum[v];
+        int r = before + inc - n;
+        while (keep) {
+            const int bit = __builtin_ctz(keep);
+            kept[s0 + r++] = s0 + 32 * w + bit;
+            keep &= keep - 1u;
+        }
+        base = total;
+        __syncthreads();
+    }
+}
+
 template <int HD, bool BF>
 __global__ __launch_bounds__(kKdCopyThreads) void k_kd_compact(CompactArgs a)
 {
@@ -297,7 +441,13 @@ hipError_t launch_kd(const KeydiffArgs& a, hipStream_t s)
     const dim3 grid((unsigned)a.nchunks, (unsigned)(a.g.B * a.g.Hkv));
     hipLaunchKernelGGL((k_kd_sum<HD, BF>), grid, dim3(64 * kKdWaves), 0, s, a);
     hipLaunchKernelGGL((k_kd_dist<HD, BF>), grid, dim3(64 * kKdWaves), 0, s, a);
-    hipLaunchKernelGGL(k_kd_topk, dim3((unsigned)(a.g.B * a.g.Hkv)), dim3(kTopkThreads), 0, s, a);
+    if (a.ecnk > 0) {  // more candidates than one workgroup holds
+        hipLaunchKernelGGL(k_kd_evict_chunk, dim3((unsigned)a.ecnk, (unsigned)(a.g.B * a.g.Hkv)), dim3(kTopkThreads),
+                           0, s, a);
+        hipLaunchKernelGGL(k_kd_evict_merge, dim3((unsigned)(a.g.B * a.g.Hkv)), dim3(kTopkThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k_kd_topk, dim3((unsigned)(a.g.B * a.g.Hkv)), dim3(kTopkThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

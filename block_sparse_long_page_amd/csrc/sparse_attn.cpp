@@ -124,11 +124,13 @@ bool fused_step_ok(const sa_kv_desc* kv, int32_t sink_len, int32_t window_len, i
 // workspace of the KeyDiff selection: the chunk key sums, then the order
 // keys of the distances (rows padded to a multiple of 4), each 256-byte
 // aligned
+// (past kKdMaxCand candidates, also each chunk's picks of tokens to evict:
+// inverted keys, then candidate indices)
 struct KeydiffWs {
-    int nchunks, Tk;
-    size_t partial, okeys, total;
+    int nchunks, Tk, ecnk;
+    size_t partial, okeys, part_keys, part_idx, total;
 };
-KeydiffWs keydiff_ws(const sa_kv_desc* kv)
+KeydiffWs keydiff_ws(const sa_kv_desc* kv, int32_t sink_len, int32_t budget)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
@@ -138,7 +140,29 @@ KeydiffWs keydiff_ws(const sa_kv_desc* kv)
     w.partial = 0;
     w.okeys = up(bh * (size_t)w.nchunks * kv->head_dim * sizeof(float));
     w.total = up(w.okeys + bh * (size_t)w.Tk * sizeof(uint32_t));
+    w.ecnk = 0;
+    w.part_keys = w.part_idx = 0;
+    const long cand = (long)kv->max_seq_len - (sink_len > 0 ? sink_len : 0);
+    if (kv->max_seq_len > budget && cand > sa::kKdMaxCand) {
+        w.ecnk = (int)((cand + sa::kTopkChunk - 1) / sa::kTopkChunk);
+        const size_t part = up(bh * (size_t)w.ecnk * sa::kTopkChunk * sizeof(uint32_t));
+        w.part_keys = w.total;
+        w.part_idx = w.part_keys + part;
+        w.total = w.part_idx + part;
+    }
     return w;
+}
+
+// Whether the eviction can rank the longest sequence's candidates: one
+// workgroup holds kKdMaxCand; past that, at most kKdMaxChunks chunks whose
+// picks (min(evicted, kTopkChunk) each) fit the merge workgroup.
+bool keydiff_fits(const sa_kv_desc* kv, int32_t sink_len, int32_t budget)
+{
+    const long cand = (long)kv->max_seq_len - sink_len;
+    if (kv->max_seq_len <= budget || cand <= sa::kKdMaxCand) return true;
+    const long chunks = (cand + sa::kTopkChunk - 1) / sa::kTopkChunk;
+    const long evicted = (long)kv->max_seq_len - budget;
+    return chunks <= sa::kKdMaxChunks && chunks * std::min<long>(evicted, sa::kTopkChunk) <= sa::kTopkMerge;
 }
 
 // workspace of the grouped decode: byte offsets of its three arrays, each
@@ -611,11 +635,11 @@ int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_
                         kv->max_pages_per_seq, nullptr, nullptr, nullptr, 0, nullptr, stream);
 }
 
-size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv)
+size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv, int32_t sink_len, int32_t budget)
 {
     sa::Geometry g;
-    if (check_kv(kv, &g) != SA_OK) return 0;
-    return keydiff_ws(kv).total;
+    if (check_kv(kv, &g) != SA_OK || sink_len < 0 || budget < 1) return 0;
+    return keydiff_ws(kv, sink_len, budget).total;
 }
 
 int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
@@ -626,14 +650,24 @@ int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t b
     if (rc != SA_OK) return rc;
     if (!kept || !kept_count || sink_len < 0 || budget < 1 || budget < sink_len) return SA_ERR_INVALID_ARG;
     if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    // the top-k workgroup holds every candidate's key in LDS
-    if (kv->max_seq_len > budget && (long)kv->max_seq_len - sink_len > sa::kKdMaxCand) return SA_ERR_UNSUPPORTED;
-    const KeydiffWs w = keydiff_ws(kv);
+    if (!keydiff_fits(kv, sink_len, budget)) return SA_ERR_UNSUPPORTED;
+    const KeydiffWs w = keydiff_ws(kv, sink_len, budget);
     // the top-k reads the order keys as 16-byte vectors
     if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 15) != 0) return SA_ERR_INVALID_ARG;
     char* base = (char*)workspace;
-    sa::KeydiffArgs a{g,         kv->max_seq_len, w.Tk, sink_len, budget, w.nchunks, (float*)(base + w.partial),
-                      (uint32_t*)(base + w.okeys), kept, kept_count};
+    sa::KeydiffArgs a{g,
+                      kv->max_seq_len,
+                      w.Tk,
+                      sink_len,
+                      budget,
+                      w.nchunks,
+                      (float*)(base + w.partial),
+                      (uint32_t*)(base + w.okeys),
+                      kept,
+                      kept_count,
+                      w.ecnk,
+                      w.ecnk ? (uint32_t*)(base + w.part_keys) : nullptr,
+                      w.ecnk ? (int32_t*)(base + w.part_idx) : nullptr};
     return finish(sa::launch_keydiff_select(a, stream), stream);
 }
 

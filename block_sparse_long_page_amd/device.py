@@ -399,7 +399,7 @@ class KeyDiffEviction:
         self.kept = torch.full((src.B, src.Hkv, budget), -1, dtype=torch.int32, device=dev)
         self.count = torch.zeros((src.B, src.Hkv), dtype=torch.int32, device=dev)
         self.src_desc, self.dst_desc = src.desc(), dst.desc()
-        self.ws_bytes = B.sparse_attn_keydiff_workspace_bytes(self.src_desc)
+        self.ws_bytes = B.sparse_attn_keydiff_workspace_bytes(self.src_desc, sink, budget)
         self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
 
     def select(self, stream=None):

@@ -460,8 +460,9 @@ int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index,
                               float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
                               float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes of sparse_attn_keydiff_select (host only; 0 for a bad descriptor). */
-size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv);
+/* Workspace bytes of sparse_attn_keydiff_select for this cache, sink and
+ * budget (host only; 0 for a bad descriptor, sink_len < 0 or budget < 1). */
+size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv, int32_t sink_len, int32_t budget);
 
 /*
  * KeyDiff eviction, the choice (course module 14, section 14.4 and exercise
@@ -478,14 +479,21 @@ size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv);
  *   kept        int32 [batch][num_kv_heads][budget]: kept positions ascending,
  *               -1 after the count.
  *   kept_count  int32 [batch][num_kv_heads]: min(L_b, budget).
- *   workspace   device scratch of sparse_attn_keydiff_workspace_bytes(kv),
- *               16-byte aligned.
+ *   workspace   device scratch of sparse_attn_keydiff_workspace_bytes(kv,
+ *               sink_len, budget), 16-byte aligned.
  * Called after each block of new tokens, this keeps a cache within budget +
  * block tokens.  A token whose page is unmapped counts as a zero key.
+ * Up to 12288 candidates (max_seq_len - sink_len) one workgroup per
+ * (sequence, KV head) ranks them; past that the tokens to evict are chosen
+ * instead (the same set): each chunk of 8192 candidates picks its
+ * min(evicted, 8192) nearest to the mean (earlier position first among
+ * equal distances) and one workgroup per (sequence, KV head) picks the
+ * evicted among those and writes the others.  This needs at most 16 chunks
+ * (131072 candidates) and chunks * min(max_seq_len - budget, 8192) <= 12288,
+ * e.g. a 2048-token block evicted from up to 49152 held tokens.
  * Errors: null pointers, sink_len < 0, budget < 1 or < sink_len, workspace
- * too small or misaligned; SA_ERR_UNSUPPORTED when max_seq_len > budget and
- * max_seq_len - sink_len > 12288 (the candidates of one (sequence, KV head)
- * are ranked in one workgroup's LDS) or batch * num_kv_heads > 65535.
+ * too small or misaligned; SA_ERR_UNSUPPORTED past the limits above or when
+ * batch * num_kv_heads > 65535.
  */
 int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
                                int32_t* kept_count, void* workspace, size_t workspace_bytes, hipStream_t stream);

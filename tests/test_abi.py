@@ -359,11 +359,13 @@ def test_block_index_checks():
 def test_keydiff_checks():
     lib = B.library()
     d = _desc()
-    ws = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d))
+    ws = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d), 4, 64)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # chunk key sums (one chunk), then the distances
     assert ws == up(2 * 2 * 1 * 128 * 4) + up(2 * 2 * 128 * 4)
-    assert lib.sparse_attn_keydiff_workspace_bytes(None) == 0
+    assert lib.sparse_attn_keydiff_workspace_bytes(None, 4, 64) == 0
+    assert lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d), -1, 64) == 0
+    assert lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(d), 4, 0) == 0
 
     def sel(**kw):
         a = dict(desc=d, sink=4, budget=64, kept=DEV, cnt=DEV, ws=DEV, wsb=ws)
@@ -379,9 +381,19 @@ def test_keydiff_checks():
     assert sel(sink=-1) == B.SA_ERR_INVALID_ARG
     assert sel(budget=0) == B.SA_ERR_INVALID_ARG
     assert sel(budget=3) == B.SA_ERR_INVALID_ARG  # below the sink
+    # past 12288 candidates: chunks of 8192 and a merge of their picks
     big = _desc(max_seq_len=16384, max_pages_per_seq=1024, num_phys_pages=2048)
-    wsb = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(big))
-    assert sel(desc=big, wsb=wsb, budget=2048, sink=4) == B.SA_ERR_UNSUPPORTED  # 16380 candidates
+    wsb = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(big), 4, 14336)
+    base = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(big), 4, 16384)  # nothing evicted: one workgroup
+    assert wsb == base + 2 * up(2 * 2 * 2 * 8192 * 4)  # two chunks' picks, keys and indices
+    assert sel(desc=big, wsb=wsb - 1, budget=14336, sink=4) == B.SA_ERR_INVALID_ARG
+    # 2 chunks x 8192 picks (16380 candidates, 14332 evicted) do not fit the merge
+    wsb2 = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(big), 4, 2048)
+    assert sel(desc=big, wsb=wsb2, budget=2048, sink=4) == B.SA_ERR_UNSUPPORTED
+    huge = _desc(batch=1, num_kv_heads=1, num_q_heads=1, max_seq_len=17 * 8192 + 8, max_pages_per_seq=17 * 512 + 1,
+                 num_phys_pages=17 * 512 + 1)
+    wsh = lib.sparse_attn_keydiff_workspace_bytes(ctypes.byref(huge), 4, 17 * 8192 + 4)
+    assert sel(desc=huge, wsb=wsh, budget=17 * 8192 + 4, sink=4) == B.SA_ERR_UNSUPPORTED  # 17 chunks
     for bad, code in BAD_DESCS:
         assert sel(desc=_desc(**bad)) == code
 

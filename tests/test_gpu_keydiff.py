@@ -76,6 +76,11 @@ CASES = {
                                   dtype="f32"),
     "bf16-hd128-near-limit": dict(B=1, Hq=8, Hkv=1, hd=128, P=64, seq_lens=[12000], budget=8192, sink=256,
                                   dtype="bf16"),
+    # past one workgroup's 12288 candidates: chunks of 8192 pick the tokens to evict, a merge chooses them
+    "bf16-hd128-past-limit": dict(B=2, Hq=8, Hkv=1, hd=128, P=64, seq_lens=[20000, 13000], budget=16384, sink=256,
+                                  dtype="bf16"),
+    "f32-hd64-past-limit-block": dict(B=1, Hq=4, Hkv=2, hd=64, P=16, seq_lens=[30000], budget=28000, sink=4,
+                                      dtype="f32"),
 }
 
 
@@ -105,10 +110,12 @@ def test_kept_positions(name):
     print(f"{name}: {band} candidates inside the band")
 
 
-def test_planted_ties_keep_the_later_position():
+@pytest.mark.parametrize("name", ["bf16-hd128-p16", "bf16-hd128-past-limit"])
+def test_planted_ties_keep_the_later_position(name):
     """Every key is one of four bf16 vectors, so distances tie exactly on both
-    sides and the kept set must equal the oracle's."""
-    pr, budget, sink = _problem("bf16-hd128-p16", seed=1)
+    sides and the kept set must equal the oracle's (also when the evicted set
+    is chosen per chunk and merged)."""
+    pr, budget, sink = _problem(name, seed=1)
     c = pr.cache
     rng = np.random.default_rng(3)
     protos = synth.store(rng.standard_normal((4, c.hd)).astype(np.float32) * [[1.0], [2.0], [3.0], [4.0]], c.dtype)
@@ -145,7 +152,7 @@ def test_compaction_copies_the_kept_rows(name, dst_P):
             np.testing.assert_array_equal(rows_v.view(sv.dtype), sv[pos])
 
 
-@pytest.mark.parametrize("name", ["bf16-hd128-p16", "f32-hd64-p7", "bf16-hd64-short"])
+@pytest.mark.parametrize("name", ["bf16-hd128-p16", "f32-hd64-p7", "bf16-hd64-short", "bf16-hd128-past-limit"])
 def test_attention_over_the_evicted_cache(name):
     """The dense decode of the evicted cache is the oracle's attention over
     the kept tokens of each KV head."""
