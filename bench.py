@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="decode sink + window on a second stream beside the selection, then the selected pages")
     ap.add_argument("--dense-steps", type=int, default=10)
+    ap.add_argument("--eager", action="store_true",
+                    help="hybrid-3layer-256k: launch every step's kernels one by one instead of replaying graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
@@ -774,7 +776,12 @@ def bench_hybrid(args):
     summarise the pages appended since the previous selection and select and
     decode with the top-k inside the decode kernel, the others decode the
     kept pages with the window grown by the steps since the selection; then
-    the combine.  Reports the average per layer-step over the schedule."""
+    the combine, whose last launch of a step also advances the sequences'
+    lengths (the next step's token appended), so a step is only library
+    launches.  By default every refresh cycle (a selecting step and the 31
+    decode steps after it) is captured as a HIP graph before the timed
+    region, which then replays the four graphs; --eager launches the kernels
+    one by one.  Reports the average per layer-step over the schedule."""
     import torch
 
     from block_sparse_long_page_amd import accounting, configs, synth
@@ -798,8 +805,6 @@ def bench_hybrid(args):
                             splits=args.splits or None)
         dec.build_meta()
         layers.append((dc, dec, hs.windows[li], [to_device(hs.q[li][t]) for t in range(T)]))
-        if li > 0:
-            hs.caches[li] = None  # the host copy is no longer needed (layer 0's serves the CPU baseline)
     torch.cuda.synchronize()
     P = layers[0][0].P
 
@@ -808,27 +813,46 @@ def bench_hybrid(args):
         for dc, dec, W, qs in layers:
             dec.build_meta((L0 - 1) // P, dc.max_pages)
 
-    def schedule(steps):
-        # The summaries are read only when selecting, so the pages appended
-        # since the last selection are summarised right before the next one
-        # (the same summaries as folding each token in as it arrives).
-        t_ref = 0
-        for t in range(steps):
-            L = L0 + t
-            if t > 0:
-                seq_lens.fill_(L)  # one token appended to every sequence
-            if t % RF == 0:
-                first = (L0 + t_ref - 1) // P  # the page that held the last token at the previous selection
-                t_ref = t
-            for dc, dec, W, qs in layers:
-                if t == t_ref:
-                    if t > 0:
-                        dec.build_meta(first, (L - 1) // P + 1)
-                    dec.select_decode(qs[t])
-                else:
-                    dec.decode(qs[t], window=W + (t - t_ref))
-                dec.combine()
+    def issue(t):
+        """The launches of step t (the lengths read L0 + t when it starts).
+        The summaries are read only when selecting, so the pages appended
+        since the last selection are summarised right before the next one
+        (the same summaries as folding each token in as it arrives)."""
+        t_ref = t - t % RF
+        L = L0 + t
+        for li, (dc, dec, W, qs) in enumerate(layers):
+            if t == t_ref:
+                if t > 0:
+                    first = (L0 + t_ref - RF - 1) // P  # the page that held the last token at the previous selection
+                    dec.build_meta(first, (L - 1) // P + 1)
+                dec.select_decode(qs[t])
+            else:
+                dec.decode(qs[t], window=W + (t - t_ref))
+            dec.combine(advance=1 if li == len(layers) - 1 else 0)
 
+    # one graph per refresh cycle: its selecting step and the decode steps until the next
+    graphs = None
+    if not args.eager:
+        graphs = []
+        reset()
+        torch.cuda.synchronize()
+        for t0 in range(0, T, RF):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for t in range(t0, min(T, t0 + RF)):
+                    issue(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def schedule(steps):
+        if graphs is None:
+            for t in range(steps):
+                issue(t)
+        else:
+            for c in range(-(-steps // RF)):
+                graphs[c].replay()
+
+    reset()
     schedule(min(args.warmup, T))
     torch.cuda.synchronize()
     reset()
@@ -839,6 +863,7 @@ def bench_hybrid(args):
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop)
+    assert int(seq_lens[0]) == L0 + T  # every step appended its token
 
     # the dominant call alone: layer 0's decode of its kept pages one step
     # after a selection (window grown by one), back to back
@@ -859,22 +884,6 @@ def bench_hybrid(args):
                for b in range(dc0.B) for h in range(dc0.Hkv))
     dec_bytes = accounting.decode_kernel_bytes(B=dc0.B, Hq=dc0.Hq, Hkv=dc0.Hkv, hd=dc0.hd, elem_bytes=2,
                                                ntok_total=ntok, splits=dec0.splits, sel_entries=int(cnt0.sum()))
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        oracle.build(force=False)
-        host = hs.caches[0]
-        host.seq_lens[:] = L0
-        sb0 = accounting.decode_step_bytes(B=dc0.B, Hq=dc0.Hq, Hkv=dc0.Hkv, hd=dc0.hd, elem_bytes=2, L=L0, P=P,
-                                           S=hs.sink, W=W0, budget=dec0.budget, mode=0, splits=dec0.splits)
-        med, calls = oracle_seconds(lambda: oracle.run(host, hs.q[0][0], mode=hs.mode, Q=1, sink=hs.sink, window=W0,
-                                                       budget=dec0.budget), args.cpu_seconds)
-        cpu = {"value": round(sb0.total / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
-               "kind": "oracle", "sample": f"the first layer's selecting step at {L0} tokens (summaries of all "
-                                           f"pages, scores, top-k, attention) in fp64, {calls} run(s); median "
-                                           f"{med * 1e3:.0f} ms, against that step's algorithmic bytes",
-               "ms_per_step": round(med * 1e3, 1)}
 
     # algorithmic bytes of the schedule
     total = 0
@@ -893,7 +902,41 @@ def bench_hybrid(args):
                 pages = (L - 1) // P - (L0 + t - RF - 1) // P + 1
                 step += dc.B * dc.Hkv * pages * (P * dc.hd * 2 + 2 * dc.hd * 2)
             total += step
-    n = T * len(layers)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle runs the same schedule: all 128 steps of the three layers
+        # (a selection at every refresh, the window grown between refreshes)
+        import oracle
+
+        oracle.build(force=False)
+        del layers, graphs
+        torch.cuda.empty_cache()
+        t_start = time.perf_counter()
+        n_sel = 0
+        for li, host in enumerate(hs.caches):
+            W, budget = hs.windows[li], hs.budgets[li]
+            sel_ref = cnt_ref = None
+            t_ref = 0
+            for t in range(T):
+                host.seq_lens[:] = L0 + t
+                if t % RF == 0:
+                    t_ref = t
+                    r = oracle.run(host, hs.q[li][t], mode=hs.mode, Q=1, sink=hs.sink, window=W, budget=budget)
+                    sel_ref, cnt_ref = r.sel, r.cnt
+                    n_sel += 1
+                else:
+                    oracle.run(host, hs.q[li][t], mode=hs.mode, Q=1, sink=hs.sink, window=W + (t - t_ref),
+                               budget=budget, sel=sel_ref, cnt=cnt_ref)
+        sec = time.perf_counter() - t_start
+        cpu = {"value": round(total / sec / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+               "cpu_model": cpu_model(), "kind": "oracle",
+               "sample": f"the whole schedule in fp64: 128 steps of the three layers ({n_sel} selecting "
+                         f"layer-steps with summaries of every page), against the schedule's algorithmic bytes; "
+                         f"{sec:.2f} s in all, {1e3 * sec / T:.1f} ms per step",
+               "ms_per_step": round(1e3 * sec / T, 2)}
+
+    n = T * len(hs.caches)
     gbs = total / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, hybrid 3-layer 256k, average over 128 steps",
@@ -904,8 +947,11 @@ def bench_hybrid(args):
         "data": "synthetic (seeded): K, V, q N(0,1); one token appended per step and layer",
         "config": {"workload": wl.name, "batch": c0.B, "q_heads": c0.Hq, "kv_heads": c0.Hkv, "head_dim": c0.hd,
                    "context": L0, "page": P, "sink": hs.sink, "layers": [
-                       {"window": W, "budget": dec.budget, "splits": dec.splits} for dc, dec, W, qs in layers],
-                   "refresh": RF, "step": "summary refresh + (select-and-decode | decode) + combine per layer"},
+                       {"window": W, "budget": b_, "splits": s_} for W, b_, s_ in
+                       zip(hs.windows, hs.budgets, [dec0.splits] * len(hs.windows))],
+                   "refresh": RF, "launch": "eager" if args.eager else "a HIP graph per refresh cycle, captured beforehand",
+                   "step": "summary refresh + (select-and-decode | decode) + combine per layer; the last combine "
+                           "advances the lengths"},
         "bytes_per_schedule": total,
         "roofline": roofline_record("k_decode_mfma (kept pages, first layer, one step after a selection)",
                                     dec_bytes, dec_ms),

@@ -76,6 +76,7 @@ _SIGS = {
     "sparse_attn_default_splits": (ctypes.c_int32, [_DESC, _I, _I, _I, _I]),
     "sparse_attn_step_path": (ctypes.c_int32, [_DESC, _I, _I, _I, _I, _P]),
     "sparse_attn_combine": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "sparse_attn_combine_advance": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I, _P]),
     "sparse_attn_decode_step_static": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P,
                                                       _P, _I, _P, _P]),
     "sparse_attn_decode_grouped": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P,
@@ -196,6 +197,13 @@ def sparse_attn_combine(num_rows: int, head_dim: int, num_splits: int, part_o, p
                         lse=None, stream=None) -> None:
     _check(_lib.sparse_attn_combine(num_rows, head_dim, num_splits, _ptr(part_o), _ptr(part_ml), _ptr(out),
                                     out_dtype, _ptr(lse), _stream(stream)), "sparse_attn_combine")
+
+
+def sparse_attn_combine_advance(num_rows: int, head_dim: int, num_splits: int, part_o, part_ml, out, out_dtype: int,
+                                lse, seq_lens, batch: int, advance: int, stream=None) -> None:
+    _check(_lib.sparse_attn_combine_advance(num_rows, head_dim, num_splits, _ptr(part_o), _ptr(part_ml), _ptr(out),
+                                            out_dtype, _ptr(lse), _ptr(seq_lens), batch, advance, _stream(stream)),
+           "sparse_attn_combine_advance")
 
 
 def sparse_attn_decode_grouped(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count, k_max: int, sink_len: int,

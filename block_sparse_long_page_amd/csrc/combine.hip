@@ -22,6 +22,10 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
     const int n = a.splits;
+    // the step's last kernel appends the next token(s): no kernel of this
+    // launch reads the lengths, and the next step's run after it
+    if (a.seq_lens && row == 0)
+        for (int b = lane; b < a.batch; b += 64) a.seq_lens[b] += a.advance;
     const float* ml = a.part_ml + (long)row * n * 2;
     const float* po = a.part_o + (long)row * n * HD + lane * CPL;
 

@@ -226,6 +226,8 @@ struct CombineArgs {
     const float* part_ml;
     void* out;
     float* lse;
+    int32_t* seq_lens;  // or null: after the merge, seq_lens[b] += advance for b < batch
+    int batch, advance;
 };
 
 // The static device scratch of the entry point that allocates nothing:

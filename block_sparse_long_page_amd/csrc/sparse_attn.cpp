@@ -723,6 +723,20 @@ int sparse_attn_decode_step_static(const sa_kv_desc* kv, const void* q, int32_t 
     return sparse_attn_combine((int32_t)rows, kv->head_dim, num_splits, part_o, part_ml, out, out_dtype, lse, stream);
 }
 
+int sparse_attn_combine_advance(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
+                                const float* part_ml, void* out, int32_t out_dtype, float* lse, int32_t* seq_lens,
+                                int32_t batch, int32_t advance, hipStream_t stream)
+{
+    if (!seq_lens || batch < 1 || advance < 0) return SA_ERR_INVALID_ARG;
+    if (!part_o || !part_ml || !out || num_rows < 1) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > kMaxSplits) return SA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits(num_rows, 64)) return SA_ERR_UNSUPPORTED;
+    sa::CombineArgs a{num_rows, head_dim, num_splits, out_dtype, part_o, part_ml, out, lse, seq_lens, batch, advance};
+    return finish(sa::launch_combine(a, stream), stream);
+}
+
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
                         const float* part_ml, void* out, int32_t out_dtype, float* lse, hipStream_t stream)
 {
@@ -731,7 +745,7 @@ int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, 
     if (head_dim != 64 && head_dim != 128) return SA_ERR_UNSUPPORTED;
     if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
     if (!grid_fits(num_rows, 64)) return SA_ERR_UNSUPPORTED;
-    sa::CombineArgs a{num_rows, head_dim, num_splits, out_dtype, part_o, part_ml, out, lse};
+    sa::CombineArgs a{num_rows, head_dim, num_splits, out_dtype, part_o, part_ml, out, lse, nullptr, 0, 0};
     return finish(sa::launch_combine(a, stream), stream);
 }
 

@@ -138,9 +138,16 @@ class SparseDecoder:
         self.combine(stream=stream)
         return self.out
 
-    def combine(self, stream=None):
-        B.sparse_attn_combine(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
-                              self.out_dtype, self.lse, stream)
+    def combine(self, stream=None, advance: int = 0):
+        """The merge of the split partials; with `advance` > 0 the same launch
+        then advances every sequence's length by that many tokens (the step's
+        last kernel appending the next token)."""
+        if advance:
+            B.sparse_attn_combine_advance(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
+                                          self.out_dtype, self.lse, self.c.seq_lens, self.c.B, advance, stream)
+        else:
+            B.sparse_attn_combine(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
+                                  self.out_dtype, self.lse, stream)
 
     def step(self, q: torch.Tensor, stream=None):
         self.select(q, stream=stream)

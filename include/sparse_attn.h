@@ -579,6 +579,22 @@ int sparse_attn_decode_step_static(const sa_kv_desc* kv, const void* q, int32_t 
 int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
                         const float* part_ml, void* out, int32_t out_dtype, float* lse, hipStream_t stream);
 
+/*
+ * sparse_attn_combine, then every sequence's length advanced:
+ * seq_lens[b] += advance for b < batch, inside the same launch.  For the
+ * last kernel of a decode step, so that the next step attends the token it
+ * appends (hybrid sparse attention page: one token appended per step while
+ * the window grows until the next selection) with no separate update of the
+ * lengths, which also lets a step be captured in a HIP graph and replayed.
+ *   seq_lens   int32 [batch], the descriptor's lengths; no other kernel may
+ *              read or write them while the call runs.
+ * Errors: those of sparse_attn_combine; SA_ERR_INVALID_ARG for a null
+ * seq_lens, batch < 1 or advance < 0.
+ */
+int sparse_attn_combine_advance(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
+                                const float* part_ml, void* out, int32_t out_dtype, float* lse, int32_t* seq_lens,
+                                int32_t batch, int32_t advance, hipStream_t stream);
+
 /* A static string naming a status code. */
 const char* sparse_attn_status_string(int status);
 

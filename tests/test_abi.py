@@ -27,7 +27,7 @@ def test_exports_every_header_function():
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
         "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
         "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path",
-        "sparse_attn_decode_step_static"}
+        "sparse_attn_decode_step_static", "sparse_attn_combine_advance"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -241,6 +241,19 @@ def test_combine_checks():
     assert comb(splits=2000) == B.SA_ERR_INVALID_ARG
     assert comb(hd=96) == B.SA_ERR_UNSUPPORTED
     assert comb(odt=3) == B.SA_ERR_UNSUPPORTED
+
+    def adv(**kw):
+        a = dict(rows=4, hd=128, splits=2, po=DEV, pml=DEV, out=DEV, odt=1, lse=None, lens=DEV, batch=2, advance=1)
+        a.update(kw)
+        return lib.sparse_attn_combine_advance(a["rows"], a["hd"], a["splits"], a["po"], a["pml"], a["out"],
+                                               a["odt"], a["lse"], a["lens"], a["batch"], a["advance"], None)
+
+    assert adv(lens=None) == B.SA_ERR_INVALID_ARG
+    assert adv(batch=0) == B.SA_ERR_INVALID_ARG
+    assert adv(advance=-1) == B.SA_ERR_INVALID_ARG
+    assert adv(rows=0) == B.SA_ERR_INVALID_ARG
+    assert adv(splits=0) == B.SA_ERR_INVALID_ARG
+    assert adv(hd=96) == B.SA_ERR_UNSUPPORTED
 
 
 def test_default_splits_fill_the_gpu():

@@ -106,8 +106,7 @@ def test_hybrid_schedule():
         t_ref = 0
         for t in range(T):
             L = L0 + t
-            if t > 0:  # one token appended: refresh the summary of the last page only
-                dc.seq_lens.fill_(L)
+            if t > 0:  # one token appended (the last combine advanced the length): refresh the last page's summary
                 last = (L - 1) // dc.P
                 dec.build_meta(last, last + 1)
             q = to_device(hs.q[li][t])
@@ -117,7 +116,7 @@ def test_hybrid_schedule():
             else:
                 dec.decode(q, window=W + (t - t_ref))
             w_eff = W + (t - t_ref)
-            dec.combine()
+            dec.combine(advance=1)  # the step's last launch appends the next token
             if t in check_at:
                 torch.cuda.synchronize()
                 cache.seq_lens[:] = L
@@ -132,6 +131,8 @@ def test_hybrid_schedule():
                 err = check_output(dec.out_f32(), ref.out, cache.dtype, f"layer {li} step {t}")
                 check_lse(dec.lse_f32(), ref.lse, f"layer {li} step {t}")
                 _say(f"[{wl.name}] layer {li} step {t} window {w_eff} max-abs {err:.2e}")
+        torch.cuda.synchronize()
+        assert int(dc.seq_lens[0]) == L0 + T
         del dc, dec
         torch.cuda.empty_cache()
     _say(f"[{wl.name}] total {time.time() - t0:.1f}s")
