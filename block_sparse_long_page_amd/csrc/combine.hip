@@ -2,7 +2,8 @@
 // DeepSeek-V4 section: partial results are combined; FlashAttention's
 // running-max rescaling).  One wave per output row; the sums run over the
 // splits in a fixed order, so the result does not depend on timing.  A
-// partial with l = 0 is empty and its o is not read into the sum; one with
+// partial with l = 0 is empty and its o is not read (past the first eight
+// splits, whose o is fetched with the (m, l) pairs); one with
 // l = NaN marks a share that was not computed and makes the row's output and
 // lse NaN.
 #include "device_common.hpp"
@@ -19,6 +20,8 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
 {
     constexpr int CPL = HD / 64;  // channels per lane
     constexpr int UNROLL = 8;     // split loads in flight
+    __shared__ float wts[kMaxSplits];    // each split's weight e^{m_s - m*} l_s
+    __shared__ short later[kMaxSplits];  // the splits past the first UNROLL with a non-zero weight, ascending
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
     const int n = a.splits;
@@ -31,13 +34,10 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
 
     // the partials of the first splits go out together with the (m, l) pairs
     float v[UNROLL][CPL];
-    auto fetch = [&](int s0) {
 #pragma unroll
-        for (int j = 0; j < UNROLL; ++j)
+    for (int j = 0; j < UNROLL; ++j)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) v[j][c] = s0 + j < n ? po[(long)(s0 + j) * HD + c] : 0.f;
-    };
-    fetch(0);
+        for (int c = 0; c < CPL; ++c) v[j][c] = j < n ? po[(long)j * HD + c] : 0.f;
     float mx = -INFINITY;
     for (int s = lane; s < n; s += 64) {
         const float2 p = *(const float2*)(ml + 2 * s);
@@ -45,30 +45,52 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a)
     }
     mx = group_max<64>(mx);
 
-    // split s's weight e^{m_s - m*} l_s sits in lane s % 64 of its block of 64
-    // splits and is read out uniformly, so the sums run over s in one order
-    float tot = 0.f, acc[CPL], w = 0.f;
+    // every split's weight (0 for an empty part; l = NaN marks a share that
+    // was not computed and poisons the row), and the later splits that carry
+    // one: only their partials are read
+    int nlater = 0;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.f;
+        if (s < n) {
+            const float2 p = *(const float2*)(ml + 2 * s);
+            w = p.y > 0.f ? expf(p.x - mx) * p.y : (p.y == p.y ? 0.f : p.y);
+            wts[s] = w;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(s < n && s >= UNROLL && w != 0.f);
+        if (s < n && s >= UNROLL && w != 0.f) later[nlater + lanes_below(m)] = (short)s;
+        nlater += __builtin_popcountll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // the sums run over the splits in ascending order (the zero weights of
+    // empty parts add nothing), so the result does not depend on timing
+    float tot = 0.f, acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-    for (int s0 = 0; s0 < n; s0 += UNROLL) {
-        if ((s0 & 63) == 0) {
-            const int s = s0 + lane;
-            w = 0.f;
-            if (s < n) {
-                const float2 p = *(const float2*)(ml + 2 * s);
-                // l = NaN marks a share that was not computed: it poisons the row
-                w = p.y > 0.f ? expf(p.x - mx) * p.y : (p.y == p.y ? 0.f : p.y);
-            }
-        }
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+        if (j >= n) break;
+        const float wj = wts[j];
+        tot += wj;
+        if (wj > 0.f)  // an empty partial (l = 0) contributes nothing, whatever its o holds
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wj, v[j][c], acc[c]);
+    }
+    for (int u0 = 0; u0 < nlater; u0 += UNROLL) {
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) v[j][c] = u0 + j < nlater ? po[(long)later[u0 + j] * HD + c] : 0.f;
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (s0 & 63) + j));
+            if (u0 + j >= nlater) break;
+            const float wj = wts[later[u0 + j]];
             tot += wj;
-            if (wj > 0.f)  // an empty partial (l = 0) contributes nothing, whatever its o holds
+            if (wj > 0.f)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wj, v[j][c], acc[c]);
         }
-        if (s0 + UNROLL < n) fetch(s0 + UNROLL);
     }
     const float inv = tot > 0.f ? 1.0f / tot : (tot == tot ? 0.f : tot);  // NaN stays NaN
     if constexpr (OUT_BF && CPL == 1) {

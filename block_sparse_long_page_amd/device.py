@@ -52,6 +52,9 @@ class DeviceCache:
     block_table: torch.Tensor
     seq_lens: torch.Tensor
     max_seq_len: int
+    # the lengths' value once the queued work has run, when a chunked prefill
+    # advanced them itself (None: unknown, so the next chunk sets them)
+    known_len: Optional[int] = None
 
     @classmethod
     def from_host(cls, c: Cache, device="cuda", max_seq_len: Optional[int] = None) -> "DeviceCache":
@@ -143,6 +146,7 @@ class SparseDecoder:
         then advances every sequence's length by that many tokens (the step's
         last kernel appending the next token)."""
         if advance:
+            self.c.known_len = None
             B.sparse_attn_combine_advance(self.rows, self.c.hd, self.splits, self.part_o, self.part_ml, self.out,
                                           self.out_dtype, self.lse, self.c.seq_lens, self.c.B, advance, stream)
         else:
@@ -373,15 +377,21 @@ class ChunkedPrefill:
         self.lse = torch.empty((self.rows,), dtype=torch.float32, device=dev)
 
     def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
-        with on_stream(stream):
-            self.c.seq_lens.fill_(c0 + self.Q)
+        """The rows [c0, c0 + Q) of the prompt.  The sequences' length must
+        read c0 + Q: it is set here unless the previous chunk was the one just
+        before, whose combine advanced it by Q."""
+        if self.c.known_len != c0 + self.Q:
+            with on_stream(stream):
+                self.c.seq_lens.fill_(c0 + self.Q)
         B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
         B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
                                     stream)
         B.sparse_attn_decode_blocks(self.desc, self.index, q, self.Q, self.sel, self.count, self.k_max, self.window,
                                     0.0, self.ts, self.ls, self.part_o, self.part_ml, self.ws, self.ws_bytes, stream)
-        B.sparse_attn_combine(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out, self.out_dtype,
-                              self.lse, stream)
+        # the next chunk's rows are appended in the same launch
+        B.sparse_attn_combine_advance(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out,
+                                      self.out_dtype, self.lse, self.c.seq_lens, self.c.B, self.Q, stream)
+        self.c.known_len = c0 + 2 * self.Q  # what the lengths read once the queued work has run
         return self.out
 
     def out_f32(self) -> np.ndarray:
