@@ -14,8 +14,8 @@ LIB = os.path.join(PKG, "libsparse_attn.so")
 # load-only reference kernels the benchmark times beside the path (not part of it)
 PROBE_LIB = os.path.join(PKG, "libsa_probe.so")
 PROBE_SOURCE = "probe.hip"
-SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "keydiff.hip", "combine.hip",
-           "noalloc.hip", "sparse_attn.cpp"]
+SOURCES = ["page_meta.hip", "select.hip", "decode.hip", "group.hip", "index.hip", "prefill.hip", "keydiff.hip",
+           "combine.hip", "noalloc.hip", "sparse_attn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -89,6 +89,10 @@ _SIGS = {
     "sparse_attn_blocks_visible": (ctypes.c_int, [_DESC, _IDX, _I, _P, _P]),
     "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                  _P, ctypes.c_size_t, _P]),
+    "sparse_attn_prefill_chunk": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
+                                                 _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "sparse_attn_prefill_num_splits": (ctypes.c_int32, [_DESC, _I, _I, _I]),
+    "sparse_attn_prefill_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX]),
     "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC, _I, _I]),
     "sparse_attn_keydiff_select": (ctypes.c_int, [_DESC, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_keydiff_compact": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P]),
@@ -277,6 +281,25 @@ def sparse_attn_decode_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_ro
                                           _ptr(sel_blocks), _ptr(sel_count), k_max, window_len, softmax_scale,
                                           token_splits, local_splits, _ptr(part_o), _ptr(part_ml), _ptr(workspace),
                                           workspace_bytes, _stream(stream)), "sparse_attn_decode_blocks")
+
+
+def sparse_attn_prefill_num_splits(kv: sa_kv_desc, window_len: int, k_max: int, token_splits: int) -> int:
+    return int(_lib.sparse_attn_prefill_num_splits(ctypes.byref(kv), window_len, k_max, token_splits))
+
+
+def sparse_attn_prefill_workspace_bytes(kv: sa_kv_desc, index: sa_block_index) -> int:
+    return int(_lib.sparse_attn_prefill_workspace_bytes(ctypes.byref(kv), ctypes.byref(index)))
+
+
+def sparse_attn_prefill_chunk(kv: sa_kv_desc, index: sa_block_index, q, num_q_rows: int, window_len: int,
+                              token_budget: int, k_max: int, softmax_scale: float, token_splits: int, visible_end,
+                              sel_blocks, sel_count, part_o, part_ml, out, out_dtype: int, lse, advance: int,
+                              workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sparse_attn_prefill_chunk(ctypes.byref(kv), ctypes.byref(index), _ptr(q), num_q_rows, window_len,
+                                          token_budget, k_max, softmax_scale, token_splits, _ptr(visible_end),
+                                          _ptr(sel_blocks), _ptr(sel_count), _ptr(part_o), _ptr(part_ml), _ptr(out),
+                                          out_dtype, _ptr(lse), advance, _ptr(workspace), workspace_bytes,
+                                          _stream(stream)), "sparse_attn_prefill_chunk")
 
 
 def sparse_attn_status_string(status: int) -> str:

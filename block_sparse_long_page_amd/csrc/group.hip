@@ -32,6 +32,15 @@
 // row's slot for this (page, chunk): slot j * token_splits + chunk, j the
 // page's index in the row's list, so the merge order is fixed and the
 // results do not depend on timing.
+//
+// Prefill mode (a chunk of a prompt over a block index, after the front of
+// prefill.hip, with no plan kernel): the units of a (sequence, KV head) are
+// first the pages of the rows' window [L - W, L), each token chunk attended
+// causally by the rows at or after its first token (the others get an empty
+// partial for that slot), then the index's blocks, largest visible part
+// first, each attended by the rows whose entry in the front's slot table
+// (indexed by block) is >= 0; a block no row chose ends its workgroups at
+// once.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -217,18 +226,80 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int nbk = g.B * g.Hkv;
     const int chunk = blockIdx.x % a.tsplit, rest = blockIdx.x / a.tsplit;
     const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-    const long ui = (long)bk * a.npg + rank;  // rank < npg: the record exists
-    const GroupPage e = a.upages[ui];
-    // this lane's two rows' slots, loaded with the record, not after it
-    const int16_t slot0 = a.slots[ui * kGroupMaxRows + (threadIdx.x & 63)];
-    const int16_t slot1 = a.slots[ui * kGroupMaxRows + 64 + (threadIdx.x & 63)];
-    if (rank >= a.nunion[bk]) return;
-    const int p = e.page;
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
     const Regions rg(g, b, a.S, a.W);
+    const bool prefill = a.pf_order != nullptr;
+    const bool win = prefill && rank < a.nwin;  // a page of the rows' window (prefill)
+    const bool blocks = a.blk_off != nullptr && !win;
 
-    // the rows that chose the page, ascending, and the page's index in each
+    // The unit: a record of the plan (page or block of the union), or in
+    // prefill mode a window page or an index block in the front's order.
+    // Each lane's two rows' slots are loaded with the unit, not after it.
+    int p, phys;
+    int16_t slot0 = -1, slot1 = -1;
+    if (!prefill) {
+        const long ui = (long)bk * a.npg + rank;  // rank < npg: the record exists
+        const GroupPage e = a.upages[ui];
+        slot0 = a.slots[ui * kGroupMaxRows + lane];
+        slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
+        if (rank >= a.nunion[bk]) return;
+        p = e.page;
+        phys = e.phys;
+    } else if (!win) {
+        p = a.pf_order[(long)bk * a.npg + (rank - a.nwin)];
+        const long ui = (long)bk * a.npg + p;
+        if (lane < a.Q) slot0 = a.slots[ui * kGroupMaxRows + lane];
+        if (64 + lane < a.Q) slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
+        // a block no row chose: nothing to write
+        if ((__builtin_amdgcn_ballot_w64(slot0 >= 0) | __builtin_amdgcn_ballot_w64(slot1 >= 0)) == 0ull) return;
+        phys = 0;
+    } else {
+        p = imax(0, rg.L - a.W) / g.P + rank;
+        const int ph = p < g.max_pages ? g.block_table[(long)b * g.max_pages + p] : -1;
+        phys = ph >= 0 && ph < g.num_phys ? ph : -1;
+    }
+
+    // this chunk of the unit's tokens: the page's middle-region tokens
+    // (contiguous rows of one physical page; an unmapped page attends
+    // nothing), the block's (visible) rows in the block layout, or the
+    // window's tokens on the page
+    int a0, a1;
+    if (blocks) {
+        const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
+        a0 = bo[p];
+        a1 = a.blk_end ? imax(a0, imin(a.blk_end[(long)bk * a.npg + p], bo[p + 1])) : bo[p + 1];
+    } else if (win) {
+        a0 = imax(p * g.P, imax(0, rg.L - a.W));
+        a1 = imin((p + 1) * g.P, rg.L);
+    } else {
+        a0 = imax(p * g.P, rg.se);
+        a1 = imin((p + 1) * g.P, rg.ws);
+    }
+    const int n = imax(0, a1 - a0);
+    const int csz = (n + a.tsplit - 1) / a.tsplit;
+    const int t0 = a0 + imin(n, chunk * csz);
+    const bool mapped = blocks || phys >= 0;
+    const int t1 = mapped ? imin(a1, t0 + csz) : t0;
+
+    if (win) {
+        // The rows at or after the chunk's first token attend it (list index
+        // k_max + unit); every other row gets an empty partial for this slot.
+        const int first = t1 > t0 ? t0 - (rg.L - a.Q) : a.Q;  // first row that sees the chunk
+        const int16_t ws = (int16_t)(a.k_max + rank);
+        slot0 = lane >= first && lane < a.Q ? ws : (int16_t)-1;
+        slot1 = 64 + lane >= first && 64 + lane < a.Q ? ws : (int16_t)-1;
+        const int nout = imin(imax(first, 0), a.Q);
+        for (int e2 = threadIdx.x; e2 < nout * G; e2 += 64 * kGW) {
+            const int row = e2 / G, h = e2 - row * G;
+            const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
+            const long slot = prow * a.split_stride + (long)ws * a.tsplit + chunk;
+            *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
+        }
+        if (nout >= a.Q) return;
+    }
+
+    // the rows that attend the unit, ascending, and the unit's index in each
     // row's list (every wave takes the same ballots)
     const uint64_t M0 = __builtin_amdgcn_ballot_w64(slot0 >= 0), M1 = __builtin_amdgcn_ballot_w64(slot1 >= 0);
     const int n0 = __builtin_popcountll(M0);
@@ -245,25 +316,6 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     }
     __syncthreads();
 
-    // this chunk of the page's middle-region tokens: contiguous rows of one
-    // physical page (an unmapped page attends nothing); or of the block's
-    // rows in the block layout
-    const bool blocks = a.blk_off != nullptr;
-    int a0, a1;
-    if (blocks) {
-        const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
-        a0 = bo[p];
-        a1 = a.blk_end ? imax(a0, imin(a.blk_end[(long)bk * a.npg + p], bo[p + 1])) : bo[p + 1];
-    } else {
-        a0 = imax(p * g.P, rg.se);
-        a1 = imin((p + 1) * g.P, rg.ws);
-    }
-    const int n = imax(0, a1 - a0);
-    const int csz = (n + a.tsplit - 1) / a.tsplit;
-    const int t0 = a0 + imin(n, chunk * csz);
-    const int phys = e.phys;
-    const bool mapped = phys >= 0;
-    const int t1 = mapped ? imin(a1, t0 + csz) : t0;
     const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
     // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
     const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
@@ -505,6 +557,17 @@ hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || max_union < 1) return e;
     const dim3 grid((unsigned)((long)max_union * a.tsplit * g.B * g.Hkv));
+    if (g.hd == 128) return launch_group_g<128>(a, grid, s);
+    if (g.hd == 64) return launch_group_g<64>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_group_prefill(const GroupArgs& a, hipStream_t s)
+{
+    const Geometry& g = a.g;
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || !a.pf_order || !a.blk_off || a.nwin < 1)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((long)(a.nwin + a.npg) * a.tsplit * g.B * g.Hkv));
     if (g.hd == 128) return launch_group_g<128>(a, grid, s);
     if (g.hd == 64) return launch_group_g<64>(a, grid, s);
     return hipErrorInvalidValue;

@@ -135,6 +135,13 @@ struct GroupArgs {
     const void* blk_v;
     int blk_n;               // rows per (sequence, KV head)
     const int32_t* blk_end;  // [B][Hkv][npg] end row of each block's visible part, or null (whole blocks)
+    // prefill mode (pf_order != null; block mode, no plan): units 0 .. nwin-1
+    // are the pages of the rows' window [L - W, L), attended causally by the
+    // rows at or after each token chunk's start (list index k_max + unit);
+    // then the blocks in pf_order, each attended by the rows whose slot in
+    // slots[b][kvh][block][row] is >= 0 (the slot table is indexed by block)
+    const int32_t* pf_order;  // [B][Hkv][npg] blocks, largest visible part first
+    int nwin;                 // window units per (sequence, KV head)
 };
 
 // Semantic block index: spherical k-means of the unit keys of positions
@@ -213,6 +220,26 @@ struct KeydiffArgs {
 };
 constexpr int kKdMaxChunks = 16;  // chunks of the two-stage eviction (131072 candidates)
 
+// The front of a sparse prefill chunk over a block index: visible ends,
+// block choice of every row and the grouped decode's slot table.
+constexpr int kPfMaxBlocks = 512;  // index blocks the front holds (8 block keys per lane)
+struct PrefillArgs {
+    Geometry g;
+    const void* q;
+    int Q, N, C;
+    const int32_t* offsets;    // [B][Hkv][C + 1]
+    const int32_t* positions;  // [B][Hkv][N]
+    const float* centres;      // [B][Hkv][C][hd]
+    int budget, k_max, W;
+    int tsplit, split_stride;  // token chunks per block; partial slots per row
+    int32_t* ends;             // [B][Hkv][C] out: end row of each block's visible part
+    int32_t* sel;              // [B][Hkv][Q][k_max] out
+    int32_t* count;            // [B][Hkv][Q] out
+    int16_t* slots;            // [B][Hkv][C][kGroupMaxRows] out: each row's list index of each block, -1 if not chosen
+    int32_t* order;            // [B][Hkv][C] out: the blocks, largest visible part first
+    float* part_ml;            // the (m, l) of the list slots a row leaves unused are set empty
+};
+
 struct CompactArgs {
     Geometry src, dst;
     int budget;
@@ -247,6 +274,9 @@ int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // plan kernel, then the grouped decode over max_union pages per (sequence, KV head)
 hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
+// the grouped decode in prefill mode (no plan kernel): (nwin + npg) units per (sequence, KV head)
+hipError_t launch_group_prefill(const GroupArgs& a, hipStream_t s);
+hipError_t launch_prefill_choose(const PrefillArgs& a, hipStream_t s);
 // the whole index build (every kernel of every iteration)
 hipError_t launch_index_build(const IndexArgs& a, hipStream_t s);
 hipError_t launch_select_blocks(const SelectBlocksArgs& a, hipStream_t s);

@@ -1,0 +1,266 @@
+// The front of one chunk of a sparse prefill over a semantic block index of
+// the prompt (semantic-blocks page: one index serves the prompt's
+// processing; the rows of a prompt chunk compare themselves with the block
+// centres and take the best blocks up to a token budget, among the parts of
+// the blocks that precede the chunk's window; the window, the chunk's own
+// recent tokens, is attended without selection).
+//
+// k_prefill_choose: one workgroup per 8 rows of one (sequence, KV head), a
+// wave per row, in one launch with no other kernel before the grouped
+// decode:
+//  * the visible part of every block (its rows of positions < L - W;
+//    positions ascend inside a block, so the part is a prefix): a k-ary
+//    search by a team of T lanes per block, T probes a round narrowing the
+//    range (T + 1)-fold, every workgroup for itself (a few rounds of loads
+//    instead of a launch); the first workgroup of each (sequence, KV head)
+//    writes the ends and the order in which the grouped decode takes the
+//    blocks (largest visible part first, quarter-octave buckets);
+//  * the row's block scores, the max over the group's heads of q_h . centre_c
+//    in fp32 (a few lanes per block when there are few blocks, their sums
+//    added pairwise);
+//  * the greedy choice by repeated arg-max over (score desc, block asc):
+//    a block is taken while fewer than k_max are taken and the running
+//    visible size stays within the budget; the first is always taken;
+//    blocks without visible rows are never candidates;
+//  * the row's list (ascending) and count, its list index of every block in
+//    the grouped decode's slot table ([block][row], -1 where it did not
+//    choose the block), and an empty partial (m = -inf, l = 0) for every
+//    slot of the list entries it does not use.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "topk_block.hpp"
+
+namespace sa {
+
+namespace {
+
+constexpr int kPfWaves = 8;                    // rows of a workgroup, a wave each
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRounds = kPfMaxBlocks / 64;   // block keys per lane (one lane per block)
+
+template <int HD, int G>
+__global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
+{
+    __shared__ int off_l[kPfMaxBlocks + 1];
+    __shared__ int size_l[kPfMaxBlocks];
+    __shared__ __attribute__((aligned(16))) float qs[kPfWaves][G][HD];
+    __shared__ int hist[256];
+    const Geometry& g = a.g;
+    const int C = a.C, N = a.N;
+    const int ngr = (a.Q + kPfWaves - 1) / kPfWaves;
+    const int grp = blockIdx.x % ngr, bk = blockIdx.x / ngr, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int bound = L - a.W;
+    const int32_t* off = a.offsets + (long)bk * (C + 1);
+    const int32_t* pos = a.positions + (long)bk * N;
+
+    // the rows' queries in fp32, and the block offsets clamped to the layout
+    constexpr int QPR = G * HD / 8;  // 16-byte pieces of one row's queries
+    for (int e = tid; e < kPfWaves * QPR; e += kPfThreads) {
+        const int w = e / QPR, rest = e - w * QPR, h = rest / (HD / 8), d8 = rest - h * (HD / 8);
+        const int row = grp * kPfWaves + w;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row < a.Q)
+            u = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD + 8 * d8);
+        float4* dst = (float4*)&qs[w][h][8 * d8];
+        dst[0] = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+        dst[1] = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
+    }
+    for (int c = tid; c <= C; c += kPfThreads) off_l[c] = imax(0, imin(off[c], N));
+    __syncthreads();
+
+    // Visible ends: block c's rows are [off_l[c], max(off_l[c], off_l[c+1]));
+    // the end is the first row whose position is >= bound.  A team of T
+    // lanes (T a power of two, T * C <= the workgroup) probes T rows that
+    // split the open range evenly; the probes below the bound are a prefix,
+    // and their count leaves one gap, until at most T rows remain, which the
+    // team tests one each.
+    {
+        int T = 1;
+        while (T < 64 && 2 * T * C <= kPfThreads) T *= 2;
+        const int teams = kPfThreads / T, k = tid & (T - 1);
+        const uint64_t team = (T == 64 ? ~0ull : ((1ull << T) - 1)) << (lane & ~(T - 1));
+        for (int c = tid / T; c < C; c += teams) {
+            int lo = off_l[c], hi = imax(lo, off_l[c + 1]);
+            while (hi - lo > T) {  // the same for every lane of the team
+                const long len = hi - lo;
+                const int m = lo + (int)(len * (k + 1) / (T + 1));  // in [lo, hi), increasing in k
+                const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pos[m] < bound) & team);
+                const int nlo = nb > 0 ? lo + (int)(len * nb / (T + 1)) + 1 : lo;
+                hi = nb < T ? lo + (int)(len * (nb + 1) / (T + 1)) : hi;
+                lo = nlo;
+            }
+            const bool below = lo + k < hi && pos[lo + k] < bound;
+            const int end = lo + __builtin_popcountll(__builtin_amdgcn_ballot_w64(below) & team);
+            if (k == 0) {
+                size_l[c] = end - off_l[c];
+                if (grp == 0) a.ends[(long)bk * C + c] = end;
+            }
+        }
+    }
+    __syncthreads();
+
+    // the decode's order of the blocks: largest visible part first (a
+    // counting sort over quarter-octave buckets; the order inside a bucket
+    // follows the atomics and affects timing only)
+    if (grp == 0) {
+        auto bucket = [&](int c) {
+            const int s = size_l[c];
+            if (s <= 0) return 255;
+            const int lb = 31 - __builtin_clz((uint32_t)s);
+            const int fr = lb >= 2 ? (s >> (lb - 2)) & 3 : 0;
+            return 254 - (4 * lb + fr);
+        };
+        for (int i = tid; i < 256; i += kPfThreads) hist[i] = 0;
+        __syncthreads();
+        for (int c = tid; c < C; c += kPfThreads) atomicAdd(&hist[bucket(c)], 1);
+        __syncthreads();
+        if (wave == 0) {
+            int v[4], s = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = hist[4 * lane + i];
+                s += v[i];
+            }
+            int run = wave_inclusive_scan(s) - s;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hist[4 * lane + i] = run;
+                run += v[i];
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < C; c += kPfThreads) a.order[(long)bk * C + atomicAdd(&hist[bucket(c)], 1)] = c;
+    }
+
+    const int r = grp * kPfWaves + wave;
+    if (r >= a.Q) return;  // no barrier below
+
+    // Scores: LPB lanes per block, each over HD / LPB channels; block
+    // cl + per * i in round i.  Lane = part * per + cl.
+    const int LPB = C <= 16 ? 4 : C <= 32 ? 2 : 1;
+    const int per = 64 / LPB, part = lane / per, cl = lane - part * per;
+    const int D = HD / LPB;
+    const int R = (C + per - 1) / per;  // rounds (<= kPfRounds)
+    uint64_t kk[kPfRounds];
+#pragma unroll
+    for (int i = 0; i < kPfRounds; ++i) {
+        kk[i] = 0ull;
+        if (i < R) {
+            const int c = cl + per * i;
+            const bool valid = c < C;
+            const float4* mu = (const float4*)(a.centres + ((long)bk * C + (valid ? c : 0)) * HD + part * D);
+            float dot[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) dot[h] = 0.f;
+            for (int d4 = 0; d4 < D / 4; ++d4) {
+                const float4 m = mu[d4];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float4 x = *(const float4*)&qs[wave][h][part * D + 4 * d4];
+                    dot[h] = fmaf(x.x, m.x, dot[h]);
+                    dot[h] = fmaf(x.y, m.y, dot[h]);
+                    dot[h] = fmaf(x.z, m.z, dot[h]);
+                    dot[h] = fmaf(x.w, m.w, dot[h]);
+                }
+            }
+            // the parts of a block differ in lane bits 4 and 5
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                if (per <= 16) dot[h] += xor_lanes<16>(dot[h]);
+                if (per <= 32) dot[h] += xor_lanes<32>(dot[h]);
+            }
+            float best = dot[0];
+#pragma unroll
+            for (int h = 1; h < G; ++h) best = fmaxf(best, dot[h]);
+            if (valid && size_l[c] > 0)
+                kk[i] = ((uint64_t)order_key(best) << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+        }
+    }
+
+    // Greedy choice by repeated arg-max (a key is 0 once taken, or for a
+    // block without visible rows).  The first block is taken whatever its
+    // size; then blocks while fewer than k_max are taken and the running
+    // size stays within the budget; the first that does not fit ends it.
+    uint32_t mine = 0;  // bit i: this lane's block of round i is taken
+    int count = 0;
+    long run = 0;
+    for (;;) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < kPfRounds; ++i) best = kk[i] > best ? kk[i] : best;
+        const uint32_t bh = (uint32_t)(best >> 32);
+        const uint32_t mh = wave_max_u32(bh);
+        if (mh == 0u) break;  // no candidate left
+        const uint32_t ml = wave_max_u32(bh == mh ? (uint32_t)best : 0u);
+        const int c = (int)(0xffffffffu - ml);
+        const int sz = size_l[c];
+        if (count > 0 && (count >= a.k_max || run + sz > a.budget)) break;
+        run += sz;
+        ++count;
+#pragma unroll
+        for (int i = 0; i < kPfRounds; ++i)
+            if (cl + per * i == c) {
+                kk[i] = 0ull;
+                mine |= 1u << i;
+            }
+    }
+
+    // the list in block order, the slot table, the unused slots
+    int32_t* sel = a.sel + ((long)bk * a.Q + r) * a.k_max;
+    int16_t* slots = a.slots + (long)bk * C * kGroupMaxRows + r;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kPfRounds; ++i) {
+        if (i < R) {
+            const int c = cl + per * i;
+            const bool t = ((mine >> i) & 1u) != 0u && part == 0;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(t);  // part-0 lanes are 0 .. per-1, blocks ascending
+            const int j = base + lanes_below(bal);
+            if (part == 0 && c < C) {
+                if (t) sel[j] = c;
+                slots[(long)c * kGroupMaxRows] = t ? (int16_t)j : (int16_t)-1;
+            }
+            base += __builtin_popcountll(bal);
+        }
+    }
+    for (int j = count + lane; j < a.k_max; j += 64) sel[j] = -1;
+    if (lane == 0) a.count[(long)bk * a.Q + r] = count;
+    const int nempty = (a.k_max - count) * a.tsplit * G;
+    for (int e = lane; e < nempty; e += 64) {
+        const int h = e % G, rest = e / G, s = rest % a.tsplit, j = count + rest / a.tsplit;
+        const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + r;
+        const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
+        *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
+    }
+}
+
+template <int HD>
+hipError_t choose_g(const PrefillArgs& a, dim3 grid, hipStream_t s)
+{
+    const dim3 block(kPfThreads);
+    switch (a.g.G) {
+    case 1: hipLaunchKernelGGL((k_prefill_choose<HD, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_prefill_choose<HD, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_prefill_choose<HD, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_prefill_choose<HD, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_prefill_choose<HD, 16>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_choose(const PrefillArgs& a, hipStream_t s)
+{
+    if (a.g.dtype != 1 || a.C < 1 || a.C > kPfMaxBlocks || a.Q < 1 || a.Q > kGroupMaxRows || a.k_max < 1)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((long)a.g.B * a.g.Hkv * ((a.Q + kPfWaves - 1) / kPfWaves)));
+    if (a.g.hd == 128) return choose_g<128>(a, grid, s);
+    if (a.g.hd == 64) return choose_g<64>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sa

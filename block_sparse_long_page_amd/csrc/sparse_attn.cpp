@@ -183,6 +183,25 @@ GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
     return w;
 }
 
+// The prefill front's workspace: the slot table [B][Hkv][C][kGroupMaxRows]
+// (int16), then the blocks' decode order [B][Hkv][C], 256-byte aligned.
+struct PrefillWs {
+    size_t slots, order, total;
+};
+PrefillWs prefill_ws(const sa_kv_desc* kv, long C)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
+    PrefillWs w;
+    w.slots = 0;
+    w.order = up(bh * (size_t)C * sa::kGroupMaxRows * sizeof(int16_t));
+    w.total = up(w.order + bh * (size_t)C * sizeof(int32_t));
+    return w;
+}
+
+// Window units of a prefill chunk: the pages that [L - W, L) can touch.
+long prefill_window_units(long window_len, long page_size) { return (window_len - 1) / page_size + 2; }
+
 // The selection's workspace: the fp32 scores [B][Hkv][Q][max_pages]; past
 // kMaxSelectPages pages per sequence also every chunk's winners (order keys,
 // then candidate indices, [B][Hkv][Q][nchunks][kTopkChunk] each), 256-byte
@@ -620,6 +639,90 @@ int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index,
                         token_splits, local_splits, part_o, part_ml, workspace, workspace_bytes, index->num_blocks,
                         index->offsets, index->k_blocks, index->v_blocks, index->num_tokens, index->visible_end,
                         stream);
+}
+
+int32_t sparse_attn_prefill_num_splits(const sa_kv_desc* kv, int32_t window_len, int32_t k_max, int32_t token_splits)
+{
+    if (!kv || kv->page_size < 1 || window_len < 1 || k_max < 1 || token_splits < 1 ||
+        token_splits > kMaxTokenSplits)
+        return -SA_ERR_INVALID_ARG;
+    const long s = (k_max + prefill_window_units(window_len, kv->page_size)) * (long)token_splits;
+    return s > kMaxSplits ? -SA_ERR_UNSUPPORTED : (int32_t)s;
+}
+
+size_t sparse_attn_prefill_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index)
+{
+    if (!kv || !index || kv->batch < 1 || kv->num_kv_heads < 1 || index->num_blocks < 1) return 0;
+    return prefill_ws(kv, index->num_blocks).total;
+}
+
+int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              int32_t window_len, int32_t token_budget, int32_t k_max, float softmax_scale,
+                              int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks, int32_t* sel_count,
+                              float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
+                              int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    const int ri = check_index(kv, index);
+    if (ri != SA_OK) return ri;
+    if (!q || !visible_end || !sel_blocks || !sel_count || !part_o || !part_ml || !out) return SA_ERR_INVALID_ARG;
+    if (num_q_rows < 1 || num_q_rows > kv->max_seq_len || window_len < num_q_rows || token_budget < 0 ||
+        advance < 0)
+        return SA_ERR_INVALID_ARG;
+    if (k_max < 1 || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
+    if (token_splits < 1 || token_splits > kMaxTokenSplits) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_BF16 || num_q_rows > sa::kGroupMaxRows || index->num_blocks > sa::kPfMaxBlocks)
+        return SA_ERR_UNSUPPORTED;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    const int32_t stride = sparse_attn_prefill_num_splits(kv, window_len, k_max, token_splits);
+    if (stride < 0) return -stride;
+    const long nwin = prefill_window_units(window_len, kv->page_size);
+    const long nbk = (long)kv->batch * kv->num_kv_heads, C = index->num_blocks;
+    const long rows = (long)kv->batch * kv->num_q_heads * num_q_rows;
+    if (!grid_fits(nbk * ((num_q_rows + 7) / 8), kDecodeThreads) ||
+        !grid_fits((nwin + C) * token_splits * nbk, kDecodeThreads) || !grid_fits(rows, 64))
+        return SA_ERR_UNSUPPORTED;
+    const PrefillWs w = prefill_ws(kv, C);
+    if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0) return SA_ERR_INVALID_ARG;
+    char* base = (char*)workspace;
+    int16_t* slots = (int16_t*)(base + w.slots);
+    int32_t* order = (int32_t*)(base + w.order);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+
+    sa::PrefillArgs f{g,          q,      num_q_rows,  index->num_tokens, (int)C, index->offsets, index->positions,
+                      index->centres, token_budget, k_max, window_len, token_splits, stride, visible_end,
+                      sel_blocks, sel_count, slots,  order,       part_ml};
+    const int r1 = finish(sa::launch_prefill_choose(f, stream), stream);
+    if (r1 != SA_OK) return r1;
+    sa::GroupArgs d{};
+    d.g = g;
+    d.q = q;
+    d.Q = num_q_rows;
+    d.k_max = k_max;
+    d.S = 0;
+    d.W = window_len;
+    d.scale_log2 = scale * 1.4426950408889634f;
+    d.tsplit = token_splits;
+    d.split_stride = stride;
+    d.part_o = part_o;
+    d.part_ml = part_ml;
+    d.slots = slots;
+    d.npg = (int)C;
+    d.blk_off = index->offsets;
+    d.blk_k = index->k_blocks;
+    d.blk_v = index->v_blocks;
+    d.blk_n = index->num_tokens;
+    d.blk_end = visible_end;
+    d.pf_order = order;
+    d.nwin = (int)nwin;
+    const int r2 = finish(sa::launch_group_prefill(d, stream), stream);
+    if (r2 != SA_OK) return r2;
+    sa::CombineArgs m{(int)rows, kv->head_dim, stride, out_dtype, part_o, part_ml, out, lse,
+                      advance > 0 ? (int32_t*)kv->seq_lens : nullptr, kv->batch, advance};
+    return finish(sa::launch_combine(m, stream), stream);
 }
 
 int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,

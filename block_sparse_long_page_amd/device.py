@@ -346,29 +346,40 @@ class ChunkedPrefill:
     """Sparse prefill of a prompt over one block index of the whole prompt
     (a built BlockIndex with num_tokens = the prompt length): the Q rows at
     [c0, c0 + Q) see the index only before their window [c0 + Q - window,
-    c0 + Q) (sparse_attn_blocks_visible), choose at most k_max blocks under
-    the token budget, read each chosen block once for all the chunk's rows
-    (split into token_splits chunks) plus the window causally
-    (sparse_attn_decode_blocks), and combine.  The cache's lengths are set to
-    c0 + Q for the chunk."""
+    c0 + Q), choose at most k_max blocks under the token budget, read each
+    chosen block once for all the chunk's rows (split into token_splits
+    chunks) plus the window causally, and combine.  The cache's lengths are
+    set to c0 + Q for the chunk.
+
+    fused=True: one call, sparse_attn_prefill_chunk (three launches: the
+    front, the grouped decode of the blocks and the window's pages, the
+    combine); fused=False: sparse_attn_blocks_visible,
+    sparse_attn_select_blocks, sparse_attn_decode_blocks (the window by the
+    per-row decode) and sparse_attn_combine_advance."""
 
     def __init__(self, ix: "BlockIndex", Q: int, window: int, k_max: Optional[int] = None, token_splits: int = 1,
-                 local_splits: int = 1, out_dtype: Optional[int] = None):
+                 local_splits: int = 1, out_dtype: Optional[int] = None, fused: bool = True):
         c = ix.c
-        self.ix, self.c, self.Q, self.window = ix, c, Q, window
+        self.ix, self.c, self.Q, self.window, self.fused = ix, c, Q, window, fused
         self.k_max = k_max or ix.C
         self.ts, self.ls = token_splits, local_splits
         dev = c.k.device
         self.ends = torch.zeros((c.B, c.Hkv, ix.C), dtype=torch.int32, device=dev)
         self.index = B.make_block_index(num_tokens=ix.N, num_blocks=ix.C, offsets=ix.offsets,
                                         positions=ix.positions, centres=ix.centres, k_blocks=ix.k_blocks,
-                                        v_blocks=ix.v_blocks, visible_end=self.ends)
+                                        v_blocks=ix.v_blocks, visible_end=None if fused else self.ends)
         self.desc = c.desc()
         self.rows = c.B * c.Hq * Q
         self.sel = torch.full((c.B, c.Hkv, Q, self.k_max), -1, dtype=torch.int32, device=dev)
         self.count = torch.zeros((c.B, c.Hkv, Q), dtype=torch.int32, device=dev)
-        self.stride = self.k_max * self.ts + self.ls
-        self.ws_bytes = B.sparse_attn_blocks_workspace_bytes(self.desc, self.index)
+        if fused:
+            self.stride = B.sparse_attn_prefill_num_splits(self.desc, window, self.k_max, self.ts)
+            if self.stride < 0:
+                raise B.SparseAttnError(-self.stride, "sparse_attn_prefill_num_splits")
+            self.ws_bytes = B.sparse_attn_prefill_workspace_bytes(self.desc, self.index)
+        else:
+            self.stride = self.k_max * self.ts + self.ls
+            self.ws_bytes = B.sparse_attn_blocks_workspace_bytes(self.desc, self.index)
         self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
         self.part_o = torch.empty((self.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
         self.part_ml = torch.empty((self.rows, self.stride, 2), dtype=torch.float32, device=dev)
@@ -383,14 +394,20 @@ class ChunkedPrefill:
         if self.c.known_len != c0 + self.Q:
             with on_stream(stream):
                 self.c.seq_lens.fill_(c0 + self.Q)
-        B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
-        B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
-                                    stream)
-        B.sparse_attn_decode_blocks(self.desc, self.index, q, self.Q, self.sel, self.count, self.k_max, self.window,
-                                    0.0, self.ts, self.ls, self.part_o, self.part_ml, self.ws, self.ws_bytes, stream)
-        # the next chunk's rows are appended in the same launch
-        B.sparse_attn_combine_advance(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out,
-                                      self.out_dtype, self.lse, self.c.seq_lens, self.c.B, self.Q, stream)
+        if self.fused:
+            B.sparse_attn_prefill_chunk(self.desc, self.index, q, self.Q, self.window, budget, self.k_max, 0.0,
+                                        self.ts, self.ends, self.sel, self.count, self.part_o, self.part_ml,
+                                        self.out, self.out_dtype, self.lse, self.Q, self.ws, self.ws_bytes, stream)
+        else:
+            B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
+            B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
+                                        stream)
+            B.sparse_attn_decode_blocks(self.desc, self.index, q, self.Q, self.sel, self.count, self.k_max,
+                                        self.window, 0.0, self.ts, self.ls, self.part_o, self.part_ml, self.ws,
+                                        self.ws_bytes, stream)
+            # the next chunk's rows are appended in the same launch
+            B.sparse_attn_combine_advance(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out,
+                                          self.out_dtype, self.lse, self.c.seq_lens, self.c.B, self.Q, stream)
         self.c.known_len = c0 + 2 * self.Q  # what the lengths read once the queued work has run
         return self.out
 

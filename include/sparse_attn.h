@@ -460,6 +460,72 @@ int sparse_attn_decode_blocks(const sa_kv_desc* kv, const sa_block_index* index,
                               float softmax_scale, int32_t token_splits, int32_t local_splits, float* part_o,
                               float* part_ml, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * One chunk of a sparse prefill over a block index of the prompt, in three
+ * launches (semantic-blocks page: one index serves the prompt's processing;
+ * the queries that chose the same block are grouped so that the block is
+ * read once for all of them; the current fragment is attended without
+ * selection).  The rows at positions [L - num_q_rows, L) of every sequence
+ * (L = its length) see the index only before their window [L - window_len,
+ * L):
+ *   1. the front, one workgroup per 8 rows: the visible part of every block
+ *      (as sparse_attn_blocks_visible), each row's block choice (as
+ *      sparse_attn_select_blocks with those visible parts), and the grouped
+ *      decode's slot table;
+ *   2. the grouped decode: every block chosen by some row is read once
+ *      (its visible rows, in token_splits chunks) for all the rows that
+ *      chose it, and every page of the window once for all the rows,
+ *      causally (row i at position L - num_q_rows + i sees window tokens
+ *      up to its own position);
+ *   3. the merge of each row's partials (sparse_attn_combine_advance).
+ * Same arithmetic as sparse_attn_blocks_visible, sparse_attn_select_blocks,
+ * sparse_attn_decode_blocks (local_splits = 1) and sparse_attn_combine: the
+ * lists are the same, and the window's tokens are split over the partials
+ * differently (per page and token chunk), so outputs differ by rounding only.
+ *   q            [batch][num_q_heads][num_q_rows][head_dim], bf16
+ *   window_len   >= num_q_rows (the window holds the rows themselves)
+ *   token_budget, k_max  as sparse_attn_select_blocks (1 <= k_max <= C)
+ *   token_splits 1..64: token chunks per chosen block and per window page
+ *   visible_end  out, int32 [batch][num_kv_heads][C] (as
+ *                sparse_attn_blocks_visible writes it); index->visible_end
+ *                is not read
+ *   sel_blocks, sel_count  out, as sparse_attn_select_blocks
+ *   part_o, part_ml  [batch * num_q_heads * num_q_rows][num_splits][head_dim]
+ *                and [..][num_splits][2] fp32, num_splits =
+ *                sparse_attn_prefill_num_splits(kv, window_len, k_max,
+ *                token_splits); every slot is written
+ *   out, out_dtype, lse  as sparse_attn_combine (lse nullable)
+ *   advance      >= 0: kv->seq_lens[b] += advance for every sequence after
+ *                the merge (0: the lengths are not written; > 0: seq_lens
+ *                must be writable device memory), so a caller can chain the
+ *                chunks of a prompt without touching the lengths itself
+ *   workspace    >= sparse_attn_prefill_workspace_bytes(kv, index) bytes,
+ *                256-byte aligned
+ * The caller keeps every sequence's prompt positions before L - window_len
+ * inside the index (num_tokens >= L - window_len); rows of positions
+ * outside [0, num_tokens) are never visible.  Results are bitwise
+ * reproducible.  bf16 caches, num_q_rows <= 128, C <= 512.
+ * Errors: those of the index checks; SA_ERR_INVALID_ARG for null outputs,
+ * num_q_rows < 1, window_len < num_q_rows, a negative budget or advance,
+ * k_max or token_splits out of range, a non-finite scale or a small or
+ * misaligned workspace; SA_ERR_UNSUPPORTED for other dtypes, more than 128
+ * rows or 512 blocks, num_splits above 1024 or a grid too large.
+ */
+int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              int32_t window_len, int32_t token_budget, int32_t k_max, float softmax_scale,
+                              int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks, int32_t* sel_count,
+                              float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
+                              int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Partial slots per row of sparse_attn_prefill_chunk: (k_max + the window's
+ * pages, (window_len - 1) / page_size + 2) * token_splits; negative error
+ * code for bad arguments or more than 1024 (host only). */
+int32_t sparse_attn_prefill_num_splits(const sa_kv_desc* kv, int32_t window_len, int32_t k_max,
+                                       int32_t token_splits);
+
+/* Workspace bytes of sparse_attn_prefill_chunk for this index (host only; 0 for bad sizes). */
+size_t sparse_attn_prefill_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index);
+
 /* Workspace bytes of sparse_attn_keydiff_select for this cache, sink and
  * budget (host only; 0 for a bad descriptor, sink_len < 0 or budget < 1). */
 size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv, int32_t sink_len, int32_t budget);

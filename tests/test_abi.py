@@ -27,7 +27,8 @@ def test_exports_every_header_function():
         "sparse_attn_build_block_index", "sparse_attn_select_blocks", "sparse_attn_blocks_workspace_bytes",
         "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
         "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path",
-        "sparse_attn_decode_step_static", "sparse_attn_combine_advance"}
+        "sparse_attn_decode_step_static", "sparse_attn_combine_advance", "sparse_attn_prefill_chunk",
+        "sparse_attn_prefill_num_splits", "sparse_attn_prefill_workspace_bytes"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -367,6 +368,62 @@ def test_block_index_checks():
     assert decode(ts=0) == B.SA_ERR_INVALID_ARG
     assert decode(po=None) == B.SA_ERR_INVALID_ARG
     assert decode(rows=129, W=129) != B.SA_OK  # past the row limit (and the 128-token cache)
+
+
+def test_prefill_chunk_checks():
+    lib = B.library()
+    d = _desc()
+    ix = _index()
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nbk, C = 4, 4
+    wsp = lib.sparse_attn_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
+    assert wsp == up(nbk * C * 128 * 2) + up(nbk * C * 4)  # slot table, block order
+    assert lib.sparse_attn_prefill_workspace_bytes(None, ctypes.byref(ix)) == 0
+    # slots per row: (k_max + window pages) * token chunks; the window [L - W, L)
+    # touches at most (W - 1) // P + 2 pages
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 16, 2, 3) == (2 + 2) * 3
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 17, 2, 1) == 2 + 3
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 1, 1, 1) == 1 + 2
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 0, 2, 1) == -B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 16, 0, 1) == -B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 16, 2, 65) == -B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_prefill_num_splits(ctypes.byref(d), 16, 600, 2) == -B.SA_ERR_UNSUPPORTED  # > 1024
+    assert lib.sparse_attn_prefill_num_splits(None, 16, 2, 1) == -B.SA_ERR_INVALID_ARG
+
+    def chunk(**kw):
+        a = dict(desc=d, ix=ix, q=DEV, rows=2, W=4, budget=64, kmax=2, scale=0.0, ts=1, ends=DEV, sel=DEV, cnt=DEV,
+                 po=DEV, pml=DEV, out=DEV, odt=B.SA_BF16, lse=None, adv=0, ws=DEV, wsb=wsp)
+        a.update(kw)
+        ixp = ctypes.byref(a["ix"]) if a["ix"] is not None else None
+        return lib.sparse_attn_prefill_chunk(ctypes.byref(a["desc"]), ixp, a["q"], a["rows"], a["W"], a["budget"],
+                                             a["kmax"], a["scale"], a["ts"], a["ends"], a["sel"], a["cnt"], a["po"],
+                                             a["pml"], a["out"], a["odt"], a["lse"], a["adv"], a["ws"], a["wsb"],
+                                             None)
+
+    assert chunk(ix=None) == B.SA_ERR_INVALID_ARG
+    for f in ("q", "ends", "sel", "cnt", "po", "pml", "out"):
+        assert chunk(**{f: None}) == B.SA_ERR_INVALID_ARG
+    assert chunk(rows=0) == B.SA_ERR_INVALID_ARG
+    assert chunk(W=1) == B.SA_ERR_INVALID_ARG  # the window must hold the rows
+    assert chunk(budget=-1) == B.SA_ERR_INVALID_ARG
+    assert chunk(adv=-1) == B.SA_ERR_INVALID_ARG
+    assert chunk(kmax=0) == B.SA_ERR_INVALID_ARG
+    assert chunk(kmax=5) == B.SA_ERR_INVALID_ARG  # more than the index's blocks
+    assert chunk(ts=0) == B.SA_ERR_INVALID_ARG
+    assert chunk(ts=65) == B.SA_ERR_INVALID_ARG
+    assert chunk(scale=float("nan")) == B.SA_ERR_INVALID_ARG
+    assert chunk(scale=float("inf")) == B.SA_ERR_INVALID_ARG
+    assert chunk(ws=None) == B.SA_ERR_INVALID_ARG
+    assert chunk(wsb=wsp - 1) == B.SA_ERR_INVALID_ARG
+    assert chunk(ws=DEV + 16) == B.SA_ERR_INVALID_ARG
+    assert chunk(odt=7) == B.SA_ERR_UNSUPPORTED
+    assert chunk(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    assert chunk(rows=129, W=129) != B.SA_OK  # past the row limit (and the 128-token cache)
+    big = _desc(max_seq_len=8192, max_pages_per_seq=512, num_phys_pages=1024)
+    assert chunk(desc=big, ix=_index(num_tokens=8192, num_blocks=513), kmax=1) == B.SA_ERR_UNSUPPORTED
+    assert chunk(desc=big, ix=_index(num_tokens=8192, num_blocks=600), kmax=600, ts=2) == B.SA_ERR_UNSUPPORTED
+    for bad, code in BAD_DESCS:
+        assert chunk(desc=_desc(**bad)) == code
 
 
 def test_keydiff_checks():

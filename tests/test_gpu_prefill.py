@@ -1,7 +1,9 @@
-"""Chunked sparse prefill on the GPU (sparse_attn_blocks_visible with
-sparse_attn_select_blocks and sparse_attn_decode_blocks over one index of the
-whole prompt) against the fp64 oracle of oracle/semantic.py, on the GPU's own
-index: the visible part of every block exactly, the block choice exactly
+"""Chunked sparse prefill on the GPU over one index of the whole prompt, by
+sparse_attn_prefill_chunk (one call: front, grouped decode of the blocks and
+the window's pages, combine) and by the separate calls
+(sparse_attn_blocks_visible, sparse_attn_select_blocks,
+sparse_attn_decode_blocks), against the fp64 oracle of oracle/semantic.py, on
+the GPU's own index: the visible part of every block exactly, the block choice exactly
 where no two block scores are within 1e-4 relative of each other at the
 budget's edge and elsewhere a valid greedy choice for an order consistent
 within that band (tests/parity.py::check_block_choice, such rows counted and
@@ -32,10 +34,14 @@ CASES = {
     "g2-hd64-ragged": (2, 64, 12, 24, 30, 9),
     "g8-hd128-chunk64": (8, 128, 20, 64, 64, 16),
     "g4-hd128-chunk128": (4, 128, 20, 128, 128, 16),
+    # the front's other lane layouts: two lanes per block (17..32 blocks), one
+    # lane per block over two rounds (more than 64), a window wider than the chunk
+    "g4-hd128-c24-wide-window": (4, 128, 30, 32, 40, 24),
+    "g1-hd128-c70": (1, 128, 40, 16, 16, 70),
 }
 
 
-def _setup(name, seed=0, ts=1, k_max=None):
+def _setup(name, seed=0, ts=1, k_max=None, fused=True):
     G, hd, nblk, T, W, C = CASES[name]
     bt = 64 if T <= 64 else 128  # the generator appends the last chunk as one page
     wl = configs.SEMANTIC_512K.scaled(batch=2, num_q_heads=2 * G, num_kv_heads=2, head_dim=hd,
@@ -49,7 +55,8 @@ def _setup(name, seed=0, ts=1, k_max=None):
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
     ix.build(iterations=3)
     torch.cuda.synchronize()
-    return pr, c, dc, ix, ChunkedPrefill(ix, T, W, k_max=k_max, token_splits=ts), q_all, L, T, W, C
+    pf = ChunkedPrefill(ix, T, W, k_max=k_max, token_splits=ts, fused=fused)
+    return pr, c, dc, ix, pf, q_all, L, T, W, C
 
 
 def _qchunk(q_all, c0, T):
@@ -61,10 +68,12 @@ def _qgroup(q_all, c, b, kvh, pos):
     return np.stack([to_f32(q_all[b, kvh * G + h, pos], c.dtype).astype(np.float64) for h in range(G)])
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name,ts,k_max", [(n, 1, None) for n in CASES] + [("g4-hd128", 3, None),
-                                                                          ("g8-hd128-chunk64", 2, 3)])
-def test_prefill_chunks_match_the_oracle(name, ts, k_max):
-    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=1, ts=ts, k_max=k_max)
+                                                                          ("g8-hd128-chunk64", 2, 3),
+                                                                          ("g4-hd128-c24-wide-window", 2, 5)])
+def test_prefill_chunks_match_the_oracle(name, ts, k_max, fused):
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=1, ts=ts, k_max=k_max, fused=fused)
     G = c.Hq // c.Hkv
     perm_all, off_all = ix.positions.cpu().numpy(), ix.offsets.cpu().numpy()
     mu_all = ix.centres.cpu().numpy().astype(np.float64)
@@ -103,12 +112,13 @@ def test_prefill_chunks_match_the_oracle(name, ts, k_max):
     assert ties <= max(2, rows // 10)
 
 
-@pytest.mark.parametrize("name,ts", [("g4-hd128", 1), ("g2-hd64-ragged", 4)])
-def test_prefill_with_every_block_is_dense_causal(name, ts):
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,ts", [("g4-hd128", 1), ("g2-hd64-ragged", 4), ("g4-hd128-c24-wide-window", 3)])
+def test_prefill_with_every_block_is_dense_causal(name, ts, fused):
     """Every chunk of the prompt with an unlimited budget: each row attends
     its whole prefix exactly once (visible block parts + window), whatever
     the token chunks per block."""
-    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=2, ts=ts)
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=2, ts=ts, fused=fused)
     G = c.Hq // c.Hkv
     keys = [[dense_keys_values(c, b, kvh) for kvh in range(c.Hkv)] for b in range(c.B)]
     for c0 in range(0, L - T + 1, T):
@@ -128,3 +138,47 @@ def test_prefill_with_every_block_is_dense_causal(name, ts):
                             qg[h], K, V, np.arange(L) <= pos, 1.0 / np.sqrt(c.hd))
         check_output(out, ref_o, c.dtype, f"{name} c0={c0}")
         check_lse(lse, ref_l, f"{name} c0={c0}")
+
+
+@pytest.mark.parametrize("name,ts", [("g4-hd128-chunk128", 3), ("g1-hd128-c70", 2)])
+def test_fused_prefill_writes_every_partial_slot(name, ts):
+    """Partials filled with NaN before each chunk: every slot the merge reads
+    is written by the call (unused list entries and window chunks a row does
+    not see included), so every output is finite and equals the separate
+    calls' to rounding."""
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup(name, seed=3, ts=ts, k_max=4)
+    ref = ChunkedPrefill(ix, T, W, k_max=4, token_splits=ts, fused=False)
+    for c0 in (0, (L - T) // 2, L - T):
+        budget = max(1, (c0 + T) // 16)
+        qd = _qchunk(q_all, c0, T)
+        pf.part_o.fill_(float("nan"))
+        pf.part_ml.fill_(float("nan"))
+        pf.chunk(qd, c0, budget)
+        torch.cuda.synchronize()
+        out, lse = pf.out_f32(), pf.lse_f32()
+        assert np.isfinite(out).all() and np.isfinite(lse).all(), f"{name} c0={c0}"
+        ref.chunk(qd, c0, budget)
+        torch.cuda.synchronize()
+        same = (pf.sel.cpu().numpy() == ref.sel.cpu().numpy()).all(axis=-1)
+        assert same.mean() > 0.9, f"{name} c0={c0}: lists differ beyond near ties"
+        np.testing.assert_array_equal(pf.ends.cpu().numpy(), ref.ends.cpu().numpy())
+        o1, o2 = out.reshape(c.B, c.Hkv, -1, T, c.hd), ref.out_f32().reshape(c.B, c.Hkv, -1, T, c.hd)
+        for b in range(c.B):
+            for kvh in range(c.Hkv):
+                for i in range(T):
+                    if same[b, kvh, i]:
+                        check_output(o1[b, kvh, :, i], o2[b, kvh, :, i].astype(np.float64), c.dtype,
+                                     f"{name} c0={c0} row {i}")
+
+
+def test_fused_prefill_is_bitwise_reproducible():
+    pr, c, dc, ix, pf, q_all, L, T, W, C = _setup("g4-hd128", seed=4, ts=3)
+    c0 = (L - T) // 2
+    qd = _qchunk(q_all, c0, T)
+    outs = []
+    for _ in range(2):
+        pf.chunk(qd, c0, max(1, (c0 + T) // 16))
+        torch.cuda.synchronize()
+        outs.append((pf.out.clone(), pf.lse.clone(), pf.sel.clone()))
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x, y)
