@@ -215,6 +215,26 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
     return x + (lane < 16 ? 0 : lane < 32 ? t0 : lane < 48 ? t0 + t1 : t0 + t1 + t2);
 }
 
+// Exclusive scan of one int per thread over a workgroup of NT threads (NT/64
+// waves); `wsum` holds NT/64 ints of LDS.  Every thread gets the total too.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int inc = wave_inclusive_scan(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    __syncthreads();  // wsum may be reused
+    return before + inc - v;
+}
+
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 

@@ -15,9 +15,13 @@
 // before it) as an empty partial (m = -inf, l = 0; the combine leaves its o
 // out).
 //
-// k_group_decode_mfma: one workgroup per (sequence, KV head, page of the
-// union, token chunk of the page), launched with the costliest pages (tokens
-// times rows) first.  The chunk's middle-region tokens are
+// k_group_decode_mfma: persistent, one workgroup per CU.  Its items are
+// (page of the union, token chunk of the page, pass) of one (sequence, KV
+// head), taken from a per-(sequence, KV head) counter in the union's order
+// (the costliest pages, tokens times rows, first); a pass holds up to 128
+// query columns, so the rows of a page chosen by many rows are split over
+// several workgroups.  (A grid of one workgroup per possible unit spent
+// tens of microseconds launching workgroups that had nothing to do.)  The chunk's middle-region tokens are
 // contiguous rows of one physical page; 64-token stages of K and V go
 // through LDS (three stages in flight in registers, two in LDS) and are read
 // by every wave.  Query columns are (row, head) pairs of the rows in the
@@ -93,6 +97,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     // candidates: the pages with middle-region tokens, or every block
     const int lo = a.blk_off ? 0 : rg.plo, hi = a.blk_off ? npg - 1 : rg.phi;
     for (int p = tid; p < 2 * npg; p += kPlanThreads) mask[p] = 0ull;
+    if (tid == 0) a.ctr[bk] = 0;  // the grouped decode's item counter
     __syncthreads();
 
     const int32_t* sel = a.sel + (long)bk * a.Q * a.k_max;
@@ -173,12 +178,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
         const unsigned long long m0 = mask[2 * p], m1 = mask[2 * p + 1];
         if ((m0 | m1) != 0ull) {
             const int at = atomicAdd(&by_cost[cost_bucket(p)], 1);
-            const int ph = a.blk_off ? 0 : btr[p];  // blocks: rows of the block layout
             GroupPage e;
             e.page = p;
-            e.phys = ph >= 0 && ph < g.num_phys ? ph : -1;
             e.nrows = __builtin_popcountll(m0) + __builtin_popcountll(m1);
-            e.pad = 0;
+            if (a.blk_off) {  // blocks: the (visible) rows of the block layout
+                const int32_t* bo = a.blk_off + (long)bk * (npg + 1);
+                e.phys = bo[p];
+                e.pad = a.blk_end ? imax(bo[p], imin(a.blk_end[(long)bk * npg + p], bo[p + 1])) : bo[p + 1];
+            } else {
+                const int ph = btr[p];
+                e.phys = ph >= 0 && ph < g.num_phys ? ph : -1;
+                e.pad = 0;
+            }
             up[at] = e;
             rank[p] = at;
         }
@@ -221,313 +232,486 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     static_assert(kStage % 16 == 0, "stages hold whole subtiles");
 
     const Geometry& g = a.g;
-    // workgroup id = (rank * B * Hkv + bk) * tsplit + chunk: the pages of
-    // every (sequence, KV head) in their launch order, interleaved
     const int nbk = g.B * g.Hkv;
-    const int chunk = blockIdx.x % a.tsplit, rest = blockIdx.x / a.tsplit;
-    const int bk = rest % nbk, rank = rest / nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
-    const Regions rg(g, b, a.S, a.W);
-    const bool prefill = a.pf_order != nullptr;
-    const bool win = prefill && rank < a.nwin;  // a page of the rows' window (prefill)
-    const bool blocks = a.blk_off != nullptr && !win;
+    const bool prefill = a.pf_rows != nullptr;
 
-    // The unit: a record of the plan (page or block of the union), or in
-    // prefill mode a window page or an index block in the front's order.
-    // Each lane's two rows' slots are loaded with the unit, not after it.
-    int p, phys;
-    int16_t slot0 = -1, slot1 = -1;
-    if (!prefill) {
-        const long ui = (long)bk * a.npg + rank;  // rank < npg: the record exists
-        const GroupPage e = a.upages[ui];
-        slot0 = a.slots[ui * kGroupMaxRows + lane];
-        slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
-        if (rank >= a.nunion[bk]) return;
-        p = e.page;
-        phys = e.phys;
-    } else if (!win) {
-        p = a.pf_order[(long)bk * a.npg + (rank - a.nwin)];
-        const long ui = (long)bk * a.npg + p;
-        if (lane < a.Q) slot0 = a.slots[ui * kGroupMaxRows + lane];
-        if (64 + lane < a.Q) slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
-        // a block no row chose: nothing to write
-        if ((__builtin_amdgcn_ballot_w64(slot0 >= 0) | __builtin_amdgcn_ballot_w64(slot1 >= 0)) == 0ull) return;
-        phys = 0;
-    } else {
-        p = imax(0, rg.L - a.W) / g.P + rank;
-        const int ph = p < g.max_pages ? g.block_table[(long)b * g.max_pages + p] : -1;
-        phys = ph >= 0 && ph < g.num_phys ? ph : -1;
-    }
+    // The units of the (sequence, KV head) being served: token range [a0, a1)
+    // (rows of the block layout for blocks, positions for pages), physical
+    // page, passes and token chunks, their launch order and the prefix of
+    // their items in that order (filled per (sequence, KV head) below).
+    __shared__ int u_a0[kGroupMaxPages], u_a1[kGroupMaxPages], u_x[kGroupMaxPages];
+    __shared__ int item_pre[kGroupMaxPages + 1];
+    __shared__ unsigned short u_ord[kGroupMaxPages];
+    __shared__ unsigned char u_np[kGroupMaxPages], u_nch[kGroupMaxPages], u_bkt[kGroupMaxPages];
+    __shared__ int hist[256];
+    __shared__ int wsum[kGW];
+    __shared__ int s_item;
 
-    // this chunk of the unit's tokens: the page's middle-region tokens
-    // (contiguous rows of one physical page; an unmapped page attends
-    // nothing), the block's (visible) rows in the block layout, or the
-    // window's tokens on the page
-    int a0, a1;
-    if (blocks) {
-        const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
-        a0 = bo[p];
-        a1 = a.blk_end ? imax(a0, imin(a.blk_end[(long)bk * a.npg + p], bo[p + 1])) : bo[p + 1];
-    } else if (win) {
-        a0 = imax(p * g.P, imax(0, rg.L - a.W));
-        a1 = imin((p + 1) * g.P, rg.L);
-    } else {
-        a0 = imax(p * g.P, rg.se);
-        a1 = imin((p + 1) * g.P, rg.ws);
-    }
-    const int n = imax(0, a1 - a0);
-    const int csz = (n + a.tsplit - 1) / a.tsplit;
-    const int t0 = a0 + imin(n, chunk * csz);
-    const bool mapped = blocks || phys >= 0;
-    const int t1 = mapped ? imin(a1, t0 + csz) : t0;
+    // One item: passes pidx, pidx + np, ... of token chunk s (of nch) of unit
+    // u of (sequence, KV head) bk.  Units: the plan's records in order, or
+    // in prefill mode the window's pages (u < nwin) and then the index's
+    // blocks (block u - nwin).
+    auto process = [&](const int bk, const int u, const int s, const int pidx, const int np, const int nch) {
+        const int b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+        const Regions rg(g, b, a.S, a.W);
+        const bool win = prefill && u < a.nwin;  // a page of the rows' window (prefill)
+        const bool blocks = a.blk_off != nullptr && !win;
+        const int a0 = u_a0[u], a1 = u_a1[u];
+        const int phys = blocks ? 0 : u_x[u];
+        const int p = blocks ? 0 : a0 / g.P;  // the page of a page unit
 
-    if (win) {
-        // The rows at or after the chunk's first token attend it (list index
-        // k_max + unit); every other row gets an empty partial for this slot.
-        const int first = t1 > t0 ? t0 - (rg.L - a.Q) : a.Q;  // first row that sees the chunk
-        const int16_t ws = (int16_t)(a.k_max + rank);
-        slot0 = lane >= first && lane < a.Q ? ws : (int16_t)-1;
-        slot1 = 64 + lane >= first && 64 + lane < a.Q ? ws : (int16_t)-1;
-        const int nout = imin(imax(first, 0), a.Q);
-        for (int e2 = threadIdx.x; e2 < nout * G; e2 += 64 * kGW) {
-            const int row = e2 / G, h = e2 - row * G;
-            const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
-            const long slot = prow * a.split_stride + (long)ws * a.tsplit + chunk;
-            *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
-        }
-        if (nout >= a.Q) return;
-    }
-
-    // the rows that attend the unit, ascending, and the unit's index in each
-    // row's list (every wave takes the same ballots)
-    const uint64_t M0 = __builtin_amdgcn_ballot_w64(slot0 >= 0), M1 = __builtin_amdgcn_ballot_w64(slot1 >= 0);
-    const int n0 = __builtin_popcountll(M0);
-    const int nr = n0 + __builtin_popcountll(M1);
-    if (wave == 0) {
-        if (slot0 >= 0) {
-            rows_l[lanes_below(M0)] = lane;
-            slot_l[lanes_below(M0)] = slot0;
-        }
-        if (slot1 >= 0) {
-            rows_l[n0 + lanes_below(M1)] = 64 + lane;
-            slot_l[n0 + lanes_below(M1)] = slot1;
-        }
-    }
-    __syncthreads();
-
-    const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
-    // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
-    const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
-                      : mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1)
-                               : 0;
-    const uint16_t* kp = (const uint16_t*)(blocks ? a.blk_k : g.k) + row0 * HD;
-    const uint16_t* vp = (const uint16_t*)(blocks ? a.blk_v : g.v) + row0 * HD;
-    const int ntok = t1 - t0;
-
-    const float sl2 = a.scale_log2, slack = kGSlack / sl2;
-    const int ncol = nr * G, ncb = (ncol + 15) / 16;
-
-    // Pass = up to kGW column blocks, one per wave.  With fewer blocks than
-    // waves, the waves of a block take turns over the 16-token subtiles of
-    // each stage and their states merge through LDS at the end of the pass,
-    // so the work follows the live columns.  (The assignment is fixed, so
-    // the results do not depend on timing.)
-    for (int pass = 0; pass * kGW < ncb; ++pass) {
-        const int npb = imin(kGW, ncb - pass * kGW);         // blocks this pass
-        const int cbi = wave % npb, gi = wave / npb;          // this wave's block, its index in the block's group
-        const int gsz = imin((kGW - cbi + npb - 1) / npb, SUB);  // waves that compute on the block
-        const bool computes = gi < gsz;
-        const int cb = pass * kGW + cbi;
-        // lane r is column 16 cb + r
-        gbf16x8_t qb[KK];
-        gf32x4_t o[NB];
-        float m_run = -INFINITY, l_run = 0.f;
-        int cpos;  // position of the column's row (causal limit)
-        {
-            const int col = 16 * cb + r, ri = col / G, h = col - ri * G;
-            const bool live = ri < nr;
-            const int row = live ? rows_l[ri] : 0;
-            // a block's tokens precede every row's window: no causal test
-            cpos = !live ? -1 : blocks ? 0x7fffffff : rg.L - a.Q + row;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (live)
-                    w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD +
-                                        32 * kk + 8 * j);
-                qb[kk] = __builtin_bit_cast(gbf16x8_t, w);
-            }
-#pragma unroll
-            for (int m = 0; m < NB; ++m) o[m] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+        // each lane's two rows' list index of the unit (-1: the row does not attend it)
+        int16_t slot0 = -1, slot1 = -1;
+        if (!prefill) {
+            const long ui = (long)bk * a.npg + u;
+            slot0 = a.slots[ui * kGroupMaxRows + lane];
+            slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
+        } else if (!win) {
+            const long ui = (long)bk * a.npg + (u - a.nwin);
+            if (lane < a.Q) slot0 = a.slots[ui * kGroupMaxRows + lane];
+            if (64 + lane < a.Q) slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
         }
 
-        // stage st: this thread's 16-byte chunks of the K and V rows of
-        // tokens t0 + 64 st .. ; chunks past the chunk's end re-read its
-        // first row and are masked (values written as zeros)
-        struct Staged {
-            uint4 k[LPS], v[LPS];
-        };
-        auto fetch = [&](int st, Staged& x) {
-            static_for<0, LPS>([&](auto U) {
-                constexpr int u = decltype(U)::value;
-                const int e = u * 64 * kGW + threadIdx.x;  // chunk of the stage
-                const int tt = st * kStage + e / CPT;
-                const long off = (tt < ntok ? (long)tt * HD : 0) + (e % CPT) * 8;
-                x.k[u] = *(const uint4*)(kp + off);
-                x.v[u] = *(const uint4*)(vp + off);
-            });
-        };
-        auto stash = [&](int st, int buf, const Staged& x) {
-            static_for<0, LPS>([&](auto U) {
-                constexpr int u = decltype(U)::value;
-                const int e = u * 64 * kGW + threadIdx.x;
-                const int tl = e / CPT, part = e % CPT;
-                const bool ok = st * kStage + tl < ntok;
-                const uint4 kw = x.k[u];
-                *(uint4*)(kl(buf) + tl * KROW + part * 16) = make_uint4(kw.x, kw.y, kw.z, kw.w);
-                const uint4 w = x.v[u];
-                *(uint4*)(vl(buf) + (tl >> 4) * VTILE + gvt_off<VROW>(tl & 15, part * 16)) =
-                    make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
-            });
-        };
-        // this wave's subtiles of stage st: gi, gi + gsz, ...
-        auto compute = [&](int st, int buf) {
-            if (!computes) return;
-            for (int sub = gi; sub < SUB; sub += gsz) {
-                const int tb = st * kStage + sub * 16;  // chunk-relative index of the subtile's token 0
-                const unsigned char* kt = kl(buf) + sub * 16 * KROW;
-                gbf16x8_t ka[KK];
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    ka[kk] = __builtin_bit_cast(gbf16x8_t, *(const uint4*)(kt + r * KROW + kk * 64 + j * 16));
-                gf32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qb[kk], s, 0, 0, 0);
-                // lane (r, j): column r, tokens 4j .. 4j+3 of the subtile
-                float z[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tt = tb + 4 * j + i;
-                    z[i] = tt < ntok && t0 + tt <= cpos ? s[i] : -INFINITY;
+        // this chunk of the unit's tokens: contiguous rows of one physical
+        // page (an unmapped page attends nothing), or of the block layout
+        const int n = imax(0, a1 - a0);
+        const int csz = (n + nch - 1) / nch;
+        const int t0 = a0 + imin(n, s * csz);
+        const bool mapped = blocks || phys >= 0;
+        const int t1 = mapped ? imin(a1, t0 + csz) : t0;
+
+        if (win) {
+            // The rows at or after the chunk's first token attend it (list index
+            // k_max + unit); every other row gets an empty partial for this
+            // slot, and the first chunk's item empties every row's slots of the
+            // chunks the unit does not have.
+            const int first = t1 > t0 ? t0 - (rg.L - a.Q) : a.Q;  // first row that sees the chunk
+            const int16_t ws = (int16_t)(a.k_max + u);
+            slot0 = lane >= first && lane < a.Q ? ws : (int16_t)-1;
+            slot1 = 64 + lane >= first && 64 + lane < a.Q ? ws : (int16_t)-1;
+            const int nout = imin(imax(first, 0), a.Q);
+            if (pidx == 0) {
+                for (int e2 = threadIdx.x; e2 < nout * G; e2 += 64 * kGW) {
+                    const int row = e2 / G, h = e2 - row * G;
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
+                    const long slot = prow * a.split_stride + (long)ws * a.tsplit + s;
+                    *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
                 }
-                float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-                mx = fmaxf(mx, xor_lanes<16>(mx));
-                mx = fmaxf(mx, xor_lanes<32>(mx));
-                const bool need = mx > m_run + slack;
-                if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                    const float mn = need ? mx : m_run;
-                    const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mn) * sl2) : 1.f;
-                    l_run *= alpha;
-                    m_run = mn;
-                    // accumulator rows are columns 4j + i: fetch their factors
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float ai = __shfl(alpha, 4 * j + i);
-#pragma unroll
-                        for (int m = 0; m < NB; ++m) o[m][i] *= ai;
-                    }
-                }
-                const float mref = m_run == -INFINITY ? 0.f : -m_run * sl2;
-                float pz[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pz[i] = __builtin_amdgcn_exp2f(fmaf(z[i], sl2, mref));  // -inf -> 0
-                    l_run += pz[i];
-                }
-                const gi16x4_t pa =
-                    __builtin_bit_cast(gi16x4_t, make_uint2(pack_bf16(pz[0], pz[1]), pack_bf16(pz[2], pz[3])));
-                // p.v: B = values of tokens 4j .. 4j+3 at channel 16m + r
-                const unsigned char* vcol = vl(buf) + sub * VTILE + 2 * r;
-#pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    gi16x4_t vb;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) vb[i] = *(const short*)(vcol + gvt_off<VROW>(4 * j + i, 32 * m));
-                    o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[m], 0, 0, 0);
+                const int nx = s == 0 ? a.tsplit - nch : 0;
+                for (int e2 = threadIdx.x; e2 < a.Q * G * nx; e2 += 64 * kGW) {
+                    const int row = e2 / (G * nx), rest = e2 - row * (G * nx), h = rest / nx, s2 = nch + rest % nx;
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
+                    const long slot = prow * a.split_stride + (long)ws * a.tsplit + s2;
+                    *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
                 }
             }
-        };
-
-        // Stages: three in flight in registers, two in LDS.  Every step
-        // issues its loads and the loop's only exit is at the end of a round
-        // of three, so the waits count one stage each; stages past the end
-        // re-read the chunk's first row and compute nothing.
-        Staged X0, X1, X2;
-        fetch(0, X0);
-        __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in stage order
-        fetch(1, X1);
-        __builtin_amdgcn_sched_barrier(0);
-        fetch(2, X2);
-        __builtin_amdgcn_sched_barrier(0);
-        for (int st = 0; st < nst; st += 3) {
-            stash(st, 0, X0);
-            __syncthreads();
-            fetch(st + 3, X0);
-            compute(st, 0);
-            stash(st + 1, 1, X1);
-            __syncthreads();
-            fetch(st + 4, X1);
-            compute(st + 1, 1);
-            __syncthreads();  // stage st is no longer read from buffer 0
-            stash(st + 2, 0, X2);
-            __syncthreads();
-            fetch(st + 5, X2);
-            compute(st + 2, 0);
-            __syncthreads();  // buffers 0 and 1 are free for the next round
+            if (nout >= a.Q) return;
         }
 
-        // Merge the states of a block's waves (group order) through LDS,
-        // then the first wave of each block writes its partials.  Lane (r, j)
-        // holds columns 4j + i at channel 16m + r.
-        l_run += xor_lanes<16>(l_run);
-        l_run += xor_lanes<32>(l_run);
-        float* wo = (float*)smem;                   // [kGW][16][HD]
-        float* wm = wo + kGW * 16 * HD;             // [kGW][16]
-        float* wl = wm + kGW * 16;                  // [kGW][16]
-        __syncthreads();  // the stage buffers are no longer read
-        if (computes) {
-#pragma unroll
-            for (int m = 0; m < NB; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wo[(wave * 16 + 4 * j + i) * HD + 16 * m + r] = o[m][i];
-            if (j == 0) {
-                wm[wave * 16 + r] = m_run;
-                wl[wave * 16 + r] = l_run;
+        // the rows that attend the unit, ascending, and the unit's index in each
+        // row's list (every wave takes the same ballots)
+        const uint64_t M0 = __builtin_amdgcn_ballot_w64(slot0 >= 0), M1 = __builtin_amdgcn_ballot_w64(slot1 >= 0);
+        const int n0 = __builtin_popcountll(M0);
+        const int nr = n0 + __builtin_popcountll(M1);
+        if (wave == 0) {
+            if (slot0 >= 0) {
+                rows_l[lanes_below(M0)] = lane;
+                slot_l[lanes_below(M0)] = slot0;
+            }
+            if (slot1 >= 0) {
+                rows_l[n0 + lanes_below(M1)] = 64 + lane;
+                slot_l[n0 + lanes_below(M1)] = slot1;
             }
         }
         __syncthreads();
-        if (gi == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int qc = 4 * j + i;
-                float mm = -INFINITY;
-                for (int k = 0; k < gsz; ++k) mm = fmaxf(mm, wm[(cbi + k * npb) * 16 + qc]);
-                float ls = 0.f, os[NB];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) os[m] = 0.f;
-                for (int k = 0; k < gsz; ++k) {
-                    const int w = cbi + k * npb;
-                    const float mw = wm[w * 16 + qc];
-                    const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - mm) * sl2);
-                    ls = fmaf(wl[w * 16 + qc], wt, ls);
-#pragma unroll
-                    for (int m = 0; m < NB; ++m) os[m] = fmaf(wo[(w * 16 + qc) * HD + 16 * m + r], wt, os[m]);
-                }
-                const int col = 16 * cb + qc, ri = col / G, h = col - ri * G;
-                if (ri >= nr) continue;
+        // a unit with fewer token chunks than tsplit: its rows' slots of the
+        // missing chunks are empty (written by the first chunk's first pass)
+        if (!win && s == 0 && pidx == 0 && nch < a.tsplit) {
+            const int nx = a.tsplit - nch;
+            for (int e2 = threadIdx.x; e2 < nr * G * nx; e2 += 64 * kGW) {
+                const int ri = e2 / (G * nx), rest = e2 - ri * (G * nx), h = rest / nx, s2 = nch + rest % nx;
                 const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + rows_l[ri];
-                const long slot = prow * a.split_stride + (long)slot_l[ri] * a.tsplit + chunk;
-                const float inv = ls > 0.f ? 1.0f / ls : 0.f;
-#pragma unroll
-                for (int m = 0; m < NB; ++m) a.part_o[slot * HD + 16 * m + r] = os[m] * inv;
-                if (r == 0) {
-                    a.part_ml[slot * 2 + 0] = ls > 0.f ? mm * sl2 * kLn2 : -INFINITY;
-                    a.part_ml[slot * 2 + 1] = ls;
-                }
+                const long slot = prow * a.split_stride + (long)slot_l[ri] * a.tsplit + s2;
+                *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
             }
         }
-        __syncthreads();  // the next pass restages the buffers
+
+        const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
+        // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
+        const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
+                          : mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1)
+                                   : 0;
+        const uint16_t* kp = (const uint16_t*)(blocks ? a.blk_k : g.k) + row0 * HD;
+        const uint16_t* vp = (const uint16_t*)(blocks ? a.blk_v : g.v) + row0 * HD;
+        const int ntok = t1 - t0;
+
+        const float sl2 = a.scale_log2, slack = kGSlack / sl2;
+        const int ncol = nr * G, ncb = (ncol + 15) / 16;
+        if (pidx * kGW >= ncb) return;  // no column block in this workgroup's passes
+
+        // Pass = up to kGW column blocks, one per wave; this workgroup takes
+        // passes pidx, pidx + npass, ... (the rows' slots are disjoint between
+        // passes, so each is written once).  With fewer blocks than waves, the
+        // waves of a block take turns over the 16-token subtiles of each stage
+        // and their states merge through LDS at the end of the pass, so the
+        // work follows the live columns.  (The assignment is fixed, so the
+        // results do not depend on timing.)
+        for (int pass = pidx; pass * kGW < ncb; pass += np) {
+            const int npb = imin(kGW, ncb - pass * kGW);         // blocks this pass
+            const int cbi = wave % npb, gi = wave / npb;          // this wave's block, its index in the block's group
+            const int gsz = imin((kGW - cbi + npb - 1) / npb, SUB);  // waves that compute on the block
+            const bool computes = gi < gsz;
+            const int cb = pass * kGW + cbi;
+            // lane r is column 16 cb + r
+            gbf16x8_t qb[KK];
+            gf32x4_t o[NB];
+            float m_run = -INFINITY, l_run = 0.f;
+            int cpos;  // position of the column's row (causal limit)
+            {
+                const int col = 16 * cb + r, ri = col / G, h = col - ri * G;
+                const bool live = ri < nr;
+                const int row = live ? rows_l[ri] : 0;
+                // a block's tokens precede every row's window: no causal test
+                cpos = !live ? -1 : blocks ? 0x7fffffff : rg.L - a.Q + row;
+    #pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    uint4 w = make_uint4(0, 0, 0, 0);
+                    if (live)
+                        w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD +
+                                            32 * kk + 8 * j);
+                    qb[kk] = __builtin_bit_cast(gbf16x8_t, w);
+                }
+    #pragma unroll
+                for (int m = 0; m < NB; ++m) o[m] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+
+            // stage st: this thread's 16-byte chunks of the K and V rows of
+            // tokens t0 + 64 st .. ; chunks past the chunk's end re-read its
+            // first row and are masked (values written as zeros)
+            struct Staged {
+                uint4 k[LPS], v[LPS];
+            };
+            auto fetch = [&](int st, Staged& x) {
+                static_for<0, LPS>([&](auto U) {
+                    constexpr int u = decltype(U)::value;
+                    const int e = u * 64 * kGW + threadIdx.x;  // chunk of the stage
+                    const int tt = st * kStage + e / CPT;
+                    const long off = (tt < ntok ? (long)tt * HD : 0) + (e % CPT) * 8;
+                    x.k[u] = *(const uint4*)(kp + off);
+                    x.v[u] = *(const uint4*)(vp + off);
+                });
+            };
+            auto stash = [&](int st, int buf, const Staged& x) {
+                static_for<0, LPS>([&](auto U) {
+                    constexpr int u = decltype(U)::value;
+                    const int e = u * 64 * kGW + threadIdx.x;
+                    const int tl = e / CPT, part = e % CPT;
+                    const bool ok = st * kStage + tl < ntok;
+                    const uint4 kw = x.k[u];
+                    *(uint4*)(kl(buf) + tl * KROW + part * 16) = make_uint4(kw.x, kw.y, kw.z, kw.w);
+                    const uint4 w = x.v[u];
+                    *(uint4*)(vl(buf) + (tl >> 4) * VTILE + gvt_off<VROW>(tl & 15, part * 16)) =
+                        make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
+                });
+            };
+            // this wave's subtiles of stage st: gi, gi + gsz, ...
+            auto compute = [&](int st, int buf) {
+                if (!computes) return;
+                for (int sub = gi; sub < SUB; sub += gsz) {
+                    const int tb = st * kStage + sub * 16;  // chunk-relative index of the subtile's token 0
+                    const unsigned char* kt = kl(buf) + sub * 16 * KROW;
+                    gbf16x8_t ka[KK];
+    #pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        ka[kk] = __builtin_bit_cast(gbf16x8_t, *(const uint4*)(kt + r * KROW + kk * 64 + j * 16));
+                    gf32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qb[kk], s, 0, 0, 0);
+                    // lane (r, j): column r, tokens 4j .. 4j+3 of the subtile
+                    float z[4];
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tt = tb + 4 * j + i;
+                        z[i] = tt < ntok && t0 + tt <= cpos ? s[i] : -INFINITY;
+                    }
+                    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+                    mx = fmaxf(mx, xor_lanes<16>(mx));
+                    mx = fmaxf(mx, xor_lanes<32>(mx));
+                    const bool need = mx > m_run + slack;
+                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                        const float mn = need ? mx : m_run;
+                        const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mn) * sl2) : 1.f;
+                        l_run *= alpha;
+                        m_run = mn;
+                        // accumulator rows are columns 4j + i: fetch their factors
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float ai = __shfl(alpha, 4 * j + i);
+    #pragma unroll
+                            for (int m = 0; m < NB; ++m) o[m][i] *= ai;
+                        }
+                    }
+                    const float mref = m_run == -INFINITY ? 0.f : -m_run * sl2;
+                    float pz[4];
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pz[i] = __builtin_amdgcn_exp2f(fmaf(z[i], sl2, mref));  // -inf -> 0
+                        l_run += pz[i];
+                    }
+                    const gi16x4_t pa =
+                        __builtin_bit_cast(gi16x4_t, make_uint2(pack_bf16(pz[0], pz[1]), pack_bf16(pz[2], pz[3])));
+                    // p.v: B = values of tokens 4j .. 4j+3 at channel 16m + r
+                    const unsigned char* vcol = vl(buf) + sub * VTILE + 2 * r;
+    #pragma unroll
+                    for (int m = 0; m < NB; ++m) {
+                        gi16x4_t vb;
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) vb[i] = *(const short*)(vcol + gvt_off<VROW>(4 * j + i, 32 * m));
+                        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[m], 0, 0, 0);
+                    }
+                }
+            };
+
+            // Stages: three in flight in registers, two in LDS.  Every step
+            // issues its loads and the loop's only exit is at the end of a round
+            // of three, so the waits count one stage each; stages past the end
+            // re-read the chunk's first row and compute nothing.
+            Staged X0, X1, X2;
+            fetch(0, X0);
+            __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in stage order
+            fetch(1, X1);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(2, X2);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int st = 0; st < nst; st += 3) {
+                stash(st, 0, X0);
+                __syncthreads();
+                fetch(st + 3, X0);
+                compute(st, 0);
+                stash(st + 1, 1, X1);
+                __syncthreads();
+                fetch(st + 4, X1);
+                compute(st + 1, 1);
+                __syncthreads();  // stage st is no longer read from buffer 0
+                stash(st + 2, 0, X2);
+                __syncthreads();
+                fetch(st + 5, X2);
+                compute(st + 2, 0);
+                __syncthreads();  // buffers 0 and 1 are free for the next round
+            }
+
+            // Merge the states of a block's waves (group order) through LDS,
+            // then the first wave of each block writes its partials.  Lane (r, j)
+            // holds columns 4j + i at channel 16m + r.
+            l_run += xor_lanes<16>(l_run);
+            l_run += xor_lanes<32>(l_run);
+            float* wo = (float*)smem;                   // [kGW][16][HD]
+            float* wm = wo + kGW * 16 * HD;             // [kGW][16]
+            float* wl = wm + kGW * 16;                  // [kGW][16]
+            __syncthreads();  // the stage buffers are no longer read
+            if (computes) {
+    #pragma unroll
+                for (int m = 0; m < NB; ++m)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) wo[(wave * 16 + 4 * j + i) * HD + 16 * m + r] = o[m][i];
+                if (j == 0) {
+                    wm[wave * 16 + r] = m_run;
+                    wl[wave * 16 + r] = l_run;
+                }
+            }
+            __syncthreads();
+            if (gi == 0) {
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int qc = 4 * j + i;
+                    float mm = -INFINITY;
+                    for (int k = 0; k < gsz; ++k) mm = fmaxf(mm, wm[(cbi + k * npb) * 16 + qc]);
+                    float ls = 0.f, os[NB];
+    #pragma unroll
+                    for (int m = 0; m < NB; ++m) os[m] = 0.f;
+                    for (int k = 0; k < gsz; ++k) {
+                        const int w = cbi + k * npb;
+                        const float mw = wm[w * 16 + qc];
+                        const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - mm) * sl2);
+                        ls = fmaf(wl[w * 16 + qc], wt, ls);
+    #pragma unroll
+                        for (int m = 0; m < NB; ++m) os[m] = fmaf(wo[(w * 16 + qc) * HD + 16 * m + r], wt, os[m]);
+                    }
+                    const int col = 16 * cb + qc, ri = col / G, h = col - ri * G;
+                    if (ri >= nr) continue;
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + rows_l[ri];
+                    const long slot = prow * a.split_stride + (long)slot_l[ri] * a.tsplit + s;
+                    const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+    #pragma unroll
+                    for (int m = 0; m < NB; ++m) a.part_o[slot * HD + 16 * m + r] = os[m] * inv;
+                    if (r == 0) {
+                        a.part_ml[slot * 2 + 0] = ls > 0.f ? mm * sl2 * kLn2 : -INFINITY;
+                        a.part_ml[slot * 2 + 1] = ls;
+                    }
+                }
+            }
+            __syncthreads();  // the next pass restages the buffers
+        }
+    };
+
+    // Persistent schedule: one workgroup per CU, in columns of 8 (one per
+    // XCD); column col serves (sequence, KV head)s col, col + ncol, ... (or
+    // col mod B*Hkv when there are fewer of them than columns).  The
+    // workgroups of a (sequence, KV head) take its items (unit, token chunk,
+    // pass) in the units' launch order (costliest first) from a counter the
+    // kernel before this one cleared, so none waits for work another could
+    // do and none is launched without work.  A unit has one pass per
+    // kGroupPassCols query columns of its rows and up to tsplit token chunks
+    // of at least kGroupChunkMin tokens.
+    const int tid = threadIdx.x;
+    const int ncol = gridDim.x >> 3, col = blockIdx.x >> 3;
+    const int bk0 = nbk >= ncol ? col : col % nbk, bstep = nbk >= ncol ? ncol : nbk;
+    for (int bk = bk0; bk < nbk; bk += bstep) {
+        const int b = bk / g.Hkv;
+        const Regions rg(g, b, a.S, a.W);
+        // the units, loads in one round
+        const int nu = prefill ? a.nwin + a.npg : imin(imax(a.nunion[bk], 0), a.npg);
+        const int wstart = imax(0, rg.L - a.W);
+        for (int u = tid; u < nu; u += 64 * kGW) {
+            int x0, x1, x = 0, nrows;
+            if (!prefill) {
+                const GroupPage e = a.upages[(long)bk * a.npg + u];
+                nrows = e.nrows;
+                if (a.blk_off) {  // blocks: the plan records the row range
+                    x0 = e.phys;
+                    x1 = e.pad;
+                } else {
+                    x0 = imax(e.page * g.P, rg.se);
+                    x1 = imin((e.page + 1) * g.P, rg.ws);
+                    x = e.phys;
+                }
+            } else if (u < a.nwin) {
+                const int pg = wstart / g.P + u;
+                x0 = imax(pg * g.P, wstart);
+                x1 = imin((pg + 1) * g.P, rg.L);
+                const int ph = pg < g.max_pages ? g.block_table[(long)b * g.max_pages + pg] : -1;
+                x = ph >= 0 && ph < g.num_phys ? ph : -1;
+                nrows = imax(1, imin(a.Q, rg.L - x0));  // one item at least: it writes the rows' empty partials
+            } else {
+                const int c = u - a.nwin;
+                const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
+                x0 = bo[c];
+                x1 = imax(x0, imin(a.blk_end[(long)bk * a.npg + c], bo[c + 1]));
+                const uint4 cr = *(const uint4*)(a.pf_rows + ((long)bk * a.npg + c) * 16);
+                const uint32_t w4[4] = {cr.x, cr.y, cr.z, cr.w};
+                nrows = 0;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    nrows += (int)((w4[q4] & 0xff) + ((w4[q4] >> 8) & 0xff) + ((w4[q4] >> 16) & 0xff) + (w4[q4] >> 24));
+            }
+            const int ntk = imax(0, x1 - x0);
+            const int npass = nrows > 0 ? (nrows * G + kGroupPassCols - 1) / kGroupPassCols : 0;
+            const int nch = imin(a.tsplit, imax(1, (ntk + kGroupChunkMin - 1) / kGroupChunkMin));
+            u_a0[u] = x0;
+            u_a1[u] = x1;
+            u_x[u] = x;
+            u_np[u] = (unsigned char)npass;
+            u_nch[u] = (unsigned char)nch;
+            // cost bucket (0: the costliest): tokens times (8 + rows), quarter octaves
+            const uint64_t cost = (uint64_t)imax(1, ntk) * (uint64_t)(8 + nrows);
+            const int lb = 63 - __builtin_clzll(cost);
+            const int fr = lb >= 2 ? (int)((cost >> (lb - 2)) & 3u) : 0;
+            u_bkt[u] = (unsigned char)(255 - imin(255, 4 * lb + fr));
+        }
+        __syncthreads();
+
+        // launch order: the plan's (already costliest first), or a stable
+        // counting sort of the units by cost bucket, the same in every
+        // workgroup of the (sequence, KV head)
+        if (!prefill) {
+            for (int k = tid; k < nu; k += 64 * kGW) u_ord[k] = (unsigned short)k;
+        } else {
+            for (int i = tid; i < 256; i += 64 * kGW) hist[i] = 0;
+            __syncthreads();
+            for (int u = tid; u < nu; u += 64 * kGW) atomicAdd(&hist[u_bkt[u]], 1);
+            __syncthreads();
+            if (wave == 0) {
+                int v[4], sum = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = hist[4 * lane + i];
+                    sum += v[i];
+                }
+                int run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hist[4 * lane + i] = run;
+                    run += v[i];
+                }
+                // units in order, 64 at a time: a unit's place is its bucket's
+                // base plus the units of that bucket before it
+                const uint64_t below = (1ull << lane) - 1ull;
+                for (int k0 = 0; k0 < nu; k0 += 64) {
+                    const int u = k0 + lane;
+                    const bool valid = u < nu;
+                    const int bkt = valid ? u_bkt[u] : 0;
+                    uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+                    for (int bit = 0; bit < 8; ++bit) {
+                        const bool on = ((bkt >> bit) & 1) != 0;
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(on);
+                        same &= on ? m : ~m;
+                    }
+                    if (valid) {
+                        u_ord[hist[bkt] + __builtin_popcountll(same & below)] = (unsigned short)u;
+                        if ((same >> lane) == 1ull) hist[bkt] += __builtin_popcountll(same);  // the group's last lane
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        // the prefix of the items in launch order, 8 units a thread
+        constexpr int UPT = (kGroupMaxPages + 64 * kGW - 1) / (64 * kGW);
+        int cnt[UPT], mine = 0;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int k = tid * UPT + i;
+            cnt[i] = 0;
+            if (k < nu) {
+                const int u = u_ord[k];
+                cnt[i] = (int)u_np[u] * (int)u_nch[u];
+            }
+            mine += cnt[i];
+        }
+        int total;
+        int run = block_exclusive_scan<64 * kGW>(mine, wsum, total);
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int k = tid * UPT + i;
+            if (k < nu) item_pre[k] = run;
+            run += cnt[i];
+        }
+        __syncthreads();
+
+        for (;;) {
+            if (tid == 0) s_item = atomicAdd(a.ctr + bk, 1);
+            __syncthreads();
+            const int it = s_item;
+            __syncthreads();  // s_item is read before the next item's fetch
+            if (it >= total) break;
+            // the unit: the last in launch order with item_pre <= it (units
+            // without items share the next one's prefix and are skipped)
+            int lo = 0, hi = nu - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (item_pre[mid] <= it)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int u = u_ord[lo];
+            const int np = u_np[u], nch = u_nch[u], kk = it - item_pre[lo];
+            process(bk, u, kk / np, kk % np, np, nch);
+            __syncthreads();  // LDS of this item is no longer read
+        }
     }
 }
 
@@ -548,29 +732,60 @@ hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
+hipError_t launch_group(const GroupArgs& a, int workgroups, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages) return hipErrorInvalidValue;
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || !a.ctr || workgroups < 8 || workgroups % 8)
+        return hipErrorInvalidValue;
     const size_t lds = (2 * sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || max_union < 1) return e;
-    const dim3 grid((unsigned)((long)max_union * a.tsplit * g.B * g.Hkv));
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)workgroups);
     if (g.hd == 128) return launch_group_g<128>(a, grid, s);
     if (g.hd == 64) return launch_group_g<64>(a, grid, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_group_prefill(const GroupArgs& a, hipStream_t s)
+hipError_t launch_group_prefill(const GroupArgs& a, int workgroups, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || !a.pf_order || !a.blk_off || a.nwin < 1)
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.nwin + a.npg > kGroupMaxPages || !a.pf_rows || !a.blk_off ||
+        !a.blk_end || a.nwin < 1 || !a.ctr || workgroups < 8 || workgroups % 8)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((long)(a.nwin + a.npg) * a.tsplit * g.B * g.Hkv));
+    const dim3 grid((unsigned)workgroups);
     if (g.hd == 128) return launch_group_g<128>(a, grid, s);
     if (g.hd == 64) return launch_group_g<64>(a, grid, s);
     return hipErrorInvalidValue;
+}
+
+namespace {
+template <int HD>
+int resident_g(int G)
+{
+    const int bs = 64 * kGW;
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (G) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 1>, bs, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 2>, bs, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 4>, bs, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 8>, bs, 0); break;
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 16>, bs, 0); break;
+    default: break;
+    }
+    return e == hipSuccess && n > 0 ? n : 1;
+}
+}  // namespace
+
+int group_workgroups(int hd, int G)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int per = hd == 64 ? resident_g<64>(G) : resident_g<128>(G);
+    return (cus * per + 7) / 8 * 8;
 }
 
 }  // namespace sa

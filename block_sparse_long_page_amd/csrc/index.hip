@@ -58,26 +58,6 @@ __device__ __forceinline__ void unpack8(const uint4 w, float* x)
     x[4] = bf_lo(w.z), x[5] = bf_hi(w.z), x[6] = bf_lo(w.w), x[7] = bf_hi(w.w);
 }
 
-// Exclusive scan of one int per thread over a workgroup of NT threads (NT/64
-// waves); `wsum` holds NT/64 ints of LDS.  Every thread gets the total too.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int inc = wave_inclusive_scan(v);
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        before += w < wave ? wsum[w] : 0;
-        total += wsum[w];
-    }
-    __syncthreads();  // wsum may be reused
-    return before + inc - v;
-}
-
 // ---- build ---------------------------------------------------------------
 
 template <int HD>

@@ -99,12 +99,13 @@ struct SelectDecodeArgs {
 
 constexpr uint32_t kStatusGaveUp = 1;  // a share of the attended set was not computed
 
-// A page of the union of the rows' page lists of one (sequence, KV head).
+// A unit of the union of the rows' lists of one (sequence, KV head): a page
+// of the paged cache, or a block of an index.
 struct __attribute__((aligned(16))) GroupPage {
-    int32_t page;   // logical page
-    int32_t phys;   // its physical page, -1 when unmapped
+    int32_t page;   // logical page, or block
+    int32_t phys;   // page: its physical page, -1 when unmapped; block: its first row in the block layout
     int32_t nrows;  // rows that chose it (the slot table names them)
-    int32_t pad;
+    int32_t pad;    // block: the end of its (visible) rows; page: 0
 };
 
 // Multi-query decode grouped by page: the union of the rows' page lists is
@@ -135,14 +136,22 @@ struct GroupArgs {
     const void* blk_v;
     int blk_n;               // rows per (sequence, KV head)
     const int32_t* blk_end;  // [B][Hkv][npg] end row of each block's visible part, or null (whole blocks)
-    // prefill mode (pf_order != null; block mode, no plan): units 0 .. nwin-1
+    // prefill mode (pf_rows != null; block mode, no plan): units 0 .. nwin-1
     // are the pages of the rows' window [L - W, L), attended causally by the
     // rows at or after each token chunk's start (list index k_max + unit);
-    // then the blocks in pf_order, each attended by the rows whose slot in
+    // then the blocks, each attended by the rows whose slot in
     // slots[b][kvh][block][row] is >= 0 (the slot table is indexed by block)
-    const int32_t* pf_order;  // [B][Hkv][npg] blocks, largest visible part first
-    int nwin;                 // window units per (sequence, KV head)
+    int nwin;                      // window units per (sequence, KV head)
+    const unsigned char* pf_rows;  // [B][Hkv][npg][16] rows of each row group of 8 that chose each block
+    int32_t* ctr;                  // [B][Hkv] item counters, zero when the decode starts
 };
+
+// Query columns (row, head) of one pass of a grouped-decode workgroup (16 per
+// wave, 8 waves); a unit with more columns is split into items of one pass.
+constexpr int kGroupPassCols = 128;
+// Fewest tokens of a token chunk: a unit of n tokens has min(tsplit,
+// ceil(n / kGroupChunkMin)) chunks (one item streams a chunk).
+constexpr int kGroupChunkMin = 512;
 
 // Semantic block index: spherical k-means of the unit keys of positions
 // [0, N) of every (sequence, KV head) into C blocks, and the block layout.
@@ -236,8 +245,9 @@ struct PrefillArgs {
     int32_t* sel;              // [B][Hkv][Q][k_max] out
     int32_t* count;            // [B][Hkv][Q] out
     int16_t* slots;            // [B][Hkv][C][kGroupMaxRows] out: each row's list index of each block, -1 if not chosen
-    int32_t* order;            // [B][Hkv][C] out: the blocks, largest visible part first
     float* part_ml;            // the (m, l) of the list slots a row leaves unused are set empty
+    unsigned char* rows;       // [B][Hkv][C][16] out: rows of each row group of 8 that chose each block (0 past the groups)
+    int32_t* ctr;              // [B][Hkv] the grouped decode's item counters, cleared here
 };
 
 struct CompactArgs {
@@ -272,10 +282,12 @@ hipError_t launch_select_decode(const SelectDecodeArgs& a, hipStream_t s);
 // resident decode workgroups per CU for this shape (occupancy query)
 int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-// plan kernel, then the grouped decode over max_union pages per (sequence, KV head)
-hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
+// plan kernel, then the grouped decode (persistent: `workgroups`, a multiple of 8)
+hipError_t launch_group(const GroupArgs& a, int workgroups, hipStream_t s);
 // the grouped decode in prefill mode (no plan kernel): (nwin + npg) units per (sequence, KV head)
-hipError_t launch_group_prefill(const GroupArgs& a, hipStream_t s);
+hipError_t launch_group_prefill(const GroupArgs& a, int workgroups, hipStream_t s);
+// resident grouped-decode workgroups on the device (CUs times occupancy), a multiple of 8
+int group_workgroups(int hd, int G);
 hipError_t launch_prefill_choose(const PrefillArgs& a, hipStream_t s);
 // the whole index build (every kernel of every iteration)
 hipError_t launch_index_build(const IndexArgs& a, hipStream_t s);

@@ -13,8 +13,7 @@
 //    search by a team of T lanes per block, T probes a round narrowing the
 //    range (T + 1)-fold, every workgroup for itself (a few rounds of loads
 //    instead of a launch); the first workgroup of each (sequence, KV head)
-//    writes the ends and the order in which the grouped decode takes the
-//    blocks (largest visible part first, quarter-octave buckets);
+//    writes the ends;
 //  * the row's block scores, the max over the group's heads of q_h . centre_c
 //    in fp32 (a few lanes per block when there are few blocks, their sums
 //    added pairwise);
@@ -25,7 +24,11 @@
 //  * the row's list (ascending) and count, its list index of every block in
 //    the grouped decode's slot table ([block][row], -1 where it did not
 //    choose the block), and an empty partial (m = -inf, l = 0) for every
-//    slot of the list entries it does not use.
+//    slot of the list entries it does not use;
+//  * per block, how many of the workgroup's 8 rows chose it (the grouped
+//    decode sizes its items from these counts without reading the slot
+//    table), and the first workgroup of a (sequence, KV head) clears the
+//    grouped decode's item counter.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "topk_block.hpp"
@@ -37,6 +40,7 @@ namespace {
 constexpr int kPfWaves = 8;                    // rows of a workgroup, a wave each
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRounds = kPfMaxBlocks / 64;   // block keys per lane (one lane per block)
+constexpr int kPfProbe = 1;                    // rows a lane reads per round of the visible-end search
 
 template <int HD, int G>
 __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
     __shared__ int off_l[kPfMaxBlocks + 1];
     __shared__ int size_l[kPfMaxBlocks];
     __shared__ __attribute__((aligned(16))) float qs[kPfWaves][G][HD];
-    __shared__ int hist[256];
+    __shared__ int nch[kPfMaxBlocks];  // rows of this workgroup that chose each block
     const Geometry& g = a.g;
     const int C = a.C, N = a.N;
     const int ngr = (a.Q + kPfWaves - 1) / kPfWaves;
@@ -68,74 +72,41 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
         dst[1] = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
     }
     for (int c = tid; c <= C; c += kPfThreads) off_l[c] = imax(0, imin(off[c], N));
+    for (int c = tid; c < C; c += kPfThreads) nch[c] = 0;
+    if (grp == 0 && tid == 0) a.ctr[bk] = 0;  // the grouped decode's item counter
     __syncthreads();
 
     // Visible ends: block c's rows are [off_l[c], max(off_l[c], off_l[c+1]));
     // the end is the first row whose position is >= bound.  A team of T
-    // lanes (T a power of two, T * C <= the workgroup) probes T rows that
-    // split the open range evenly; the probes below the bound are a prefix,
-    // and their count leaves one gap, until at most T rows remain, which the
-    // team tests one each.
-    {
-        int T = 1;
-        while (T < 64 && 2 * T * C <= kPfThreads) T *= 2;
-        const int teams = kPfThreads / T, k = tid & (T - 1);
-        const uint64_t team = (T == 64 ? ~0ull : ((1ull << T) - 1)) << (lane & ~(T - 1));
-        for (int c = tid / T; c < C; c += teams) {
-            int lo = off_l[c], hi = imax(lo, off_l[c + 1]);
-            while (hi - lo > T) {  // the same for every lane of the team
-                const long len = hi - lo;
-                const int m = lo + (int)(len * (k + 1) / (T + 1));  // in [lo, hi), increasing in k
-                const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pos[m] < bound) & team);
-                const int nlo = nb > 0 ? lo + (int)(len * nb / (T + 1)) + 1 : lo;
-                hi = nb < T ? lo + (int)(len * (nb + 1) / (T + 1)) : hi;
-                lo = nlo;
-            }
-            const bool below = lo + k < hi && pos[lo + k] < bound;
-            const int end = lo + __builtin_popcountll(__builtin_amdgcn_ballot_w64(below) & team);
-            if (k == 0) {
-                size_l[c] = end - off_l[c];
-                if (grp == 0) a.ends[(long)bk * C + c] = end;
-            }
-        }
-    }
-    __syncthreads();
-
-    // the decode's order of the blocks: largest visible part first (a
-    // counting sort over quarter-octave buckets; the order inside a bucket
-    // follows the atomics and affects timing only)
-    if (grp == 0) {
-        auto bucket = [&](int c) {
-            const int s = size_l[c];
-            if (s <= 0) return 255;
-            const int lb = 31 - __builtin_clz((uint32_t)s);
-            const int fr = lb >= 2 ? (s >> (lb - 2)) & 3 : 0;
-            return 254 - (4 * lb + fr);
-        };
-        for (int i = tid; i < 256; i += kPfThreads) hist[i] = 0;
-        __syncthreads();
-        for (int c = tid; c < C; c += kPfThreads) atomicAdd(&hist[bucket(c)], 1);
-        __syncthreads();
-        if (wave == 0) {
-            int v[4], s = 0;
+    // lanes (T a power of two, T * C <= the workgroup) reads NP = T * kPfProbe
+    // rows a round: while more than NP rows remain, rows that split the open
+    // range evenly (those below the bound are a prefix, and their count
+    // leaves one gap), then the remaining rows themselves, whose count below
+    // the bound gives the end.  The first round's loads are issued before
+    // the scores below and consumed after them.
+    int T = 1;
+    while (T < 64 && 2 * T * C <= kPfThreads) T *= 2;
+    const int teams = kPfThreads / T, k = tid & (T - 1), NP = T * kPfProbe;
+    int probe[kPfProbe];
+    auto load_round = [&](int lo, int hi) {
+        const long len = hi - lo;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[i] = hist[4 * lane + i];
-                s += v[i];
-            }
-            int run = wave_inclusive_scan(s) - s;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hist[4 * lane + i] = run;
-                run += v[i];
-            }
+        for (int u = 0; u < kPfProbe; ++u) {
+            const int i = k * kPfProbe + u;
+            const int m = len > NP ? lo + (int)(len * (i + 1) / (NP + 1)) : lo + i;
+            probe[u] = m < hi ? pos[m] : 0x7fffffff;  // past the range: never below the bound
         }
-        __syncthreads();
-        for (int c = tid; c < C; c += kPfThreads) a.order[(long)bk * C + atomicAdd(&hist[bucket(c)], 1)] = c;
+    };
+    const int c_first = tid / T;
+    int lo_first = 0, hi_first = 0;
+    if (c_first < C) {
+        lo_first = off_l[c_first];
+        hi_first = imax(lo_first, off_l[c_first + 1]);
+        load_round(lo_first, hi_first);
     }
 
     const int r = grp * kPfWaves + wave;
-    if (r >= a.Q) return;  // no barrier below
+    const bool row_ok = r < a.Q;
 
     // Scores: LPB lanes per block, each over HD / LPB channels; block
     // cl + per * i in round i.  Lane = part * per + cl.
@@ -174,65 +145,117 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
             float best = dot[0];
 #pragma unroll
             for (int h = 1; h < G; ++h) best = fmaxf(best, dot[h]);
-            if (valid && size_l[c] > 0)
-                kk[i] = ((uint64_t)order_key(best) << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+            if (valid) kk[i] = ((uint64_t)order_key(best) << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
         }
     }
 
-    // Greedy choice by repeated arg-max (a key is 0 once taken, or for a
-    // block without visible rows).  The first block is taken whatever its
-    // size; then blocks while fewer than k_max are taken and the running
-    // size stays within the budget; the first that does not fit ends it.
-    uint32_t mine = 0;  // bit i: this lane's block of round i is taken
-    int count = 0;
-    long run = 0;
-    for (;;) {
-        uint64_t best = 0ull;
+    // complete the search (the first round's probes are in `probe`)
+    for (int c = c_first; c < C; c += teams) {
+        int lo = lo_first, hi = hi_first;
+        if (c != c_first) {
+            lo = off_l[c];
+            hi = imax(lo, off_l[c + 1]);
+            load_round(lo, hi);
+        }
+        int end;
+        for (;;) {  // the same for every lane of the team
+            int nb = 0;
 #pragma unroll
-        for (int i = 0; i < kPfRounds; ++i) best = kk[i] > best ? kk[i] : best;
-        const uint32_t bh = (uint32_t)(best >> 32);
-        const uint32_t mh = wave_max_u32(bh);
-        if (mh == 0u) break;  // no candidate left
-        const uint32_t ml = wave_max_u32(bh == mh ? (uint32_t)best : 0u);
-        const int c = (int)(0xffffffffu - ml);
-        const int sz = size_l[c];
-        if (count > 0 && (count >= a.k_max || run + sz > a.budget)) break;
-        run += sz;
-        ++count;
-#pragma unroll
-        for (int i = 0; i < kPfRounds; ++i)
-            if (cl + per * i == c) {
-                kk[i] = 0ull;
-                mine |= 1u << i;
+            for (int u = 0; u < kPfProbe; ++u) nb += probe[u] < bound;
+            for (int o = 1; o < T; o <<= 1) nb += __shfl_xor(nb, o);
+            const long len = hi - lo;
+            if (len <= NP) {
+                end = lo + nb;
+                break;
             }
+            const int nlo = nb > 0 ? lo + (int)(len * nb / (NP + 1)) + 1 : lo;
+            hi = nb < NP ? lo + (int)(len * (nb + 1) / (NP + 1)) : hi;
+            lo = nlo;
+            load_round(lo, hi);
+        }
+        if (k == 0) {
+            size_l[c] = end - off_l[c];
+            if (grp == 0) a.ends[(long)bk * C + c] = end;
+        }
     }
+    __syncthreads();
 
-    // the list in block order, the slot table, the unused slots
-    int32_t* sel = a.sel + ((long)bk * a.Q + r) * a.k_max;
-    int16_t* slots = a.slots + (long)bk * C * kGroupMaxRows + r;
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < kPfRounds; ++i) {
-        if (i < R) {
+    if (row_ok) {
+        // blocks without visible rows are not candidates
+    #pragma unroll
+        for (int i = 0; i < kPfRounds; ++i) {
             const int c = cl + per * i;
-            const bool t = ((mine >> i) & 1u) != 0u && part == 0;
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(t);  // part-0 lanes are 0 .. per-1, blocks ascending
-            const int j = base + lanes_below(bal);
-            if (part == 0 && c < C) {
-                if (t) sel[j] = c;
-                slots[(long)c * kGroupMaxRows] = t ? (int16_t)j : (int16_t)-1;
+            if (i < R && c < C && size_l[c] <= 0) kk[i] = 0ull;
+        }
+
+        // Greedy choice by repeated arg-max (a key is 0 once taken, or for a
+        // block without visible rows).  The first block is taken whatever its
+        // size; then blocks while fewer than k_max are taken and the running
+        // size stays within the budget; the first that does not fit ends it.
+        uint32_t mine = 0;  // bit i: this lane's block of round i is taken
+        int count = 0;
+        long run = 0;
+        for (;;) {
+            uint64_t best = 0ull;
+    #pragma unroll
+            for (int i = 0; i < kPfRounds; ++i) best = kk[i] > best ? kk[i] : best;
+            const uint32_t bh = (uint32_t)(best >> 32);
+            const uint32_t mh = wave_max_u32(bh);
+            if (mh == 0u) break;  // no candidate left
+            const uint32_t ml = wave_max_u32(bh == mh ? (uint32_t)best : 0u);
+            const int c = (int)(0xffffffffu - ml);
+            const int sz = size_l[c];
+            if (count > 0 && (count >= a.k_max || run + sz > a.budget)) break;
+            run += sz;
+            ++count;
+    #pragma unroll
+            for (int i = 0; i < kPfRounds; ++i)
+                if (cl + per * i == c) {
+                    kk[i] = 0ull;
+                    mine |= 1u << i;
+                }
+        }
+
+        // the list in block order, the slot table, the unused slots
+        int32_t* sel = a.sel + ((long)bk * a.Q + r) * a.k_max;
+        int16_t* slots = a.slots + (long)bk * C * kGroupMaxRows + r;
+        int base = 0;
+    #pragma unroll
+        for (int i = 0; i < kPfRounds; ++i) {
+            if (i < R) {
+                const int c = cl + per * i;
+                const bool t = ((mine >> i) & 1u) != 0u && part == 0;
+                const uint64_t bal = __builtin_amdgcn_ballot_w64(t);  // part-0 lanes are 0 .. per-1, blocks ascending
+                const int j = base + lanes_below(bal);
+                if (part == 0 && c < C) {
+                    if (t) {
+                        sel[j] = c;
+                        atomicAdd(&nch[c], 1);
+                    }
+                    slots[(long)c * kGroupMaxRows] = t ? (int16_t)j : (int16_t)-1;
+                }
+                base += __builtin_popcountll(bal);
             }
-            base += __builtin_popcountll(bal);
+        }
+        for (int j = count + lane; j < a.k_max; j += 64) sel[j] = -1;
+        if (lane == 0) a.count[(long)bk * a.Q + r] = count;
+        const int nempty = (a.k_max - count) * a.tsplit * G;
+        for (int e = lane; e < nempty; e += 64) {
+            const int h = e % G, rest = e / G, s = rest % a.tsplit, j = count + rest / a.tsplit;
+            const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + r;
+            const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
+            *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
         }
     }
-    for (int j = count + lane; j < a.k_max; j += 64) sel[j] = -1;
-    if (lane == 0) a.count[(long)bk * a.Q + r] = count;
-    const int nempty = (a.k_max - count) * a.tsplit * G;
-    for (int e = lane; e < nempty; e += 64) {
-        const int h = e % G, rest = e / G, s = rest % a.tsplit, j = count + rest / a.tsplit;
-        const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + r;
-        const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
-        *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
+
+    // rows of this group of 8 that chose each block (the decode's passes);
+    // the first group also zeroes the entries past the last group
+    __syncthreads();
+    for (int c = tid; c < C; c += kPfThreads) {
+        unsigned char* rc = a.rows + ((long)bk * C + c) * 16;
+        rc[grp] = (unsigned char)nch[c];
+        if (grp == 0)
+            for (int q8 = ngr; q8 < 16; ++q8) rc[q8] = 0;
     }
 }
 

@@ -98,6 +98,27 @@ int occupancy(int hd, int G, int dtype)
     return v;
 }
 
+// workgroups of the persistent grouped decode on the current device (CUs
+// times resident workgroups per CU), queried once per device and shape
+int group_grid(int hd, int G)
+{
+    constexpr int kDevices = 64;
+    static std::atomic<int> cache[kDevices][2][5];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if ((hd != 64 && hd != 128) || !pow2_group(G)) return 8;
+    int gi = 0;
+    while ((1 << gi) < G) ++gi;
+    if (dev < 0 || dev >= kDevices) return sa::group_workgroups(hd, G);
+    std::atomic<int>& c = cache[dev][hd == 128][gi];
+    int v = c.load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = sa::group_workgroups(hd, G);
+        c.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 // fewest splits that leave every workgroup of the select-and-decode kernel
 // at most kRowsWG row-table entries: a share of the sink + window rounded up
 // to a multiple of 16 (up to 16 more than toks / s) plus a share of the
@@ -168,7 +189,7 @@ bool keydiff_fits(const sa_kv_desc* kv, int32_t sink_len, int32_t budget)
 // workspace of the grouped decode: byte offsets of its three arrays, each
 // 256-byte aligned
 struct GroupedWs {
-    size_t nunion, upages, slots, total;
+    size_t nunion, ctr, upages, slots, total;
 };
 // npg: candidate units per (sequence, KV head) (pages, or an index's blocks)
 GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
@@ -177,16 +198,19 @@ GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
     const size_t bh = (size_t)kv->batch * kv->num_kv_heads, mp = (size_t)npg;
     GroupedWs w;
     w.nunion = 0;
-    w.upages = up(w.nunion + bh * sizeof(int32_t));
+    w.ctr = up(w.nunion + bh * sizeof(int32_t));
+    w.upages = up(w.ctr + bh * sizeof(int32_t));
     w.slots = up(w.upages + bh * mp * sizeof(sa::GroupPage));
     w.total = up(w.slots + bh * mp * sa::kGroupMaxRows * sizeof(int16_t));
     return w;
 }
 
 // The prefill front's workspace: the slot table [B][Hkv][C][kGroupMaxRows]
-// (int16), then the blocks' decode order [B][Hkv][C], 256-byte aligned.
+// (int16), the rows of each row group of 8 that chose each block
+// [B][Hkv][C][16] (uint8), the decode's item counters [B][Hkv], each
+// 256-byte aligned.
 struct PrefillWs {
-    size_t slots, order, total;
+    size_t slots, rows, ctr, total;
 };
 PrefillWs prefill_ws(const sa_kv_desc* kv, long C)
 {
@@ -194,8 +218,9 @@ PrefillWs prefill_ws(const sa_kv_desc* kv, long C)
     const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
     PrefillWs w;
     w.slots = 0;
-    w.order = up(bh * (size_t)C * sa::kGroupMaxRows * sizeof(int16_t));
-    w.total = up(w.order + bh * (size_t)C * sizeof(int32_t));
+    w.rows = up(bh * (size_t)C * sa::kGroupMaxRows * sizeof(int16_t));
+    w.ctr = up(w.rows + bh * (size_t)C * 16);
+    w.total = up(w.ctr + bh * sizeof(int32_t));
     return w;
 }
 
@@ -472,9 +497,6 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
     if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
     if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits, kDecodeThreads))
         return SA_ERR_UNSUPPORTED;
-    const long max_union = std::min<long>(npg, (long)num_q_rows * k_max);
-    if (!grid_fits(max_union * token_splits * kv->batch * kv->num_kv_heads, kDecodeThreads))
-        return SA_ERR_UNSUPPORTED;
     const GroupedWs w = grouped_ws(kv, npg);
     if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
         return SA_ERR_INVALID_ARG;
@@ -488,7 +510,8 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
                         (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots),
                         npg,        blk_off,    blk_k,      blk_v,   blk_n,
                         blk_end};
-        const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
+        a.ctr = (int32_t*)(base + w.ctr);
+        const int r1 = finish(sa::launch_group(a, group_grid(kv->head_dim, g.G), stream), stream);
         if (r1 != SA_OK) return r1;
     }
     const long off = (long)k_max * token_splits;
@@ -682,19 +705,19 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
     const long nwin = prefill_window_units(window_len, kv->page_size);
     const long nbk = (long)kv->batch * kv->num_kv_heads, C = index->num_blocks;
     const long rows = (long)kv->batch * kv->num_q_heads * num_q_rows;
-    if (!grid_fits(nbk * ((num_q_rows + 7) / 8), kDecodeThreads) ||
-        !grid_fits((nwin + C) * token_splits * nbk, kDecodeThreads) || !grid_fits(rows, 64))
-        return SA_ERR_UNSUPPORTED;
+    if (nwin + C > sa::kGroupMaxPages) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits(nbk * ((num_q_rows + 7) / 8), kDecodeThreads) || !grid_fits(rows, 64)) return SA_ERR_UNSUPPORTED;
     const PrefillWs w = prefill_ws(kv, C);
     if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0) return SA_ERR_INVALID_ARG;
     char* base = (char*)workspace;
     int16_t* slots = (int16_t*)(base + w.slots);
-    int32_t* order = (int32_t*)(base + w.order);
+    unsigned char* chosen_rows = (unsigned char*)(base + w.rows);
+    int32_t* ctr = (int32_t*)(base + w.ctr);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
 
     sa::PrefillArgs f{g,          q,      num_q_rows,  index->num_tokens, (int)C, index->offsets, index->positions,
                       index->centres, token_budget, k_max, window_len, token_splits, stride, visible_end,
-                      sel_blocks, sel_count, slots,  order,       part_ml};
+                      sel_blocks, sel_count, slots,  part_ml,     chosen_rows, ctr};
     const int r1 = finish(sa::launch_prefill_choose(f, stream), stream);
     if (r1 != SA_OK) return r1;
     sa::GroupArgs d{};
@@ -716,9 +739,10 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
     d.blk_v = index->v_blocks;
     d.blk_n = index->num_tokens;
     d.blk_end = visible_end;
-    d.pf_order = order;
     d.nwin = (int)nwin;
-    const int r2 = finish(sa::launch_group_prefill(d, stream), stream);
+    d.pf_rows = chosen_rows;
+    d.ctr = ctr;
+    const int r2 = finish(sa::launch_group_prefill(d, group_grid(kv->head_dim, g.G), stream), stream);
     if (r2 != SA_OK) return r2;
     sa::CombineArgs m{(int)rows, kv->head_dim, stride, out_dtype, part_o, part_ml, out, lse,
                       advance > 0 ? (int32_t*)kv->seq_lens : nullptr, kv->batch, advance};

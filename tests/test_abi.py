@@ -187,8 +187,8 @@ def test_decode_grouped_checks():
     lib = B.library()
     d = _desc()
     ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
-    # counts, page records (16 bytes), slots; each region 256-byte aligned
-    assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 128 * 2 + 255) // 256) * 256
+    # counts, item counters, page records (16 bytes), slots; each region 256-byte aligned
+    assert ws == 256 + 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 128 * 2 + 255) // 256) * 256
     assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
 
     def grouped(**kw):
@@ -351,7 +351,7 @@ def test_block_index_checks():
     assert select(kmax=5) == B.SA_ERR_INVALID_ARG  # more than the index's blocks
 
     wsd = lib.sparse_attn_blocks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
-    assert wsd == 256 + up(nbk * C * 16) + up(nbk * C * 128 * 2)
+    assert wsd == 256 + 256 + up(nbk * C * 16) + up(nbk * C * 128 * 2)
 
     def decode(**kw):
         a = dict(q=DEV, rows=2, sel=DEV, cnt=DEV, kmax=2, W=4, scale=0.0, ts=1, ls=1, po=DEV, pml=DEV, ws=DEV, wsb=wsd)
@@ -377,7 +377,8 @@ def test_prefill_chunk_checks():
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     nbk, C = 4, 4
     wsp = lib.sparse_attn_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
-    assert wsp == up(nbk * C * 128 * 2) + up(nbk * C * 4)  # slot table, block order
+    # slot table, rows of each group of 8 per block, item counters
+    assert wsp == up(nbk * C * 128 * 2) + up(nbk * C * 16) + up(nbk * 4)
     assert lib.sparse_attn_prefill_workspace_bytes(None, ctypes.byref(ix)) == 0
     # slots per row: (k_max + window pages) * token chunks; the window [L - W, L)
     # touches at most (W - 1) // P + 2 pages
@@ -519,11 +520,13 @@ def test_launches_past_the_dispatch_limit_are_refused():
     ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
     assert lib.sparse_attn_decode_step(ctypes.byref(d), DEV, 1, DEV, 0, 16, 16, 32, 0.0, 1024, DEV, DEV, DEV, ws,
                                        DEV, DEV, None) == B.SA_ERR_UNSUPPORTED
-    # grouped: union of min(4096 pages, 128 rows * 8) = 1024 pages x 64 token chunks x 128 (b, kvh) x 512
+    # grouped: the persistent decode's grid is one workgroup per CU; the
+    # per-row decode of the sink and window, 64 * 2 * 128 rows x 1024 local
+    # splits of 512 work-items = 2^33, is refused
     g = _desc(batch=64, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=4096, num_phys_pages=4096,
               max_seq_len=4096 * 16)
     gws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(g))
-    assert lib.sparse_attn_decode_grouped(ctypes.byref(g), DEV, 128, DEV, DEV, 8, 16, 128, 0.0, 64, 1, DEV, DEV,
+    assert lib.sparse_attn_decode_grouped(ctypes.byref(g), DEV, 128, DEV, DEV, 0, 16, 128, 0.0, 1, 1024, DEV, DEV,
                                           DEV, gws, None) == B.SA_ERR_UNSUPPORTED
     # combine: one 64-lane wave per row
     assert lib.sparse_attn_combine(1 << 26, 128, 2, DEV, DEV, DEV, 1, None, None) == B.SA_ERR_UNSUPPORTED
