@@ -253,6 +253,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     // u of (sequence, KV head) bk.  Units: the plan's records in order, or
     // in prefill mode the window's pages (u < nwin) and then the index's
     // blocks (block u - nwin).
+    int next_item = -1;  // thread 0: the next item's index, when the item fetched it
     auto process = [&](const int bk, const int u, const int s, const int pidx, const int np, const int nch) {
         const int b = bk / g.Hkv, kvh = bk - b * g.Hkv;
         const Regions rg(g, b, a.S, a.W);
@@ -281,6 +282,54 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         const int t0 = a0 + imin(n, s * csz);
         const bool mapped = blocks || phys >= 0;
         const int t1 = mapped ? imin(a1, t0 + csz) : t0;
+
+        const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
+        // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
+        const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
+                          : mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1)
+                                   : 0;
+        const uint16_t* kp = (const uint16_t*)(blocks ? a.blk_k : g.k) + row0 * HD;
+        const uint16_t* vp = (const uint16_t*)(blocks ? a.blk_v : g.v) + row0 * HD;
+        const int ntok = t1 - t0;
+
+        // stage st: this thread's 16-byte chunks of the K and V rows of
+        // tokens t0 + 64 st .. ; chunks past the chunk's end re-read its
+        // first row and are masked (values written as zeros)
+        struct Staged {
+            uint4 k[LPS], v[LPS];
+        };
+        auto fetch = [&](int st, Staged& x) {
+            static_for<0, LPS>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int e = u * 64 * kGW + threadIdx.x;  // chunk of the stage
+                const int tt = st * kStage + e / CPT;
+                const long off = (tt < ntok ? (long)tt * HD : 0) + (e % CPT) * 8;
+                x.k[u] = *(const uint4*)(kp + off);
+                x.v[u] = *(const uint4*)(vp + off);
+            });
+        };
+        auto stash = [&](int st, int buf, const Staged& x) {
+            static_for<0, LPS>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int e = u * 64 * kGW + threadIdx.x;
+                const int tl = e / CPT, part = e % CPT;
+                const bool ok = st * kStage + tl < ntok;
+                const uint4 kw = x.k[u];
+                *(uint4*)(kl(buf) + tl * KROW + part * 16) = make_uint4(kw.x, kw.y, kw.z, kw.w);
+                const uint4 w = x.v[u];
+                *(uint4*)(vl(buf) + (tl >> 4) * VTILE + gvt_off<VROW>(tl & 15, part * 16)) =
+                    make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
+            });
+        };
+        // The first pass's three stages are issued now, with the rows' slots
+        // in flight: their addresses need only the unit's token range.
+        Staged X0, X1, X2;
+        fetch(0, X0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in stage order
+        fetch(1, X1);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(2, X2);
+        __builtin_amdgcn_sched_barrier(0);
 
         if (win) {
             // The rows at or after the chunk's first token attend it (list index
@@ -338,14 +387,6 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             }
         }
 
-        const int nst = (imax(0, t1 - t0) + kStage - 1) / kStage;
-        // K/V row of token t0 (inside the page or the sequence's rows even when the chunk is empty)
-        const long row0 = blocks   ? (long)bk * a.blk_n + imin(t0, a.blk_n - 1)
-                          : mapped ? ((long)phys * g.Hkv + kvh) * g.P + imin(t0 - p * g.P, g.P - 1)
-                                   : 0;
-        const uint16_t* kp = (const uint16_t*)(blocks ? a.blk_k : g.k) + row0 * HD;
-        const uint16_t* vp = (const uint16_t*)(blocks ? a.blk_v : g.v) + row0 * HD;
-        const int ntok = t1 - t0;
 
         const float sl2 = a.scale_log2, slack = kGSlack / sl2;
         const int ncol = nr * G, ncb = (ncol + 15) / 16;
@@ -387,35 +428,6 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 for (int m = 0; m < NB; ++m) o[m] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
             }
 
-            // stage st: this thread's 16-byte chunks of the K and V rows of
-            // tokens t0 + 64 st .. ; chunks past the chunk's end re-read its
-            // first row and are masked (values written as zeros)
-            struct Staged {
-                uint4 k[LPS], v[LPS];
-            };
-            auto fetch = [&](int st, Staged& x) {
-                static_for<0, LPS>([&](auto U) {
-                    constexpr int u = decltype(U)::value;
-                    const int e = u * 64 * kGW + threadIdx.x;  // chunk of the stage
-                    const int tt = st * kStage + e / CPT;
-                    const long off = (tt < ntok ? (long)tt * HD : 0) + (e % CPT) * 8;
-                    x.k[u] = *(const uint4*)(kp + off);
-                    x.v[u] = *(const uint4*)(vp + off);
-                });
-            };
-            auto stash = [&](int st, int buf, const Staged& x) {
-                static_for<0, LPS>([&](auto U) {
-                    constexpr int u = decltype(U)::value;
-                    const int e = u * 64 * kGW + threadIdx.x;
-                    const int tl = e / CPT, part = e % CPT;
-                    const bool ok = st * kStage + tl < ntok;
-                    const uint4 kw = x.k[u];
-                    *(uint4*)(kl(buf) + tl * KROW + part * 16) = make_uint4(kw.x, kw.y, kw.z, kw.w);
-                    const uint4 w = x.v[u];
-                    *(uint4*)(vl(buf) + (tl >> 4) * VTILE + gvt_off<VROW>(tl & 15, part * 16)) =
-                        make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
-                });
-            };
             // this wave's subtiles of stage st: gi, gi + gsz, ...
             auto compute = [&](int st, int buf) {
                 if (!computes) return;
@@ -478,29 +490,34 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             // issues its loads and the loop's only exit is at the end of a round
             // of three, so the waits count one stage each; stages past the end
             // re-read the chunk's first row and compute nothing.
-            Staged X0, X1, X2;
-            fetch(0, X0);
-            __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in stage order
-            fetch(1, X1);
-            __builtin_amdgcn_sched_barrier(0);
-            fetch(2, X2);
-            __builtin_amdgcn_sched_barrier(0);
+            if (pass != pidx) {  // the first pass's stages were issued with the unit
+                fetch(0, X0);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(1, X1);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(2, X2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             for (int st = 0; st < nst; st += 3) {
                 stash(st, 0, X0);
                 __syncthreads();
                 fetch(st + 3, X0);
                 compute(st, 0);
+                if (st + 1 >= nst) break;  // the last stage (the buffers are read no more)
                 stash(st + 1, 1, X1);
                 __syncthreads();
                 fetch(st + 4, X1);
                 compute(st + 1, 1);
                 __syncthreads();  // stage st is no longer read from buffer 0
+                if (st + 2 >= nst) break;
                 stash(st + 2, 0, X2);
                 __syncthreads();
                 fetch(st + 5, X2);
                 compute(st + 2, 0);
                 __syncthreads();  // buffers 0 and 1 are free for the next round
             }
+            // the next item's index, taken while this one merges
+            if (threadIdx.x == 0 && (pass + np) * kGW >= ncb) next_item = atomicAdd(a.ctr + bk, 1);
 
             // Merge the states of a block's waves (group order) through LDS,
             // then the first wave of each block writes its partials.  Lane (r, j)
@@ -627,6 +644,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         // workgroup of the (sequence, KV head)
         if (!prefill) {
             for (int k = tid; k < nu; k += 64 * kGW) u_ord[k] = (unsigned short)k;
+            __syncthreads();  // other threads read these entries below
         } else {
             for (int i = tid; i < 256; i += 64 * kGW) hist[i] = 0;
             __syncthreads();
@@ -691,10 +709,12 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         }
         __syncthreads();
 
+        next_item = -1;
         for (;;) {
-            if (tid == 0) s_item = atomicAdd(a.ctr + bk, 1);
+            if (tid == 0) s_item = next_item >= 0 ? next_item : atomicAdd(a.ctr + bk, 1);
             __syncthreads();
             const int it = s_item;
+            next_item = -1;
             __syncthreads();  // s_item is read before the next item's fetch
             if (it >= total) break;
             // the unit: the last in launch order with item_pre <= it (units
