@@ -97,7 +97,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     // candidates: the pages with middle-region tokens, or every block
     const int lo = a.blk_off ? 0 : rg.plo, hi = a.blk_off ? npg - 1 : rg.phi;
     for (int p = tid; p < 2 * npg; p += kPlanThreads) mask[p] = 0ull;
-    if (tid == 0) a.ctr[bk] = 0;  // the grouped decode's item counter
     __syncthreads();
 
     const int32_t* sel = a.sel + (long)bk * a.Q * a.k_max;
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     }
 }
 
-template <int HD, int G>
+template <int HD, int G, bool PF>
 __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
 {
     constexpr int KK = HD / 32;          // q.k products per 16-token subtile (32 channels each)
@@ -235,45 +234,35 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int nbk = g.B * g.Hkv;
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
-    const bool prefill = a.pf_rows != nullptr;
-
-    // The units of the (sequence, KV head) being served: token range [a0, a1)
-    // (rows of the block layout for blocks, positions for pages), physical
-    // page, passes and token chunks, their launch order and the prefix of
-    // their items in that order (filled per (sequence, KV head) below).
-    __shared__ int u_a0[kGroupMaxPages], u_a1[kGroupMaxPages], u_x[kGroupMaxPages];
-    __shared__ int item_pre[kGroupMaxPages + 1];
-    __shared__ unsigned short u_ord[kGroupMaxPages];
-    __shared__ unsigned char u_np[kGroupMaxPages], u_nch[kGroupMaxPages], u_bkt[kGroupMaxPages];
-    __shared__ int hist[256];
-    __shared__ int wsum[kGW];
-    __shared__ int s_item;
+    constexpr bool prefill = PF;  // prefill mode (persistent), else plan mode
 
     // One item: passes pidx, pidx + np, ... of token chunk s (of nch) of unit
     // u of (sequence, KV head) bk.  Units: the plan's records in order, or
     // in prefill mode the window's pages (u < nwin) and then the index's
     // blocks (block u - nwin).
     int next_item = -1;  // thread 0: the next item's index, when the item fetched it
-    auto process = [&](const int bk, const int u, const int s, const int pidx, const int np, const int nch) {
-        const int b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-        const Regions rg(g, b, a.S, a.W);
-        const bool win = prefill && u < a.nwin;  // a page of the rows' window (prefill)
-        const bool blocks = a.blk_off != nullptr && !win;
-        const int a0 = u_a0[u], a1 = u_a1[u];
-        const int phys = blocks ? 0 : u_x[u];
-        const int p = blocks ? 0 : a0 / g.P;  // the page of a page unit
-
-        // each lane's two rows' list index of the unit (-1: the row does not attend it)
-        int16_t slot0 = -1, slot1 = -1;
+    // each lane's two rows' list index of unit u (-1: the row does not attend it)
+    auto load_slots = [&](const int bk, const int u, int16_t& slot0, int16_t& slot1) {
+        slot0 = -1;
+        slot1 = -1;
         if (!prefill) {
             const long ui = (long)bk * a.npg + u;
             slot0 = a.slots[ui * kGroupMaxRows + lane];
             slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
-        } else if (!win) {
+        } else if (u >= a.nwin) {
             const long ui = (long)bk * a.npg + (u - a.nwin);
             if (lane < a.Q) slot0 = a.slots[ui * kGroupMaxRows + lane];
             if (64 + lane < a.Q) slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
         }
+    };
+    auto process = [&](const int bk, const int u, const int s, const int pidx, const int np, const int nch,
+                       const int a0, const int a1, const int x, int16_t slot0, int16_t slot1) {
+        const int b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+        const Regions rg(g, b, a.S, a.W);
+        const bool win = prefill && u < a.nwin;  // a page of the rows' window (prefill)
+        const bool blocks = a.blk_off != nullptr && !win;
+        const int phys = blocks ? 0 : x;
+        const int p = blocks ? 0 : a0 / g.P;  // the page of a page unit
 
         // this chunk of the unit's tokens: contiguous rows of one physical
         // page (an unmapped page attends nothing), or of the block layout
@@ -503,13 +492,15 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 __syncthreads();
                 fetch(st + 3, X0);
                 compute(st, 0);
-                if (st + 1 >= nst) break;  // the last stage (the buffers are read no more)
+                // prefill (many short chunks): stop at the last stage.  (In plan mode the
+                // exits cost the loop's overlap of loads more than the stages they skip.)
+                if (PF && st + 1 >= nst) break;
                 stash(st + 1, 1, X1);
                 __syncthreads();
                 fetch(st + 4, X1);
                 compute(st + 1, 1);
                 __syncthreads();  // stage st is no longer read from buffer 0
-                if (st + 2 >= nst) break;
+                if (PF && st + 2 >= nst) break;
                 stash(st + 2, 0, X2);
                 __syncthreads();
                 fetch(st + 5, X2);
@@ -517,7 +508,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 __syncthreads();  // buffers 0 and 1 are free for the next round
             }
             // the next item's index, taken while this one merges
-            if (threadIdx.x == 0 && (pass + np) * kGW >= ncb) next_item = atomicAdd(a.ctr + bk, 1);
+            if (prefill && threadIdx.x == 0 && (pass + np) * kGW >= ncb) next_item = atomicAdd(a.ctr + bk, 1);
 
             // Merge the states of a block's waves (group order) through LDS,
             // then the first wave of each block writes its partials.  Lane (r, j)
@@ -573,6 +564,50 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         }
     };
 
+    // A unit's token range, physical page and passes from the plan's record.
+    auto plan_unit = [&](const GroupPage& e, const Regions& rg, int& x0, int& x1, int& x) {
+        if (a.blk_off) {  // blocks: the plan records the row range
+            x0 = e.phys;
+            x1 = e.pad;
+            x = 0;
+        } else {
+            x0 = imax(e.page * g.P, rg.se);
+            x1 = imin((e.page + 1) * g.P, rg.ws);
+            x = e.phys;
+        }
+    };
+    auto unit_chunks = [&](int ntk) { return imin(a.tsplit, imax(1, (ntk + kGroupChunkMin - 1) / kGroupChunkMin)); };
+
+    if constexpr (!PF) {
+        // Plan mode: one workgroup per (unit of the union, token chunk); id =
+        // (rank * B * Hkv + bk) * tsplit + chunk, the costliest units of every
+        // (sequence, KV head) first.  Nearly every unit of the bound is in the
+        // union here, so a grid sized to it launches few idle workgroups.
+        const int chunk = blockIdx.x % a.tsplit, rest = blockIdx.x / a.tsplit;
+        const int bk = rest % nbk, rank = rest / nbk;
+        const GroupPage e = a.upages[(long)bk * a.npg + rank];  // rank < npg: the record exists
+        int16_t slot0, slot1;
+        load_slots(bk, rank, slot0, slot1);  // with the record, not after it
+        if (rank >= a.nunion[bk]) return;
+        const Regions rg(g, bk / g.Hkv, a.S, a.W);
+        int x0, x1, x;
+        plan_unit(e, rg, x0, x1, x);
+        const int nch = unit_chunks(imax(0, x1 - x0));
+        if (chunk >= nch) return;  // the first chunk's workgroup empties this chunk's slots
+        process(bk, rank, chunk, 0, 1, nch, x0, x1, x, slot0, slot1);
+    } else {
+    // The units of the (sequence, KV head) being served: token range [a0, a1)
+    // (rows of the block layout for blocks, positions for pages), physical
+    // page, passes and token chunks, their launch order and the prefix of
+    // their items in that order (filled per (sequence, KV head) below).
+    __shared__ int u_a0[kGroupMaxPages], u_a1[kGroupMaxPages], u_x[kGroupMaxPages];
+    __shared__ int item_pre[kGroupMaxPages + 1];
+    __shared__ unsigned short u_ord[kGroupMaxPages];
+    __shared__ unsigned char u_np[kGroupMaxPages], u_nch[kGroupMaxPages], u_bkt[kGroupMaxPages];
+    __shared__ int hist[256];
+    __shared__ int wsum[kGW];
+    __shared__ int s_item;
+
     // Persistent schedule: one workgroup per CU, in columns of 8 (one per
     // XCD); column col serves (sequence, KV head)s col, col + ncol, ... (or
     // col mod B*Hkv when there are fewer of them than columns).  The
@@ -589,22 +624,11 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         const int b = bk / g.Hkv;
         const Regions rg(g, b, a.S, a.W);
         // the units, loads in one round
-        const int nu = prefill ? a.nwin + a.npg : imin(imax(a.nunion[bk], 0), a.npg);
+        const int nu = a.nwin + a.npg;
         const int wstart = imax(0, rg.L - a.W);
         for (int u = tid; u < nu; u += 64 * kGW) {
             int x0, x1, x = 0, nrows;
-            if (!prefill) {
-                const GroupPage e = a.upages[(long)bk * a.npg + u];
-                nrows = e.nrows;
-                if (a.blk_off) {  // blocks: the plan records the row range
-                    x0 = e.phys;
-                    x1 = e.pad;
-                } else {
-                    x0 = imax(e.page * g.P, rg.se);
-                    x1 = imin((e.page + 1) * g.P, rg.ws);
-                    x = e.phys;
-                }
-            } else if (u < a.nwin) {
+            if (u < a.nwin) {
                 const int pg = wstart / g.P + u;
                 x0 = imax(pg * g.P, wstart);
                 x1 = imin((pg + 1) * g.P, rg.L);
@@ -625,7 +649,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             }
             const int ntk = imax(0, x1 - x0);
             const int npass = nrows > 0 ? (nrows * G + kGroupPassCols - 1) / kGroupPassCols : 0;
-            const int nch = imin(a.tsplit, imax(1, (ntk + kGroupChunkMin - 1) / kGroupChunkMin));
+            const int nch = unit_chunks(ntk);
             u_a0[u] = x0;
             u_a1[u] = x1;
             u_x[u] = x;
@@ -639,13 +663,9 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         }
         __syncthreads();
 
-        // launch order: the plan's (already costliest first), or a stable
-        // counting sort of the units by cost bucket, the same in every
-        // workgroup of the (sequence, KV head)
-        if (!prefill) {
-            for (int k = tid; k < nu; k += 64 * kGW) u_ord[k] = (unsigned short)k;
-            __syncthreads();  // other threads read these entries below
-        } else {
+        // launch order: a stable counting sort of the units by cost bucket,
+        // the same in every workgroup of the (sequence, KV head)
+        {
             for (int i = tid; i < 256; i += 64 * kGW) hist[i] = 0;
             __syncthreads();
             for (int u = tid; u < nu; u += 64 * kGW) atomicAdd(&hist[u_bkt[u]], 1);
@@ -729,22 +749,25 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             }
             const int u = u_ord[lo];
             const int np = u_np[u], nch = u_nch[u], kk = it - item_pre[lo];
-            process(bk, u, kk / np, kk % np, np, nch);
+            int16_t slot0, slot1;
+            load_slots(bk, u, slot0, slot1);
+            process(bk, u, kk / np, kk % np, np, nch, u_a0[u], u_a1[u], u_x[u], slot0, slot1);
             __syncthreads();  // LDS of this item is no longer read
         }
     }
+    }
 }
 
-template <int HD>
+template <int HD, bool PF>
 hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 block(64 * kGW);
     switch (a.g.G) {
-    case 1: hipLaunchKernelGGL((k_group_decode_mfma<HD, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_group_decode_mfma<HD, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_group_decode_mfma<HD, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_group_decode_mfma<HD, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_group_decode_mfma<HD, 16>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_group_decode_mfma<HD, 1, PF>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_group_decode_mfma<HD, 2, PF>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_group_decode_mfma<HD, 4, PF>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_group_decode_mfma<HD, 8, PF>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_group_decode_mfma<HD, 16, PF>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -752,18 +775,17 @@ hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_group(const GroupArgs& a, int workgroups, hipStream_t s)
+hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || !a.ctr || workgroups < 8 || workgroups % 8)
-        return hipErrorInvalidValue;
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || a.pf_rows) return hipErrorInvalidValue;
     const size_t lds = (2 * sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)workgroups);
-    if (g.hd == 128) return launch_group_g<128>(a, grid, s);
-    if (g.hd == 64) return launch_group_g<64>(a, grid, s);
+    if (e != hipSuccess || max_union < 1) return e;
+    const dim3 grid((unsigned)((long)max_union * a.tsplit * g.B * g.Hkv));
+    if (g.hd == 128) return launch_group_g<128, false>(a, grid, s);
+    if (g.hd == 64) return launch_group_g<64, false>(a, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -774,8 +796,8 @@ hipError_t launch_group_prefill(const GroupArgs& a, int workgroups, hipStream_t 
         !a.blk_end || a.nwin < 1 || !a.ctr || workgroups < 8 || workgroups % 8)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)workgroups);
-    if (g.hd == 128) return launch_group_g<128>(a, grid, s);
-    if (g.hd == 64) return launch_group_g<64>(a, grid, s);
+    if (g.hd == 128) return launch_group_g<128, true>(a, grid, s);
+    if (g.hd == 64) return launch_group_g<64, true>(a, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -787,11 +809,11 @@ int resident_g(int G)
     int n = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (G) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 1>, bs, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 2>, bs, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 4>, bs, 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 8>, bs, 0); break;
-    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 16>, bs, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 1, true>, bs, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 2, true>, bs, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 4, true>, bs, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 8, true>, bs, 0); break;
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_group_decode_mfma<HD, 16, true>, bs, 0); break;
     default: break;
     }
     return e == hipSuccess && n > 0 ? n : 1;
