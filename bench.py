@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--middle-splits", type=int, default=0, help="splits of the selected-pages decode")
     ap.add_argument("--separate", action="store_true",
                     help="select, decode and combine as three launches instead of the fused select-and-decode step")
+    ap.add_argument("--merge", action="store_true",
+                    help="llama3-70b-layer-128k / hybrid-3layer-256k: the decode kernel merges its partials in its "
+                         "own last workgroups (sparse_attn_decode_step_merged, sparse_attn_decode_merged) instead of "
+                         "the separate combine kernel")
     ap.add_argument("--overlap", action="store_true",
                     help="decode sink + window on a second stream beside the selection, then the selected pages")
     ap.add_argument("--dense-steps", type=int, default=10)
@@ -831,6 +835,8 @@ def bench_hybrid(args):
     torch.cuda.synchronize()
     P = layers[0][0].P
 
+    merge = args.merge  # the decode kernels merge their partials (no combine launch)
+
     def reset():
         seq_lens.fill_(L0)
         for dc, dec, W, qs in layers:
@@ -844,14 +850,21 @@ def bench_hybrid(args):
         t_ref = t - t % RF
         L = L0 + t
         for li, (dc, dec, W, qs) in enumerate(layers):
+            adv = 1 if li == len(layers) - 1 else 0
             if t == t_ref:
                 if t > 0:
                     first = (L0 + t_ref - RF - 1) // P  # the page that held the last token at the previous selection
                     dec.build_meta(first, (L - 1) // P + 1)
-                dec.select_decode(qs[t])
+                if merge:
+                    dec.select_decode_merged(qs[t], advance=adv)
+                else:
+                    dec.select_decode(qs[t])
+            elif merge:
+                dec.decode_merged(qs[t], window=W + (t - t_ref), advance=adv)
             else:
                 dec.decode(qs[t], window=W + (t - t_ref))
-            dec.combine(advance=1 if li == len(layers) - 1 else 0)
+            if not merge:
+                dec.combine(advance=adv)
 
     # one graph per refresh cycle: its selecting step and the decode steps until the next
     graphs = None
@@ -898,7 +911,10 @@ def bench_hybrid(args):
     K = 50
     start.record()
     for _ in range(K):
-        dec0.decode(qs0[1], window=W0 + 1)
+        if merge:
+            dec0.decode_merged(qs0[1], window=W0 + 1)
+        else:
+            dec0.decode(qs0[1], window=W0 + 1)
     stop.record()
     torch.cuda.synchronize()
     dec_ms = start.elapsed_time(stop) / K
@@ -907,6 +923,8 @@ def bench_hybrid(args):
                for b in range(dc0.B) for h in range(dc0.Hkv))
     dec_bytes = accounting.decode_kernel_bytes(B=dc0.B, Hq=dc0.Hq, Hkv=dc0.Hkv, hd=dc0.hd, elem_bytes=2,
                                                ntok_total=ntok, splits=dec0.splits, sel_entries=int(cnt0.sum()))
+    if merge:  # the merge in the last workgroups: the partials read back, out and lse written
+        dec_bytes += dec0.rows * (dec0.splits * (dc0.hd + 2) * 4 + dc0.hd * 2 + 4)
 
     # algorithmic bytes of the schedule
     total = 0
@@ -973,11 +991,13 @@ def bench_hybrid(args):
                        {"window": W, "budget": b_, "splits": s_} for W, b_, s_ in
                        zip(hs.windows, hs.budgets, [dec0.splits] * len(hs.windows))],
                    "refresh": RF, "launch": "eager" if args.eager else "a HIP graph per refresh cycle, captured beforehand",
-                   "step": "summary refresh + (select-and-decode | decode) + combine per layer; the last combine "
-                           "advances the lengths"},
+                   "step": ("summary refresh + (select-and-decode | decode) per layer, each decode kernel merging "
+                            "its partials in its last workgroups; the last layer's advances the lengths") if merge else
+                           ("summary refresh + (select-and-decode | decode) + combine per layer; the last combine "
+                            "advances the lengths")},
         "bytes_per_schedule": total,
-        "roofline": roofline_record("k_decode_mfma (kept pages, first layer, one step after a selection)",
-                                    dec_bytes, dec_ms),
+        "roofline": roofline_record("k_decode_mfma (kept pages, first layer, one step after a selection"
+                                    + (", merging its partials)" if merge else ")"), dec_bytes, dec_ms),
         "cpu_baseline": cpu,
     }))
 
@@ -1061,8 +1081,18 @@ def main():
         B.sparse_attn_combine(dec.rows, c.hd, dec.splits, dec.part_o, dec.part_ml, dec.out, dec.out_dtype,
                               dec.lse)
 
-    mode = "overlap" if args.overlap else "separate" if args.separate else "fused"
-    step = {"overlap": step_overlapped, "separate": step_sequential, "fused": step_fused}[mode]
+    def select_decode_merged(r):
+        B.sparse_attn_decode_step_merged(descs[r], q, 1, metas[r], pr.mode, pr.sink, pr.window, pr.budget, 0.0,
+                                         dec.splits, dec.sel, dec.count, dec.ws, dec.ws_bytes, dec.part_o,
+                                         dec.part_ml, dec.out, dec.out_dtype, dec.lse, 0)
+
+    def step_merged(r, ev=None):
+        select_decode_merged(r)
+
+    mode = ("overlap" if args.overlap else "separate" if args.separate else "fused+merge" if args.merge
+            else "fused")
+    step = {"overlap": step_overlapped, "separate": step_sequential, "fused": step_fused,
+            "fused+merge": step_merged}[mode]
 
     for i in range(args.warmup):
         step(i % R)
@@ -1077,12 +1107,15 @@ def main():
                                       W=pr.window, budget=pr.budget, mode=pr.mode, splits=dec.splits,
                                       attended=attended)
     n_cand = accounting.candidate_pages(L, c.P, pr.sink, pr.window)
-    if mode == "fused":
-        # the launch pair of sparse_attn_decode_step: page scores, then top-k + decode
+    if mode in ("fused", "fused+merge"):
+        # the launch pair of sparse_attn_decode_step: page scores, then top-k + decode (+ the merge of the
+        # partials in the decode kernel's last workgroups: the partials read back, out and lse written)
         dec_kernel = ("k_score_quest_mfma" if pr.mode == B.SA_QUEST else "k_score") + " + k_select_decode_mfma"
         dec_bytes = accounting.select_decode_bytes(B=c.B, Hq=c.Hq, Hkv=c.Hkv, hd=c.hd, elem_bytes=2,
                                                    ntok_total=sum(attended), splits=dec.splits, meta=sb.meta,
                                                    n_cand=n_cand, k_max=dec.k_max)
+        if mode == "fused+merge":
+            dec_bytes += dec.rows * (dec.splits * (c.hd + 2) * 4 + c.hd * 2 + 4)
     elif mode == "separate":
         # one decode launch over sink + window + selected pages
         dec_kernel = "k_decode_mfma"
@@ -1114,6 +1147,9 @@ def main():
     if mode == "fused":
         def launch(r):
             select_decode(r)
+    elif mode == "fused+merge":
+        def launch(r):
+            select_decode_merged(r)
     elif mode == "separate":
         def launch(r):
             B.sparse_attn_decode(descs[r], q, 1, dec.sel, dec.count, dec.k_max, pr.sink, pr.window, B.SA_PART_ALL,

@@ -89,6 +89,11 @@ _SIGS = {
     "sparse_attn_blocks_visible": (ctypes.c_int, [_DESC, _IDX, _I, _P, _P]),
     "sparse_attn_decode_blocks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P,
                                                  _P, ctypes.c_size_t, _P]),
+    "sparse_attn_merge_counters": (ctypes.c_int32, [_DESC, _I]),
+    "sparse_attn_decode_merged": (ctypes.c_int, [_DESC, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
+                                                 _I, _P, _I, _P, _P]),
+    "sparse_attn_decode_step_merged": (ctypes.c_int, [_DESC, _P, _I, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P,
+                                                      _P, ctypes.c_size_t, _P, _P, _P, _I, _P, _I, _P]),
     "sparse_attn_prefill_chunk": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                                                  _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "sparse_attn_prefill_num_splits": (ctypes.c_int32, [_DESC, _I, _I, _I]),
@@ -281,6 +286,30 @@ def sparse_attn_decode_blocks(kv: sa_kv_desc, index: sa_block_index, q, num_q_ro
                                           _ptr(sel_blocks), _ptr(sel_count), k_max, window_len, softmax_scale,
                                           token_splits, local_splits, _ptr(part_o), _ptr(part_ml), _ptr(workspace),
                                           workspace_bytes, _stream(stream)), "sparse_attn_decode_blocks")
+
+
+def sparse_attn_merge_counters(kv: sa_kv_desc, num_q_rows: int) -> int:
+    return int(_lib.sparse_attn_merge_counters(ctypes.byref(kv), num_q_rows))
+
+
+def sparse_attn_decode_merged(kv: sa_kv_desc, q, num_q_rows: int, sel_pages, sel_count, k_max: int, sink_len: int,
+                              window_len: int, softmax_scale: float, num_splits: int, part_o, part_ml, out,
+                              out_dtype: int, lse, advance: int, counters, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_merged(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(sel_pages), _ptr(sel_count),
+                                          k_max, sink_len, window_len, softmax_scale, num_splits, _ptr(part_o),
+                                          _ptr(part_ml), _ptr(out), out_dtype, _ptr(lse), advance, _ptr(counters),
+                                          _stream(stream)), "sparse_attn_decode_merged")
+
+
+def sparse_attn_decode_step_merged(kv: sa_kv_desc, q, num_q_rows: int, meta, score_mode: int, sink_len: int,
+                                   window_len: int, token_budget: int, softmax_scale: float, num_splits: int,
+                                   sel_pages, sel_count, workspace, workspace_bytes: int, part_o, part_ml, out,
+                                   out_dtype: int, lse, advance: int, stream=None) -> None:
+    _check(_lib.sparse_attn_decode_step_merged(ctypes.byref(kv), _ptr(q), num_q_rows, _ptr(meta), score_mode,
+                                               sink_len, window_len, token_budget, softmax_scale, num_splits,
+                                               _ptr(sel_pages), _ptr(sel_count), _ptr(workspace), workspace_bytes,
+                                               _ptr(part_o), _ptr(part_ml), _ptr(out), out_dtype, _ptr(lse), advance,
+                                               _stream(stream)), "sparse_attn_decode_step_merged")
 
 
 def sparse_attn_prefill_num_splits(kv: sa_kv_desc, window_len: int, k_max: int, token_splits: int) -> int:

@@ -21,6 +21,7 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "merge.hpp"
 #include "topk_block.hpp"
 
 namespace sa {
@@ -465,8 +466,9 @@ struct MfmaCore {
     // every wave first leaves its loop); the workgroup merges them with one
     // exponential per (wave, head) and writes the partial of its G heads:
     // part_o / part_ml rows prow0 + h * prow_step, slot `slot`.
+    // coherent: agent-scope stores, for the kernel's own last workgroup to merge
     __device__ __forceinline__ void finish(float* part_o, float* part_ml, long prow0, long prow_step, int stride,
-                                           int slot, bool failed = false)
+                                           int slot, bool failed = false, bool coherent = false)
     {
         // head r's sum over the 4 lanes holding it
         l_run += xor_lanes<16>(l_run);
@@ -510,14 +512,62 @@ struct MfmaCore {
                 ls = inv;
             }
             const long prow = (prow0 + h * prow_step) * stride + slot;
-            *(float4*)(part_o + prow * HD + c4 * 4) = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
-            if (c4 == 0) {
-                part_ml[prow * 2 + 0] = mo;
-                part_ml[prow * 2 + 1] = ls;
+            const float4 ov = make_float4(os.x * inv, os.y * inv, os.z * inv, os.w * inv);
+            float* po = part_o + prow * HD + c4 * 4;
+            if (coherent) {
+                __hip_atomic_store(po + 0, ov.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(po + 1, ov.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(po + 2, ov.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(po + 3, ov.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (c4 == 0) {
+                    __hip_atomic_store(part_ml + prow * 2 + 0, mo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(part_ml + prow * 2 + 1, ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+                *(float4*)po = ov;
+                if (c4 == 0) {
+                    part_ml[prow * 2 + 0] = mo;
+                    part_ml[prow * 2 + 1] = ls;
+                }
             }
         }
     }
 };
+
+// The merge of a (sequence b, KV head, row) problem's split partials by the
+// last of its `splits` workgroups to finish (MergeArgs): every workgroup
+// waits for its own agent-scope partial stores to complete, then counts
+// itself in; the last one merges the problem's G output rows, a wave per
+// row, with agent-scope loads (merge_row, the combine kernel's arithmetic),
+// and clears the counter.  The last problem of a sequence to merge advances
+// its length: by then no workgroup of the launch reads it any more.
+template <int HD, int G, int NW>
+__device__ __forceinline__ void merge_tail(const MergeArgs& m, long prob, int b, int splits, int stride, long prow0,
+                                           long prow_step, const float* part_o, const float* part_ml,
+                                           int probs_per_batch)
+{
+    __shared__ int s_last;
+    __shared__ float wts[NW][kMergeMaxSplits];
+    __shared__ short later[NW][kMergeMaxSplits];
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(m.arrive + prob, 1u) == (unsigned)(splits - 1) ? 1 : 0;
+    __syncthreads();
+    if (!s_last) return;
+    const int wave = threadIdx.x >> 6;
+    for (int h = wave; h < G; h += NW) {
+        const long prow = prow0 + h * prow_step;
+        merge_row<HD, true>(part_ml + prow * stride * 2, part_o + prow * stride * HD, splits, wts[wave], later[wave],
+                            m.out_dtype == 1, m.out, m.lse, prow);
+    }
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(m.arrive + prob, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (m.seq_lens && m.advance != 0 && atomicAdd(m.batch_done + b, 1u) == (unsigned)(probs_per_batch - 1)) {
+            __hip_atomic_store(m.batch_done + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            m.seq_lens[b] += m.advance;
+        }
+    }
+}
 
 // Row index ((phys * Hkv + kvh) * P + offset) of token t, or -1 when t is past
 // the row's position or its page is unmapped.
@@ -602,7 +652,11 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
         core.nrows = cnt;
         core.run(A, B, C, 0);
     }
-    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split);
+    const long prow0 = ((long)b * g.Hq + kvh * G) * a.Q + row;
+    core.finish(a.part_o, a.part_ml, prow0, a.Q, a.split_stride, split, false, a.m.out != nullptr);
+    if (a.m.out)
+        merge_tail<HD, G, NW>(a.m, prob, b, a.splits, a.split_stride, prow0, a.Q, a.part_o, a.part_ml,
+                              g.Hkv * a.Q);
 }
 
 // Selection and decode in one kernel, for the steps that select.  Every
@@ -817,7 +871,11 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     const bool failed = __syncthreads_or(!done) != 0;
     if (failed && threadIdx.x == 0 && a.status) __hip_atomic_store(a.status, kStatusGaveUp, __ATOMIC_RELAXED,
                                                                    __HIP_MEMORY_SCOPE_AGENT);
-    core.finish(a.part_o, a.part_ml, ((long)b * g.Hq + kvh * G) * a.Q + row, a.Q, a.split_stride, split, failed);
+    const long prow0 = ((long)b * g.Hq + kvh * G) * a.Q + row;
+    core.finish(a.part_o, a.part_ml, prow0, a.Q, a.split_stride, split, failed, a.m.out != nullptr);
+    if (a.m.out)
+        merge_tail<HD, G, NW>(a.m, prob, b, a.splits, a.split_stride, prow0, a.Q, a.part_o, a.part_ml,
+                              g.Hkv * a.Q);
 }
 
 template <int HD, int G>

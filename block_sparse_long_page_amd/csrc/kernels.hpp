@@ -61,10 +61,28 @@ struct SelectArgs {
     int kc;                // winners per chunk: min(k_max, kTopkChunk)
     uint32_t* part_keys;   // [B][Hkv][Q][nchunks][kc] order keys of each chunk's winners
     int32_t* part_idx;     // [B][Hkv][Q][nchunks][kc] their candidate indices, ascending
+    uint32_t* counters;    // the merging decode's counters, cleared by the score kernel (or null)
+    int ncounters;
 };
 
 constexpr int kTopkChunk = 8192;   // candidates a chunk of the two-stage selection ranks
 constexpr int kTopkMerge = 12288;  // winners the merge workgroup ranks (nchunks * kc)
+
+// The merge of a decode kernel's split partials in its own last workgroup
+// per (sequence, KV head, row) (out == null: partials only).  The partials
+// go out with agent-scope stores, then each workgroup counts itself in; the
+// last one reads them back with agent-scope loads and merges as the combine
+// kernel does.  The counters return to zero by the end of every launch.
+constexpr int kMergeMaxSplits = 64;  // splits a merging decode supports
+struct MergeArgs {
+    void* out;              // [B * Hq * Q][hd], out_dtype
+    int out_dtype;          // 1: bf16, else fp32
+    float* lse;             // [B * Hq * Q] or null
+    uint32_t* arrive;       // [B][Hkv][Q] workgroups arrived
+    uint32_t* batch_done;   // [B] (sequence, KV head, row)s merged
+    int32_t* seq_lens;      // or null: seq_lens[b] += advance once every problem of b has merged
+    int advance;
+};
 
 struct DecodeArgs {
     Geometry g;
@@ -79,6 +97,7 @@ struct DecodeArgs {
     int split_stride;  // partial slots per row
     float* part_o;
     float* part_ml;
+    MergeArgs m;
 };
 
 struct SelectDecodeArgs {
@@ -95,6 +114,7 @@ struct SelectDecodeArgs {
     int32_t* count;
     uint32_t* status;  // set to kStatusGaveUp by a workgroup whose bounded wait ran out
     int spin_max;      // bound on the wait for the page list (rounds)
+    MergeArgs m;
 };
 
 constexpr uint32_t kStatusGaveUp = 1;  // a share of the attended set was not computed
@@ -143,7 +163,7 @@ struct GroupArgs {
     // slots[b][kvh][block][row] is >= 0 (the slot table is indexed by block)
     int nwin;                      // window units per (sequence, KV head)
     const unsigned char* pf_rows;  // [B][Hkv][npg][16] rows of each row group of 8 that chose each block
-    int32_t* ctr;                  // [B][Hkv] item counters, zero when the decode starts
+    int32_t* ctr;                  // [B][Hkv] prefill: item counters, zero when the decode starts
 };
 
 // Query columns (row, head) of one pass of a grouped-decode workgroup (16 per
@@ -282,9 +302,11 @@ hipError_t launch_select_decode(const SelectDecodeArgs& a, hipStream_t s);
 // resident decode workgroups per CU for this shape (occupancy query)
 int decode_wgs_per_cu(int hd, int G, int dtype);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-// plan kernel, then the grouped decode (persistent: `workgroups`, a multiple of 8)
-hipError_t launch_group(const GroupArgs& a, int workgroups, hipStream_t s);
-// the grouped decode in prefill mode (no plan kernel): (nwin + npg) units per (sequence, KV head)
+// n zeros at p (a kernel, so that a captured graph holds no memset node)
+hipError_t launch_zero_u32(uint32_t* p, long n, hipStream_t s);
+// plan kernel, then the grouped decode over max_union units per (sequence, KV head)
+hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s);
+// the grouped decode in prefill mode (no plan kernel; persistent: `workgroups`, a multiple of 8)
 hipError_t launch_group_prefill(const GroupArgs& a, int workgroups, hipStream_t s);
 // resident grouped-decode workgroups on the device (CUs times occupancy), a multiple of 8
 int group_workgroups(int hd, int G);

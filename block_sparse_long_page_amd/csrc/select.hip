@@ -73,6 +73,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score_f32_mfma(SelectArgs 
     const int r = lane & 15, j = lane >> 4;
 
     if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.status = 0u;
+    if (a.counters && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < a.ncounters; i += blockDim.x) a.counters[i] = 0u;
     int pid = blockIdx.y;
     const int row = pid % a.Q;
     pid /= a.Q;
@@ -232,6 +234,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score_quest_mfma(SelectArg
     const int r = lane & 15, j = lane >> 4;
 
     if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.status = 0u;
+    if (a.counters && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < a.ncounters; i += blockDim.x) a.counters[i] = 0u;
     int pid = blockIdx.y;
     const int row = pid % a.Q;
     pid /= a.Q;

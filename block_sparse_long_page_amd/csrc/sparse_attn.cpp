@@ -189,7 +189,7 @@ bool keydiff_fits(const sa_kv_desc* kv, int32_t sink_len, int32_t budget)
 // workspace of the grouped decode: byte offsets of its three arrays, each
 // 256-byte aligned
 struct GroupedWs {
-    size_t nunion, ctr, upages, slots, total;
+    size_t nunion, upages, slots, total;
 };
 // npg: candidate units per (sequence, KV head) (pages, or an index's blocks)
 GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
@@ -198,8 +198,7 @@ GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
     const size_t bh = (size_t)kv->batch * kv->num_kv_heads, mp = (size_t)npg;
     GroupedWs w;
     w.nunion = 0;
-    w.ctr = up(w.nunion + bh * sizeof(int32_t));
-    w.upages = up(w.ctr + bh * sizeof(int32_t));
+    w.upages = up(w.nunion + bh * sizeof(int32_t));
     w.slots = up(w.upages + bh * mp * sizeof(sa::GroupPage));
     w.total = up(w.slots + bh * mp * sa::kGroupMaxRows * sizeof(int16_t));
     return w;
@@ -267,7 +266,26 @@ bool select_fits(const sa_kv_desc* kv, int32_t k_max)
 // the selecting step's workspace: the scores, then (256-byte aligned) its
 // status word
 size_t status_offset(const sa_kv_desc* kv, int32_t rows) { return (select_ws_bytes(kv, rows) + 255) & ~(size_t)255; }
-size_t step_ws_bytes(const sa_kv_desc* kv, int32_t rows) { return status_offset(kv, rows) + 256; }
+// the merge's counters: one per (sequence, KV head, row), then one per sequence
+long merge_counters(const sa_kv_desc* kv, int32_t rows) { return (long)kv->batch * kv->num_kv_heads * rows + kv->batch; }
+size_t counters_offset(const sa_kv_desc* kv, int32_t rows) { return status_offset(kv, rows) + 256; }
+size_t step_ws_bytes(const sa_kv_desc* kv, int32_t rows)
+{
+    return counters_offset(kv, rows) + (((size_t)merge_counters(kv, rows) * sizeof(uint32_t) + 255) & ~(size_t)255);
+}
+sa::MergeArgs merge_args(const sa_kv_desc* kv, int32_t rows, void* out, int32_t out_dtype, float* lse,
+                         uint32_t* counters, int32_t advance)
+{
+    sa::MergeArgs m{};
+    m.out = out;
+    m.out_dtype = out_dtype == SA_BF16 ? 1 : 0;
+    m.lse = lse;
+    m.arrive = counters;
+    m.batch_done = counters + (long)kv->batch * kv->num_kv_heads * rows;
+    m.seq_lens = advance > 0 ? (int32_t*)kv->seq_lens : nullptr;
+    m.advance = advance;
+    return m;
+}
 
 // The checks of sparse_attn_decode_step's arguments other than its
 // workspace and partials (shared with the variant that keeps them in the
@@ -454,6 +472,88 @@ int sparse_attn_decode_step(const sa_kv_desc* kv, const void* q, int32_t num_q_r
     return st == 0 ? SA_OK : SA_ERR_HIP;
 }
 
+int32_t sparse_attn_merge_counters(const sa_kv_desc* kv, int32_t num_q_rows)
+{
+    if (!kv || kv->batch < 1 || kv->num_kv_heads < 1 || num_q_rows < 1) return -SA_ERR_INVALID_ARG;
+    const long n = merge_counters(kv, num_q_rows);
+    return n > 0x7fffffffl ? -SA_ERR_UNSUPPORTED : (int32_t)n;
+}
+
+int sparse_attn_decode_merged(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                              const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                              float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, void* out,
+                              int32_t out_dtype, float* lse, int32_t advance, uint32_t* counters, hipStream_t stream)
+{
+    sa::Geometry g;
+    const int rc = check_kv(kv, &g);
+    if (rc != SA_OK) return rc;
+    if (!q || !part_o || !part_ml || !out || !counters || num_q_rows < 1 || sink_len < 0 || window_len < 1 ||
+        k_max < 0 || advance < 0)
+        return SA_ERR_INVALID_ARG;
+    if (num_q_rows > kv->max_seq_len) return SA_ERR_INVALID_ARG;
+    if (sel_pages && !sel_count) return SA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > sa::kMergeMaxSplits) return SA_ERR_INVALID_ARG;
+    if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * num_splits, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    sa::DecodeArgs a{g,        q,          num_q_rows,  sel_pages, sel_count, sel_pages ? k_max : 0,
+                     sink_len, window_len, SA_PART_ALL, scale * 1.4426950408889634f,   num_splits,
+                     num_splits, part_o,   part_ml};
+    a.m = merge_args(kv, num_q_rows, out, out_dtype, lse, counters, advance);
+    return finish(sa::launch_decode(a, stream), stream);
+}
+
+int sparse_attn_decode_step_merged(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                                   int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                                   float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                                   void* workspace, size_t workspace_bytes, float* part_o, float* part_ml, void* out,
+                                   int32_t out_dtype, float* lse, int32_t advance, hipStream_t stream)
+{
+    const int rc = check_step(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget, softmax_scale,
+                              num_splits, sel_pages, sel_count);
+    if (rc != SA_OK) return rc;
+    if (!part_o || !part_ml || !out || advance < 0) return SA_ERR_INVALID_ARG;
+    if (num_splits > sa::kMergeMaxSplits) return SA_ERR_INVALID_ARG;
+    if (kv->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (out_dtype != SA_F32 && out_dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < step_ws_bytes(kv, num_q_rows)) return SA_ERR_INVALID_ARG;
+    const int k_max = token_budget / kv->page_size;
+    sa::Geometry g;
+    (void)check_kv(kv, &g);  // validated above: fills g
+    uint32_t* counters = (uint32_t*)((char*)workspace + counters_offset(kv, num_q_rows));
+    const bool fused = k_max > 0 && fused_step_ok(kv, sink_len, window_len, k_max, num_splits, workspace);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
+    if (!fused) {
+        const int r0 = finish(sa::launch_zero_u32(counters, merge_counters(kv, num_q_rows), stream), stream);
+        if (r0 != SA_OK) return r0;
+        const int r1 = sparse_attn_select(kv, q, num_q_rows, meta, score_mode, sink_len, window_len, token_budget,
+                                          sel_pages, sel_count, workspace, workspace_bytes, stream);
+        if (r1 != SA_OK) return r1;
+        return sparse_attn_decode_merged(kv, q, num_q_rows, sel_pages, sel_count, k_max, sink_len, window_len,
+                                         softmax_scale, num_splits, part_o, part_ml, out, out_dtype, lse, advance,
+                                         counters, stream);
+    }
+    uint32_t* status = (uint32_t*)((char*)workspace + status_offset(kv, num_q_rows));
+    sa::SelectArgs sarg{g,     q,         num_q_rows, meta, score_mode, sink_len, window_len, k_max, sel_pages,
+                        sel_count, (float*)workspace, 1, status, 0, 0, nullptr, nullptr,
+                        counters, (int)merge_counters(kv, num_q_rows)};
+    const int r1 = finish(sa::launch_select(sarg, stream), stream);
+    if (r1 != SA_OK) return r1;
+    sa::SelectDecodeArgs d{g,          q,          num_q_rows, (const float*)workspace,
+                           k_max,      sink_len,   window_len, scale * 1.4426950408889634f,
+                           num_splits, num_splits, part_o,     part_ml,
+                           sel_pages,  sel_count,  status,     spin_limit()};
+    d.m = merge_args(kv, num_q_rows, out, out_dtype, lse, counters, advance);
+    const int r2 = finish(sa::launch_select_decode(d, stream), stream);
+    if (r2 != SA_OK || !sync_mode()) return r2;
+    uint32_t st = 0;
+    if (hipMemcpy(&st, status, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return SA_ERR_HIP;
+    return st == 0 ? SA_OK : SA_ERR_HIP;
+}
+
 int32_t sparse_attn_step_path(const sa_kv_desc* kv, int32_t sink_len, int32_t window_len, int32_t token_budget,
                               int32_t num_splits, const void* workspace)
 {
@@ -497,6 +597,9 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
     if ((long)kv->batch * kv->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
     if (!grid_fits((long)kv->batch * kv->num_kv_heads * num_q_rows * local_splits, kDecodeThreads))
         return SA_ERR_UNSUPPORTED;
+    const long max_union = std::min<long>(npg, (long)num_q_rows * k_max);
+    if (!grid_fits(max_union * token_splits * kv->batch * kv->num_kv_heads, kDecodeThreads))
+        return SA_ERR_UNSUPPORTED;
     const GroupedWs w = grouped_ws(kv, npg);
     if (k_max > 0 && (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0))
         return SA_ERR_INVALID_ARG;
@@ -510,8 +613,7 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
                         (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots),
                         npg,        blk_off,    blk_k,      blk_v,   blk_n,
                         blk_end};
-        a.ctr = (int32_t*)(base + w.ctr);
-        const int r1 = finish(sa::launch_group(a, group_grid(kv->head_dim, g.G), stream), stream);
+        const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
         if (r1 != SA_OK) return r1;
     }
     const long off = (long)k_max * token_splits;

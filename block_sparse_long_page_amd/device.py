@@ -114,6 +114,9 @@ class SparseDecoder:
         self.out_dtype = cache.dtype if out_dtype is None else out_dtype
         self.out = torch.empty((rows, cache.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
         self.lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+        # the merging decode's counters: zero before the first call, and every call leaves them zero
+        self.counters = torch.zeros(max(1, B.sparse_attn_merge_counters(self.desc, Q)), dtype=torch.int32,
+                                    device=dev)
 
     def build_meta(self, page_begin: int = 0, page_end: Optional[int] = None, stream=None):
         B.sparse_attn_build_page_meta(self.desc, self.mode, page_begin,
@@ -135,6 +138,27 @@ class SparseDecoder:
         B.sparse_attn_decode_step(self.desc, q, self.Q, self.meta, self.mode, self.sink, self.window, self.budget,
                                   scale, self.splits, self.sel, self.count, self.ws, self.ws_bytes, self.part_o,
                                   self.part_ml, stream)
+
+    def decode_merged(self, q: torch.Tensor, window: Optional[int] = None, scale: float = 0.0, advance: int = 0,
+                      stream=None):
+        """Decode of the kept pages with the merge in the kernel's own last
+        workgroups (sparse_attn_decode_merged): out and lse in one launch; with
+        `advance` > 0 every sequence's length then grows by that many tokens."""
+        if advance:
+            self.c.known_len = None
+        B.sparse_attn_decode_merged(self.desc, q, self.Q, self.sel, self.count, self.k_max, self.sink,
+                                    self.window if window is None else window, scale, self.splits, self.part_o,
+                                    self.part_ml, self.out, self.out_dtype, self.lse, advance, self.counters, stream)
+
+    def select_decode_merged(self, q: torch.Tensor, scale: float = 0.0, advance: int = 0, stream=None):
+        """A selecting step whose decode kernel also merges
+        (sparse_attn_decode_step_merged): out and lse in two launches."""
+        if advance:
+            self.c.known_len = None
+        B.sparse_attn_decode_step_merged(self.desc, q, self.Q, self.meta, self.mode, self.sink, self.window,
+                                         self.budget, scale, self.splits, self.sel, self.count, self.ws, self.ws_bytes,
+                                         self.part_o, self.part_ml, self.out, self.out_dtype, self.lse, advance,
+                                         stream)
 
     def fused_step(self, q: torch.Tensor, stream=None):
         self.select_decode(q, stream=stream)

@@ -278,7 +278,7 @@ int sparse_attn_decode(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, 
  *   and part_o / part_ml for sparse_attn_combine.
  *   workspace   at least sparse_attn_workspace_bytes(kv, num_q_rows) bytes:
  *               the scores, then a status word (cleared by the step's first
- *               kernel).
+ *               kernel), then the counters of sparse_attn_decode_step_merged.
  * The fused kernel runs for bf16 caches with 1 <= k_max <= 1024, at most 8448
  * pages per sequence, max_pages_per_seq a multiple of 4, block_table and
  * workspace 16-byte aligned, and num_splits >= (S + W + k_max * page_size) /
@@ -660,6 +660,58 @@ int sparse_attn_combine(int32_t num_rows, int32_t head_dim, int32_t num_splits, 
 int sparse_attn_combine_advance(int32_t num_rows, int32_t head_dim, int32_t num_splits, const float* part_o,
                                 const float* part_ml, void* out, int32_t out_dtype, float* lse, int32_t* seq_lens,
                                 int32_t batch, int32_t advance, hipStream_t stream);
+
+/*
+ * The split-K decode with the log-sum-exp merge in its own last workgroups
+ * (one launch where sparse_attn_decode + sparse_attn_combine take two; the
+ * merge's arithmetic is the combine's, so out and lse are bitwise those of
+ * the two calls).  Every workgroup of a (sequence, KV head, row) writes its
+ * partials with agent-scope stores (coherent across the XCDs' caches),
+ * waits for them to complete and counts itself in; the last of the
+ * num_splits to arrive reads the problem's partials back with agent-scope
+ * loads, merges its group's rows and clears its counter.  With advance > 0
+ * the last problem of each sequence to merge then adds `advance` to the
+ * sequence's length (kv->seq_lens is written: device memory), when no
+ * workgroup of the launch reads it any more.
+ *   Arguments as in sparse_attn_decode with parts = SA_PART_ALL and
+ *   split_stride = num_splits, and as in sparse_attn_combine for out,
+ *   out_dtype and lse.
+ *   num_splits  1..64
+ *   counters    uint32 [sparse_attn_merge_counters(kv, num_q_rows)]: zero
+ *               before the first call; every call that completes leaves them
+ *               zero.  Calls that overlap on one counter array race.
+ * bf16 caches.  Errors: those of sparse_attn_decode; SA_ERR_INVALID_ARG for a
+ * null out or counters, advance < 0 or num_splits past 64;
+ * SA_ERR_UNSUPPORTED for fp32 caches or another out_dtype.
+ */
+int sparse_attn_decode_merged(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,
+                              const int32_t* sel_count, int32_t k_max, int32_t sink_len, int32_t window_len,
+                              float softmax_scale, int32_t num_splits, float* part_o, float* part_ml, void* out,
+                              int32_t out_dtype, float* lse, int32_t advance, uint32_t* counters, hipStream_t stream);
+
+/* Counters of the merging decode for this shape: one per (sequence, KV head,
+ * row) and one per sequence (host only; a negative error code for bad
+ * arguments). */
+int32_t sparse_attn_merge_counters(const sa_kv_desc* kv, int32_t num_q_rows);
+
+/*
+ * A selecting step with the merge in its decode kernel:
+ * sparse_attn_decode_step whose select-and-decode kernel (or, on the
+ * separate path, whose decode) merges as sparse_attn_decode_merged does; the
+ * counters live in the workspace after the status word and are cleared by
+ * the step's first kernel (on the separate path by a small fill kernel), so
+ * the workspace needs no preparation.  out and lse are bitwise those of
+ * sparse_attn_decode_step + sparse_attn_combine.
+ *   Arguments as in sparse_attn_decode_step, plus out, out_dtype, lse (as in
+ *   sparse_attn_combine) and advance (as in sparse_attn_decode_merged).
+ *   workspace  at least sparse_attn_workspace_bytes(kv, num_q_rows) bytes.
+ * Errors: those of sparse_attn_decode_step and sparse_attn_decode_merged.
+ */
+int sparse_attn_decode_step_merged(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,
+                                   int32_t score_mode, int32_t sink_len, int32_t window_len, int32_t token_budget,
+                                   float softmax_scale, int32_t num_splits, int32_t* sel_pages, int32_t* sel_count,
+                                   void* workspace, size_t workspace_bytes, float* part_o, float* part_ml, void* out,
+                                   int32_t out_dtype, float* lse, int32_t advance, hipStream_t stream);
 
 /* A static string naming a status code. */
 const char* sparse_attn_status_string(int status);

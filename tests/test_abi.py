@@ -28,7 +28,8 @@ def test_exports_every_header_function():
         "sparse_attn_decode_blocks", "sparse_attn_blocks_visible", "sparse_attn_keydiff_workspace_bytes",
         "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path",
         "sparse_attn_decode_step_static", "sparse_attn_combine_advance", "sparse_attn_prefill_chunk",
-        "sparse_attn_prefill_num_splits", "sparse_attn_prefill_workspace_bytes"}
+        "sparse_attn_prefill_num_splits", "sparse_attn_prefill_workspace_bytes", "sparse_attn_decode_merged",
+        "sparse_attn_decode_step_merged", "sparse_attn_merge_counters"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -95,8 +96,9 @@ def test_select_checks():
     lib = B.library()
     d = _desc()
     ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
-    # fp32 scores [B][Hkv][Q][max_pages], then a 256-byte status area of the selecting step
-    assert ws == ((4 * 2 * 2 * 1 * 8 + 255) // 256) * 256 + 256
+    # fp32 scores [B][Hkv][Q][max_pages], then a 256-byte status area of the selecting step, then the
+    # merge's counters (one per (sequence, KV head, row), one per sequence), each 256-byte aligned
+    assert ws == ((4 * 2 * 2 * 1 * 8 + 255) // 256) * 256 + 256 + 256
 
     def sel(**kw):
         a = dict(q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, sel=DEV, cnt=DEV, ws=DEV, wsb=ws)
@@ -187,8 +189,8 @@ def test_decode_grouped_checks():
     lib = B.library()
     d = _desc()
     ws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(d))
-    # counts, item counters, page records (16 bytes), slots; each region 256-byte aligned
-    assert ws == 256 + 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 128 * 2 + 255) // 256) * 256
+    # counts, page records (16 bytes), slots; each region 256-byte aligned
+    assert ws == 256 + ((2 * 2 * 8 * 16 + 255) // 256) * 256 + ((2 * 2 * 8 * 128 * 2 + 255) // 256) * 256
     assert lib.sparse_attn_grouped_workspace_bytes(None) == 0
 
     def grouped(**kw):
@@ -223,6 +225,58 @@ def test_decode_grouped_checks():
     assert grouped(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
     for bad, code in BAD_DESCS:
         assert grouped(desc=_desc(**bad)) == code
+
+
+def test_merged_decode_checks():
+    """The decode and selecting step that merge in their own last workgroup:
+    every argument is checked before any HIP call."""
+    lib = B.library()
+    d = _desc()
+    assert lib.sparse_attn_merge_counters(ctypes.byref(d), 3) == 2 * 2 * 3 + 2
+    assert lib.sparse_attn_merge_counters(None, 1) == -B.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_merge_counters(ctypes.byref(d), 0) == -B.SA_ERR_INVALID_ARG
+
+    def dec(**kw):
+        a = dict(desc=d, q=DEV, rows=1, sel=DEV, cnt=DEV, kmax=2, S=16, W=16, scale=0.0, splits=4, po=DEV, pml=DEV,
+                 out=DEV, odt=B.SA_BF16, lse=None, adv=0, ctr=DEV)
+        a.update(kw)
+        return lib.sparse_attn_decode_merged(ctypes.byref(a["desc"]), a["q"], a["rows"], a["sel"], a["cnt"],
+                                             a["kmax"], a["S"], a["W"], a["scale"], a["splits"], a["po"], a["pml"],
+                                             a["out"], a["odt"], a["lse"], a["adv"], a["ctr"], None)
+
+    for f in ("q", "po", "pml", "out", "ctr"):
+        assert dec(**{f: None}) == B.SA_ERR_INVALID_ARG
+    assert dec(cnt=None) == B.SA_ERR_INVALID_ARG  # a page list needs its counts
+    assert dec(rows=0) == B.SA_ERR_INVALID_ARG
+    assert dec(S=-1) == B.SA_ERR_INVALID_ARG
+    assert dec(W=0) == B.SA_ERR_INVALID_ARG
+    assert dec(adv=-1) == B.SA_ERR_INVALID_ARG
+    assert dec(splits=0) == B.SA_ERR_INVALID_ARG
+    assert dec(splits=65) == B.SA_ERR_INVALID_ARG  # the last workgroup merges at most 64 splits
+    assert dec(scale=float("nan")) == B.SA_ERR_INVALID_ARG
+    assert dec(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    assert dec(odt=7) == B.SA_ERR_UNSUPPORTED
+    for bad, code in BAD_DESCS:
+        assert dec(desc=_desc(**bad)) == code
+    ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
+
+    def step(**kw):
+        a = dict(desc=d, q=DEV, rows=1, meta=DEV, mode=0, S=16, W=16, budget=32, scale=0.0, splits=4, sel=DEV,
+                 cnt=DEV, ws=DEV, wsb=ws, po=DEV, pml=DEV, out=DEV, odt=B.SA_BF16, lse=None, adv=0)
+        a.update(kw)
+        return lib.sparse_attn_decode_step_merged(ctypes.byref(a["desc"]), a["q"], a["rows"], a["meta"], a["mode"],
+                                                  a["S"], a["W"], a["budget"], a["scale"], a["splits"], a["sel"],
+                                                  a["cnt"], a["ws"], a["wsb"], a["po"], a["pml"], a["out"], a["odt"],
+                                                  a["lse"], a["adv"], None)
+
+    for f in ("q", "meta", "po", "pml", "out", "ws", "cnt"):
+        assert step(**{f: None}) == B.SA_ERR_INVALID_ARG
+    assert step(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert step(adv=-1) == B.SA_ERR_INVALID_ARG
+    assert step(splits=65) == B.SA_ERR_INVALID_ARG
+    assert step(mode=9) == B.SA_ERR_UNSUPPORTED
+    assert step(desc=_desc(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    assert step(odt=7) == B.SA_ERR_UNSUPPORTED
 
 
 def test_combine_checks():
@@ -351,7 +405,7 @@ def test_block_index_checks():
     assert select(kmax=5) == B.SA_ERR_INVALID_ARG  # more than the index's blocks
 
     wsd = lib.sparse_attn_blocks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix))
-    assert wsd == 256 + 256 + up(nbk * C * 16) + up(nbk * C * 128 * 2)
+    assert wsd == 256 + up(nbk * C * 16) + up(nbk * C * 128 * 2)
 
     def decode(**kw):
         a = dict(q=DEV, rows=2, sel=DEV, cnt=DEV, kmax=2, W=4, scale=0.0, ts=1, ls=1, po=DEV, pml=DEV, ws=DEV, wsb=wsd)
@@ -520,12 +574,13 @@ def test_launches_past_the_dispatch_limit_are_refused():
     ws = lib.sparse_attn_workspace_bytes(ctypes.byref(d), 1)
     assert lib.sparse_attn_decode_step(ctypes.byref(d), DEV, 1, DEV, 0, 16, 16, 32, 0.0, 1024, DEV, DEV, DEV, ws,
                                        DEV, DEV, None) == B.SA_ERR_UNSUPPORTED
-    # grouped: the persistent decode's grid is one workgroup per CU; the
-    # per-row decode of the sink and window, 64 * 2 * 128 rows x 1024 local
-    # splits of 512 work-items = 2^33, is refused
+    # grouped: union of min(4096 pages, 128 rows * 8) = 1024 pages x 64 token chunks x 128 (b, kvh) x 512
     g = _desc(batch=64, num_q_heads=8, num_kv_heads=2, max_pages_per_seq=4096, num_phys_pages=4096,
               max_seq_len=4096 * 16)
     gws = lib.sparse_attn_grouped_workspace_bytes(ctypes.byref(g))
+    assert lib.sparse_attn_decode_grouped(ctypes.byref(g), DEV, 128, DEV, DEV, 8, 16, 128, 0.0, 64, 1, DEV, DEV,
+                                          DEV, gws, None) == B.SA_ERR_UNSUPPORTED
+    # and the per-row decode of the sink and window: 64 * 2 * 128 rows x 1024 local splits of 512 = 2^33
     assert lib.sparse_attn_decode_grouped(ctypes.byref(g), DEV, 128, DEV, DEV, 0, 16, 128, 0.0, 1, 1024, DEV, DEV,
                                           DEV, gws, None) == B.SA_ERR_UNSUPPORTED
     # combine: one 64-lane wave per row
