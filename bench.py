@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
+    ap.add_argument("--traffic-from", default="",
+                    help="no GPU: write the HBM traffic record from the rocprofv3 counter runs under this folder "
+                         "(prof_fetch, prof_write: the bench under --pmc FETCH_SIZE / WRITE_SIZE, its JSON line in "
+                         "fetch.out; prof_cfetch, prof_cwrite: the same counters over --copy-probe)")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only the warmup and the timed region (for profiler runs)")
     ap.add_argument("--token-splits", type=int, default=0,
@@ -231,6 +235,64 @@ def traffic_record(kernel: str):
     if rec.get("kernel_sources_sha256") != kernel_sources_sha256() or rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
+
+
+def counter_means(folder: str) -> dict:
+    """Mean Counter_Value per dispatch of every kernel (by its k_* name) in
+    the rocprofv3 counter-collection CSV under `folder`."""
+    import csv
+    import glob
+    import re
+
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    tot, n = {}, {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            m = re.search(r"\b(k_\w+)", row["Kernel_Name"])
+            k = m.group(1) if m else row["Kernel_Name"]
+            tot[k] = tot.get(k, 0.0) + float(row["Counter_Value"])
+            n[k] = n.get(k, 0) + 1
+    return {k: tot[k] / n[k] for k in tot}
+
+
+def write_traffic_record(folder: str):
+    """The committed traffic record: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the step's kernels, each scaled by what the same counter
+    reads for a 1 GiB device copy (1 GiB read, 1 GiB written), keyed to the
+    kernel sources' digest."""
+    lines = [ln for ln in open(os.path.join(folder, "fetch.out")) if ln.startswith("{")]
+    line = json.loads(lines[-1])
+    kernel = line["roofline"]["kernel"]
+    copy_kib = (1 << 30) / 1024
+    cf = counter_means(os.path.join(folder, "prof_cfetch"))
+    cw = counter_means(os.path.join(folder, "prof_cwrite"))
+    # the copy is the only kernel of the probe run with a 1 GiB-scale reading
+    fetch_copy, write_copy = max(cf.values()), max(cw.values())
+    fs, ws = copy_kib / fetch_copy, copy_kib / write_copy
+    fetch = counter_means(os.path.join(folder, "prof_fetch"))
+    write = counter_means(os.path.join(folder, "prof_write"))
+    per = {}
+    print(f"| counter | copy reading (KiB / dispatch) | scale |\n|---|---|---|\n"
+          f"| FETCH_SIZE | {fetch_copy:.1f} | {fs:.4f} |\n| WRITE_SIZE | {write_copy:.1f} | {ws:.4f} |\n")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |\n|---|---|---|---|---|")
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if not k.startswith("k_"):
+            continue
+        rd, wr = int(fetch[k] * 1024 * fs), int(write.get(k, 0.0) * 1024 * ws)
+        per[k] = {"read": rd, "written": wr}
+        print(f"| `{k}` | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} |")
+    parts = [k.strip() for k in kernel.split("+")]
+    total = sum(per[k]["read"] + per[k]["written"] for k in parts)
+    rec = {"kernel": kernel, "workload": line["config"]["workload"], "kernel_sources_sha256": kernel_sources_sha256(),
+           "bytes_per_launch": total, "fetch_scale": round(fs, 6), "write_scale": round(ws, 6),
+           "per_kernel_bytes": per, "algorithmic_bytes_per_launch": line["roofline"]["bytes_per_launch"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    alg = rec["algorithmic_bytes_per_launch"]
+    print(f"\n{kernel}: {total / 1e6:.2f} MB of HBM traffic against {alg / 1e6:.2f} MB algorithmic: "
+          f"ratio {total / alg:.3f}")
 
 
 def replicate(pool, c, R):
@@ -1007,6 +1069,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path has no collectives; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_from:
+        write_traffic_record(args.traffic_from)
+        return
 
     import numpy as np
     import torch
