@@ -621,6 +621,9 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     const int ncol = gridDim.x >> 3, col = blockIdx.x >> 3;
     const int bk0 = nbk >= ncol ? col : col % nbk, bstep = nbk >= ncol ? ncol : nbk;
     for (int bk = bk0; bk < nbk; bk += bstep) {
+        // the first item's index is fetched with the units' loads: its round
+        // trip overlaps theirs
+        const int first_item = tid == 0 ? atomicAdd(a.ctr + bk, 1) : -1;
         const int b = bk / g.Hkv;
         const Regions rg(g, b, a.S, a.W);
         // the units, loads in one round
@@ -729,7 +732,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
         }
         __syncthreads();
 
-        next_item = -1;
+        next_item = first_item;
         for (;;) {
             if (tid == 0) s_item = next_item >= 0 ? next_item : atomicAdd(a.ctr + bk, 1);
             __syncthreads();

@@ -225,18 +225,22 @@ __device__ __forceinline__ void block_topk_keys(int n, int k, const uint32_t* ke
 // k): keys with a larger digit are chosen outright (set in a bitmap by wave
 // ballots), and when at most 64 keys carry digit d they are gathered and one
 // wave ranks them by direct comparison of (key, lower index first), taking
-// the best k - (count above).  One wave then emits the bitmap in ascending
-// index order.  More than 64 keys at the boundary (many equal or nearly
-// equal scores) falls back to the multi-pass select above, same result.
+// the best k - (count above).  When more keys carry d, the next 8 bits of
+// just those keys are histogrammed, and so on, until the boundary bucket
+// (the keys matching every decided bit) holds at most 64 keys; only a bucket
+// of more than 64 equal keys falls back to the multi-pass select above (same
+// result).  The workgroup then emits the bitmap in ascending index order, a
+// word per thread placed by a block scan.
 //
-// The steps are separate functions so that a caller can run the last ones on
-// a single wave while its other waves go on with other work:
-//   topk_begin       every thread, before the barrier that publishes the keys
-//   topk_digits      every thread after it (histogram), then a barrier
-//   topk_boundary    any wave: the boundary digit, its count, the count above
-//   topk_collect_block  every thread: the bitmap of larger digits and the
-//                       boundary keys, then a barrier
-//   topk_emit_wave   one wave: ranks the boundary keys, emits ascending
+// The steps:
+//   topk_begin          every thread, before the barrier that publishes the keys
+//   topk_digits         every thread after it (histogram), then a barrier
+//   topk_boundary       every wave: the boundary digit, its count, the count above
+//   topk_refine         every thread, while the bucket holds more than 64 keys
+//   topk_collect_block  every thread: the bitmap of keys above the bucket and
+//                       the bucket's keys, then a barrier
+//   take_boundary       one wave: ranks the bucket's keys into the bitmap
+//   emit_bitmap_block   every thread, after a barrier
 // ---------------------------------------------------------------------------
 
 struct TopkPlan {
@@ -244,14 +248,17 @@ struct TopkPlan {
     int shift;        // the digit is (key >> shift) & dmask
     uint32_t dmask;
     int d, nd, above;  // boundary digit, its key count, keys with a larger digit
+    // the decided bits: the boundary bucket is the keys with (key & hmask) ==
+    // prefix, the keys above it those with (key & hmask) > prefix
+    uint32_t hmask, prefix;
 };
 
-// Every thread, with its min and max key: clears the histogram and publishes
+// Every thread, with its min and max key: clears the histograms and publishes
 // the wave's key range.
 __device__ __forceinline__ void topk_begin(TopkScratch& sh, uint32_t lo, uint32_t hi)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[0][i] = 0;
+    for (int i = tid; i < kTopkPasses * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
     if (tid == 0) sh.nb = 0;
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
@@ -285,47 +292,91 @@ __device__ __forceinline__ TopkPlan topk_digits(TopkScratch& sh, int n, const ui
     const int width = top + 1 < 8 ? top + 1 : 8;
     t.shift = top + 1 - width;
     t.dmask = (1u << width) - 1u;
+    t.hmask = ~((1u << t.shift) - 1u);
+    t.prefix = t.hi & ~((2u << top) - 1u);  // the bits every key shares (none when top = 31)
 #pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kTopkThreads) atomicAdd(&sh.hist[0][(keys[i] >> t.shift) & t.dmask], 1);
     return t;
+}
+
+// Any wave: in a 256-entry digit histogram, the digit where the count of
+// keys from the top reaches need (1 <= need <= the histogram's total), its
+// count, and the count of keys with a larger digit.
+__device__ __forceinline__ void boundary_digit(const int* hist, int need, int& d, int& nd, int& above)
+{
+    const int lane = threadIdx.x & 63;
+    // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
+    const int4 c = *(const int4*)&hist[252 - 4 * lane];
+    const int s4 = c.x + c.y + c.z + c.w;
+    const int above4 = wave_inclusive_scan(s4) - s4;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(above4 < need && above4 + s4 >= need);
+    const int hl = (int)__builtin_ctzll(hit);
+    above = __builtin_amdgcn_readlane(above4, hl);
+    const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
+    const int cy = __builtin_amdgcn_readlane(c.y, hl), cx = __builtin_amdgcn_readlane(c.x, hl);
+    if (above + cw >= need) {
+        d = 255 - 4 * hl;
+        nd = cw;
+    } else if (above + cw + cz >= need) {
+        d = 254 - 4 * hl;
+        nd = cz;
+        above += cw;
+    } else if (above + cw + cz + cy >= need) {
+        d = 253 - 4 * hl;
+        nd = cy;
+        above += cw + cz;
+    } else {
+        d = 252 - 4 * hl;
+        nd = cx;
+        above += cw + cz + cy;
+    }
 }
 
 // Any wave, after the histogram's barrier (and only when lo != hi): the
 // digit where the count of keys from the top reaches k.
 __device__ __forceinline__ void topk_boundary(const TopkScratch& sh, int k, TopkPlan& t)
 {
-    const int lane = threadIdx.x & 63;
-    // lane j owns digits 255-4j .. 252-4j, so lane order is digit order from the top
-    const int4 c = *(const int4*)&sh.hist[0][252 - 4 * lane];
-    const int s4 = c.x + c.y + c.z + c.w;
-    const int above4 = wave_inclusive_scan(s4) - s4;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(above4 < k && above4 + s4 >= k);
-    const int hl = (int)__builtin_ctzll(hit);
-    int above = __builtin_amdgcn_readlane(above4, hl);
-    const int cw = __builtin_amdgcn_readlane(c.w, hl), cz = __builtin_amdgcn_readlane(c.z, hl);
-    const int cy = __builtin_amdgcn_readlane(c.y, hl), cx = __builtin_amdgcn_readlane(c.x, hl);
-    if (above + cw >= k) {
-        t.d = 255 - 4 * hl;
-        t.nd = cw;
-    } else if (above + cw + cz >= k) {
-        t.d = 254 - 4 * hl;
-        t.nd = cz;
-        above += cw;
-    } else if (above + cw + cz + cy >= k) {
-        t.d = 253 - 4 * hl;
-        t.nd = cy;
-        above += cw + cz;
-    } else {
-        t.d = 252 - 4 * hl;
-        t.nd = cx;
-        above += cw + cz + cy;
-    }
-    t.above = above;
+    boundary_digit(sh.hist[0], k, t.d, t.nd, t.above);
+    t.prefix |= (uint32_t)t.d << t.shift;
 }
 
-// Every thread (a barrier must follow): keys with a larger digit into the
-// bitmap (word w holds indices 64w .. 64w+63), keys with digit d into the
-// boundary list (t.nd <= kTopkBoundMax).
+// Every thread, after topk_boundary, while the boundary bucket holds more
+// than kTopkBoundMax keys: the next 8 bits of the bucket's keys (the
+// histograms topk_begin cleared, one per pass; every thread reads every key,
+// only the bucket's are counted), until the bucket holds at most
+// kTopkBoundMax keys or every bit is decided.  Returns whether it does (else
+// its keys are all equal).
+__device__ __forceinline__ bool topk_refine(TopkScratch& sh, int n, int k, const uint32_t* keys, TopkPlan& t)
+{
+    int pass = 1;
+    while (t.nd > kTopkBoundMax && t.shift > 0 && pass < kTopkPasses) {
+        const int width = t.shift < 8 ? t.shift : 8;
+        const int shift = t.shift - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        int* hist = sh.hist[pass];
+#pragma unroll 4
+        for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+            const uint32_t key = keys[i];
+            if ((key & t.hmask) == t.prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+        }
+        __syncthreads();
+        int d, nd, above;
+        boundary_digit(hist, k - t.above, d, nd, above);
+        t.above += above;
+        t.d = d;
+        t.nd = nd;
+        t.shift = shift;
+        t.dmask = dmask;
+        t.hmask |= dmask << shift;
+        t.prefix |= (uint32_t)d << shift;
+        ++pass;
+    }
+    return t.nd <= kTopkBoundMax;
+}
+
+// Every thread (a barrier must follow): keys above the boundary bucket into
+// the bitmap (word w holds indices 64w .. 64w+63), the bucket's keys into
+// the boundary list (t.nd <= kTopkBoundMax).
 __device__ __forceinline__ void topk_collect_block(int n, const uint32_t* keys, const TopkPlan& t, TopkScratch& sh)
 {
     constexpr int NW = kTopkThreads / 64;
@@ -333,11 +384,11 @@ __device__ __forceinline__ void topk_collect_block(int n, const uint32_t* keys, 
     const int rounds = (n + kTopkThreads - 1) / kTopkThreads;
     for (int r = 0; r < rounds; ++r) {
         const int i = r * kTopkThreads + tid;
-        const uint32_t key = i < n ? keys[i] : 0u;
-        const int dig = (int)((key >> t.shift) & t.dmask);
-        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && dig > t.d);
+        const uint32_t mk = (i < n ? keys[i] : 0u) & t.hmask;
+        const uint64_t up = __builtin_amdgcn_ballot_w64(i < n && mk > t.prefix);
         if (lane == 0) sh.chosen[r * NW + wave] = up;
-        if (i < n && dig == t.d) {
+        if (i < n && mk == t.prefix) {
+            const uint32_t key = keys[i];
             const int slot = atomicAdd(&sh.nb, 1);
             sh.b_key[slot] = key;
             sh.b_idx[slot] = i;
@@ -386,15 +437,20 @@ __device__ __forceinline__ void emit_bitmap(int n, const uint64_t* chosen, Emit 
     }
 }
 
-// One wave, once the bitmap and the boundary list are complete: takes the
-// best k - above boundary keys and emits every chosen index in ascending
-// order.
+// Every thread: emits the set bits of the bitmap of n <= 64 * kTopkThreads
+// indices in ascending order, a word per thread placed by a block scan of
+// the words' counts (wsum: kTopkThreads / 64 ints of LDS).
 template <typename Emit>
-__device__ __forceinline__ void topk_emit_wave(int n, int k, const TopkPlan& t, TopkScratch& sh, Emit emit)
+__device__ __forceinline__ void emit_bitmap_block(int n, const uint64_t* chosen, int* wsum, Emit emit)
 {
-    take_boundary(t.nd, k - t.above, sh.b_key, sh.b_idx, sh.chosen);
-    __builtin_amdgcn_wave_barrier();
-    emit_bitmap(n, sh.chosen, emit);
+    const int w = threadIdx.x;
+    uint64_t bits = w < (n + 63) / 64 ? chosen[w] : 0ull;
+    int total;
+    int pos = block_exclusive_scan<kTopkThreads>(__builtin_popcountll(bits), wsum, total);
+    while (bits) {
+        emit(pos++, 64 * w + __builtin_ctzll(bits));
+        bits &= bits - 1;
+    }
 }
 
 // The whole selection by the block (all 512 threads), keys already in LDS
@@ -413,14 +469,17 @@ __device__ __forceinline__ void block_topk_fast(int n, int k, const uint32_t* ke
     }
     __syncthreads();
     topk_boundary(sh, k, t);
-    if (t.nd > kTopkBoundMax) {  // uniform: every wave read the same histogram
-        __syncthreads();         // the multi-pass select clears the histogram first
+    // uniform: every wave read the same histograms
+    if (t.nd > kTopkBoundMax && !topk_refine(sh, n, k, keys, t)) {
+        __syncthreads();  // more equal keys at the boundary than one wave ranks: the multi-pass select
         block_topk_keys(n, k, keys, t.lo, t.hi, sh, emit);
         return;
     }
     topk_collect_block(n, keys, t, sh);
     __syncthreads();
-    if ((tid >> 6) == 0) topk_emit_wave(n, k, t, sh, emit);
+    if ((tid >> 6) == 0) take_boundary(t.nd, k - t.above, sh.b_key, sh.b_idx, sh.chosen);
+    __syncthreads();
+    emit_bitmap_block(n, sh.chosen, sh.gts, emit);
 }
 
 // ---------------------------------------------------------------------------

@@ -490,3 +490,49 @@ def test_selection_over_chunks_of_candidates(pattern):
                      cnt=cnt)
     check_output(dec.out_f32(), ref.out, c.dtype, pattern)
     check_lse(dec.lse_f32(), ref.lse, pattern)
+
+
+@pytest.mark.parametrize("pattern", ["clustered", "random", "few-values"])
+def test_block_topk_is_exact_on_the_gpu_scores(pattern):
+    """The separate selection's top-k (k_topk) against the exact top-k of the
+    fp32 scores the score kernel left in the workspace (larger first, ties to
+    the lower page; -0 ranks as +0): no band, every page must match.
+    'clustered' draws every key near one vector, so the scores crowd into a
+    few radix buckets and the boundary bucket is refined over further digits;
+    'few-values' leaves more than 64 equal scores at the boundary."""
+    pr = synth.random_problem(B=2, Hq=16, Hkv=2, hd=128, P=8, seq_lens=[16384, 9000], sink=32, window=64,
+                              budget=300 * 8, mode="quest", seed=23, shuffle=True)
+    c = pr.cache
+    rng = np.random.default_rng(7)
+    base = rng.standard_normal((c.Hkv, c.hd)).astype(np.float32)
+    if pattern == "clustered":
+        k = base[None, :, None, :] + 0.02 * rng.standard_normal(c.k.shape).astype(np.float32)
+        c.k[:] = synth.store(k, c.dtype)
+    elif pattern == "few-values":
+        vecs = synth.store(rng.standard_normal((5, c.Hkv, c.hd)).astype(np.float32), c.dtype)
+        for b in range(c.B):
+            for p in range(-(-int(c.seq_lens[b]) // c.P)):
+                c.k[c.block_table[b, p]] = vecs[(p * 7) % 5][:, None, :]
+    dc = DeviceCache.from_host(c)
+    dec = SparseDecoder(dc, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+    q = to_device(pr.q)
+    dec.build_meta()
+    dec.select(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    scores = dec.ws[: c.B * c.Hkv * c.max_pages * 4].view(torch.float32).cpu().numpy()
+    scores = scores.reshape(c.B, c.Hkv, c.max_pages)
+    kp = pr.budget // c.P
+    for b in range(c.B):
+        L = int(c.seq_lens[b])
+        se = min(pr.sink, L)
+        ws = max(se, L - pr.window)
+        plo = se // c.P
+        ncand = (ws - 1) // c.P - plo + 1 if ws > se else 0
+        k = min(kp, ncand)
+        for h in range(c.Hkv):
+            s = scores[b, h, plo:plo + ncand].astype(np.float32) + np.float32(0.0)  # -0 -> +0
+            order = np.lexsort((np.arange(ncand), -s.astype(np.float64)))
+            want = np.sort(order[:k]) + plo
+            assert cnt[b, h, 0] == k
+            np.testing.assert_array_equal(sel[b, h, 0, :k], want, err_msg=f"{pattern} b{b} h{h}")
