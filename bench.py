@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=10)
     ap.add_argument("--eager", action="store_true",
                     help="hybrid-3layer-256k: launch every step's kernels one by one instead of replaying graphs")
+    ap.add_argument("--direct", action="store_true",
+                    help="keydiff-llama3.1-8b-8k: sum every held key for the mean instead of carrying the held "
+                         "tokens' key sums from the copy that filled the cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain device copy of 1 GiB (calibration)")
@@ -586,7 +589,12 @@ def bench_keydiff(args):
     block: each step ranks every token of every (sequence, KV head) by the
     distance of its key to the mean key, keeps the sink and the farthest
     tokens up to the budget, and copies the kept K and V rows into the
-    evicted cache."""
+    evicted cache.  By default the step is the steady state of a blockwise
+    eviction: the first 8192 positions are what the previous eviction's copy
+    left, with the key sums of their slots (written untimed, by an identity
+    copy, before timing), so the mean sums only the new block's keys; the
+    step's copy writes the sums the next eviction would carry.  --direct sums
+    every held key instead."""
     import torch
 
     from block_sparse_long_page_amd import binding as B, configs, synth
@@ -601,17 +609,32 @@ def bench_keydiff(args):
     pool = DeviceCache.from_host(c)
     tables = replicate(pool, c, R)
     dst = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, wl.budget, c.dtype)
-    evs = []
+    carried = not args.direct
+    evs, carry = [], []
     for r in range(R):
-        ev = KeyDiffEviction(pool, dst, wl.budget, wl.sink)
+        ev = KeyDiffEviction(pool, dst, wl.budget, wl.sink, sums=carried)
         ev.src_desc = pool.desc(tables[r])
         evs.append(ev)
+        if carried:  # the copy that left positions [0, budget) of this replica (untimed)
+            filler = KeyDiffEviction(pool, dst, wl.budget, 0, sums=True)
+            filler.src_desc = pool.desc(tables[r])
+            filler.kept.copy_(torch.arange(wl.budget, dtype=torch.int32, device=filler.kept.device)
+                              .expand_as(filler.kept))
+            filler.count.fill_(wl.budget)
+            B.sparse_attn_keydiff_compact_sums(filler.src_desc, filler.kept, filler.count, wl.budget,
+                                               filler.dst_desc, filler.slot_sums)
+            carry.append(filler.carried())
+    torch.cuda.synchronize()
 
     def select(r):
-        evs[r].select()
+        evs[r].select(carried=carry[r] if carried else None)
 
     def compact(r):
-        B.sparse_attn_keydiff_compact(evs[r].src_desc, evs[r].kept, evs[r].count, wl.budget, evs[r].dst_desc)
+        if carried:
+            B.sparse_attn_keydiff_compact_sums(evs[r].src_desc, evs[r].kept, evs[r].count, wl.budget,
+                                               evs[r].dst_desc, evs[r].slot_sums)
+        else:
+            B.sparse_attn_keydiff_compact(evs[r].src_desc, evs[r].kept, evs[r].count, wl.budget, evs[r].dst_desc)
 
     def step(r):
         select(r)
@@ -643,6 +666,10 @@ def bench_keydiff(args):
     # positions and the kept K and V rows and writes the rows
     sel_bytes = nbk * (L * row + nch * c.hd * 4 * 2 + L * 4 * 2 + wl.budget * 4)
     comp_bytes = nbk * (kept_n * 4 + kept_n * row * 2 * 2)
+    if carried:  # the carried slot sums read, the next ones written
+        groups = B.sparse_attn_keydiff_slot_groups(wl.budget)
+        sel_bytes += nbk * groups * c.hd * 4
+        comp_bytes += nbk * groups * c.hd * 4
     step_bytes = sel_bytes + comp_bytes
     gbs = step_bytes / (ms * 1e-3) / 1e9
     comp_gbs = comp_bytes / (comp_ms * 1e-3) / 1e9
@@ -680,7 +707,10 @@ def bench_keydiff(args):
         "data": "synthetic (seeded): K from 64 Gaussian clusters with 4 needle pages per (b, kvh), V N(0,1)",
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "cache_tokens": L, "budget": wl.budget, "block": wl.block, "sink": wl.sink, "page": c.P,
-                   "replicas": R, "step": "keydiff select (sums, distances, top-k) + compaction"},
+                   "replicas": R, "carried_sums": carried,
+                   "step": ("keydiff select with the held tokens' key sums carried (the new block summed, distances, "
+                            "top-k) + compaction writing the next sums") if carried else
+                           "keydiff select (sums, distances, top-k) + compaction"},
         "roofline": {"bound": "hbm", "kernel": "k_kd_compact", "achieved": round(comp_gbs, 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(comp_gbs / 8000.0, 4), "traffic": None,
                      "bytes_per_launch": comp_bytes, "avg_launch_us": round(comp_ms * 1e3, 2)},

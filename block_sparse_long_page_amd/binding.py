@@ -101,6 +101,10 @@ _SIGS = {
     "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC, _I, _I]),
     "sparse_attn_keydiff_select": (ctypes.c_int, [_DESC, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_keydiff_compact": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P]),
+    "sparse_attn_keydiff_compact_sums": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P, _P]),
+    "sparse_attn_keydiff_select_carried": (ctypes.c_int, [_DESC, _I, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
+                                                          _P]),
+    "sparse_attn_keydiff_slot_groups": (ctypes.c_int32, [_I]),
     "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -267,6 +271,26 @@ def sparse_attn_keydiff_compact(src: sa_kv_desc, kept, kept_count, budget: int, 
                                 stream=None) -> None:
     _check(_lib.sparse_attn_keydiff_compact(ctypes.byref(src), _ptr(kept), _ptr(kept_count), budget,
                                             ctypes.byref(dst), _stream(stream)), "sparse_attn_keydiff_compact")
+
+
+def sparse_attn_keydiff_compact_sums(src: sa_kv_desc, kept, kept_count, budget: int, dst: sa_kv_desc, slot_sums,
+                                     stream=None) -> None:
+    _check(_lib.sparse_attn_keydiff_compact_sums(ctypes.byref(src), _ptr(kept), _ptr(kept_count), budget,
+                                                 ctypes.byref(dst), _ptr(slot_sums), _stream(stream)),
+           "sparse_attn_keydiff_compact_sums")
+
+
+def sparse_attn_keydiff_select_carried(kv: sa_kv_desc, sink_len: int, budget: int, slot_sums, slot_groups: int,
+                                       carried_count, kept, kept_count, workspace, workspace_bytes: int,
+                                       stream=None) -> None:
+    _check(_lib.sparse_attn_keydiff_select_carried(ctypes.byref(kv), sink_len, budget, _ptr(slot_sums), slot_groups,
+                                                   _ptr(carried_count), _ptr(kept), _ptr(kept_count),
+                                                   _ptr(workspace), workspace_bytes, _stream(stream)),
+           "sparse_attn_keydiff_select_carried")
+
+
+def sparse_attn_keydiff_slot_groups(budget: int) -> int:
+    return int(_lib.sparse_attn_keydiff_slot_groups(budget))
 
 
 def sparse_attn_blocks_visible(kv: sa_kv_desc, index: sa_block_index, window_len: int, visible_end,

@@ -246,6 +246,13 @@ struct KeydiffArgs {
     int ecnk;             // chunks per (sequence, KV head)
     uint32_t* part_keys;  // [B][Hkv][ecnk][kTopkChunk] inverted order keys of each chunk's picks
     int32_t* part_idx;    // [B][Hkv][ecnk][kTopkChunk] their candidate indices, ascending
+    // Key sums carried from the compaction that filled the cache (null: none):
+    // group i of (b, kvh) is the sum of the keys of positions [64i, 64i + 64);
+    // a chunk of positions below carried_count[b][kvh] takes its sum from its
+    // groups instead of the keys.
+    const float* carried;          // [B][Hkv][carried_groups][hd]
+    const int32_t* carried_count;  // [B][Hkv]
+    int carried_groups;
 };
 constexpr int kKdMaxChunks = 16;  // chunks of the two-stage eviction (131072 candidates)
 
@@ -275,7 +282,9 @@ struct CompactArgs {
     int budget;
     const int32_t* kept;
     const int32_t* count;
+    float* slot_sums;  // null, or [B][Hkv][ceil(budget / kKdSlots)][hd]: the key sum of each group of slots
 };
+constexpr int kKdSlots = 64;  // destination slots per compaction workgroup, and per carried key sum
 
 struct CombineArgs {
     int rows, hd, splits, out_dtype;

@@ -6,7 +6,10 @@
 //
 //  * k_kd_sum: per (sequence, KV head, chunk of kKdChunk tokens) the fp32 sum
 //    of the keys (rows in order in each lane, then lanes and waves in a fixed
-//    order: bitwise reproducible).
+//    order: bitwise reproducible).  A chunk that the previous eviction's
+//    compaction filled takes its sum from the key sums that compaction left
+//    (one per group of kKdSlots slots, added in order) instead of reading its
+//    keys again: between evictions only the new block's keys are summed.
 //  * k_kd_dist: every workgroup rebuilds the mean key from the chunk sums, in
 //    chunk order, and writes the order key of each candidate's squared
 //    distance to it, candidates in reverse position order.
@@ -15,7 +18,8 @@
 //    position is kept: the candidates are ranked in reverse position order
 //    and the block top-k prefers the lower index.  Kept positions ascending.
 //  * k_kd_compact: copies the kept tokens' K and V rows, in order, into
-//    slots 0 .. count-1 of a destination cache.
+//    slots 0 .. count-1 of a destination cache, and optionally writes the key
+//    sum of every group of kKdSlots slots (the next eviction's carried sums).
 // The sum and distance passes stream the keys with 16-byte loads; each wave
 // resolves the block-table entries of the pages its rows span once, up front.
 #include <type_traits>
@@ -28,10 +32,11 @@ namespace sa {
 
 namespace {
 
+static_assert(kKdChunk % kKdSlots == 0, "a chunk of the sum pass is whole groups of carried sums");
+
 constexpr int kKdWaves = 4;
 constexpr int kKdRowsPerWave = kKdChunk / kKdWaves;
 constexpr int kKdU = 16;            // row loads per lane in flight
-constexpr int kKdSlots = 64;        // destination slots per compaction workgroup
 constexpr int kKdCopyThreads = 256;
 
 __device__ __forceinline__ int kd_len(const Geometry& g, int T, int b)
@@ -129,6 +134,18 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_sum(KeydiffArgs a)
     const int L = kd_len(g, a.T, b);
     const int t0 = blockIdx.x * kKdChunk;
     if (t0 >= L) return;
+    float* const dst = a.partial + ((long)bh * a.nchunks + blockIdx.x) * HD;
+    if (a.carried && t0 + kKdChunk <= imin(imin(a.carried_count[bh], kKdSlots * a.carried_groups), L)) {
+        // a chunk the last compaction filled: the sum of its groups' sums, in order
+        const float* cs = a.carried + ((long)bh * a.carried_groups + blockIdx.x * (kKdChunk / kKdSlots)) * HD;
+        for (int c = threadIdx.x; c < HD; c += 64 * kKdWaves) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < kKdChunk / kKdSlots; ++i) s += cs[i * HD + c];
+            dst[c] = s;
+        }
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % Lay::LPT, rg = lane / Lay::LPT;
     const int r0 = imin(L, t0 + wave * kKdRowsPerWave), r1 = imin(L, r0 + kKdRowsPerWave);
@@ -153,7 +170,7 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_sum(KeydiffArgs a)
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kKdWaves; ++w) s += wsum[w][c];
-        a.partial[((long)bh * a.nchunks + blockIdx.x) * HD + c] = s;
+        dst[c] = s;
     }
 }
 
@@ -432,6 +449,36 @@ __global__ __launch_bounds__(kKdCopyThreads) void k_kd_compact(CompactArgs a)
         if (dst_off[it] < 0) continue;
         ((uint4*)d.k)[dst_off[it]] = kv[it][0];
         ((uint4*)d.v)[dst_off[it]] = kv[it][1];
+    }
+    if (a.slot_sums) {
+        // the key sum of this group of slots (a key not copied counts as
+        // zero): each thread adds its rows (slots j0 + it * RPI + tid / PPR,
+        // in order) for the channels of its piece, then the row groups are
+        // added in order
+        using Lay = KdLayout<HD, BF>;
+        constexpr int RPI = kKdCopyThreads / PPR;  // row groups
+        __shared__ float part[RPI][HD];
+        float acc[Lay::CH];
+#pragma unroll
+        for (int c = 0; c < Lay::CH; ++c) acc[c] = 0.f;
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            float x[Lay::CH];
+            Lay::unpack(kv[it][0], x);  // zeros when the row was not copied
+#pragma unroll
+            for (int c = 0; c < Lay::CH; ++c) acc[c] += x[c];
+        }
+        const int piece = threadIdx.x % PPR;
+#pragma unroll
+        for (int c = 0; c < Lay::CH; ++c) part[threadIdx.x / PPR][piece * Lay::CH + c] = acc[c];
+        __syncthreads();
+        float* out = a.slot_sums + ((long)bh * gridDim.x + blockIdx.x) * HD;
+        for (int c = threadIdx.x; c < HD; c += kKdCopyThreads) {
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) s += part[r][c];
+            out[c] = s;
+        }
     }
 }
 

@@ -871,8 +871,11 @@ size_t sparse_attn_keydiff_workspace_bytes(const sa_kv_desc* kv, int32_t sink_le
     return keydiff_ws(kv, sink_len, budget).total;
 }
 
-int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
-                               int32_t* kept_count, void* workspace, size_t workspace_bytes, hipStream_t stream)
+namespace {
+
+int keydiff_select_impl(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, const float* slot_sums,
+                        int32_t slot_groups, const int32_t* carried_count, int32_t* kept, int32_t* kept_count,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
@@ -896,12 +899,15 @@ int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t b
                       kept_count,
                       w.ecnk,
                       w.ecnk ? (uint32_t*)(base + w.part_keys) : nullptr,
-                      w.ecnk ? (int32_t*)(base + w.part_idx) : nullptr};
+                      w.ecnk ? (int32_t*)(base + w.part_idx) : nullptr,
+                      slot_sums,
+                      carried_count,
+                      slot_groups};
     return finish(sa::launch_keydiff_select(a, stream), stream);
 }
 
-int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
-                                int32_t budget, const sa_kv_desc* dst, hipStream_t stream)
+int keydiff_compact_impl(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count, int32_t budget,
+                         const sa_kv_desc* dst, float* slot_sums, hipStream_t stream)
 {
     sa::Geometry gs, gd;
     const int rs = check_kv(src, &gs);
@@ -914,9 +920,47 @@ int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, cons
         return SA_ERR_INVALID_ARG;
     if ((long)dst->max_pages_per_seq * dst->page_size < budget) return SA_ERR_INVALID_ARG;
     if ((long)src->batch * src->num_kv_heads > kMaxGridY) return SA_ERR_UNSUPPORTED;
-    if (!grid_fits(((long)budget + 63) / 64, 256)) return SA_ERR_UNSUPPORTED;
-    sa::CompactArgs a{gs, gd, budget, kept, kept_count};
+    if (!grid_fits(((long)budget + sa::kKdSlots - 1) / sa::kKdSlots, 256)) return SA_ERR_UNSUPPORTED;
+    sa::CompactArgs a{gs, gd, budget, kept, kept_count, slot_sums};
     return finish(sa::launch_keydiff_compact(a, stream), stream);
+}
+
+}  // namespace
+
+int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t budget, int32_t* kept,
+                               int32_t* kept_count, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return keydiff_select_impl(kv, sink_len, budget, nullptr, 0, nullptr, kept, kept_count, workspace,
+                               workspace_bytes, stream);
+}
+
+int sparse_attn_keydiff_select_carried(const sa_kv_desc* kv, int32_t sink_len, int32_t budget,
+                                       const float* slot_sums, int32_t slot_groups, const int32_t* carried_count,
+                                       int32_t* kept, int32_t* kept_count, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream)
+{
+    if (!slot_sums || !carried_count || slot_groups < 1) return SA_ERR_INVALID_ARG;
+    return keydiff_select_impl(kv, sink_len, budget, slot_sums, slot_groups, carried_count, kept, kept_count,
+                               workspace, workspace_bytes, stream);
+}
+
+int32_t sparse_attn_keydiff_slot_groups(int32_t budget)
+{
+    if (budget < 1) return -SA_ERR_INVALID_ARG;
+    return (budget + sa::kKdSlots - 1) / sa::kKdSlots;
+}
+
+int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
+                                int32_t budget, const sa_kv_desc* dst, hipStream_t stream)
+{
+    return keydiff_compact_impl(src, kept, kept_count, budget, dst, nullptr, stream);
+}
+
+int sparse_attn_keydiff_compact_sums(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
+                                     int32_t budget, const sa_kv_desc* dst, float* slot_sums, hipStream_t stream)
+{
+    if (!slot_sums) return SA_ERR_INVALID_ARG;
+    return keydiff_compact_impl(src, kept, kept_count, budget, dst, slot_sums, stream);
 }
 
 int sparse_attn_decode_step_static(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const void* meta,

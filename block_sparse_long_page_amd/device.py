@@ -449,9 +449,15 @@ class KeyDiffEviction:
     """KeyDiff eviction of a DeviceCache to a token budget: the kept tokens of
     every (sequence, KV head) (sparse_attn_keydiff_select) and their K and V
     rows copied, in order, into `dst` (sparse_attn_keydiff_compact), whose
-    lengths are then set to the kept counts."""
+    lengths are then set to the kept counts.
 
-    def __init__(self, src: DeviceCache, dst: DeviceCache, budget: int, sink: int):
+    With `sums=True` the copy also writes the key sums of every 64 slots it
+    fills (sparse_attn_keydiff_compact_sums, into `slot_sums`), and
+    select(carried=...) takes such sums for the cache's first positions
+    (sparse_attn_keydiff_select_carried): the carried eviction of a cache that
+    an earlier eviction's copy filled."""
+
+    def __init__(self, src: DeviceCache, dst: DeviceCache, budget: int, sink: int, sums: bool = False):
         self.src, self.dst, self.budget, self.sink = src, dst, budget, sink
         dev = src.k.device
         self.kept = torch.full((src.B, src.Hkv, budget), -1, dtype=torch.int32, device=dev)
@@ -459,13 +465,32 @@ class KeyDiffEviction:
         self.src_desc, self.dst_desc = src.desc(), dst.desc()
         self.ws_bytes = B.sparse_attn_keydiff_workspace_bytes(self.src_desc, sink, budget)
         self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.slot_groups = B.sparse_attn_keydiff_slot_groups(budget)
+        self.slot_sums = (torch.zeros((src.B, src.Hkv, self.slot_groups, src.hd), dtype=torch.float32, device=dev)
+                          if sums else None)
 
-    def select(self, stream=None):
-        B.sparse_attn_keydiff_select(self.src_desc, self.sink, self.budget, self.kept, self.count, self.ws,
-                                     self.ws_bytes, stream)
+    def select(self, stream=None, carried=None):
+        """carried: (slot_sums, slot_groups, carried_count) of the copy that
+        filled this eviction's source cache, or None."""
+        if carried is None:
+            B.sparse_attn_keydiff_select(self.src_desc, self.sink, self.budget, self.kept, self.count, self.ws,
+                                         self.ws_bytes, stream)
+        else:
+            sums, groups, ccount = carried
+            B.sparse_attn_keydiff_select_carried(self.src_desc, self.sink, self.budget, sums, groups, ccount,
+                                                 self.kept, self.count, self.ws, self.ws_bytes, stream)
+
+    def carried(self):
+        """What the next eviction of `dst` carries from this one's copy."""
+        assert self.slot_sums is not None
+        return self.slot_sums, self.slot_groups, self.count
 
     def compact(self, stream=None):
-        B.sparse_attn_keydiff_compact(self.src_desc, self.kept, self.count, self.budget, self.dst_desc, stream)
+        if self.slot_sums is None:
+            B.sparse_attn_keydiff_compact(self.src_desc, self.kept, self.count, self.budget, self.dst_desc, stream)
+        else:
+            B.sparse_attn_keydiff_compact_sums(self.src_desc, self.kept, self.count, self.budget, self.dst_desc,
+                                               self.slot_sums, stream)
         # every KV head keeps min(L, budget) tokens: the first head's count is the sequence's
         with on_stream(stream):
             self.dst.seq_lens.copy_(self.count[:, 0])

@@ -580,6 +580,53 @@ int sparse_attn_keydiff_select(const sa_kv_desc* kv, int32_t sink_len, int32_t b
 int sparse_attn_keydiff_compact(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
                                 int32_t budget, const sa_kv_desc* dst, hipStream_t stream);
 
+/*
+ * KeyDiff eviction with the held keys' sums carried from the last eviction
+ * (course module 14, section 14.4: blockwise eviction; the mean key of the
+ * held set is what each eviction measures distances to).  After an eviction
+ * the cache holds the kept tokens, whose key sums that eviction's copy can
+ * leave behind (sparse_attn_keydiff_compact_sums); until the next eviction
+ * only new tokens are appended, so its mean needs the keys of the new block
+ * and those sums, not the keys of the whole cache.
+ *
+ * sparse_attn_keydiff_compact_sums: sparse_attn_keydiff_compact, and for
+ * every (sequence, KV head) the fp32 sum of the keys copied into each group
+ * of 64 destination slots [64i, 64i + 64) (a key not copied counts as zero),
+ * added in a fixed order (bitwise reproducible); groups at or past
+ * kept_count are not written.
+ *   slot_sums  fp32 [batch][num_kv_heads][sparse_attn_keydiff_slot_groups(
+ *              budget)][head_dim]
+ *
+ * sparse_attn_keydiff_select_carried: sparse_attn_keydiff_select on a cache
+ * whose positions [0, carried_count[b][kvh]) hold the keys that a
+ * sparse_attn_keydiff_compact_sums call copied there (its slot_sums and its
+ * kept_count, for this cache as its dst); new tokens may follow them.  Each
+ * 512-position chunk of a (sequence, KV head) that lies wholly below
+ * min(carried_count, L_b) takes its key sum from its 8 groups' sums instead
+ * of its keys; the others are summed from the keys.  The choice rule is
+ * sparse_attn_keydiff_select's; the mean differs from it by fp32 rounding
+ * only (the order of the additions).  The caller keeps the carried positions
+ * unchanged between the two calls.
+ *   slot_sums, slot_groups  as written by the compaction, slot_groups =
+ *              sparse_attn_keydiff_slot_groups(its budget)
+ *   carried_count  int32 [batch][num_kv_heads], the compaction's kept_count
+ *              (values past 64 * slot_groups count as 64 * slot_groups)
+ *   the rest as in sparse_attn_keydiff_select (same workspace size).
+ * Errors: those of sparse_attn_keydiff_select and sparse_attn_keydiff_compact;
+ * SA_ERR_INVALID_ARG for a null slot_sums or carried_count, or slot_groups < 1.
+ */
+int sparse_attn_keydiff_compact_sums(const sa_kv_desc* src, const int32_t* kept, const int32_t* kept_count,
+                                     int32_t budget, const sa_kv_desc* dst, float* slot_sums, hipStream_t stream);
+int sparse_attn_keydiff_select_carried(const sa_kv_desc* kv, int32_t sink_len, int32_t budget,
+                                       const float* slot_sums, int32_t slot_groups, const int32_t* carried_count,
+                                       int32_t* kept, int32_t* kept_count, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* Groups of 64 slots whose key sums sparse_attn_keydiff_compact_sums writes
+ * per (sequence, KV head) for this budget: ceil(budget / 64) (host only;
+ * -SA_ERR_INVALID_ARG for budget < 1). */
+int32_t sparse_attn_keydiff_slot_groups(int32_t budget);
+
 /* Which kernels sparse_attn_decode_step queues for these arguments (host
  * only): SA_STEP_FUSED (score kernel, then the select-and-decode kernel) or
  * SA_STEP_SEPARATE (sparse_attn_select, then sparse_attn_decode);

@@ -29,7 +29,8 @@ def test_exports_every_header_function():
         "sparse_attn_keydiff_select", "sparse_attn_keydiff_compact", "sparse_attn_step_path",
         "sparse_attn_decode_step_static", "sparse_attn_combine_advance", "sparse_attn_prefill_chunk",
         "sparse_attn_prefill_num_splits", "sparse_attn_prefill_workspace_bytes", "sparse_attn_decode_merged",
-        "sparse_attn_decode_step_merged", "sparse_attn_merge_counters"}
+        "sparse_attn_decode_step_merged", "sparse_attn_merge_counters", "sparse_attn_keydiff_compact_sums",
+        "sparse_attn_keydiff_select_carried", "sparse_attn_keydiff_slot_groups"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -528,6 +529,37 @@ def test_keydiff_checks():
         a.update(kw)
         return lib.sparse_attn_keydiff_compact(ctypes.byref(a["src"]), a["kept"], a["cnt"], a["budget"],
                                                ctypes.byref(a["dst"]), None)
+
+    def sel_c(**kw):
+        a = dict(desc=d, sink=4, budget=64, sums=DEV, groups=1, ccount=DEV, kept=DEV, cnt=DEV, ws=DEV, wsb=ws)
+        a.update(kw)
+        return lib.sparse_attn_keydiff_select_carried(ctypes.byref(a["desc"]), a["sink"], a["budget"], a["sums"],
+                                                      a["groups"], a["ccount"], a["kept"], a["cnt"], a["ws"],
+                                                      a["wsb"], None)
+
+    assert sel_c(sums=None) == B.SA_ERR_INVALID_ARG
+    assert sel_c(ccount=None) == B.SA_ERR_INVALID_ARG
+    assert sel_c(groups=0) == B.SA_ERR_INVALID_ARG
+    assert sel_c(kept=None) == B.SA_ERR_INVALID_ARG
+    assert sel_c(wsb=ws - 1) == B.SA_ERR_INVALID_ARG
+    assert sel_c(budget=3) == B.SA_ERR_INVALID_ARG
+    for bad, code in BAD_DESCS:
+        assert sel_c(desc=_desc(**bad)) == code
+    assert lib.sparse_attn_keydiff_slot_groups(64) == 1
+    assert lib.sparse_attn_keydiff_slot_groups(65) == 2
+    assert lib.sparse_attn_keydiff_slot_groups(8192) == 128
+    assert lib.sparse_attn_keydiff_slot_groups(0) == -B.SA_ERR_INVALID_ARG
+
+    def comp_s(**kw):
+        a = dict(src=d, dst=_desc(max_pages_per_seq=4, num_phys_pages=8, max_seq_len=64), kept=DEV, cnt=DEV,
+                 budget=64, sums=DEV)
+        a.update(kw)
+        return lib.sparse_attn_keydiff_compact_sums(ctypes.byref(a["src"]), a["kept"], a["cnt"], a["budget"],
+                                                    ctypes.byref(a["dst"]), a["sums"], None)
+
+    assert comp_s(sums=None) == B.SA_ERR_INVALID_ARG
+    assert comp_s(kept=None) == B.SA_ERR_INVALID_ARG
+    assert comp_s(budget=65) == B.SA_ERR_INVALID_ARG
 
     assert comp(kept=None) == B.SA_ERR_INVALID_ARG
     assert comp(cnt=None) == B.SA_ERR_INVALID_ARG

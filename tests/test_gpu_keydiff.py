@@ -179,11 +179,16 @@ def test_attention_over_the_evicted_cache(name):
     check_lse(dec.lse_f32(), ref_l, name)
 
 
-def test_blockwise_schedule_on_the_gpu_state():
+@pytest.mark.parametrize("carried", [False, True])
+def test_blockwise_schedule_on_the_gpu_state(carried):
     """A 4000-token sequence arrives in blocks of 300; after each block the
     cache (kept tokens, then the block) is evicted back to 512 tokens and
     compacted into the other of two buffers.  Each eviction is checked
-    against the oracle on the keys the GPU's cache holds at that moment."""
+    against the oracle on the keys the GPU's cache holds at that moment.
+    carried: each copy also writes the key sums of every 64 slots it fills
+    (checked against the sums of the rows it copied), and the next eviction
+    takes the held tokens' mean from them (only the new block's keys are
+    summed)."""
     block, budget, sink = 300, 512, 8
     pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=128, P=16, seq_lens=[4000, 4000], sink=sink, window=1,
                               budget=budget, dtype="bf16", seed=77, clusters=8)
@@ -198,6 +203,8 @@ def test_blockwise_schedule_on_the_gpu_state():
     cur = 0
     n_in = 0
     band = 0
+    prev = None  # the eviction whose copy filled the current source
+    n_carried = 0
     for t0 in range(0, 4000, block):
         src = bufs[cur]
         t1 = min(4000, t0 + block)
@@ -216,8 +223,13 @@ def test_blockwise_schedule_on_the_gpu_state():
         n_cache = n_in + (t1 - t0)
         src.seq_lens.fill_(n_cache)
         dst = bufs[1 - cur]
-        ev = KeyDiffEviction(src, dst, budget, sink)
-        ev.evict()
+        ev = KeyDiffEviction(src, dst, budget, sink, sums=carried)
+        if carried and prev is not None:
+            ev.select(carried=prev.carried())
+            n_carried += int(prev.count.min().item()) // 512
+        else:
+            ev.select()
+        ev.compact()
         torch.cuda.synchronize()
         got = ev.kept_positions()
         for b in range(c.B):
@@ -227,11 +239,25 @@ def test_blockwise_schedule_on_the_gpu_state():
                 held[b][h] = held[b][h][got[b][h]]
         n_in = min(n_cache, budget)
         assert list(dst.seq_lens.cpu().numpy()) == [n_in] * c.B
+        if carried:  # the slot sums: the copied keys of each group of 64 slots
+            sums = ev.slot_sums.cpu().numpy()
+            for b in range(c.B):
+                for h in range(c.Hkv):
+                    kk = synth.to_f32(full_k[b, h, held[b][h]], c.dtype).astype(np.float64)
+                    for i in range(-(-n_in // 64)):
+                        grp = kk[64 * i: 64 * (i + 1)]
+                        want = grp.sum(0)
+                        tol = 1e-5 * np.abs(grp).sum(0) + 1e-6
+                        assert (np.abs(sums[b, h, i] - want) <= tol).all(), (t0, b, h, i)
+        prev = ev
         cur = 1 - cur
     for b in range(c.B):
         for h in range(c.Hkv):
             assert list(held[b][h][:sink]) == list(range(sink)) and len(held[b][h]) == budget
-    print(f"blockwise: {band} candidates inside the band over {-(-4000 // block)} evictions")
+    if carried:
+        assert n_carried > 0  # some evictions took whole chunks from the carried sums
+    print(f"blockwise: {band} candidates inside the band over {-(-4000 // block)} evictions, "
+          f"{n_carried} carried chunks")
 
 
 def test_full_size_eviction():
@@ -258,3 +284,41 @@ def test_full_size_eviction():
         src_row = c.k[c.block_table[b, p // c.P], kvh, p % c.P]
         np.testing.assert_array_equal(dk[j // c.P + b * dst.max_pages, kvh, j % c.P].view(src_row.dtype), src_row)
     print(f"full size: {band} candidates inside the band")
+
+
+def test_full_size_carried_eviction():
+    """The same layer as the steady state of a blockwise eviction: the first
+    8192 positions of every (sequence, KV head) as an earlier eviction's copy
+    left them (an identity copy writes their slot sums), the last 2048 the
+    new block.  The carried selection's kept sets are within the band of the
+    oracle on the whole cache (the needle tokens all kept); the count of
+    positions that differ from the direct selection is reported."""
+    wl = configs.KEYDIFF_8K
+    pr = synth.workload_problem(wl)
+    c = pr.cache
+    src = DeviceCache.from_host(c)
+    held = wl.budget
+    # the copy that would have filled positions [0, held): identity kept lists into a scratch cache
+    scratch = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, held, c.dtype)
+    filler = KeyDiffEviction(src, scratch, held, 0, sums=True)
+    filler.kept.copy_(torch.arange(held, dtype=torch.int32, device=filler.kept.device).expand_as(filler.kept))
+    filler.count.fill_(held)
+    filler.compact()
+    dst = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, wl.budget, c.dtype)
+    ev = KeyDiffEviction(src, dst, wl.budget, wl.sink, sums=True)
+    ev.select(carried=filler.carried())
+    ev.compact()
+    direct = KeyDiffEviction(src, dst, wl.budget, wl.sink)
+    direct.select()
+    torch.cuda.synchronize()
+    got, ref = ev.kept_positions(), direct.kept_positions()
+    band, differ = 0, 0
+    for b in range(c.B):
+        for kvh in range(c.Hkv):
+            keys = dense_keys_values(c, b, kvh)[0]
+            band += check_kept(got[b][kvh], keys, wl.budget, wl.sink)
+            differ += len(set(got[b][kvh].tolist()) ^ set(ref[b][kvh].tolist()))
+    for (b, kvh, p) in pr.needles:
+        assert set(range(p * c.P, (p + 1) * c.P)) <= set(got[b][kvh].tolist())
+    print(f"full size, carried: {band} candidates inside the band; {differ} positions differ from the direct "
+          f"selection (its mean rounds differently)")
