@@ -215,6 +215,7 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_dist(KeydiffArgs a)
 __global__ __launch_bounds__(kTopkThreads) void k_kd_topk(KeydiffArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint32_t keys[kKdMaxCand];
+    __shared__ int32_t staged[kKdMaxCand];  // the kept candidates' positions, in order, before one coalesced write
     __shared__ TopkScratch sh;
     const Geometry& g = a.g;
     const int bh = blockIdx.x, b = bh / g.Hkv;
@@ -260,7 +261,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_kd_topk(KeydiffArgs a)
                 }
         }
     }
-    block_topk_fast(m, k, keys, lo, hi, sh, [&](int pos, int j) { kept[s0 + (k - 1 - pos)] = L - 1 - j; });
+    block_topk_fast(m, k, keys, lo, hi, sh, [&](int pos, int j) { staged[k - 1 - pos] = L - 1 - j; });
+    __syncthreads();
+    for (int i = tid; i < k; i += kTopkThreads) kept[s0 + i] = staged[i];
 }
 
 // Past kKdMaxCand candidates the evicted tokens are chosen instead of the
