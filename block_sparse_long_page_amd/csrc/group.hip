@@ -15,14 +15,20 @@
 // before it) as an empty partial (m = -inf, l = 0; the combine leaves its o
 // out).
 //
-// k_group_decode_mfma: persistent, one workgroup per CU.  Its items are
-// (page of the union, token chunk of the page, pass) of one (sequence, KV
-// head), taken from a per-(sequence, KV head) counter in the union's order
-// (the costliest pages, tokens times rows, first); a pass holds up to 128
-// query columns, so the rows of a page chosen by many rows are split over
-// several workgroups.  (A grid of one workgroup per possible unit spent
-// tens of microseconds launching workgroups that had nothing to do.)  The chunk's middle-region tokens are
-// contiguous rows of one physical page; 64-token stages of K and V go
+// k_group_decode_mfma: an item is (unit of the union, token chunk of the
+// unit, pass) of one (sequence, KV head); a pass holds up to 128 query
+// columns.  Two schedules share the item code:
+//  * plan mode (after k_group_plan): one workgroup per (launch rank,
+//    (sequence, KV head), token chunk), all passes of its unit in turn; the
+//    plan's records are in launch order, the costliest units (tokens times
+//    rows) first;
+//  * prefill mode: persistent, one workgroup per CU slot; each builds the
+//    units of its (sequence, KV head)s in LDS and takes items from a
+//    per-(sequence, KV head) counter in that order, so the rows of a unit
+//    chosen by many rows are split over several workgroups.  (A grid of one
+//    workgroup per possible unit spent tens of microseconds launching
+//    workgroups that had nothing to do.)
+// The chunk's middle-region tokens are contiguous rows of one physical page; 64-token stages of K and V go
 // through LDS (three stages in flight in registers, two in LDS) and are read
 // by every wave.  Query columns are (row, head) pairs of the rows in the
 // mask, 16 per MFMA column block; each wave owns one column block per pass
