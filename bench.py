@@ -77,6 +77,9 @@ def parse():
                     help="semantic-512k: token chunks per page; semantic-prefill-64k: per block (0: default)")
     ap.add_argument("--iterations", type=int, default=8, help="semantic-512k-index: k-means iterations")
     ap.add_argument("--k-max", type=int, default=10, help="semantic-prefill-64k: most blocks a row takes")
+    ap.add_argument("--chunks-per-call", type=int, default=16,
+                    help="semantic-prefill-64k: consecutive chunks per sparse_attn_prefill_chunks call (1: one "
+                         "sparse_attn_prefill_chunk call per chunk)")
     ap.add_argument("--score", default="quest", choices=["quest", "mean", "centroid", "compressed"],
                     help="llama3-70b-layer-128k: page summary and score (compressed: mean keys of two-page "
                          "blocks with a one-page stride)")
@@ -757,8 +760,17 @@ def bench_prefill(args):
     # holds about 2 blocks of the average 2048 tokens; rows that reach the cap
     # are counted below), each block in 3 token chunks so that the few blocks
     # a chunk reads spread over the GPU; the dense run takes every block
-    pf = ChunkedPrefill(ix, T, W, k_max=min(C, args.k_max), token_splits=args.token_splits or 3)
-    pf_dense = ChunkedPrefill(ix, T, W, k_max=C, token_splits=1)
+    per = max(1, args.chunks_per_call)
+    pf = ChunkedPrefill(ix, T, W, k_max=min(C, args.k_max), token_splits=args.token_splits or 3, per_call=per)
+    pf_dense = ChunkedPrefill(ix, T, W, k_max=C, token_splits=1, per_call=per)
+    # one call per chunk, for the byte count's pass (its lists are the same bit for bit)
+    pf1 = pf if per == 1 else ChunkedPrefill(ix, T, W, k_max=pf.k_max, token_splits=pf.ts)
+    # the calls: consecutive chunks, their rows contiguous ([B][Hq][n * T][hd])
+    calls = []
+    for j0 in range(0, nch, per):
+        n = min(per, nch - j0)
+        qg = q_dev[j0:j0 + n].permute(1, 2, 0, 3, 4).contiguous().view(c.B, c.Hq, n * T, c.hd)
+        calls.append((j0, qg, [max(1, (j + 1) * T // 16) for j in range(j0, j0 + n)]))
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
@@ -790,11 +802,13 @@ def bench_prefill(args):
         ix.build(args.iterations)
 
     def chunks(dense):
-        for j in range(nch):
-            if dense:
-                pf_dense.chunk(q_dev[j], j * T, 10**9)
+        for j0, qg, budgets in calls:
+            if per == 1:
+                (pf_dense if dense else pf).chunk(q_dev[j0], j0 * T, 10**9 if dense else budgets[0])
+            elif dense:
+                pf_dense.chunks(qg, j0 * T, [10**9] * len(budgets))
             else:
-                pf.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
+                pf.chunks(qg, j0 * T, budgets)
 
     build()
     chunks(False)
@@ -814,10 +828,10 @@ def bench_prefill(args):
     chunk_bytes = 0
     at_cap = 0
     for j in range(nch):
-        pf.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
-        sel, cnt = pf.sel.cpu().numpy(), pf.count.cpu().numpy()
+        pf1.chunk(q_dev[j], j * T, max(1, (j + 1) * T // 16))
+        sel, cnt = pf1.sel.cpu().numpy(), pf1.count.cpu().numpy()
         at_cap += int((cnt == pf.k_max).sum())
-        ends, off = pf.ends.cpu().numpy(), ix.offsets.cpu().numpy()
+        ends, off = pf1.ends.cpu().numpy(), ix.offsets.cpu().numpy()
         vis_tok = 0
         for b in range(c.B):
             for h in range(c.Hkv):
@@ -875,7 +889,7 @@ def bench_prefill(args):
                 "V N(0,1), query rows around 4 topics per (b, kvh)",
         "config": {"workload": wl.name, "batch": c.B, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.hd,
                    "prompt": L, "chunk": T, "window": W, "blocks": C, "iterations": args.iterations,
-                   "k_max": pf.k_max, "token_splits": pf.ts,
+                   "k_max": pf.k_max, "token_splits": pf.ts, "chunks_per_call": per,
                    "budget": "1/16 of the chunk's length"},
         "index_build_ms": round(build_ms, 3), "sparse_chunks_ms": round(sparse_ms, 3),
         "dense_chunks_ms": None if args.only_timed else round(dense_ms, 3),

@@ -96,8 +96,11 @@ _SIGS = {
                                                       _P, ctypes.c_size_t, _P, _P, _P, _I, _P, _I, _P]),
     "sparse_attn_prefill_chunk": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                                                  _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "sparse_attn_prefill_chunks": (ctypes.c_int, [_DESC, _IDX, _P, _I, _I, _I, _P, _I, ctypes.c_float, _I, _P, _P,
+                                                  _P, _P, _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "sparse_attn_prefill_num_splits": (ctypes.c_int32, [_DESC, _I, _I, _I]),
     "sparse_attn_prefill_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX]),
+    "sparse_attn_prefill_chunks_workspace_bytes": (ctypes.c_size_t, [_DESC, _IDX, _I]),
     "sparse_attn_keydiff_workspace_bytes": (ctypes.c_size_t, [_DESC, _I, _I]),
     "sparse_attn_keydiff_select": (ctypes.c_int, [_DESC, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "sparse_attn_keydiff_compact": (ctypes.c_int, [_DESC, _P, _P, _I, _DESC, _P]),
@@ -353,6 +356,24 @@ def sparse_attn_prefill_chunk(kv: sa_kv_desc, index: sa_block_index, q, num_q_ro
                                           _ptr(sel_blocks), _ptr(sel_count), _ptr(part_o), _ptr(part_ml), _ptr(out),
                                           out_dtype, _ptr(lse), advance, _ptr(workspace), workspace_bytes,
                                           _stream(stream)), "sparse_attn_prefill_chunk")
+
+
+def sparse_attn_prefill_chunks_workspace_bytes(kv: sa_kv_desc, index: sa_block_index, num_chunks: int) -> int:
+    return int(_lib.sparse_attn_prefill_chunks_workspace_bytes(ctypes.byref(kv), ctypes.byref(index), num_chunks))
+
+
+def sparse_attn_prefill_chunks(kv: sa_kv_desc, index: sa_block_index, q, num_q_rows: int, num_chunks: int,
+                               window_len: int, token_budgets, k_max: int, softmax_scale: float, token_splits: int,
+                               visible_end, sel_blocks, sel_count, part_o, part_ml, out, out_dtype: int, lse,
+                               advance: int, workspace, workspace_bytes: int, stream=None) -> None:
+    """token_budgets: a sequence of num_chunks ints (passed as a host array)."""
+    budgets = (ctypes.c_int32 * max(1, len(token_budgets)))(*[int(x) for x in token_budgets])
+    _check(_lib.sparse_attn_prefill_chunks(ctypes.byref(kv), ctypes.byref(index), _ptr(q), num_q_rows, num_chunks,
+                                           window_len, ctypes.addressof(budgets), k_max, softmax_scale,
+                                           token_splits, _ptr(visible_end), _ptr(sel_blocks), _ptr(sel_count),
+                                           _ptr(part_o), _ptr(part_ml), _ptr(out), out_dtype, _ptr(lse), advance,
+                                           _ptr(workspace), workspace_bytes, _stream(stream)),
+           "sparse_attn_prefill_chunks")
 
 
 def sparse_attn_status_string(status: int) -> str:

@@ -79,9 +79,10 @@ __device__ __forceinline__ int gvt_off(int t, int b)
 // the (sequence, KV head)'s candidate range from its length
 struct Regions {
     int L, se, ws, plo, phi;
-    __device__ __forceinline__ Regions(const Geometry& g, int b, int S, int W)
+    // extra: tokens past the sequence's length (a later prefill chunk of the same call)
+    __device__ __forceinline__ Regions(const Geometry& g, int b, int S, int W, int extra = 0)
     {
-        L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+        L = imax(0, imin(g.seq_lens[b] + extra, g.max_pages * g.P));
         se = imin(S, L);
         ws = imax(se, L - W);
         plo = se / g.P;
@@ -238,33 +239,35 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
 
     const Geometry& g = a.g;
     const int nbk = g.B * g.Hkv;
+    const int QS = a.Q * a.nck;  // row stride of q and the partials (a.Q rows per chunk)
     const int lane = threadIdx.x & 63, wave = wave_index();
     const int r = lane & 15, j = lane >> 4;
     constexpr bool prefill = PF;  // prefill mode (persistent), else plan mode
 
     // One item: passes pidx, pidx + np, ... of token chunk s (of nch) of unit
-    // u of (sequence, KV head) bk.  Units: the plan's records in order, or
-    // in prefill mode the window's pages (u < nwin) and then the index's
-    // blocks (block u - nwin).
+    // u of (prompt chunk, sequence, KV head) vb (vb = bk in plan mode).
+    // Units: the plan's records in order, or in prefill mode the window's
+    // pages (u < nwin) and then the index's blocks (block u - nwin).
     int next_item = -1;  // thread 0: the next item's index, when the item fetched it
     // each lane's two rows' list index of unit u (-1: the row does not attend it)
-    auto load_slots = [&](const int bk, const int u, int16_t& slot0, int16_t& slot1) {
+    auto load_slots = [&](const int vb, const int u, int16_t& slot0, int16_t& slot1) {
         slot0 = -1;
         slot1 = -1;
         if (!prefill) {
-            const long ui = (long)bk * a.npg + u;
+            const long ui = (long)vb * a.npg + u;
             slot0 = a.slots[ui * kGroupMaxRows + lane];
             slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
         } else if (u >= a.nwin) {
-            const long ui = (long)bk * a.npg + (u - a.nwin);
+            const long ui = (long)vb * a.npg + (u - a.nwin);
             if (lane < a.Q) slot0 = a.slots[ui * kGroupMaxRows + lane];
             if (64 + lane < a.Q) slot1 = a.slots[ui * kGroupMaxRows + 64 + lane];
         }
     };
-    auto process = [&](const int bk, const int u, const int s, const int pidx, const int np, const int nch,
+    auto process = [&](const int vb, const int u, const int s, const int pidx, const int np, const int nch,
                        const int a0, const int a1, const int x, int16_t slot0, int16_t slot1) {
-        const int b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-        const Regions rg(g, b, a.S, a.W);
+        const int ck = vb / nbk, bk = vb - ck * nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+        const int rb = ck * a.Q;  // the chunk's first row
+        const Regions rg(g, b, a.S, a.W, rb);
         const bool win = prefill && u < a.nwin;  // a page of the rows' window (prefill)
         const bool blocks = a.blk_off != nullptr && !win;
         const int phys = blocks ? 0 : x;
@@ -339,14 +342,14 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             if (pidx == 0) {
                 for (int e2 = threadIdx.x; e2 < nout * G; e2 += 64 * kGW) {
                     const int row = e2 / G, h = e2 - row * G;
-                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * QS + rb + row;
                     const long slot = prow * a.split_stride + (long)ws * a.tsplit + s;
                     *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
                 }
                 const int nx = s == 0 ? a.tsplit - nch : 0;
                 for (int e2 = threadIdx.x; e2 < a.Q * G * nx; e2 += 64 * kGW) {
                     const int row = e2 / (G * nx), rest = e2 - row * (G * nx), h = rest / nx, s2 = nch + rest % nx;
-                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + row;
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * QS + rb + row;
                     const long slot = prow * a.split_stride + (long)ws * a.tsplit + s2;
                     *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
                 }
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             const int nx = a.tsplit - nch;
             for (int e2 = threadIdx.x; e2 < nr * G * nx; e2 += 64 * kGW) {
                 const int ri = e2 / (G * nx), rest = e2 - ri * (G * nx), h = rest / nx, s2 = nch + rest % nx;
-                const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + rows_l[ri];
+                const long prow = ((long)b * g.Hq + kvh * G + h) * QS + rb + rows_l[ri];
                 const long slot = prow * a.split_stride + (long)slot_l[ri] * a.tsplit + s2;
                 *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
             }
@@ -415,8 +418,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 for (int kk = 0; kk < KK; ++kk) {
                     uint4 w = make_uint4(0, 0, 0, 0);
                     if (live)
-                        w = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD +
-                                            32 * kk + 8 * j);
+                        w = *(const uint4*)((const uint16_t*)a.q +
+                                            (((long)b * g.Hq + kvh * G + h) * QS + rb + row) * HD + 32 * kk + 8 * j);
                     qb[kk] = __builtin_bit_cast(gbf16x8_t, w);
                 }
     #pragma unroll
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 __syncthreads();  // buffers 0 and 1 are free for the next round
             }
             // the next item's index, taken while this one merges
-            if (prefill && threadIdx.x == 0 && (pass + np) * kGW >= ncb) next_item = atomicAdd(a.ctr + bk, 1);
+            if (prefill && threadIdx.x == 0 && (pass + np) * kGW >= ncb) next_item = atomicAdd(a.ctr + vb, 1);
 
             // Merge the states of a block's waves (group order) through LDS,
             // then the first wave of each block writes its partials.  Lane (r, j)
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                     }
                     const int col = 16 * cb + qc, ri = col / G, h = col - ri * G;
                     if (ri >= nr) continue;
-                    const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + rows_l[ri];
+                    const long prow = ((long)b * g.Hq + kvh * G + h) * QS + rb + rows_l[ri];
                     const long slot = prow * a.split_stride + (long)slot_l[ri] * a.tsplit + s;
                     const float inv = ls > 0.f ? 1.0f / ls : 0.f;
     #pragma unroll
@@ -615,23 +618,24 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
     __shared__ int s_item;
 
     // Persistent schedule: one workgroup per CU, in columns of 8 (one per
-    // XCD); column col serves (sequence, KV head)s col, col + ncol, ... (or
-    // col mod B*Hkv when there are fewer of them than columns).  The
-    // workgroups of a (sequence, KV head) take its items (unit, token chunk,
-    // pass) in the units' launch order (costliest first) from a counter the
-    // kernel before this one cleared, so none waits for work another could
-    // do and none is launched without work.  A unit has one pass per
+    // XCD); column col serves (prompt chunk, sequence, KV head)s col, col +
+    // ncol, ... (or col mod their number when there are fewer of them than
+    // columns).  The workgroups of a (chunk, sequence, KV head) take its
+    // items (unit, token chunk, pass) in the units' launch order (costliest
+    // first) from a counter the kernel before this one cleared, so none waits
+    // for work another could do and none is launched without work.  A unit has one pass per
     // kGroupPassCols query columns of its rows and up to tsplit token chunks
     // of at least kGroupChunkMin tokens.
     const int tid = threadIdx.x;
     const int ncol = gridDim.x >> 3, col = blockIdx.x >> 3;
-    const int bk0 = nbk >= ncol ? col : col % nbk, bstep = nbk >= ncol ? ncol : nbk;
-    for (int bk = bk0; bk < nbk; bk += bstep) {
+    const int nvb = nbk * a.nck;  // (prompt chunk, sequence, KV head)s
+    const int vb0 = nvb >= ncol ? col : col % nvb, vstep = nvb >= ncol ? ncol : nvb;
+    for (int vb = vb0; vb < nvb; vb += vstep) {
         // the first item's index is fetched with the units' loads: its round
         // trip overlaps theirs
-        const int first_item = tid == 0 ? atomicAdd(a.ctr + bk, 1) : -1;
-        const int b = bk / g.Hkv;
-        const Regions rg(g, b, a.S, a.W);
+        const int first_item = tid == 0 ? atomicAdd(a.ctr + vb, 1) : -1;
+        const int ck = vb / nbk, bk = vb - ck * nbk, b = bk / g.Hkv;
+        const Regions rg(g, b, a.S, a.W, ck * a.Q);
         // the units, loads in one round
         const int nu = a.nwin + a.npg;
         const int wstart = imax(0, rg.L - a.W);
@@ -648,8 +652,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 const int c = u - a.nwin;
                 const int32_t* bo = a.blk_off + (long)bk * (a.npg + 1);
                 x0 = bo[c];
-                x1 = imax(x0, imin(a.blk_end[(long)bk * a.npg + c], bo[c + 1]));
-                const uint4 cr = *(const uint4*)(a.pf_rows + ((long)bk * a.npg + c) * 16);
+                x1 = imax(x0, imin(a.blk_end[(long)vb * a.npg + c], bo[c + 1]));
+                const uint4 cr = *(const uint4*)(a.pf_rows + ((long)vb * a.npg + c) * 16);
                 const uint32_t w4[4] = {cr.x, cr.y, cr.z, cr.w};
                 nrows = 0;
 #pragma unroll
@@ -740,7 +744,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
 
         next_item = first_item;
         for (;;) {
-            if (tid == 0) s_item = next_item >= 0 ? next_item : atomicAdd(a.ctr + bk, 1);
+            if (tid == 0) s_item = next_item >= 0 ? next_item : atomicAdd(a.ctr + vb, 1);
             __syncthreads();
             const int it = s_item;
             next_item = -1;
@@ -759,8 +763,8 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             const int u = u_ord[lo];
             const int np = u_np[u], nch = u_nch[u], kk = it - item_pre[lo];
             int16_t slot0, slot1;
-            load_slots(bk, u, slot0, slot1);
-            process(bk, u, kk / np, kk % np, np, nch, u_a0[u], u_a1[u], u_x[u], slot0, slot1);
+            load_slots(vb, u, slot0, slot1);
+            process(vb, u, kk / np, kk % np, np, nch, u_a0[u], u_a1[u], u_x[u], slot0, slot1);
             __syncthreads();  // LDS of this item is no longer read
         }
     }
@@ -787,7 +791,8 @@ hipError_t launch_group_g(const GroupArgs& a, dim3 grid, hipStream_t s)
 hipError_t launch_group(const GroupArgs& a, int max_union, hipStream_t s)
 {
     const Geometry& g = a.g;
-    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || a.pf_rows) return hipErrorInvalidValue;
+    if (g.dtype != 1 || a.Q > kGroupMaxRows || a.npg > kGroupMaxPages || a.pf_rows || a.nck != 1)
+        return hipErrorInvalidValue;
     const size_t lds = (2 * sizeof(unsigned long long) + sizeof(int)) * (size_t)a.npg;
     hipLaunchKernelGGL(k_group_plan, dim3((unsigned)(g.B * g.Hkv)), dim3(kPlanThreads), lds, s, a);
     hipError_t e = hipGetLastError();
@@ -802,7 +807,7 @@ hipError_t launch_group_prefill(const GroupArgs& a, int workgroups, hipStream_t 
 {
     const Geometry& g = a.g;
     if (g.dtype != 1 || a.Q > kGroupMaxRows || a.nwin + a.npg > kGroupMaxPages || !a.pf_rows || !a.blk_off ||
-        !a.blk_end || a.nwin < 1 || !a.ctr || workgroups < 8 || workgroups % 8)
+        !a.blk_end || a.nwin < 1 || !a.ctr || workgroups < 8 || workgroups % 8 || a.nck < 1 || a.nck > kPfMaxChunks)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)workgroups);
     if (g.hd == 128) return launch_group_g<128, true>(a, grid, s);

@@ -162,8 +162,13 @@ struct GroupArgs {
     // then the blocks, each attended by the rows whose slot in
     // slots[b][kvh][block][row] is >= 0 (the slot table is indexed by block)
     int nwin;                      // window units per (sequence, KV head)
-    const unsigned char* pf_rows;  // [B][Hkv][npg][16] rows of each row group of 8 that chose each block
-    int32_t* ctr;                  // [B][Hkv] prefill: item counters, zero when the decode starts
+    const unsigned char* pf_rows;  // [nck][B][Hkv][npg][16] rows of each row group of 8 that chose each block
+    int32_t* ctr;                  // [nck][B][Hkv] prefill: item counters, zero when the decode starts
+    // prefill: chunks of Q rows in the call (1 otherwise); chunk j's rows are
+    // rows j*Q .. of q and the partials (row stride nck*Q), its length
+    // seq_lens[b] + j*Q, and slots, pf_rows, blk_end and ctr hold one copy
+    // per chunk (index vb = j * B * Hkv + bk)
+    int nck;
 };
 
 // Query columns (row, head) of one pass of a grouped-decode workgroup (16 per
@@ -259,22 +264,28 @@ constexpr int kKdMaxChunks = 16;  // chunks of the two-stage eviction (131072 ca
 // The front of a sparse prefill chunk over a block index: visible ends,
 // block choice of every row and the grouped decode's slot table.
 constexpr int kPfMaxBlocks = 512;  // index blocks the front holds (8 block keys per lane)
+// One call serves nck consecutive chunks of Q rows: chunk j's rows are rows
+// j*Q .. j*Q + Q-1 of the row dimension (nck*Q rows of q, lists and
+// partials), its length is seq_lens[b] + j*Q, and its per-chunk arrays are
+// indexed by vb = j * B * Hkv + b * Hkv + kvh.
+constexpr int kPfMaxChunks = 16;
 struct PrefillArgs {
     Geometry g;
-    const void* q;
-    int Q, N, C;
+    const void* q;             // [B][Hq][nck * Q][hd]
+    int Q, N, C, nck;
     const int32_t* offsets;    // [B][Hkv][C + 1]
     const int32_t* positions;  // [B][Hkv][N]
     const float* centres;      // [B][Hkv][C][hd]
-    int budget, k_max, W;
+    int budget[kPfMaxChunks];  // token budget of each chunk
+    int k_max, W;
     int tsplit, split_stride;  // token chunks per block; partial slots per row
-    int32_t* ends;             // [B][Hkv][C] out: end row of each block's visible part
-    int32_t* sel;              // [B][Hkv][Q][k_max] out
-    int32_t* count;            // [B][Hkv][Q] out
-    int16_t* slots;            // [B][Hkv][C][kGroupMaxRows] out: each row's list index of each block, -1 if not chosen
+    int32_t* ends;             // [nck][B][Hkv][C] out: end row of each block's visible part
+    int32_t* sel;              // [B][Hkv][nck * Q][k_max] out
+    int32_t* count;            // [B][Hkv][nck * Q] out
+    int16_t* slots;            // [nck][B][Hkv][C][kGroupMaxRows] out: each row's list index of each block, -1 if not chosen
     float* part_ml;            // the (m, l) of the list slots a row leaves unused are set empty
-    unsigned char* rows;       // [B][Hkv][C][16] out: rows of each row group of 8 that chose each block (0 past the groups)
-    int32_t* ctr;              // [B][Hkv] the grouped decode's item counters, cleared here
+    unsigned char* rows;       // [nck][B][Hkv][C][16] out: rows of each row group of 8 that chose each block (0 past the groups)
+    int32_t* ctr;              // [nck][B][Hkv] the grouped decode's item counters, cleared here
 };
 
 struct CompactArgs {

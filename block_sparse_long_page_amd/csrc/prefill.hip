@@ -5,9 +5,10 @@
 // the blocks that precede the chunk's window; the window, the chunk's own
 // recent tokens, is attended without selection).
 //
-// k_prefill_choose: one workgroup per 8 rows of one (sequence, KV head), a
-// wave per row, in one launch with no other kernel before the grouped
-// decode:
+// k_prefill_choose: one workgroup per 8 rows of one (chunk, sequence, KV
+// head), a wave per row, in one launch with no other kernel before the
+// grouped decode (a call may serve several consecutive chunks of the prompt,
+// each with its own length and budget):
 //  * the visible part of every block (its rows of positions < L - W;
 //    positions ascend inside a block, so the part is a prefix): a k-ary
 //    search by a team of T lanes per block, T probes a round narrowing the
@@ -52,10 +53,14 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
     const Geometry& g = a.g;
     const int C = a.C, N = a.N;
     const int ngr = (a.Q + kPfWaves - 1) / kPfWaves;
-    const int grp = blockIdx.x % ngr, bk = blockIdx.x / ngr, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+    const int nbk = g.B * g.Hkv;
+    const int grp = blockIdx.x % ngr, vb = blockIdx.x / ngr;  // vb: (chunk, sequence, KV head)
+    const int ck = vb / nbk, bk = vb - ck * nbk, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
+    const int QS = a.Q * a.nck, row0 = ck * a.Q;  // row stride of q, lists and partials; the chunk's first row
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
-    const int L = imax(0, imin(g.seq_lens[b], g.max_pages * g.P));
+    const int L = imax(0, imin(g.seq_lens[b] + row0, g.max_pages * g.P));
     const int bound = L - a.W;
+    const int budget = a.budget[ck];
     const int32_t* off = a.offsets + (long)bk * (C + 1);
     const int32_t* pos = a.positions + (long)bk * N;
 
@@ -66,14 +71,15 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
         const int row = grp * kPfWaves + w;
         uint4 u = make_uint4(0, 0, 0, 0);
         if (row < a.Q)
-            u = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * a.Q + row) * HD + 8 * d8);
+            u = *(const uint4*)((const uint16_t*)a.q + (((long)b * g.Hq + kvh * G + h) * QS + row0 + row) * HD +
+                                8 * d8);
         float4* dst = (float4*)&qs[w][h][8 * d8];
         dst[0] = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
         dst[1] = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
     }
     for (int c = tid; c <= C; c += kPfThreads) off_l[c] = imax(0, imin(off[c], N));
     for (int c = tid; c < C; c += kPfThreads) nch[c] = 0;
-    if (grp == 0 && tid == 0) a.ctr[bk] = 0;  // the grouped decode's item counter
+    if (grp == 0 && tid == 0) a.ctr[vb] = 0;  // the grouped decode's item counter
     __syncthreads();
 
     // Visible ends: block c's rows are [off_l[c], max(off_l[c], off_l[c+1]));
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
         }
         if (k == 0) {
             size_l[c] = end - off_l[c];
-            if (grp == 0) a.ends[(long)bk * C + c] = end;
+            if (grp == 0) a.ends[(long)vb * C + c] = end;
         }
     }
     __syncthreads();
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
             const uint32_t ml = wave_max_u32(bh == mh ? (uint32_t)best : 0u);
             const int c = (int)(0xffffffffu - ml);
             const int sz = size_l[c];
-            if (count > 0 && (count >= a.k_max || run + sz > a.budget)) break;
+            if (count > 0 && (count >= a.k_max || run + sz > budget)) break;
             run += sz;
             ++count;
     #pragma unroll
@@ -217,8 +223,8 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
         }
 
         // the list in block order, the slot table, the unused slots
-        int32_t* sel = a.sel + ((long)bk * a.Q + r) * a.k_max;
-        int16_t* slots = a.slots + (long)bk * C * kGroupMaxRows + r;
+        int32_t* sel = a.sel + ((long)bk * QS + row0 + r) * a.k_max;
+        int16_t* slots = a.slots + (long)vb * C * kGroupMaxRows + r;
         int base = 0;
     #pragma unroll
         for (int i = 0; i < kPfRounds; ++i) {
@@ -238,11 +244,11 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
             }
         }
         for (int j = count + lane; j < a.k_max; j += 64) sel[j] = -1;
-        if (lane == 0) a.count[(long)bk * a.Q + r] = count;
+        if (lane == 0) a.count[(long)bk * QS + row0 + r] = count;
         const int nempty = (a.k_max - count) * a.tsplit * G;
         for (int e = lane; e < nempty; e += 64) {
             const int h = e % G, rest = e / G, s = rest % a.tsplit, j = count + rest / a.tsplit;
-            const long prow = ((long)b * g.Hq + kvh * G + h) * a.Q + r;
+            const long prow = ((long)b * g.Hq + kvh * G + h) * QS + row0 + r;
             const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
             *(float2*)(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
         }
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill_choose(PrefillArgs a)
     // the first group also zeroes the entries past the last group
     __syncthreads();
     for (int c = tid; c < C; c += kPfThreads) {
-        unsigned char* rc = a.rows + ((long)bk * C + c) * 16;
+        unsigned char* rc = a.rows + ((long)vb * C + c) * 16;
         rc[grp] = (unsigned char)nch[c];
         if (grp == 0)
             for (int q8 = ngr; q8 < 16; ++q8) rc[q8] = 0;
@@ -278,9 +284,10 @@ hipError_t choose_g(const PrefillArgs& a, dim3 grid, hipStream_t s)
 
 hipError_t launch_prefill_choose(const PrefillArgs& a, hipStream_t s)
 {
-    if (a.g.dtype != 1 || a.C < 1 || a.C > kPfMaxBlocks || a.Q < 1 || a.Q > kGroupMaxRows || a.k_max < 1)
+    if (a.g.dtype != 1 || a.C < 1 || a.C > kPfMaxBlocks || a.Q < 1 || a.Q > kGroupMaxRows || a.k_max < 1 ||
+        a.nck < 1 || a.nck > kPfMaxChunks)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((long)a.g.B * a.g.Hkv * ((a.Q + kPfWaves - 1) / kPfWaves)));
+    const dim3 grid((unsigned)((long)a.nck * a.g.B * a.g.Hkv * ((a.Q + kPfWaves - 1) / kPfWaves)));
     if (a.g.hd == 128) return choose_g<128>(a, grid, s);
     if (a.g.hd == 64) return choose_g<64>(a, grid, s);
     return hipErrorInvalidValue;

@@ -211,10 +211,11 @@ GroupedWs grouped_ws(const sa_kv_desc* kv, long npg)
 struct PrefillWs {
     size_t slots, rows, ctr, total;
 };
-PrefillWs prefill_ws(const sa_kv_desc* kv, long C)
+// nck: prompt chunks per call (each has its own slot table, row counts and counters)
+PrefillWs prefill_ws(const sa_kv_desc* kv, long C, long nck = 1)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t bh = (size_t)kv->batch * kv->num_kv_heads;
+    const size_t bh = (size_t)kv->batch * kv->num_kv_heads * nck;
     PrefillWs w;
     w.slots = 0;
     w.rows = up(bh * (size_t)C * sa::kGroupMaxRows * sizeof(int16_t));
@@ -612,7 +613,7 @@ int grouped_impl(const sa_kv_desc* kv, const sa::Geometry& g, const void* q, int
                         (int)stride, part_o,    part_ml,    (int32_t*)(base + w.nunion),
                         (sa::GroupPage*)(base + w.upages), (int16_t*)(base + w.slots),
                         npg,        blk_off,    blk_k,      blk_v,   blk_n,
-                        blk_end};
+                        blk_end,    0,          nullptr,    nullptr, 1};
         const int r1 = finish(sa::launch_group(a, (int)max_union, stream), stream);
         if (r1 != SA_OK) return r1;
     }
@@ -777,25 +778,42 @@ int32_t sparse_attn_prefill_num_splits(const sa_kv_desc* kv, int32_t window_len,
 
 size_t sparse_attn_prefill_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index)
 {
-    if (!kv || !index || kv->batch < 1 || kv->num_kv_heads < 1 || index->num_blocks < 1) return 0;
-    return prefill_ws(kv, index->num_blocks).total;
+    return sparse_attn_prefill_chunks_workspace_bytes(kv, index, 1);
 }
 
-int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
-                              int32_t window_len, int32_t token_budget, int32_t k_max, float softmax_scale,
-                              int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks, int32_t* sel_count,
-                              float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
-                              int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream)
+size_t sparse_attn_prefill_chunks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index,
+                                                  int32_t num_chunks)
+{
+    if (!kv || !index || kv->batch < 1 || kv->num_kv_heads < 1 || index->num_blocks < 1 || num_chunks < 1 ||
+        num_chunks > sa::kPfMaxChunks)
+        return 0;
+    return prefill_ws(kv, index->num_blocks, num_chunks).total;
+}
+
+namespace {
+
+// num_chunks consecutive chunks of num_q_rows rows (rows j * num_q_rows ..
+// of q, the lists and the partials for chunk j, whose length is
+// seq_lens[b] + j * num_q_rows), token_budgets[j] each
+int prefill_impl(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                 int32_t num_chunks, int32_t window_len, const int32_t* token_budgets, int32_t k_max,
+                 float softmax_scale, int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks,
+                 int32_t* sel_count, float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
+                 int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     sa::Geometry g;
     const int rc = check_kv(kv, &g);
     if (rc != SA_OK) return rc;
     const int ri = check_index(kv, index);
     if (ri != SA_OK) return ri;
-    if (!q || !visible_end || !sel_blocks || !sel_count || !part_o || !part_ml || !out) return SA_ERR_INVALID_ARG;
-    if (num_q_rows < 1 || num_q_rows > kv->max_seq_len || window_len < num_q_rows || token_budget < 0 ||
+    if (!q || !visible_end || !sel_blocks || !sel_count || !part_o || !part_ml || !out || !token_budgets)
+        return SA_ERR_INVALID_ARG;
+    if (num_chunks < 1 || num_chunks > sa::kPfMaxChunks) return SA_ERR_INVALID_ARG;
+    if (num_q_rows < 1 || (long)num_q_rows * num_chunks > kv->max_seq_len || window_len < num_q_rows ||
         advance < 0)
         return SA_ERR_INVALID_ARG;
+    for (int jc = 0; jc < num_chunks; ++jc)
+        if (token_budgets[jc] < 0) return SA_ERR_INVALID_ARG;
     if (k_max < 1 || k_max > index->num_blocks) return SA_ERR_INVALID_ARG;
     if (token_splits < 1 || token_splits > kMaxTokenSplits) return SA_ERR_INVALID_ARG;
     if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return SA_ERR_INVALID_ARG;
@@ -806,10 +824,11 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
     if (stride < 0) return -stride;
     const long nwin = prefill_window_units(window_len, kv->page_size);
     const long nbk = (long)kv->batch * kv->num_kv_heads, C = index->num_blocks;
-    const long rows = (long)kv->batch * kv->num_q_heads * num_q_rows;
+    const long rows = (long)kv->batch * kv->num_q_heads * num_q_rows * num_chunks;
     if (nwin + C > sa::kGroupMaxPages) return SA_ERR_UNSUPPORTED;
-    if (!grid_fits(nbk * ((num_q_rows + 7) / 8), kDecodeThreads) || !grid_fits(rows, 64)) return SA_ERR_UNSUPPORTED;
-    const PrefillWs w = prefill_ws(kv, C);
+    if (!grid_fits(nbk * num_chunks * ((num_q_rows + 7) / 8), kDecodeThreads) || !grid_fits(rows, 64))
+        return SA_ERR_UNSUPPORTED;
+    const PrefillWs w = prefill_ws(kv, C, num_chunks);
     if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0) return SA_ERR_INVALID_ARG;
     char* base = (char*)workspace;
     int16_t* slots = (int16_t*)(base + w.slots);
@@ -817,9 +836,28 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
     int32_t* ctr = (int32_t*)(base + w.ctr);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)kv->head_dim);
 
-    sa::PrefillArgs f{g,          q,      num_q_rows,  index->num_tokens, (int)C, index->offsets, index->positions,
-                      index->centres, token_budget, k_max, window_len, token_splits, stride, visible_end,
-                      sel_blocks, sel_count, slots,  part_ml,     chosen_rows, ctr};
+    sa::PrefillArgs f{};
+    f.g = g;
+    f.q = q;
+    f.Q = num_q_rows;
+    f.N = index->num_tokens;
+    f.C = (int)C;
+    f.nck = num_chunks;
+    f.offsets = index->offsets;
+    f.positions = index->positions;
+    f.centres = index->centres;
+    for (int jc = 0; jc < num_chunks; ++jc) f.budget[jc] = token_budgets[jc];
+    f.k_max = k_max;
+    f.W = window_len;
+    f.tsplit = token_splits;
+    f.split_stride = stride;
+    f.ends = visible_end;
+    f.sel = sel_blocks;
+    f.count = sel_count;
+    f.slots = slots;
+    f.part_ml = part_ml;
+    f.rows = chosen_rows;
+    f.ctr = ctr;
     const int r1 = finish(sa::launch_prefill_choose(f, stream), stream);
     if (r1 != SA_OK) return r1;
     sa::GroupArgs d{};
@@ -844,11 +882,37 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
     d.nwin = (int)nwin;
     d.pf_rows = chosen_rows;
     d.ctr = ctr;
+    d.nck = num_chunks;
     const int r2 = finish(sa::launch_group_prefill(d, group_grid(kv->head_dim, g.G), stream), stream);
     if (r2 != SA_OK) return r2;
     sa::CombineArgs m{(int)rows, kv->head_dim, stride, out_dtype, part_o, part_ml, out, lse,
                       advance > 0 ? (int32_t*)kv->seq_lens : nullptr, kv->batch, advance};
     return finish(sa::launch_combine(m, stream), stream);
+}
+
+}  // namespace
+
+int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                              int32_t window_len, int32_t token_budget, int32_t k_max, float softmax_scale,
+                              int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks, int32_t* sel_count,
+                              float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
+                              int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_impl(kv, index, q, num_q_rows, 1, window_len, &token_budget, k_max, softmax_scale, token_splits,
+                        visible_end, sel_blocks, sel_count, part_o, part_ml, out, out_dtype, lse, advance, workspace,
+                        workspace_bytes, stream);
+}
+
+int sparse_attn_prefill_chunks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                               int32_t num_chunks, int32_t window_len, const int32_t* token_budgets, int32_t k_max,
+                               float softmax_scale, int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks,
+                               int32_t* sel_count, float* part_o, float* part_ml, void* out, int32_t out_dtype,
+                               float* lse, int32_t advance, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    return prefill_impl(kv, index, q, num_q_rows, num_chunks, window_len, token_budgets, k_max, softmax_scale,
+                        token_splits, visible_end, sel_blocks, sel_count, part_o, part_ml, out, out_dtype, lse,
+                        advance, workspace, workspace_bytes, stream);
 }
 
 int sparse_attn_decode_grouped(const sa_kv_desc* kv, const void* q, int32_t num_q_rows, const int32_t* sel_pages,

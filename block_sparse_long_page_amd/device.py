@@ -379,37 +379,43 @@ class ChunkedPrefill:
     front, the grouped decode of the blocks and the window's pages, the
     combine); fused=False: sparse_attn_blocks_visible,
     sparse_attn_select_blocks, sparse_attn_decode_blocks (the window by the
-    per-row decode) and sparse_attn_combine_advance."""
+    per-row decode) and sparse_attn_combine_advance.  per_call > 1 (fused):
+    chunks() runs up to that many consecutive chunks in one
+    sparse_attn_prefill_chunks call (the same results as one call each)."""
 
     def __init__(self, ix: "BlockIndex", Q: int, window: int, k_max: Optional[int] = None, token_splits: int = 1,
-                 local_splits: int = 1, out_dtype: Optional[int] = None, fused: bool = True):
+                 local_splits: int = 1, out_dtype: Optional[int] = None, fused: bool = True, per_call: int = 1):
         c = ix.c
         self.ix, self.c, self.Q, self.window, self.fused = ix, c, Q, window, fused
+        self.per_call = per_call if fused else 1
         self.k_max = k_max or ix.C
         self.ts, self.ls = token_splits, local_splits
         dev = c.k.device
-        self.ends = torch.zeros((c.B, c.Hkv, ix.C), dtype=torch.int32, device=dev)
+        n = self.per_call
+        # visible ends: [B][Hkv][C], or [per_call][B][Hkv][C] per chunk of a call
+        self.ends = torch.zeros(((n,) if n > 1 else ()) + (c.B, c.Hkv, ix.C), dtype=torch.int32, device=dev)
         self.index = B.make_block_index(num_tokens=ix.N, num_blocks=ix.C, offsets=ix.offsets,
                                         positions=ix.positions, centres=ix.centres, k_blocks=ix.k_blocks,
                                         v_blocks=ix.v_blocks, visible_end=None if fused else self.ends)
         self.desc = c.desc()
         self.rows = c.B * c.Hq * Q
-        self.sel = torch.full((c.B, c.Hkv, Q, self.k_max), -1, dtype=torch.int32, device=dev)
-        self.count = torch.zeros((c.B, c.Hkv, Q), dtype=torch.int32, device=dev)
+        self.sel = torch.full((c.B, c.Hkv, n * Q, self.k_max), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((c.B, c.Hkv, n * Q), dtype=torch.int32, device=dev)
+        self.last_n = 1  # chunks of the last call
         if fused:
             self.stride = B.sparse_attn_prefill_num_splits(self.desc, window, self.k_max, self.ts)
             if self.stride < 0:
                 raise B.SparseAttnError(-self.stride, "sparse_attn_prefill_num_splits")
-            self.ws_bytes = B.sparse_attn_prefill_workspace_bytes(self.desc, self.index)
+            self.ws_bytes = B.sparse_attn_prefill_chunks_workspace_bytes(self.desc, self.index, n)
         else:
             self.stride = self.k_max * self.ts + self.ls
             self.ws_bytes = B.sparse_attn_blocks_workspace_bytes(self.desc, self.index)
         self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
-        self.part_o = torch.empty((self.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
-        self.part_ml = torch.empty((self.rows, self.stride, 2), dtype=torch.float32, device=dev)
+        self.part_o = torch.empty((n * self.rows, self.stride, c.hd), dtype=torch.float32, device=dev)
+        self.part_ml = torch.empty((n * self.rows, self.stride, 2), dtype=torch.float32, device=dev)
         self.out_dtype = c.dtype if out_dtype is None else out_dtype
-        self.out = torch.empty((self.rows, c.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
-        self.lse = torch.empty((self.rows,), dtype=torch.float32, device=dev)
+        self.out = torch.empty((n * self.rows, c.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
+        self.lse = torch.empty((n * self.rows,), dtype=torch.float32, device=dev)
 
     def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
         """The rows [c0, c0 + Q) of the prompt.  The sequences' length must
@@ -433,16 +439,37 @@ class ChunkedPrefill:
             B.sparse_attn_combine_advance(self.rows, self.c.hd, self.stride, self.part_o, self.part_ml, self.out,
                                           self.out_dtype, self.lse, self.c.seq_lens, self.c.B, self.Q, stream)
         self.c.known_len = c0 + 2 * self.Q  # what the lengths read once the queued work has run
+        self.last_n = 1
+        return self.out
+
+    def chunks(self, q: torch.Tensor, c0: int, budgets, stream=None):
+        """len(budgets) <= per_call consecutive chunks from row c0 in one call:
+        q is [B][Hq][n * Q][hd] (chunk j's rows at j*Q), budgets[j] chunk j's
+        token budget.  Outputs and lengths as n chunk() calls leave them, with
+        the rows of every chunk: out, lse, sel and count hold the call's
+        [..][n * Q][..] layout from their first element (out_f32, lse_f32)."""
+        n = len(budgets)
+        assert self.fused and 1 <= n <= self.per_call
+        if self.c.known_len != c0 + self.Q:
+            with on_stream(stream):
+                self.c.seq_lens.fill_(c0 + self.Q)
+        B.sparse_attn_prefill_chunks(self.desc, self.index, q, self.Q, n, self.window, budgets, self.k_max, 0.0,
+                                     self.ts, self.ends, self.sel, self.count, self.part_o, self.part_ml, self.out,
+                                     self.out_dtype, self.lse, n * self.Q, self.ws, self.ws_bytes, stream)
+        self.c.known_len = c0 + (n + 1) * self.Q
+        self.last_n = n
         return self.out
 
     def out_f32(self) -> np.ndarray:
-        o = self.out.cpu().numpy()
+        n = self.last_n
+        o = self.out[: n * self.rows].cpu().numpy()
         if self.out_dtype == B.SA_BF16:
             o = (o.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
-        return o.reshape(self.c.B, self.c.Hq, self.Q, self.c.hd)
+        return o.reshape(self.c.B, self.c.Hq, n * self.Q, self.c.hd)
 
     def lse_f32(self) -> np.ndarray:
-        return self.lse.cpu().numpy().reshape(self.c.B, self.c.Hq, self.Q)
+        n = self.last_n
+        return self.lse[: n * self.rows].cpu().numpy().reshape(self.c.B, self.c.Hq, n * self.Q)
 
 
 class KeyDiffEviction:

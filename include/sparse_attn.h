@@ -517,6 +517,45 @@ int sparse_attn_prefill_chunk(const sa_kv_desc* kv, const sa_block_index* index,
                               float* part_o, float* part_ml, void* out, int32_t out_dtype, float* lse,
                               int32_t advance, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Several consecutive chunks of a prompt in one call: the same as
+ * num_chunks calls of sparse_attn_prefill_chunk, chunk j on rows
+ * j*num_q_rows .. (j+1)*num_q_rows - 1 at length L_b + j*num_q_rows (L_b =
+ * kv->seq_lens[b] when the call starts, chunk 0's rows included) with token
+ * budget token_budgets[j], and with the same results bit for bit; the three
+ * launches serve every chunk, so their fixed costs are paid once.  Chunks are
+ * independent once the index is built (each sees the index's tokens before
+ * its own window and attends its window causally).
+ *   q            [batch][num_q_heads][num_chunks * num_q_rows][head_dim], bf16
+ *   num_chunks   1..16
+ *   token_budgets  host array of num_chunks budgets (>= 0)
+ *   visible_end  out, int32 [num_chunks][batch][num_kv_heads][C]
+ *   sel_blocks, sel_count  out, [batch][num_kv_heads][num_chunks *
+ *                num_q_rows][k_max] and [..][num_chunks * num_q_rows]
+ *   part_o, part_ml  [batch * num_q_heads * num_chunks * num_q_rows]
+ *                [num_splits][head_dim] / [..][num_splits][2]
+ *   out, lse     [batch][num_q_heads][num_chunks * num_q_rows][head_dim] / [..]
+ *   advance      as in sparse_attn_prefill_chunk (num_chunks * num_q_rows to
+ *                chain calls)
+ *   workspace    >= sparse_attn_prefill_chunks_workspace_bytes(kv, index,
+ *                num_chunks) bytes, 256-byte aligned
+ * The rest as in sparse_attn_prefill_chunk.  The caller keeps L_b +
+ * num_chunks*num_q_rows within the cache (lengths past it are clamped).
+ * Errors: those of sparse_attn_prefill_chunk; SA_ERR_INVALID_ARG for
+ * num_chunks outside 1..16, a null token_budgets or a negative budget.
+ */
+int sparse_attn_prefill_chunks(const sa_kv_desc* kv, const sa_block_index* index, const void* q, int32_t num_q_rows,
+                               int32_t num_chunks, int32_t window_len, const int32_t* token_budgets, int32_t k_max,
+                               float softmax_scale, int32_t token_splits, int32_t* visible_end, int32_t* sel_blocks,
+                               int32_t* sel_count, float* part_o, float* part_ml, void* out, int32_t out_dtype,
+                               float* lse, int32_t advance, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Workspace bytes of sparse_attn_prefill_chunks for this index and chunk
+ * count (host only; 0 for bad sizes or num_chunks outside 1..16). */
+size_t sparse_attn_prefill_chunks_workspace_bytes(const sa_kv_desc* kv, const sa_block_index* index,
+                                                  int32_t num_chunks);
+
 /* Partial slots per row of sparse_attn_prefill_chunk: (k_max + the window's
  * pages, (window_len - 1) / page_size + 2) * token_splits; negative error
  * code for bad arguments or more than 1024 (host only). */

@@ -30,7 +30,8 @@ def test_exports_every_header_function():
         "sparse_attn_decode_step_static", "sparse_attn_combine_advance", "sparse_attn_prefill_chunk",
         "sparse_attn_prefill_num_splits", "sparse_attn_prefill_workspace_bytes", "sparse_attn_decode_merged",
         "sparse_attn_decode_step_merged", "sparse_attn_merge_counters", "sparse_attn_keydiff_compact_sums",
-        "sparse_attn_keydiff_select_carried", "sparse_attn_keydiff_slot_groups"}
+        "sparse_attn_keydiff_select_carried", "sparse_attn_keydiff_slot_groups", "sparse_attn_prefill_chunks",
+        "sparse_attn_prefill_chunks_workspace_bytes"}
     lib = B.library()
     for n in names:
         assert getattr(lib, n) is not None
@@ -480,6 +481,37 @@ def test_prefill_chunk_checks():
     assert chunk(desc=big, ix=_index(num_tokens=8192, num_blocks=600), kmax=600, ts=2) == B.SA_ERR_UNSUPPORTED
     for bad, code in BAD_DESCS:
         assert chunk(desc=_desc(**bad)) == code
+
+    # several chunks per call: one slot table, row-count table and counter per chunk
+    for n in (1, 3, 16):
+        assert lib.sparse_attn_prefill_chunks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix), n) == \
+            up(n * nbk * C * 128 * 2) + up(n * nbk * C * 16) + up(n * nbk * 4)
+    assert lib.sparse_attn_prefill_chunks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix), 0) == 0
+    assert lib.sparse_attn_prefill_chunks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix), 17) == 0
+    assert lib.sparse_attn_prefill_chunks_workspace_bytes(None, ctypes.byref(ix), 2) == 0
+    ws3 = lib.sparse_attn_prefill_chunks_workspace_bytes(ctypes.byref(d), ctypes.byref(ix), 3)
+
+    def chunks(**kw):
+        a = dict(desc=d, ix=ix, q=DEV, rows=2, n=3, W=4, budgets=[64, 64, 64], kmax=2, scale=0.0, ts=1, ends=DEV,
+                 sel=DEV, cnt=DEV, po=DEV, pml=DEV, out=DEV, odt=B.SA_BF16, lse=None, adv=0, ws=DEV, wsb=ws3)
+        a.update(kw)
+        bud = None if a["budgets"] is None else (ctypes.c_int32 * len(a["budgets"]))(*a["budgets"])
+        ixp = ctypes.byref(a["ix"]) if a["ix"] is not None else None
+        return lib.sparse_attn_prefill_chunks(ctypes.byref(a["desc"]), ixp, a["q"], a["rows"], a["n"], a["W"],
+                                              None if bud is None else ctypes.addressof(bud), a["kmax"], a["scale"],
+                                              a["ts"], a["ends"], a["sel"], a["cnt"], a["po"], a["pml"], a["out"],
+                                              a["odt"], a["lse"], a["adv"], a["ws"], a["wsb"], None)
+
+    assert chunks(budgets=None) == B.SA_ERR_INVALID_ARG
+    assert chunks(budgets=[64, -1, 64]) == B.SA_ERR_INVALID_ARG
+    assert chunks(n=0) == B.SA_ERR_INVALID_ARG
+    assert chunks(n=17, budgets=[1] * 17) == B.SA_ERR_INVALID_ARG
+    assert chunks(wsb=ws3 - 1) == B.SA_ERR_INVALID_ARG  # three chunks' tables
+    assert chunks(rows=64, n=3, W=64) == B.SA_ERR_INVALID_ARG  # 192 rows past the 128-token cache
+    for f in ("q", "ends", "sel", "cnt", "po", "pml", "out"):
+        assert chunks(**{f: None}) == B.SA_ERR_INVALID_ARG
+    for bad, code in BAD_DESCS:
+        assert chunks(desc=_desc(**bad)) == code
 
 
 def test_keydiff_checks():

@@ -182,3 +182,42 @@ def test_fused_prefill_is_bitwise_reproducible():
         outs.append((pf.out.clone(), pf.lse.clone(), pf.sel.clone()))
     for x, y in zip(outs[0], outs[1]):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name,ts,per_call", [("g4-hd128", 3, 3), ("g8-hd128-chunk64", 2, 4),
+                                              ("g1-hd128-c70", 2, 2), ("g2-hd64-ragged", 1, 5)])
+def test_several_chunks_per_call_equal_one_call_each(name, ts, per_call):
+    """sparse_attn_prefill_chunks over consecutive chunks (the last call of
+    the prompt with fewer) gives, bit for bit, the outputs, lse, lists,
+    counts and visible ends of one sparse_attn_prefill_chunk call per chunk,
+    and leaves the lengths where those calls do."""
+    pr, c, dc, ix, one, q_all, L, T, W, C = _setup(name, seed=6, ts=ts, k_max=4)
+    many = ChunkedPrefill(ix, T, W, k_max=4, token_splits=ts, per_call=per_call)
+    starts = list(range(0, L - T + 1, T))
+    for g0 in range(0, len(starts), per_call):
+        group = starts[g0:g0 + per_call]
+        budgets = [max(1, (c0 + T) // 16) for c0 in group]
+        n = len(group)
+        qd = to_device(np.ascontiguousarray(q_all[:, :, group[0]:group[-1] + T]))
+        many.part_o.fill_(float("nan"))
+        many.part_ml.fill_(float("nan"))
+        many.chunks(qd, group[0], budgets)
+        torch.cuda.synchronize()
+        lens_many = dc.seq_lens.clone()
+        out_m = many.out[: n * one.rows].view(c.B, c.Hq, n, T, c.hd)
+        lse_m = many.lse[: n * one.rows].view(c.B, c.Hq, n, T)
+        # a call of n chunks lays its lists out as [B][Hkv][n * T][...] from the buffers' start
+        km = many.sel.shape[-1]
+        sel_m = many.sel.view(-1)[: c.B * c.Hkv * n * T * km].view(c.B, c.Hkv, n, T, km)
+        cnt_m = many.count.view(-1)[: c.B * c.Hkv * n * T].view(c.B, c.Hkv, n, T)
+        ends_m = many.ends.view(-1, c.B, c.Hkv, C)[:n]
+        for jc, c0 in enumerate(group):
+            one.chunk(_qchunk(q_all, c0, T), c0, budgets[jc])
+            torch.cuda.synchronize()
+            ctx = f"{name} chunk at {c0} ({jc} of {n})"
+            assert torch.equal(out_m[:, :, jc], one.out.view(c.B, c.Hq, T, c.hd)), ctx
+            assert torch.equal(lse_m[:, :, jc], one.lse.view(c.B, c.Hq, T)), ctx
+            assert torch.equal(sel_m[:, :, jc], one.sel), ctx
+            assert torch.equal(cnt_m[:, :, jc], one.count), ctx
+            assert torch.equal(ends_m[jc], one.ends), ctx
+        assert torch.equal(dc.seq_lens, lens_many)  # both left the lengths at the next chunk's
