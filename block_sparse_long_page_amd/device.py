@@ -417,17 +417,22 @@ class ChunkedPrefill:
         self.out = torch.empty((n * self.rows, c.hd), dtype=_TORCH_ELEM[self.out_dtype], device=dev)
         self.lse = torch.empty((n * self.rows,), dtype=torch.float32, device=dev)
 
-    def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None):
+    def chunk(self, q: torch.Tensor, c0: int, budget: int, stream=None, advance: Optional[int] = None):
         """The rows [c0, c0 + Q) of the prompt.  The sequences' length must
         read c0 + Q: it is set here unless the previous chunk was the one just
-        before, whose combine advanced it by Q."""
+        before, whose combine advanced it by Q.  advance=0 (fused) leaves the
+        lengths at c0 + Q (the same rows again, e.g. a decode step's chunk)."""
         if self.c.known_len != c0 + self.Q:
             with on_stream(stream):
                 self.c.seq_lens.fill_(c0 + self.Q)
+        adv = self.Q if advance is None else advance
         if self.fused:
             B.sparse_attn_prefill_chunk(self.desc, self.index, q, self.Q, self.window, budget, self.k_max, 0.0,
                                         self.ts, self.ends, self.sel, self.count, self.part_o, self.part_ml,
-                                        self.out, self.out_dtype, self.lse, self.Q, self.ws, self.ws_bytes, stream)
+                                        self.out, self.out_dtype, self.lse, adv, self.ws, self.ws_bytes, stream)
+            self.c.known_len = c0 + self.Q + adv
+            self.last_n = 1
+            return self.out
         else:
             B.sparse_attn_blocks_visible(self.desc, self.index, self.window, self.ends, stream)
             B.sparse_attn_select_blocks(self.desc, self.index, q, self.Q, budget, self.k_max, self.sel, self.count,
