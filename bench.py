@@ -9,8 +9,9 @@ scores, keys from 64 Gaussian clusters), on seeded synthetic inputs already
 resident in HBM.
 
 To keep the 256 MB last-level cache from serving repeated reads, the timed
-steps rotate over R copies of the cache (distinct physical pages, the same
-contents), so each step reads pages no recent step touched.
+steps rotate over R copies of the cache and of its summaries (distinct
+physical pages, the same contents; R = 10 by default, so the copies' summaries
+alone exceed the cache), so each step reads data no recent step touched.
 
 Prints one JSON line: selected-KV GB/s (algorithmic bytes / step time),
 us/step, the roofline of the decode kernel (HIP-event time of its launches
@@ -46,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the cache rotated over the steps (0: the workload's default, 10 for the "
+                         "headline step, 6 for the eviction, 3 for the semantic chunk)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--local-splits", type=int, default=0, help="splits of the sink+window decode")
     ap.add_argument("--middle-splits", type=int, default=0, help="splits of the selected-pages decode")
@@ -339,7 +342,7 @@ def bench_semantic(args):
     pr = synth.workload_problem(wl)
     c = pr.cache
     log(f"inputs {time.time() - t0:.1f}s")
-    R = max(1, min(args.replicas, 3))  # 2 GiB of K+V per copy
+    R = max(1, min(args.replicas or 3, 3))  # 2 GiB of K+V per copy
     pool = DeviceCache.from_host(c)
     tables = replicate(pool, c, R)
     q = to_device(pr.q)
@@ -608,7 +611,7 @@ def bench_keydiff(args):
     pr = synth.workload_problem(wl)
     c = pr.cache
     log(f"inputs {time.time() - t0:.1f}s")
-    R = max(1, args.replicas)
+    R = max(1, args.replicas or 6)
     pool = DeviceCache.from_host(c)
     tables = replicate(pool, c, R)
     dst = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, wl.budget, c.dtype)
@@ -1150,8 +1153,11 @@ def main():
     c = pr.cache
     log(f"inputs {time.time() - t0:.1f}s")
 
-    # R copies of the cache in one physical-page pool; replica r's table points at its own pages
-    R = max(1, args.replicas)
+    # R copies of the cache in one physical-page pool; replica r's table points at its own pages.
+    # Ten copies: the K/V a step reads (205 MB) and the summaries (33 MB per
+    # copy, 330 MB in all) both exceed the 256 MB last-level cache, so no step
+    # finds the data of a recent one there.
+    R = max(1, args.replicas or 10)
     pool = DeviceCache.from_host(c)
     tables = replicate(pool, c, R)
     q = to_device(pr.q)

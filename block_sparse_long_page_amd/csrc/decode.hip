@@ -284,8 +284,12 @@ struct MfmaLds {
     float wv_m[Plan::NW][G], wv_l[Plan::NW][G];
 };
 
-// Per-lane state and tile pipeline of the matrix-core decode.
-template <int HD, int G>
+// Per-lane state and tile pipeline of the matrix-core decode.  NT: the K and
+// V tiles are loaded non-temporal (a selecting step reads its pages once:
+// they give way in the caches to the reused rows, scores and queries); the
+// decode of kept pages, which reads the same pages again at the next step,
+// loads them normally.
+template <int HD, int G, bool NT = false>
 struct MfmaCore {
     using Plan = MfmaPlan<HD, G>;
     static constexpr int NW = Plan::NW, KK = Plan::KK, NB = Plan::NB, VLD = Plan::VLD, LPT = Plan::LPT;
@@ -364,12 +368,16 @@ struct MfmaCore {
         B.rv[tt] = rv;
         const int rk = t0 + r < limit ? imax(rows[t0 + r], 0) : 0;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) B.k[tt][kk] = *(const uint4*)(kbase + (long)rk * HD + 32 * kk + 8 * j);
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint16_t* kp = kbase + (long)rk * HD + 32 * kk + 8 * j;
+            B.k[tt][kk] = NT ? ld_stream(kp) : *(const uint4*)kp;
+        }
         const int rows4[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
         for (int v = 0; v < VLD; ++v) {
             const int rr = imax(rows4[HD == 128 ? v : 2 * v + (r >> 3)], 0);
-            B.v[tt][v] = *(const uint4*)(vbase + (long)rr * HD + 8 * vchunk);
+            const uint16_t* vp = vbase + (long)rr * HD + 8 * vchunk;
+            B.v[tt][v] = NT ? ld_stream(vp) : *(const uint4*)vp;
         }
     }
 
@@ -673,7 +681,7 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_decode_mfma(Deco
 template <int HD, int G>
 __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mfma(SelectDecodeArgs a)
 {
-    using Core = MfmaCore<HD, G>;
+    using Core = MfmaCore<HD, G, true>;
     constexpr int NW = Core::NW;
     constexpr int SW = NW - 1;  // the wave that ranks the pages
     static_assert(Core::TPS == 1, "one tile per wave step");

@@ -236,6 +236,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
 }
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// A 16-byte load marked non-temporal, for what a kernel streams once (the K
+// and V rows of a selecting step, the rows a copy moves): the streamed lines
+// leave the caches to the data that is reused (block-table rows, scores,
+// queries, partials).
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p)
+{
+    const nt_u32x4 w = __builtin_nontemporal_load((const nt_u32x4*)p);
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
 // n / d for 0 <= n < 2^31 with a host-computed magic pair (Granlund and

@@ -302,8 +302,10 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 const int e = u * 64 * kGW + threadIdx.x;  // chunk of the stage
                 const int tt = st * kStage + e / CPT;
                 const long off = (tt < ntok ? (long)tt * HD : 0) + (e % CPT) * 8;
-                x.k[u] = *(const uint4*)(kp + off);
-                x.v[u] = *(const uint4*)(vp + off);
+                // plan mode (a decode step's pages, read once) non-temporal;
+                // prefill chunks read blocks their neighbours read again
+                x.k[u] = PF ? *(const uint4*)(kp + off) : ld_stream(kp + off);
+                x.v[u] = PF ? *(const uint4*)(vp + off) : ld_stream(vp + off);
             });
         };
         auto stash = [&](int st, int buf, const Staged& x) {

@@ -34,6 +34,8 @@ namespace {
 
 static_assert(kKdChunk % kKdSlots == 0, "a chunk of the sum pass is whole groups of carried sums");
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kKdWaves = 4;
 constexpr int kKdRowsPerWave = kKdChunk / kKdWaves;
 constexpr int kKdU = 16;            // row loads per lane in flight
@@ -443,15 +445,19 @@ __global__ __launch_bounds__(kKdCopyThreads) void k_kd_compact(CompactArgs a)
         const int dph = d.block_table[(long)b * d.max_pages + dp];
         if (sph < 0 || sph >= s.num_phys || dph < 0 || dph >= d.num_phys) continue;
         const long so = (((long)sph * s.Hkv + kvh) * s.P + (p - sp * s.P)) * PPR + piece;
-        kv[it][0] = ((const uint4*)s.k)[so];
-        kv[it][1] = ((const uint4*)s.v)[so];
+        kv[it][0] = ld_stream((const uint4*)s.k + so);
+        kv[it][1] = ld_stream((const uint4*)s.v + so);
         dst_off[it] = (((long)dph * d.Hkv + kvh) * d.P + (j - dp * d.P)) * PPR + piece;
     }
+    // the copy's stores are non-temporal: the evicted cache is not read again
+    // soon, and written back at once they do not land, as dirty lines of the
+    // last-level cache, in the next kernels' reads
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         if (dst_off[it] < 0) continue;
-        ((uint4*)d.k)[dst_off[it]] = kv[it][0];
-        ((uint4*)d.v)[dst_off[it]] = kv[it][1];
+        const uint4 k4 = kv[it][0], v4 = kv[it][1];
+        __builtin_nontemporal_store(u32x4_t{k4.x, k4.y, k4.z, k4.w}, (u32x4_t*)d.k + dst_off[it]);
+        __builtin_nontemporal_store(u32x4_t{v4.x, v4.y, v4.z, v4.w}, (u32x4_t*)d.v + dst_off[it]);
     }
     if (a.slot_sums) {
         // the key sum of this group of slots (a key not copied counts as

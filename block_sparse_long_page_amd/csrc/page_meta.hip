@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_page_meta(MetaArgs a)
         for (int u = 0; u < U; ++u) {
             const int r = base + u * RPW + rg;
             const E* row = r < g.P ? slab + (long)r * HD : slab1 + (long)(r - g.P) * HD;
-            w[u] = r < nt ? *(const uint4*)row : make_uint4(0, 0, 0, 0);
+            w[u] = r < nt ? ld_stream(row) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

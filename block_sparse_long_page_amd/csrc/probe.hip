@@ -11,6 +11,7 @@
 //    round of 8 by wave w, three tiles in flight per wave;
 //  * k_probe_stream reads one contiguous buffer, 16 bytes per lane, eight
 //    loads in flight per lane.
+// Both use non-temporal loads, as the attention kernels do for K and V.
 //
 // Every loaded word is folded into a register that is compared with a
 // constant at the end, so no load can be dropped and nothing is written
@@ -24,6 +25,14 @@ constexpr int kWaves = 8;
 constexpr uint32_t kNever = 0x9e3779b9u;
 
 __device__ __forceinline__ uint32_t fold(uint4 x) { return x.x ^ x.y ^ x.z ^ x.w; }
+
+// non-temporal 16-byte loads, as the attention kernels stream K and V
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p)
+{
+    const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
 
 // TILE_U4: 16-byte pieces of one 16-token tile of K (or V) per lane
 template <int TILE_U4>
@@ -47,8 +56,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_probe_pages(const uint4* k, con
         const long base = (long)slab * slab_u4 + (long)(tt % tiles_per_slab) * (TILE_U4 * 64);
 #pragma unroll
         for (int i = 0; i < TILE_U4; ++i) {
-            buf[0][i] = k[base + i * 64 + lane];
-            buf[1][i] = v[base + i * 64 + lane];
+            buf[0][i] = ld_nt(k + base + i * 64 + lane);
+            buf[1][i] = ld_nt(v + base + i * 64 + lane);
         }
     };
     auto use = [&](const uint4 (&buf)[2][TILE_U4], int t) {
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(256) void k_probe_stream(const uint4* src, long n_u
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n_u4; i += stride * kStreamUnroll) {
         uint4 x[kStreamUnroll];
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u) x[u] = i + u * stride < n_u4 ? src[i + u * stride] : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kStreamUnroll; ++u) x[u] = i + u * stride < n_u4 ? ld_nt(src + i + u * stride) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) acc ^= fold(x[u]);
     }
