@@ -761,10 +761,14 @@ def bench_prefill(args):
     ix = BlockIndex(dc, L, C, Q=T, window=W, budget=0, k_max=C)
     # at most 10 blocks per row (the budget, 1/16 of at most 65664 tokens,
     # holds about 2 blocks of the average 2048 tokens; rows that reach the cap
-    # are counted below), each block in 3 token chunks so that the few blocks
-    # a chunk reads spread over the GPU; the dense run takes every block
+    # are counted below).  With one chunk per call each block is read in 3
+    # token chunks so that the few blocks a chunk reads spread over the GPU;
+    # with several chunks per call they fill it already, and one token chunk
+    # per block keeps the partials (written, then read by the combine) few.
+    # The dense run takes every block.
     per = max(1, args.chunks_per_call)
-    pf = ChunkedPrefill(ix, T, W, k_max=min(C, args.k_max), token_splits=args.token_splits or 3, per_call=per)
+    ts = args.token_splits or (3 if per == 1 else 1)
+    pf = ChunkedPrefill(ix, T, W, k_max=min(C, args.k_max), token_splits=ts, per_call=per)
     pf_dense = ChunkedPrefill(ix, T, W, k_max=C, token_splits=1, per_call=per)
     # one call per chunk, for the byte count's pass (its lists are the same bit for bit)
     pf1 = pf if per == 1 else ChunkedPrefill(ix, T, W, k_max=pf.k_max, token_splits=pf.ts)
