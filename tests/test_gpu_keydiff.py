@@ -322,3 +322,40 @@ def test_full_size_carried_eviction():
         assert set(range(p * c.P, (p + 1) * c.P)) <= set(got[b][kvh].tolist())
     print(f"full size, carried: {band} candidates inside the band; {differ} positions differ from the direct "
           f"selection (its mean rounds differently)")
+
+
+@pytest.mark.parametrize("name", ["f32-hd64-p7", "bf16-hd64-short", "f32-hd128-one-evicted", "bf16-hd128-past-limit"])
+def test_carried_sums_on_every_layout(name):
+    """The copy's slot sums (every 64 destination slots: the sum of the keys
+    copied there) on fp32 and bf16 caches of head dim 64 and 128, ragged
+    counts included; then a second eviction of the evicted cache to 7/8 of
+    the budget that carries those sums chooses within the band of the oracle
+    on the keys that cache holds."""
+    pr, budget, sink = _problem(name, seed=9)
+    c = pr.cache
+    src = DeviceCache.from_host(c)
+    dst = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, budget, c.dtype)
+    ev = KeyDiffEviction(src, dst, budget, sink, sums=True)
+    ev.evict()
+    torch.cuda.synchronize()
+    got = ev.kept_positions()
+    sums = ev.slot_sums.cpu().numpy()
+    held = [[dense_keys_values(c, b, kvh)[0][got[b][kvh]] for kvh in range(c.Hkv)] for b in range(c.B)]
+    for b in range(c.B):
+        for kvh in range(c.Hkv):
+            kk = held[b][kvh]
+            for i in range(-(-len(kk) // 64)):
+                grp = kk[64 * i: 64 * (i + 1)]
+                tol = 1e-5 * np.abs(grp).sum(0) + 1e-6
+                assert (np.abs(sums[b, kvh, i] - grp.sum(0)) <= tol).all(), (name, b, kvh, i)
+    budget2 = max(sink, budget - max(1, budget // 8))  # (a small eviction keeps the past-limit case in range)
+    dst2 = DeviceCache.empty(c.B, c.Hq, c.Hkv, c.hd, c.P, budget2, c.dtype)
+    ev2 = KeyDiffEviction(dst, dst2, budget2, sink)
+    ev2.select(carried=ev.carried())
+    torch.cuda.synchronize()
+    got2 = ev2.kept_positions()
+    band = 0
+    for b in range(c.B):
+        for kvh in range(c.Hkv):
+            band += check_kept(got2[b][kvh], held[b][kvh], budget2, sink)
+    print(f"{name}: second eviction with carried sums, {band} candidates inside the band")
