@@ -43,8 +43,10 @@
 // page's index in the row's list, so the merge order is fixed and the
 // results do not depend on timing.
 //
-// Prefill mode (a chunk of a prompt over a block index, after the front of
-// prefill.hip, with no plan kernel): the units of a (sequence, KV head) are
+// Prefill mode (one or several consecutive chunks of a prompt over a block
+// index, after the front of prefill.hip, with no plan kernel; each chunk
+// has its own length, slot table and counters): the units of a (chunk,
+// sequence, KV head) are
 // first the pages of the rows' window [L - W, L), each token chunk attended
 // causally by the rows at or after its first token (the others get an empty
 // partial for that slot), then the index's blocks, largest visible part

@@ -27,6 +27,8 @@
  *   sparse_attn_blocks_visible     the part of each block before a prompt
  *                                  chunk's window (chunked prefill over an
  *                                  index of the whole prompt)
+ *   sparse_attn_prefill_chunk(s)   one chunk (or up to 16 consecutive
+ *                                  chunks) of that prefill in three launches
  *
  * and, for KeyDiff eviction (course module 14, section 14.4: tokens whose
  * keys lie closest to the mean key are evicted, the sink never, blockwise so
@@ -35,6 +37,9 @@
  *   sparse_attn_keydiff_select     the tokens each (sequence, KV head) keeps
  *   sparse_attn_keydiff_compact    their K and V rows, in order, into a cache
  *                                  of the budget's size
+ *   sparse_attn_keydiff_compact_sums, sparse_attn_keydiff_select_carried
+ *                                  the same with the held keys' sums carried
+ *                                  from one eviction to the next
  *
  * sparse_attn_decode_step runs select and decode of a selecting step with the
  * top-k inside the decode kernel (two launches instead of three).
