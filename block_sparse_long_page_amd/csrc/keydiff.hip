@@ -6,7 +6,7 @@
 //
 //  * k_kd_sum: per (sequence, KV head, chunk of kKdChunk tokens) the fp32 sum
 //    of the keys (rows in order in each lane, then lanes and waves in a fixed
-//    order: bitwise reproducible).  A chunk that the previous eviction's
+//    order: bitwise reproducible); the last chunks are launched first.  A chunk that the previous eviction's
 //    compaction filled takes its sum from the key sums that compaction left
 //    (one per group of kKdSlots slots, added in order) instead of reading its
 //    keys again: between evictions only the new block's keys are summed.
@@ -38,6 +38,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKdWaves = 4;
 constexpr int kKdRowsPerWave = kKdChunk / kKdWaves;
+static_assert(kKdRowsPerWave <= 128, "a wave's rows span at most 128 pages");
 constexpr int kKdU = 16;            // row loads per lane in flight
 constexpr int kKdCopyThreads = 256;
 
@@ -46,25 +47,27 @@ __device__ __forceinline__ int kd_len(const Geometry& g, int T, int b)
     return imax(0, imin(imin(g.seq_lens[b], T), g.max_pages * g.P));
 }
 
-// Physical pages of the logical pages [pg0, pg0 + npg) of one sequence, one
-// per lane (npg <= 64), looked up by a lane exchange; with more pages each
-// row reads its own entry.  Unmapped pages give -1.
+// Block-table entries of the logical pages [pg0, pg0 + npg) of one sequence
+// (npg <= 128, the pages of one wave's rows), two per lane, looked up by lane
+// exchanges.  Entries past npg are -1; every entry is checked against the
+// pool before use.
 struct WavePages {
-    const int32_t* bt;
-    int pg0, npg, mine, num_phys;
-    __device__ __forceinline__ void init(const int32_t* table, int first, int n, int nphys)
+    int pg0, npg, lo, hi;  // lo: page pg0 + lane, hi: page pg0 + 64 + lane
+    __device__ __forceinline__ void init(const int32_t* table, int first, int n)
     {
-        bt = table;
         pg0 = first;
         npg = n;
-        num_phys = nphys;
         const int lane = threadIdx.x & 63;
-        mine = n <= 64 && lane < n ? bt[first + lane] : -1;
+        lo = lane < n ? table[first + lane] : -1;
+        hi = 64 + lane < n ? table[first + 64 + lane] : -1;
     }
-    __device__ __forceinline__ int phys(int page) const
+    // every lane of the wave takes part
+    __device__ __forceinline__ int entry(int page) const
     {
-        const int p = npg <= 64 ? __shfl(mine, page - pg0) : bt[page];
-        return p >= 0 && p < num_phys ? p : -1;
+        const int i = page - pg0;
+        if (npg <= 64) return __shfl(lo, i);
+        const int a = __shfl(lo, i & 63), b = __shfl(hi, i & 63);
+        return i < 64 ? a : b;
     }
 };
 
@@ -90,34 +93,51 @@ struct KdLayout {
     }
 };
 
-// Streams rows [r0, r1) of (b, kvh), kKdU loads per lane in flight, calling
-// f(row, x) with this lane's CH channels of each row; rows past r1 and rows
-// on unmapped pages read as zeros (a zero key).
-template <int HD, bool BF, typename F>
-__device__ __forceinline__ void kd_stream(const Geometry& g, const FastDiv& pdiv, int b, int kvh, int r0, int r1, F f)
+// The block-table entries of the pages that rows [w0, w0 + kKdRowsPerWave)
+// of sequence b span (clipped to the table), loaded before the sequence's
+// length is known, so that this load and the length's are in flight
+// together.  The rows a wave streams are a prefix of that range.
+__device__ __forceinline__ WavePages kd_wave_pages(const Geometry& g, const FastDiv& pdiv, int b, int w0)
+{
+    WavePages wp;
+    const int cap = g.max_pages * g.P;
+    const int hi = imin(w0 + kKdRowsPerWave, cap);
+    const int pg0 = pdiv.div(imin(w0, cap - 1));
+    wp.init(g.block_table + (long)b * g.max_pages, pg0, w0 < hi ? pdiv.div(hi - 1) - pg0 + 1 : 0);
+    return wp;
+}
+
+// Streams rows [r0, r1) of (b, kvh) (pages resolved by wp), U loads per lane
+// in flight, calling f(row, x) with this lane's CH channels of each row; rows
+// past r1 and rows on unmapped pages read as zeros (a zero key).  The pages
+// of a round's rows are resolved before any of its loads is issued: a
+// block-table load between two row loads would make each row load wait for
+// the ones before it.
+template <int HD, bool BF, int U, typename F>
+__device__ __forceinline__ void kd_stream(const Geometry& g, const FastDiv& pdiv, const WavePages& wp, int kvh,
+                                          int r0, int r1, F f)
 {
     using Lay = KdLayout<HD, BF>;
     typedef typename Lay::E E;
     const int lane = threadIdx.x & 63;
     const int sub = lane % Lay::LPT, rg = lane / Lay::LPT;
     if (r0 >= r1) return;
-    WavePages wp;
-    const int pg0 = pdiv.div(r0);
-    wp.init(g.block_table + (long)b * g.max_pages, pg0, pdiv.div(r1 - 1) - pg0 + 1, g.num_phys);
-    for (int base = r0; base < r1; base += Lay::RPW * kKdU) {
-        uint4 w[kKdU];
+    for (int base = r0; base < r1; base += Lay::RPW * U) {
+        int ph[U];
 #pragma unroll
-        for (int u = 0; u < kKdU; ++u) {
+        for (int u = 0; u < U; ++u) ph[u] = wp.entry(pdiv.div(imin(base + u * Lay::RPW + rg, r1 - 1)));
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             const int t = base + u * Lay::RPW + rg;
             const int page = pdiv.div(imin(t, r1 - 1));
-            const int ph = wp.phys(page);  // every lane takes part in the exchange
             w[u] = make_uint4(0, 0, 0, 0);
-            if (t < r1 && ph >= 0)
-                w[u] = *(const uint4*)((const E*)g.k + (((long)ph * g.Hkv + kvh) * g.P + (t - page * g.P)) * HD +
+            if (t < r1 && ph[u] >= 0 && ph[u] < g.num_phys)
+                w[u] = *(const uint4*)((const E*)g.k + (((long)ph[u] * g.Hkv + kvh) * g.P + (t - page * g.P)) * HD +
                                        sub * Lay::CH);
         }
 #pragma unroll
-        for (int u = 0; u < kKdU; ++u) {
+        for (int u = 0; u < U; ++u) {
             float x[Lay::CH];
             Lay::unpack(w[u], x);
             f(base + u * Lay::RPW + rg, x);
@@ -132,14 +152,23 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_sum(KeydiffArgs a)
     __shared__ float wsum[kKdWaves][HD];
     const Geometry& g = a.g;
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
-    const int bh = blockIdx.y, b = bh / g.Hkv, kvh = bh % g.Hkv;
-    const int L = kd_len(g, a.T, b);
-    const int t0 = blockIdx.x * kKdChunk;
+    // workgroup (i, j) sums chunk nchunks-1-j of pair i: the last chunks,
+    // which hold the newest tokens and are never carried, are dispatched first
+    const int bh = blockIdx.x, b = bh / g.Hkv, kvh = bh % g.Hkv, chunk = a.nchunks - 1 - (int)blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t0 = chunk * kKdChunk;
+    const int w0 = t0 + wave * kKdRowsPerWave;
+    // the length, the carried count and the wave's block-table entries are
+    // independent: all three loads are issued before any is waited for
+    const int len = g.seq_lens[b];
+    const int ccount = a.carried ? a.carried_count[bh] : 0;
+    const WavePages wp = kd_wave_pages(g, pdiv, b, w0);
+    const int L = imax(0, imin(imin(len, a.T), g.max_pages * g.P));
     if (t0 >= L) return;
-    float* const dst = a.partial + ((long)bh * a.nchunks + blockIdx.x) * HD;
-    if (a.carried && t0 + kKdChunk <= imin(imin(a.carried_count[bh], kKdSlots * a.carried_groups), L)) {
+    float* const dst = a.partial + ((long)bh * a.nchunks + chunk) * HD;
+    if (a.carried && t0 + kKdChunk <= imin(imin(ccount, kKdSlots * a.carried_groups), L)) {
         // a chunk the last compaction filled: the sum of its groups' sums, in order
-        const float* cs = a.carried + ((long)bh * a.carried_groups + blockIdx.x * (kKdChunk / kKdSlots)) * HD;
+        const float* cs = a.carried + ((long)bh * a.carried_groups + chunk * (kKdChunk / kKdSlots)) * HD;
         for (int c = threadIdx.x; c < HD; c += 64 * kKdWaves) {
             float s = 0.f;
 #pragma unroll
@@ -148,14 +177,16 @@ __global__ __launch_bounds__(64 * kKdWaves) void k_kd_sum(KeydiffArgs a)
         }
         return;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % Lay::LPT, rg = lane / Lay::LPT;
-    const int r0 = imin(L, t0 + wave * kKdRowsPerWave), r1 = imin(L, r0 + kKdRowsPerWave);
+    const int r0 = imin(L, w0), r1 = imin(L, r0 + kKdRowsPerWave);
 
     float acc[Lay::CH];
 #pragma unroll
     for (int c = 0; c < Lay::CH; ++c) acc[c] = 0.f;
-    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int, const float (&x)[Lay::CH]) {
+    // the wave's rows in one round of loads, at most 32 per lane (each lane
+    // adds its rows in order)
+    constexpr int U = kKdRowsPerWave / Lay::RPW < 32 ? kKdRowsPerWave / Lay::RPW : 32;
+    kd_stream<HD, BF, U>(g, pdiv, wp, kvh, r0, r1, [&](int, const float (&x)[Lay::CH]) {
 #pragma unroll
         for (int c = 0; c < Lay::CH; ++c) acc[c] += x[c];
     });
@@ -180,34 +211,65 @@ template <int HD, bool BF>
 __global__ __launch_bounds__(64 * kKdWaves) void k_kd_dist(KeydiffArgs a)
 {
     using Lay = KdLayout<HD, BF>;
-    __shared__ float mean[HD];
+    constexpr int NT = 64 * kKdWaves;
+    constexpr int TPC = NT / HD;  // threads per channel of the mean
+    constexpr int MJ = 16;        // chunk sums a thread loads per round
+    static_assert(TPC * HD == NT, "threads tile the channels");
+    __shared__ float part[TPC][HD];
     const Geometry& g = a.g;
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
     const int bh = blockIdx.y, b = bh / g.Hkv, kvh = bh % g.Hkv;
-    const int L = kd_len(g, a.T, b);
-    const int t0 = blockIdx.x * kKdChunk;
-    if (t0 >= L) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane % Lay::LPT;
+    const int t0 = blockIdx.x * kKdChunk;
+    const int w0 = t0 + wave * kKdRowsPerWave;
+    // The mean key: thread (h, c) adds the sums of channel c over its share
+    // of the chunks, in chunk order; the TPC shares are then added in order.
+    // The first round of chunk-sum loads, the length and the wave's
+    // block-table entries are in flight together (chunks past the length
+    // were not written and are masked out once it is known).
+    const int c = threadIdx.x % HD, h = threadIdx.x / HD;
+    const int per = (a.nchunks + TPC - 1) / TPC;
+    const int j0 = h * per, j1 = imin(a.nchunks, j0 + per);
+    const float* ps = a.partial + (long)bh * a.nchunks * HD + c;
+    float v[MJ];
+#pragma unroll
+    for (int u = 0; u < MJ; ++u) v[u] = j0 + u < j1 ? ps[(long)(j0 + u) * HD] : 0.f;
+    const int len = g.seq_lens[b];
+    const WavePages wp = kd_wave_pages(g, pdiv, b, w0);
+    const int L = imax(0, imin(imin(len, a.T), g.max_pages * g.P));
+    if (t0 >= L) return;
     const int nch = (L + kKdChunk - 1) / kKdChunk;
-    for (int c = threadIdx.x; c < HD; c += 64 * kKdWaves) {
-        float s = 0.f;
-        for (int j = 0; j < nch; ++j) s += a.partial[((long)bh * a.nchunks + j) * HD + c];
-        mean[c] = s / (float)L;
+    const int je = imin(j1, nch);
+    float s = 0.f;
+    for (int jb = j0;;) {
+#pragma unroll
+        for (int u = 0; u < MJ; ++u)
+            if (jb + u < je) s += v[u];
+        jb += MJ;
+        if (jb >= je) break;
+#pragma unroll
+        for (int u = 0; u < MJ; ++u) v[u] = jb + u < je ? ps[(long)(jb + u) * HD] : 0.f;
     }
+    part[h][c] = s;
     __syncthreads();
     float m[Lay::CH];
 #pragma unroll
-    for (int c = 0; c < Lay::CH; ++c) m[c] = mean[sub * Lay::CH + c];
-    const int r0 = imin(L, t0 + wave * kKdRowsPerWave), r1 = imin(L, r0 + kKdRowsPerWave);
+    for (int e = 0; e < Lay::CH; ++e) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPC; ++i) t += part[i][sub * Lay::CH + e];
+        m[e] = t / (float)L;
+    }
+    const int r0 = imin(L, w0), r1 = imin(L, r0 + kKdRowsPerWave);
     // token t goes to index L-1-t (the sink's indices, past the candidates, are never read)
     uint32_t* okeys = a.okeys + (long)bh * a.Tk + (L - 1);
-    kd_stream<HD, BF>(g, pdiv, b, kvh, r0, r1, [&](int t, const float (&x)[Lay::CH]) {
+    kd_stream<HD, BF, kKdU>(g, pdiv, wp, kvh, r0, r1, [&](int t, const float (&x)[Lay::CH]) {
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < Lay::CH; ++c) {
-            const float e = x[c] - m[c];
-            d = fmaf(e, e, d);
+        for (int e = 0; e < Lay::CH; ++e) {
+            const float df = x[e] - m[e];
+            d = fmaf(df, df, d);
         }
         d = group_sum<Lay::LPT>(d);
         if (sub == 0 && t < r1) okeys[-t] = order_key(d);
@@ -495,7 +557,7 @@ template <int HD, bool BF>
 hipError_t launch_kd(const KeydiffArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)a.nchunks, (unsigned)(a.g.B * a.g.Hkv));
-    hipLaunchKernelGGL((k_kd_sum<HD, BF>), grid, dim3(64 * kKdWaves), 0, s, a);
+    hipLaunchKernelGGL((k_kd_sum<HD, BF>), dim3(grid.y, grid.x), dim3(64 * kKdWaves), 0, s, a);
     hipLaunchKernelGGL((k_kd_dist<HD, BF>), grid, dim3(64 * kKdWaves), 0, s, a);
     if (a.ecnk > 0) {  // more candidates than one workgroup holds
         hipLaunchKernelGGL(k_kd_evict_chunk, dim3((unsigned)a.ecnk, (unsigned)(a.g.B * a.g.Hkv)), dim3(kTopkThreads),
