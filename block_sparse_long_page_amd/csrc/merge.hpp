@@ -53,8 +53,10 @@ __device__ __forceinline__ void merge_row(const float* ml, const float* po_row, 
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[j][c] = j < n ? merge_ld<COHERENT>(po + (long)j * HD + c) : 0.f;
     float mx = -INFINITY;
+    float2 first = make_float2(0.f, 0.f);  // this lane's pair among the first 64 splits, kept for the weights
     for (int s = lane; s < n; s += 64) {
         const float2 p = merge_ld2<COHERENT>(ml + 2 * s);
+        if (s == lane) first = p;
         if (p.y > 0.f) mx = fmaxf(mx, p.x);
     }
     mx = group_max<64>(mx);
@@ -67,7 +69,7 @@ __device__ __forceinline__ void merge_row(const float* ml, const float* po_row, 
         const int s = s0 + lane;
         float w = 0.f;
         if (s < n) {
-            const float2 p = merge_ld2<COHERENT>(ml + 2 * s);
+            const float2 p = s0 == 0 ? first : merge_ld2<COHERENT>(ml + 2 * s);
             w = p.y > 0.f ? expf(p.x - mx) * p.y : (p.y == p.y ? 0.f : p.y);
             wts[s] = w;
         }

@@ -81,6 +81,10 @@ CASES = {
                                   dtype="bf16"),
     "f32-hd64-past-limit-block": dict(B=1, Hq=4, Hkv=2, hd=64, P=16, seq_lens=[30000], budget=28000, sink=4,
                                       dtype="f32"),
+    # one-token pages: a wave's 128 rows span 128 pages, two block-table
+    # entries per lane; two-token pages: exactly 64
+    "bf16-hd128-p1": dict(B=1, Hq=4, Hkv=2, hd=128, P=1, seq_lens=[1500], budget=700, sink=3, dtype="bf16"),
+    "f32-hd64-p2": dict(B=2, Hq=2, Hkv=1, hd=64, P=2, seq_lens=[1001, 640], budget=300, sink=2, dtype="f32"),
 }
 
 
@@ -110,7 +114,7 @@ def test_kept_positions(name):
     print(f"{name}: {band} candidates inside the band")
 
 
-@pytest.mark.parametrize("name", ["bf16-hd128-p16", "bf16-hd128-past-limit"])
+@pytest.mark.parametrize("name", ["bf16-hd128-p16", "bf16-hd128-past-limit", "bf16-hd128-p1"])
 def test_planted_ties_keep_the_later_position(name):
     """Every key is one of four bf16 vectors, so distances tie exactly on both
     sides and the kept set must equal the oracle's (also when the evicted set
@@ -130,7 +134,7 @@ def test_planted_ties_keep_the_later_position(name):
 
 
 @pytest.mark.parametrize("name,dst_P", [("bf16-hd128-p16", 16), ("bf16-hd128-p16", 64), ("f32-hd64-p7", 10),
-                                        ("bf16-hd64-short", 64)])
+                                        ("bf16-hd64-short", 64), ("bf16-hd128-p1", 1), ("f32-hd64-p2", 2)])
 def test_compaction_copies_the_kept_rows(name, dst_P):
     pr, budget, sink = _problem(name)
     c = pr.cache
@@ -324,7 +328,8 @@ def test_full_size_carried_eviction():
           f"selection (its mean rounds differently)")
 
 
-@pytest.mark.parametrize("name", ["f32-hd64-p7", "bf16-hd64-short", "f32-hd128-one-evicted", "bf16-hd128-past-limit"])
+@pytest.mark.parametrize("name", ["f32-hd64-p7", "bf16-hd64-short", "f32-hd128-one-evicted", "bf16-hd128-past-limit",
+                                  "bf16-hd128-p1"])
 def test_carried_sums_on_every_layout(name):
     """The copy's slot sums (every 64 destination slots: the sum of the keys
     copied there) on fp32 and bf16 caches of head dim 64 and 128, ragged
