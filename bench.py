@@ -1365,15 +1365,19 @@ def main():
     dec_gbps = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
 
     cpu = None
+    accuracy = None
     if not args.no_cpu_baseline:
+        import numpy as np
+
         import oracle
 
         oracle.build(force=False)
         times = []
+        own = None
         t_end = time.time() + args.cpu_seconds
         while len(times) < 3 or time.time() < t_end:
             t1 = time.perf_counter()
-            oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
+            own = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget)
             times.append(time.perf_counter() - t1)
             if len(times) >= 200:
                 break
@@ -1382,6 +1386,20 @@ def main():
                "kind": "oracle", "sample": f"the full step (summaries of all pages, scores, top-k, attention) "
                                            f"in fp64, repeated {len(times)} times; median {med * 1e3:.1f} ms/step",
                "ms_per_step": round(med * 1e3, 2), "cpu_model": cpu_model()}
+        if mode != "overlap":
+            # The step's accuracy, outside the timed region: one step on the
+            # first copy (the host cache's own block table), its output
+            # against the oracle attending the same page lists in fp64, and
+            # its page lists against the oracle's own selection.
+            step(0)
+            torch.cuda.synchronize()
+            gsel, gcnt = dec.selection()
+            ref = oracle.run(c, pr.q, mode=pr.mode, Q=1, sink=pr.sink, window=pr.window, budget=pr.budget,
+                             sel=gsel, cnt=gcnt)
+            err = float(np.abs(dec.out_f32().astype(np.float64) - ref.out).max())
+            accuracy = {"max_abs_err": float(f"{err:.3e}"), "tolerance": 2e-2 if c.dtype == B.SA_BF16 else 1e-4,
+                        "reference": "the fp64 oracle attending the step's own page lists (first copy)",
+                        "identical_page_lists": f"{int((gsel == own.sel).all(axis=-1).sum())}/{gcnt.size}"}
 
     rec = {
         "metric": "selected-KV GB/s (% of HBM peak) + us/decode step, 128k ctx GQA-8",
@@ -1408,6 +1426,7 @@ def main():
                      "traffic": traffic_record(dec_kernel), "bytes_per_launch": dec_bytes,
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
+        "accuracy": accuracy,
         "step_us": step_dist,
         "stream_ref": stream_ref,
         "stream_ref_us": stream_ref["us"],
