@@ -122,18 +122,31 @@ __global__ __launch_bounds__(256) void k_idx_assign(IndexArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, j = lane >> 4;
     const int tbase = blockIdx.x * (64 * TT) + wave * 16 * TT;
 
-    ibf16x8_t kb[TT][KK];
+    // the key rows of the wave's tiles: the block-table entries of all
+    // tiles first, then every key load (a table load between two key loads
+    // would make each wait for the ones before it)
+    const int32_t* btr = g.block_table + (long)b * g.max_pages;
+    int ph[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         const int t = tbase + 16 * tt + r;
-        const long row = t < a.N ? key_row(g, pdiv, b, kvh, t) : -1;
+        ph[tt] = t < a.N ? btr[pdiv.div(t)] : -1;
+    }
+    long rows[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {  // as key_row: -1 past the keys or on an unmapped page
+        const int t = tbase + 16 * tt + r, p = pdiv.div(t);
+        rows[tt] = ph[tt] >= 0 && ph[tt] < g.num_phys ? ((long)ph[tt] * g.Hkv + kvh) * g.P + (t - p * g.P) : -1;
+    }
+    ibf16x8_t kb[TT][KK];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
-            if (row >= 0) w = *(const uint4*)((const uint16_t*)g.k + row * HD + 32 * kk + 8 * j);
+            if (rows[tt] >= 0) w = *(const uint4*)((const uint16_t*)g.k + rows[tt] * HD + 32 * kk + 8 * j);
             kb[tt][kk] = __builtin_bit_cast(ibf16x8_t, w);
         }
-    }
     float best[TT];
     int bidx[TT];
 #pragma unroll
@@ -144,9 +157,23 @@ __global__ __launch_bounds__(256) void k_idx_assign(IndexArgs a)
     const uint16_t* cb = a.cent_bf + (long)bk * a.C * HD;
     for (int c0 = 0; c0 < a.C; c0 += CH) {
         const int nc = imin(CH, a.C - c0);
-        __syncthreads();  // the previous round's centres are no longer read
-        for (int e = threadIdx.x; e < nc * HD / 8; e += 256)
-            ((uint4*)cl)[e] = ((const uint4*)(cb + (long)c0 * HD))[e];
+        {
+            // the round's centres into LDS: every thread's loads in flight
+            // together (the first round's with the key loads), then stored
+            // once the previous round's centres are no longer read
+            constexpr int PER = CH * HD / 8 / 256;
+            static_assert(PER * 256 == CH * HD / 8, "16-byte pieces tile the workgroup");
+            uint4 w[PER];
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int e = u * 256 + (int)threadIdx.x;
+                w[u] = e < nc * HD / 8 ? ((const uint4*)(cb + (long)c0 * HD))[e] : make_uint4(0, 0, 0, 0);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < PER; ++u)  // rows past nc hold zeros and are not read
+                ((uint4*)cl)[u * 256 + (int)threadIdx.x] = w[u];
+        }
         __syncthreads();
         for (int blk = 0; blk * 16 < nc; ++blk) {
             const int cr = 16 * blk + r;  // this lane's centre row of the A operand
@@ -325,21 +352,19 @@ __global__ __launch_bounds__(256) void k_idx_seg(IndexArgs a)
     const int nrows = imin(offsets[c + 1] - r0, kIndexSegment);
     const int32_t* pos = a.positions + (long)bk * a.N;
     const float* inv = a.inv_norm + (long)bk * a.N;
-    // row r of the segment: lane r (r < 64) or lane r - 64 of the second pair
-    int rowA = 0, rowB = 0;
-    float wA = 0.f, wB = 0.f;
-    if (lane < nrows) {
-        const int t = pos[r0 + lane];
-        const long row = key_row(g, pdiv, b, kvh, t);
-        rowA = row >= 0 ? (int)row : 0;  // rows fit 31 bits (checked on the host)
-        wA = row >= 0 ? inv[t] : 0.f;
-    }
-    if (64 + lane < nrows) {
-        const int t = pos[r0 + 64 + lane];
-        const long row = key_row(g, pdiv, b, kvh, t);
-        rowB = row >= 0 ? (int)row : 0;
-        wB = row >= 0 ? inv[t] : 0.f;
-    }
+    // row r of the segment: lane r (r < 64) or lane r - 64 of the second
+    // pair; both positions, then both block-table entries with both 1/|k|,
+    // are loaded together
+    const int32_t* btr = g.block_table + (long)b * g.max_pages;
+    const int tA = lane < nrows ? pos[r0 + lane] : -1;
+    const int tB = 64 + lane < nrows ? pos[r0 + 64 + lane] : -1;
+    const int phA = tA >= 0 ? btr[pdiv.div(tA)] : -1, phB = tB >= 0 ? btr[pdiv.div(tB)] : -1;
+    const float iA = tA >= 0 ? inv[tA] : 0.f, iB = tB >= 0 ? inv[tB] : 0.f;
+    // as key_row: a position on an unmapped page weighs 0 (rows fit 31 bits, checked on the host)
+    const bool okA = phA >= 0 && phA < g.num_phys, okB = phB >= 0 && phB < g.num_phys;
+    const int rowA = okA ? (int)(((long)phA * g.Hkv + kvh) * g.P + (tA - pdiv.div(tA) * g.P)) : 0;
+    const int rowB = okB ? (int)(((long)phB * g.Hkv + kvh) * g.P + (tB - pdiv.div(tB) * g.P)) : 0;
+    const float wA = okA ? iA : 0.f, wB = okB ? iB : 0.f;
     float acc[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
