@@ -245,9 +245,16 @@ __global__ __launch_bounds__(1024) void k_idx_scan(IndexArgs a)
     __shared__ int tot_l[kIndexMaxBlocks], off_l[kIndexMaxBlocks];
     const int bk = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int32_t* cnt = a.cnt + (long)bk * a.C * a.nchunks;
+    constexpr int NL = 8;  // a lane's counts of one block loaded together
     for (int c = wave; c < a.C; c += 16) {
         int s = 0;
-        for (int k = lane; k < a.nchunks; k += 64) s += cnt[(long)c * a.nchunks + k];
+        for (int k0 = lane; k0 < a.nchunks; k0 += 64 * NL) {
+            int v[NL];
+#pragma unroll
+            for (int u = 0; u < NL; ++u) v[u] = k0 + 64 * u < a.nchunks ? cnt[(long)c * a.nchunks + k0 + 64 * u] : 0;
+#pragma unroll
+            for (int u = 0; u < NL; ++u) s += v[u];
+        }
         s = __builtin_amdgcn_readlane(wave_inclusive_scan(s), 63);
         if (lane == 0) tot_l[c] = s;
     }
@@ -288,36 +295,54 @@ __global__ __launch_bounds__(1024) void k_idx_scan(IndexArgs a)
     // each chunk's first row in block c: off[c] + the counts of the earlier chunks
     for (int c = wave; c < a.C; c += 16) {
         int carry = off_l[c];
-        for (int k0 = 0; k0 < a.nchunks; k0 += 64) {
-            const int k = k0 + lane;
-            const int n = k < a.nchunks ? cnt[(long)c * a.nchunks + k] : 0;
-            const int inc = wave_inclusive_scan(n);
-            if (k < a.nchunks) cnt[(long)c * a.nchunks + k] = carry + inc - n;
-            carry += __builtin_amdgcn_readlane(inc, 63);
+        for (int k1 = 0; k1 < a.nchunks; k1 += 64 * NL) {
+            int v[NL];
+#pragma unroll
+            for (int u = 0; u < NL; ++u) {
+                const int k = k1 + 64 * u + lane;
+                v[u] = k < a.nchunks ? cnt[(long)c * a.nchunks + k] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < NL; ++u) {
+                const int k = k1 + 64 * u + lane;
+                const int inc = wave_inclusive_scan(v[u]);
+                if (k < a.nchunks) cnt[(long)c * a.nchunks + k] = carry + inc - v[u];
+                carry += __builtin_amdgcn_readlane(inc, 63);
+            }
         }
     }
 }
 
-// One wave per chunk: 64 tokens at a time in position order; a token's row
-// is its block's next free row plus the number of earlier lanes with the
-// same block.
+// One wave per chunk: 64 tokens at a time in position order (the chunk's
+// assignments all loaded first); a token's row is its block's next free row
+// plus the number of earlier lanes with the same block.
 __global__ __launch_bounds__(64) void k_idx_scatter(IndexArgs a)
 {
     extern __shared__ int cur[];  // [C] next free row of each block for this chunk
     const int bk = blockIdx.y, chunk = blockIdx.x, lane = threadIdx.x;
     const int32_t* base = a.cnt + (long)bk * a.C * a.nchunks + chunk;
-    for (int c = lane; c < a.C; c += 64) cur[c] = base[(long)c * a.nchunks];
-    __builtin_amdgcn_wave_barrier();
     const int32_t* as = a.assign + (long)bk * a.N;
     int32_t* pos = a.positions + (long)bk * a.N;
-    for (int s = 0; s < kIndexChunk; s += 64) {
-        const int t = chunk * kIndexChunk + s + lane;
-        const int c = t < a.N ? as[t] : -1;
+    // the chunk's assignments, loaded with the blocks' first rows before the
+    // ordered scatter
+    constexpr int NS = kIndexChunk / 64;
+    int cs[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int t = chunk * kIndexChunk + 64 * u + lane;
+        cs[u] = t < a.N ? as[t] : -1;
+    }
+    for (int c = lane; c < a.C; c += 64) cur[c] = base[(long)c * a.nchunks];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int t = chunk * kIndexChunk + 64 * u + lane;
+        const int c = cs[u];
         int before = 0, after = 0;
-        for (int u = 0; u < 64; ++u) {
-            const int cu = __builtin_amdgcn_readlane(c, u);
-            before += u < lane && cu == c;
-            after += u > lane && cu == c;
+        for (int l = 0; l < 64; ++l) {
+            const int cu = __builtin_amdgcn_readlane(c, l);
+            before += l < lane && cu == c;
+            after += l > lane && cu == c;
         }
         const int at = c >= 0 ? cur[c] + before : 0;
         __builtin_amdgcn_wave_barrier();  // every lane has read its block's counter
