@@ -64,23 +64,40 @@ template <int HD>
 __global__ __launch_bounds__(256) void k_idx_norms(IndexArgs a)
 {
     constexpr int LPT = HD / 8;         // lanes per key (16 bytes each)
-    constexpr int TPB = 256 / LPT;      // keys per workgroup
+    constexpr int TPB = 256 / LPT;      // keys per workgroup and round
+    constexpr int RK = kIndexRowsPerThread;
     const Geometry& g = a.g;
     const FastDiv pdiv{g.pdiv.d, g.pdiv.magic, g.pdiv.shift};
     const int bk = blockIdx.y, b = bk / g.Hkv, kvh = bk - b * g.Hkv;
-    const int t = blockIdx.x * TPB + (int)threadIdx.x / LPT, part = threadIdx.x % LPT;
-    float s = 0.f;
-    if (t < a.N) {
-        const long row = key_row(g, pdiv, b, kvh, t);
-        if (row >= 0) {
-            float x[8];
-            unpack8(*(const uint4*)((const uint16_t*)g.k + row * HD + 8 * part), x);
+    const int part = threadIdx.x % LPT;
+    const int32_t* btr = g.block_table + (long)b * g.max_pages;
+    // RK keys per lane group: their table entries, then their row loads, all
+    // in flight together
+    int t[RK], ph[RK];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = fmaf(x[e], x[e], s);
+    for (int u = 0; u < RK; ++u) {
+        t[u] = (blockIdx.x * RK + u) * TPB + (int)threadIdx.x / LPT;
+        ph[u] = t[u] < a.N ? btr[pdiv.div(t[u])] : -1;
+    }
+    uint4 w[RK];
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+        w[u] = make_uint4(0, 0, 0, 0);
+        if (ph[u] >= 0 && ph[u] < g.num_phys) {  // as key_row: an unmapped page reads as a zero key
+            const long row = ((long)ph[u] * g.Hkv + kvh) * g.P + (t[u] - pdiv.div(t[u]) * g.P);
+            w[u] = *(const uint4*)((const uint16_t*)g.k + row * HD + 8 * part);
         }
     }
-    s = group_sum<LPT>(s);
-    if (t < a.N && part == 0) a.inv_norm[(long)bk * a.N + t] = s > 0.f ? 1.0f / sqrtf(s) : 0.f;
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+        float x[8];
+        unpack8(w[u], x);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(x[e], x[e], s);
+        s = group_sum<LPT>(s);
+        if (t[u] < a.N && part == 0) a.inv_norm[(long)bk * a.N + t[u]] = s > 0.f ? 1.0f / sqrtf(s) : 0.f;
+    }
 }
 
 template <int HD>
@@ -453,7 +470,8 @@ __global__ __launch_bounds__(256) void k_idx_centre(IndexArgs a)
     }
 }
 
-// 16 bytes of one key row and one value row per thread
+// 16 bytes of one key row and one value row per thread (the rows are read
+// in block order, at random positions: four rows per thread were no faster)
 template <int HD>
 __global__ __launch_bounds__(256) void k_idx_gather(IndexArgs a)
 {
@@ -488,7 +506,8 @@ hipError_t build_hd(const IndexArgs& a, hipStream_t s)
     const int nbk = a.g.B * a.g.Hkv;
     const dim3 b256(256);
     const size_t lds_c = (size_t)a.C * sizeof(int);
-    hipLaunchKernelGGL((k_idx_norms<HD>), dim3((a.N + 256 / (HD / 8) - 1) / (256 / (HD / 8)), nbk), b256, 0, s, a);
+    const int keys_wg = 256 / (HD / 8) * kIndexRowsPerThread;  // keys per workgroup of the norms
+    hipLaunchKernelGGL((k_idx_norms<HD>), dim3((a.N + keys_wg - 1) / keys_wg, nbk), b256, 0, s, a);
     hipLaunchKernelGGL((k_idx_init<HD>), dim3((a.C + 256 / (HD / 8) - 1) / (256 / (HD / 8)), nbk), b256, 0, s, a);
     for (int it = 0; it <= a.iters; ++it) {
         hipLaunchKernelGGL((k_idx_assign<HD>), dim3((a.N + 255) / 256, nbk), b256, 0, s, a);

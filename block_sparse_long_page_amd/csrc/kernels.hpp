@@ -203,6 +203,7 @@ struct IndexArgs {
 
 constexpr int kIndexChunk = 1024;    // tokens per counting-sort chunk
 constexpr int kIndexSegment = 128;   // rows per centre-update segment
+constexpr int kIndexRowsPerThread = 4;  // keys a lane group of the norms handles
 constexpr int kIndexMaxBlocks = 4096;
 
 // Block choice of one (sequence, KV head, row) against an index.
