@@ -65,6 +65,7 @@ typedef short gi16x4_t __attribute__((ext_vector_type(4)));
 typedef float gf32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPlanThreads = 256;
+constexpr int kPlanBatch = 8;  // list entries per thread whose loads go out together
 constexpr int kGW = 8;           // waves of a grouped-decode workgroup
 constexpr int kStage = 64;       // tokens per LDS stage
 constexpr float kGSlack = 8.0f;  // log2 units, as the per-row decode
@@ -116,26 +117,54 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     // candidates, or not above their predecessor (a repeated unit among
     // them) are not attended: their slots hold empty partials, so a page is
     // attended at most once per row and the results stay deterministic.
-    auto listed = [&](int idx, int r, int j) -> int {
-        if (j >= imax(0, imin(cnt[r], a.k_max))) return -1;
-        const int p = sel[idx];
-        if (p < lo || p > hi) return -1;
-        return j == 0 || p > sel[idx - 1] ? p : -1;
+    // The entries a thread handles are read kPlanBatch at a time, every
+    // load of a batch in flight together: the entry, the one before it and
+    // the row's count.
+    const int nent = a.Q * a.k_max;
+    struct Listed {
+        int p[kPlanBatch];
     };
-    for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
-        const int r = idx / a.k_max, j = idx - r * a.k_max;
-        const int p = listed(idx, r, j);
-        if (p >= 0) {
-            atomicOr(&mask[2 * p + (r >> 6)], 1ull << (r & 63));
-        } else {
-            // a slot this row does not use: an empty partial (m = -inf, l = 0)
-            // for every head and chunk; the combine does not read its o
-            for (int h = 0; h < g.G; ++h) {
-                const long prow = ((long)b * g.Hq + kvh * g.G + h) * a.Q + r;
-                for (int s = 0; s < a.tsplit; ++s) {
-                    const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
-                    a.part_ml[slot * 2 + 0] = -INFINITY;
-                    a.part_ml[slot * 2 + 1] = 0.f;
+    auto listed_batch = [&](int base) {
+        int pv[kPlanBatch], pb[kPlanBatch], cr[kPlanBatch];
+#pragma unroll
+        for (int u = 0; u < kPlanBatch; ++u) {
+            const int idx = base + u * kPlanThreads + tid;
+            const int r = idx / a.k_max, j = idx - r * a.k_max;
+            pv[u] = idx < nent ? sel[idx] : -1;
+            pb[u] = idx < nent && j > 0 ? sel[idx - 1] : -1;
+            cr[u] = idx < nent ? cnt[r] : 0;
+        }
+        Listed l;
+#pragma unroll
+        for (int u = 0; u < kPlanBatch; ++u) {
+            const int idx = base + u * kPlanThreads + tid;
+            const int r = idx / a.k_max, j = idx - r * a.k_max;
+            const int p = pv[u];
+            const bool used = idx < nent && j < imax(0, imin(cr[u], a.k_max)) && p >= lo && p <= hi;
+            l.p[u] = used && (j == 0 || p > pb[u]) ? p : -1;
+        }
+        return l;
+    };
+    for (int base = 0; base < nent; base += kPlanBatch * kPlanThreads) {
+        const Listed l = listed_batch(base);
+#pragma unroll
+        for (int u = 0; u < kPlanBatch; ++u) {
+            const int idx = base + u * kPlanThreads + tid;
+            if (idx >= nent) break;
+            const int r = idx / a.k_max, j = idx - r * a.k_max;
+            const int p = l.p[u];
+            if (p >= 0) {
+                atomicOr(&mask[2 * p + (r >> 6)], 1ull << (r & 63));
+            } else {
+                // a slot this row does not use: an empty partial (m = -inf, l = 0)
+                // for every head and chunk; the combine does not read its o
+                for (int h = 0; h < g.G; ++h) {
+                    const long prow = ((long)b * g.Hq + kvh * g.G + h) * a.Q + r;
+                    for (int s = 0; s < a.tsplit; ++s) {
+                        const long slot = prow * a.split_stride + (long)j * a.tsplit + s;
+                        a.part_ml[slot * 2 + 0] = -INFINITY;
+                        a.part_ml[slot * 2 + 1] = 0.f;
+                    }
                 }
             }
         }
@@ -208,10 +237,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_group_plan(GroupArgs a)
     __syncthreads();
 
     // each row's index j of every page it lists: its slot for that page
-    for (int idx = tid; idx < a.Q * a.k_max; idx += kPlanThreads) {
-        const int r = idx / a.k_max, j = idx - r * a.k_max;
-        const int p = listed(idx, r, j);
-        if (p >= 0) sl[rank[p] * kGroupMaxRows + r] = (int16_t)j;
+    for (int base = 0; base < nent; base += kPlanBatch * kPlanThreads) {
+        const Listed l = listed_batch(base);
+#pragma unroll
+        for (int u = 0; u < kPlanBatch; ++u) {
+            const int idx = base + u * kPlanThreads + tid;
+            if (idx >= nent) break;
+            const int r = idx / a.k_max, j = idx - r * a.k_max;
+            if (l.p[u] >= 0) sl[rank[l.p[u]] * kGroupMaxRows + r] = (int16_t)j;
+        }
     }
 }
 
