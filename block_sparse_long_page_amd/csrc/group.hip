@@ -466,7 +466,7 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
 
             // this wave's subtiles of stage st: gi, gi + gsz, ...
             auto compute = [&](int st, int buf) {
-                if (!computes) return;
+                if (!computes || st >= nst) return;  // a stage past the chunk's end attends nothing
                 for (int sub = gi; sub < SUB; sub += gsz) {
                     const int tb = st * kStage + sub * 16;  // chunk-relative index of the subtile's token 0
                     const unsigned char* kt = kl(buf) + sub * 16 * KROW;
@@ -525,7 +525,9 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
             // Stages: three in flight in registers, two in LDS.  Every step
             // issues its loads and the loop's only exit is at the end of a round
             // of three, so the waits count one stage each; stages past the end
-            // re-read the chunk's first row and compute nothing.
+            // re-read the chunk's first row and are not computed.  (Leaving the
+            // loop at a chunk's last stage instead made the compiler wait for
+            // every load in flight at the top of the loop: slower.)
             if (pass != pidx) {  // the first pass's stages were issued with the unit
                 fetch(0, X0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -539,15 +541,11 @@ __global__ __launch_bounds__(64 * kGW) void k_group_decode_mfma(GroupArgs a)
                 __syncthreads();
                 fetch(st + 3, X0);
                 compute(st, 0);
-                // prefill (many short chunks): stop at the last stage.  (In plan mode the
-                // exits cost the loop's overlap of loads more than the stages they skip.)
-                if (PF && st + 1 >= nst) break;
                 stash(st + 1, 1, X1);
                 __syncthreads();
                 fetch(st + 4, X1);
                 compute(st + 1, 1);
                 __syncthreads();  // stage st is no longer read from buffer 0
-                if (PF && st + 2 >= nst) break;
                 stash(st + 2, 0, X2);
                 __syncthreads();
                 fetch(st + 5, X2);
