@@ -446,27 +446,30 @@ struct MfmaCore {
 
     // All rounds of the row table, three in flight per wave; the first
     // `loaded` rounds (0 .. 3) may already be loaded into A, B, C.
+    // Rounds of the row table, three in flight.  Every step issues its
+    // loads (rounds past the end read row 0, masked, from one cached line)
+    // and the loop leaves only at the end of a round of three, so the waits
+    // count one round each (conditional loads or an exit inside the round
+    // made the compiler wait for every load in flight).
     __device__ __forceinline__ void run(Buf& A, Buf& B, Buf& C, int loaded)
     {
         const int nr = (nrows + RT - 1) / RT;
-        if (loaded < 1 && nr > 0) load(0, A);
-        if (loaded < 2 && nr > 1) load(1, B);
-        if (loaded < 3 && nr > 2) load(2, C);
+        if (loaded < 1) load(0, A);
+        if (loaded < 2) load(1, B);
+        if (loaded < 3) load(2, C);
         for (int rd = 0; rd < nr; rd += 3) {
 #pragma unroll
             for (int tt = 0; tt < TPS; ++tt)
                 if (busy(rd, tt)) compute(A, tt);
-            if (rd + 3 < nr) load(rd + 3, A);
-            if (rd + 1 >= nr) break;
+            load(rd + 3, A);
 #pragma unroll
             for (int tt = 0; tt < TPS; ++tt)
                 if (busy(rd + 1, tt)) compute(B, tt);
-            if (rd + 4 < nr) load(rd + 4, B);
-            if (rd + 2 >= nr) break;
+            load(rd + 4, B);
 #pragma unroll
             for (int tt = 0; tt < TPS; ++tt)
                 if (busy(rd + 2, tt)) compute(C, tt);
-            if (rd + 5 < nr) load(rd + 5, C);
+            load(rd + 5, C);
         }
     }
 
@@ -481,7 +484,7 @@ struct MfmaCore {
         // head r's sum over the 4 lanes holding it
         l_run += xor_lanes<16>(l_run);
         l_run += xor_lanes<32>(l_run);
-        __syncthreads();
+        lds_barrier();  // the tile loads past the last tile are not waited for
         float* const wv_o = (float*)sm.tiles;  // [NW][G][HD]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -495,7 +498,7 @@ struct MfmaCore {
             sm.wv_m[wave][r] = m_run * sl2;  // -inf stays -inf
             sm.wv_l[wave][r] = l_run;
         }
-        __syncthreads();
+        lds_barrier();
         for (int i = threadIdx.x; i < G * HD / 4; i += 64 * NW) {
             const int h = i / (HD / 4), c4 = i % (HD / 4);
             float ms = -INFINITY;
@@ -694,6 +697,7 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
     __shared__ uint32_t key_range[NW][2];
     __shared__ int sel_lds[kSelCap];
     __shared__ int sel_ready;
+    __shared__ int s_failed;  // some wave gave up its wait for the page list
     __shared__ MfmaLds<HD, G> lds;
 
     int bid = blockIdx.x;
@@ -764,7 +768,10 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
         key_range[wave][0] = lo;
         key_range[wave][1] = hi;
     }
-    if (threadIdx.x == 0) sel_ready = 0;
+    if (threadIdx.x == 0) {
+        sel_ready = 0;
+        s_failed = 0;
+    }
     __syncthreads();
     const int32_t* bt = bt_lds;
 
@@ -876,7 +883,9 @@ __global__ __launch_bounds__((64 * MfmaPlan<HD, G>::NW)) void k_select_decode_mf
             __builtin_amdgcn_s_sleep(2);  // waiting for the page list
         }
     }
-    const bool failed = __syncthreads_or(!done) != 0;
+    if (!done) s_failed = 1;
+    lds_barrier();  // (the masked loads of the last round are not waited for)
+    const bool failed = s_failed != 0;
     if (failed && threadIdx.x == 0 && a.status) __hip_atomic_store(a.status, kStatusGaveUp, __ATOMIC_RELAXED,
                                                                    __HIP_MEMORY_SCOPE_AGENT);
     const long prow0 = ((long)b * g.Hq + kvh * G) * a.Q + row;

@@ -247,6 +247,18 @@ __device__ __forceinline__ uint4 ld_stream(const void* p)
     const nt_u32x4 w = __builtin_nontemporal_load((const nt_u32x4*)p);
     return make_uint4(w.x, w.y, w.z, w.w);
 }
+
+// A workgroup barrier that orders LDS accesses only.  Global loads still in
+// flight (those of a tile pipeline that ran past its last tile, whose
+// results are not used) are not waited for, as __syncthreads would: on this
+// chip one counter covers global loads and stores, and its release waits
+// for all of them.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
 // n / d for 0 <= n < 2^31 with a host-computed magic pair (Granlund and
