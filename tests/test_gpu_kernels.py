@@ -241,6 +241,24 @@ def test_dense_path(name):
     check_lse(dec.lse_f32(), ref.lse, name)
 
 
+# (lengths of the two sequences, splits): with one split a workgroup's row
+# table holds every token, so these put its last round of 128 rows (8 waves
+# of 16) at 1, 127, 128 and 129 rows, the rounds' count at each residue of the
+# three in flight, and the 2048-row chunks of the table one past and one short
+@pytest.mark.parametrize("lens,splits", [
+    ([1, 127], 1), ([128, 129], 1), ([255, 256], 1), ([383, 384], 1), ([385, 511], 1), ([640, 767], 1),
+    ([2047, 2048], 1), ([2049, 2433], 1), ([4481, 6145], 1), ([6145, 385], 3), ([769, 3], 5)])
+@pytest.mark.parametrize("hd", [128, 64])
+def test_dense_decode_at_round_edges(lens, splits, hd):
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=hd, P=16, seq_lens=lens, sink=4, window=32, budget=64,
+                              dtype="bf16", seed=sum(lens) + hd, shuffle=True, spare_pages=3)
+    dc, dec = _run(pr, splits=splits, dense=True)
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=10**9)
+    what = f"lens={lens} splits={splits} hd={hd}"
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, what)
+    check_lse(dec.lse_f32(), ref.lse, what)
+
+
 @pytest.mark.parametrize("name", ["bf16-hd128-g8-p64", "f32-hd64-g4-p16", "bf16-hd64-g1-p7"])
 def test_split_count_invariance_and_determinism(name):
     pr = _problem(name, "quest", seed=3)
