@@ -130,6 +130,40 @@ def test_select_decode_step(name, mode, splits):
     assert torch.equal(dec.out, out1) and torch.equal(dec.lse, lse1)
 
 
+# (sink, window, budget, splits, length), 16-token pages: the select-and-decode
+# workgroup's sink-and-window share at 1, 15, 16 and 128 tokens and at about
+# three tiles per streaming wave, its middle share at one tile, one tile per
+# wave and the most one workgroup takes (2048 tokens, 16 tiles per wave), a
+# first selected page cut by the sink, and a sequence with fewer candidate
+# pages than the budget (nothing ranked)
+@pytest.mark.parametrize("S,W,budget,splits,L", [
+    (0, 1, 16, 1, 600), (7, 8, 128, 1, 1000), (1, 14, 2016, 1, 4000), (64, 337, 1600, 1, 5000),
+    (3, 1000, 1008, 3, 6000), (16, 112, 1888, 2, 3000), (4, 32, 1984, 1, 300)])
+@pytest.mark.parametrize("hd", [128, 64])
+def test_select_decode_at_tile_edges(S, W, budget, splits, L, hd):
+    # the select-and-decode kernel runs when every workgroup's table fits in
+    # 2048 entries (its share of the sink and window rounded up to 16, plus
+    # its share of the pages) and the block-table rows are 16-byte vectors
+    assert splits >= -(-(S + W + budget) // 2031)
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=hd, P=16, seq_lens=[L, L - 17], sink=S, window=W, budget=budget,
+                              dtype="bf16", seed=L + S + W + hd, shuffle=True, spare_pages=3, clusters=8,
+                              max_pages=-(-L // 64) * 4)
+    dc, dec = _run(pr, splits=splits)
+    sel_ref, cnt_ref = dec.selection()
+    q = to_device(pr.q)
+    dec.sel.fill_(-7)
+    dec.count.fill_(-7)
+    dec.fused_step(q)
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    np.testing.assert_array_equal(cnt, cnt_ref)
+    np.testing.assert_array_equal(sel, sel_ref)
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=1, sink=S, window=W, budget=budget, sel=sel, cnt=cnt)
+    what = f"S={S} W={W} budget={budget} splits={splits} L={L} hd={hd}"
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, what)
+    check_lse(dec.lse_f32(), ref.lse, what)
+
+
 @pytest.mark.parametrize("pattern", ["all-equal", "two-values", "two-values-wide", "small-tie-band"])
 @pytest.mark.parametrize("fused", [False, True])
 def test_tied_scores_take_the_lower_pages(pattern, fused):
