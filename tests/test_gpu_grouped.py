@@ -4,7 +4,8 @@ decode of the same selection, and its determinism.  Shapes cover every GQA
 group size, both head dims, pages of 16 to 2048 tokens, 5 to 128 query rows,
 windows shorter than the row count (causal masking of middle tokens), two
 passes over the query columns (G = 8 with 64 rows), rows whose lists are
-shorter than k_max, and several token and sink/window split counts."""
+shorter than k_max, several token and sink/window split counts, and
+pages whose chunks end at the edges of the 64-token stages."""
 import numpy as np
 import pytest
 
@@ -82,6 +83,28 @@ def test_grouped_matches_oracle_and_per_row(name, splits):
     torch.cuda.synchronize()
     check_output(out_g, dec.out_f32(), pr.cache.dtype, name + " grouped vs per-row")
     np.testing.assert_allclose(lse_g, dec.lse_f32(), rtol=0, atol=2e-3)
+
+
+# (page size, length, budget, token splits, head dim): a page's chunk of
+# tokens at 1, 63 and 65 tokens and at 192, 193 and 200 (three stages of 64
+# in flight, one past them, and a ragged fourth), pages that are no power of two
+@pytest.mark.parametrize("P,L,budget,ts,hd", [
+    (1, 600, 64, 1, 128), (63, 3000, 630, 1, 128), (65, 3000, 650, 1, 64), (192, 5000, 1920, 1, 128),
+    (193, 5000, 1930, 1, 64), (400, 6000, 2000, 2, 128)])
+def test_grouped_at_stage_edges(P, L, budget, ts, hd):
+    pr = synth.random_problem(B=2, Hq=8, Hkv=2, hd=hd, P=P, seq_lens=[L, L - 77], sink=5, window=70, budget=budget,
+                              Q=8, mode="quest", dtype="bf16", seed=P + L + hd, shuffle=True, spare_pages=3,
+                              clusters=6)
+    dc, dec, gs, q = _setup(pr, ts, 1)
+    gs.decode(q)
+    gs.combine()
+    torch.cuda.synchronize()
+    sel, cnt = dec.selection()
+    ref = oracle.run(pr.cache, pr.q, mode=pr.mode, Q=pr.Q, sink=pr.sink, window=pr.window, budget=pr.budget,
+                     sel=sel, cnt=cnt)
+    what = f"P={P} L={L} budget={budget} ts={ts} hd={hd}"
+    check_output(dec.out_f32(), ref.out, pr.cache.dtype, what)
+    check_lse(dec.lse_f32(), ref.lse, what)
 
 
 def test_grouped_shares_pages_between_rows():
