@@ -114,6 +114,27 @@ def test_kept_positions(name):
     print(f"{name}: {band} candidates inside the band")
 
 
+# lengths one short of, at and one past the 512-token chunks of the sum pass
+# and the 128 rows a wave streams, with pages of 1 and 2 tokens (a wave's
+# rows over 128 and 64 pages) and of 16
+@pytest.mark.parametrize("P,lens,budget,sink,hd,dtype", [
+    (16, [512, 513, 1023], 300, 4, 128, "bf16"), (1, [127, 128, 129], 100, 1, 128, "bf16"),
+    (1, [1024, 1025, 640], 500, 0, 64, "bf16"), (2, [511, 2049, 64], 256, 8, 128, "f32")])
+def test_kept_positions_at_chunk_edges(P, lens, budget, sink, hd, dtype):
+    pr = synth.random_problem(B=3, Hq=4, Hkv=2, hd=hd, P=P, seq_lens=lens, sink=sink, window=1, budget=budget,
+                              dtype=dtype, seed=sum(lens) + P, shuffle=True, spare_pages=3, clusters=16)
+    c = pr.cache
+    _, _, ev = _evict(pr, budget, sink)
+    kept = ev.kept.cpu().numpy()
+    cnt = ev.count.cpu().numpy()
+    for b in range(c.B):
+        L = int(c.seq_lens[b])
+        for kvh in range(c.Hkv):
+            assert cnt[b, kvh] == min(L, budget)
+            assert (kept[b, kvh, cnt[b, kvh]:] == -1).all()
+            check_kept(kept[b, kvh, : cnt[b, kvh]], dense_keys_values(c, b, kvh)[0], budget, sink)
+
+
 @pytest.mark.parametrize("name", ["bf16-hd128-p16", "bf16-hd128-past-limit", "bf16-hd128-p1"])
 def test_planted_ties_keep_the_later_position(name):
     """Every key is one of four bf16 vectors, so distances tie exactly on both
