@@ -41,6 +41,11 @@ CASES = {
     "hd64-g8-random-300-blocks": ("random", dict(B=1, Hq=8, Hkv=1, hd=64, P=32, L=5000 + 16, W=16, dup=1000), 5000,
                                   300),
     "hd128-g1-more-blocks-than-clusters": ("semantic", dict(hd=128, G=1), None, 20),
+    # key counts one past a workgroup's 256 keys of the assignment and centre
+    # counts one past, one short of and at its rounds of 128 centres
+    "hd128-g2-edges-257-129": ("random", dict(B=1, Hq=4, Hkv=2, hd=128, P=16, L=257 + 8, W=8), 257, 129),
+    "hd64-g4-p1-edges-1023-128": ("random", dict(B=2, Hq=4, Hkv=1, hd=64, P=1, L=1023 + 16, W=16), 1023, 128),
+    "hd128-g1-p64-edges-768-127": ("random", dict(B=1, Hq=2, Hkv=2, hd=128, P=64, L=768 + 8, W=8), 768, 127),
 }
 
 
